@@ -1,0 +1,185 @@
+"""MI355X-native Kimi Delta Attention (KDA): Python binding of ``libkda.so``.
+
+Thin ctypes marshalling over the C ABI declared in ``include/kda.h``: torch
+supplies device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels. There is no fallback: if the
+library is not built, importing the functions raises.
+
+    o, final_state = chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None)
+    o = decode_step(q, k, v, log_alpha, beta, state)          # state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["chunk_fwd", "decode_step", "workspace_size", "abi_version", "status_str",
+           "library_path", "KDAError", "CHUNK"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+CHUNK = 64
+
+KDA_F32, KDA_BF16 = 0, 1
+_DT = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    """A non-OK status returned by the C ABI."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)}")
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run gated_delta_rule_41_amd.build.build() "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.kda_abi_version.restype = ctypes.c_int
+    lib.kda_abi_version.argtypes = []
+    lib.kda_status_str.restype = ctypes.c_char_p
+    lib.kda_status_str.argtypes = [ctypes.c_int]
+    lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
+    lib.kda_chunk_fwd_workspace_size.argtypes = [I32, I64, I32, I32, I32, ctypes.c_int,
+                                                 ctypes.POINTER(SZ)]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, SZ, P]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(_load().kda_abi_version())
+
+
+def status_str(status: int) -> str:
+    return _load().kda_status_str(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"{name}: dtype {t.dtype} not supported (float32 or bfloat16)")
+    return _DT[t.dtype]
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, device: torch.device):
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_size(N: int, T_total: int, H: int, dk: int, dv: int,
+                   in_dtype: torch.dtype = torch.bfloat16) -> int:
+    out = ctypes.c_size_t(0)
+    st = _load().kda_chunk_fwd_workspace_size(int(N), int(T_total), int(H), int(dk), int(dv),
+                                              _DT[in_dtype], ctypes.byref(out))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_fwd_workspace_size")
+    return int(out.value)
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+              beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, *, out_dtype: torch.dtype = torch.float32,
+              want_final_state: bool = True, o: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA prefill over a packed batch (see ``kda_chunk_fwd`` in include/kda.h).
+
+    q, k, log_alpha [T, H, dk]; v [T, H, dv]; beta [T, H]; initial_state
+    [N, H, dk, dv] fp32 or None; cu_seqlens [N+1] int32 on the device or None.
+    Returns (o [T, H, dv] out_dtype, final_state [N, H, dk, dv] fp32 or None).
+    ``final_state`` may be passed as ``initial_state`` for an in-place carry.
+    """
+    lib = _load()
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
+        _check(t, name, dev)
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, log_alpha must be [T, H, dk] and v [T, H, dv]")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", dev)
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = 1
+    if initial_state is not None:
+        _check(initial_state, "initial_state", dev)
+        if initial_state.dtype != torch.float32:
+            raise TypeError("initial_state must be float32")
+    in_dt = _dtype_code(q, "q")
+    gate_dt = _dtype_code(log_alpha, "log_alpha")
+    if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != log_alpha.dtype:
+        raise TypeError("q, k, v must share a dtype; log_alpha and beta must share a dtype")
+    if o is None:
+        o = torch.empty(T, H, dv, dtype=out_dtype, device=dev)
+    out_dt = _dtype_code(o, "o")
+    if final_state is None and want_final_state:
+        final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+    sz = ctypes.c_size_t(0)
+    lib.kda_chunk_fwd_workspace_size(max(N, 1), T, H, dk, dv, in_dt, ctypes.byref(sz))
+    ws_bytes = int(sz.value)  # 0 when the shape is invalid; kda_chunk_fwd then reports why
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+                           _ptr(cu_seqlens), N, T, H, dk, dv, in_dt, gate_dt, out_dt, _ptr(o),
+                           _ptr(final_state), _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_fwd")
+    return o, final_state
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+                beta: torch.Tensor, state: torch.Tensor, *, out_dtype: torch.dtype = torch.float32,
+                o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One recurrent KDA token per sequence (see ``kda_decode_step``): q, k,
+    log_alpha [N, H, dk]; v [N, H, dv]; beta [N, H]; state [N, H, dk, dv] fp32,
+    updated in place. Returns o [N, H, dv]."""
+    lib = _load()
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta),
+                    ("state", state)):
+        _check(t, name, dev)
+    if state.dtype != torch.float32:
+        raise TypeError("state must be float32")
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    if o is None:
+        o = torch.empty(N, H, dv, dtype=out_dtype, device=dev)
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state),
+                             N, H, dk, dv, _dtype_code(q, "q"), _dtype_code(log_alpha, "log_alpha"),
+                             _dtype_code(o, "o"), _ptr(o), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_decode_step")
+    return o

@@ -1,0 +1,241 @@
+// C ABI of the KDA library: argument validation, workspace carve-up, launches.
+// See include/kda.h for the contract of every entry point.
+#include "../../include/kda.h"
+#include "kda_launch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <mutex>
+
+namespace kda {
+
+static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+hipError_t allow_dynamic_lds(const void* kernel, int bytes) {
+    // one bit per (kernel, device); the attribute is idempotent, so a race only repeats the call
+    struct Entry {
+        const void* k;
+        std::atomic<uint64_t> devs;
+    };
+    static Entry table[32];
+    static std::atomic<int> used{0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    const uint64_t bit = 1ull << (dev & 63);
+    const int nu = used.load(std::memory_order_acquire);
+    for (int i = 0; i < nu; ++i)
+        if (table[i].k == kernel && (table[i].devs.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    for (int i = 0; i < nu; ++i)
+        if (table[i].k == kernel) {
+            table[i].devs.fetch_or(bit);
+            return hipSuccess;
+        }
+    static std::mutex mu;
+    std::lock_guard<std::mutex> lock(mu);
+    const int n2 = used.load();
+    for (int i = 0; i < n2; ++i)
+        if (table[i].k == kernel) {
+            table[i].devs.fetch_or(bit);
+            return hipSuccess;
+        }
+    if (n2 < 32) {
+        table[n2].k = kernel;
+        table[n2].devs.store(bit);
+        used.store(n2 + 1, std::memory_order_release);
+    }
+    return hipSuccess;
+}
+
+int64_t chunk_capacity(int N, int64_t T, bool have_cu) {
+    // sum_i ceil(L_i / 64) <= floor((T + 63 N) / 64); one sequence: ceil(T / 64)
+    if (!have_cu) return (T + KDA_CHUNK - 1) / KDA_CHUNK;
+    return (T + (int64_t)(KDA_CHUNK - 1) * N) / KDA_CHUNK;
+}
+
+WsPlan plan_workspace(int64_t NC, int H, int D, bool f32) {
+    const size_t es = f32 ? 4 : 2;
+    const size_t ch = (size_t)NC * (size_t)H;  // chunk-heads
+    const size_t sz[8] = {
+        ch * KDA_CHUNK * D * es,       // qp
+        ch * D * KDA_CHUNK * es,       // km
+        ch * KDA_CHUNK * D * es,       // wn
+        ch * KDA_CHUNK * D * es,       // u
+        ch * KDA_CHUNK * KDA_CHUNK * es,  // aqk
+        ch * D * 4,                    // gam
+        ch * (size_t)D * D * es,       // h
+        ch * KDA_CHUNK * D * es,       // vn
+    };
+    WsPlan p;
+    size_t o = 0;
+    for (int i = 0; i < 8; ++i) {
+        p.off[i] = o;
+        o = align_up(o + sz[i], 256);
+    }
+    p.total = o;
+    return p;
+}
+
+}  // namespace kda
+
+using namespace kda;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool dtype_ok(int d) { return d == KDA_F32 || d == KDA_BF16; }
+size_t esize(int d) { return d == KDA_F32 ? 4 : 2; }
+
+bool head_ok(int32_t dk, int32_t dv) { return (dk == 64 && dv == 64) || (dk == 128 && dv == 128); }
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_str(int s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: a size is out of range";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported head size or dtype";
+        case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: a base address is not 16-byte aligned";
+        case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP call or kernel launch failed";
+        default: return "KDA_ERR_UNKNOWN";
+    }
+}
+
+kda_status kda_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
+                                        kda_dtype in_dtype, size_t* bytes) {
+    if (!bytes) return KDA_ERR_NULL;
+    if (N <= 0 || H <= 0 || T_total < 0 || T_total >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    if (!head_ok(dk, dv) || !dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
+    // the workspace is sized for the packed case; it also covers one sequence
+    const int64_t NC = chunk_capacity(N, T_total, true);
+    *bytes = plan_workspace(NC, H, dk, in_dtype == KDA_F32).total;
+    return KDA_OK;
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
+                         const float* initial_state, const int32_t* cu_seqlens, int32_t N, int64_t T_total,
+                         int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype gate_dtype,
+                         kda_dtype out_dtype, void* o, float* final_state, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (N <= 0 || H <= 0 || T_total < 0 || T_total >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    if (T_total > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
+    if (!cu_seqlens && N != 1) return KDA_ERR_SHAPE;
+    if (!head_ok(dk, dv) || !dtype_ok(in_dtype) || !dtype_ok(gate_dtype) || !dtype_ok(out_dtype))
+        return KDA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(beta) ||
+        !aligned16(o) || !aligned16(initial_state) || !aligned16(final_state) || !aligned16(cu_seqlens))
+        return KDA_ERR_ALIGN;
+    const size_t T = (size_t)T_total;
+    const size_t nqk = T * H * dk * esize(in_dtype), nv = T * H * dv * esize(in_dtype);
+    const size_t nla = T * H * dk * esize(gate_dtype), nb = T * H * esize(gate_dtype);
+    const size_t no = T * H * dv * esize(out_dtype), ns = (size_t)N * H * dk * dv * 4;
+    const size_t ncu = cu_seqlens ? (size_t)(N + 1) * 4 : 0;
+    const void* ins[7] = {q, k, v, log_alpha, beta, initial_state, cu_seqlens};
+    const size_t nin[7] = {nqk, nqk, nv, nla, nb, ns, ncu};
+    for (int i = 0; i < 7; ++i) {
+        if (overlaps(o, no, ins[i], nin[i])) return KDA_ERR_ALIAS;
+        if (i != 5 && overlaps(final_state, ns, ins[i], nin[i])) return KDA_ERR_ALIAS;
+    }
+    if (overlaps(o, no, final_state, ns)) return KDA_ERR_ALIAS;
+    if (final_state && initial_state && final_state != initial_state &&
+        overlaps(final_state, ns, initial_state, ns))
+        return KDA_ERR_ALIAS;
+
+    const bool f32 = in_dtype == KDA_F32;
+    const int64_t NC = chunk_capacity(N, T_total, cu_seqlens != nullptr);
+    const WsPlan plan = plan_workspace(NC, H, dk, f32);
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < plan.total)
+        return KDA_ERR_WORKSPACE;
+    for (int i = 0; i < 7; ++i)
+        if (overlaps(workspace, plan.total, ins[i], nin[i])) return KDA_ERR_ALIAS;
+    if (overlaps(workspace, plan.total, o, no) || overlaps(workspace, plan.total, final_state, ns))
+        return KDA_ERR_ALIAS;
+    if (NC >= (int64_t(1) << 31) / H) return KDA_ERR_SHAPE;
+
+    char* w = static_cast<char*>(workspace);
+    ChunkArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.la = log_alpha;
+    a.beta = beta;
+    a.s0 = initial_state;
+    a.cu = cu_seqlens;
+    a.s_final = final_state;
+    a.o = o;
+    a.N = N;
+    a.T = (int)T_total;
+    a.H = H;
+    a.D = dk;
+    a.NC = (int)NC;
+    a.in_f32 = f32;
+    a.gate_f32 = gate_dtype == KDA_F32;
+    a.out_f32 = out_dtype == KDA_F32;
+    a.qp = w + plan.off[0];
+    a.km = w + plan.off[1];
+    a.wn = w + plan.off[2];
+    a.u = w + plan.off[3];
+    a.aqk = w + plan.off[4];
+    a.gam = reinterpret_cast<float*>(w + plan.off[5]);
+    a.h = w + plan.off[6];
+    a.vn = w + plan.off[7];
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (NC > 0 && launch_prep(a, st) != hipSuccess) return KDA_ERR_HIP;
+    if (launch_recur(a, st) != hipSuccess) return KDA_ERR_HIP;
+    if (NC > 0 && launch_output(a, st) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
+                           float* state, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype,
+                           kda_dtype gate_dtype, kda_dtype out_dtype, void* o, void* stream) {
+    if (!q || !k || !v || !log_alpha || !beta || !state || !o) return KDA_ERR_NULL;
+    if (N <= 0 || H <= 0 || (int64_t)N * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    if (!head_ok(dk, dv) || !dtype_ok(in_dtype) || !dtype_ok(gate_dtype) || !dtype_ok(out_dtype))
+        return KDA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(beta) ||
+        !aligned16(state) || !aligned16(o))
+        return KDA_ERR_ALIGN;
+    const size_t NH = (size_t)N * H;
+    const size_t no = NH * dv * esize(out_dtype), ns = NH * dk * dv * 4;
+    const void* ins[5] = {q, k, v, log_alpha, beta};
+    const size_t nin[5] = {NH * dk * esize(in_dtype), NH * dk * esize(in_dtype), NH * dv * esize(in_dtype),
+                           NH * dk * esize(gate_dtype), NH * esize(gate_dtype)};
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(o, no, ins[i], nin[i]) || overlaps(state, ns, ins[i], nin[i])) return KDA_ERR_ALIAS;
+    if (overlaps(o, no, state, ns)) return KDA_ERR_ALIAS;
+    DecodeArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.la = log_alpha;
+    a.beta = beta;
+    a.state = state;
+    a.o = o;
+    a.N = N;
+    a.H = H;
+    a.D = dk;
+    a.in_f32 = in_dtype == KDA_F32;
+    a.gate_f32 = gate_dtype == KDA_F32;
+    a.out_f32 = out_dtype == KDA_F32;
+    if (launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+}  // extern "C"

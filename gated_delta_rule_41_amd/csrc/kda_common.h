@@ -1,0 +1,313 @@
+// Shared device helpers of the KDA HIP library (gfx950 / CDNA4, wave64).
+//
+// Matrix-core conventions used by every kernel
+// -------------------------------------------
+// All chunk products run on 16x16 output tiles:
+//   half policy: v_mfma_f32_16x16x32_f16 / _bf16 (one instruction per 32-deep slice)
+//   fp32 policy: v_mfma_f32_16x16x4_f32   (eight instructions per 32-deep slice)
+// Lane l of a wave (n = l & 15, g = l >> 4) holds
+//   A operand: row m = n of the 16 x 32 slice, eight k-slots (g, j), j = 0..7
+//   B operand: col n of the 32 x 16 slice, the same eight k-slots (g, j)
+//   C/D:       col n, rows 4g + i (i = 0..3) of the 16 x 16 tile
+// The hardware contracts slot (g, j) of A with slot (g, j) of B, so which
+// logical k a slot carries is ours to choose, as long as both operands agree.
+// We always use the "split" order
+//      k(g, j) = 16 * (j >> 2) + 4 * g + (j & 3)
+// because then a B operand made of two stacked accumulator tiles (rows 0-15
+// and 16-31 of the slice) is just the lane's own accumulator registers:
+// slots j = 0..3 are tile 0 rows 4g..4g+3, slots j = 4..7 are tile 1 rows
+// 4g..4g+3. State tiles and corrected values therefore move from one product
+// to the next without any cross-lane exchange; operands that come from memory
+// are stored pre-permuted in this order so that each lane loads one 16-byte
+// (bf16) or 32-byte (fp32) vector per slice.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int CH = 64;   // chunk length
+constexpr int SUB = 16;  // secondary-chunk length (one MFMA tile)
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
+    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+// round-to-nearest-even fp32 <-> fp16
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// k-slot -> logical k inside a 32-deep slice ("split" order, see above)
+__host__ __device__ constexpr int kslot(int g, int j) { return 16 * (j >> 2) + 4 * g + (j & 3); }
+
+// ---------------------------------------------------------------- operands
+// Value-path products (WY solve, W S, K-^T V_new, Q+ h, A_qk V_new) take fp16
+// operands with fp32 accumulation when the inputs are bf16: fp16 has 3 more
+// mantissa bits than bf16 at the same matrix-core rate, which the accuracy
+// target needs (a single bf16 rounding of the dominant k u^T term already costs
+// a few percent of the state's RMS). Every value-path operand is bounded by the
+// input magnitudes (|q|, |k| for the gated factors; |v| for U, V_new and the
+// state), so the fp16 range holds while |v| and the state stay below ~3e4.
+// With fp32 inputs every product runs in fp32.
+template <bool F32> struct Pol;
+template <> struct Pol<false> {
+    using E = uint16_t;  // fp16 bits
+    struct Frag { f16x8_t v; };
+    static __device__ __forceinline__ float to_f(E x) { return h2f(x); }
+    static __device__ __forceinline__ E from_f(float x) { return f2h(x); }
+    static __device__ __forceinline__ Frag make(const float (&x)[8]) {
+        Frag f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f.v[j] = (_Float16)x[j];
+        return f;
+    }
+    static __device__ __forceinline__ Frag zero() {
+        Frag f;
+        f.v = __builtin_bit_cast(f16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+        return f;
+    }
+    static __device__ __forceinline__ Frag load(const E* p) {  // 16-byte aligned
+        Frag f;
+        f.v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+        return f;
+    }
+    static __device__ __forceinline__ void store(E* p, const Frag& f) {
+        *reinterpret_cast<u32x4_t*>(p) = __builtin_bit_cast(u32x4_t, f.v);
+    }
+    static __device__ __forceinline__ void mma(f32x4_t& acc, const Frag& a, const Frag& b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
+    }
+};
+template <> struct Pol<true> {
+    using E = float;
+    struct Frag { float v[8]; };
+    static __device__ __forceinline__ float to_f(E x) { return x; }
+    static __device__ __forceinline__ E from_f(float x) { return x; }
+    static __device__ __forceinline__ Frag make(const float (&x)[8]) {
+        Frag f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f.v[j] = x[j];
+        return f;
+    }
+    static __device__ __forceinline__ Frag zero() {
+        Frag f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f.v[j] = 0.f;
+        return f;
+    }
+    static __device__ __forceinline__ Frag load(const E* p) {  // 16-byte aligned
+        Frag f;
+        const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0];
+        const f32x4_t b = reinterpret_cast<const f32x4_t*>(p)[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f.v[j] = a[j];
+            f.v[4 + j] = b[j];
+        }
+        return f;
+    }
+    static __device__ __forceinline__ void store(E* p, const Frag& f) {
+        reinterpret_cast<f32x4_t*>(p)[0] = f32x4_t{f.v[0], f.v[1], f.v[2], f.v[3]};
+        reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{f.v[4], f.v[5], f.v[6], f.v[7]};
+    }
+    static __device__ __forceinline__ void mma(f32x4_t& acc, const Frag& a, const Frag& b) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+    }
+};
+
+// Gated intra-chunk products (A_kk, A_qk). Their anchored factors span up to
+// 2^100, outside the fp16 range, so with bf16 inputs they run as split bf16:
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi), and
+// a b ~= a_hi b_hi + a_lo b_hi + a_hi b_lo (16 mantissa bits, fp32 range).
+// The B operand (keys) is kept in LDS as a hi array followed by a lo array.
+template <bool F32> struct APol;
+template <> struct APol<false> {
+    using E = uint16_t;  // bf16 bits
+    static constexpr int PLANES = 2;
+    struct Frag { bf16x8_t hi, lo; };
+    static __device__ __forceinline__ Frag make(const float (&x)[8]) {
+        Frag f;
+        u32x4_t h, l;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint16_t h0 = f2bf(x[2 * j]), h1 = f2bf(x[2 * j + 1]);
+            h[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            l[j] = pack2bf(x[2 * j] - bf2f(h0), x[2 * j + 1] - bf2f(h1));
+        }
+        f.hi = __builtin_bit_cast(bf16x8_t, h);
+        f.lo = __builtin_bit_cast(bf16x8_t, l);
+        return f;
+    }
+    // planes: hi at p, lo at p + plane
+    static __device__ __forceinline__ Frag load(const E* p, int plane) {
+        Frag f;
+        f.hi = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+        f.lo = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p + plane));
+        return f;
+    }
+    static __device__ __forceinline__ void store(E* p, int plane, const Frag& f) {
+        *reinterpret_cast<u32x4_t*>(p) = __builtin_bit_cast(u32x4_t, f.hi);
+        *reinterpret_cast<u32x4_t*>(p + plane) = __builtin_bit_cast(u32x4_t, f.lo);
+    }
+    static __device__ __forceinline__ void mma(f32x4_t& acc, const Frag& a, const Frag& b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+    }
+};
+template <> struct APol<true> {
+    using E = float;
+    static constexpr int PLANES = 1;
+    using Frag = Pol<true>::Frag;
+    static __device__ __forceinline__ Frag make(const float (&x)[8]) { return Pol<true>::make(x); }
+    static __device__ __forceinline__ Frag load(const E* p, int) { return Pol<true>::load(p); }
+    static __device__ __forceinline__ void store(E* p, int, const Frag& f) { Pol<true>::store(p, f); }
+    static __device__ __forceinline__ void mma(f32x4_t& acc, const Frag& a, const Frag& b) {
+        Pol<true>::mma(acc, a, b);
+    }
+};
+
+// B operand built from two accumulator tiles (rows 0-15 = t0, rows 16-31 = t1)
+template <bool F32>
+__device__ __forceinline__ typename Pol<F32>::Frag frag_from_acc(const f32x4_t& t0, const f32x4_t& t1) {
+    float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+    return Pol<F32>::make(x);
+}
+
+// ---------------------------------------------------------------- input loads
+template <typename T> __device__ __forceinline__ float ld_in(const T* p, int64_t i);
+template <> __device__ __forceinline__ float ld_in<uint16_t>(const uint16_t* p, int64_t i) { return bf2f(p[i]); }
+template <> __device__ __forceinline__ float ld_in<float>(const float* p, int64_t i) { return p[i]; }
+
+// four consecutive input elements starting at i (i multiple of 4)
+template <typename T> __device__ __forceinline__ void ld_in4(const T* p, int64_t i, float (&x)[4]);
+template <> __device__ __forceinline__ void ld_in4<uint16_t>(const uint16_t* p, int64_t i, float (&x)[4]) {
+    const u32x2_t u = *reinterpret_cast<const u32x2_t*>(p + i);
+    x[0] = __uint_as_float(u[0] << 16);
+    x[1] = __uint_as_float(u[0] & 0xffff0000u);
+    x[2] = __uint_as_float(u[1] << 16);
+    x[3] = __uint_as_float(u[1] & 0xffff0000u);
+}
+template <> __device__ __forceinline__ void ld_in4<float>(const float* p, int64_t i, float (&x)[4]) {
+    const f32x4_t u = *reinterpret_cast<const f32x4_t*>(p + i);
+    x[0] = u[0];
+    x[1] = u[1];
+    x[2] = u[2];
+    x[3] = u[3];
+}
+
+// ---------------------------------------------------------------- wave scans
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+// Chunk slot -> (sequence, first token, length). Chunk slots of sequence i are
+// [co_i, co_i + ceil(len_i / 64)) with co_i the running sum of chunk counts.
+// Every lane of the calling wave must call it with the same gc.
+struct ChunkLoc {
+    int seq;
+    int t0;
+    int L;
+};
+__device__ __forceinline__ bool locate_chunk(const int32_t* __restrict__ cu, int N, int T, int gc,
+                                             ChunkLoc& out) {
+    if (cu == nullptr) {
+        const int t0 = gc * CH;
+        if (t0 >= T) return false;
+        out.seq = 0;
+        out.t0 = t0;
+        out.L = min(CH, T - t0);
+        return true;
+    }
+    const int lane = threadIdx.x & 63;
+    int base = 0;
+    for (int s0 = 0; s0 < N; s0 += 64) {
+        const int i = s0 + lane;
+        int start = 0, len = 0, nch = 0;
+        if (i < N) {
+            start = cu[i];
+            len = cu[i + 1] - start;
+            nch = (len + CH - 1) / CH;
+        }
+        const int incl = wave_incl_scan(nch);
+        const int total = __shfl(incl, 63, 64);
+        if (gc < base + total) {
+            const unsigned long long m = __ballot(i < N && base + incl > gc);
+            const int src = __ffsll((long long)m) - 1;
+            const int excl = __shfl(incl - nch, src, 64);
+            const int st = __shfl(start, src, 64);
+            const int ln = __shfl(len, src, 64);
+            const int lc = gc - base - excl;
+            out.seq = s0 + src;
+            out.t0 = st + lc * CH;
+            out.L = min(CH, ln - lc * CH);
+            return true;
+        }
+        base += total;
+    }
+    return false;
+}
+
+// Chunk-slot offset and chunk count of sequence `seq` (uniform across the wave).
+__device__ __forceinline__ void seq_chunks(const int32_t* __restrict__ cu, int T, int seq, int& co, int& nch) {
+    if (cu == nullptr) {
+        co = 0;
+        nch = (T + CH - 1) / CH;
+        return;
+    }
+    const int lane = threadIdx.x & 63;
+    int base = 0;
+    for (int s0 = 0; s0 < seq; s0 += 64) {
+        const int i = s0 + lane;
+        int n = 0;
+        if (i < seq) n = (cu[i + 1] - cu[i] + CH - 1) / CH;
+        const int incl = wave_incl_scan(n);
+        base += __shfl(incl, 63, 64);
+    }
+    co = base;
+    nch = (cu[seq + 1] - cu[seq] + CH - 1) / CH;
+}
+
+// ---------------------------------------------------------------- workspace
+// Per (chunk slot, head) intermediates, each array [NC][H][...]:
+//   qp   [64][D]   gated queries  Q+ = exp(g) * q, rows in order, k = key channel (split order per 32)
+//   km   [D][64]   decayed keys K- = exp(g_last - g) * k, transposed: row = key channel, k = chunk row
+//   wn   [64][D]   -W (negated key WY factor), k = key channel (split order)
+//   u    [D/16][4][64 lanes][4]   U in accumulator-tile order (value col tile, row tile, lane, i)
+//   aqk  [64][64]  gated query-key matrix (lower incl. diagonal), k = chunk col (split order)
+//   gam  [D] fp32  exp(g_last) per key channel
+//   h    [D/16][D/32][64 lanes][8]   chunk-entry state as B-operand fragments (value col tile, k slice)
+//   vn   [D/16][2][64 lanes][8]      corrected values V_new as B-operand fragments
+template <typename E>
+struct Ws {
+    E* qp;
+    E* km;
+    E* wn;
+    E* u;
+    E* aqk;
+    float* gam;
+    E* h;
+    E* vn;
+};
+
+}  // namespace kda

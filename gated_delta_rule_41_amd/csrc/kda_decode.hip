@@ -1,0 +1,129 @@
+// K4: one recurrent KDA decode step, in place on the fp32 state.
+//
+// For each (sequence, head), with a = exp(log_alpha), state S (dk x dv):
+//   u = beta * (v - S^T (a * k))       residual against the decayed state
+//   S <- Diag(a) S + k u^T             decay, then delta-rule write
+//   o = S^T q                          read with the updated state
+// (the recurrence for one token; GeekNews "Kimi Linear" summary, sections
+// "Da atenção linear ao Gated DeltaNet" and "Controle fino de memória no Kimi
+// Delta Attention"; the fixed-size state that decode streams is the point of
+// remio.ai "Kimi Linear Acabou de Superar ...", section "Por Que a
+// Decodificação de Contexto Longo Coloca a Atenção Completa sob Pressão").
+//
+// Memory-bound: 2 * dk * dv * 4 bytes of state per head-step. One 256-thread
+// workgroup per (sequence, head); thread t owns four adjacent value columns
+// (one 16-byte vector per row) of dk / R rows, R = 1024 / dv row groups, so a
+// wave reads whole 512-byte rows and every state byte is read and written once
+// with 16-byte coalesced accesses. The two column sums (S^T (a*k) and S^T q)
+// are reduced across row groups through LDS.
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <int D, typename TIn, typename TG, bool OUT_F32>
+__global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                                     const TIn* __restrict__ v, const TG* __restrict__ la,
+                                                     const TG* __restrict__ beta, float* __restrict__ state,
+                                                     void* __restrict__ o, int NH) {
+    constexpr int CQ = D / 4;        // column quads
+    constexpr int R = 256 / CQ;      // row groups
+    constexpr int RPT = D / R;       // rows per thread
+    __shared__ f32x4_t red[R][CQ];
+
+    const int unit = blockIdx.x;     // sequence * H + head
+    if (unit >= NH) return;
+    const int tid = threadIdx.x;
+    const int cq = tid % CQ;
+    const int rg = tid / CQ;
+    const int64_t vec = (int64_t)unit * D;
+    f32x4_t* S = reinterpret_cast<f32x4_t*>(state + (int64_t)unit * D * D);
+
+    f32x4_t s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(&S[(rg + R * i) * CQ + cq]);
+
+    float a[RPT], kk[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + R * i;
+        a[i] = __expf(ld_in(la, vec + r));
+        kk[i] = ld_in(k, vec + r);
+    }
+    // partial S^T (a * k) over this thread's rows
+    f32x4_t p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const float w = a[i] * kk[i];
+        p += w * s[i];
+    }
+    red[rg][cq] = p;
+    __syncthreads();
+    f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < R; ++i) tot += red[i][cq];
+    const float b = ld_in(beta, (int64_t)unit);
+    float vv[4];
+    ld_in4(v, vec + 4 * cq, vv);
+    f32x4_t u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) u[j] = b * (vv[j] - tot[j]);
+
+    // decay + write, stream the new state out, and accumulate S^T q
+    f32x4_t po = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + R * i;
+        const f32x4_t ns = a[i] * s[i] + kk[i] * u;
+        __builtin_nontemporal_store(ns, &S[r * CQ + cq]);
+        po += ld_in(q, vec + r) * ns;
+    }
+    __syncthreads();  // everyone has read red[] for the first sum
+    red[rg][cq] = po;
+    __syncthreads();
+    if (rg == 0) {
+        f32x4_t ot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < R; ++i) ot += red[i][cq];
+        if (OUT_F32) {
+            reinterpret_cast<f32x4_t*>(static_cast<float*>(o) + vec)[cq] = ot;
+        } else {
+            u32x2_t w;
+            w[0] = pack2bf(ot[0], ot[1]);
+            w[1] = pack2bf(ot[2], ot[3]);
+            reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(o) + vec)[cq] = w;
+        }
+    }
+}
+
+template <int D, typename TIn, typename TG>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+    const int NH = a.N * a.H;
+    dim3 grid(NH), block(256);
+    if (a.out_f32)
+        hipLaunchKernelGGL((decode_kernel<D, TIn, TG, true>), grid, block, 0, st, (const TIn*)a.q,
+                           (const TIn*)a.k, (const TIn*)a.v, (const TG*)a.la, (const TG*)a.beta, a.state,
+                           a.o, NH);
+    else
+        hipLaunchKernelGGL((decode_kernel<D, TIn, TG, false>), grid, block, 0, st, (const TIn*)a.q,
+                           (const TIn*)a.k, (const TIn*)a.v, (const TG*)a.la, (const TG*)a.beta, a.state,
+                           a.o, NH);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st) {
+    if (a.in_f32) {
+        if (a.gate_f32) return launch_decode_t<D, float, float>(a, st);
+        return launch_decode_t<D, float, uint16_t>(a, st);
+    }
+    if (a.gate_f32) return launch_decode_t<D, uint16_t, float>(a, st);
+    return launch_decode_t<D, uint16_t, uint16_t>(a, st);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+    if (a.N == 0) return hipSuccess;
+    return a.D == 128 ? launch_decode_d<128>(a, st) : launch_decode_d<64>(a, st);
+}
+
+}  // namespace kda

@@ -1,0 +1,49 @@
+// Internal launch interface between the C ABI (kda_abi.hip) and the kernels.
+// Arguments are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    const void *q, *k, *v, *la, *beta;
+    float* state;
+    void* o;
+    int N, H, D;
+    bool in_f32, gate_f32, out_f32;
+};
+
+struct ChunkArgs {
+    const void *q, *k, *v, *la, *beta;
+    const float* s0;        // may be null
+    const int32_t* cu;      // may be null (one sequence)
+    float* s_final;         // may be null
+    void* o;
+    int N, T, H, D;
+    int NC;                 // chunk-slot capacity of the workspace
+    bool in_f32, gate_f32, out_f32;
+    // workspace arrays (element type bf16 bits or fp32, per in_f32)
+    void *qp, *km, *wn, *u, *aqk, *h, *vn;
+    float* gam;
+};
+
+// Workspace carve-up shared by the size query and the launcher.
+struct WsPlan {
+    size_t off[8];   // qp, km, wn, u, aqk, gam, h, vn
+    size_t total;
+};
+WsPlan plan_workspace(int64_t NC, int H, int D, bool f32);
+int64_t chunk_capacity(int N, int64_t T, bool have_cu);
+
+// Opt a kernel into more than 64 KiB of dynamic LDS, once per device.
+hipError_t allow_dynamic_lds(const void* kernel, int bytes);
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_prep(const ChunkArgs& a, hipStream_t st);
+hipError_t launch_recur(const ChunkArgs& a, hipStream_t st);
+hipError_t launch_output(const ChunkArgs& a, hipStream_t st);
+
+}  // namespace kda

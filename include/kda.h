@@ -1,0 +1,145 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) library.
+ *
+ * KDA is a gated delta-rule recurrence with a per-channel (diagonal) forget
+ * gate. For one sequence and one head, with a state S of dk x dv:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                       alpha_t = exp(log_alpha_t)
+ *
+ * The delta rule with a channel-wise gate is described on the GeekNews "Kimi
+ * Linear" summary (pt.news.hada.io topic 31936), sections "Da atenção linear ao
+ * Gated DeltaNet" and "Controle fino de memória no Kimi Delta Attention";
+ * prefill uses the chunkwise-parallel algorithm of sections "Algoritmo paralelo
+ * por chunks" and "Menos computação que o DPLR geral" (fixed-size chunks whose
+ * final state seeds the next, WY factors from one UT transform built by forward
+ * substitution, matrix-form state update, output = inter-chunk recurrent part +
+ * intra-chunk parallel part). Decode is one recurrent step with a fixed-size
+ * state (remio.ai "Kimi Linear Acabou de Superar a Atenção Completa em Seus
+ * Próprios Termos", section "Por Que a Decodificação de Contexto Longo Coloca a
+ * Atenção Completa sob Pressão").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers (HIP, gfx950) unless marked host.
+ *    Every tensor is dense and contiguous in the layout given; all base
+ *    addresses must be 16-byte aligned (KDA_ERR_ALIGN otherwise).
+ *  - Layouts are token-major: q, k, log_alpha [T, H, dk]; v [T, H, dv];
+ *    beta [T, H]; o [T, H, dv]; states [N, H, dk, dv] fp32 (dv fastest).
+ *  - No query scaling is applied (callers pre-scale q if they want 1/sqrt(dk)).
+ *  - Supported head sizes: (dk, dv) in {(64, 64), (128, 128)}.
+ *  - Supported dtypes: in_dtype (q, k, v) and gate_dtype (log_alpha, beta) are
+ *    each KDA_BF16 or KDA_F32; out_dtype (o) KDA_F32 or KDA_BF16. With
+ *    in_dtype == KDA_BF16 the chunk products run on bf16 matrix cores with
+ *    fp32 accumulation and an fp32 state; with KDA_F32 they run in fp32.
+ *  - log_alpha must be finite (<= 0 for the overflow guarantees; 0 is allowed).
+ *    Non-finite inputs give undefined (typically NaN) outputs; inputs are not scanned.
+ *  - Ownership: the caller owns every buffer. The library never allocates or
+ *    frees device memory and keeps no pointer after a call returns.
+ *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and the call returns without synchronising. Buffers must stay
+ *    valid until the stream has passed the enqueued work. No host<->device
+ *    copies are made; cu_seqlens is read on the device only.
+ *  - Errors: arguments are validated on the host before any HIP call and a
+ *    status is returned; nothing is enqueued on failure. KDA_ERR_HIP reports
+ *    a launch failure. No C++ exception crosses this boundary.
+ *  - Thread safety: every entry point may be called from several host threads
+ *    at once; calls on one stream run in order. The library holds no mutable
+ *    global state besides a lazily filled, read-only device-properties cache.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+#define KDA_CHUNK 64 /* fixed chunk length of the prefill algorithm */
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL */
+    KDA_ERR_SHAPE = 2,       /* a size is out of range (<= 0, too large) */
+    KDA_ERR_UNSUPPORTED = 3, /* unsupported (dk, dv) or dtype combination */
+    KDA_ERR_ALIGN = 4,       /* a base address is not 16-byte aligned */
+    KDA_ERR_ALIAS = 5,       /* an output overlaps an input it must not overlap */
+    KDA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
+    KDA_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
+} kda_status;
+
+/* Version of this ABI (KDA_ABI_VERSION of the built library). */
+int kda_abi_version(void);
+
+/* Static, human-readable name of a status code ("KDA_OK", ...). Never NULL. */
+const char* kda_status_str(int status);
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for a batch of N sequences
+ * with T_total tokens in all (host call, no device access). The workspace
+ * holds the per-chunk factors (gated queries and keys, WY factors, the
+ * intra-chunk query-key matrix, chunk-entry states, corrected values) for at
+ * most floor((T_total + 63*N) / 64) chunks per head.
+ *   bytes: host out-pointer, written on KDA_OK.
+ */
+kda_status kda_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk,
+                                        int32_t dv, kda_dtype in_dtype, size_t* bytes);
+
+/*
+ * Chunkwise prefill of a packed batch: kda_chunk_fwd(q, k, v, log_alpha, beta,
+ * initial_state, cu_seqlens) -> (o, final_state).
+ *
+ *   q, k          [T_total, H, dk] in_dtype
+ *   v             [T_total, H, dv] in_dtype
+ *   log_alpha     [T_total, H, dk] gate_dtype   (natural-log forget gate per key channel)
+ *   beta          [T_total, H]     gate_dtype   (delta-rule write strength)
+ *   initial_state [N, H, dk, dv] fp32, or NULL for zero states
+ *   cu_seqlens    [N+1] int32 device array of sequence starts (cu[0] = 0,
+ *                 non-decreasing, cu[N] = T_total), or NULL for one sequence
+ *                 (then N must be 1). Zero-length sequences are allowed (their
+ *                 final state equals the initial state). A malformed array is
+ *                 undefined behaviour (it is not read on the host).
+ *   o             [T_total, H, dv] out_dtype, written for every token
+ *                 (q, k, v, log_alpha, beta and o may be NULL when T_total == 0)
+ *   final_state   [N, H, dk, dv] fp32, or NULL if not wanted. It may be the
+ *                 same pointer as initial_state (in-place carry); any other
+ *                 overlap with an input is KDA_ERR_ALIAS.
+ *   workspace     device buffer of at least kda_chunk_fwd_workspace_size()
+ *                 bytes, 256-byte aligned; its contents on entry do not matter
+ *                 and are clobbered.
+ * Chunks of KDA_CHUNK tokens never cross a sequence boundary; a sequence's last
+ * chunk may be partial. The call is deterministic (no atomics): the same inputs
+ * give bitwise identical outputs.
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                         int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
+                         kda_dtype in_dtype, kda_dtype gate_dtype, kda_dtype out_dtype, void* o,
+                         float* final_state, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * One recurrent decode step for N independent sequences, one token each:
+ * kda_decode_step(q, k, v, log_alpha, beta, state) -> (o, state').
+ *
+ *   q, k       [N, H, dk] in_dtype;  v [N, H, dv] in_dtype
+ *   log_alpha  [N, H, dk] gate_dtype; beta [N, H] gate_dtype
+ *   state      [N, H, dk, dv] fp32, read and overwritten in place with S_t
+ *   o          [N, H, dv] out_dtype, o = S_t^T q (the updated state)
+ * o must not overlap state or any input (KDA_ERR_ALIAS).
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                           const void* beta, float* state, int32_t N, int32_t H, int32_t dk,
+                           int32_t dv, kda_dtype in_dtype, kda_dtype gate_dtype,
+                           kda_dtype out_dtype, void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,143 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/kda.h declares, sizes the workspace as documented and
+rejects bad arguments with the right status before touching the device.
+
+Argument-validation calls use fake, never-dereferenced device addresses: every
+case here fails validation, so nothing is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_41_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, WORKSPACE, HIP = range(8)
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = kda._load()
+    names = declared_functions()
+    assert names == ["kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
+                     "kda_decode_step", "kda_status_str"]
+    for nm in names:
+        assert hasattr(lib, nm), nm
+
+
+def test_version_and_status_strings():
+    assert kda.abi_version() == 1
+    for s in range(8):
+        assert kda.status_str(s).startswith("KDA_")
+    assert kda.status_str(99) == "KDA_ERR_UNKNOWN"
+
+
+def test_workspace_size_formula():
+    # per chunk-head, d = 128, bf16 factors: Q+, K-, -W, U, V_new 16 KiB each, A_qk 8 KiB,
+    # gamma 512 B, chunk-entry state 32 KiB -> 123392 B; chunks = floor((T + 63 N) / 64)
+    assert kda.workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 123392
+    assert kda.workspace_size(16, 135000, 32, 128, 128) == ((135000 + 63 * 16) // 64) * 32 * 123392
+    # fp32 factors double every array but gamma
+    assert kda.workspace_size(1, 256, 1, 64, 64, __import__("torch").float32) == 4 * (
+        4 * (64 * 64 * 4) + 64 * 64 * 4 + 64 * 4 + 64 * 64 * 4 + 64 * 64 * 4)
+    with pytest.raises(kda.KDAError):
+        kda.workspace_size(1, 10, 1, 96, 96)
+    with pytest.raises(kda.KDAError):
+        kda.workspace_size(0, 10, 1, 64, 64)
+
+
+class Fake:
+    """Fake device addresses laid out far apart (never dereferenced)."""
+
+    def __init__(self):
+        self.base = 0x7F0000000000
+        self.i = 0
+
+    def __call__(self, off=0):
+        self.i += 1
+        return self.base + self.i * (1 << 36) + off
+
+
+def chunk_call(**over):
+    f = Fake()
+    a = dict(q=f(), k=f(), v=f(), la=f(), beta=f(), s0=None, cu=None, N=1, T=256, H=2, dk=64, dv=64,
+             in_dt=BF16, gate_dt=BF16, out_dt=F32, o=f(), sf=f(), ws=f(), ws_bytes=1 << 40, stream=None)
+    a.update(over)
+    lib = kda._load()
+    P = ctypes.c_void_p
+    return lib.kda_chunk_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["la"]), P(a["beta"]), P(a["s0"]),
+                             P(a["cu"]), a["N"], a["T"], a["H"], a["dk"], a["dv"], a["in_dt"],
+                             a["gate_dt"], a["out_dt"], P(a["o"]), P(a["sf"]), P(a["ws"]),
+                             a["ws_bytes"], P(a["stream"]))
+
+
+def test_chunk_fwd_validation():
+    assert chunk_call(q=None) == NULL
+    assert chunk_call(o=None) == NULL
+    assert chunk_call(N=0) == SHAPE
+    assert chunk_call(T=-1) == SHAPE
+    assert chunk_call(T=1 << 31) == SHAPE
+    assert chunk_call(N=2) == SHAPE  # several sequences need cu_seqlens
+    assert chunk_call(dk=96, dv=96) == UNSUP
+    assert chunk_call(dk=64, dv=128) == UNSUP
+    assert chunk_call(in_dt=5) == UNSUP
+    assert chunk_call(out_dt=2) == UNSUP
+    f = Fake()
+    assert chunk_call(q=f(2)) == ALIGN
+    assert chunk_call(cu=f(4), N=1) == ALIGN
+    # o overlapping q
+    q = f()
+    assert chunk_call(q=q, o=q + 64) == ALIAS
+    # final state overlapping an input other than the initial state
+    k = f()
+    assert chunk_call(k=k, sf=k) == ALIAS
+    # partially overlapping initial/final state
+    s = f()
+    assert chunk_call(s0=s, sf=s + 256) == ALIAS
+    # workspace
+    assert chunk_call(ws=None) == WORKSPACE
+    assert chunk_call(ws=f(16)) == WORKSPACE
+    need = kda.workspace_size(1, 256, 2, 64, 64)
+    assert chunk_call(ws_bytes=need - 1) == WORKSPACE
+    w = f()
+    assert chunk_call(ws=w, q=w + need // 2) == ALIAS
+
+
+def decode_call(**over):
+    f = Fake()
+    a = dict(q=f(), k=f(), v=f(), la=f(), beta=f(), state=f(), N=4, H=2, dk=128, dv=128,
+             in_dt=BF16, gate_dt=BF16, out_dt=F32, o=f(), stream=None)
+    a.update(over)
+    P = ctypes.c_void_p
+    return kda._load().kda_decode_step(P(a["q"]), P(a["k"]), P(a["v"]), P(a["la"]), P(a["beta"]),
+                                       P(a["state"]), a["N"], a["H"], a["dk"], a["dv"], a["in_dt"],
+                                       a["gate_dt"], a["out_dt"], P(a["o"]), P(a["stream"]))
+
+
+def test_decode_validation():
+    assert decode_call(state=None) == NULL
+    assert decode_call(N=0) == SHAPE
+    assert decode_call(dk=32, dv=32) == UNSUP
+    f = Fake()
+    assert decode_call(state=f(8)) == ALIGN
+    s = f()
+    assert decode_call(state=s, o=s + 1024) == ALIAS
+    v = f()
+    assert decode_call(v=v, state=v) == ALIAS
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="would launch on fake pointers")
+def test_valid_arguments_reach_the_launch_without_gpu():
+    """With no GPU present, valid arguments pass validation and the launch
+    itself reports KDA_ERR_HIP (the library never falls back to the CPU)."""
+    assert decode_call() == HIP
+    assert chunk_call() == HIP

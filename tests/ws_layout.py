@@ -1,0 +1,98 @@
+"""Decoder of the prefill workspace layout (fp16 factors for bf16 inputs, fp32 for fp32), for tests that compare the GPU's
+per-chunk intermediates with the CPU chunkwise form. It mirrors the layout
+documented in gated_delta_rule_41_amd/csrc/kda_common.h (the "split" k order
+inside each 32-deep slice: k(g, j) = 16 (j >> 2) + 4 g + (j & 3))."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+CH = 64
+
+
+def kslot(g, j):
+    return 16 * (j >> 2) + 4 * g + (j & 3)
+
+
+# position p = 8 g + j inside a slice -> logical index
+SPLIT = np.array([kslot(p >> 3, p & 7) for p in range(32)])
+
+
+def chunk_capacity(N, T, have_cu):
+    return (T + CH - 1) // CH if not have_cu else (T + (CH - 1) * N) // CH
+
+
+def plan(NC, H, D, f32):
+    es = 4 if f32 else 2
+    ch = NC * H
+    sizes = [ch * CH * D * es, ch * D * CH * es, ch * CH * D * es, ch * CH * D * es,
+             ch * CH * CH * es, ch * D * 4, ch * D * D * es, ch * CH * D * es]
+    off, o = [], 0
+    for s in sizes:
+        off.append(o)
+        o = (o + s + 255) // 256 * 256
+    return off, o
+
+
+def _as_f(raw: np.ndarray, f32: bool) -> np.ndarray:
+    """fp32 factors with fp32 inputs; fp16 factors with bf16 inputs."""
+    if f32:
+        return raw.view(np.float32).astype(np.float64)
+    return raw.view(np.float16).astype(np.float64)
+
+
+def decode(ws: torch.Tensor, N, T, H, D, f32, have_cu, gc, h):
+    """Intermediates of chunk slot gc, head h as fp64 numpy arrays."""
+    NC = chunk_capacity(N, T, have_cu)
+    off, _ = plan(NC, H, D, f32)
+    es = 4 if f32 else 2
+    raw = ws.cpu().numpy()
+    chh = gc * H + h
+    NS, NCT = D // 32, D // 16
+
+    def arr(i, n_el, es_=es, f=f32):
+        b = off[i] + chh * n_el * es_
+        return _as_f(raw[b:b + n_el * es_].copy(), f)
+
+    out = {}
+    qp = arr(0, CH * D).reshape(CH, NS, 32)
+    out["Qp"] = np.zeros((CH, D))
+    out["Qp"][:, (np.arange(NS)[:, None] * 32 + SPLIT[None, :]).ravel()] = qp.reshape(CH, -1)
+    km = arr(1, D * CH).reshape(D, 2, 32)
+    Km_T = np.zeros((D, CH))
+    Km_T[:, (np.arange(2)[:, None] * 32 + SPLIT[None, :]).ravel()] = km.reshape(D, -1)
+    out["Km"] = Km_T.T
+    wn = arr(2, CH * D).reshape(CH, NS, 32)
+    W = np.zeros((CH, D))
+    W[:, (np.arange(NS)[:, None] * 32 + SPLIT[None, :]).ravel()] = -wn.reshape(CH, -1)
+    out["W"] = W
+    u = arr(3, CH * D).reshape(NCT, 4, 64, 4)
+    U = np.zeros((CH, D))
+    for ct in range(NCT):
+        for I in range(4):
+            for l in range(64):
+                n, g = l & 15, l >> 4
+                for i in range(4):
+                    U[16 * I + 4 * g + i, 16 * ct + n] = u[ct, I, l, i]
+    out["U"] = U
+    aq = arr(4, CH * CH).reshape(CH, 2, 32)
+    A = np.zeros((CH, CH))
+    A[:, (np.arange(2)[:, None] * 32 + SPLIT[None, :]).ravel()] = aq.reshape(CH, -1)
+    out["Aqk"] = A
+    b = off[5] + chh * D * 4
+    out["gam"] = raw[b:b + D * 4].copy().view(np.float32).astype(np.float64)
+    hh = arr(6, D * D).reshape(NCT, NS, 64, 8)
+    Hm = np.zeros((D, D))
+    vn = arr(7, CH * D).reshape(NCT, 2, 64, 8)
+    Vn = np.zeros((CH, D))
+    for ct in range(NCT):
+        for l in range(64):
+            n, g = l & 15, l >> 4
+            for j in range(8):
+                for s in range(NS):
+                    Hm[32 * s + kslot(g, j), 16 * ct + n] = hh[ct, s, l, j]
+                for s in range(2):
+                    Vn[32 * s + kslot(g, j), 16 * ct + n] = vn[ct, s, l, j]
+    out["h"] = Hm
+    out["Vn"] = Vn
+    return out
