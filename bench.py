@@ -1,0 +1,281 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one chunkwise prefill call (per-chunk preparation, inter-chunk
+state recursion, fused output) on the ``prefill-4k`` workload: B=1, H=32,
+T=4096, dk=dv=128, chunk 64, bf16 inputs, fp32 initial/final state and fp32
+output (synthetic, seeded; see kda_inputs). The decode step (the remaining row
+of the hot path) is timed in the same run on ``decode-256`` (256 sequences x 32
+heads, fp32 states of 512 MiB, updated in place) and reported in the same JSON
+line. Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--decode-steps S] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + TFLOP/s (% MFMA peak); decode state GB/s (% HBM peak)"
+PEAK_BF16 = 2.5e15       # dense bf16/fp16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12        # HBM3E, B/s
+# per token-head, d = 128, chunk 64 ("Work and bytes")
+FLOP_PER_TOKEN_HEAD = 140629
+ALG_BYTES_PER_TOKEN_HEAD = 1538            # q,k,v,log_alpha bf16 + beta bf16 + o fp32
+KERNEL_BYTES_PER_TOKEN_HEAD = {            # compulsory traffic of each prefill kernel
+    "prep": 1026 + 1160,                   # reads q,k,v,log_alpha,beta; writes Q+,K-,W,U,A_qk,gamma
+    "recur": 776 + 768,                    # reads W,K-,U,gamma; writes h, V_new
+    "output": 1152 + 512,                  # reads Q+,A_qk,h,V_new; writes o (fp32)
+}
+KERNEL_SYMBOL = {"prep": "prep_kernel", "recur": "recur_kernel", "output": "output_kernel",
+                 "decode": "decode_kernel"}
+KERNEL_SOURCE = {"prep": "kda_prep.hip", "recur": "kda_recur.hip", "output": "kda_output.hip",
+                 "decode": "kda_decode.hip"}
+
+
+def hip_runtime():
+    for name in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+        try:
+            lib = ctypes.CDLL(name)
+            lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            return lib
+        except OSError:
+            continue
+    raise RuntimeError("libamdhip64.so not found")
+
+
+class Events:
+    def __init__(self, hip, n):
+        self.hip = hip
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e.value)
+
+    def record(self, i, stream):
+        if self.hip.hipEventRecord(ctypes.c_void_p(self.ev[i]), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        self.hip.hipEventSynchronize(ctypes.c_void_p(self.ev[b]))
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(self.ev[a]),
+                                        ctypes.c_void_p(self.ev[b])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCE[kernel], "kda_common.h"):
+        with open(os.path.join(ROOT, "gated_delta_rule_41_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, units: int):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_prefill-4k.json" if kernel != "decode"
+                        else "pmc_decode_decode-256.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_prefill(kda, case, steps, warmup, hip, stream):
+    import torch
+    dev = case.q.device
+    ws = torch.empty(kda.workspace_size(case.N, case.T_total, case.H, case.dk, case.dv, case.q.dtype),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty(case.T_total, case.H, case.dv, dtype=torch.float32, device=dev)
+    fs = torch.empty(case.N, case.H, case.dk, case.dv, dtype=torch.float32, device=dev)
+
+    def call(events=None):
+        kda.chunk_fwd(case.q, case.k, case.v, case.log_alpha, case.beta, case.initial_state,
+                      case.cu_seqlens, o=o, final_state=fs, workspace=ws, events=events)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # per-kernel durations: HIP events at the stage boundaries, on the launch stream
+    ev = Events(hip, 4 * steps)
+    for s in range(steps):
+        call(events=ev.ev[4 * s:4 * s + 4])
+    torch.cuda.synchronize()
+    per = {"prep": 0.0, "recur": 0.0, "output": 0.0}
+    span = 0.0
+    for s in range(steps):
+        b = 4 * s
+        per["prep"] += ev.ms(b, b + 1)
+        per["recur"] += ev.ms(b + 1, b + 2)
+        per["output"] += ev.ms(b + 2, b + 3)
+        span += ev.ms(b, b + 3)
+    ev.close()
+    per = {k_: v_ / steps for k_, v_ in per.items()}
+    return wall_ms, per, span / steps, o, fs
+
+
+def time_decode(kda, dec, steps, warmup, hip, stream):
+    import torch
+    state = dec["state"]
+    o = torch.empty(state.shape[0], state.shape[1], state.shape[3], dtype=torch.float32,
+                    device=state.device)
+    n_in = dec["q"].shape[0]
+    for s in range(warmup):
+        j = s % n_in
+        kda.decode_step(dec["q"][j], dec["k"][j], dec["v"][j], dec["log_alpha"][j], dec["beta"][j], state, o=o)
+    torch.cuda.synchronize()
+    ev = Events(hip, 2)
+    ev.record(0, stream)
+    for s in range(steps):
+        j = s % n_in
+        kda.decode_step(dec["q"][j], dec["k"][j], dec["v"][j], dec["log_alpha"][j], dec["beta"][j], state, o=o)
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(0, 1) / steps
+    ev.close()
+    return ms
+
+
+def cpu_baseline(case):
+    """The oracle (fp64 token recurrence, OpenMP over (sequence, head, column
+    block)) on the host cores, on the same prefill-4k inputs copied to host."""
+    import oracle
+    host = [t.cpu() for t in (case.q, case.k, case.v, case.log_alpha, case.beta, case.initial_state)]
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
+    heads = list(range(case.H))
+    t0 = time.perf_counter()
+    oracle.recurrence(*host, None, heads=heads, want_o=True, col_blocks=2, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": case.T_total / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"prefill-4k in full: T={case.T_total}, H={case.H}, d={case.dk}, fp64, "
+                      f"{dt:.2f} s wall"}, host
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is a design in DESIGN.md, not built", file=sys.stderr)
+        return 2
+
+    import torch
+    import gated_delta_rule_41_amd as kda
+    import kda_inputs as ki
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 3
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hip = hip_runtime()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    case = ki.make_prefill("prefill-4k", dev)
+    TH = case.T_total * case.H
+    wall_ms, per, span_ms, o, fs = time_prefill(kda, case, args.steps, args.warmup, hip, stream)
+    tokens_per_s = case.T_total / (wall_ms * 1e-3)
+    flops = FLOP_PER_TOKEN_HEAD * TH
+    tflops = flops / (wall_ms * 1e-3) / 1e12
+    alg_bytes = ALG_BYTES_PER_TOKEN_HEAD * TH + 2 * case.N * case.H * case.dk * case.dv * 4
+    ai = flops / alg_bytes
+    ceiling = min(PEAK_BF16, ai * PEAK_HBM)
+
+    dom = max(per, key=per.get)
+    kb = KERNEL_BYTES_PER_TOKEN_HEAD[dom] * TH
+    if dom == "recur":
+        kb += 2 * case.N * case.H * case.dk * case.dv * 4
+    achieved = kb / (per[dom] * 1e-3) / 1e9
+    roof = {"kernel": KERNEL_SYMBOL[dom], "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4),
+            "traffic": traffic_from_profiles(dom, TH), "avg_launch_ms": round(per[dom], 5),
+            "alg_bytes_per_launch": kb}
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16/f32",
+        "data": "synthetic",
+        "config": {"workload": "prefill-4k", "B": 1, "T": case.T_total, "H": case.H, "dk": case.dk,
+                   "dv": case.dv, "chunk": 64, "inputs": "bf16", "state": "f32", "o": "f32",
+                   "log_alpha": "-softplus(N(0,1)+2)"},
+        "prefill": {"tflops": round(tflops, 2), "mfma_peak_frac": round(tflops * 1e12 / PEAK_BF16, 4),
+                    "alg_roofline_frac": round(flops / (wall_ms * 1e-3) / ceiling, 4),
+                    "alg_ceiling_tflops": round(ceiling / 1e12, 1),
+                    "kernel_ms": {k_: round(v_, 5) for k_, v_ in per.items()},
+                    "event_span_ms": round(span_ms, 5)},
+        "roofline": roof,
+    }
+
+    if not args.no_decode:
+        dec_inputs = min(args.decode_steps, 100)  # distinct per-step inputs, cycled
+        dec = ki.make_decode(256, 32, 128, dec_inputs, dev)
+        dms = time_decode(kda, dec, args.decode_steps, 10, hip, stream)
+        NH = 256 * 32
+        state_bytes = 2 * NH * 128 * 128 * 4
+        alg = state_bytes + NH * (4 * 128 * 2 + 2 + 128 * 4)
+        out["decode"] = {"workload": "decode-256", "steps": args.decode_steps,
+                         "ms_per_step": round(dms, 5), "state_GBps": round(state_bytes / dms / 1e6, 1),
+                         "alg_GBps": round(alg / dms / 1e6, 1),
+                         "hbm_frac": round(alg / dms / 1e6 / (PEAK_HBM / 1e9), 4),
+                         "roofline": {"kernel": "decode_kernel", "bound": "hbm",
+                                      "achieved": round(alg / dms / 1e6, 1), "peak": PEAK_HBM / 1e9,
+                                      "unit": "GB/s", "frac": round(alg / dms / 1e6 / (PEAK_HBM / 1e9), 4),
+                                      "traffic": traffic_from_profiles("decode", NH)}}
+        del dec
+
+    if not args.no_cpu_baseline:
+        import numpy as np
+        cb, host = cpu_baseline(case)
+        out["cpu_baseline"] = cb
+        # spot parity of this very run against the oracle (head 0, all tokens)
+        import oracle
+        o_ref, s_ref, _ = oracle.recurrence(*host, None, heads=[0], col_blocks=8)
+        oo = o[:, 0].double().cpu().numpy()
+        ss = fs[0, 0].double().cpu().numpy()
+        e_o = float(np.max(np.abs(oo - o_ref[:, 0])) / np.sqrt(np.mean(o_ref[:, 0] ** 2)))
+        e_s = float(np.max(np.abs(ss - s_ref[0, 0])) / np.sqrt(np.mean(s_ref[0, 0] ** 2)))
+        out["parity_head0"] = {"err_o": e_o, "err_state": e_s, "tol": 2e-2}
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

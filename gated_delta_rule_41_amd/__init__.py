@@ -60,6 +60,8 @@ def _load():
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, SZ, P]
+    lib.kda_chunk_fwd_timed.restype = ctypes.c_int
+    lib.kda_chunk_fwd_timed.argtypes = lib.kda_chunk_fwd.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
@@ -111,13 +113,16 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
               cu_seqlens: Optional[torch.Tensor] = None, *, out_dtype: torch.dtype = torch.float32,
               want_final_state: bool = True, o: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              workspace: Optional[torch.Tensor] = None,
+              events=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA prefill over a packed batch (see ``kda_chunk_fwd`` in include/kda.h).
 
     q, k, log_alpha [T, H, dk]; v [T, H, dv]; beta [T, H]; initial_state
     [N, H, dk, dv] fp32 or None; cu_seqlens [N+1] int32 on the device or None.
     Returns (o [T, H, dv] out_dtype, final_state [N, H, dk, dv] fp32 or None).
     ``final_state`` may be passed as ``initial_state`` for an in-place carry.
+    ``events``: optional sequence of 4 raw hipEvent_t handles (ints or None),
+    recorded at the stage boundaries (see ``kda_chunk_fwd_timed``).
     """
     lib = _load()
     dev = q.device
@@ -152,9 +157,14 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     ws_bytes = int(sz.value)  # 0 when the shape is invalid; kda_chunk_fwd then reports why
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
-                           _ptr(cu_seqlens), N, T, H, dk, dv, in_dt, gate_dt, out_dt, _ptr(o),
-                           _ptr(final_state), _ptr(workspace), workspace.numel(), _stream(dev))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+            _ptr(cu_seqlens), N, T, H, dk, dv, in_dt, gate_dt, out_dt, _ptr(o),
+            _ptr(final_state), _ptr(workspace), workspace.numel(), _stream(dev))
+    if events is None:
+        st = lib.kda_chunk_fwd(*args)
+    else:
+        ev = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) if e else None for e in events])
+        st = lib.kda_chunk_fwd_timed(*args, ev)
     if st != 0:
         raise KDAError(st, "kda_chunk_fwd")
     return o, final_state

@@ -85,6 +85,7 @@ using namespace kda;
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned_to(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     if (!a || !b || na == 0 || nb == 0) return false;
@@ -133,13 +134,25 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype gate_dtype,
                          kda_dtype out_dtype, void* o, float* final_state, void* workspace,
                          size_t workspace_bytes, void* stream) {
+    return kda_chunk_fwd_timed(q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, T_total, H, dk, dv,
+                               in_dtype, gate_dtype, out_dtype, o, final_state, workspace, workspace_bytes,
+                               stream, nullptr);
+}
+
+kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* log_alpha,
+                               const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                               int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
+                               kda_dtype in_dtype, kda_dtype gate_dtype, kda_dtype out_dtype, void* o,
+                               float* final_state, void* workspace, size_t workspace_bytes, void* stream,
+                               void* const* events) {
     if (N <= 0 || H <= 0 || T_total < 0 || T_total >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     if (T_total > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
     if (!cu_seqlens && N != 1) return KDA_ERR_SHAPE;
     if (!head_ok(dk, dv) || !dtype_ok(in_dtype) || !dtype_ok(gate_dtype) || !dtype_ok(out_dtype))
         return KDA_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(beta) ||
-        !aligned16(o) || !aligned16(initial_state) || !aligned16(final_state) || !aligned16(cu_seqlens))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(o) ||
+        !aligned16(initial_state) || !aligned16(final_state) || !aligned_to(beta, esize(gate_dtype)) ||
+        !aligned_to(cu_seqlens, 4))
         return KDA_ERR_ALIGN;
     const size_t T = (size_t)T_total;
     const size_t nqk = T * H * dk * esize(in_dtype), nv = T * H * dv * esize(in_dtype);
@@ -196,9 +209,16 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
     a.h = w + plan.off[6];
     a.vn = w + plan.off[7];
     hipStream_t st = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) {
+        return !events || !events[i] || hipEventRecord(static_cast<hipEvent_t>(events[i]), st) == hipSuccess;
+    };
+    if (!mark(0)) return KDA_ERR_HIP;
     if (NC > 0 && launch_prep(a, st) != hipSuccess) return KDA_ERR_HIP;
+    if (!mark(1)) return KDA_ERR_HIP;
     if (launch_recur(a, st) != hipSuccess) return KDA_ERR_HIP;
+    if (!mark(2)) return KDA_ERR_HIP;
     if (NC > 0 && launch_output(a, st) != hipSuccess) return KDA_ERR_HIP;
+    if (!mark(3)) return KDA_ERR_HIP;
     return KDA_OK;
 }
 
@@ -209,8 +229,8 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
     if (N <= 0 || H <= 0 || (int64_t)N * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     if (!head_ok(dk, dv) || !dtype_ok(in_dtype) || !dtype_ok(gate_dtype) || !dtype_ok(out_dtype))
         return KDA_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(beta) ||
-        !aligned16(state) || !aligned16(o))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(state) ||
+        !aligned16(o) || !aligned_to(beta, esize(gate_dtype)))
         return KDA_ERR_ALIGN;
     const size_t NH = (size_t)N * H;
     const size_t no = NH * dv * esize(out_dtype), ns = NH * dk * dv * 4;

@@ -63,27 +63,40 @@ __device__ __forceinline__ int split_pos(int r) {
 
 __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
 
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32
+
+// LDS plan (bytes). Row strides are padded so that the matrix-core operand
+// reads (one 16-byte vector per lane, lanes = 16 rows x 4 k-groups) and the
+// transposing writes spread over the banks.
 template <int D, bool F32>
 struct PrepSmem {
     using E = typename Pol<F32>::E;
     using AE = typename APol<F32>::E;
-    static constexpr int KT_PLANE = 64 * D;                              // elements per Kt plane
-    static constexpr int R1 = APol<F32>::PLANES * 64 * D * (int)sizeof(AE);  // Kt, later -W / slow-path scan
-    static constexpr int R4a = D * 64 * (int)sizeof(E);                 // K-^T staging
-    static constexpr int R4b = 64 * 64 * 4 + 64 * 64 * (int)sizeof(E) + 4 * 256 * 4;  // Akk, Aqk, T_II
+    static constexpr int KT_STRIDE = D + 8;                  // Kt row (elements)
+    static constexpr int KT_PLANE = 64 * KT_STRIDE;          // elements per hi / lo plane
+    static constexpr int KM_STRIDE = 64 + 4;                 // K-^T staging row (elements)
+    static constexpr int BK_STRIDE = 64 + 4;                 // beta K+ transposed row (elements)
+    static constexpr int AK_STRIDE = 20;                     // A_kk / T_II block row (floats)
+    static constexpr int AK_BLOCK = 16 * AK_STRIDE;          // floats per 16 x 16 block
+    static constexpr int R1 = APol<F32>::PLANES * KT_PLANE * (int)sizeof(AE);  // Kt; later -W, slow-path scans
+    static constexpr int R4a = D * KM_STRIDE * (int)sizeof(E);                // K-^T staging
+    static constexpr int R4b = 10 * AK_BLOCK * 4;                             // A_kk lower blocks
     static constexpr int R4 = R4a > R4b ? R4a : R4b;
-    static constexpr int R3 = 64 * D * (int)sizeof(E);                   // beta K+
-    static_assert(64 * D * 4 <= R1, "slow-path scan must fit in R1");
+    static constexpr int R3 = D * BK_STRIDE * (int)sizeof(E);                 // beta K+, transposed
+    static constexpr int CONST = 22 * D * 4;                                  // tot xf eA eL cIJ; later T_II
+    static constexpr int BETA = 64 * 4;
+    static constexpr int BYTES = R1 + R4 + R3 + CONST + BETA;
+    static_assert(64 * D * 4 <= R1, "slow-path scans must fit in R1");
     static_assert(64 * D * (int)sizeof(E) <= R1, "-W staging must fit in R1");
-    static constexpr int CONST = 22 * D * 4 + 64 * 4;  // tot xf eA eL cIJ, beta
-    static constexpr int BYTES = R1 + R4 + R3 + CONST;
+    static_assert(4 * AK_BLOCK * 4 <= CONST, "T_II must fit in the constants area");
 };
 
 template <int D, typename TIn, typename TG, bool F32>
-__global__ __launch_bounds__(256) void prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
-                                                   const TIn* __restrict__ v, const TG* __restrict__ la,
-                                                   const TG* __restrict__ beta, const int32_t* __restrict__ cu,
-                                                   int N, int T, int H, Ws<typename Pol<F32>::E> ws) {
+__global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                                      const TIn* __restrict__ v, const TG* __restrict__ la,
+                                                      const TG* __restrict__ beta,
+                                                      const int32_t* __restrict__ cu, int N, int T, int H,
+                                                      Ws<typename Pol<F32>::E> ws) {
     using P = Pol<F32>;
     using E = typename P::E;
     using Frag = typename P::Frag;
@@ -93,25 +106,26 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn* __restrict__ q, co
     using SM = PrepSmem<D, F32>;
     constexpr int NS = D / 32;    // 32-deep slices over a head dimension
     constexpr int NCT = D / 16;   // 16-wide column tiles over a head dimension
-    constexpr int PL = SM::KT_PLANE;
+    constexpr int TPW = NCT / 2;  // WY column tiles per wave (W tiles on waves 0-1, U tiles on 2-3)
+    constexpr int KTS = SM::KT_STRIDE, KMS = SM::KM_STRIDE, BKS = SM::BK_STRIDE, AKS = SM::AK_STRIDE;
+    constexpr int AKB = SM::AK_BLOCK;
 
     extern __shared__ __align__(16) char smem[];
-    AE* Kt_s = reinterpret_cast<AE*>(smem);                     // [planes][64][NS][4][8]
-    E* Ws_s = reinterpret_cast<E*>(smem);                       // [64][NS][4][8] (-W), after Kt is dead
+    AE* Kt_s = reinterpret_cast<AE*>(smem);                     // [planes][64][KTS] keys 2^(G_aJ - G)
+    E* Ws_s = reinterpret_cast<E*>(smem);                       // [64][NS][4][8] -W (after Kt is dead)
     float* xl_slow = reinterpret_cast<float*>(smem);            // [64][D] slow path: local scans
     char* r4 = smem + SM::R1;
-    E* Km_s = reinterpret_cast<E*>(r4);                         // [D][2][4][8]
-    float* Akk_s = reinterpret_cast<float*>(r4);                // [64][64]
-    E* Aqk_s = reinterpret_cast<E*>(r4 + 64 * 64 * 4);          // [64][64]
-    float* Td_s = reinterpret_cast<float*>(r4 + 64 * 64 * 4 + 64 * 64 * sizeof(E));  // [4][16][16]
-    E* Bk_s = reinterpret_cast<E*>(smem + SM::R1 + SM::R4);     // [64][D]
+    E* Km_s = reinterpret_cast<E*>(r4);                         // [D][KMS] K-^T in split row order
+    float* Akk_s = reinterpret_cast<float*>(r4);                // 10 blocks [16][AKS]: diag I at I, (I,J) at 4+pair
+    E* Bk_t = reinterpret_cast<E*>(smem + SM::R1 + SM::R4);     // [D][BKS] beta K+ transposed
     float* cst = reinterpret_cast<float*>(smem + SM::R1 + SM::R4 + SM::R3);
     float* tot = cst;                 // [4][D]  sum of the block's log2 gates
     float* xf = tot + 4 * D;          // [4][D]  log2 gate of the block's first row
     float* eA = xf + 4 * D;           // [4][D]  2^G(first row of I)
     float* eL = eA + 4 * D;           // [4][D]  2^(G_last - G(first row of I))
     float* cIJ = eL + 4 * D;          // [6][D]  2^(G(first row of I) - G(first row of J)), I > J
-    float* beta_s = cIJ + 6 * D;      // [64]
+    float* Td_s = cst;                // [4][16][AKS] T_II, after the constants are dead
+    float* beta_s = cst + 22 * D;     // [64]
 
     const int gc = blockIdx.x;
     const int h = blockIdx.y;
@@ -126,22 +140,34 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn* __restrict__ q, co
     const bool valid = r < L;
     const int64_t rowoff = ((int64_t)(t0 + r) * H + h) * D;
 
-    // ---- 1. log2 gate, scanned inside each 16-row block (per key channel)
-    float xl[NS][8];
+    // ---- 0. all row inputs of this lane: log alpha, q, k (channels 32 s + split(g, j))
+    float xl[NS][8], q8[NS][8], k8[NS][8];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         float a4[4] = {0.f, 0.f, 0.f, 0.f}, b4[4] = {0.f, 0.f, 0.f, 0.f};
+        float c4[4] = {0.f, 0.f, 0.f, 0.f}, d4[4] = {0.f, 0.f, 0.f, 0.f};
+        float e4[4] = {0.f, 0.f, 0.f, 0.f}, f4[4] = {0.f, 0.f, 0.f, 0.f};
         if (valid) {
             ld_in4(la, rowoff + 32 * s + 4 * g, a4);
             ld_in4(la, rowoff + 32 * s + 16 + 4 * g, b4);
+            ld_in4(q, rowoff + 32 * s + 4 * g, c4);
+            ld_in4(q, rowoff + 32 * s + 16 + 4 * g, d4);
+            ld_in4(k, rowoff + 32 * s + 4 * g, e4);
+            ld_in4(k, rowoff + 32 * s + 16 + 4 * g, f4);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             xl[s][j] = a4[j] * LOG2E;
             xl[s][4 + j] = b4[j] * LOG2E;
+            q8[s][j] = c4[j];
+            q8[s][4 + j] = d4[j];
+            k8[s][j] = e4[j];
+            k8[s][4 + j] = f4[j];
         }
     }
-    // inclusive scan across the 16 rows of this wave (lanes n of one DPP row)
+    if (g == 0) beta_s[r] = valid ? ld_in(beta, (int64_t)(t0 + r) * H + h) : 0.f;
+
+    // ---- 1. log2 gate scanned inside each 16-row block (lanes n of one DPP row)
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) {
 #pragma unroll
@@ -152,11 +178,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn* __restrict__ q, co
     if (n == 0 || n == 15) {
         float* dst = (n == 0 ? xf : tot) + w * D;
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) dst[32 * s + kslot(g, j)] = xl[s][j];
+        for (int s = 0; s < NS; ++s) {
+            *reinterpret_cast<f32x4_t*>(dst + 32 * s + 4 * g) = f32x4_t{xl[s][0], xl[s][1], xl[s][2], xl[s][3]};
+            *reinterpret_cast<f32x4_t*>(dst + 32 * s + 16 + 4 * g) =
+                f32x4_t{xl[s][4], xl[s][5], xl[s][6], xl[s][7]};
+        }
     }
-    if (g == 0) beta_s[r] = valid ? ld_in(beta, (int64_t)(t0 + r) * H + h) : 0.f;
     __syncthreads();
 
     // ---- 2. per-block channel constants from block sums, and the overflow guard
@@ -171,21 +198,21 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn* __restrict__ q, co
         if (ty < 4) {  // 2^G(a_I) = 2^(sum_{J<I} tot_J + xf_I)
             float e = ff[ty];
             for (int J = 0; J < ty; ++J) e += tt[J];
-            eA[ty * D + c] = exp2f(e);
+            eA[ty * D + c] = ex2(e);
         } else if (ty < 8) {  // 2^(G_last - G(a_I)) = 2^((tot_I - xf_I) + sum_{J>I} tot_J)
             const int I = ty - 4;
             float e = tt[I] - ff[I];
             for (int J = I + 1; J < 4; ++J) e += tt[J];
-            eL[I * D + c] = exp2f(e);
+            eL[I * D + c] = ex2(e);
         } else if (ty < 14) {  // 2^((tot_J - xf_J) + sum_{J<K<I} tot_K + xf_I)
             const int p = ty - 8;
             const int I = p < 1 ? 1 : (p < 3 ? 2 : 3);
             const int J = p - pair_index(I, 0);
             float e = tt[J] - ff[J] + ff[I];
             for (int K = J + 1; K < I; ++K) e += tt[K];
-            cIJ[p * D + c] = exp2f(e);
+            cIJ[p * D + c] = ex2(e);
         } else {
-            ws.gam[chh * D + c] = exp2f(tt[0] + tt[1] + tt[2] + tt[3]);
+            ws.gam[chh * D + c] = ex2(tt[0] + tt[1] + tt[2] + tt[3]);
         }
     }
     int bad = 0;
@@ -200,43 +227,39 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn* __restrict__ q, co
     float qs[NS][8], ks[NS][8];  // q 2^(G - G_aw), k 2^(G - G_aw)  (fast path)
     E* qp_out = ws.qp + chh * 64 * D;
     E* km_out = ws.km + chh * D * 64;
+    const int kmpos = 32 * (r >> 5) + split_pos(r);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        float q8[8], k8[8];
-        {
-            float a4[4] = {0.f, 0.f, 0.f, 0.f}, b4[4] = {0.f, 0.f, 0.f, 0.f};
-            float c4[4] = {0.f, 0.f, 0.f, 0.f}, d4[4] = {0.f, 0.f, 0.f, 0.f};
-            if (valid) {
-                ld_in4(q, rowoff + 32 * s + 4 * g, a4);
-                ld_in4(q, rowoff + 32 * s + 16 + 4 * g, b4);
-                ld_in4(k, rowoff + 32 * s + 4 * g, c4);
-                ld_in4(k, rowoff + 32 * s + 16 + 4 * g, d4);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                q8[j] = a4[j];
-                q8[4 + j] = b4[j];
-                k8[j] = c4[j];
-                k8[4 + j] = d4[j];
-            }
-        }
-        float qpv[8], ktv[8];
+        float qpv[8];
         if (!slow) {
+            float xf8[8], ea8[8], el8[8], ktv[8];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int c0 = 32 * s + 16 * hf + 4 * g;
+                const f32x4_t a = *reinterpret_cast<const f32x4_t*>(xf + w * D + c0);
+                const f32x4_t b = *reinterpret_cast<const f32x4_t*>(eA + w * D + c0);
+                const f32x4_t c = *reinterpret_cast<const f32x4_t*>(eL + w * D + c0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    xf8[4 * hf + j] = a[j];
+                    ea8[4 * hf + j] = b[j];
+                    el8[4 * hf + j] = c[j];
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int c = 32 * s + kslot(g, j);
-                const float dA = xl[s][j] - xf[w * D + c];  // G_r - G_aw, local sums only
-                const float e = exp2f(dA);
-                const float ei = exp2f(-dA);
-                const float ea = eA[w * D + c];
-                qs[s][j] = q8[j] * e;
-                ks[s][j] = k8[j] * e;
-                ktv[j] = k8[j] * ei;
-                qpv[j] = qs[s][j] * ea;
-                Km_s[c * 64 + 32 * (r >> 5) + split_pos(r)] = P::from_f(ktv[j] * eL[w * D + c]);
-                Bk_s[r * D + c] = P::from_f(ks[s][j] * ea * br);
+                const float dA = xl[s][j] - xf8[j];  // G_r - G_aw, local sums only
+                const float e = ex2(dA);
+                const float ei = ex2(-dA);
+                qs[s][j] = q8[s][j] * e;
+                ks[s][j] = k8[s][j] * e;
+                ktv[j] = k8[s][j] * ei;
+                qpv[j] = qs[s][j] * ea8[j];
+                Km_s[c * KMS + kmpos] = P::from_f(ktv[j] * el8[j]);
+                Bk_t[c * BKS + r] = P::from_f(ks[s][j] * ea8[j] * br);
             }
-            AP::store(Kt_s + (r * NS + s) * 32 + g * 8, PL, AP::make(ktv));
+            AP::store(Kt_s + r * KTS + s * 32 + g * 8, SM::KT_PLANE, AP::make(ktv));
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -245,9 +268,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn* __restrict__ q, co
                 for (int J = 0; J < w; ++J) pre += tot[J * D + c];
                 for (int J = w + 1; J < 4; ++J) post += tot[J * D + c];
                 const float eg = exp2f(pre + xl[s][j]);  // 2^G_r
-                qpv[j] = q8[j] * eg;
-                km_out[c * 64 + 32 * (r >> 5) + split_pos(r)] = P::from_f(k8[j] * exp2f(post));
-                Bk_s[r * D + c] = P::from_f(k8[j] * eg * br);
+                qpv[j] = q8[s][j] * eg;
+                km_out[c * 64 + kmpos] = P::from_f(k8[s][j] * exp2f(post));
+                Bk_t[c * BKS + r] = P::from_f(k8[s][j] * eg * br);
                 xl_slow[r * D + c] = xl[s][j];
                 qs[s][j] = 0.f;
                 ks[s][j] = 0.f;
@@ -260,9 +283,15 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn* __restrict__ q, co
     // ---- 3b. K-^T to the workspace (fast path) / exact gated products (slow path)
     float akk_sl[16], aqk_sl[16];
     if (!slow) {
-        constexpr int VEC = 16 / sizeof(E);
-        for (int idx = tid; idx < D * 64 / VEC; idx += 256)
-            reinterpret_cast<u32x4_t*>(km_out)[idx] = reinterpret_cast<const u32x4_t*>(Km_s)[idx];
+        for (int idx = tid; idx < D * 16; idx += 256) {  // 4 elements per item
+            const int c = idx >> 4, qd = idx & 15;
+            const E* src = Km_s + c * KMS + 4 * qd;
+            E* dst = km_out + c * 64 + 4 * qd;
+            if constexpr (F32)
+                *reinterpret_cast<f32x4_t*>(dst) = *reinterpret_cast<const f32x4_t*>(src);
+            else
+                *reinterpret_cast<u32x2_t*>(dst) = *reinterpret_cast<const u32x2_t*>(src);
+        }
     } else {
         // pair (rr, ii) = (p >> 6, p & 63), p = tid + 256 m; exponent
         // G_rr - G_ii = xl_rr - xl_ii + sum of the whole-block totals between them
@@ -289,54 +318,87 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn* __restrict__ q, co
     }
     __syncthreads();
 
-    // ---- 3c. A_qk and A_kk
+    // values of the U tiles (waves 2-3), in accumulator layout, fetched early
+    float vv[TPW][4][4];
+    if (w >= 2) {
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 16 * I + 4 * g + i;
+                    const int ct = (w - 2) * TPW + tt;
+                    vv[tt][I][i] = rr < L ? ld_in(v, ((int64_t)(t0 + rr) * H + h) * D + 16 * ct + n) : 0.f;
+                }
+    }
+
+    // ---- 3c. A_qk (straight to the workspace) and A_kk (LDS, lower blocks only)
+    E* aqk_out = ws.aqk + chh * 64 * 64;
+    auto aqk_put = [&](int rr, int cc, float x) {
+        const int s2 = cc >> 5, c2 = cc & 31;
+        aqk_out[(rr * 2 + s2) * 32 + 8 * ((c2 & 15) >> 2) + 4 * (c2 >> 4) + (c2 & 3)] = P::from_f(x);
+    };
     if (!slow) {
         const int I = w;
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             if (J > I) {
-                // upper blocks are zero
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = 16 * I + 4 * g + i, cc = 16 * J + n;
-                    Akk_s[rr * 64 + cc] = 0.f;
-                    Aqk_s[rr * 64 + cc] = P::from_f(0.f);
-                }
+                for (int i = 0; i < 4; ++i) aqk_put(16 * I + 4 * g + i, 16 * J + n, 0.f);
                 continue;
             }
             f32x4_t aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 float xq[8], xk[8];
+                if (J < I) {
+                    const float* cp = cIJ + pair_index(I, J) * D + 32 * s + 4 * g;
+                    const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(cp);
+                    const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(cp + 16);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float cf = (J < I) ? cIJ[pair_index(I, J) * D + 32 * s + kslot(g, j)] : 1.f;
-                    xq[j] = qs[s][j] * cf;
-                    xk[j] = ks[s][j] * cf;
+                    for (int j = 0; j < 4; ++j) {
+                        xq[j] = qs[s][j] * c0[j];
+                        xk[j] = ks[s][j] * c0[j];
+                        xq[4 + j] = qs[s][4 + j] * c1[j];
+                        xk[4 + j] = ks[s][4 + j] * c1[j];
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        xq[j] = qs[s][j];
+                        xk[j] = ks[s][j];
+                    }
                 }
-                const AFrag b = AP::load(Kt_s + ((16 * J + n) * NS + s) * 32 + g * 8, PL);
+                const AFrag b = AP::load(Kt_s + (16 * J + n) * KTS + s * 32 + g * 8, SM::KT_PLANE);
                 AP::mma(aq, AP::make(xq), b);
                 AP::mma(ak, AP::make(xk), b);
             }
+            const int blk = (J == I) ? I : 4 + pair_index(I, J);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int rr = 16 * I + 4 * g + i, cc = 16 * J + n;
-                const bool lo_incl = (J < I) || (n <= 4 * g + i);
-                const bool lo_strict = (J < I) || (n < 4 * g + i);
-                Aqk_s[rr * 64 + cc] = P::from_f(lo_incl ? aq[i] : 0.f);
-                Akk_s[rr * 64 + cc] = lo_strict ? ak[i] * beta_s[rr] : 0.f;
+                const int rl = 4 * g + i;  // row inside the block
+                const bool lo_incl = (J < I) || (n <= rl);
+                const bool lo_strict = (J < I) || (n < rl);
+                aqk_put(16 * I + rl, 16 * J + n, lo_incl ? aq[i] : 0.f);
+                Akk_s[blk * AKB + rl * AKS + n] = lo_strict ? ak[i] * beta_s[16 * I + rl] : 0.f;
             }
         }
     } else {
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             const int p = tid + 256 * m;
-            Akk_s[p] = akk_sl[m];
-            Aqk_s[p] = P::from_f(aqk_sl[m]);
+            const int rr = p >> 6, ii = p & 63, I = rr >> 4, J = ii >> 4;
+            aqk_put(rr, ii, aqk_sl[m]);
+            if (J <= I) {
+                const int blk = (J == I) ? I : 4 + pair_index(I, J);
+                Akk_s[blk * AKB + (rr & 15) * AKS + (ii & 15)] = akk_sl[m];
+            }
         }
     }
     __syncthreads();
-    // ---- 4a. diagonal-block inverses T_II = (I + A_II)^-1 (wave 0); A_qk out (waves 1-3)
+
+    // ---- 4a. diagonal-block inverses T_II = (I + A_II)^-1 by row forward substitution (wave 0)
     if (w == 0) {
         const int b = l >> 4, j = l & 15;
         float acc[16];
@@ -346,67 +408,79 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn* __restrict__ q, co
         for (int i = 0; i < 16; ++i) {
             const float ti = acc[i];
 #pragma unroll
-            for (int rr = i + 1; rr < 16; ++rr) acc[rr] -= Akk_s[(16 * b + rr) * 64 + 16 * b + i] * ti;
+            for (int rr = i + 1; rr < 16; ++rr) acc[rr] -= Akk_s[b * AKB + rr * AKS + i] * ti;
         }
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) Td_s[(b * 16 + rr) * 16 + j] = acc[rr];
-    } else {
-        E* aqk_out = ws.aqk + chh * 64 * 64;
-        for (int idx = tid - 64; idx < 64 * 2 * 4; idx += 192) {
-            const int rr = idx >> 3, s = (idx >> 2) & 1, gg = idx & 3;
-            float x[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] = P::to_f(Aqk_s[rr * 64 + 32 * s + kslot(gg, j)]);
-            P::store(aqk_out + ((rr * 2 + s) * 4 + gg) * 8, P::make(x));
-        }
+        for (int rr = 0; rr < 16; ++rr) Td_s[b * AKB + rr * AKS + j] = acc[rr];
     }
     __syncthreads();
 
     // ---- 4b. WY factors by blocked forward substitution: X = (I + A_kk)^-1 [beta K+ | beta V]
     {
-        constexpr int TPW = NCT / 2;  // column tiles per wave (2 NCT tiles over 4 waves)
+        const bool isW = w < 2;
         E* u_out = ws.u + chh * 64 * D;
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t X[TPW][4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            // operands shared by every column tile of this wave
+            Frag aoff[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                if (2 * s >= I) break;
+                float xa[8];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int K = 2 * s + hf;
+                    if (K < I) {
+                        const f32x4_t a =
+                            *reinterpret_cast<const f32x4_t*>(Akk_s + (4 + pair_index(I, K)) * AKB + n * AKS + 4 * g);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) xa[4 * hf + j] = -a[j];
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) xa[4 * hf + j] = 0.f;
+                    }
+                }
+                aoff[s] = P::make(xa);
+            }
+            Frag at;
+            {
+                const f32x4_t a = *reinterpret_cast<const f32x4_t*>(Td_s + I * AKB + n * AKS + 4 * g);
+                float ta[8] = {a[0], a[1], a[2], a[3], 0.f, 0.f, 0.f, 0.f};
+                at = P::make(ta);
+            }
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                const int ct = (w & 1) * TPW + tt;  // column tile inside W (waves 0-1) or U (waves 2-3)
+                f32x4_t Y;
+                if (isW) {
+                    float b4[4];
+                    if constexpr (F32) {
+                        const f32x4_t bb = *reinterpret_cast<const f32x4_t*>(Bk_t + (16 * ct + n) * BKS + 16 * I + 4 * g);
+                        b4[0] = bb[0]; b4[1] = bb[1]; b4[2] = bb[2]; b4[3] = bb[3];
+                    } else {
+                        const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(Bk_t + (16 * ct + n) * BKS + 16 * I + 4 * g);
+                        b4[0] = h2f(bb[0] & 0xffffu); b4[1] = h2f(bb[0] >> 16);
+                        b4[2] = h2f(bb[1] & 0xffffu); b4[3] = h2f(bb[1] >> 16);
+                    }
+                    Y = f32x4_t{b4[0], b4[1], b4[2], b4[3]};
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Y[i] = beta_s[16 * I + 4 * g + i] * vv[tt][I][i];
+                }
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (2 * s >= I) break;
+                    P::mma(Y, aoff[s], frag_from_acc<F32>(X[tt][2 * s], (2 * s + 1 < I) ? X[tt][2 * s + 1] : zero));
+                }
+                X[tt][I] = zero;
+                P::mma(X[tt][I], at, frag_from_acc<F32>(Y, zero));
+            }
+        }
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
-            const int ctg = w * TPW + tt;           // 0 .. 2 NCT - 1
-            const bool isW = ctg < NCT;
-            const int ct = isW ? ctg : ctg - NCT;   // column tile inside W or U
-            f32x4_t X[4];
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                f32x4_t Y;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = 16 * I + 4 * g + i;
-                    if (isW) {
-                        Y[i] = P::to_f(Bk_s[rr * D + 16 * ct + n]);
-                    } else {
-                        Y[i] = rr < L ? beta_s[rr] * ld_in(v, ((int64_t)(t0 + rr) * H + h) * D + 16 * ct + n)
-                                      : 0.f;
-                    }
-                }
-                if (I > 0) {
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        if (2 * s >= I) break;
-                        float xa[8];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const int col = 32 * s + kslot(g, j);
-                            xa[j] = (col < 16 * I) ? -Akk_s[(16 * I + n) * 64 + col] : 0.f;
-                        }
-                        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-                        const Frag bx = frag_from_acc<F32>(X[2 * s], (2 * s + 1 < I) ? X[2 * s + 1] : zero);
-                        P::mma(Y, P::make(xa), bx);
-                    }
-                }
-                float ta[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) ta[j] = (j < 4) ? Td_s[(I * 16 + n) * 16 + 4 * g + j] : 0.f;
-                const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-                X[I] = zero;
-                P::mma(X[I], P::make(ta), frag_from_acc<F32>(Y, zero));
-            }
+            const int ct = (w & 1) * TPW + tt;
             if (isW) {
                 // -W into LDS in the split k order over key channels
 #pragma unroll
@@ -415,14 +489,20 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn* __restrict__ q, co
                     for (int i = 0; i < 4; ++i) {
                         const int rr = 16 * I + 4 * g + i;
                         const int s = ct >> 1, gg = n >> 2, jj = 4 * (ct & 1) + (n & 3);
-                        Ws_s[(rr * NS + s) * 32 + gg * 8 + jj] = P::from_f(-X[I][i]);
+                        Ws_s[(rr * NS + s) * 32 + gg * 8 + jj] = P::from_f(-X[tt][I][i]);
                     }
             } else {
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     E* dst = u_out + ((ct * 4 + I) * 64 + l) * 4;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dst[i] = P::from_f(X[I][i]);
+                    if constexpr (F32) {
+                        *reinterpret_cast<f32x4_t*>(dst) = X[tt][I];
+                    } else {
+                        u32x2_t pk;
+                        pk[0] = (uint32_t)f2h(X[tt][I][0]) | ((uint32_t)f2h(X[tt][I][1]) << 16);
+                        pk[1] = (uint32_t)f2h(X[tt][I][2]) | ((uint32_t)f2h(X[tt][I][3]) << 16);
+                        *reinterpret_cast<u32x2_t*>(dst) = pk;
+                    }
                 }
             }
         }

@@ -8,17 +8,27 @@
 //     S    <- Diag(gamma) S + K-^T V_new         (gamma = exp(g_last) per key channel)
 //
 // Columns of S are independent (each product above touches value column j
-// only through column j), so one wave owns a 16-wide value-column slab of one
-// (sequence, head) and keeps its dk x 16 fp32 slab of S in accumulator
-// registers for the whole sequence: nothing but the per-chunk factors moves.
-// Thanks to the split k order (kda_common.h) the accumulator tiles of S and of
-// V_new are directly the B operands of the next product: no LDS round trip and
-// no cross-lane shuffle on the dependency chain. The per-chunk factors for
-// chunk n+1 are loaded while chunk n computes.
+// only through column j), so one workgroup owns a 16-wide value-column slab of
+// one (sequence, head). Its compute wave keeps the dk x 16 fp32 slab of S in
+// accumulator registers for the whole sequence. Thanks to the split k order
+// (kda_common.h) the accumulator tiles of S and of V_new are directly the B
+// operands of the next product: no LDS round trip and no cross-lane shuffle on
+// the dependency chain.
+//
+// Feeding the chain: two producer waves stream each chunk's factors (-W, K-^T,
+// this slab's U, gamma) into a ring of LDS slots with direct global->LDS loads,
+// RING - 1 chunks ahead of the compute wave. A wave's vector-memory queue
+// returns in order, so keeping these loads off the compute wave means its
+// chain never waits behind a memory round trip; producers wait for their own
+// loads with an explicit vmcnt and hand slots over at one barrier per chunk.
+// Inside a slot, 16-byte granules (one fp16 operand fragment each) are
+// XOR-swizzled within each 256-byte segment (granule c stored at
+// c ^ ((c >> 4) & 15)) so that the compute wave's operand reads (16 rows x 4
+// k-groups per instruction) hit distinct banks.
 //
 // Workgroup -> work mapping is XCD-aware: workgroups are dispatched round-robin
-// over the 8 XCDs, so the dv/16 slabs of one (sequence, head) are given ids that
-// are congruent mod 8 and land on the same XCD, where they share the L2 copy of
+// over the 8 XCDs, so the dv/16 slabs of one (sequence, head) get ids that are
+// congruent mod 8 and land on the same XCD, where they share the L2 copy of
 // that head's W and K- factors.
 #include "kda_common.h"
 #include "kda_launch.h"
@@ -26,49 +36,107 @@
 namespace kda {
 
 template <int D, bool F32>
-struct ChunkFactors {
-    using P = Pol<F32>;
-    using E = typename P::E;
-    using Frag = typename P::Frag;
-    static constexpr int NS = D / 32;
-    static constexpr int NT = D / 16;
-    Frag wn[4][NS];     // -W rows 16I + n, slice s
-    Frag km[NT][2];     // K-^T rows 16t + n, chunk-row slice s
-    E u[4][4];          // U rows 16I + 4g + i, this slab's column n
-    f32x4_t gam[NT];    // gamma for rows 16t + 4g + i
-
-    __device__ __forceinline__ void load(const Ws<E>& ws, int64_t chh, int ct, int l) {
-        const int n = l & 15, g = l >> 4;
-        const E* wp = ws.wn + chh * 64 * D;
-        const E* kp = ws.km + chh * D * 64;
-        const E* up = ws.u + chh * 64 * D + (int64_t)ct * 4 * 64 * 4;
-        const float* gp = ws.gam + chh * D;
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-            for (int s = 0; s < NS; ++s) wn[I][s] = P::load(wp + ((16 * I + n) * NS + s) * 32 + g * 8);
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) km[t][s] = P::load(kp + ((16 * t + n) * 2 + s) * 32 + g * 8);
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) u[I][i] = up[(I * 64 + l) * 4 + i];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) gam[t] = *reinterpret_cast<const f32x4_t*>(gp + 16 * t + 4 * g);
-    }
+struct RecurPlan {
+    using E = typename Pol<F32>::E;
+    static constexpr int FB = 64 * D * (int)sizeof(E);   // bytes of -W (and of K-^T) per chunk-head
+    static constexpr int UB = 64 * 16 * (int)sizeof(E);  // bytes of one slab's U
+    static constexpr int GB = D * 4;                     // bytes of gamma
+    static constexpr int GPAD = 1024;                    // gamma region rounded up to one whole load
+    static constexpr int SLOT = 2 * FB + UB + GPAD;      // one ring slot
+    static constexpr int RING = (4 * SLOT <= 150 * 1024) ? 4 : 2;
+    static constexpr int LDS = RING * SLOT;
+    // global->LDS loads per chunk and producer wave (16 bytes per lane, 1 KiB per load)
+    static constexpr int OPS_W = FB / 1024, OPS_U = UB / 1024, OPS_G = 1;
+    static constexpr int OPS0 = OPS_W + OPS_U;   // producer 0: -W and U
+    static constexpr int OPS1 = OPS_W + OPS_G;   // producer 1: K-^T and gamma
+    static constexpr int OPS = OPS0 > OPS1 ? OPS0 : OPS1;
+    static_assert((RING - 2) * OPS <= 63, "in-flight loads must fit the 6-bit vmcnt");
+    static_assert(FB % 1024 == 0 && UB % 1024 == 0 && GB <= GPAD, "slot parts are whole 1 KiB loads");
 };
 
+// granule swizzle of the ring slots; fp32 fragments span two granules, so the
+// fp32 path keeps the plain layout
+template <bool F32>
+__device__ __forceinline__ int swz(int c) {
+    if constexpr (F32) return c;
+    return c ^ ((c >> 4) & 15);
+}
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// wait until at most n of this wave's vector-memory operations are outstanding
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// wait until only the loads of the `after` chunks issued last are outstanding
+template <int OPS, int RING>
+__device__ __forceinline__ void wait_chunks(int after) {
+    if constexpr (RING >= 4) {
+        if (after >= 2) {
+            wait_vm<2 * OPS>();
+            return;
+        }
+    }
+    if constexpr (RING >= 3) {
+        if (after >= 1) {
+            wait_vm<OPS>();
+            return;
+        }
+    }
+    wait_vm<0>();
+}
+
+// Producer: issue the global->LDS loads of one chunk (this producer's half).
+// Both producers issue exactly OPS loads per chunk, so one vmcnt threshold
+// serves both.
 template <int D, bool F32>
-__global__ __launch_bounds__(64) void recur_kernel(const float* __restrict__ s0, float* __restrict__ s_final,
-                                                   const int32_t* __restrict__ cu, int N, int T, int H,
-                                                   Ws<typename Pol<F32>::E> ws) {
+__device__ __forceinline__ void produce(const Ws<typename Pol<F32>::E>& ws, int64_t chh, int ct, int pw, int l,
+                                       char* slot) {
+    using PL = RecurPlan<D, F32>;
+    if (pw == 0) {
+        const char* wp = reinterpret_cast<const char*>(ws.wn + chh * 64 * D);
+#pragma unroll
+        for (int j = 0; j < PL::OPS_W; ++j) dma16(wp + swz<F32>(64 * j + l) * 16, slot + j * 1024);
+        const char* up = reinterpret_cast<const char*>(ws.u + chh * 64 * D + (int64_t)ct * 4 * 64 * 4);
+#pragma unroll
+        for (int j = 0; j < PL::OPS_U; ++j) dma16(up + (64 * j + l) * 16, slot + 2 * PL::FB + j * 1024);
+        // pad to OPS loads: repeat the last U load (same source, same destination)
+#pragma unroll
+        for (int j = PL::OPS0; j < PL::OPS; ++j)
+            dma16(up + (64 * (PL::OPS_U - 1) + l) * 16, slot + 2 * PL::FB + (PL::OPS_U - 1) * 1024);
+    } else {
+        const char* kp = reinterpret_cast<const char*>(ws.km + chh * D * 64);
+#pragma unroll
+        for (int j = 0; j < PL::OPS_W; ++j) dma16(kp + swz<F32>(64 * j + l) * 16, slot + PL::FB + j * 1024);
+        // gamma: lanes past its end re-load its first granule into the unread tail of its region
+        const char* gp = reinterpret_cast<const char*>(ws.gam + chh * D) + (l * 16 < PL::GB ? l * 16 : 0);
+        dma16(gp, slot + 2 * PL::FB + PL::UB);
+        // pad to OPS loads: repeat the gamma load (same source, same destination)
+#pragma unroll
+        for (int j = PL::OPS1; j < PL::OPS; ++j) dma16(gp, slot + 2 * PL::FB + PL::UB);
+    }
+}
+
+template <int D, bool F32>
+__global__ __launch_bounds__(192) void recur_kernel(const float* __restrict__ s0, float* __restrict__ s_final,
+                                                    const int32_t* __restrict__ cu, int N, int T, int H,
+                                                    Ws<typename Pol<F32>::E> ws) {
     using P = Pol<F32>;
     using E = typename P::E;
     using Frag = typename P::Frag;
+    using PL = RecurPlan<D, F32>;
     constexpr int NS = D / 32;
     constexpr int NT = D / 16;  // row tiles over dk == column slabs over dv
+    constexpr int RING = PL::RING;
+    constexpr int OPS = PL::OPS;
+
+    extern __shared__ __align__(16) char ring[];
 
     // XCD-aware decode of the workgroup id
     const int b = blockIdx.x;
@@ -81,26 +149,50 @@ __global__ __launch_bounds__(64) void recur_kernel(const float* __restrict__ s0,
         unit = b / NT;
         ct = b % NT;
     }
-    if (unit >= NU) return;
+    if (unit >= NU) return;  // uniform over the workgroup
     const int seq = unit / H, h = unit % H;
-    const int l = threadIdx.x, n = l & 15, g = l >> 4;
+    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 15, g = l >> 4;
 
     int co, nch;
     seq_chunks(cu, T, seq, co, nch);
 
-    // state slab: rows 16t + 4g + i, column 16 ct + n
-    f32x4_t S[NT];
+    if (wv > 0) {
+        // ---------------- producers (waves 1 and 2)
+        const int pw = wv - 1;
+        const int pre = nch < RING - 1 ? nch : RING - 1;
+        for (int c = 0; c < pre; ++c) produce<D, F32>(ws, (int64_t)(co + c) * H + h, ct, pw, l, ring + c * PL::SLOT);
+        // chunk 0 has landed once at most the (pre - 1) later chunks are outstanding
+        wait_chunks<OPS, RING>(pre - 1);
+        __builtin_amdgcn_s_barrier();
+        for (int c = 0; c < nch; ++c) {
+            // slot (c + RING - 1) % RING was read by the compute wave in chunk c - 1,
+            // which it finished before the barrier that ended that chunk
+            const int nx = c + RING - 1;
+            if (nx < nch) produce<D, F32>(ws, (int64_t)(co + nx) * H + h, ct, pw, l, ring + (nx % RING) * PL::SLOT);
+            // chunk c + 1 has landed once only the chunks issued after it are outstanding
+            const int after = (nch - 1 < nx ? nch - 1 : nx) - (c + 1);
+            wait_chunks<OPS, RING>(after);
+            __builtin_amdgcn_s_barrier();
+        }
+        return;
+    }
+
+    // ---------------- compute wave
+    f32x4_t S[NT];  // state slab: rows 16t + 4g + i, column 16 ct + n
     const int64_t sbase = (int64_t)unit * D * D + 16 * ct + n;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[t][i] = s0 ? s0[sbase + (int64_t)(16 * t + 4 * g + i) * D] : 0.f;
 
-    ChunkFactors<D, F32> cur, nxt;
-    if (nch > 0) cur.load(ws, (int64_t)co * H + h, ct, l);
+    __builtin_amdgcn_s_barrier();
     for (int c = 0; c < nch; ++c) {
+        const char* slot = ring + (c % RING) * PL::SLOT;
+        const char* wsl = slot;
+        const char* ksl = slot + PL::FB;
+        const E* usl = reinterpret_cast<const E*>(slot + 2 * PL::FB);
+        const float* gsl = reinterpret_cast<const float*>(slot + 2 * PL::FB + PL::UB);
         const int64_t chh = (int64_t)(co + c) * H + h;
-        if (c + 1 < nch) nxt.load(ws, chh + H, ct, l);
 
         // h_n = S as B-operand fragments (also the operand of W S below)
         Frag sb[NS];
@@ -114,11 +206,20 @@ __global__ __launch_bounds__(64) void recur_kernel(const float* __restrict__ s0,
         f32x4_t V[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) V[I][i] = P::to_f(cur.u[I][i]);
-#pragma unroll
-            for (int s = 0; s < NS; ++s) P::mma(V[I], cur.wn[I][s], sb[s]);
+            if constexpr (F32) {
+                V[I] = *reinterpret_cast<const f32x4_t*>(usl + (I * 64 + l) * 4);
+            } else {
+                const u32x2_t u = *reinterpret_cast<const u32x2_t*>(usl + (I * 64 + l) * 4);
+                V[I] = f32x4_t{h2f(u[0] & 0xffffu), h2f(u[0] >> 16), h2f(u[1] & 0xffffu), h2f(u[1] >> 16)};
+            }
         }
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int gr = ((16 * I + n) * NS + s) * 4 + g;  // fragment of -W (row 16I+n, slice s, group g)
+                P::mma(V[I], P::load(reinterpret_cast<const E*>(wsl + swz<F32>(gr) * 8 * sizeof(E))), sb[s]);
+            }
         Frag vb[2];
         E* vp = ws.vn + chh * 64 * D + (int64_t)ct * 2 * 64 * 8;
 #pragma unroll
@@ -128,12 +229,15 @@ __global__ __launch_bounds__(64) void recur_kernel(const float* __restrict__ s0,
         }
         // S <- Diag(gamma) S + K-^T V_new
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            S[t] = cur.gam[t] * S[t];
+        for (int t = 0; t < NT; ++t) S[t] = *reinterpret_cast<const f32x4_t*>(gsl + 16 * t + 4 * g) * S[t];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) P::mma(S[t], cur.km[t][s], vb[s]);
-        }
-        if (c + 1 < nch) cur = nxt;
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int gr = ((16 * t + n) * 2 + s) * 4 + g;  // fragment of K-^T (row 16t+n, slice s, group g)
+                P::mma(S[t], P::load(reinterpret_cast<const E*>(ksl + swz<F32>(gr) * 8 * sizeof(E))), vb[s]);
+            }
+        __builtin_amdgcn_s_barrier();
     }
     if (s_final) {
 #pragma unroll
@@ -146,11 +250,15 @@ __global__ __launch_bounds__(64) void recur_kernel(const float* __restrict__ s0,
 template <int D, bool F32>
 static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     using E = typename Pol<F32>::E;
+    using PL = RecurPlan<D, F32>;
     Ws<E> ws{(E*)a.qp, (E*)a.km, (E*)a.wn, (E*)a.u, (E*)a.aqk, a.gam, (E*)a.h, (E*)a.vn};
     constexpr int NT = D / 16;
     const int NU = a.N * a.H;
-    dim3 grid(NU * NT), block(64);
-    hipLaunchKernelGGL((recur_kernel<D, F32>), grid, block, 0, st, a.s0, a.s_final, a.cu, a.N, a.T, a.H, ws);
+    auto kern = recur_kernel<D, F32>;
+    const hipError_t e = allow_dynamic_lds((const void*)kern, PL::LDS);
+    if (e != hipSuccess) return e;
+    dim3 grid(NU * NT), block(192);
+    hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.cu, a.N, a.T, a.H, ws);
     return hipGetLastError();
 }
 

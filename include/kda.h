@@ -22,8 +22,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers (HIP, gfx950) unless marked host.
- *    Every tensor is dense and contiguous in the layout given; all base
- *    addresses must be 16-byte aligned (KDA_ERR_ALIGN otherwise).
+ *    Every tensor is dense and contiguous in the layout given; base addresses
+ *    must be 16-byte aligned, except beta and cu_seqlens, which need only the
+ *    alignment of their element type (KDA_ERR_ALIGN otherwise).
  *  - Layouts are token-major: q, k, log_alpha [T, H, dk]; v [T, H, dv];
  *    beta [T, H]; o [T, H, dv]; states [N, H, dk, dv] fp32 (dv fastest).
  *  - No query scaling is applied (callers pre-scale q if they want 1/sqrt(dk)).
@@ -122,6 +123,22 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          kda_dtype in_dtype, kda_dtype gate_dtype, kda_dtype out_dtype, void* o,
                          float* final_state, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * kda_chunk_fwd with timing hooks, for profiling and benchmarking. Arguments
+ * and behaviour are those of kda_chunk_fwd; in addition, each non-NULL
+ * events[i] (a hipEvent_t created by the caller) is recorded on `stream` at
+ * stage boundary i: 0 before the per-chunk preparation kernel, 1 between it
+ * and the state-recursion kernel, 2 between that and the output kernel, 3
+ * after the output kernel. events may be NULL (then this is kda_chunk_fwd).
+ * A failed hipEventRecord returns KDA_ERR_HIP.
+ */
+kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* log_alpha,
+                               const void* beta, const float* initial_state,
+                               const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
+                               int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype gate_dtype,
+                               kda_dtype out_dtype, void* o, float* final_state, void* workspace,
+                               size_t workspace_bytes, void* stream, void* const* events);
 
 /*
  * One recurrent decode step for N independent sequences, one token each:

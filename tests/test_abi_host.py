@@ -28,8 +28,8 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = kda._load()
     names = declared_functions()
-    assert names == ["kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
-                     "kda_decode_step", "kda_status_str"]
+    assert names == ["kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_timed",
+                     "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_status_str"]
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -93,7 +93,9 @@ def test_chunk_fwd_validation():
     assert chunk_call(out_dt=2) == UNSUP
     f = Fake()
     assert chunk_call(q=f(2)) == ALIGN
-    assert chunk_call(cu=f(4), N=1) == ALIGN
+    assert chunk_call(cu=f(2), N=1) == ALIGN
+    assert chunk_call(beta=f(1)) == ALIGN
+    assert chunk_call(la=f(8)) == ALIGN
     # o overlapping q
     q = f()
     assert chunk_call(q=q, o=q + 64) == ALIAS

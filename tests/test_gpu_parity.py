@@ -66,3 +66,140 @@ def test_decode_steps(dt, d):
         eo, es = err(o, o_ref), err(state, S_ref)
         say(f"    step {s}: err(o)={eo:.3e} err(S)={es:.3e}")
         assert eo <= tol_for(dt) and es <= tol_for(dt)
+
+
+def _case_from(q, k, v, la, b, s0=None, lengths=None):
+    cu = None
+    if lengths is not None and len(lengths) > 1:
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device=DEV)
+    return ki.PrefillCase("custom", q, k, v, la, b, s0, cu, list(lengths or [q.shape[0]]))
+
+
+def test_prefill_then_decode_equals_longer_prefill():
+    """Recovery after a prefill: prefill(T) then one decode step matches
+    prefill(T+1), and both match the oracle."""
+    T = 300
+    case = ki.make_prefill("prefill-4k-slow", DEV, lengths=[T + 1], H=4)
+    say(f"[prefill+decode] T={T}")
+    o_all, S_all = kda.chunk_fwd(case.q, case.k, case.v, case.log_alpha, case.beta, case.initial_state)
+    _, S_T = kda.chunk_fwd(case.q[:T], case.k[:T], case.v[:T], case.log_alpha[:T], case.beta[:T],
+                           case.initial_state)
+    od = kda.decode_step(case.q[T:], case.k[T:], case.v[T:], case.log_alpha[T:], case.beta[T:], S_T)
+    torch.cuda.synchronize()
+    o_ref, S_ref, _ = oracle.recurrence(case.q, case.k, case.v, case.log_alpha, case.beta, case.initial_state)
+    e1, e2, e3 = err(od[0], o_ref[T]), err(S_T, S_ref), err(o_all[T], o_ref[T])
+    say(f"    err(decode o)={e1:.3e} err(carried S)={e2:.3e} err(prefill o)={e3:.3e}")
+    assert max(e1, e2, e3) <= TOL_BF16
+
+
+def test_single_token_prefill_equals_decode():
+    dec = ki.make_decode(6, 4, 128, 1, DEV, seed=5)
+    q, k, v, la, b = (dec[n][0] for n in ("q", "k", "v", "log_alpha", "beta"))
+    say("[T=1 prefill vs decode] N=6 H=4")
+    lengths = [1] * 6
+    case = _case_from(q, k, v, la, b, dec["state"].clone(), lengths)
+    o_p, S_p = gpu_prefill(case)
+    st = dec["state"].clone()
+    o_d = kda.decode_step(q, k, v, la, b, st)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.decode_step(q, k, v, la, b, dec["state"])
+    assert err(o_p, o_ref) <= TOL_BF16 and err(S_p, S_ref) <= TOL_BF16
+    assert err(o_d, o_ref) <= TOL_BF16 and err(st, S_ref) <= TOL_BF16
+
+
+def test_split_prefill_with_carry_equals_whole():
+    """Chunked prefill across calls, with the state carried in place
+    (final_state aliasing initial_state), equals one call and the oracle,
+    including splits that are not multiples of the chunk length."""
+    case = ki.make_prefill("prefill-4k-slow", DEV, lengths=[1000], H=4)
+    say("[split+carry] T=1000 split at 1, 64, 500, 777")
+    o_all, S_all = gpu_prefill(case)
+    S = case.initial_state.clone()
+    outs = []
+    for a, e in [(0, 1), (1, 64), (64, 500), (500, 777), (777, 1000)]:
+        oo, _ = kda.chunk_fwd(case.q[a:e].contiguous(), case.k[a:e].contiguous(), case.v[a:e].contiguous(),
+                              case.log_alpha[a:e].contiguous(), case.beta[a:e].contiguous(), S,
+                              final_state=S)
+        outs.append(oo)
+    torch.cuda.synchronize()
+    o_split = torch.cat(outs)
+    o_ref, S_ref, _ = oracle.recurrence(case.q, case.k, case.v, case.log_alpha, case.beta, case.initial_state)
+    e = [err(o_split, o_ref), err(S, S_ref), err(o_all, o_ref), err(S_all, S_ref)]
+    say("    " + " ".join(f"{x:.3e}" for x in e))
+    assert max(e) <= TOL_BF16
+
+
+def test_deterministic_bitwise():
+    case = ki.make_prefill("varlen-16", DEV, lengths=[700, 65, 1], H=8, s0_std=0.02)
+    say("[determinism]")
+    o1, S1 = gpu_prefill(case)
+    o2, S2 = gpu_prefill(case)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_bf16_output():
+    """A bf16 output is the fp32 output rounded to nearest even, bit for bit
+    (the rounding of o itself is the caller's choice, not a path error)."""
+    case = ki.make_prefill("prefill-4k", DEV, lengths=[333], H=4)
+    say("[bf16 output]")
+    o16, S16 = gpu_prefill(case, out_dtype=torch.bfloat16)
+    o32, S32 = gpu_prefill(case, out_dtype=torch.float32)
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(S16, S32)
+    o_ref, S_ref, _ = oracle.recurrence(case.q, case.k, case.v, case.log_alpha, case.beta, case.initial_state)
+    assert err(o32, o_ref) <= TOL_BF16 and err(S32, S_ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_extreme_decay_exact_path(dt):
+    """Gate ranges beyond the secondary-chunk guard (here up to -12 nats per
+    token) take the exact elementwise path for the gated products."""
+    case = ki.make_prefill("prefill-4k", DEV, lengths=[150, 64], H=2, dtype=dt, s0_std=0.02)
+    la = case.log_alpha.float()
+    la[:, 0] = -12.0 * torch.rand_like(la[:, 0])
+    case.log_alpha.copy_(la.to(dt))
+    check_prefill(case, tol_for(dt), label=f"extreme decay {dt}")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_no_decay_and_zero_beta(dt):
+    """alpha = 1 (DeltaNet) on one head, beta = 0 (gates only) on another."""
+    case = ki.make_prefill("prefill-4k", DEV, lengths=[200, 129], H=3, dtype=dt, s0_std=0.02)
+    case.log_alpha[:, 0] = 0
+    case.beta[:, 1] = 0
+    check_prefill(case, tol_for(dt), label=f"alpha=1 / beta=0 {dt}")
+
+
+def test_exact_retrieval_fp32():
+    """beta = 1, unit keys, q = k: the output equals v at every token."""
+    case = ki.make_prefill("prefill-4k", DEV, lengths=[300], H=2, dtype=torch.float32, s0_std=0.02)
+    case.beta.fill_(1.0)
+    k = case.k.double()
+    case.k.copy_((k / k.norm(dim=-1, keepdim=True)).float())
+    case.q.copy_(case.k)
+    say("[exact retrieval fp32]")
+    o, S = gpu_prefill(case)
+    e = err(o, case.v.double().cpu().numpy())
+    say(f"    err(o - v)={e:.3e}")
+    assert e <= TOL_F32
+
+
+@pytest.mark.parametrize("d,dt,gdt", [(64, torch.bfloat16, torch.bfloat16), (128, torch.float32, torch.float32),
+                                      (128, torch.bfloat16, torch.float32), (64, torch.float32, torch.bfloat16)])
+def test_head_sizes_and_mixed_dtypes(d, dt, gdt):
+    case = ki.make_prefill("varlen-16", DEV, lengths=[90, 3, 130], H=2, dk=d, dv=d, dtype=dt, s0_std=0.02)
+    case.log_alpha = case.log_alpha.to(gdt)
+    case.beta = case.beta.to(gdt)
+    check_prefill(case, tol_for(dt), label=f"d={d} in={dt} gates={gdt}")
+
+
+def test_all_empty_sequences():
+    """Zero tokens: final states equal the initial states."""
+    H, d = 2, 128
+    e = torch.empty(0, H, d, dtype=torch.bfloat16, device=DEV)
+    s0 = torch.randn(3, H, d, d, device=DEV)
+    cu = torch.zeros(4, dtype=torch.int32, device=DEV)
+    say("[empty]")
+    o, S = kda.chunk_fwd(e, e, e, e, torch.empty(0, H, dtype=torch.bfloat16, device=DEV), s0, cu)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(S, s0)
