@@ -35,9 +35,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build libkda.so)")
 
 
+# per-source device-compiler options
+FILE_FLAGS = {
+    # keep the recurrence's MFMA accumulators (the state) in VGPRs: the state is
+    # converted to fp16 operands every chunk, and AGPR<->VGPR moves would sit on
+    # the sequential chain
+    "kda_recur.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + HIPCC_FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + list(extra) + ["-c", src, "-o", obj]
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(line for line in res.stdout.splitlines() if "packed-fp32-ops" not in line)
     if res.returncode != 0:

@@ -168,6 +168,17 @@ template <> struct APol<false> {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
     }
+    // two independent products sharing B, interleaved so each accumulator's
+    // dependent MFMAs are separated by the other's
+    static __device__ __forceinline__ void mma2(f32x4_t& c0, const Frag& a0, f32x4_t& c1, const Frag& a1,
+                                                const Frag& b) {
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.lo, b.hi, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.lo, b.hi, c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.hi, b.lo, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.hi, b.lo, c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.hi, b.hi, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.hi, b.hi, c1, 0, 0, 0);
+    }
 };
 template <> struct APol<true> {
     using E = float;
@@ -178,6 +189,14 @@ template <> struct APol<true> {
     static __device__ __forceinline__ void store(E* p, int, const Frag& f) { Pol<true>::store(p, f); }
     static __device__ __forceinline__ void mma(f32x4_t& acc, const Frag& a, const Frag& b) {
         Pol<true>::mma(acc, a, b);
+    }
+    static __device__ __forceinline__ void mma2(f32x4_t& c0, const Frag& a0, f32x4_t& c1, const Frag& a1,
+                                                const Frag& b) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.v[j], b.v[j], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.v[j], b.v[j], c1, 0, 0, 0);
+        }
     }
 };
 

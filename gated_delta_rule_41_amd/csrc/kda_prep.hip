@@ -75,7 +75,7 @@ struct PrepSmem {
     static constexpr int KT_STRIDE = D + 8;                  // Kt row (elements)
     static constexpr int KT_PLANE = 64 * KT_STRIDE;          // elements per hi / lo plane
     static constexpr int KM_STRIDE = 64 + 4;                 // K-^T staging row (elements)
-    static constexpr int BK_STRIDE = 64 + 4;                 // beta K+ transposed row (elements)
+    static constexpr int BK_STRIDE = 64 + 4;                 // beta K+ / beta V transposed row (elements)
     static constexpr int AK_STRIDE = 20;                     // A_kk / T_II block row (floats)
     static constexpr int AK_BLOCK = 16 * AK_STRIDE;          // floats per 16 x 16 block
     static constexpr int R1 = APol<F32>::PLANES * KT_PLANE * (int)sizeof(AE);  // Kt; later -W, slow-path scans
@@ -85,9 +85,17 @@ struct PrepSmem {
     static constexpr int R3 = D * BK_STRIDE * (int)sizeof(E);                 // beta K+, transposed
     static constexpr int CONST = 22 * D * 4;                                  // tot xf eA eL cIJ; later T_II
     static constexpr int BETA = 64 * 4;
-    static constexpr int BYTES = R1 + R4 + R3 + CONST + BETA;
+    // beta V (transposed) and the -W staging share R1 once Kt is dead when both
+    // fit (16-bit operands); otherwise beta V gets a region of its own
+    static constexpr int RBV = D * BK_STRIDE * (int)sizeof(E);
+    static constexpr bool BV_IN_R1 = RBV + 64 * D * (int)sizeof(E) <= R1;
+    static constexpr int R5 = BV_IN_R1 ? 0 : RBV;
+    static constexpr int BYTES = R1 + R4 + R3 + CONST + BETA + R5;
+    static constexpr int BV_AT = BV_IN_R1 ? 0 : R1 + R4 + R3 + CONST + BETA;
+    static constexpr int WS_AT = BV_IN_R1 ? RBV : 0;
     static_assert(64 * D * 4 <= R1, "slow-path scans must fit in R1");
     static_assert(64 * D * (int)sizeof(E) <= R1, "-W staging must fit in R1");
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
     static_assert(4 * AK_BLOCK * 4 <= CONST, "T_II must fit in the constants area");
 };
 
@@ -112,7 +120,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q,
 
     extern __shared__ __align__(16) char smem[];
     AE* Kt_s = reinterpret_cast<AE*>(smem);                     // [planes][64][KTS] keys 2^(G_aJ - G)
-    E* Ws_s = reinterpret_cast<E*>(smem);                       // [64][NS][4][8] -W (after Kt is dead)
+    E* Bv_t = reinterpret_cast<E*>(smem + SM::BV_AT);           // [D][BKS] beta V transposed
+    E* Ws_s = reinterpret_cast<E*>(smem + SM::WS_AT);           // [64][NS][4][8] -W (after Kt is dead)
     float* xl_slow = reinterpret_cast<float*>(smem);            // [64][D] slow path: local scans
     char* r4 = smem + SM::R1;
     E* Km_s = reinterpret_cast<E*>(r4);                         // [D][KMS] K-^T in split row order
@@ -141,12 +150,13 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q,
     const int64_t rowoff = ((int64_t)(t0 + r) * H + h) * D;
 
     // ---- 0. all row inputs of this lane: log alpha, q, k (channels 32 s + split(g, j))
-    float xl[NS][8], q8[NS][8], k8[NS][8];
+    float xl[NS][8], q8[NS][8], k8[NS][8], v8[NS][8];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         float a4[4] = {0.f, 0.f, 0.f, 0.f}, b4[4] = {0.f, 0.f, 0.f, 0.f};
         float c4[4] = {0.f, 0.f, 0.f, 0.f}, d4[4] = {0.f, 0.f, 0.f, 0.f};
         float e4[4] = {0.f, 0.f, 0.f, 0.f}, f4[4] = {0.f, 0.f, 0.f, 0.f};
+        float g4[4] = {0.f, 0.f, 0.f, 0.f}, h4[4] = {0.f, 0.f, 0.f, 0.f};
         if (valid) {
             ld_in4(la, rowoff + 32 * s + 4 * g, a4);
             ld_in4(la, rowoff + 32 * s + 16 + 4 * g, b4);
@@ -154,6 +164,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q,
             ld_in4(q, rowoff + 32 * s + 16 + 4 * g, d4);
             ld_in4(k, rowoff + 32 * s + 4 * g, e4);
             ld_in4(k, rowoff + 32 * s + 16 + 4 * g, f4);
+            ld_in4(v, rowoff + 32 * s + 4 * g, g4);
+            ld_in4(v, rowoff + 32 * s + 16 + 4 * g, h4);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -163,6 +175,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q,
             q8[s][4 + j] = d4[j];
             k8[s][j] = e4[j];
             k8[s][4 + j] = f4[j];
+            v8[s][j] = g4[j];
+            v8[s][4 + j] = h4[j];
         }
     }
     if (g == 0) beta_s[r] = valid ? ld_in(beta, (int64_t)(t0 + r) * H + h) : 0.f;
@@ -318,21 +332,6 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q,
     }
     __syncthreads();
 
-    // values of the U tiles (waves 2-3), in accumulator layout, fetched early
-    float vv[TPW][4][4];
-    if (w >= 2) {
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-            for (int I = 0; I < 4; ++I)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = 16 * I + 4 * g + i;
-                    const int ct = (w - 2) * TPW + tt;
-                    vv[tt][I][i] = rr < L ? ld_in(v, ((int64_t)(t0 + rr) * H + h) * D + 16 * ct + n) : 0.f;
-                }
-    }
-
     // ---- 3c. A_qk (straight to the workspace) and A_kk (LDS, lower blocks only)
     E* aqk_out = ws.aqk + chh * 64 * 64;
     auto aqk_put = [&](int rr, int cc, float x) {
@@ -349,6 +348,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q,
                 continue;
             }
             f32x4_t aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+            AFrag bkt[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) bkt[s] = AP::load(Kt_s + (16 * J + n) * KTS + s * 32 + g * 8, SM::KT_PLANE);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 float xq[8], xk[8];
@@ -370,9 +372,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q,
                         xk[j] = ks[s][j];
                     }
                 }
-                const AFrag b = AP::load(Kt_s + (16 * J + n) * KTS + s * 32 + g * 8, SM::KT_PLANE);
-                AP::mma(aq, AP::make(xq), b);
-                AP::mma(ak, AP::make(xk), b);
+                AP::mma2(aq, AP::make(xq), ak, AP::make(xk), bkt[s]);
             }
             const int blk = (J == I) ? I : 4 + pair_index(I, J);
 #pragma unroll
@@ -397,6 +397,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q,
         }
     }
     __syncthreads();
+
+    // beta V, transposed like beta K+, into the now free Kt region
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Bv_t[(32 * s + kslot(g, j)) * BKS + r] = P::from_f(v8[s][j] * br);
 
     // ---- 4a. diagonal-block inverses T_II = (I + A_II)^-1 by row forward substitution (wave 0)
     if (w == 0) {
@@ -454,20 +460,14 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q,
             for (int tt = 0; tt < TPW; ++tt) {
                 const int ct = (w & 1) * TPW + tt;  // column tile inside W (waves 0-1) or U (waves 2-3)
                 f32x4_t Y;
-                if (isW) {
-                    float b4[4];
+                {
+                    const E* bsrc = (isW ? Bk_t : Bv_t) + (16 * ct + n) * BKS + 16 * I + 4 * g;
                     if constexpr (F32) {
-                        const f32x4_t bb = *reinterpret_cast<const f32x4_t*>(Bk_t + (16 * ct + n) * BKS + 16 * I + 4 * g);
-                        b4[0] = bb[0]; b4[1] = bb[1]; b4[2] = bb[2]; b4[3] = bb[3];
+                        Y = *reinterpret_cast<const f32x4_t*>(bsrc);
                     } else {
-                        const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(Bk_t + (16 * ct + n) * BKS + 16 * I + 4 * g);
-                        b4[0] = h2f(bb[0] & 0xffffu); b4[1] = h2f(bb[0] >> 16);
-                        b4[2] = h2f(bb[1] & 0xffffu); b4[3] = h2f(bb[1] >> 16);
+                        const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(bsrc);
+                        Y = f32x4_t{h2f(bb[0] & 0xffffu), h2f(bb[0] >> 16), h2f(bb[1] & 0xffffu), h2f(bb[1] >> 16)};
                     }
-                    Y = f32x4_t{b4[0], b4[1], b4[2], b4[3]};
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) Y[i] = beta_s[16 * I + 4 * g + i] * vv[tt][I][i];
                 }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {

@@ -194,15 +194,15 @@ __global__ __launch_bounds__(192) void recur_kernel(const float* __restrict__ s0
         const float* gsl = reinterpret_cast<const float*>(slot + 2 * PL::FB + PL::UB);
         const int64_t chh = (int64_t)(co + c) * H + h;
 
-        // h_n = S as B-operand fragments (also the operand of W S below)
-        Frag sb[NS];
-        E* hp = ws.h + chh * D * D + (int64_t)ct * NS * 64 * 8;
+        // every LDS read of this chunk first, so their latencies overlap
+        Frag wf[4][NS], kf[NT][2];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            sb[s] = frag_from_acc<F32>(S[2 * s], S[2 * s + 1]);
-            P::store(hp + (s * 64 + l) * 8, sb[s]);
-        }
-        // V_new = U + (-W) S
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int gr = ((16 * I + n) * NS + s) * 4 + g;  // fragment of -W (row 16I+n, slice s, group g)
+                wf[I][s] = P::load(reinterpret_cast<const E*>(wsl + swz<F32>(gr) * 8 * sizeof(E)));
+            }
         f32x4_t V[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
@@ -214,12 +214,29 @@ __global__ __launch_bounds__(192) void recur_kernel(const float* __restrict__ s0
             }
         }
 #pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int gr = ((16 * t + n) * 2 + s) * 4 + g;  // fragment of K-^T (row 16t+n, slice s, group g)
+                kf[t][s] = P::load(reinterpret_cast<const E*>(ksl + swz<F32>(gr) * 8 * sizeof(E)));
+            }
+        f32x4_t gm[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) gm[t] = *reinterpret_cast<const f32x4_t*>(gsl + 16 * t + 4 * g);
+
+        // h_n = S as B-operand fragments (also the operand of W S below)
+        Frag sb[NS];
+        E* hp = ws.h + chh * D * D + (int64_t)ct * NS * 64 * 8;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            sb[s] = frag_from_acc<F32>(S[2 * s], S[2 * s + 1]);
+            P::store(hp + (s * 64 + l) * 8, sb[s]);
+        }
+        // V_new = U + (-W) S
+#pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                const int gr = ((16 * I + n) * NS + s) * 4 + g;  // fragment of -W (row 16I+n, slice s, group g)
-                P::mma(V[I], P::load(reinterpret_cast<const E*>(wsl + swz<F32>(gr) * 8 * sizeof(E))), sb[s]);
-            }
+            for (int I = 0; I < 4; ++I) P::mma(V[I], wf[I][s], sb[s]);
         Frag vb[2];
         E* vp = ws.vn + chh * 64 * D + (int64_t)ct * 2 * 64 * 8;
 #pragma unroll
@@ -229,14 +246,11 @@ __global__ __launch_bounds__(192) void recur_kernel(const float* __restrict__ s0
         }
         // S <- Diag(gamma) S + K-^T V_new
 #pragma unroll
-        for (int t = 0; t < NT; ++t) S[t] = *reinterpret_cast<const f32x4_t*>(gsl + 16 * t + 4 * g) * S[t];
+        for (int t = 0; t < NT; ++t) S[t] = gm[t] * S[t];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int gr = ((16 * t + n) * 2 + s) * 4 + g;  // fragment of K-^T (row 16t+n, slice s, group g)
-                P::mma(S[t], P::load(reinterpret_cast<const E*>(ksl + swz<F32>(gr) * 8 * sizeof(E))), vb[s]);
-            }
+            for (int t = 0; t < NT; ++t) P::mma(S[t], kf[t][s], vb[s]);
         __builtin_amdgcn_s_barrier();
     }
     if (s_final) {
