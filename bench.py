@@ -9,6 +9,11 @@ heads, fp32 states of 512 MiB, updated in place) and reported in the same JSON
 line. Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--decode-steps S] [--no-cpu-baseline]
+
+Profiling helpers (used to write the summaries under profiles/):
+    python bench.py --copy-calibration MIB        # counter calibration kernel only
+    python bench.py --report-trace DB             # kernel-trace database -> markdown
+    python bench.py --report-pmc FETCH_DB WRITE_DB CAL_FETCH_DB CAL_WRITE_DB CAL_BYTES
 """
 from __future__ import annotations
 
@@ -182,7 +187,95 @@ def cpu_baseline(case):
                       f"{dt:.2f} s wall"}, host
 
 
+def copy_calibration(mib: int = 512, reps: int = 5):
+    """A plain streaming kernel of known size (y = x * 1, fp32, ``mib`` MiB read and
+    ``mib`` MiB written per launch) whose FETCH_SIZE / WRITE_SIZE counters give
+    the scale from those counters to bytes. Run in a process of its own so that
+    it is the only multiply kernel the profiler sees."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": 4 * n, "bytes_written": 4 * n, "reps": reps}}))
+    return 0
+
+
+def _rocpd(path):
+    import sqlite3
+    return sqlite3.connect(f"file:{path}?mode=ro", uri=True).cursor()
+
+
+def _short(name: str) -> str:
+    base = name.split("(")[0]
+    return base.replace("void ", "").replace("kda::", "")
+
+
+def report_trace(db: str) -> int:
+    """Markdown table of this library's kernels from a rocprofv3 --kernel-trace
+    database: dispatch count and duration statistics (microseconds)."""
+    cur = _rocpd(db)
+    rows = cur.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+                       "from kernels where name like '%kda::%' group by name order by sum(duration) desc").fetchall()
+    print("| kernel | calls | avg us | min us | max us | total us |")
+    print("|---|---|---|---|---|---|")
+    for name, n, avg, mn, mx, tot in rows:
+        print(f"| `{_short(name)}` | {n} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | {tot / 1e3:.1f} |")
+    return 0
+
+
+def _counter_avg(db: str, counter: str, like: str):
+    cur = _rocpd(db)
+    return cur.execute("select kernel_name, count(*), avg(value) from counters_collection "
+                       "where counter_name = ? and kernel_name like ? group by kernel_name",
+                       (counter, like)).fetchall()
+
+
+def report_pmc(fetch_db: str, write_db: str, cal_fetch_db: str, cal_write_db: str, cal_bytes: int) -> int:
+    """HBM traffic per launch of each library kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch, one rocprofv3 --pmc run each), each scaled by
+    what the same counter reads for the calibration copy kernel of known size.
+    Writes profiles/pmc_<kernel>_<workload>.json (read back by the roofline
+    report while the kernel source is unchanged) and prints a markdown table."""
+    cf = _counter_avg(cal_fetch_db, "FETCH_SIZE", "%MulFunctor%")
+    cw = _counter_avg(cal_write_db, "WRITE_SIZE", "%MulFunctor%")
+    if not cf or not cw:
+        print("calibration kernel not found in the counter databases", file=sys.stderr)
+        return 1
+    f_fetch = cal_bytes / (cf[0][2] * 1024.0)
+    f_write = cal_bytes / (cw[0][2] * 1024.0)
+    fe = {_short(n): (c, v) for n, c, v in _counter_avg(fetch_db, "FETCH_SIZE", "%kda::%")}
+    wr = {_short(n): (c, v) for n, c, v in _counter_avg(write_db, "WRITE_SIZE", "%kda::%")}
+    print(f"calibration (y = x*1 over {cal_bytes >> 20} MiB): FETCH_SIZE {cf[0][2]:.0f} KiB -> scale {f_fetch:.4f}; "
+          f"WRITE_SIZE {cw[0][2]:.0f} KiB -> scale {f_write:.4f}\n")
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) |")
+    print("|---|---|---|---|---|")
+    for name in sorted(fe):
+        if name not in wr:
+            continue
+        kern = next((k for k, sym in KERNEL_SYMBOL.items() if name.startswith(sym)), None)
+        b = fe[name][1] * 1024 * f_fetch + wr[name][1] * 1024 * f_write
+        print(f"| `{name}` | {fe[name][0]} | {fe[name][1]:.0f} | {wr[name][1]:.0f} | {b:.4g} |")
+        if kern is None:
+            continue
+        wl = "decode-256" if kern == "decode" else "prefill-4k"
+        rec = {"kernel": name, "workload": wl, "source_sha": source_sha(kern),
+               "fetch_kib": fe[name][1], "write_kib": wr[name][1],
+               "fetch_scale": f_fetch, "write_scale": f_write, "bytes_per_launch": round(b)}
+        with open(os.path.join(ROOT, "profiles", f"pmc_{kern}_{wl}.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+    return 0
+
+
 def main(argv=None):
+    if argv is None:
+        argv = sys.argv[1:]
+    if argv[:1] == ["--report-trace"]:
+        return report_trace(argv[1])
+    if argv[:1] == ["--report-pmc"]:
+        return report_pmc(argv[1], argv[2], argv[3], argv[4], int(argv[5]))
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -190,7 +283,11 @@ def main(argv=None):
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run the counter calibration copy kernel over MIB MiB")
     args = ap.parse_args(argv)
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is a design in DESIGN.md, not built", file=sys.stderr)
