@@ -31,8 +31,10 @@
  *  - Supported head sizes: (dk, dv) in {(64, 64), (128, 128)}.
  *  - Supported dtypes: in_dtype (q, k, v) and gate_dtype (log_alpha, beta) are
  *    each KDA_BF16 or KDA_F32; out_dtype (o) KDA_F32 or KDA_BF16. With
- *    in_dtype == KDA_BF16 the chunk products run on bf16 matrix cores with
- *    fp32 accumulation and an fp32 state; with KDA_F32 they run in fp32.
+ *    in_dtype == KDA_BF16 the chunk products run on 16-bit matrix cores with
+ *    fp32 accumulation and an fp32 state (fp16 operands for the value path;
+ *    the gated query-key products use bf16 operands split into a high and a
+ *    low part); with KDA_F32 they run on fp32 matrix cores.
  *  - log_alpha must be finite (<= 0 for the overflow guarantees; 0 is allowed).
  *    Non-finite inputs give undefined (typically NaN) outputs; inputs are not scanned.
  *  - Ownership: the caller owns every buffer. The library never allocates or
