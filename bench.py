@@ -1,7 +1,8 @@
 """Benchmark of the KDA hot path on one MI355X.
 
-One step = one chunkwise prefill call (per-chunk preparation, inter-chunk
-state recursion, fused output) on the ``prefill-4k`` workload: B=1, H=32,
+One step = one chunkwise prefill call (per-chunk preparation, then the
+inter-chunk state recursion with the chunk outputs fused in) on the
+``prefill-4k`` workload: B=1, H=32,
 T=4096, dk=dv=128, chunk 64, bf16 inputs, fp32 initial/final state and fp32
 output (synthetic, seeded; see kda_inputs). The decode step (the remaining row
 of the hot path) is timed in the same run on ``decode-256`` (256 sequences x 32
@@ -36,13 +37,13 @@ FLOP_PER_TOKEN_HEAD = 140629
 ALG_BYTES_PER_TOKEN_HEAD = 1538            # q,k,v,log_alpha bf16 + beta bf16 + o fp32
 KERNEL_BYTES_PER_TOKEN_HEAD = {            # compulsory traffic of each prefill kernel
     "prep": 1026 + 1160,                   # reads q,k,v,log_alpha,beta; writes Q+,K-,W,U,A_qk,gamma
-    "recur": 776 + 768,                    # reads W,K-,U,gamma; writes h, V_new
-    "output": 1152 + 512,                  # reads Q+,A_qk,h,V_new; writes o (fp32)
+    # with bf16 inputs the output is fused into the state recursion:
+    "recur": 776 + 384 + 512,              # reads W,K-,U,gamma,Q+,A_qk; writes o (fp32)
 }
-KERNEL_SYMBOL = {"prep": "prep_kernel", "recur": "recur_kernel", "output": "output_kernel",
-                 "decode": "decode_kernel"}
-KERNEL_SOURCE = {"prep": "kda_prep.hip", "recur": "kda_recur.hip", "output": "kda_output.hip",
-                 "decode": "kda_decode.hip"}
+# fp32 inputs (not benchmarked) run the unfused pair: recursion 776 + 768 (h_n,
+# V_new written), output 1152 + 512
+KERNEL_SYMBOL = {"prep": "prep_kernel", "recur": "recur_kernel", "decode": "decode_kernel"}
+KERNEL_SOURCE = {"prep": "kda_prep.hip", "recur": "kda_recur.hip", "decode": "kda_decode.hip"}
 
 
 def hip_runtime():
@@ -137,13 +138,12 @@ def time_prefill(kda, case, steps, warmup, hip, stream):
     for s in range(steps):
         call(events=ev.ev[4 * s:4 * s + 4])
     torch.cuda.synchronize()
-    per = {"prep": 0.0, "recur": 0.0, "output": 0.0}
+    per = {"prep": 0.0, "recur": 0.0}
     span = 0.0
     for s in range(steps):
         b = 4 * s
         per["prep"] += ev.ms(b, b + 1)
-        per["recur"] += ev.ms(b + 1, b + 2)
-        per["output"] += ev.ms(b + 2, b + 3)
+        per["recur"] += ev.ms(b + 1, b + 3)  # state recursion with the fused output
         span += ev.ms(b, b + 3)
     ev.close()
     per = {k_: v_ / steps for k_, v_ in per.items()}
@@ -321,7 +321,7 @@ def main(argv=None):
 
     dom = max(per, key=per.get)
     kb = KERNEL_BYTES_PER_TOKEN_HEAD[dom] * TH
-    if dom == "recur":
+    if dom == "recur":  # plus the initial and final states
         kb += 2 * case.N * case.H * case.dk * case.dv * 4
     achieved = kb / (per[dom] * 1e-3) / 1e9
     roof = {"kernel": KERNEL_SYMBOL[dom], "bound": "hbm", "achieved": round(achieved, 1),

@@ -65,8 +65,8 @@ WsPlan plan_workspace(int64_t NC, int H, int D, bool f32) {
         ch * KDA_CHUNK * D * es,       // u
         ch * KDA_CHUNK * KDA_CHUNK * es,  // aqk
         ch * D * 4,                    // gam
-        ch * (size_t)D * D * es,       // h
-        ch * KDA_CHUNK * D * es,       // vn
+        output_fused(f32) ? 0 : ch * (size_t)D * D * es,   // h (only without the fused output)
+        output_fused(f32) ? 0 : ch * KDA_CHUNK * D * es,   // vn
     };
     WsPlan p;
     size_t o = 0;
@@ -217,7 +217,7 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
     if (!mark(1)) return KDA_ERR_HIP;
     if (launch_recur(a, st) != hipSuccess) return KDA_ERR_HIP;
     if (!mark(2)) return KDA_ERR_HIP;
-    if (NC > 0 && launch_output(a, st) != hipSuccess) return KDA_ERR_HIP;
+    if (NC > 0 && !output_fused(f32) && launch_output(a, st) != hipSuccess) return KDA_ERR_HIP;
     if (!mark(3)) return KDA_ERR_HIP;
     return KDA_OK;
 }

@@ -46,4 +46,10 @@ hipError_t launch_prep(const ChunkArgs& a, hipStream_t st);
 hipError_t launch_recur(const ChunkArgs& a, hipStream_t st);
 hipError_t launch_output(const ChunkArgs& a, hipStream_t st);
 
+// With 16-bit operands the state-recursion kernel also computes the chunk
+// outputs (h_n and V_new stay on chip); with fp32 operands its LDS cannot
+// hold the exchange buffers, and a separate output kernel reads h_n and V_new
+// from the workspace.
+inline bool output_fused(bool in_f32) { return !in_f32; }
+
 }  // namespace kda

@@ -33,9 +33,11 @@
 #include "kda_common.h"
 #include "kda_launch.h"
 
+#include <type_traits>
+
 namespace kda {
 
-template <int D, bool F32>
+template <int D, bool F32, bool FUSED>
 struct RecurPlan {
     using E = typename Pol<F32>::E;
     static constexpr int FB = 64 * D * (int)sizeof(E);   // bytes of -W (and of K-^T) per chunk-head
@@ -43,8 +45,12 @@ struct RecurPlan {
     static constexpr int GB = D * 4;                     // bytes of gamma
     static constexpr int GPAD = 1024;                    // gamma region rounded up to one whole load
     static constexpr int SLOT = 2 * FB + UB + GPAD;      // one ring slot
-    static constexpr int RING = (4 * SLOT <= 150 * 1024) ? 4 : 2;
-    static constexpr int LDS = RING * SLOT;
+    // with the fused output: two buffers of (h_n slab [D x 16], V_new slab [64 x 16])
+    static constexpr int HVS = (D * 16 + 64 * 16) * (int)sizeof(E);
+    static constexpr int HV = FUSED ? 2 * HVS : 0;
+    static constexpr int RING = (4 * SLOT + HV <= 160 * 1024) ? 4 : 2;
+    static constexpr int LDS = RING * SLOT + HV;
+    static_assert(LDS <= 160 * 1024, "LDS budget");
     // global->LDS loads per chunk and producer wave (16 bytes per lane, 1 KiB per load)
     static constexpr int OPS_W = FB / 1024, OPS_U = UB / 1024, OPS_G = 1;
     static constexpr int OPS0 = OPS_W + OPS_U;   // producer 0: -W and U
@@ -74,6 +80,9 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// wait until this wave's LDS operations have completed
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
 // wait until only the loads of the `after` chunks issued last are outstanding
 template <int OPS, int RING>
 __device__ __forceinline__ void wait_chunks(int after) {
@@ -95,10 +104,10 @@ __device__ __forceinline__ void wait_chunks(int after) {
 // Producer: issue the global->LDS loads of one chunk (this producer's half).
 // Both producers issue exactly OPS loads per chunk, so one vmcnt threshold
 // serves both.
-template <int D, bool F32>
+template <int D, bool F32, bool FUSED>
 __device__ __forceinline__ void produce(const Ws<typename Pol<F32>::E>& ws, int64_t chh, int ct, int pw, int l,
                                        char* slot) {
-    using PL = RecurPlan<D, F32>;
+    using PL = RecurPlan<D, F32, FUSED>;
     if (pw == 0) {
         const char* wp = reinterpret_cast<const char*>(ws.wn + chh * 64 * D);
 #pragma unroll
@@ -123,14 +132,22 @@ __device__ __forceinline__ void produce(const Ws<typename Pol<F32>::E>& ws, int6
     }
 }
 
-template <int D, bool F32>
-__global__ __launch_bounds__(192) void recur_kernel(const float* __restrict__ s0, float* __restrict__ s_final,
-                                                    const int32_t* __restrict__ cu, int N, int T, int H,
-                                                    Ws<typename Pol<F32>::E> ws) {
+// With FUSED, two more waves compute each chunk's output O = Q+ h_n + A_qk V_new
+// for this slab's 16 columns, one chunk behind the compute wave: the compute
+// wave leaves h_n and V_new in an LDS buffer (two buffers, by chunk parity)
+// instead of the workspace, and the output waves, taking alternate chunks,
+// fetch Q+ and A_qk into registers one chunk ahead. Waves: 0 compute, 1-2
+// output, 3-4 producers. Every wave executes the same 1 + nch barriers.
+template <int D, bool F32, bool FUSED, bool OUT_F32>
+__global__ __launch_bounds__(FUSED ? 320 : 192) void recur_kernel(const float* __restrict__ s0,
+                                                                  float* __restrict__ s_final,
+                                                                  const int32_t* __restrict__ cu, int N, int T,
+                                                                  int H, Ws<typename Pol<F32>::E> ws,
+                                                                  void* __restrict__ o) {
     using P = Pol<F32>;
     using E = typename P::E;
     using Frag = typename P::Frag;
-    using PL = RecurPlan<D, F32>;
+    using PL = RecurPlan<D, F32, FUSED>;
     constexpr int NS = D / 32;
     constexpr int NT = D / 16;  // row tiles over dk == column slabs over dv
     constexpr int RING = PL::RING;
@@ -155,12 +172,88 @@ __global__ __launch_bounds__(192) void recur_kernel(const float* __restrict__ s0
 
     int co, nch;
     seq_chunks(cu, T, seq, co, nch);
+    char* hvbase = ring + RING * PL::SLOT;  // h_n / V_new exchange buffers (FUSED)
+
+    if (FUSED && (wv == 1 || wv == 2)) {
+        // ---------------- output waves: wave 1 + p computes the outputs of the
+        // chunks j = p (mod 2). It fetches chunk j's Q+ and A_qk at the start of
+        // iteration j and computes O_j in iteration j + 1, once the compute wave
+        // has left h_j and V_j in the exchange buffer j & 1.
+        const int p = wv - 1;
+        const int tstart = cu ? cu[seq] : 0;
+        const int len = cu ? cu[seq + 1] - tstart : T;
+        Frag qa[4][NS], aa[4][2];
+        auto issue = [&](int c) {
+            const int64_t chh = (int64_t)(co + c) * H + h;
+            const E* qp = ws.qp + chh * 64 * D;
+            const E* ap = ws.aqk + chh * 64 * 64;
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int s = 0; s < NS; ++s) qa[I][s] = P::load(qp + ((16 * I + n) * NS + s) * 32 + g * 8);
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (16 * I + 15 >= 32 * s) aa[I][s] = P::load(ap + ((16 * I + n) * 2 + s) * 32 + g * 8);
+        };
+        // only a sequence's last chunk can be partial; every other chunk stores
+        // all 64 rows without a per-row branch
+        auto consume = [&](int c, auto masked) {
+            const E* hb = reinterpret_cast<const E*>(hvbase + (c & 1) * PL::HVS);
+            const E* vb = hb + D * 16;
+            f32x4_t acc[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) acc[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const Frag bh = P::load(hb + (s * 64 + l) * 8);
+#pragma unroll
+                for (int I = 0; I < 4; ++I) P::mma(acc[I], qa[I][s], bh);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const Frag bv = P::load(vb + (s * 64 + l) * 8);
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+                    if (16 * I + 15 >= 32 * s) P::mma(acc[I], aa[I][s], bv);
+            }
+            const int t0 = tstart + 64 * c;
+            const int L = min(64, len - 64 * c);
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 16 * I + 4 * g + i;
+                    if (!decltype(masked)::value || rr < L) {
+                        const int64_t oi = ((int64_t)(t0 + rr) * H + h) * D + 16 * ct + n;
+                        if constexpr (OUT_F32)
+                            static_cast<float*>(o)[oi] = acc[I][i];
+                        else
+                            static_cast<uint16_t*>(o)[oi] = f2bf(acc[I][i]);
+                    }
+                }
+        };
+        __builtin_amdgcn_s_barrier();
+        if (p == 1 && nch > 0) __builtin_amdgcn_s_barrier();  // iteration 0 (chunk 0 is wave 1's)
+        for (int j = p; j < nch; j += 2) {
+            issue(j);
+            __builtin_amdgcn_s_barrier();  // end of iteration j
+            if (j + 1 < nch) {
+                consume(j, std::false_type{});
+                __builtin_amdgcn_s_barrier();  // end of iteration j + 1
+            } else {
+                consume(j, std::true_type{});
+            }
+        }
+        return;
+    }
 
     if (wv > 0) {
-        // ---------------- producers (waves 1 and 2)
-        const int pw = wv - 1;
+        // ---------------- producers (waves 1 and 2; 3 and 4 when fused)
+        const int pw = FUSED ? wv - 3 : wv - 1;
         const int pre = nch < RING - 1 ? nch : RING - 1;
-        for (int c = 0; c < pre; ++c) produce<D, F32>(ws, (int64_t)(co + c) * H + h, ct, pw, l, ring + c * PL::SLOT);
+        for (int c = 0; c < pre; ++c) produce<D, F32, FUSED>(ws, (int64_t)(co + c) * H + h, ct, pw, l, ring + c * PL::SLOT);
         // chunk 0 has landed once at most the (pre - 1) later chunks are outstanding
         wait_chunks<OPS, RING>(pre - 1);
         __builtin_amdgcn_s_barrier();
@@ -168,7 +261,7 @@ __global__ __launch_bounds__(192) void recur_kernel(const float* __restrict__ s0
             // slot (c + RING - 1) % RING was read by the compute wave in chunk c - 1,
             // which it finished before the barrier that ended that chunk
             const int nx = c + RING - 1;
-            if (nx < nch) produce<D, F32>(ws, (int64_t)(co + nx) * H + h, ct, pw, l, ring + (nx % RING) * PL::SLOT);
+            if (nx < nch) produce<D, F32, FUSED>(ws, (int64_t)(co + nx) * H + h, ct, pw, l, ring + (nx % RING) * PL::SLOT);
             // chunk c + 1 has landed once only the chunks issued after it are outstanding
             const int after = (nch - 1 < nx ? nch - 1 : nx) - (c + 1);
             wait_chunks<OPS, RING>(after);
@@ -224,9 +317,11 @@ __global__ __launch_bounds__(192) void recur_kernel(const float* __restrict__ s0
 #pragma unroll
         for (int t = 0; t < NT; ++t) gm[t] = *reinterpret_cast<const f32x4_t*>(gsl + 16 * t + 4 * g);
 
-        // h_n = S as B-operand fragments (also the operand of W S below)
+        // h_n = S as B-operand fragments (also the operand of W S below); to the
+        // output wave's LDS buffer when fused, else to the workspace
         Frag sb[NS];
-        E* hp = ws.h + chh * D * D + (int64_t)ct * NS * 64 * 8;
+        E* hp = FUSED ? reinterpret_cast<E*>(hvbase + (c & 1) * PL::HVS)
+                      : ws.h + chh * D * D + (int64_t)ct * NS * 64 * 8;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             sb[s] = frag_from_acc<F32>(S[2 * s], S[2 * s + 1]);
@@ -238,7 +333,8 @@ __global__ __launch_bounds__(192) void recur_kernel(const float* __restrict__ s0
 #pragma unroll
             for (int I = 0; I < 4; ++I) P::mma(V[I], wf[I][s], sb[s]);
         Frag vb[2];
-        E* vp = ws.vn + chh * 64 * D + (int64_t)ct * 2 * 64 * 8;
+        E* vp = FUSED ? reinterpret_cast<E*>(hvbase + (c & 1) * PL::HVS) + D * 16
+                      : ws.vn + chh * 64 * D + (int64_t)ct * 2 * 64 * 8;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             vb[s] = frag_from_acc<F32>(V[2 * s], V[2 * s + 1]);
@@ -251,6 +347,7 @@ __global__ __launch_bounds__(192) void recur_kernel(const float* __restrict__ s0
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int t = 0; t < NT; ++t) P::mma(S[t], kf[t][s], vb[s]);
+        if constexpr (FUSED) wait_lgkm0();  // h_n / V_new in LDS before the hand-over
         __builtin_amdgcn_s_barrier();
     }
     if (s_final) {
@@ -261,24 +358,29 @@ __global__ __launch_bounds__(192) void recur_kernel(const float* __restrict__ s0
     }
 }
 
-template <int D, bool F32>
+template <int D, bool F32, bool FUSED, bool OUT_F32>
 static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     using E = typename Pol<F32>::E;
-    using PL = RecurPlan<D, F32>;
+    using PL = RecurPlan<D, F32, FUSED>;
     Ws<E> ws{(E*)a.qp, (E*)a.km, (E*)a.wn, (E*)a.u, (E*)a.aqk, a.gam, (E*)a.h, (E*)a.vn};
     constexpr int NT = D / 16;
     const int NU = a.N * a.H;
-    auto kern = recur_kernel<D, F32>;
+    auto kern = recur_kernel<D, F32, FUSED, OUT_F32>;
     const hipError_t e = allow_dynamic_lds((const void*)kern, PL::LDS);
     if (e != hipSuccess) return e;
-    dim3 grid(NU * NT), block(192);
-    hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.cu, a.N, a.T, a.H, ws);
+    dim3 grid(NU * NT), block(FUSED ? 320 : 192);
+    hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.cu, a.N, a.T, a.H, ws, a.o);
     return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_recur_d(const ChunkArgs& a, hipStream_t st) {
+    if (a.in_f32) return launch_recur_t<D, true, false, true>(a, st);
+    return a.out_f32 ? launch_recur_t<D, false, true, true>(a, st) : launch_recur_t<D, false, true, false>(a, st);
+}
+
 hipError_t launch_recur(const ChunkArgs& a, hipStream_t st) {
-    if (a.D == 128) return a.in_f32 ? launch_recur_t<128, true>(a, st) : launch_recur_t<128, false>(a, st);
-    return a.in_f32 ? launch_recur_t<64, true>(a, st) : launch_recur_t<64, false>(a, st);
+    return a.D == 128 ? launch_recur_d<128>(a, st) : launch_recur_d<64>(a, st);
 }
 
 }  // namespace kda

@@ -86,8 +86,9 @@ const char* kda_status_str(int status);
  * Bytes of device workspace kda_chunk_fwd needs for a batch of N sequences
  * with T_total tokens in all (host call, no device access). The workspace
  * holds the per-chunk factors (gated queries and keys, WY factors, the
- * intra-chunk query-key matrix, chunk-entry states, corrected values) for at
- * most floor((T_total + 63*N) / 64) chunks per head.
+ * intra-chunk query-key matrix, the chunk decay; with fp32 inputs also the
+ * chunk-entry states and corrected values) for at most
+ * floor((T_total + 63*N) / 64) chunks per head.
  *   bytes: host out-pointer, written on KDA_OK.
  */
 kda_status kda_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk,
@@ -132,7 +133,9 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
  * events[i] (a hipEvent_t created by the caller) is recorded on `stream` at
  * stage boundary i: 0 before the per-chunk preparation kernel, 1 between it
  * and the state-recursion kernel, 2 between that and the output kernel, 3
- * after the output kernel. events may be NULL (then this is kda_chunk_fwd).
+ * after the output kernel. With bf16 inputs the output is computed inside the
+ * state-recursion kernel, so events 2 and 3 are recorded back to back.
+ * events may be NULL (then this is kda_chunk_fwd).
  * A failed hipEventRecord returns KDA_ERR_HIP.
  */
 kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* log_alpha,

@@ -42,11 +42,12 @@ def test_version_and_status_strings():
 
 
 def test_workspace_size_formula():
-    # per chunk-head, d = 128, bf16 factors: Q+, K-, -W, U, V_new 16 KiB each, A_qk 8 KiB,
-    # gamma 512 B, chunk-entry state 32 KiB -> 123392 B; chunks = floor((T + 63 N) / 64)
-    assert kda.workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 123392
-    assert kda.workspace_size(16, 135000, 32, 128, 128) == ((135000 + 63 * 16) // 64) * 32 * 123392
-    # fp32 factors double every array but gamma
+    # per chunk-head, d = 128, 16-bit factors: Q+, K-, -W, U 16 KiB each, A_qk 8 KiB,
+    # gamma 512 B -> 74240 B (the fused output keeps h_n and V_new on chip);
+    # chunks = floor((T + 63 N) / 64)
+    assert kda.workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 74240
+    assert kda.workspace_size(16, 135000, 32, 128, 128) == ((135000 + 63 * 16) // 64) * 32 * 74240
+    # fp32 factors double every array but gamma, and add h_n and V_new
     assert kda.workspace_size(1, 256, 1, 64, 64, __import__("torch").float32) == 4 * (
         4 * (64 * 64 * 4) + 64 * 64 * 4 + 64 * 4 + 64 * 64 * 4 + 64 * 64 * 4)
     with pytest.raises(kda.KDAError):

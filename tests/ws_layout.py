@@ -23,10 +23,13 @@ def chunk_capacity(N, T, have_cu):
 
 
 def plan(NC, H, D, f32):
+    """Array offsets and total size. With 16-bit factors the output is fused
+    into the state recursion and the chunk-entry states / corrected values stay
+    on chip (their arrays are empty)."""
     es = 4 if f32 else 2
     ch = NC * H
     sizes = [ch * CH * D * es, ch * D * CH * es, ch * CH * D * es, ch * CH * D * es,
-             ch * CH * CH * es, ch * D * 4, ch * D * D * es, ch * CH * D * es]
+             ch * CH * CH * es, ch * D * 4, ch * D * D * es if f32 else 0, ch * CH * D * es if f32 else 0]
     off, o = [], 0
     for s in sizes:
         off.append(o)
@@ -81,6 +84,8 @@ def decode(ws: torch.Tensor, N, T, H, D, f32, have_cu, gc, h):
     out["Aqk"] = A
     b = off[5] + chh * D * 4
     out["gam"] = raw[b:b + D * 4].copy().view(np.float32).astype(np.float64)
+    if not f32:
+        return out
     hh = arr(6, D * D).reshape(NCT, NS, 64, 8)
     Hm = np.zeros((D, D))
     vn = arr(7, CH * D).reshape(NCT, 2, 64, 8)
