@@ -168,16 +168,30 @@ template <> struct APol<false> {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
     }
-    // two independent products sharing B, interleaved so each accumulator's
-    // dependent MFMAs are separated by the other's
-    static __device__ __forceinline__ void mma2(f32x4_t& c0, const Frag& a0, f32x4_t& c1, const Frag& a1,
-                                                const Frag& b) {
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.lo, b.hi, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.lo, b.hi, c1, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.hi, b.lo, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.hi, b.lo, c1, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.hi, b.hi, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.hi, b.hi, c1, 0, 0, 0);
+    // The gated query-key and key-key products of one block, sharing B:
+    // cq += xq B in split bf16 (xq split by truncation: hi keeps the top 16
+    // bits exactly, lo = x - hi rounded to nearest, about 16 significant bits
+    // in all), ck += xk B with xk and B rounded once to bf16 (the key-key
+    // matrix only feeds the UT transform, where bf16 operands cost nothing
+    // measurable against the fp16 value path). Interleaved so dependent MFMAs
+    // of one accumulator are separated by the other's.
+    static __device__ __forceinline__ void mma_qk(f32x4_t& cq, const float (&xq)[8], f32x4_t& ck,
+                                                  const float (&xk)[8], const Frag& b) {
+        u32x4_t qh, ql, kh;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t b0 = __float_as_uint(xq[2 * j]) & 0xffff0000u;
+            const uint32_t b1 = __float_as_uint(xq[2 * j + 1]) & 0xffff0000u;
+            qh[j] = (b0 >> 16) | b1;
+            ql[j] = pack2bf(xq[2 * j] - __uint_as_float(b0), xq[2 * j + 1] - __uint_as_float(b1));
+            kh[j] = pack2bf(xk[2 * j], xk[2 * j + 1]);
+        }
+        const bf16x8_t qhi = __builtin_bit_cast(bf16x8_t, qh), qlo = __builtin_bit_cast(bf16x8_t, ql);
+        const bf16x8_t khi = __builtin_bit_cast(bf16x8_t, kh);
+        cq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qlo, b.hi, cq, 0, 0, 0);
+        ck = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, b.hi, ck, 0, 0, 0);
+        cq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi, b.lo, cq, 0, 0, 0);
+        cq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi, b.hi, cq, 0, 0, 0);
     }
 };
 template <> struct APol<true> {
@@ -190,12 +204,13 @@ template <> struct APol<true> {
     static __device__ __forceinline__ void mma(f32x4_t& acc, const Frag& a, const Frag& b) {
         Pol<true>::mma(acc, a, b);
     }
-    static __device__ __forceinline__ void mma2(f32x4_t& c0, const Frag& a0, f32x4_t& c1, const Frag& a1,
-                                                const Frag& b) {
+    static __device__ __forceinline__ void mma_qk(f32x4_t& cq, const float (&xq)[8], f32x4_t& ck,
+                                                  const float (&xk)[8], const Frag& b) {
+        const Frag a0 = make(xq), a1 = make(xk);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.v[j], b.v[j], c0, 0, 0, 0);
-            c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.v[j], b.v[j], c1, 0, 0, 0);
+            cq = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.v[j], b.v[j], cq, 0, 0, 0);
+            ck = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.v[j], b.v[j], ck, 0, 0, 0);
         }
     }
 };

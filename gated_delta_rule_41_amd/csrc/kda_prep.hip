@@ -99,10 +99,50 @@ struct PrepSmem {
     static_assert(4 * AK_BLOCK * 4 <= CONST, "T_II must fit in the constants area");
 };
 
+// One lane's share of an input row (channels 32 s + split(g, j), j < 8, of each
+// 32-channel slice s), held raw (unconverted) so that the loads of every
+// input can be issued before the first one is waited for.
+template <typename T, int NS>
+struct RowRaw {
+    static constexpr int W = sizeof(T) == 2 ? 2 : 4;  // dwords per 4 elements
+    uint32_t d[NS][2][W];
+    __device__ __forceinline__ void load(const T* p, int64_t off, int g) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const T* src = p + off + 32 * s + 16 * hf + 4 * g;
+                if constexpr (W == 2) {
+                    const u32x2_t u = *reinterpret_cast<const u32x2_t*>(src);
+                    d[s][hf][0] = u[0];
+                    d[s][hf][1] = u[1];
+                } else {
+                    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(src);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) d[s][hf][j] = u[j];
+                }
+            }
+    }
+    __device__ __forceinline__ void get(float (&x)[NS][8], bool valid, float scale) const {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float f;
+                    if constexpr (W == 2)
+                        f = __uint_as_float((j & 1) ? (d[s][hf][j >> 1] & 0xffff0000u) : (d[s][hf][j >> 1] << 16));
+                    else
+                        f = __uint_as_float(d[s][hf][j]);
+                    x[s][4 * hf + j] = valid ? f * scale : 0.f;
+                }
+    }
+};
+
 template <int D, typename TIn, typename TG, bool F32>
-__global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
-                                                      const TIn* __restrict__ v, const TG* __restrict__ la,
-                                                      const TG* __restrict__ beta,
+__global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k, const TIn* v,
+                                                      const TG* la, const TG* beta,
                                                       const int32_t* __restrict__ cu, int N, int T, int H,
                                                       Ws<typename Pol<F32>::E> ws) {
     using P = Pol<F32>;
@@ -149,37 +189,28 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q,
     const bool valid = r < L;
     const int64_t rowoff = ((int64_t)(t0 + r) * H + h) * D;
 
-    // ---- 0. all row inputs of this lane: log alpha, q, k (channels 32 s + split(g, j))
+    // ---- 0. all row inputs of this lane (channels 32 s + split(g, j)). Rows past
+    // the end of the sequence load row t0 (always valid) and are zeroed
+    // afterwards, so the loads carry no branch and all of them are in flight at
+    // once.
+    const int64_t ldoff = valid ? rowoff : ((int64_t)t0 * H + h) * D;
+    // (The input pointers are deliberately not __restrict__: loads through
+    // restrict-qualified read-only pointers may be moved freely, and the
+    // compiler would sink these towards their first uses, serialising them
+    // behind the gate scans. The empty asm statement below pins them.)
+    RowRaw<TG, NS> rla;
+    RowRaw<TIn, NS> rq, rk, rv;
+    rla.load(la, ldoff, g);  // first: the scans wait only for it
+    rq.load(q, ldoff, g);
+    rk.load(k, ldoff, g);
+    rv.load(v, ldoff, g);
+    const float bval = ld_in(beta, (int64_t)(valid ? t0 + r : t0) * H + h);
+    asm volatile("" ::: "memory");
     float xl[NS][8], q8[NS][8], k8[NS][8], v8[NS][8];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        float a4[4] = {0.f, 0.f, 0.f, 0.f}, b4[4] = {0.f, 0.f, 0.f, 0.f};
-        float c4[4] = {0.f, 0.f, 0.f, 0.f}, d4[4] = {0.f, 0.f, 0.f, 0.f};
-        float e4[4] = {0.f, 0.f, 0.f, 0.f}, f4[4] = {0.f, 0.f, 0.f, 0.f};
-        float g4[4] = {0.f, 0.f, 0.f, 0.f}, h4[4] = {0.f, 0.f, 0.f, 0.f};
-        if (valid) {
-            ld_in4(la, rowoff + 32 * s + 4 * g, a4);
-            ld_in4(la, rowoff + 32 * s + 16 + 4 * g, b4);
-            ld_in4(q, rowoff + 32 * s + 4 * g, c4);
-            ld_in4(q, rowoff + 32 * s + 16 + 4 * g, d4);
-            ld_in4(k, rowoff + 32 * s + 4 * g, e4);
-            ld_in4(k, rowoff + 32 * s + 16 + 4 * g, f4);
-            ld_in4(v, rowoff + 32 * s + 4 * g, g4);
-            ld_in4(v, rowoff + 32 * s + 16 + 4 * g, h4);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            xl[s][j] = a4[j] * LOG2E;
-            xl[s][4 + j] = b4[j] * LOG2E;
-            q8[s][j] = c4[j];
-            q8[s][4 + j] = d4[j];
-            k8[s][j] = e4[j];
-            k8[s][4 + j] = f4[j];
-            v8[s][j] = g4[j];
-            v8[s][4 + j] = h4[j];
-        }
-    }
-    if (g == 0) beta_s[r] = valid ? ld_in(beta, (int64_t)(t0 + r) * H + h) : 0.f;
+    rla.get(xl, valid, LOG2E);
+    rq.get(q8, valid, 1.f);
+    rk.get(k8, valid, 1.f);
+    rv.get(v8, valid, 1.f);
 
     // ---- 1. log2 gate scanned inside each 16-row block (lanes n of one DPP row)
 #pragma unroll
@@ -198,41 +229,49 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q,
                 f32x4_t{xl[s][4], xl[s][5], xl[s][6], xl[s][7]};
         }
     }
+    if (g == 0) beta_s[r] = valid ? bval : 0.f;
     __syncthreads();
 
-    // ---- 2. per-block channel constants from block sums, and the overflow guard
-    for (int idx = tid; idx < 15 * D; idx += 256) {
-        const int ty = idx / D, c = idx % D;
+    // ---- 2. per-block channel constants from block sums, and the overflow guard.
+    // Thread t serves channel t % D and every P-th of the 15 constants, P = 256 / D
+    // (the part t / D is uniform over a wave).
+    int bad = 0;
+    {
+        constexpr int P = 256 / D;
+        const int c = tid % D, part = tid / D;
         float tt[4], ff[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             tt[I] = tot[I * D + c];
             ff[I] = xf[I * D + c];
         }
-        if (ty < 4) {  // 2^G(a_I) = 2^(sum_{J<I} tot_J + xf_I)
-            float e = ff[ty];
-            for (int J = 0; J < ty; ++J) e += tt[J];
-            eA[ty * D + c] = ex2(e);
-        } else if (ty < 8) {  // 2^(G_last - G(a_I)) = 2^((tot_I - xf_I) + sum_{J>I} tot_J)
-            const int I = ty - 4;
-            float e = tt[I] - ff[I];
-            for (int J = I + 1; J < 4; ++J) e += tt[J];
-            eL[I * D + c] = ex2(e);
-        } else if (ty < 14) {  // 2^((tot_J - xf_J) + sum_{J<K<I} tot_K + xf_I)
-            const int p = ty - 8;
-            const int I = p < 1 ? 1 : (p < 3 ? 2 : 3);
-            const int J = p - pair_index(I, 0);
-            float e = tt[J] - ff[J] + ff[I];
-            for (int K = J + 1; K < I; ++K) e += tt[K];
-            cIJ[p * D + c] = ex2(e);
-        } else {
-            ws.gam[chh * D + c] = ex2(tt[0] + tt[1] + tt[2] + tt[3]);
-        }
-    }
-    int bad = 0;
-    if (tid < D) {
 #pragma unroll
-        for (int I = 0; I < 4; ++I) bad |= !(xf[I * D + tid] - tot[I * D + tid] <= GUARD);
+        for (int ty = 0; ty < 15; ++ty) {
+            if (ty % P != part) continue;
+            if (ty < 4) {  // 2^G(a_I) = 2^(sum_{J<I} tot_J + xf_I)
+                float e = ff[ty];
+                for (int J = 0; J < ty; ++J) e += tt[J];
+                eA[ty * D + c] = ex2(e);
+            } else if (ty < 8) {  // 2^(G_last - G(a_I)) = 2^((tot_I - xf_I) + sum_{J>I} tot_J)
+                const int I = ty - 4;
+                float e = tt[I] - ff[I];
+                for (int J = I + 1; J < 4; ++J) e += tt[J];
+                eL[I * D + c] = ex2(e);
+            } else if (ty < 14) {  // 2^((tot_J - xf_J) + sum_{J<K<I} tot_K + xf_I)
+                const int p = ty - 8;
+                const int I = p < 1 ? 1 : (p < 3 ? 2 : 3);
+                const int J = p - pair_index(I, 0);
+                float e = tt[J] - ff[J] + ff[I];
+                for (int K = J + 1; K < I; ++K) e += tt[K];
+                cIJ[p * D + c] = ex2(e);
+            } else {
+                ws.gam[chh * D + c] = ex2(tt[0] + tt[1] + tt[2] + tt[3]);
+            }
+        }
+        if (part == 0) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) bad |= !(ff[I] - tt[I] <= GUARD);
+        }
     }
     const bool slow = __syncthreads_or(bad) != 0;
 
@@ -372,7 +411,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* __restrict__ q,
                         xk[j] = ks[s][j];
                     }
                 }
-                AP::mma2(aq, AP::make(xq), ak, AP::make(xk), bkt[s]);
+                AP::mma_qk(aq, xq, ak, xk, bkt[s]);
             }
             const int blk = (J == I) ? I : 4 + pair_index(I, J);
 #pragma unroll
