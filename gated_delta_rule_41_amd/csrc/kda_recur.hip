@@ -176,9 +176,8 @@ __global__ __launch_bounds__(FUSED ? 320 : 192) void recur_kernel(const float* _
 
     if (FUSED && (wv == 1 || wv == 2)) {
         // ---------------- output waves: wave 1 + p computes the outputs of the
-        // chunks j = p (mod 2). It fetches chunk j's Q+ and A_qk at the start of
-        // iteration j and computes O_j in iteration j + 1, once the compute wave
-        // has left h_j and V_j in the exchange buffer j & 1.
+        // chunks j = p (mod 2) in iteration j + 1, once the compute wave has left
+        // h_j and V_j in the exchange buffer j & 1.
         const int p = wv - 1;
         const int tstart = cu ? cu[seq] : 0;
         const int len = cu ? cu[seq + 1] - tstart : T;
@@ -234,13 +233,16 @@ __global__ __launch_bounds__(FUSED ? 320 : 192) void recur_kernel(const float* _
                     }
                 }
         };
+        // chunk j's operands are fetched right after chunk j - 2's output is
+        // computed (in iteration j - 1), two chain steps before they are used
+        if (p < nch) issue(p);
         __builtin_amdgcn_s_barrier();
         if (p == 1 && nch > 0) __builtin_amdgcn_s_barrier();  // iteration 0 (chunk 0 is wave 1's)
         for (int j = p; j < nch; j += 2) {
-            issue(j);
-            __builtin_amdgcn_s_barrier();  // end of iteration j
+            __builtin_amdgcn_s_barrier();  // end of iteration j: h_j, V_j are in the buffer
             if (j + 1 < nch) {
                 consume(j, std::false_type{});
+                if (j + 2 < nch) issue(j + 2);
                 __builtin_amdgcn_s_barrier();  // end of iteration j + 1
             } else {
                 consume(j, std::true_type{});
