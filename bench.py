@@ -172,6 +172,29 @@ def time_decode(kda, dec, steps, warmup, hip, stream):
     return ms
 
 
+def copy_bandwidth(hip, stream, mib: int = 1024, reps: int = 20):
+    """Achievable HBM rate of a plain streaming kernel on this GPU (y = x * 1 over
+    ``mib`` MiB of fp32, read + write), as a measured reference beside the
+    datasheet peak."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    ev = Events(hip, 2)
+    ev.record(0, stream)
+    for _ in range(reps):
+        torch.mul(x, 1.0, out=y)
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(0, 1) / reps
+    ev.close()
+    del x, y
+    return 2 * 4 * n / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(case):
     """The oracle (fp64 token recurrence, OpenMP over (sequence, head, column
     block)) on the host cores, on the same prefill-4k inputs copied to host."""
@@ -352,10 +375,13 @@ def main(argv=None):
         NH = 256 * 32
         state_bytes = 2 * NH * 128 * 128 * 4
         alg = state_bytes + NH * (4 * 128 * 2 + 2 + 128 * 4)
+        copy_gbps = copy_bandwidth(hip, stream)
         out["decode"] = {"workload": "decode-256", "steps": args.decode_steps,
                          "ms_per_step": round(dms, 5), "state_GBps": round(state_bytes / dms / 1e6, 1),
                          "alg_GBps": round(alg / dms / 1e6, 1),
                          "hbm_frac": round(alg / dms / 1e6 / (PEAK_HBM / 1e9), 4),
+                         "measured_copy_GBps": round(copy_gbps, 1),
+                         "frac_of_measured_copy": round(alg / dms / 1e6 / copy_gbps, 4),
                          "roofline": {"kernel": "decode_kernel", "bound": "hbm",
                                       "achieved": round(alg / dms / 1e6, 1), "peak": PEAK_HBM / 1e9,
                                       "unit": "GB/s", "frac": round(alg / dms / 1e6 / (PEAK_HBM / 1e9), 4),
