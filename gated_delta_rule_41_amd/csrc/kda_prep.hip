@@ -68,10 +68,18 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 // LDS plan (bytes). Row strides are padded so that the matrix-core operand
 // reads (one 16-byte vector per lane, lanes = 16 rows x 4 k-groups) and the
 // transposing writes spread over the banks.
+//
+// With 16-bit operands (MT) the row -> channel transposes that K-^T, beta K+
+// and beta V need are done on the matrix cores: a product with a 0/1 selector
+// (exact) turns a lane-per-row operand into a lane-per-channel accumulator
+// tile, which is stored with one 8-byte access per lane. K-^T then goes
+// straight to the workspace, and beta K+ / beta V are kept as accumulator
+// tiles [column tile][row block][lane], the form the WY solve consumes.
 template <int D, bool F32>
 struct PrepSmem {
     using E = typename Pol<F32>::E;
     using AE = typename APol<F32>::E;
+    static constexpr bool MT = !F32;
     static constexpr int KT_STRIDE = D + 8;                  // Kt row (elements)
     static constexpr int KT_PLANE = 64 * KT_STRIDE;          // elements per hi / lo plane
     static constexpr int KM_STRIDE = 64 + 4;                 // K-^T staging row (elements)
@@ -81,13 +89,13 @@ struct PrepSmem {
     static constexpr int R1 = APol<F32>::PLANES * KT_PLANE * (int)sizeof(AE);  // Kt; later -W, slow-path scans
     static constexpr int R4a = D * KM_STRIDE * (int)sizeof(E);                // K-^T staging
     static constexpr int R4b = 10 * AK_BLOCK * 4;                             // A_kk lower blocks
-    static constexpr int R4 = R4a > R4b ? R4a : R4b;
-    static constexpr int R3 = D * BK_STRIDE * (int)sizeof(E);                 // beta K+, transposed
+    static constexpr int R4 = MT ? R4b : (R4a > R4b ? R4a : R4b);
+    static constexpr int R3 = MT ? 64 * D * (int)sizeof(E) : D * BK_STRIDE * (int)sizeof(E);  // beta K+, transposed
     static constexpr int CONST = 22 * D * 4;                                  // tot xf eA eL cIJ; later T_II
     static constexpr int BETA = 64 * 4;
     // beta V (transposed) and the -W staging share R1 once Kt is dead when both
     // fit (16-bit operands); otherwise beta V gets a region of its own
-    static constexpr int RBV = D * BK_STRIDE * (int)sizeof(E);
+    static constexpr int RBV = MT ? 64 * D * (int)sizeof(E) : D * BK_STRIDE * (int)sizeof(E);
     static constexpr bool BV_IN_R1 = RBV + 64 * D * (int)sizeof(E) <= R1;
     static constexpr int R5 = BV_IN_R1 ? 0 : RBV;
     static constexpr int BYTES = R1 + R4 + R3 + CONST + BETA + R5;
@@ -160,13 +168,13 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
 
     extern __shared__ __align__(16) char smem[];
     AE* Kt_s = reinterpret_cast<AE*>(smem);                     // [planes][64][KTS] keys 2^(G_aJ - G)
-    E* Bv_t = reinterpret_cast<E*>(smem + SM::BV_AT);           // [D][BKS] beta V transposed
+    E* Bv_t = reinterpret_cast<E*>(smem + SM::BV_AT);           // beta V transposed ([D][BKS] or tiles)
     E* Ws_s = reinterpret_cast<E*>(smem + SM::WS_AT);           // [64][NS][4][8] -W (after Kt is dead)
     float* xl_slow = reinterpret_cast<float*>(smem);            // [64][D] slow path: local scans
     char* r4 = smem + SM::R1;
     E* Km_s = reinterpret_cast<E*>(r4);                         // [D][KMS] K-^T in split row order
     float* Akk_s = reinterpret_cast<float*>(r4);                // 10 blocks [16][AKS]: diag I at I, (I,J) at 4+pair
-    E* Bk_t = reinterpret_cast<E*>(smem + SM::R1 + SM::R4);     // [D][BKS] beta K+ transposed
+    E* Bk_t = reinterpret_cast<E*>(smem + SM::R1 + SM::R4);     // beta K+ transposed ([D][BKS] or tiles)
     float* cst = reinterpret_cast<float*>(smem + SM::R1 + SM::R4 + SM::R3);
     float* tot = cst;                 // [4][D]  sum of the block's log2 gates
     float* xf = tot + 4 * D;          // [4][D]  log2 gate of the block's first row
@@ -275,6 +283,40 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     }
     const bool slow = __syncthreads_or(bad) != 0;
 
+    // 0/1 selectors for the matrix-core transposes (16-bit operands): with A a
+    // lane-per-row operand over a 32-channel slice, A sel[hf] is the 16 x 16
+    // block of channels 16 hf .. 16 hf + 15 in accumulator layout (lane n holds
+    // channel 16 hf + n, rows 4 g .. 4 g + 3), exactly
+    Frag sel[2];
+    if constexpr (SM::MT) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            float x[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) x[jj] = (g == (n >> 2) && jj == 4 * hf + (n & 3)) ? 1.f : 0.f;
+            sel[hf] = P::make(x);
+        }
+    }
+    // transposes one slice s of a lane-per-row vector: K-^T blocks to the
+    // workspace (8 bytes per lane at rows 16 w + 4 g + (0..3) of channel
+    // 32 s + 16 hf + n, in the split row order), or beta-scaled blocks to
+    // accumulator tiles [column tile][row block][lane] in LDS
+    auto tr_slice = [&](const float (&x)[8], int s, E* km_dst, E* tile_dst) {
+        const Frag a = P::make(x);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+            P::mma(t, a, sel[hf]);
+            u32x2_t pk;
+            pk[0] = (uint32_t)f2h(t[0]) | ((uint32_t)f2h(t[1]) << 16);
+            pk[1] = (uint32_t)f2h(t[2]) | ((uint32_t)f2h(t[3]) << 16);
+            if (km_dst)
+                *reinterpret_cast<u32x2_t*>(km_dst + (32 * s + 16 * hf + n) * 64 + 32 * (w >> 1) + 8 * g + 4 * (w & 1)) = pk;
+            else
+                *reinterpret_cast<u32x2_t*>(tile_dst + (((2 * s + hf) * 4 + w) * 64 + l) * 4) = pk;
+        }
+    };
+
     // ---- 3. gated scalings
     const float br = beta_s[r];
     float qs[NS][8], ks[NS][8];  // q 2^(G - G_aw), k 2^(G - G_aw)  (fast path)
@@ -285,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     for (int s = 0; s < NS; ++s) {
         float qpv[8];
         if (!slow) {
-            float xf8[8], ea8[8], el8[8], ktv[8];
+            float xf8[8], ea8[8], el8[8], ktv[8], kmv[8], bkv[8];
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const int c0 = 32 * s + 16 * hf + 4 * g;
@@ -309,11 +351,20 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
                 ks[s][j] = k8[s][j] * e;
                 ktv[j] = k8[s][j] * ei;
                 qpv[j] = qs[s][j] * ea8[j];
-                Km_s[c * KMS + kmpos] = P::from_f(ktv[j] * el8[j]);
-                Bk_t[c * BKS + r] = P::from_f(ks[s][j] * ea8[j] * br);
+                kmv[j] = ktv[j] * el8[j];
+                bkv[j] = ks[s][j] * ea8[j] * br;
+                if constexpr (!SM::MT) {
+                    Km_s[c * KMS + kmpos] = P::from_f(kmv[j]);
+                    Bk_t[c * BKS + r] = P::from_f(bkv[j]);
+                }
+            }
+            if constexpr (SM::MT) {
+                tr_slice(kmv, s, km_out, nullptr);
+                tr_slice(bkv, s, nullptr, Bk_t);
             }
             AP::store(Kt_s + r * KTS + s * 32 + g * 8, SM::KT_PLANE, AP::make(ktv));
         } else {
+            float kmv[8], bkv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int c = 32 * s + kslot(g, j);
@@ -322,20 +373,28 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
                 for (int J = w + 1; J < 4; ++J) post += tot[J * D + c];
                 const float eg = exp2f(pre + xl[s][j]);  // 2^G_r
                 qpv[j] = q8[s][j] * eg;
-                km_out[c * 64 + kmpos] = P::from_f(k8[s][j] * exp2f(post));
-                Bk_t[c * BKS + r] = P::from_f(k8[s][j] * eg * br);
+                kmv[j] = k8[s][j] * exp2f(post);
+                bkv[j] = k8[s][j] * eg * br;
+                if constexpr (!SM::MT) {
+                    km_out[c * 64 + kmpos] = P::from_f(kmv[j]);
+                    Bk_t[c * BKS + r] = P::from_f(bkv[j]);
+                }
                 xl_slow[r * D + c] = xl[s][j];
                 qs[s][j] = 0.f;
                 ks[s][j] = 0.f;
+            }
+            if constexpr (SM::MT) {
+                tr_slice(kmv, s, km_out, nullptr);
+                tr_slice(bkv, s, nullptr, Bk_t);
             }
         }
         P::store(qp_out + (r * NS + s) * 32 + g * 8, P::make(qpv));
     }
     __syncthreads();
 
-    // ---- 3b. K-^T to the workspace (fast path) / exact gated products (slow path)
+    // ---- 3b. K-^T to the workspace (fast path, fp32 operands) / exact gated products (slow path)
     float akk_sl[16], aqk_sl[16];
-    if (!slow) {
+    if (!slow && !SM::MT) {
         for (int idx = tid; idx < D * 16; idx += 256) {  // 4 elements per item
             const int c = idx >> 4, qd = idx & 15;
             const E* src = Km_s + c * KMS + 4 * qd;
@@ -345,7 +404,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
             else
                 *reinterpret_cast<u32x2_t*>(dst) = *reinterpret_cast<const u32x2_t*>(src);
         }
-    } else {
+    } else if (slow) {
         // pair (rr, ii) = (p >> 6, p & 63), p = tid + 256 m; exponent
         // G_rr - G_ii = xl_rr - xl_ii + sum of the whole-block totals between them
 #pragma unroll 1
@@ -369,7 +428,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
             akk_sl[m] = ii < rr ? sk * beta_s[rr] : 0.f;
         }
     }
-    __syncthreads();
+    if (slow || !SM::MT) __syncthreads();  // (block-uniform condition)
 
     // ---- 3c. A_qk (straight to the workspace) and A_kk (LDS, lower blocks only)
     E* aqk_out = ws.aqk + chh * 64 * 64;
@@ -439,9 +498,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
 
     // beta V, transposed like beta K+, into the now free Kt region
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < NS; ++s) {
+        if constexpr (SM::MT) {
+            float bvv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) Bv_t[(32 * s + kslot(g, j)) * BKS + r] = P::from_f(v8[s][j] * br);
+            for (int j = 0; j < 8; ++j) bvv[j] = v8[s][j] * br;
+            tr_slice(bvv, s, nullptr, Bv_t);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) Bv_t[(32 * s + kslot(g, j)) * BKS + r] = P::from_f(v8[s][j] * br);
+        }
+    }
 
     // ---- 4a. diagonal-block inverses T_II = (I + A_II)^-1 by row forward substitution (wave 0)
     if (w == 0) {
@@ -499,7 +566,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
             for (int tt = 0; tt < TPW; ++tt) {
                 const int ct = (w & 1) * TPW + tt;  // column tile inside W (waves 0-1) or U (waves 2-3)
                 f32x4_t Y;
-                {
+                if constexpr (SM::MT) {
+                    const u32x2_t bb =
+                        *reinterpret_cast<const u32x2_t*>((isW ? Bk_t : Bv_t) + ((ct * 4 + I) * 64 + l) * 4);
+                    Y = f32x4_t{h2f(bb[0] & 0xffffu), h2f(bb[0] >> 16), h2f(bb[1] & 0xffffu), h2f(bb[1] >> 16)};
+                } else {
                     const E* bsrc = (isW ? Bk_t : Bv_t) + (16 * ct + n) * BKS + 16 * I + 4 * g;
                     if constexpr (F32) {
                         Y = *reinterpret_cast<const f32x4_t*>(bsrc);
