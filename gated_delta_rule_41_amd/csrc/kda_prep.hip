@@ -436,8 +436,44 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
         const int s2 = cc >> 5, c2 = cc & 31;
         aqk_out[(rr * 2 + s2) * 32 + 8 * ((c2 & 15) >> 2) + 4 * (c2 >> 4) + (c2 & 3)] = P::from_f(x);
     };
-    if (!slow) {
-        const int I = w;
+    // Wave I computes the blocks (I, J <= I) of both matrices, slice by slice
+    // over the channels so that the operands of every block of a slice are
+    // read together (I is made a compile-time constant per wave).
+    auto products = [&](auto Ic) {
+        constexpr int I = decltype(Ic)::value;
+        f32x4_t aq[I + 1], ak[I + 1];
+#pragma unroll
+        for (int J = 0; J <= I; ++J) {
+            aq[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            ak[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            AFrag bkt[I + 1];
+#pragma unroll
+            for (int J = 0; J <= I; ++J)
+                bkt[J] = AP::load(Kt_s + (16 * J + n) * KTS + s * 32 + g * 8, SM::KT_PLANE);
+            f32x4_t c0[I + 1], c1[I + 1];
+#pragma unroll
+            for (int J = 0; J < I; ++J) {
+                const float* cp = cIJ + pair_index(I, J) * D + 32 * s + 4 * g;
+                c0[J] = *reinterpret_cast<const f32x4_t*>(cp);
+                c1[J] = *reinterpret_cast<const f32x4_t*>(cp + 16);
+            }
+#pragma unroll
+            for (int J = 0; J <= I; ++J) {
+                float xq[8], xk[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float a = J < I ? c0[J][j] : 1.f, b = J < I ? c1[J][j] : 1.f;
+                    xq[j] = qs[s][j] * a;
+                    xk[j] = ks[s][j] * a;
+                    xq[4 + j] = qs[s][4 + j] * b;
+                    xk[4 + j] = ks[s][4 + j] * b;
+                }
+                AP::mma_qk(aq[J], xq, ak[J], xk, bkt[J]);
+            }
+        }
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             if (J > I) {
@@ -445,42 +481,23 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
                 for (int i = 0; i < 4; ++i) aqk_put(16 * I + 4 * g + i, 16 * J + n, 0.f);
                 continue;
             }
-            f32x4_t aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
-            AFrag bkt[NS];
-#pragma unroll
-            for (int s = 0; s < NS; ++s) bkt[s] = AP::load(Kt_s + (16 * J + n) * KTS + s * 32 + g * 8, SM::KT_PLANE);
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                float xq[8], xk[8];
-                if (J < I) {
-                    const float* cp = cIJ + pair_index(I, J) * D + 32 * s + 4 * g;
-                    const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(cp);
-                    const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(cp + 16);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        xq[j] = qs[s][j] * c0[j];
-                        xk[j] = ks[s][j] * c0[j];
-                        xq[4 + j] = qs[s][4 + j] * c1[j];
-                        xk[4 + j] = ks[s][4 + j] * c1[j];
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        xq[j] = qs[s][j];
-                        xk[j] = ks[s][j];
-                    }
-                }
-                AP::mma_qk(aq, xq, ak, xk, bkt[s]);
-            }
             const int blk = (J == I) ? I : 4 + pair_index(I, J);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rl = 4 * g + i;  // row inside the block
                 const bool lo_incl = (J < I) || (n <= rl);
                 const bool lo_strict = (J < I) || (n < rl);
-                aqk_put(16 * I + rl, 16 * J + n, lo_incl ? aq[i] : 0.f);
-                Akk_s[blk * AKB + rl * AKS + n] = lo_strict ? ak[i] * beta_s[16 * I + rl] : 0.f;
+                aqk_put(16 * I + rl, 16 * J + n, lo_incl ? aq[J][i] : 0.f);
+                Akk_s[blk * AKB + rl * AKS + n] = lo_strict ? ak[J][i] * beta_s[16 * I + rl] : 0.f;
             }
+        }
+    };
+    if (!slow) {
+        switch (w) {
+            case 0: products(std::integral_constant<int, 0>{}); break;
+            case 1: products(std::integral_constant<int, 1>{}); break;
+            case 2: products(std::integral_constant<int, 2>{}); break;
+            default: products(std::integral_constant<int, 3>{}); break;
         }
     } else {
 #pragma unroll
