@@ -92,7 +92,7 @@ struct PrepSmem {
     static constexpr int R4 = MT ? R4b : (R4a > R4b ? R4a : R4b);
     static constexpr int R3 = MT ? 64 * D * (int)sizeof(E) : D * BK_STRIDE * (int)sizeof(E);  // beta K+, transposed
     static constexpr int CONST = 22 * D * 4;                                  // tot xf eA eL cIJ; later T_II
-    static constexpr int BETA = 64 * 4;
+    static constexpr int BETA = 64 * 4 + 16;  // beta per row, then one overflow flag per wave
     // beta V (transposed) and the -W staging share R1 once Kt is dead when both
     // fit (16-bit operands); otherwise beta V gets a region of its own
     static constexpr int RBV = MT ? 64 * D * (int)sizeof(E) : D * BK_STRIDE * (int)sizeof(E);
@@ -183,6 +183,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     float* cIJ = eL + 4 * D;          // [6][D]  2^(G(first row of I) - G(first row of J)), I > J
     float* Td_s = cst;                // [4][16][AKS] T_II, after the constants are dead
     float* beta_s = cst + 22 * D;     // [64]
+    int* slow_s = reinterpret_cast<int*>(beta_s + 64);  // [4] per-wave overflow flags
 
     const int gc = blockIdx.x;
     const int h = blockIdx.y;
@@ -281,7 +282,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
             for (int I = 0; I < 4; ++I) bad |= !(ff[I] - tt[I] <= GUARD);
         }
     }
-    const bool slow = __syncthreads_or(bad) != 0;
+    // one flag per wave (a ballot), so the barrier that publishes the
+    // constants also publishes the guard
+    const bool wave_bad = __ballot(bad) != 0;
+    if (l == 0) slow_s[w] = wave_bad;
+    __syncthreads();
+    const bool slow = (slow_s[0] | slow_s[1] | slow_s[2] | slow_s[3]) != 0;
 
     // 0/1 selectors for the matrix-core transposes (16-bit operands): with A a
     // lane-per-row operand over a 32-channel slice, A sel[hf] is the 16 x 16
@@ -300,8 +306,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     // transposes one slice s of a lane-per-row vector: K-^T blocks to the
     // workspace (8 bytes per lane at rows 16 w + 4 g + (0..3) of channel
     // 32 s + 16 hf + n, in the split row order), or beta-scaled blocks to
-    // accumulator tiles [column tile][row block][lane] in LDS
-    auto tr_slice = [&](const float (&x)[8], int s, E* km_dst, E* tile_dst) {
+    // accumulator tiles [column tile][row block][lane] in LDS (the destination
+    // kind is a compile-time choice, so the phase stays one basic block)
+    auto tr_slice = [&](const float (&x)[8], int s, auto to_km, E* dst) {
         const Frag a = P::make(x);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -310,10 +317,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
             u32x2_t pk;
             pk[0] = (uint32_t)f2h(t[0]) | ((uint32_t)f2h(t[1]) << 16);
             pk[1] = (uint32_t)f2h(t[2]) | ((uint32_t)f2h(t[3]) << 16);
-            if (km_dst)
-                *reinterpret_cast<u32x2_t*>(km_dst + (32 * s + 16 * hf + n) * 64 + 32 * (w >> 1) + 8 * g + 4 * (w & 1)) = pk;
+            if constexpr (decltype(to_km)::value)
+                *reinterpret_cast<u32x2_t*>(dst + (32 * s + 16 * hf + n) * 64 + 32 * (w >> 1) + 8 * g + 4 * (w & 1)) = pk;
             else
-                *reinterpret_cast<u32x2_t*>(tile_dst + (((2 * s + hf) * 4 + w) * 64 + l) * 4) = pk;
+                *reinterpret_cast<u32x2_t*>(dst + (((2 * s + hf) * 4 + w) * 64 + l) * 4) = pk;
         }
     };
 
@@ -323,11 +330,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     E* qp_out = ws.qp + chh * 64 * D;
     E* km_out = ws.km + chh * D * 64;
     const int kmpos = 32 * (r >> 5) + split_pos(r);
+    // fast and slow paths each cover every slice inside one branch
+    if (!slow) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        float qpv[8];
-        if (!slow) {
-            float xf8[8], ea8[8], el8[8], ktv[8], kmv[8], bkv[8];
+        for (int s = 0; s < NS; ++s) {
+            float xf8[8], ea8[8], el8[8], ktv[8], kmv[8], bkv[8], qpv[8];
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const int c0 = 32 * s + 16 * hf + 4 * g;
@@ -359,12 +366,16 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
                 }
             }
             if constexpr (SM::MT) {
-                tr_slice(kmv, s, km_out, nullptr);
-                tr_slice(bkv, s, nullptr, Bk_t);
+                tr_slice(kmv, s, std::true_type{}, km_out);
+                tr_slice(bkv, s, std::false_type{}, Bk_t);
             }
             AP::store(Kt_s + r * KTS + s * 32 + g * 8, SM::KT_PLANE, AP::make(ktv));
-        } else {
-            float kmv[8], bkv[8];
+            P::store(qp_out + (r * NS + s) * 32 + g * 8, P::make(qpv));
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            float kmv[8], bkv[8], qpv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int c = 32 * s + kslot(g, j);
@@ -384,11 +395,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
                 ks[s][j] = 0.f;
             }
             if constexpr (SM::MT) {
-                tr_slice(kmv, s, km_out, nullptr);
-                tr_slice(bkv, s, nullptr, Bk_t);
+                tr_slice(kmv, s, std::true_type{}, km_out);
+                tr_slice(bkv, s, std::false_type{}, Bk_t);
             }
+            P::store(qp_out + (r * NS + s) * 32 + g * 8, P::make(qpv));
         }
-        P::store(qp_out + (r * NS + s) * 32 + g * 8, P::make(qpv));
     }
     __syncthreads();
 
@@ -520,7 +531,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
             float bvv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) bvv[j] = v8[s][j] * br;
-            tr_slice(bvv, s, nullptr, Bv_t);
+            tr_slice(bvv, s, std::false_type{}, Bv_t);
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) Bv_t[(32 * s + kslot(g, j)) * BKS + r] = P::from_f(v8[s][j] * br);
