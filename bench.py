@@ -32,7 +32,9 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA prefill tokens/s + TFLOP/s (% MFMA peak); decode state GB/s (% HBM peak)"
 PEAK_BF16 = 2.5e15       # dense bf16/fp16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12        # HBM3E, B/s
-# per token-head, d = 128, chunk 64 ("Work and bytes")
+# per token-head, d = 128, chunk 64: flops of the chunkwise form (three d x d
+# state products, five triangular chunk products, the forward substitution) and
+# the operator's compulsory HBM bytes (its inputs and its output, once each)
 FLOP_PER_TOKEN_HEAD = 140629
 ALG_BYTES_PER_TOKEN_HEAD = 1538            # q,k,v,log_alpha bf16 + beta bf16 + o fp32
 KERNEL_BYTES_PER_TOKEN_HEAD = {            # compulsory traffic of each prefill kernel
@@ -316,8 +318,8 @@ def main(argv=None):
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding is a design in DESIGN.md, not built", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is not implemented", file=sys.stderr)
         return 2
 
     import torch
