@@ -48,8 +48,9 @@ struct RecurPlan {
     // with the fused output: two buffers of (h_n slab [D x 16], V_new slab [64 x 16])
     static constexpr int HVS = (D * 16 + 64 * 16) * (int)sizeof(E);
     static constexpr int HV = FUSED ? 2 * HVS : 0;
-    static constexpr int RING = (4 * SLOT + HV <= 160 * 1024) ? 4 : 2;
-    static constexpr int LDS = RING * SLOT + HV;
+    static constexpr int WARM = FUSED ? 256 : 0;  // target of the L2 warm-up loads (never read)
+    static constexpr int RING = (4 * SLOT + HV + WARM <= 160 * 1024) ? 4 : 2;
+    static constexpr int LDS = RING * SLOT + HV + WARM;
     static_assert(LDS <= 160 * 1024, "LDS budget");
     // global->LDS loads per chunk and producer wave (16 bytes per lane, 1 KiB per load)
     static constexpr int OPS_W = FB / 1024, OPS_U = UB / 1024, OPS_G = 1;
@@ -58,6 +59,15 @@ struct RecurPlan {
     static constexpr int OPS = OPS0 > OPS1 ? OPS0 : OPS1;
     static_assert((RING - 2) * OPS <= 63, "in-flight loads must fit the 6-bit vmcnt");
     static_assert(FB % 1024 == 0 && UB % 1024 == 0 && GB <= GPAD, "slot parts are whole 1 KiB loads");
+    // L2 warm-up (fused kernel): the 128-byte lines of one chunk-head's -W, K-^T,
+    // Q+ and A_qk are shared out over the head's D/16 slab workgroups; a second
+    // load covers this slab's U and the head's gamma
+    static constexpr int LINES_W = FB / 128, LINES_A = 64 * 64 * (int)sizeof(E) / 128;
+    static constexpr int LINES = 3 * LINES_W + LINES_A;
+    static constexpr int LINES_PER = (LINES + D / 16 - 1) / (D / 16);
+    static constexpr int LINES_U = UB / 128, LINES_G = GB / 128;
+    static_assert(!FUSED || (LINES_PER <= 64 && LINES_U + LINES_G <= 64), "two warm-up loads per chunk");
+    static constexpr int AHEAD = 3;  // chunks warmed ahead of the compute wave (2..6 measured; 3 best)
 };
 
 // granule swizzle of the ring slots; fp32 fragments span two granules, so the
@@ -132,14 +142,45 @@ __device__ __forceinline__ void produce(const Ws<typename Pol<F32>::E>& ws, int6
     }
 }
 
+// L2 warm-up: 4-byte global->LDS loads, one per 128-byte line, touch this
+// workgroup's share of one chunk's -W, K-^T, Q+, A_qk lines and its own U and
+// gamma lines, so that the producers' DMA and the output waves' loads of that
+// chunk, a few chain steps later, hit the XCD's L2 instead of HBM. The LDS
+// target is a scratch area nobody reads.
+template <int D, bool F32, bool FUSED>
+__device__ __forceinline__ void warm_chunk(const Ws<typename Pol<F32>::E>& ws, int64_t chh, int ct, int l,
+                                           char* dst) {
+    using PL = RecurPlan<D, F32, FUSED>;
+    int L = ct * PL::LINES_PER + (l < PL::LINES_PER ? l : PL::LINES_PER - 1);
+    L = L < PL::LINES ? L : PL::LINES - 1;
+    const char* p;
+    if (L < PL::LINES_W)
+        p = reinterpret_cast<const char*>(ws.wn + chh * 64 * D) + L * 128;
+    else if (L < 2 * PL::LINES_W)
+        p = reinterpret_cast<const char*>(ws.km + chh * 64 * D) + (L - PL::LINES_W) * 128;
+    else if (L < 3 * PL::LINES_W)
+        p = reinterpret_cast<const char*>(ws.qp + chh * 64 * D) + (L - 2 * PL::LINES_W) * 128;
+    else
+        p = reinterpret_cast<const char*>(ws.aqk + chh * 64 * 64) + (L - 3 * PL::LINES_W) * 128;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)p,
+                                     (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+    const int m = l < PL::LINES_U + PL::LINES_G ? l : 0;
+    const char* pu = m < PL::LINES_U
+                         ? reinterpret_cast<const char*>(ws.u + chh * 64 * D + (int64_t)ct * 4 * 64 * 4) + m * 128
+                         : reinterpret_cast<const char*>(ws.gam + chh * D) + (m - PL::LINES_U) * 128;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)pu,
+                                     (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+}
+
 // With FUSED, two more waves compute each chunk's output O = Q+ h_n + A_qk V_new
 // for this slab's 16 columns, one chunk behind the compute wave: the compute
 // wave leaves h_n and V_new in an LDS buffer (two buffers, by chunk parity)
 // instead of the workspace, and the output waves, taking alternate chunks,
 // fetch Q+ and A_qk into registers one chunk ahead. Waves: 0 compute, 1-2
-// output, 3-4 producers. Every wave executes the same 1 + nch barriers.
+// output, 3-4 producers, 5 L2 warm-up. Every wave executes the same 1 + nch
+// barriers.
 template <int D, bool F32, bool FUSED, bool OUT_F32>
-__global__ __launch_bounds__(FUSED ? 320 : 192) void recur_kernel(const float* __restrict__ s0,
+__global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* __restrict__ s0,
                                                                   float* __restrict__ s_final,
                                                                   const int32_t* __restrict__ cu, int N, int T,
                                                                   int H, Ws<typename Pol<F32>::E> ws,
@@ -248,6 +289,22 @@ __global__ __launch_bounds__(FUSED ? 320 : 192) void recur_kernel(const float* _
                 consume(j, std::true_type{});
             }
         }
+        return;
+    }
+
+    if (FUSED && wv == 5) {
+        // ---------------- L2 warm-up wave: chunk c + AHEAD during chunk c; it
+        // never waits for its loads except to bound the counter and at the end
+        char* wdst = hvbase + PL::HV;
+        const int pre = nch < PL::AHEAD ? nch : PL::AHEAD;
+        for (int c = 0; c < pre; ++c) warm_chunk<D, F32, FUSED>(ws, (int64_t)(co + c) * H + h, ct, l, wdst);
+        __builtin_amdgcn_s_barrier();
+        for (int c = 0; c < nch; ++c) {
+            if (c + PL::AHEAD < nch) warm_chunk<D, F32, FUSED>(ws, (int64_t)(co + c + PL::AHEAD) * H + h, ct, l, wdst);
+            wait_vm<48>();
+            __builtin_amdgcn_s_barrier();
+        }
+        wait_vm<0>();  // the LDS target stays allocated until the loads have landed
         return;
     }
 
@@ -370,7 +427,7 @@ static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     auto kern = recur_kernel<D, F32, FUSED, OUT_F32>;
     const hipError_t e = allow_dynamic_lds((const void*)kern, PL::LDS);
     if (e != hipSuccess) return e;
-    dim3 grid(NU * NT), block(FUSED ? 320 : 192);
+    dim3 grid(NU * NT), block(FUSED ? 384 : 192);
     hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.cu, a.N, a.T, a.H, ws, a.o);
     return hipGetLastError();
 }
