@@ -44,6 +44,16 @@ def test_prefill_4k_workload(wl):
     check_prefill(case, TOL_BF16)
 
 
+@pytest.mark.parametrize("d,dt,H", [(64, torch.bfloat16, 32), (128, torch.float32, 8)])
+def test_prefill_4k_shape_other_paths(d, dt, H):
+    """The prefill-4k shape (T = 4096, 64 chained chunks) on the paths the
+    benchmark does not time: d = 64 with bf16 inputs (fused output, four slab
+    workgroups per head) and fp32 inputs (recursion and output kernels apart,
+    h_n and V_new through the workspace)."""
+    case = ki.make_prefill("prefill-4k", DEV, H=H, dk=d, dv=d, dtype=dt)
+    check_prefill(case, tol_for(dt), label=f"prefill-4k shape d={d} {dt}")
+
+
 def test_varlen_small_with_empty_sequences():
     lens = [1, 15, 16, 17, 0, 63, 64, 65, 130, 0, 4097]
     case = ki.make_prefill("varlen-16", DEV, lengths=lens, H=3, s0_std=0.02)
