@@ -14,7 +14,8 @@
 //     vectors are both tied to the key): A_kk[r,i] = beta_r sum_c k_rc k_ic
 //     2^(G_rc - G_ic) (i < r) and A_qk[r,i] = sum_c q_rc k_ic 2^(G_rc - G_ic)
 //     (i <= r), with secondary chunking: block (I, J) of 16 x 16 is one
-//     matrix-core product (split bf16 with bf16 inputs) of
+//     matrix-core product (with bf16 inputs: split bf16 for A_qk, plain bf16
+//     for A_kk, which only feeds the UT transform) of
 //     (x_r 2^(G_r - G_aI)) 2^(G_aI - G_aJ) by k_i 2^(G_aJ - G_i), a_I = first
 //     row of block I. Left factors are <= 1, right factors lie in [1, 2^R_J]
 //     with R_J the sub-chunk's gate range; a range above GUARD (log2 units)
