@@ -91,11 +91,18 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _check(t: torch.Tensor, name: str, device: torch.device):
-    if not t.is_cuda or t.device != device:
-        raise ValueError(f"{name} must be on {device}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+def _check(items, device: torch.device):
+    """items: (name, tensor, expected shape or None). The library takes sizes from
+    q and v only and trusts every other buffer to match them, so every shape is
+    checked first (this needs no GPU), then the device and layout of each."""
+    for name, t, shape in items:
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    for name, t, _ in items:
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} must be on {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
 
 
 def workspace_size(N: int, T_total: int, H: int, dk: int, dv: int,
@@ -126,23 +133,31 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     """
     lib = _load()
     dev = q.device
-    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
-        _check(t, name, dev)
     if q.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, log_alpha must be [T, H, dk] and v [T, H, dv]")
     T, H, dk = q.shape
     dv = v.shape[2]
+    items = [("q", q, (T, H, dk)), ("k", k, (T, H, dk)), ("v", v, (T, H, dv)),
+             ("log_alpha", log_alpha, (T, H, dk)), ("beta", beta, (T, H))]
     if cu_seqlens is not None:
-        _check(cu_seqlens, "cu_seqlens", dev)
-        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
-            raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 >= 2 offsets")
+        items.append(("cu_seqlens", cu_seqlens, None))
         N = cu_seqlens.numel() - 1
     else:
         N = 1
     if initial_state is not None:
-        _check(initial_state, "initial_state", dev)
-        if initial_state.dtype != torch.float32:
-            raise TypeError("initial_state must be float32")
+        items.append(("initial_state", initial_state, (N, H, dk, dv)))
+    if o is not None:
+        items.append(("o", o, (T, H, dv)))
+    if final_state is not None:
+        items.append(("final_state", final_state, (N, H, dk, dv)))
+    if workspace is not None:
+        items.append(("workspace", workspace, None))
+    _check(items, dev)
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
     in_dt = _dtype_code(q, "q")
     gate_dt = _dtype_code(log_alpha, "log_alpha")
     if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != log_alpha.dtype:
@@ -159,7 +174,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
             _ptr(cu_seqlens), N, T, H, dk, dv, in_dt, gate_dt, out_dt, _ptr(o),
-            _ptr(final_state), _ptr(workspace), workspace.numel(), _stream(dev))
+            _ptr(final_state), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(dev))
     if events is None:
         st = lib.kda_chunk_fwd(*args)
     else:
@@ -178,13 +194,17 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: to
     updated in place. Returns o [N, H, dv]."""
     lib = _load()
     dev = q.device
-    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta),
-                    ("state", state)):
-        _check(t, name, dev)
-    if state.dtype != torch.float32:
-        raise TypeError("state must be float32")
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, log_alpha must be [N, H, dk] and v [N, H, dv]")
     N, H, dk = q.shape
     dv = v.shape[2]
+    items = [("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("v", v, (N, H, dv)),
+             ("log_alpha", log_alpha, (N, H, dk)), ("beta", beta, (N, H)), ("state", state, (N, H, dk, dv))]
+    if o is not None:
+        items.append(("o", o, (N, H, dv)))
+    _check(items, dev)
+    if state.dtype != torch.float32:
+        raise TypeError("state must be float32")
     if o is None:
         o = torch.empty(N, H, dv, dtype=out_dtype, device=dev)
     st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state),
