@@ -98,6 +98,13 @@ size_t esize(int d) { return d == KDA_F32 ? 4 : 2; }
 
 bool head_ok(int32_t dk, int32_t dv) { return (dk == 64 && dv == 64) || (dk == 128 && dv == 128); }
 
+// T_total < 2^31 tokens and H <= 2^16 heads keep every byte count below 2^64;
+// the state recursion launches N * H * dv / 16 <= N * H * 8 workgroups
+bool chunk_sizes_ok(int32_t N, int64_t T_total, int32_t H) {
+    if (N <= 0 || H <= 0 || H > (1 << 16) || T_total < 0 || T_total >= (int64_t(1) << 31)) return false;
+    return (int64_t)N * H * 8 < (int64_t(1) << 31);
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,7 +128,7 @@ const char* kda_status_str(int s) {
 kda_status kda_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
                                         kda_dtype in_dtype, size_t* bytes) {
     if (!bytes) return KDA_ERR_NULL;
-    if (N <= 0 || H <= 0 || T_total < 0 || T_total >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
     if (!head_ok(dk, dv) || !dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
     // the workspace is sized for the packed case; it also covers one sequence
     const int64_t NC = chunk_capacity(N, T_total, true);
@@ -145,7 +152,7 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
                                kda_dtype in_dtype, kda_dtype gate_dtype, kda_dtype out_dtype, void* o,
                                float* final_state, void* workspace, size_t workspace_bytes, void* stream,
                                void* const* events) {
-    if (N <= 0 || H <= 0 || T_total < 0 || T_total >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
     if (T_total > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
     if (!cu_seqlens && N != 1) return KDA_ERR_SHAPE;
     if (!head_ok(dk, dv) || !dtype_ok(in_dtype) || !dtype_ok(gate_dtype) || !dtype_ok(out_dtype))

@@ -29,6 +29,8 @@
  *    beta [T, H]; o [T, H, dv]; states [N, H, dk, dv] fp32 (dv fastest).
  *  - No query scaling is applied (callers pre-scale q if they want 1/sqrt(dk)).
  *  - Supported head sizes: (dk, dv) in {(64, 64), (128, 128)}.
+ *  - Size limits (KDA_ERR_SHAPE beyond them): prefill T_total < 2^31,
+ *    H <= 65536 and N * H * 8 < 2^31; decode N * H < 2^31.
  *  - Supported dtypes: in_dtype (q, k, v) and gate_dtype (log_alpha, beta) are
  *    each KDA_BF16 or KDA_F32; out_dtype (o) KDA_F32 or KDA_BF16. With
  *    in_dtype == KDA_BF16 the chunk products run on 16-bit matrix cores with

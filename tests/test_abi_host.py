@@ -88,6 +88,9 @@ def test_chunk_fwd_validation():
     assert chunk_call(T=-1) == SHAPE
     assert chunk_call(T=1 << 31) == SHAPE
     assert chunk_call(N=2) == SHAPE  # several sequences need cu_seqlens
+    assert chunk_call(H=(1 << 16) + 1) == SHAPE
+    f0 = Fake()
+    assert chunk_call(N=1 << 15, H=1 << 13, cu=f0()) == SHAPE  # N * H * 8 state-slab workgroups >= 2^31
     assert chunk_call(dk=96, dv=96) == UNSUP
     assert chunk_call(dk=64, dv=128) == UNSUP
     assert chunk_call(in_dt=5) == UNSUP
