@@ -147,17 +147,33 @@ def test_deterministic_bitwise():
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
-def test_bf16_output():
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_bf16_output(dt):
     """A bf16 output is the fp32 output rounded to nearest even, bit for bit
-    (the rounding of o itself is the caller's choice, not a path error)."""
-    case = ki.make_prefill("prefill-4k", DEV, lengths=[333], H=4)
-    say("[bf16 output]")
+    (the rounding of o itself is the caller's choice, not a path error). With
+    bf16 inputs o is stored by the recursion's output waves, with fp32 inputs
+    by the separate output kernel."""
+    case = ki.make_prefill("prefill-4k", DEV, lengths=[333], H=4, dtype=dt)
+    say(f"[bf16 output, {dt} inputs]")
     o16, S16 = gpu_prefill(case, out_dtype=torch.bfloat16)
     o32, S32 = gpu_prefill(case, out_dtype=torch.float32)
     assert o16.dtype == torch.bfloat16
     assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(S16, S32)
     o_ref, S_ref, _ = oracle.recurrence(case.q, case.k, case.v, case.log_alpha, case.beta, case.initial_state)
-    assert err(o32, o_ref) <= TOL_BF16 and err(S32, S_ref) <= TOL_BF16
+    assert err(o32, o_ref) <= tol_for(dt) and err(S32, S_ref) <= tol_for(dt)
+
+
+def test_decode_bf16_output():
+    """The decode step's bf16 output is its fp32 output rounded to nearest even."""
+    dec = ki.make_decode(8, 4, 128, 1, DEV)
+    say("[decode bf16 output]")
+    s_a, s_b = dec["state"].clone(), dec["state"].clone()
+    args = (dec["q"][0], dec["k"][0], dec["v"][0], dec["log_alpha"][0], dec["beta"][0])
+    o16 = kda.decode_step(*args, s_a, out_dtype=torch.bfloat16)
+    o32 = kda.decode_step(*args, s_b, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(s_a, s_b)
 
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
