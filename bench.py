@@ -308,7 +308,8 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed prefill steps first (500 take ~80 ms and bring the GPU to steady clocks)")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -373,7 +374,7 @@ def main(argv=None):
     if not args.no_decode:
         dec_inputs = min(args.decode_steps, 100)  # distinct per-step inputs, cycled
         dec = ki.make_decode(256, 32, 128, dec_inputs, dev)
-        dms = time_decode(kda, dec, args.decode_steps, 10, hip, stream)
+        dms = time_decode(kda, dec, args.decode_steps, 50, hip, stream)
         NH = 256 * 32
         state_bytes = 2 * NH * 128 * 128 * 4
         alg = state_bytes + NH * (4 * 128 * 2 + 2 + 128 * 4)
