@@ -193,6 +193,10 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
     constexpr int NT = D / 16;  // row tiles over dk == column slabs over dv
     constexpr int RING = PL::RING;
     constexpr int OPS = PL::OPS;
+    // With the fused output the compute wave reads chunk c + 1's -W fragments
+    // while chunk c's key-value products run, so the producers keep one more
+    // chunk landed ahead of each barrier (the 4-slot ring has room for it).
+    constexpr int LOOK = (FUSED && RING >= 4) ? 1 : 0;
 
     extern __shared__ __align__(16) char ring[];
 
@@ -313,17 +317,21 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
         const int pw = FUSED ? wv - 3 : wv - 1;
         const int pre = nch < RING - 1 ? nch : RING - 1;
         for (int c = 0; c < pre; ++c) produce<D, F32, FUSED>(ws, (int64_t)(co + c) * H + h, ct, pw, l, ring + c * PL::SLOT);
-        // chunk 0 has landed once at most the (pre - 1) later chunks are outstanding
-        wait_chunks<OPS, RING>(pre - 1);
+        // chunks 0 .. LOOK have landed once only the chunks issued after them are outstanding
+        {
+            const int need = nch - 1 < LOOK ? nch - 1 : LOOK;
+            wait_chunks<OPS, RING>(pre - 1 - need);
+        }
         __builtin_amdgcn_s_barrier();
         for (int c = 0; c < nch; ++c) {
-            // slot (c + RING - 1) % RING was read by the compute wave in chunk c - 1,
-            // which it finished before the barrier that ended that chunk
+            // slot (c + RING - 1) % RING was last read by the compute wave in chunk
+            // c - 1, which it finished before the barrier that ended that chunk
             const int nx = c + RING - 1;
             if (nx < nch) produce<D, F32, FUSED>(ws, (int64_t)(co + nx) * H + h, ct, pw, l, ring + (nx % RING) * PL::SLOT);
-            // chunk c + 1 has landed once only the chunks issued after it are outstanding
-            const int after = (nch - 1 < nx ? nch - 1 : nx) - (c + 1);
-            wait_chunks<OPS, RING>(after);
+            // chunk c + 1 + LOOK has landed once only the chunks issued after it are outstanding
+            const int last = nch - 1 < nx ? nch - 1 : nx;
+            const int need = nch - 1 < c + 1 + LOOK ? nch - 1 : c + 1 + LOOK;
+            wait_chunks<OPS, RING>(last - need);
             __builtin_amdgcn_s_barrier();
         }
         return;
@@ -337,17 +345,9 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[t][i] = s0 ? s0[sbase + (int64_t)(16 * t + 4 * g + i) * D] : 0.f;
 
-    __builtin_amdgcn_s_barrier();
-    for (int c = 0; c < nch; ++c) {
-        const char* slot = ring + (c % RING) * PL::SLOT;
-        const char* wsl = slot;
-        const char* ksl = slot + PL::FB;
-        const E* usl = reinterpret_cast<const E*>(slot + 2 * PL::FB);
-        const float* gsl = reinterpret_cast<const float*>(slot + 2 * PL::FB + PL::UB);
-        const int64_t chh = (int64_t)(co + c) * H + h;
-
-        // every LDS read of this chunk first, so their latencies overlap
-        Frag wf[4][NS], kf[NT][2];
+    Frag wf[4][NS];  // -W fragments (with LOOK, of the chunk after the current one once read)
+    auto load_w = [&](int c) {
+        const char* wsl = ring + (c % RING) * PL::SLOT;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -355,6 +355,19 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
                 const int gr = ((16 * I + n) * NS + s) * 4 + g;  // fragment of -W (row 16I+n, slice s, group g)
                 wf[I][s] = P::load(reinterpret_cast<const E*>(wsl + swz<F32>(gr) * 8 * sizeof(E)));
             }
+    };
+    __builtin_amdgcn_s_barrier();
+    if (LOOK && nch > 0) load_w(0);
+    for (int c = 0; c < nch; ++c) {
+        const char* slot = ring + (c % RING) * PL::SLOT;
+        const char* ksl = slot + PL::FB;
+        const E* usl = reinterpret_cast<const E*>(slot + 2 * PL::FB);
+        const float* gsl = reinterpret_cast<const float*>(slot + 2 * PL::FB + PL::UB);
+        const int64_t chh = (int64_t)(co + c) * H + h;
+
+        // every LDS read of this chunk first, so their latencies overlap
+        Frag kf[NT][2];
+        if (!LOOK) load_w(c);
         f32x4_t V[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
@@ -391,6 +404,9 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
         for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int I = 0; I < 4; ++I) P::mma(V[I], wf[I][s], sb[s]);
+        // the next chunk's -W while this chunk's key-value products run (the
+        // last chunk re-reads its own)
+        if (LOOK) load_w(c + 1 < nch ? c + 1 : c);
         Frag vb[2];
         E* vp = FUSED ? reinterpret_cast<E*>(hvbase + (c & 1) * PL::HVS) + D * 16
                       : ws.vn + chh * 64 * D + (int64_t)ct * 2 * 64 * 8;
