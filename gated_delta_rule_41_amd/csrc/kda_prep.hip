@@ -186,8 +186,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     float* beta_s = cst + 22 * D;     // [64]
     int* slow_s = reinterpret_cast<int*>(beta_s + 64);  // [4] per-wave overflow flags
 
-    const int gc = blockIdx.x;
-    const int h = blockIdx.y;
+    // head fastest: the workgroups dispatched together read whole token rows of
+    // the inputs and write consecutive workspace blocks, in the chunk order the
+    // state recursion consumes them
+    const int gc = blockIdx.x / H;
+    const int h = blockIdx.x - gc * H;
     ChunkLoc loc;
     if (!locate_chunk(cu, N, T, gc, loc)) return;
     const int t0 = loc.t0, L = loc.L;
@@ -663,7 +666,7 @@ static hipError_t launch_prep_t(const ChunkArgs& a, hipStream_t st) {
     auto kern = prep_kernel<D, TIn, TG, F32>;
     const hipError_t e = allow_dynamic_lds((const void*)kern, SM::BYTES);
     if (e != hipSuccess) return e;
-    dim3 grid(a.NC, a.H), block(256);
+    dim3 grid(a.NC * a.H), block(256);  // NC * H < 2^31 (checked by the caller)
     hipLaunchKernelGGL(kern, grid, block, SM::BYTES, st, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
                        (const TG*)a.la, (const TG*)a.beta, a.cu, a.N, a.T, a.H, ws);
     return hipGetLastError();
