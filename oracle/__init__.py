@@ -14,12 +14,17 @@ Contents
   parallel form (WY/UT factors, forward substitution, inter-chunk state
   recursion) derived from the same recurrence; it also serves as the spec of
   the chunk intermediates.
+* ``dplr_recurrence`` -- the same kind of fp64 token loop for the general
+  diagonal-plus-low-rank transition S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1}
+  + k_t v_t^T that KDA specialises (the comparison operator).
 * ``build``       -- compiles ``kda_oracle.c`` with the host C compiler.
 
 Pinned by ``tests/test_oracle_pins.py`` (exact retrieval, beta = 0 closed form,
 DeltaNet and Gated DeltaNet reductions, dense-transition brute force,
 linearity, norm bound, split/carry and varlen/separate equivalence, a
-hand-derived scalar example in ``tests/golden``) and by
+hand-derived scalar example in ``tests/golden``), ``tests/test_dplr_oracle.py``
+(the DPLR loop against the KDA oracle, masked linear attention, exact
+retrieval, a hand-derived example) and by
 ``tests/test_chunkwise_cpu.py`` (chunkwise form equal to the recurrence to
 1e-10 in fp64; triangular inverse against a library solve).
 """
@@ -64,6 +69,11 @@ def _load():
                       P, P, P, P, P, ctypes.c_int, ctypes.c_int,
                       ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, ctypes.c_int64, P,
                       ctypes.c_int32, ctypes.c_int32]
+        f = lib.kda_oracle_dplr_forward
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                      P, P, P, P, P, P, ctypes.c_int, ctypes.c_int,
+                      ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         _lib = lib
     return _lib
 
@@ -170,3 +180,51 @@ def decode_step(q, k, v, log_alpha, beta, state, *, heads=None, threads: int = 0
     cu = np.arange(N + 1, dtype=np.int64)
     o, S, _ = recurrence(q, k, v, log_alpha, beta, state, cu, heads=heads, threads=threads)
     return o, S
+
+
+def _cu_array(cu_seqlens, T):
+    if cu_seqlens is None:
+        return np.array([0, T], dtype=np.int64)
+    try:
+        import torch
+        if isinstance(cu_seqlens, torch.Tensor):
+            cu_seqlens = cu_seqlens.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+
+
+def dplr_recurrence(q, k, v, a, b, log_alpha, initial_state=None, cu_seqlens=None, *,
+                    heads: Optional[Sequence[int]] = None, want_o: bool = True,
+                    col_blocks: int = 1, threads: int = 0):
+    """Token-by-token fp64 recurrence of the general DPLR transition
+    S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t
+    (see ``kda_oracle.c``). Shapes: q, k, a, b, log_alpha [T, H, dk];
+    v [T, H, dv]; initial_state [N, H, dk, dv] or None; cu_seqlens [N+1] or
+    None. q, k, v, a, b share one dtype. Returns (o or None, S_final), fp64."""
+    lib = _load()
+    bufs = [_as_host_buffer(x) for x in (q, k, v, a, b)]
+    if len({d for _, d in bufs}) != 1:
+        raise TypeError("q, k, v, a, b must share a dtype")
+    (qa, in_dt), (ka, _), (va, _), (aa, _), (ba, _) = bufs
+    la, gate_dt = _as_host_buffer(log_alpha)
+    T, H, dk = qa.shape
+    dv = va.shape[2]
+    cu = _cu_array(cu_seqlens, T)
+    N = len(cu) - 1
+    s0 = None
+    if initial_state is not None:
+        s0a, _ = _as_host_buffer(initial_state)
+        s0 = np.ascontiguousarray(s0a, dtype=np.float64)
+    S_final = np.zeros((N, H, dk, dv), dtype=np.float64)
+    o = np.zeros((T, H, dv), dtype=np.float64) if want_o else None
+    hs, nh = None, H
+    if heads is not None:
+        hs = np.ascontiguousarray(np.asarray(heads, dtype=np.int32))
+        nh = len(hs)
+    rc = lib.kda_oracle_dplr_forward(T, H, dk, dv, _ptr(qa), _ptr(ka), _ptr(va), _ptr(aa), _ptr(ba),
+                                     _ptr(la), in_dt, gate_dt, N, _ptr(cu), _ptr(s0), _ptr(S_final),
+                                     _ptr(o), _ptr(hs), nh, col_blocks, threads)
+    if rc != 0:
+        raise ValueError(f"kda_oracle_dplr_forward failed with code {rc}")
+    return o, S_final

@@ -167,3 +167,116 @@ def chunkwise(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, *,
     if keep:
         return o, S_fin, kept
     return o, S_fin
+
+
+# ---------------------------------------------------------------------------
+# General DPLR transition, chunkwise (the comparison operator)
+#
+#   S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t
+#
+# KDA ties both low-rank vectors to the key; with free a and b the chunk needs
+# four gated intra-chunk matrices instead of two (GeekNews "Kimi Linear"
+# summary, section "Menos computação que o DPLR geral"). Derivation, per chunk
+# of L tokens with entry state H, inclusive cumulative log-gate g_r and
+# exclusive one e_r = g_r - log alpha_r (the low-rank read of row r sees the
+# state before row r's decay):
+#   u_r = S_{r-1}^T b_r = H^T (b_r exp(e_r)) + sum_{s<r} A_bk[r,s] v_s - sum_{s<r} A_ba[r,s] u_s
+#   A_bx[r,s] = sum_c b_rc x_sc exp(e_rc - g_sc)   (s < r)
+#   A_qx[r,s] = sum_c q_rc x_sc exp(g_rc - g_sc)   (s <= r)
+#   so u = W' H + U' with T = (I + A_ba)^-1, W' = T B~ (B~_r = exp(e_r) b_r), U' = T A_bk V;
+#   O  = Q+ H + A_qk V - A_qa u
+#   S' = Diag(exp(g_last)) H + K-^T V - A-^T u   (K-, A-: rows scaled by exp(g_last - g_s))
+# ---------------------------------------------------------------------------
+
+
+def gated_products_lr(x, gl, y, gr, e, sub: Optional[int] = None, strict: bool = False):
+    """P[r, i] = sum_c x_rc y_ic exp(gl_rc - gr_ic) for i <= r (i < r if strict).
+
+    With ``sub`` the exponentials are anchored at the exclusive gate e at each
+    sub-chunk start a (e_a = gate total before the sub-chunk):
+    exp(gl_r - gr_i) = exp(gl_r - e_aI) exp(e_aI - e_aJ) exp(e_aJ - gr_i);
+    for gl in {g, e} and gr = g the first two factors are <= 1 and the last lies
+    in [1, exp(-sum of log alpha over sub-chunk J)]."""
+    L = x.shape[0]
+    P = np.zeros((L, L))
+    if sub is None:
+        for r in range(L):
+            top = r if strict else r + 1
+            if top == 0:
+                continue
+            P[r, :top] = (x[r][None, :] * y[:top] * np.exp(gl[r][None, :] - gr[:top])).sum(axis=1)
+        return P
+    nb = (L + sub - 1) // sub
+    for I in range(nb):
+        rI = slice(I * sub, min(L, (I + 1) * sub))
+        eI = e[I * sub]
+        left = x[rI] * np.exp(gl[rI] - eI)
+        for J in range(I + 1):
+            rJ = slice(J * sub, min(L, (J + 1) * sub))
+            eJ = e[J * sub]
+            blk = (left * np.exp(eI - eJ)) @ (y[rJ] * np.exp(eJ - gr[rJ])).T
+            if I == J:
+                n = blk.shape[0]
+                blk = blk * np.tril(np.ones((n, n)), -1 if strict else 0)
+            P[rI, rJ] = blk
+    return P
+
+
+def dplr_chunk_step(q, k, v, a, b, la, S, *, sub=None, blocked=None):
+    """One DPLR chunk: returns (O, S_next, intermediates dict)."""
+    L = q.shape[0]
+    g = np.cumsum(la, axis=0)
+    e = g - la
+    Qp = np.exp(g) * q
+    Bt = np.exp(e) * b
+    dec = np.exp(g[L - 1][None, :] - g)
+    Km, Am = dec * k, dec * a
+    gam = np.exp(g[L - 1])
+    Aba = gated_products_lr(b, e, a, g, e, sub=sub, strict=True)
+    Abk = gated_products_lr(b, e, k, g, e, sub=sub, strict=True)
+    Aqk = gated_products_lr(q, g, k, g, e, sub=sub, strict=False)
+    Aqa = gated_products_lr(q, g, a, g, e, sub=sub, strict=False)
+    rhs = np.concatenate([Bt, Abk @ v], axis=1)
+    if blocked:
+        X = blocked_solve(Aba, rhs, blocked)
+    else:
+        X = forward_substitution_inverse(Aba) @ rhs
+    dk = k.shape[1]
+    W, U = X[:, :dk], X[:, dk:]
+    u = W @ S + U
+    Oh = Aqk @ v
+    O = Qp @ S + Oh - Aqa @ u
+    S_next = gam[:, None] * S + Km.T @ v - Am.T @ u
+    inter = dict(g=g, Qp=Qp, Km=Km, Am=Am, Bt=Bt, gam=gam, Aba=Aba, Abk=Abk, Aqk=Aqk, Aqa=Aqa,
+                 W=W, U=U, u=u, Oh=Oh, h=S.copy())
+    return O, S_next, inter
+
+
+def dplr_chunkwise(q, k, v, a, b, log_alpha, initial_state=None, cu_seqlens=None, *,
+                   chunk: int = 64, sub: Optional[int] = None, blocked: Optional[int] = None,
+                   keep: bool = False):
+    """Chunkwise fp64 forward of the general DPLR transition over a packed
+    batch; same shapes and return convention as ``oracle.dplr_recurrence``."""
+    q, k, v, a, b, la = (_f64(x) for x in (q, k, v, a, b, log_alpha))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    cu = [0, T] if cu_seqlens is None else [int(x) for x in _f64(cu_seqlens)]
+    N = len(cu) - 1
+    S0 = None if initial_state is None else _f64(initial_state)
+    o = np.zeros((T, H, dv))
+    S_fin = np.zeros((N, H, dk, dv))
+    kept = []
+    for n in range(N):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if S0 is None else S0[n, h].copy()
+            for c0 in range(cu[n], cu[n + 1], chunk):
+                sl = slice(c0, min(c0 + chunk, cu[n + 1]))
+                O, S, inter = dplr_chunk_step(q[sl, h], k[sl, h], v[sl, h], a[sl, h], b[sl, h], la[sl, h], S,
+                                              sub=sub, blocked=blocked)
+                o[sl, h] = O
+                if keep:
+                    kept.append(((n, h, c0), inter))
+            S_fin[n, h] = S
+    if keep:
+        return o, S_fin, kept
+    return o, S_fin

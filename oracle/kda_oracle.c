@@ -189,3 +189,117 @@ int kda_oracle_forward(int64_t T_total, int32_t H, int32_t dk, int32_t dv,
     }
     return bad ? -6 : 0;
 }
+
+/*
+ * General diagonal-plus-low-rank (DPLR) transition -- the comparison operator.
+ *
+ *     S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,    o_t = S_t^T q_t
+ *
+ * with a_t, b_t free per-(token, head) key-space vectors. This is the general
+ * transition that KDA specialises (GeekNews "Kimi Linear" summary, section
+ * "Menos computação que o DPLR geral": KDA ties both low-rank vectors to the
+ * key, a = beta k and b = alpha * k with written key beta k, which is what
+ * saves gated matrices and products against the general case). One token, in
+ * the order the formula fixes:
+ *     1. low-rank read:  u <- S^T b_t              (the state before this token)
+ *     2. decay:          S <- Diag(alpha_t) S
+ *     3. update:         S <- S - a_t u^T + k_t v_t^T
+ *     4. read:           o_t <- S^T q_t
+ * Inputs: q, k, a, b, log_alpha [T_total, H, dk] (q, k, v, a, b in in_dt;
+ * log_alpha in gate_dt), v [T_total, H, dv]; other arguments as in
+ * kda_oracle_forward (no recorded positions). Columns of S stay independent
+ * (step 1 reads column j through column j only), so column blocks are exact.
+ */
+int kda_oracle_dplr_forward(int64_t T_total, int32_t H, int32_t dk, int32_t dv,
+                            const void* q, const void* k, const void* v, const void* a,
+                            const void* b, const void* log_alpha, int in_dt, int gate_dt,
+                            int32_t N, const int64_t* cu_seqlens,
+                            const double* S0, double* S_final, double* o,
+                            const int32_t* heads, int32_t n_heads,
+                            int32_t col_blocks, int32_t n_threads) {
+    if (H <= 0 || dk <= 0 || dv <= 0 || N < 0 || !cu_seqlens) return -1;
+    if (cu_seqlens[0] != 0 || cu_seqlens[N] != T_total) return -2;
+    for (int32_t i = 0; i < N; ++i)
+        if (cu_seqlens[i + 1] < cu_seqlens[i]) return -3;
+    if (col_blocks < 1) col_blocks = 1;
+    if (col_blocks > dv) col_blocks = dv;
+    const int32_t nh = heads ? n_heads : H;
+    if (heads)
+        for (int32_t i = 0; i < nh; ++i)
+            if (heads[i] < 0 || heads[i] >= H) return -4;
+    const int64_t n_units = (int64_t)N * nh * col_blocks;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+        double* vec = (double*)malloc(sizeof(double) * (size_t)dk * 5);
+        double* u = (double*)malloc(sizeof(double) * (size_t)dv * 2);
+        if (!S || !vec || !u) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            double *qq = vec, *kk = vec + dk, *aa = vec + 2 * dk, *bb = vec + 3 * dk, *al = vec + 4 * dk;
+            double* vv = u + dv;
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t unit = 0; unit < n_units; ++unit) {
+                const int32_t cb = (int32_t)(unit % col_blocks);
+                const int32_t hi = (int32_t)((unit / col_blocks) % nh);
+                const int32_t seq = (int32_t)(unit / ((int64_t)col_blocks * nh));
+                const int32_t h = heads ? heads[hi] : hi;
+                const int32_t j0 = (int32_t)(((int64_t)dv * cb) / col_blocks);
+                const int32_t j1 = (int32_t)(((int64_t)dv * (cb + 1)) / col_blocks);
+                const int32_t nc = j1 - j0;
+                const int64_t sbase = ((int64_t)seq * H + h) * dk * dv;
+                for (int32_t c = 0; c < dk; ++c)
+                    for (int32_t j = 0; j < nc; ++j)
+                        S[(int64_t)c * nc + j] = S0 ? S0[sbase + (int64_t)c * dv + j0 + j] : 0.0;
+                for (int64_t t = cu_seqlens[seq]; t < cu_seqlens[seq + 1]; ++t) {
+                    const int64_t kb = (t * H + h) * dk;
+                    const int64_t vb = (t * H + h) * dv;
+                    for (int32_t c = 0; c < dk; ++c) {
+                        qq[c] = load_as_f64(q, in_dt, kb + c);
+                        kk[c] = load_as_f64(k, in_dt, kb + c);
+                        aa[c] = load_as_f64(a, in_dt, kb + c);
+                        bb[c] = load_as_f64(b, in_dt, kb + c);
+                        al[c] = exp(load_as_f64(log_alpha, gate_dt, kb + c));
+                    }
+                    for (int32_t j = 0; j < nc; ++j) vv[j] = load_as_f64(v, in_dt, vb + j0 + j);
+                    /* 1. low-rank read of the previous state: u = S^T b */
+                    for (int32_t j = 0; j < nc; ++j) u[j] = 0.0;
+                    for (int32_t c = 0; c < dk; ++c) {
+                        const double* Sr = S + (int64_t)c * nc;
+                        for (int32_t j = 0; j < nc; ++j) u[j] += Sr[j] * bb[c];
+                    }
+                    /* 2.-3. decay, then subtract a u^T and add k v^T */
+                    for (int32_t c = 0; c < dk; ++c) {
+                        double* Sr = S + (int64_t)c * nc;
+                        for (int32_t j = 0; j < nc; ++j)
+                            Sr[j] = al[c] * Sr[j] - aa[c] * u[j] + kk[c] * vv[j];
+                    }
+                    /* 4. read: o_t = S^T q */
+                    if (o) {
+                        for (int32_t j = 0; j < nc; ++j) u[j] = 0.0;
+                        for (int32_t c = 0; c < dk; ++c) {
+                            const double* Sr = S + (int64_t)c * nc;
+                            for (int32_t j = 0; j < nc; ++j) u[j] += Sr[j] * qq[c];
+                        }
+                        for (int32_t j = 0; j < nc; ++j) o[vb + j0 + j] = u[j];
+                    }
+                }
+                if (S_final)
+                    for (int32_t c = 0; c < dk; ++c)
+                        for (int32_t j = 0; j < nc; ++j)
+                            S_final[sbase + (int64_t)c * dv + j0 + j] = S[(int64_t)c * nc + j];
+            }
+        }
+        free(S);
+        free(vec);
+        free(u);
+    }
+    return bad ? -6 : 0;
+}

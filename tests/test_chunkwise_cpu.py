@@ -116,3 +116,66 @@ def test_padding_rows_are_neutral():
                               pad(b[:, 0]), S0, sub=16, blocked=16)
     np.testing.assert_allclose(O2[:T], O1, atol=1e-12)
     np.testing.assert_allclose(S2, S1, atol=1e-12)
+
+
+def dplr_case(T, H, dk, dv, shift=0.0):
+    q = _unit(rng.standard_normal((T, H, dk)))
+    k = _unit(rng.standard_normal((T, H, dk)))
+    v = rng.standard_normal((T, H, dv))
+    ah = _unit(rng.standard_normal((T, H, dk)))
+    la = -np.logaddexp(0.0, rng.standard_normal((T, H, dk)) + shift)
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))
+    return q, k, v, beta[..., None] * ah, np.exp(la) * ah, la
+
+
+@pytest.mark.parametrize("T", [1, 17, 64, 65, 200])
+@pytest.mark.parametrize("chunk", [1, 4, 16, 64])
+def test_dplr_chunkwise_matches_recurrence(T, chunk):
+    """The four-matrix chunk algebra of the general DPLR transition (and its
+    anchored secondary chunking / blocked substitution) equals the token loop."""
+    H, dk, dv = 2, 8, 4
+    q, k, v, a, b, la = dplr_case(T, H, dk, dv)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    o_ref, S_ref = oracle.dplr_recurrence(q, k, v, a, b, la, S0)
+    o, S = cw.dplr_chunkwise(q, k, v, a, b, la, S0, chunk=chunk)
+    assert _err(o, o_ref) < 1e-10 and _err(S, S_ref) < 1e-10
+    if chunk >= 16:
+        o2, S2 = cw.dplr_chunkwise(q, k, v, a, b, la, S0, chunk=chunk, sub=16, blocked=16)
+        assert _err(o2, o_ref) < 1e-10 and _err(S2, S_ref) < 1e-10
+
+
+def test_dplr_chunkwise_independent_ab_varlen_fast_decay():
+    """Independent a and b (no structure shared with k), packed sequences and
+    the fast-decay gate, with secondary chunking: still the token loop."""
+    lens = [64, 1, 130, 0, 77]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, H, dk, dv = int(cu[-1]), 2, 16, 8
+    q = _unit(rng.standard_normal((T, H, dk)))
+    k = _unit(rng.standard_normal((T, H, dk)))
+    a = 0.5 * _unit(rng.standard_normal((T, H, dk)))
+    b = 0.5 * _unit(rng.standard_normal((T, H, dk)))
+    v = rng.standard_normal((T, H, dv))
+    la = -np.logaddexp(0.0, rng.standard_normal((T, H, dk)) + 2.0)
+    S0 = rng.standard_normal((len(lens), H, dk, dv))
+    o_ref, S_ref = oracle.dplr_recurrence(q, k, v, a, b, la, S0, cu)
+    o, S = cw.dplr_chunkwise(q, k, v, a, b, la, S0, cu, sub=16, blocked=16)
+    assert _err(o, o_ref) < 1e-10 and _err(S, S_ref) < 1e-10
+
+
+def test_dplr_anchored_factors_are_bounded():
+    """With the exclusive-gate anchors every left and cross factor is <= 1 and
+    every right factor lies in [1, exp(-sum of log alpha over its sub-chunk)]."""
+    L, dk, sub = 64, 8, 16
+    la = -np.logaddexp(0.0, rng.standard_normal((L, dk)) + 2.0)
+    g = np.cumsum(la, axis=0)
+    e = g - la
+    for I in range(L // sub):
+        rI = slice(I * sub, (I + 1) * sub)
+        eI = e[I * sub]
+        assert np.all(g[rI] - eI <= 1e-12) and np.all(e[rI] - eI <= 1e-12)
+        for J in range(I + 1):
+            eJ = e[J * sub]
+            assert np.all(eI - eJ <= 1e-12)
+            right = eJ - g[J * sub:(J + 1) * sub]
+            assert np.all(right >= -1e-12)
+            assert np.all(right <= -la[J * sub:(J + 1) * sub].sum(axis=0) + 1e-12)
