@@ -7,9 +7,11 @@ T=4096, dk=dv=128, chunk 64, bf16 inputs, fp32 initial/final state and fp32
 output (synthetic, seeded; see kda_inputs). The decode step (the remaining row
 of the hot path) is timed in the same run on ``decode-256`` (256 sequences x 32
 heads, fp32 states of 512 MiB, updated in place) and reported in the same JSON
-line. Prints ONE JSON line.
+line. Prints ONE JSON line. The general-DPLR comparison operator (the transition KDA specialises,
+with free low-rank vectors a, b) is timed on the same workload and reported
+beside it under "dplr_comparison".
 
-    python bench.py [--steps K] [--warmup W] [--decode-steps S] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--decode-steps S] [--no-cpu-baseline] [--no-dplr]
 
 Profiling helpers (used to write the summaries under profiles/):
     python bench.py --copy-calibration MIB        # counter calibration kernel only
@@ -150,6 +152,32 @@ def time_prefill(kda, case, steps, warmup, hip, stream):
     ev.close()
     per = {k_: v_ / steps for k_, v_ in per.items()}
     return wall_ms, per, span / steps, o, fs
+
+
+def time_dplr(kda, case, steps, warmup):
+    """Whole-call time of the general-DPLR prefill (its two kernels) on the
+    stream the binding launches on, with torch events (torch's current stream)."""
+    import torch
+    dev = case.q.device
+    ws = torch.empty(kda.dplr_workspace_size(case.N, case.T_total, case.H, case.dk, case.dv),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty(case.T_total, case.H, case.dv, dtype=torch.float32, device=dev)
+    fs = torch.empty(case.N, case.H, case.dk, case.dv, dtype=torch.float32, device=dev)
+
+    def call():
+        kda.dplr_chunk_fwd(case.q, case.k, case.v, case.a, case.b, case.log_alpha, case.initial_state,
+                           case.cu_seqlens, o=o, final_state=fs, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, o, fs
 
 
 def time_decode(kda, dec, steps, warmup, hip, stream):
@@ -313,6 +341,7 @@ def main(argv=None):
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-dplr", action="store_true", help="skip the general-DPLR comparison")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run the counter calibration copy kernel over MIB MiB")
     args = ap.parse_args(argv)
@@ -370,6 +399,19 @@ def main(argv=None):
                     "event_span_ms": round(span_ms, 5)},
         "roofline": roof,
     }
+
+    if not args.no_dplr:
+        dcase = ki.make_dplr("prefill-4k", dev)
+        dplr_ms, _, _ = time_dplr(kda, dcase, args.steps, 200)
+        # per token-head, d = 128, chunk 64: four gated chunk matrices, three
+        # WY/intra products, three d x d state products, output (see DESIGN)
+        dplr_flops = 206165 * TH
+        out["dplr_comparison"] = {
+            "workload": "prefill-4k (+ a = beta a_hat, b = a_hat)", "ms_per_step": round(dplr_ms, 5),
+            "tokens_per_s": round(case.T_total / (dplr_ms * 1e-3), 1),
+            "tflops": round(dplr_flops / (dplr_ms * 1e-3) / 1e12, 2),
+            "time_ratio_dplr_over_kda": round(dplr_ms / wall_ms, 3)}
+        del dcase
 
     if not args.no_decode:
         dec_inputs = min(args.decode_steps, 100)  # distinct per-step inputs, cycled

@@ -7,6 +7,8 @@ library is not built, importing the functions raises.
 
     o, final_state = chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None)
     o = decode_step(q, k, v, log_alpha, beta, state)          # state updated in place
+    o, final_state = dplr_chunk_fwd(q, k, v, a, b, log_alpha, initial_state=None, cu_seqlens=None)
+                     # the general DPLR transition KDA specialises (comparison operator)
 """
 from __future__ import annotations
 
@@ -16,8 +18,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "decode_step", "workspace_size", "abi_version", "status_str",
-           "library_path", "KDAError", "CHUNK"]
+__all__ = ["chunk_fwd", "decode_step", "workspace_size", "dplr_chunk_fwd", "dplr_workspace_size",
+           "abi_version", "status_str", "library_path", "KDAError", "CHUNK"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -62,6 +64,11 @@ def _load():
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, SZ, P]
     lib.kda_chunk_fwd_timed.restype = ctypes.c_int
     lib.kda_chunk_fwd_timed.argtypes = lib.kda_chunk_fwd.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
+    lib.kda_dplr_chunk_fwd_workspace_size.restype = ctypes.c_int
+    lib.kda_dplr_chunk_fwd_workspace_size.argtypes = lib.kda_chunk_fwd_workspace_size.argtypes
+    lib.kda_dplr_chunk_fwd.restype = ctypes.c_int
+    lib.kda_dplr_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, I32, I64, I32, I32, I32,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, SZ, P]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
@@ -213,3 +220,72 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: to
     if st != 0:
         raise KDAError(st, "kda_decode_step")
     return o
+
+
+def dplr_workspace_size(N: int, T_total: int, H: int, dk: int, dv: int) -> int:
+    """Workspace bytes of ``dplr_chunk_fwd`` (bf16 inputs)."""
+    out = ctypes.c_size_t(0)
+    st = _load().kda_dplr_chunk_fwd_workspace_size(int(N), int(T_total), int(H), int(dk), int(dv),
+                                                   KDA_BF16, ctypes.byref(out))
+    if st != 0:
+        raise KDAError(st, "kda_dplr_chunk_fwd_workspace_size")
+    return int(out.value)
+
+
+def dplr_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
+                   log_alpha: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                   cu_seqlens: Optional[torch.Tensor] = None, *, out_dtype: torch.dtype = torch.float32,
+                   want_final_state: bool = True, o: Optional[torch.Tensor] = None,
+                   final_state: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise prefill of the general DPLR transition
+    S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t
+    (see ``kda_dplr_chunk_fwd`` in include/kda.h). q, k, a, b, log_alpha
+    [T, H, dk]; v [T, H, dv]; q, k, v, a, b bf16. Other arguments and the
+    return value as ``chunk_fwd``."""
+    lib = _load()
+    dev = q.device
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, a, b, log_alpha must be [T, H, dk] and v [T, H, dv]")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    items = [("q", q, (T, H, dk)), ("k", k, (T, H, dk)), ("v", v, (T, H, dv)), ("a", a, (T, H, dk)),
+             ("b", b, (T, H, dk)), ("log_alpha", log_alpha, (T, H, dk))]
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 >= 2 offsets")
+        items.append(("cu_seqlens", cu_seqlens, None))
+        N = cu_seqlens.numel() - 1
+    else:
+        N = 1
+    if initial_state is not None:
+        items.append(("initial_state", initial_state, (N, H, dk, dv)))
+    if o is not None:
+        items.append(("o", o, (T, H, dv)))
+    if final_state is not None:
+        items.append(("final_state", final_state, (N, H, dk, dv)))
+    if workspace is not None:
+        items.append(("workspace", workspace, None))
+    _check(items, dev)
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v, a, b)):
+        raise TypeError("q, k, v, a, b must be bfloat16")
+    gate_dt = _dtype_code(log_alpha, "log_alpha")
+    if o is None:
+        o = torch.empty(T, H, dv, dtype=out_dtype, device=dev)
+    out_dt = _dtype_code(o, "o")
+    if final_state is None and want_final_state:
+        final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+    sz = ctypes.c_size_t(0)
+    lib.kda_dplr_chunk_fwd_workspace_size(max(N, 1), T, H, dk, dv, KDA_BF16, ctypes.byref(sz))
+    if workspace is None:
+        workspace = torch.empty(max(int(sz.value), 1), dtype=torch.uint8, device=dev)
+    st = lib.kda_dplr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha),
+                                _ptr(initial_state), _ptr(cu_seqlens), N, T, H, dk, dv, KDA_BF16, gate_dt,
+                                out_dt, _ptr(o), _ptr(final_state), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_dplr_chunk_fwd")
+    return o, final_state

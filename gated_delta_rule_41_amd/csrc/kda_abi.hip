@@ -78,6 +78,20 @@ WsPlan plan_workspace(int64_t NC, int H, int D, bool f32) {
     return p;
 }
 
+WsPlan plan_workspace_dplr(int64_t NC, int H, int D) {
+    const size_t ch = (size_t)NC * (size_t)H;
+    const size_t f = ch * KDA_CHUNK * D * 2;  // one [64][D] fp16 factor per chunk-head
+    const size_t sz[8] = {f, f, f, f, f, ch * KDA_CHUNK * KDA_CHUNK * 2, f, ch * D * 4};
+    WsPlan p;
+    size_t o = 0;
+    for (int i = 0; i < 8; ++i) {
+        p.off[i] = o;
+        o = align_up(o + sz[i], 256);
+    }
+    p.total = o;
+    return p;
+}
+
 }  // namespace kda
 
 using namespace kda;
@@ -226,6 +240,91 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
     if (!mark(2)) return KDA_ERR_HIP;
     if (NC > 0 && !output_fused(f32) && launch_output(a, st) != hipSuccess) return KDA_ERR_HIP;
     if (!mark(3)) return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+kda_status kda_dplr_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
+                                             kda_dtype in_dtype, size_t* bytes) {
+    if (!bytes) return KDA_ERR_NULL;
+    if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
+    if (!head_ok(dk, dv) || in_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    *bytes = plan_workspace_dplr(chunk_capacity(N, T_total, true), H, dk).total;
+    return KDA_OK;
+}
+
+kda_status kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const void* b,
+                              const void* log_alpha, const float* initial_state, const int32_t* cu_seqlens,
+                              int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype,
+                              kda_dtype gate_dtype, kda_dtype out_dtype, void* o, float* final_state,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
+    if (T_total > 0 && (!q || !k || !v || !a || !b || !log_alpha || !o)) return KDA_ERR_NULL;
+    if (!cu_seqlens && N != 1) return KDA_ERR_SHAPE;
+    if (!head_ok(dk, dv) || in_dtype != KDA_BF16 || !dtype_ok(gate_dtype) || !dtype_ok(out_dtype))
+        return KDA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(a) || !aligned16(b) ||
+        !aligned16(log_alpha) || !aligned16(o) || !aligned16(initial_state) || !aligned16(final_state) ||
+        !aligned_to(cu_seqlens, 4))
+        return KDA_ERR_ALIGN;
+    const size_t T = (size_t)T_total;
+    const size_t nx = T * H * dk * 2, nla = T * H * dk * esize(gate_dtype);
+    const size_t no = T * H * dv * esize(out_dtype), ns = (size_t)N * H * dk * dv * 4;
+    const size_t ncu = cu_seqlens ? (size_t)(N + 1) * 4 : 0;
+    const void* ins[8] = {q, k, v, a, b, log_alpha, initial_state, cu_seqlens};
+    const size_t nin[8] = {nx, nx, nx, nx, nx, nla, ns, ncu};
+    for (int i = 0; i < 8; ++i) {
+        if (overlaps(o, no, ins[i], nin[i])) return KDA_ERR_ALIAS;
+        if (i != 6 && overlaps(final_state, ns, ins[i], nin[i])) return KDA_ERR_ALIAS;
+    }
+    if (overlaps(o, no, final_state, ns)) return KDA_ERR_ALIAS;
+    if (final_state && initial_state && final_state != initial_state &&
+        overlaps(final_state, ns, initial_state, ns))
+        return KDA_ERR_ALIAS;
+    const int64_t NC = chunk_capacity(N, T_total, cu_seqlens != nullptr);
+    const WsPlan plan = plan_workspace_dplr(NC, H, dk);
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < plan.total)
+        return KDA_ERR_WORKSPACE;
+    for (int i = 0; i < 8; ++i)
+        if (overlaps(workspace, plan.total, ins[i], nin[i])) return KDA_ERR_ALIAS;
+    if (overlaps(workspace, plan.total, o, no) || overlaps(workspace, plan.total, final_state, ns))
+        return KDA_ERR_ALIAS;
+    if (NC >= (int64_t(1) << 31) / H) return KDA_ERR_SHAPE;
+
+    char* w = static_cast<char*>(workspace);
+    ChunkArgs c;
+    c.q = q;
+    c.k = k;
+    c.v = v;
+    c.la = log_alpha;
+    c.beta = nullptr;
+    c.s0 = initial_state;
+    c.cu = cu_seqlens;
+    c.s_final = final_state;
+    c.o = o;
+    c.N = N;
+    c.T = (int)T_total;
+    c.H = H;
+    c.D = dk;
+    c.NC = (int)NC;
+    c.in_f32 = false;
+    c.gate_f32 = gate_dtype == KDA_F32;
+    c.out_f32 = out_dtype == KDA_F32;
+    c.dplr = true;
+    c.lr_a = a;
+    c.lr_b = b;
+    c.qp = w + plan.off[0];
+    c.km = w + plan.off[1];
+    c.am = w + plan.off[2];
+    c.wn = w + plan.off[3];
+    c.u = w + plan.off[4];
+    c.aqk = w + plan.off[5];
+    c.oh = w + plan.off[6];
+    c.gam = reinterpret_cast<float*>(w + plan.off[7]);
+    c.h = nullptr;
+    c.vn = nullptr;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (NC > 0 && launch_dplr_prep(c, st) != hipSuccess) return KDA_ERR_HIP;
+    if (launch_recur(c, st) != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
 }
 

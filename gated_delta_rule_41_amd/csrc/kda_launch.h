@@ -28,6 +28,11 @@ struct ChunkArgs {
     // workspace arrays (element type bf16 bits or fp32, per in_f32)
     void *qp, *km, *wn, *u, *aqk, *h, *vn;
     float* gam;
+    // general DPLR transition only: the low-rank vectors a, b [T, H, D] (bf16)
+    // and two more workspace arrays (decayed a transposed; A_qk V)
+    bool dplr = false;
+    const void *lr_a = nullptr, *lr_b = nullptr;
+    void *am = nullptr, *oh = nullptr;
 };
 
 // Workspace carve-up shared by the size query and the launcher.
@@ -36,6 +41,8 @@ struct WsPlan {
     size_t total;
 };
 WsPlan plan_workspace(int64_t NC, int H, int D, bool f32);
+// general DPLR transition (16-bit factors): qp, km, am, wn, u, aqk, oh, gam
+WsPlan plan_workspace_dplr(int64_t NC, int H, int D);
 int64_t chunk_capacity(int N, int64_t T, bool have_cu);
 
 // Opt a kernel into more than 64 KiB of dynamic LDS, once per device.
@@ -45,6 +52,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prep(const ChunkArgs& a, hipStream_t st);
 hipError_t launch_recur(const ChunkArgs& a, hipStream_t st);
 hipError_t launch_output(const ChunkArgs& a, hipStream_t st);
+hipError_t launch_dplr_prep(const ChunkArgs& a, hipStream_t st);
 
 // With 16-bit operands the state-recursion kernel also computes the chunk
 // outputs (h_n and V_new stay on chip); with fp32 operands its LDS cannot

@@ -37,7 +37,7 @@
 
 namespace kda {
 
-template <int D, bool F32, bool FUSED>
+template <int D, bool F32, bool FUSED, bool DPLR = false>
 struct RecurPlan {
     using E = typename Pol<F32>::E;
     static constexpr int FB = 64 * D * (int)sizeof(E);   // bytes of -W (and of K-^T) per chunk-head
@@ -48,9 +48,16 @@ struct RecurPlan {
     // with the fused output: two buffers of (h_n slab [D x 16], V_new slab [64 x 16])
     static constexpr int HVS = (D * 16 + 64 * 16) * (int)sizeof(E);
     static constexpr int HV = FUSED ? 2 * HVS : 0;
-    static constexpr int WARM = FUSED ? 256 : 0;  // target of the L2 warm-up loads (never read)
-    static constexpr int RING = (4 * SLOT + HV + WARM <= 160 * 1024) ? 4 : 2;
-    static constexpr int LDS = RING * SLOT + HV + WARM;
+    // DPLR: two buffers of the state-independent update K-^T V of this slab
+    // (fp16, accumulator-tile order), by chunk parity
+    static constexpr int PBS = (D / 16) * 64 * 4 * 2;
+    static constexpr int PB = DPLR ? 2 * PBS : 0;
+    // target of the L2 warm-up loads (never read); DPLR has no room for it and
+    // aims them at the unread tail of ring slot 0's gamma region instead
+    static constexpr int WARM = (FUSED && !DPLR) ? 256 : 0;
+    static constexpr int RING = (4 * SLOT + HV + PB + WARM <= 160 * 1024) ? 4 : 2;
+    static constexpr int LDS = RING * SLOT + HV + PB + WARM;
+    static_assert(!DPLR || (FUSED && GPAD - GB >= 256), "warm-up target in the gamma pad");
     static_assert(LDS <= 160 * 1024, "LDS budget");
     // global->LDS loads per chunk and producer wave (16 bytes per lane, 1 KiB per load)
     static constexpr int OPS_W = FB / 1024, OPS_U = UB / 1024, OPS_G = 1;
@@ -66,7 +73,10 @@ struct RecurPlan {
     static constexpr int LINES = 3 * LINES_W + LINES_A;
     static constexpr int LINES_PER = (LINES + D / 16 - 1) / (D / 16);
     static constexpr int LINES_U = UB / 128, LINES_G = GB / 128;
-    static_assert(!FUSED || (LINES_PER <= 64 && LINES_U + LINES_G <= 64), "two warm-up loads per chunk");
+    // DPLR: the second load also covers this slab's share of K-^T and its A_qk V tiles
+    static constexpr int LINES_K = DPLR ? FB / 128 / (D / 16) : 0, LINES_O = DPLR ? UB / 128 : 0;
+    static constexpr int LINES_2 = LINES_U + LINES_G + LINES_K + LINES_O;
+    static_assert(!FUSED || (LINES_PER <= 64 && LINES_2 <= 64), "two warm-up loads per chunk");
     static constexpr int AHEAD = 3;  // chunks warmed ahead of the compute wave (2..6 measured; 3 best)
 };
 
@@ -114,10 +124,10 @@ __device__ __forceinline__ void wait_chunks(int after) {
 // Producer: issue the global->LDS loads of one chunk (this producer's half).
 // Both producers issue exactly OPS loads per chunk, so one vmcnt threshold
 // serves both.
-template <int D, bool F32, bool FUSED>
+template <int D, bool F32, bool FUSED, bool DPLR>
 __device__ __forceinline__ void produce(const Ws<typename Pol<F32>::E>& ws, int64_t chh, int ct, int pw, int l,
                                        char* slot) {
-    using PL = RecurPlan<D, F32, FUSED>;
+    using PL = RecurPlan<D, F32, FUSED, DPLR>;
     if (pw == 0) {
         const char* wp = reinterpret_cast<const char*>(ws.wn + chh * 64 * D);
 #pragma unroll
@@ -130,7 +140,8 @@ __device__ __forceinline__ void produce(const Ws<typename Pol<F32>::E>& ws, int6
         for (int j = PL::OPS0; j < PL::OPS; ++j)
             dma16(up + (64 * (PL::OPS_U - 1) + l) * 16, slot + 2 * PL::FB + (PL::OPS_U - 1) * 1024);
     } else {
-        const char* kp = reinterpret_cast<const char*>(ws.km + chh * D * 64);
+        // the state update's key factor: K-^T (KDA) or A-^T (DPLR)
+        const char* kp = reinterpret_cast<const char*>((DPLR ? ws.am : ws.km) + chh * D * 64);
 #pragma unroll
         for (int j = 0; j < PL::OPS_W; ++j) dma16(kp + swz<F32>(64 * j + l) * 16, slot + PL::FB + j * 1024);
         // gamma: lanes past its end re-load its first granule into the unread tail of its region
@@ -147,27 +158,35 @@ __device__ __forceinline__ void produce(const Ws<typename Pol<F32>::E>& ws, int6
 // gamma lines, so that the producers' DMA and the output waves' loads of that
 // chunk, a few chain steps later, hit the XCD's L2 instead of HBM. The LDS
 // target is a scratch area nobody reads.
-template <int D, bool F32, bool FUSED>
+template <int D, bool F32, bool FUSED, bool DPLR>
 __device__ __forceinline__ void warm_chunk(const Ws<typename Pol<F32>::E>& ws, int64_t chh, int ct, int l,
                                            char* dst) {
-    using PL = RecurPlan<D, F32, FUSED>;
+    using PL = RecurPlan<D, F32, FUSED, DPLR>;
     int L = ct * PL::LINES_PER + (l < PL::LINES_PER ? l : PL::LINES_PER - 1);
     L = L < PL::LINES ? L : PL::LINES - 1;
     const char* p;
     if (L < PL::LINES_W)
         p = reinterpret_cast<const char*>(ws.wn + chh * 64 * D) + L * 128;
     else if (L < 2 * PL::LINES_W)
-        p = reinterpret_cast<const char*>(ws.km + chh * 64 * D) + (L - PL::LINES_W) * 128;
+        p = reinterpret_cast<const char*>((DPLR ? ws.am : ws.km) + chh * 64 * D) + (L - PL::LINES_W) * 128;
     else if (L < 3 * PL::LINES_W)
         p = reinterpret_cast<const char*>(ws.qp + chh * 64 * D) + (L - 2 * PL::LINES_W) * 128;
     else
         p = reinterpret_cast<const char*>(ws.aqk + chh * 64 * 64) + (L - 3 * PL::LINES_W) * 128;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)p,
                                      (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
-    const int m = l < PL::LINES_U + PL::LINES_G ? l : 0;
-    const char* pu = m < PL::LINES_U
-                         ? reinterpret_cast<const char*>(ws.u + chh * 64 * D + (int64_t)ct * 4 * 64 * 4) + m * 128
-                         : reinterpret_cast<const char*>(ws.gam + chh * D) + (m - PL::LINES_U) * 128;
+    const int m = l < PL::LINES_2 ? l : 0;
+    const char* pu;
+    if (m < PL::LINES_U)
+        pu = reinterpret_cast<const char*>(ws.u + chh * 64 * D + (int64_t)ct * 4 * 64 * 4) + m * 128;
+    else if (m < PL::LINES_U + PL::LINES_G)
+        pu = reinterpret_cast<const char*>(ws.gam + chh * D) + (m - PL::LINES_U) * 128;
+    else if (m < PL::LINES_U + PL::LINES_G + PL::LINES_K)
+        pu = reinterpret_cast<const char*>(ws.km + chh * 64 * D) +
+             (ct * PL::LINES_K + m - PL::LINES_U - PL::LINES_G) * 128;
+    else
+        pu = reinterpret_cast<const char*>(ws.oh + chh * 64 * D + (int64_t)ct * 4 * 64 * 4) +
+             (m - PL::LINES_U - PL::LINES_G - PL::LINES_K) * 128;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)pu,
                                      (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
 }
@@ -177,18 +196,28 @@ __device__ __forceinline__ void warm_chunk(const Ws<typename Pol<F32>::E>& ws, i
 // wave leaves h_n and V_new in an LDS buffer (two buffers, by chunk parity)
 // instead of the workspace, and the output waves, taking alternate chunks,
 // fetch Q+ and A_qk into registers one chunk ahead. Waves: 0 compute, 1-2
-// output, 3-4 producers, 5 L2 warm-up. Every wave executes the same 1 + nch
-// barriers.
-template <int D, bool F32, bool FUSED, bool OUT_F32>
-__global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* __restrict__ s0,
+// output, 3-4 producers, 5 L2 warm-up (6: DPLR state-independent update).
+// Every wave executes the same 1 + nch barriers.
+//
+// DPLR (the general transition, factors from kda_dplr_prep.hip): the chain is
+// the same with -u = -U' + (-W') h in place of V_new and A-^T in place of
+// K-^T, plus two state-independent terms: the state update adds K-^T V and the
+// output adds A_qk V (from the workspace, as the output accumulators' start).
+// A seventh wave computes K-^T V for this slab one chunk ahead of the compute
+// wave and leaves it in an LDS buffer by chunk parity; its operands are
+// fetched one chain step earlier still.
+template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false>
+__global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 192) void recur_kernel(const float* __restrict__ s0,
                                                                   float* __restrict__ s_final,
                                                                   const int32_t* __restrict__ cu, int N, int T,
                                                                   int H, Ws<typename Pol<F32>::E> ws,
-                                                                  void* __restrict__ o) {
+                                                                  void* __restrict__ o,
+                                                                  const void* __restrict__ vsrc) {
     using P = Pol<F32>;
     using E = typename P::E;
     using Frag = typename P::Frag;
-    using PL = RecurPlan<D, F32, FUSED>;
+    using PL = RecurPlan<D, F32, FUSED, DPLR>;
+    static_assert(!DPLR || (FUSED && !F32), "the DPLR chain runs on 16-bit factors with the fused output");
     constexpr int NS = D / 32;
     constexpr int NT = D / 16;  // row tiles over dk == column slabs over dv
     constexpr int RING = PL::RING;
@@ -218,6 +247,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
     int co, nch;
     seq_chunks(cu, T, seq, co, nch);
     char* hvbase = ring + RING * PL::SLOT;  // h_n / V_new exchange buffers (FUSED)
+    char* pbase = hvbase + PL::HV;          // K-^T V buffers (DPLR)
 
     if (FUSED && (wv == 1 || wv == 2)) {
         // ---------------- output waves: wave 1 + p computes the outputs of the
@@ -227,10 +257,16 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
         const int tstart = cu ? cu[seq] : 0;
         const int len = cu ? cu[seq + 1] - tstart : T;
         Frag qa[4][NS], aa[4][2];
+        u32x2_t ohr[4];  // DPLR: this slab's A_qk V tiles (fp16)
         auto issue = [&](int c) {
             const int64_t chh = (int64_t)(co + c) * H + h;
             const E* qp = ws.qp + chh * 64 * D;
             const E* ap = ws.aqk + chh * 64 * 64;
+            if constexpr (DPLR) {
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+                    ohr[I] = *reinterpret_cast<const u32x2_t*>(ws.oh + chh * 64 * D + (((int64_t)ct * 4 + I) * 64 + l) * 4);
+            }
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
@@ -247,8 +283,21 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
             const E* hb = reinterpret_cast<const E*>(hvbase + (c & 1) * PL::HVS);
             const E* vb = hb + D * 16;
             f32x4_t acc[4];
+            if constexpr (DPLR) {
+                // keep the conversion below the barrier that precedes this call:
+                // hoisted above it, it would make the wave wait there for every
+                // load it has in flight
 #pragma unroll
-            for (int I = 0; I < 4; ++I) acc[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int I = 0; I < 4; ++I) asm volatile("" : "+v"(ohr[I]));
+            }
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                if constexpr (DPLR)
+                    acc[I] = f32x4_t{h2f(ohr[I][0] & 0xffffu), h2f(ohr[I][0] >> 16), h2f(ohr[I][1] & 0xffffu),
+                                     h2f(ohr[I][1] >> 16)};
+                else
+                    acc[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const Frag bh = P::load(hb + (s * 64 + l) * 8);
@@ -296,15 +345,94 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
         return;
     }
 
+    if (DPLR && wv == 6) {
+        // ---------------- DPLR: K-^T V of chunk c + 1 in iteration c, for the
+        // compute wave's state update in iteration c + 1. A wave of its own, so
+        // that the only loads it ever waits for are its own operands, issued
+        // one iteration before their use.
+        const int tstart = cu ? cu[seq] : 0;
+        const int len = cu ? cu[seq + 1] - tstart : T;
+        // DPLR: K-^T V of chunk c for this slab. Its operands (K-^T fragments,
+        // and this slab's values over the chunk rows, zero past the sequence
+        // end) are loaded by load_kv one iteration before put_kv multiplies
+        // them and stores the product in buffer c & 1.
+        Frag kq[DPLR ? NT : 1][2];
+        uint16_t vraw[2][8];  // values as loaded (bf16 bits); converted only when used
+        int vlen = 0;         // rows of the chunk whose values are loaded
+        auto load_kv = [&](int c) {
+            if constexpr (DPLR) {
+                const int64_t chh = (int64_t)(co + c) * H + h;
+                const E* kp = ws.km + chh * D * 64;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) kq[t][s] = P::load(kp + ((16 * t + n) * 2 + s) * 32 + g * 8);
+                const int t0 = tstart + 64 * c;
+                const int L = min(64, len - 64 * c);
+                const uint16_t* vin = static_cast<const uint16_t*>(vsrc);
+                // rows past the end load row 0 (branch-free) and are zeroed in put_kv
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const int row = 32 * s + kslot(g, jj);
+                        vraw[s][jj] = vin[((int64_t)(t0 + (row < L ? row : 0)) * H + h) * D + 16 * ct + n];
+                    }
+                vlen = L;
+            }
+        };
+        auto put_kv = [&](int c) {
+            if constexpr (DPLR) {
+                Frag vq[2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    float x[8];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) x[jj] = 32 * s + kslot(g, jj) < vlen ? bf2f(vraw[s][jj]) : 0.f;
+                    vq[s] = P::make(x);
+                }
+                f32x4_t pk[NT];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) pk[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) P::mma(pk[t], kq[t][s], vq[s]);
+                char* pb = pbase + (c & 1) * PL::PBS;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    u32x2_t w2;
+                    w2[0] = (uint32_t)f2h(pk[t][0]) | ((uint32_t)f2h(pk[t][1]) << 16);
+                    w2[1] = (uint32_t)f2h(pk[t][2]) | ((uint32_t)f2h(pk[t][3]) << 16);
+                    *reinterpret_cast<u32x2_t*>(pb + (t * 64 + l) * 8) = w2;
+                }
+                wait_lgkm0();  // in LDS before the next barrier hands it over
+            }
+        };
+        if (nch > 0) {
+            load_kv(0);
+            put_kv(0);
+            if (nch > 1) load_kv(1);
+        }
+        __builtin_amdgcn_s_barrier();
+        for (int c = 0; c < nch; ++c) {
+            if (c + 1 < nch) put_kv(c + 1);
+            if (c + 2 < nch) load_kv(c + 2);
+            __builtin_amdgcn_s_barrier();
+        }
+        return;
+    }
+
     if (FUSED && wv == 5) {
         // ---------------- L2 warm-up wave: chunk c + AHEAD during chunk c; it
         // never waits for its loads except to bound the counter and at the end
-        char* wdst = hvbase + PL::HV;
+        char* wdst = DPLR ? ring + 2 * PL::FB + PL::UB + PL::GB : hvbase + PL::HV;
         const int pre = nch < PL::AHEAD ? nch : PL::AHEAD;
-        for (int c = 0; c < pre; ++c) warm_chunk<D, F32, FUSED>(ws, (int64_t)(co + c) * H + h, ct, l, wdst);
+        for (int c = 0; c < pre; ++c) warm_chunk<D, F32, FUSED, DPLR>(ws, (int64_t)(co + c) * H + h, ct, l, wdst);
         __builtin_amdgcn_s_barrier();
         for (int c = 0; c < nch; ++c) {
-            if (c + PL::AHEAD < nch) warm_chunk<D, F32, FUSED>(ws, (int64_t)(co + c + PL::AHEAD) * H + h, ct, l, wdst);
+            if (c + PL::AHEAD < nch)
+                warm_chunk<D, F32, FUSED, DPLR>(ws, (int64_t)(co + c + PL::AHEAD) * H + h, ct, l, wdst);
             wait_vm<48>();
             __builtin_amdgcn_s_barrier();
         }
@@ -316,7 +444,8 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
         // ---------------- producers (waves 1 and 2; 3 and 4 when fused)
         const int pw = FUSED ? wv - 3 : wv - 1;
         const int pre = nch < RING - 1 ? nch : RING - 1;
-        for (int c = 0; c < pre; ++c) produce<D, F32, FUSED>(ws, (int64_t)(co + c) * H + h, ct, pw, l, ring + c * PL::SLOT);
+        for (int c = 0; c < pre; ++c)
+            produce<D, F32, FUSED, DPLR>(ws, (int64_t)(co + c) * H + h, ct, pw, l, ring + c * PL::SLOT);
         // chunks 0 .. LOOK have landed once only the chunks issued after them are outstanding
         {
             const int need = nch - 1 < LOOK ? nch - 1 : LOOK;
@@ -327,7 +456,8 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
             // slot (c + RING - 1) % RING was last read by the compute wave in chunk
             // c - 1, which it finished before the barrier that ended that chunk
             const int nx = c + RING - 1;
-            if (nx < nch) produce<D, F32, FUSED>(ws, (int64_t)(co + nx) * H + h, ct, pw, l, ring + (nx % RING) * PL::SLOT);
+            if (nx < nch)
+                produce<D, F32, FUSED, DPLR>(ws, (int64_t)(co + nx) * H + h, ct, pw, l, ring + (nx % RING) * PL::SLOT);
             // chunk c + 1 + LOOK has landed once only the chunks issued after it are outstanding
             const int last = nch - 1 < nx ? nch - 1 : nx;
             const int need = nch - 1 < c + 1 + LOOK ? nch - 1 : c + 1 + LOOK;
@@ -388,6 +518,12 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
         f32x4_t gm[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) gm[t] = *reinterpret_cast<const f32x4_t*>(gsl + 16 * t + 4 * g);
+        u32x2_t kv[DPLR ? NT : 1];  // DPLR: K-^T V of this chunk and slab
+        if constexpr (DPLR) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                kv[t] = *reinterpret_cast<const u32x2_t*>(pbase + (c & 1) * PL::PBS + (t * 64 + l) * 8);
+        }
 
         // h_n = S as B-operand fragments (also the operand of W S below); to the
         // output wave's LDS buffer when fused, else to the workspace
@@ -415,9 +551,15 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
             vb[s] = frag_from_acc<F32>(V[2 * s], V[2 * s + 1]);
             P::store(vp + (s * 64 + l) * 8, vb[s]);
         }
-        // S <- Diag(gamma) S + K-^T V_new
+        // S <- Diag(gamma) S + K-^T V_new  (DPLR: + K-^T V + A-^T (-u))
 #pragma unroll
-        for (int t = 0; t < NT; ++t) S[t] = gm[t] * S[t];
+        for (int t = 0; t < NT; ++t) {
+            if constexpr (DPLR)
+                S[t] = gm[t] * S[t] + f32x4_t{h2f(kv[t][0] & 0xffffu), h2f(kv[t][0] >> 16), h2f(kv[t][1] & 0xffffu),
+                                              h2f(kv[t][1] >> 16)};
+            else
+                S[t] = gm[t] * S[t];
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -433,18 +575,18 @@ __global__ __launch_bounds__(FUSED ? 384 : 192) void recur_kernel(const float* _
     }
 }
 
-template <int D, bool F32, bool FUSED, bool OUT_F32>
+template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false>
 static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     using E = typename Pol<F32>::E;
-    using PL = RecurPlan<D, F32, FUSED>;
-    Ws<E> ws{(E*)a.qp, (E*)a.km, (E*)a.wn, (E*)a.u, (E*)a.aqk, a.gam, (E*)a.h, (E*)a.vn};
+    using PL = RecurPlan<D, F32, FUSED, DPLR>;
+    Ws<E> ws{(E*)a.qp, (E*)a.km, (E*)a.wn, (E*)a.u, (E*)a.aqk, a.gam, (E*)a.h, (E*)a.vn, (E*)a.am, (E*)a.oh};
     constexpr int NT = D / 16;
     const int NU = a.N * a.H;
-    auto kern = recur_kernel<D, F32, FUSED, OUT_F32>;
+    auto kern = recur_kernel<D, F32, FUSED, OUT_F32, DPLR>;
     const hipError_t e = allow_dynamic_lds((const void*)kern, PL::LDS);
     if (e != hipSuccess) return e;
-    dim3 grid(NU * NT), block(FUSED ? 384 : 192);
-    hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.cu, a.N, a.T, a.H, ws, a.o);
+    dim3 grid(NU * NT), block(FUSED ? (DPLR ? 448 : 384) : 192);
+    hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.cu, a.N, a.T, a.H, ws, a.o, a.v);
     return hipGetLastError();
 }
 
@@ -455,6 +597,13 @@ static hipError_t launch_recur_d(const ChunkArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_recur(const ChunkArgs& a, hipStream_t st) {
+    if (a.dplr) {  // 16-bit factors only (checked by the caller)
+        if (a.D == 128)
+            return a.out_f32 ? launch_recur_t<128, false, true, true, true>(a, st)
+                             : launch_recur_t<128, false, true, false, true>(a, st);
+        return a.out_f32 ? launch_recur_t<64, false, true, true, true>(a, st)
+                         : launch_recur_t<64, false, true, false, true>(a, st);
+    }
     return a.D == 128 ? launch_recur_d<128>(a, st) : launch_recur_d<64>(a, st);
 }
 

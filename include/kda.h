@@ -148,6 +148,43 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
                                size_t workspace_bytes, void* stream, void* const* events);
 
 /*
+ * Bytes of device workspace kda_dplr_chunk_fwd needs (host call, no device
+ * access): seven 16-bit per-chunk factors and the chunk decay, for at most
+ * floor((T_total + 63*N) / 64) chunks per head. in_dtype must be KDA_BF16.
+ *   bytes: host out-pointer, written on KDA_OK.
+ */
+kda_status kda_dplr_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk,
+                                             int32_t dv, kda_dtype in_dtype, size_t* bytes);
+
+/*
+ * Chunkwise prefill of the general diagonal-plus-low-rank (DPLR) transition,
+ * the operator KDA specialises, for comparison with kda_chunk_fwd:
+ *
+ *     S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t
+ *
+ * with free low-rank vectors a_t, b_t per (token, head). KDA is the case
+ * a = beta k, b = alpha * k with written key beta k (GeekNews "Kimi Linear"
+ * summary, section "Menos computação que o DPLR geral": tying both vectors
+ * to the key saves two of the four gated intra-chunk matrices and three
+ * chunk products).
+ *
+ *   q, k, a, b    [T_total, H, dk] bf16 (in_dtype must be KDA_BF16)
+ *   v             [T_total, H, dv] bf16
+ *   log_alpha     [T_total, H, dk] gate_dtype
+ *   initial_state, cu_seqlens, o, final_state, workspace: as kda_chunk_fwd
+ *                 (workspace sized by kda_dplr_chunk_fwd_workspace_size)
+ * Same conventions, size limits, error codes and determinism as
+ * kda_chunk_fwd; there is no beta input. Two kernels are enqueued (chunk
+ * preparation, then the state recursion with the fused output).
+ */
+kda_status kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const void* b,
+                              const void* log_alpha, const float* initial_state,
+                              const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
+                              int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype gate_dtype,
+                              kda_dtype out_dtype, void* o, float* final_state, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * One recurrent decode step for N independent sequences, one token each:
  * kda_decode_step(q, k, v, log_alpha, beta, state) -> (o, state').
  *

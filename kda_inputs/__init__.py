@@ -24,6 +24,13 @@ per channel, with shift 0 for ``tiny-fp32`` and +2 for the bf16 workloads; the
 ``-slow`` variants use shift -2 (mean alpha near 0.84). Everything is drawn in
 fp32 and rounded once to the input dtype with round-to-nearest-even.
 
+General-DPLR comparison inputs (``make_dplr``): the same q, k, v, log_alpha
+as the named workload, plus low-rank vectors a = beta * a_hat and b = a_hat
+with a_hat ~ N(0,1) L2-normalised over dk, drawn independently of k (beta is
+the workload's sigmoid draw). Then Diag(alpha) - a b^T is symmetric with
+eigenvalues in [-beta, 1], so the state stays bounded over any length while
+a and b share nothing with the written key k.
+
 Random numbers come from torch generators seeded from (workload, tensor,
 window); on a GPU device the draws happen on that device (Philox), so the same
 seed gives the same tensors on every run of the same software stack.
@@ -215,3 +222,26 @@ def make_decode(N: int = 256, H: int = 32, d: int = 128, steps: int = 1000, devi
         fill_token_inputs(N, H, d, d, dtype, device, gate_shift, parts + ("step", s),
                           out=(q[s], k[s], v[s], la[s], b[s]))
     return dict(state=s0, q=q, k=k, v=v, log_alpha=la, beta=b)
+
+
+@dataclasses.dataclass
+class DplrCase(PrefillCase):
+    a: Optional[torch.Tensor] = None  # [T_total, H, dk]
+    b: Optional[torch.Tensor] = None  # [T_total, H, dk]
+
+
+def make_dplr(workload: str = "prefill-4k", device="cpu", **kw) -> DplrCase:
+    """A prefill case of the named workload (same overrides as ``make_prefill``)
+    with the low-rank vectors of the general DPLR transition added."""
+    base = make_prefill(workload, device, **kw)
+    T, H, dk = base.T_total, base.H, base.dk
+    a = torch.empty(T, H, dk, dtype=base.q.dtype, device=device)
+    b = torch.empty_like(a)
+    parts = ("dplr", workload, kw.get("seed", 0), H, dk, str(base.q.dtype), T)
+    for w0 in range(0, T, WINDOW):
+        n = min(WINDOW, T - w0)
+        sl = slice(w0, w0 + n)
+        ah = _l2n(_normal((n, H, dk), device, *parts, "ahat", w0 // WINDOW))
+        a[sl] = (base.beta[sl].float()[..., None] * ah).to(a.dtype)
+        b[sl] = ah.to(b.dtype)
+    return DplrCase(**{f.name: getattr(base, f.name) for f in dataclasses.fields(PrefillCase)}, a=a, b=b)

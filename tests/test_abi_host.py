@@ -29,7 +29,8 @@ def test_library_exports_every_declared_function():
     lib = kda._load()
     names = declared_functions()
     assert names == ["kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_timed",
-                     "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_status_str"]
+                     "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_dplr_chunk_fwd",
+                     "kda_dplr_chunk_fwd_workspace_size", "kda_status_str"]
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -141,9 +142,52 @@ def test_decode_validation():
     assert decode_call(v=v, state=v) == ALIAS
 
 
+def test_dplr_workspace_size_formula():
+    # per chunk-head, d = 128: Q+, K-^T, A-^T, -W', -U', A_qk V 16 KiB each (fp16),
+    # A_qa 8 KiB, gamma 512 B -> 107008 B
+    assert kda.dplr_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 107008
+    assert kda.dplr_workspace_size(3, 100, 2, 64, 64) == ((100 + 63 * 3) // 64) * 2 * (6 * 8192 + 8192 + 256)
+    with pytest.raises(kda.KDAError):
+        kda.dplr_workspace_size(1, 10, 1, 96, 96)
+    out = ctypes.c_size_t(0)
+    assert kda._load().kda_dplr_chunk_fwd_workspace_size(1, 10, 1, 64, 64, F32, ctypes.byref(out)) == UNSUP
+
+
+def dplr_call(**over):
+    f = Fake()
+    a = dict(q=f(), k=f(), v=f(), a=f(), b=f(), la=f(), s0=None, cu=None, N=1, T=256, H=2, dk=64, dv=64,
+             in_dt=BF16, gate_dt=BF16, out_dt=F32, o=f(), sf=f(), ws=f(), ws_bytes=1 << 40, stream=None)
+    a.update(over)
+    P = ctypes.c_void_p
+    return kda._load().kda_dplr_chunk_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["a"]), P(a["b"]), P(a["la"]),
+                                          P(a["s0"]), P(a["cu"]), a["N"], a["T"], a["H"], a["dk"], a["dv"],
+                                          a["in_dt"], a["gate_dt"], a["out_dt"], P(a["o"]), P(a["sf"]),
+                                          P(a["ws"]), a["ws_bytes"], P(a["stream"]))
+
+
+def test_dplr_validation():
+    assert dplr_call(a=None) == NULL
+    assert dplr_call(b=None) == NULL
+    assert dplr_call(N=2) == SHAPE
+    assert dplr_call(T=1 << 31) == SHAPE
+    assert dplr_call(in_dt=F32) == UNSUP  # 16-bit factors only
+    assert dplr_call(dk=64, dv=128) == UNSUP
+    f = Fake()
+    assert dplr_call(b=f(8)) == ALIGN
+    a_ = f()
+    assert dplr_call(a=a_, o=a_ + 128) == ALIAS
+    b_ = f()
+    assert dplr_call(b=b_, sf=b_) == ALIAS
+    need = kda.dplr_workspace_size(1, 256, 2, 64, 64)
+    assert dplr_call(ws_bytes=need - 1) == WORKSPACE
+    w = f()
+    assert dplr_call(ws=w, b=w + need // 2) == ALIAS
+
+
 @pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="would launch on fake pointers")
 def test_valid_arguments_reach_the_launch_without_gpu():
     """With no GPU present, valid arguments pass validation and the launch
     itself reports KDA_ERR_HIP (the library never falls back to the CPU)."""
     assert decode_call() == HIP
     assert chunk_call() == HIP
+    assert dplr_call() == HIP

@@ -65,3 +65,12 @@ def test_decode_shapes(name, shape):
         a[name] = torch.zeros(*shape)
     with pytest.raises(ValueError, match=name):
         kda.decode_step(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["state"], o=o)
+
+
+@pytest.mark.parametrize("name", ["a", "b"])
+def test_dplr_low_rank_vector_shapes(name):
+    z = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)
+    a = dict(q=z(T, H, D), k=z(T, H, D), v=z(T, H, D), a=z(T, H, D), b=z(T, H, D), log_alpha=z(T, H, D))
+    a[name] = z(T, H, D - 1)
+    with pytest.raises(ValueError, match=name):
+        kda.dplr_chunk_fwd(**a)

@@ -101,3 +101,58 @@ def decode(ws: torch.Tensor, N, T, H, D, f32, have_cu, gc, h):
     out["h"] = Hm
     out["Vn"] = Vn
     return out
+
+
+def plan_dplr(NC, H, D):
+    """Offsets of the general-DPLR workspace (16-bit factors): qp, km, am, wn,
+    u, aqk, oh, gam."""
+    ch = NC * H
+    f = ch * CH * D * 2
+    sizes = [f, f, f, f, f, ch * CH * CH * 2, f, ch * D * 4]
+    off, o = [], 0
+    for s in sizes:
+        off.append(o)
+        o = (o + s + 255) // 256 * 256
+    return off, o
+
+
+def _tiles(raw16: np.ndarray, D) -> np.ndarray:
+    """[D/16][4][64 lanes][4] accumulator-order tiles -> [64, D]."""
+    t = raw16.reshape(D // 16, 4, 64, 4)
+    out = np.zeros((CH, D))
+    for ct in range(D // 16):
+        for I in range(4):
+            for l in range(64):
+                n, g = l & 15, l >> 4
+                out[16 * I + 4 * g:16 * I + 4 * g + 4, 16 * ct + n] = t[ct, I, l]
+    return out
+
+
+def decode_dplr(ws: torch.Tensor, N, T, H, D, have_cu, gc, h):
+    """General-DPLR intermediates of chunk slot gc, head h (fp64): Qp, Km, Am,
+    W (= W'), U (= U'), Aqa, Oh (= A_qk V), gam."""
+    NC = chunk_capacity(N, T, have_cu)
+    off, _ = plan_dplr(NC, H, D)
+    raw = ws.cpu().numpy()
+    chh = gc * H + h
+    NS = D // 32
+
+    def arr(i, n_el):
+        b = off[i] + chh * n_el * 2
+        return _as_f(raw[b:b + n_el * 2].copy(), False)
+
+    def split_cols(x, nsl):  # [rows][nsl][32] split order -> [rows, 32 nsl]
+        out = np.zeros((x.shape[0], 32 * nsl))
+        out[:, (np.arange(nsl)[:, None] * 32 + SPLIT[None, :]).ravel()] = x.reshape(x.shape[0], -1)
+        return out
+
+    out = {"Qp": split_cols(arr(0, CH * D).reshape(CH, NS, 32), NS),
+           "Km": split_cols(arr(1, D * CH).reshape(D, 2, 32), 2).T,
+           "Am": split_cols(arr(2, D * CH).reshape(D, 2, 32), 2).T,
+           "W": -split_cols(arr(3, CH * D).reshape(CH, NS, 32), NS),
+           "U": -_tiles(arr(4, CH * D), D),
+           "Aqa": split_cols(arr(5, CH * CH).reshape(CH, 2, 32), 2),
+           "Oh": _tiles(arr(6, CH * D), D)}
+    b = off[7] + chh * D * 4
+    out["gam"] = raw[b:b + D * 4].copy().view(np.float32).astype(np.float64)
+    return out
