@@ -81,7 +81,8 @@ WsPlan plan_workspace(int64_t NC, int H, int D, bool f32) {
 WsPlan plan_workspace_dplr(int64_t NC, int H, int D) {
     const size_t ch = (size_t)NC * (size_t)H;
     const size_t f = ch * KDA_CHUNK * D * 2;  // one [64][D] fp16 factor per chunk-head
-    const size_t sz[8] = {f, f, f, f, f, ch * KDA_CHUNK * KDA_CHUNK * 2, f, ch * D * 4};
+    const size_t kv = ch * D * (D > KDA_CHUNK ? D : KDA_CHUNK) * 2;  // K-^T V (and the K-^T scratch)
+    const size_t sz[8] = {f, kv, f, f, f, ch * KDA_CHUNK * KDA_CHUNK * 2, f, ch * D * 4};
     WsPlan p;
     size_t o = 0;
     for (int i = 0; i < 8; ++i) {

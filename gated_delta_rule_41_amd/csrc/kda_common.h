@@ -333,7 +333,9 @@ __device__ __forceinline__ void seq_chunks(const int32_t* __restrict__ cu, int T
 //   h    [D/16][D/32][64 lanes][8]   chunk-entry state as B-operand fragments (value col tile, k slice)
 //   vn   [D/16][2][64 lanes][8]      corrected values V_new as B-operand fragments
 // The general DPLR transition (16-bit factors only) uses the same arrays for
-// its analogues -- qp: Q+, km: K-^T, wn: -W', u: -U', aqk: A_qa, gam -- and two more:
+// its analogues -- qp: Q+, wn: -W', u: -U', aqk: A_qa, gam; km holds the state
+// update's state-independent part K-^T V [D/16 col tile][D/16 row tile][64 lanes][4]
+// (D x max(D, 64) elements) -- and two more:
 //   am   [D][64]   decayed A-vectors A- = exp(g_last - g) * a, transposed like km
 //   oh   [D/16][4][64 lanes][4]   the output's state-independent part A_qk V, accumulator-tile order
 template <typename E>

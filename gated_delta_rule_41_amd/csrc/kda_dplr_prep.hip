@@ -26,7 +26,7 @@
 // block's whole gate range (first row included). A range above GUARD switches
 // the chunk to an exact elementwise path.
 //
-// Outputs (workspace, layouts in kda_common.h): Q+ (qp), K-^T (km), A-^T (am),
+// Outputs (workspace, layouts in kda_common.h): Q+ (qp), K-^T V (km), A-^T (am),
 // -W' (wn), -U' (u), A_qa (aqk), A_qk V (oh) and gamma = 2^G_last. The state
 // recursion then runs the KDA chain with -u in place of V_new (see
 // kda_recur.hip). Rows past the end of a sequence are zero (q = k = v = a =
@@ -278,7 +278,10 @@ __global__ __launch_bounds__(256, 2) void dplr_prep_kernel(const uint16_t* q, co
     // ---- 3. gated scalings
     float qs[NS][8], bs[NS][8];  // left factors q 2^(G - E_aw), b 2^(E - E_aw) (fast path); b 2^E (slow)
     E* qp_out = ws.qp + chh * 64 * D;
-    E* km_out = ws.km + chh * D * 64;
+    // K-^T goes to the start of this chunk-head's K-^T V array, as scratch: it is
+    // read back (by other waves) once every wave is past the barriers below,
+    // and the product overwrites it
+    E* km_out = ws.km + chh * D * D;
     E* am_out = ws.am + chh * D * 64;
     if (!slow) {
 #pragma unroll
@@ -564,7 +567,38 @@ __global__ __launch_bounds__(256, 2) void dplr_prep_kernel(const uint16_t* q, co
             if (!isW) *reinterpret_cast<u32x2_t*>(u_out + ((ct * 4 + I) * 64 + l) * 4) = pack4h(X[tt][I], -1.f);
         }
     }
-    __syncthreads();  // every block and tile read: R1 takes the -W' staging
+    // ---- 8. the state update's state-independent part K-^T V, dk x dv: wave w
+    // takes row tiles t = w * NT/4 .. and every column tile; K-^T (scratch,
+    // written before several barriers) as A operands, the V tiles as B
+    constexpr int TW = NCT / 4;  // row tiles per wave
+    f32x4_t kvt[TW][NCT];
+    {
+        Frag ka[TW][2];
+#pragma unroll
+        for (int i = 0; i < TW; ++i)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) ka[i][s] = P::load(km_out + ((16 * (w * TW + i) + n) * 2 + s) * 32 + g * 8);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const Frag b0 = tiles_frag(Vt_t, ct, 0, l), b1 = tiles_frag(Vt_t, ct, 1, l);
+#pragma unroll
+            for (int i = 0; i < TW; ++i) {
+                kvt[i][ct] = zero;
+                P::mma(kvt[i][ct], ka[i][0], b0);
+                P::mma(kvt[i][ct], ka[i][1], b1);
+            }
+        }
+    }
+    __syncthreads();  // every block and tile read, the K-^T scratch too: R1 takes the -W' staging
+    {
+        // K-^T V in [column tile][row tile][64 lanes][4]: one slab's share is 4 D bytes, contiguous
+        E* kv_out = ws.km + chh * D * D;
+#pragma unroll
+        for (int i = 0; i < TW; ++i)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                *reinterpret_cast<u32x2_t*>(kv_out + ((ct * NCT + w * TW + i) * 64 + l) * 4) = pack4h(kvt[i][ct], 1.f);
+    }
     if (isW) {
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {

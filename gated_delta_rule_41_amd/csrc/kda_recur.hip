@@ -52,6 +52,7 @@ struct RecurPlan {
     // (fp16, accumulator-tile order), by chunk parity
     static constexpr int PBS = (D / 16) * 64 * 4 * 2;
     static constexpr int PB = DPLR ? 2 * PBS : 0;
+    static_assert(PBS % 1024 == 0, "K-^T V share in whole 1 KiB loads");
     // target of the L2 warm-up loads (never read); DPLR has no room for it and
     // aims them at the unread tail of ring slot 0's gamma region instead
     static constexpr int WARM = (FUSED && !DPLR) ? 256 : 0;
@@ -73,10 +74,10 @@ struct RecurPlan {
     static constexpr int LINES = 3 * LINES_W + LINES_A;
     static constexpr int LINES_PER = (LINES + D / 16 - 1) / (D / 16);
     static constexpr int LINES_U = UB / 128, LINES_G = GB / 128;
-    // DPLR: the second load also covers this slab's share of K-^T and its A_qk V tiles
-    static constexpr int LINES_K = DPLR ? FB / 128 / (D / 16) : 0, LINES_O = DPLR ? UB / 128 : 0;
-    static constexpr int LINES_2 = LINES_U + LINES_G + LINES_K + LINES_O;
-    static_assert(!FUSED || (LINES_PER <= 64 && LINES_2 <= 64), "two warm-up loads per chunk");
+    // DPLR: the second load also covers this slab's A_qk V tiles, a third its K-^T V share
+    static constexpr int LINES_O = DPLR ? UB / 128 : 0, LINES_KV = DPLR ? PBS / 128 : 0;
+    static constexpr int LINES_2 = LINES_U + LINES_G + LINES_O;
+    static_assert(!FUSED || (LINES_PER <= 64 && LINES_2 <= 64 && LINES_KV <= 64), "warm-up loads per chunk");
     static constexpr int AHEAD = 3;  // chunks warmed ahead of the compute wave (2..6 measured; 3 best)
 };
 
@@ -181,14 +182,17 @@ __device__ __forceinline__ void warm_chunk(const Ws<typename Pol<F32>::E>& ws, i
         pu = reinterpret_cast<const char*>(ws.u + chh * 64 * D + (int64_t)ct * 4 * 64 * 4) + m * 128;
     else if (m < PL::LINES_U + PL::LINES_G)
         pu = reinterpret_cast<const char*>(ws.gam + chh * D) + (m - PL::LINES_U) * 128;
-    else if (m < PL::LINES_U + PL::LINES_G + PL::LINES_K)
-        pu = reinterpret_cast<const char*>(ws.km + chh * 64 * D) +
-             (ct * PL::LINES_K + m - PL::LINES_U - PL::LINES_G) * 128;
     else
         pu = reinterpret_cast<const char*>(ws.oh + chh * 64 * D + (int64_t)ct * 4 * 64 * 4) +
-             (m - PL::LINES_U - PL::LINES_G - PL::LINES_K) * 128;
+             (m - PL::LINES_U - PL::LINES_G) * 128;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)pu,
                                      (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+    if constexpr (DPLR) {
+        const int k = l < PL::LINES_KV ? l : 0;
+        const char* pk = reinterpret_cast<const char*>(ws.km + chh * D * D) + (int64_t)ct * PL::PBS + k * 128;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)pk,
+                                         (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+    }
 }
 
 // With FUSED, two more waves compute each chunk's output O = Q+ h_n + A_qk V_new
@@ -203,16 +207,14 @@ __device__ __forceinline__ void warm_chunk(const Ws<typename Pol<F32>::E>& ws, i
 // the same with -u = -U' + (-W') h in place of V_new and A-^T in place of
 // K-^T, plus two state-independent terms: the state update adds K-^T V and the
 // output adds A_qk V (from the workspace, as the output accumulators' start).
-// A seventh wave computes K-^T V for this slab one chunk ahead of the compute
-// wave and leaves it in an LDS buffer by chunk parity; its operands are
-// fetched one chain step earlier still.
+// The prep kernel computes K-^T V; a seventh wave copies this slab's share of
+// it into an LDS buffer (by chunk parity) one chunk ahead of the compute wave.
 template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false>
 __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 192) void recur_kernel(const float* __restrict__ s0,
                                                                   float* __restrict__ s_final,
                                                                   const int32_t* __restrict__ cu, int N, int T,
                                                                   int H, Ws<typename Pol<F32>::E> ws,
-                                                                  void* __restrict__ o,
-                                                                  const void* __restrict__ vsrc) {
+                                                                  void* __restrict__ o) {
     using P = Pol<F32>;
     using E = typename P::E;
     using Frag = typename P::Frag;
@@ -346,78 +348,24 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 192) void recur_kernel
     }
 
     if (DPLR && wv == 6) {
-        // ---------------- DPLR: K-^T V of chunk c + 1 in iteration c, for the
-        // compute wave's state update in iteration c + 1. A wave of its own, so
-        // that the only loads it ever waits for are its own operands, issued
-        // one iteration before their use.
-        const int tstart = cu ? cu[seq] : 0;
-        const int len = cu ? cu[seq + 1] - tstart : T;
-        // DPLR: K-^T V of chunk c for this slab. Its operands (K-^T fragments,
-        // and this slab's values over the chunk rows, zero past the sequence
-        // end) are loaded by load_kv one iteration before put_kv multiplies
-        // them and stores the product in buffer c & 1.
-        Frag kq[DPLR ? NT : 1][2];
-        uint16_t vraw[2][8];  // values as loaded (bf16 bits); converted only when used
-        int vlen = 0;         // rows of the chunk whose values are loaded
-        auto load_kv = [&](int c) {
-            if constexpr (DPLR) {
-                const int64_t chh = (int64_t)(co + c) * H + h;
-                const E* kp = ws.km + chh * D * 64;
+        // ---------------- DPLR: the state update's state-independent part K-^T V
+        // (computed by the prep kernel) of chunk c + 1, copied into LDS buffer
+        // (c + 1) & 1 during iteration c: the compute wave reads it in
+        // iteration c + 1, and its last reader of that buffer (chunk c - 1)
+        // finished before the barrier that ended iteration c - 1
+        auto fetch = [&](int c) {
+            const char* src = reinterpret_cast<const char*>(ws.km + ((int64_t)(co + c) * H + h) * D * D) +
+                              (int64_t)ct * PL::PBS;
+            char* dst = pbase + (c & 1) * PL::PBS;
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) kq[t][s] = P::load(kp + ((16 * t + n) * 2 + s) * 32 + g * 8);
-                const int t0 = tstart + 64 * c;
-                const int L = min(64, len - 64 * c);
-                const uint16_t* vin = static_cast<const uint16_t*>(vsrc);
-                // rows past the end load row 0 (branch-free) and are zeroed in put_kv
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) {
-                        const int row = 32 * s + kslot(g, jj);
-                        vraw[s][jj] = vin[((int64_t)(t0 + (row < L ? row : 0)) * H + h) * D + 16 * ct + n];
-                    }
-                vlen = L;
-            }
+            for (int j = 0; j < PL::PBS / 1024; ++j) dma16(src + j * 1024 + l * 16, dst + j * 1024);
         };
-        auto put_kv = [&](int c) {
-            if constexpr (DPLR) {
-                Frag vq[2];
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    float x[8];
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) x[jj] = 32 * s + kslot(g, jj) < vlen ? bf2f(vraw[s][jj]) : 0.f;
-                    vq[s] = P::make(x);
-                }
-                f32x4_t pk[NT];
-#pragma unroll
-                for (int t = 0; t < NT; ++t) pk[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) P::mma(pk[t], kq[t][s], vq[s]);
-                char* pb = pbase + (c & 1) * PL::PBS;
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    u32x2_t w2;
-                    w2[0] = (uint32_t)f2h(pk[t][0]) | ((uint32_t)f2h(pk[t][1]) << 16);
-                    w2[1] = (uint32_t)f2h(pk[t][2]) | ((uint32_t)f2h(pk[t][3]) << 16);
-                    *reinterpret_cast<u32x2_t*>(pb + (t * 64 + l) * 8) = w2;
-                }
-                wait_lgkm0();  // in LDS before the next barrier hands it over
-            }
-        };
-        if (nch > 0) {
-            load_kv(0);
-            put_kv(0);
-            if (nch > 1) load_kv(1);
-        }
+        if (nch > 0) fetch(0);
+        wait_vm<0>();
         __builtin_amdgcn_s_barrier();
         for (int c = 0; c < nch; ++c) {
-            if (c + 1 < nch) put_kv(c + 1);
-            if (c + 2 < nch) load_kv(c + 2);
+            if (c + 1 < nch) fetch(c + 1);
+            wait_vm<0>();
             __builtin_amdgcn_s_barrier();
         }
         return;
@@ -586,7 +534,7 @@ static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     const hipError_t e = allow_dynamic_lds((const void*)kern, PL::LDS);
     if (e != hipSuccess) return e;
     dim3 grid(NU * NT), block(FUSED ? (DPLR ? 448 : 384) : 192);
-    hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.cu, a.N, a.T, a.H, ws, a.o, a.v);
+    hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.cu, a.N, a.T, a.H, ws, a.o);
     return hipGetLastError();
 }
 

@@ -248,7 +248,7 @@ def dplr_chunk_step(q, k, v, a, b, la, S, *, sub=None, blocked=None):
     O = Qp @ S + Oh - Aqa @ u
     S_next = gam[:, None] * S + Km.T @ v - Am.T @ u
     inter = dict(g=g, Qp=Qp, Km=Km, Am=Am, Bt=Bt, gam=gam, Aba=Aba, Abk=Abk, Aqk=Aqk, Aqa=Aqa,
-                 W=W, U=U, u=u, Oh=Oh, h=S.copy())
+                 W=W, U=U, u=u, Oh=Oh, KV=Km.T @ v, h=S.copy())
     return O, S_next, inter
 
 

@@ -143,9 +143,9 @@ def test_decode_validation():
 
 
 def test_dplr_workspace_size_formula():
-    # per chunk-head, d = 128: Q+, K-^T, A-^T, -W', -U', A_qk V 16 KiB each (fp16),
-    # A_qa 8 KiB, gamma 512 B -> 107008 B
-    assert kda.dplr_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 107008
+    # per chunk-head, d = 128: Q+, A-^T, -W', -U', A_qk V 16 KiB each (fp16),
+    # K-^T V 32 KiB, A_qa 8 KiB, gamma 512 B -> 123392 B
+    assert kda.dplr_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 123392
     assert kda.dplr_workspace_size(3, 100, 2, 64, 64) == ((100 + 63 * 3) // 64) * 2 * (6 * 8192 + 8192 + 256)
     with pytest.raises(kda.KDAError):
         kda.dplr_workspace_size(1, 10, 1, 96, 96)

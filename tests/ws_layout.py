@@ -108,7 +108,7 @@ def plan_dplr(NC, H, D):
     u, aqk, oh, gam."""
     ch = NC * H
     f = ch * CH * D * 2
-    sizes = [f, f, f, f, f, ch * CH * CH * 2, f, ch * D * 4]
+    sizes = [f, ch * D * max(D, CH) * 2, f, f, f, ch * CH * CH * 2, f, ch * D * 4]
     off, o = [], 0
     for s in sizes:
         off.append(o)
@@ -129,8 +129,8 @@ def _tiles(raw16: np.ndarray, D) -> np.ndarray:
 
 
 def decode_dplr(ws: torch.Tensor, N, T, H, D, have_cu, gc, h):
-    """General-DPLR intermediates of chunk slot gc, head h (fp64): Qp, Km, Am,
-    W (= W'), U (= U'), Aqa, Oh (= A_qk V), gam."""
+    """General-DPLR intermediates of chunk slot gc, head h (fp64): Qp, KV (= K-^T V),
+    Am, W (= W'), U (= U'), Aqa, Oh (= A_qk V), gam."""
     NC = chunk_capacity(N, T, have_cu)
     off, _ = plan_dplr(NC, H, D)
     raw = ws.cpu().numpy()
@@ -141,13 +141,23 @@ def decode_dplr(ws: torch.Tensor, N, T, H, D, have_cu, gc, h):
         b = off[i] + chh * n_el * 2
         return _as_f(raw[b:b + n_el * 2].copy(), False)
 
+    def kv_tiles(x):  # [D/16 col tile][D/16 row tile][64 lanes][4] -> [D, D]
+        t = x.reshape(D // 16, D // 16, 64, 4)
+        out = np.zeros((D, D))
+        for ct in range(D // 16):
+            for rt in range(D // 16):
+                for l in range(64):
+                    n, g = l & 15, l >> 4
+                    out[16 * rt + 4 * g:16 * rt + 4 * g + 4, 16 * ct + n] = t[ct, rt, l]
+        return out
+
     def split_cols(x, nsl):  # [rows][nsl][32] split order -> [rows, 32 nsl]
         out = np.zeros((x.shape[0], 32 * nsl))
         out[:, (np.arange(nsl)[:, None] * 32 + SPLIT[None, :]).ravel()] = x.reshape(x.shape[0], -1)
         return out
 
     out = {"Qp": split_cols(arr(0, CH * D).reshape(CH, NS, 32), NS),
-           "Km": split_cols(arr(1, D * CH).reshape(D, 2, 32), 2).T,
+           "KV": kv_tiles(arr(1, D * max(D, CH))[:D * D]),
            "Am": split_cols(arr(2, D * CH).reshape(D, 2, 32), 2).T,
            "W": -split_cols(arr(3, CH * D).reshape(CH, NS, 32), NS),
            "U": -_tiles(arr(4, CH * D), D),
