@@ -46,8 +46,21 @@ KERNEL_BYTES_PER_TOKEN_HEAD = {            # compulsory traffic of each prefill 
 }
 # fp32 inputs (not benchmarked) run the unfused pair: recursion 776 + 768 (h_n,
 # V_new written), output 1152 + 512
-KERNEL_SYMBOL = {"prep": "prep_kernel", "recur": "recur_kernel", "decode": "decode_kernel"}
-KERNEL_SOURCE = {"prep": "kda_prep.hip", "recur": "kda_recur.hip", "decode": "kda_decode.hip"}
+KERNEL_SYMBOL = {"prep": "prep_kernel", "recur": "recur_kernel", "decode": "decode_kernel",
+                 "dplr_prep": "dplr_prep_kernel", "dplr_recur": "recur_kernel"}
+KERNEL_SOURCE = {"prep": "kda_prep.hip", "recur": "kda_recur.hip", "decode": "kda_decode.hip",
+                 "dplr_prep": "kda_dplr_prep.hip", "dplr_recur": "kda_recur.hip"}
+
+
+def kernel_key(short_name: str):
+    """Which of this library's kernels a demangled name (arguments stripped) is.
+    The state recursion's last template argument selects the DPLR chain."""
+    if short_name.startswith("recur_kernel<"):
+        return "dplr_recur" if short_name.endswith(", true>") else "recur"
+    for key in ("dplr_prep", "prep", "decode"):
+        if short_name.startswith(KERNEL_SYMBOL[key] + "<"):
+            return key
+    return None
 
 
 def hip_runtime():
@@ -312,7 +325,7 @@ def report_pmc(fetch_db: str, write_db: str, cal_fetch_db: str, cal_write_db: st
     for name in sorted(fe):
         if name not in wr:
             continue
-        kern = next((k for k, sym in KERNEL_SYMBOL.items() if name.startswith(sym)), None)
+        kern = kernel_key(name)
         b = fe[name][1] * 1024 * f_fetch + wr[name][1] * 1024 * f_write
         print(f"| `{name}` | {fe[name][0]} | {fe[name][1]:.0f} | {wr[name][1]:.0f} | {b:.4g} |")
         if kern is None:
@@ -402,7 +415,7 @@ def main(argv=None):
 
     if not args.no_dplr:
         dcase = ki.make_dplr("prefill-4k", dev)
-        dplr_ms, _, _ = time_dplr(kda, dcase, args.steps, 200)
+        dplr_ms, _, _ = time_dplr(kda, dcase, args.steps, max(3, min(200, args.warmup)))
         # per token-head, d = 128, chunk 64: four gated chunk matrices, three
         # WY/intra products, three d x d state products, output (see DESIGN)
         dplr_flops = 206165 * TH
@@ -410,7 +423,9 @@ def main(argv=None):
             "workload": "prefill-4k (+ a = beta a_hat, b = a_hat)", "ms_per_step": round(dplr_ms, 5),
             "tokens_per_s": round(case.T_total / (dplr_ms * 1e-3), 1),
             "tflops": round(dplr_flops / (dplr_ms * 1e-3) / 1e12, 2),
-            "time_ratio_dplr_over_kda": round(dplr_ms / wall_ms, 3)}
+            "time_ratio_dplr_over_kda": round(dplr_ms / wall_ms, 3),
+            "hbm_bytes_per_launch": {"prep": traffic_from_profiles("dplr_prep", TH),
+                                     "recur": traffic_from_profiles("dplr_recur", TH)}}
         del dcase
 
     if not args.no_decode:
