@@ -7,6 +7,8 @@ library is not built, importing the functions raises.
 
     o, final_state = chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None)
     o = decode_step(q, k, v, log_alpha, beta, state)          # state updated in place
+    grads = chunk_bwd(q, k, v, log_alpha, beta, d_o, initial_state=None, cu_seqlens=None,
+                      d_final_state=None)                     # dict of fp32 gradients
     o, final_state = dplr_chunk_fwd(q, k, v, a, b, log_alpha, initial_state=None, cu_seqlens=None)
                      # the general DPLR transition KDA specialises (comparison operator)
 """
@@ -18,8 +20,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "decode_step", "workspace_size", "dplr_chunk_fwd", "dplr_workspace_size",
-           "abi_version", "status_str", "library_path", "KDAError", "CHUNK"]
+__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "workspace_size", "bwd_workspace_size", "dplr_chunk_fwd",
+           "dplr_workspace_size", "abi_version", "status_str", "library_path", "KDAError", "CHUNK"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -69,6 +71,11 @@ def _load():
     lib.kda_dplr_chunk_fwd.restype = ctypes.c_int
     lib.kda_dplr_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, I32, I64, I32, I32, I32,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, SZ, P]
+    lib.kda_chunk_bwd_workspace_size.restype = ctypes.c_int
+    lib.kda_chunk_bwd_workspace_size.argtypes = [I32, I64, I32, I32, I32, ctypes.POINTER(SZ)]
+    lib.kda_chunk_bwd.restype = ctypes.c_int
+    lib.kda_chunk_bwd.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int, ctypes.c_int,
+                                  P, P, P, P, P, P, P, P, P, SZ, P]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
@@ -289,3 +296,68 @@ def dplr_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.T
     if st != 0:
         raise KDAError(st, "kda_dplr_chunk_fwd")
     return o, final_state
+
+
+def bwd_workspace_size(N: int, T_total: int, H: int, dk: int, dv: int) -> int:
+    """Workspace bytes of ``chunk_bwd``."""
+    out = ctypes.c_size_t(0)
+    st = _load().kda_chunk_bwd_workspace_size(int(N), int(T_total), int(H), int(dk), int(dv), ctypes.byref(out))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_bwd_workspace_size")
+    return int(out.value)
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor, beta: torch.Tensor,
+              d_o: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, d_final_state: Optional[torch.Tensor] = None, *,
+              want_initial_grad: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
+    """Backward of ``chunk_fwd`` (see ``kda_chunk_bwd`` in include/kda.h): the
+    same inputs, d_o [T, H, dv] fp32 and optionally d_final_state [N, H, dk, dv]
+    fp32. Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha, dbeta and
+    dinitial_state (None unless want_initial_grad)."""
+    lib = _load()
+    dev = q.device
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, log_alpha must be [T, H, dk] and v [T, H, dv]")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    items = [("q", q, (T, H, dk)), ("k", k, (T, H, dk)), ("v", v, (T, H, dv)),
+             ("log_alpha", log_alpha, (T, H, dk)), ("beta", beta, (T, H)), ("d_o", d_o, (T, H, dv))]
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 >= 2 offsets")
+        items.append(("cu_seqlens", cu_seqlens, None))
+        N = cu_seqlens.numel() - 1
+    else:
+        N = 1
+    if initial_state is not None:
+        items.append(("initial_state", initial_state, (N, H, dk, dv)))
+    if d_final_state is not None:
+        items.append(("d_final_state", d_final_state, (N, H, dk, dv)))
+    if workspace is not None:
+        items.append(("workspace", workspace, None))
+    _check(items, dev)
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state), ("d_o", d_o)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    in_dt = _dtype_code(q, "q")
+    gate_dt = _dtype_code(log_alpha, "log_alpha")
+    if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != log_alpha.dtype:
+        raise TypeError("q, k, v must share a dtype; log_alpha and beta must share a dtype")
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dq": torch.empty(T, H, dk, **f32), "dk": torch.empty(T, H, dk, **f32),
+         "dv": torch.empty(T, H, dv, **f32), "dlog_alpha": torch.empty(T, H, dk, **f32),
+         "dbeta": torch.empty(T, H, **f32),
+         "dinitial_state": torch.empty(N, H, dk, dv, **f32) if want_initial_grad else None}
+    sz = ctypes.c_size_t(0)
+    lib.kda_chunk_bwd_workspace_size(max(N, 1), T, H, dk, dv, ctypes.byref(sz))
+    if workspace is None:
+        workspace = torch.empty(max(int(sz.value), 1), dtype=torch.uint8, device=dev)
+    st = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+                           _ptr(cu_seqlens), N, T, H, dk, dv, in_dt, gate_dt, _ptr(d_o), _ptr(d_final_state),
+                           _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["dbeta"]),
+                           _ptr(g["dinitial_state"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_bwd")
+    return g

@@ -329,6 +329,132 @@ kda_status kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const
     return KDA_OK;
 }
 
+// backward workspace: forward recompute (fp32 factors, h_n, V_new), the state-gradient
+// recursion's operands and outputs, its added term, and the local kernel's scratch
+static size_t bwd_workspace(int64_t NC, int H, int D, size_t off[4]) {
+    const size_t f = plan_workspace(NC, H, D, true).total;
+    const size_t pb = align_up((size_t)NC * H * D * D * 4, 256);
+    const size_t sc = align_up((size_t)NC * H * (size_t)bwd_scr_floats(D) * 4, 256);
+    off[0] = 0;
+    off[1] = f;
+    off[2] = 2 * f;
+    off[3] = 2 * f + pb;
+    return 2 * f + pb + sc;
+}
+
+static void carve(ChunkArgs& a, char* base, int64_t NC, int H, int D) {
+    const WsPlan p = plan_workspace(NC, H, D, true);
+    a.qp = base + p.off[0];
+    a.km = base + p.off[1];
+    a.wn = base + p.off[2];
+    a.u = base + p.off[3];
+    a.aqk = base + p.off[4];
+    a.gam = reinterpret_cast<float*>(base + p.off[5]);
+    a.h = base + p.off[6];
+    a.vn = base + p.off[7];
+}
+
+kda_status kda_chunk_bwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
+                                        size_t* bytes) {
+    if (!bytes) return KDA_ERR_NULL;
+    if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
+    if (!head_ok(dk, dv)) return KDA_ERR_UNSUPPORTED;
+    size_t off[4];
+    *bytes = bwd_workspace(chunk_capacity(N, T_total, true), H, dk, off);
+    return KDA_OK;
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
+                         const float* initial_state, const int32_t* cu_seqlens, int32_t N, int64_t T_total,
+                         int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype gate_dtype,
+                         const float* d_o, const float* d_final_state, float* dq, float* dk_out, float* dv_out,
+                         float* dlog_alpha, float* dbeta, float* d_initial_state, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
+    if (T_total > 0 && (!q || !k || !v || !log_alpha || !beta || !d_o || !dq || !dk_out || !dv_out ||
+                        !dlog_alpha || !dbeta))
+        return KDA_ERR_NULL;
+    if (!cu_seqlens && N != 1) return KDA_ERR_SHAPE;
+    if (!head_ok(dk, dv) || !dtype_ok(in_dtype) || !dtype_ok(gate_dtype)) return KDA_ERR_UNSUPPORTED;
+    const void* al[] = {q, k, v, log_alpha, initial_state, d_o, d_final_state, dq, dk_out, dv_out, dlog_alpha,
+                        d_initial_state};
+    for (const void* p : al)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    if (!aligned_to(beta, esize(gate_dtype)) || !aligned_to(dbeta, 4) || !aligned_to(cu_seqlens, 4))
+        return KDA_ERR_ALIGN;
+    const size_t T = (size_t)T_total;
+    const size_t nqk = T * H * dk * esize(in_dtype), nv = T * H * dv * esize(in_dtype);
+    const size_t nla = T * H * dk * esize(gate_dtype), nb = T * H * esize(gate_dtype);
+    const size_t ns = (size_t)N * H * dk * dv * 4, ncu = cu_seqlens ? (size_t)(N + 1) * 4 : 0;
+    const size_t ndo = T * H * dv * 4, ng = T * H * dk * 4, ngv = T * H * dv * 4, ngb = T * H * 4;
+    const void* ins[8] = {q, k, v, log_alpha, beta, initial_state, cu_seqlens, d_o};
+    const size_t nin[8] = {nqk, nqk, nv, nla, nb, ns, ncu, ndo};
+    const void* dfin = d_final_state;
+    void* outs[6] = {dq, dk_out, dv_out, dlog_alpha, dbeta, d_initial_state};
+    const size_t nout[6] = {ng, ng, ngv, ng, ngb, ns};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 8; ++j)
+            if (overlaps(outs[i], nout[i], ins[j], nin[j])) return KDA_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], nout[i], outs[j], nout[j])) return KDA_ERR_ALIAS;
+        // the initial states' gradient may replace the final states' (in-place)
+        if (!(i == 5 && outs[i] == dfin) && overlaps(outs[i], nout[i], dfin, ns)) return KDA_ERR_ALIAS;
+    }
+    const int64_t NC = chunk_capacity(N, T_total, cu_seqlens != nullptr);
+    size_t off[4];
+    const size_t need = bwd_workspace(NC, H, dk, off);
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    for (int j = 0; j < 8; ++j)
+        if (overlaps(workspace, need, ins[j], nin[j])) return KDA_ERR_ALIAS;
+    for (int i = 0; i < 6; ++i)
+        if (overlaps(workspace, need, outs[i], nout[i])) return KDA_ERR_ALIAS;
+    if (overlaps(workspace, need, dfin, ns)) return KDA_ERR_ALIAS;
+    if (NC >= (int64_t(1) << 31) / H) return KDA_ERR_SHAPE;
+
+    char* w = static_cast<char*>(workspace);
+    BwdArgs b;
+    ChunkArgs& F = b.fwd;
+    F.q = q;
+    F.k = k;
+    F.v = v;
+    F.la = log_alpha;
+    F.beta = beta;
+    F.s0 = initial_state;
+    F.cu = cu_seqlens;
+    F.s_final = nullptr;
+    F.o = nullptr;
+    F.N = N;
+    F.T = (int)T_total;
+    F.H = H;
+    F.D = dk;
+    F.NC = (int)NC;
+    F.in_f32 = in_dtype == KDA_F32;
+    F.gate_f32 = gate_dtype == KDA_F32;
+    F.out_f32 = true;
+    F.f32_factors = true;
+    carve(F, w + off[0], NC, H, dk);
+    ChunkArgs& R = b.rec;
+    R = F;
+    R.s0 = d_final_state;
+    R.s_final = d_initial_state;
+    carve(R, w + off[1], NC, H, dk);
+    R.pb = reinterpret_cast<const float*>(w + off[2]);
+    b.d_o = d_o;
+    b.dq = dq;
+    b.dk = dk_out;
+    b.dv = dv_out;
+    b.dla = dlog_alpha;
+    b.dbeta = dbeta;
+    b.scr = reinterpret_cast<float*>(w + off[3]);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (NC > 0 && launch_prep(F, st) != hipSuccess) return KDA_ERR_HIP;
+    if (NC > 0 && launch_recur(F, st) != hipSuccess) return KDA_ERR_HIP;
+    if (NC > 0 && launch_bwd_prep(b, st) != hipSuccess) return KDA_ERR_HIP;
+    if (launch_recur(R, st) != hipSuccess) return KDA_ERR_HIP;
+    if (NC > 0 && launch_bwd_local(b, st) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
                            float* state, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype,
                            kda_dtype gate_dtype, kda_dtype out_dtype, void* o, void* stream) {

@@ -350,6 +350,9 @@ struct Ws {
     E* vn;
     E* am = nullptr;
     E* oh = nullptr;
+    // backward state-gradient recursion: a state-independent term added to the
+    // state each chunk, [dv/16][dk/16][64 lanes][4] fp32 per chunk-head
+    const float* pb = nullptr;
 };
 
 }  // namespace kda

@@ -33,7 +33,23 @@ struct ChunkArgs {
     bool dplr = false;
     const void *lr_a = nullptr, *lr_b = nullptr;
     void *am = nullptr, *oh = nullptr;
+    // backward: fp32 factors whatever the input dtype (the forward recompute),
+    // and the state-gradient recursion's extra state-independent term
+    bool f32_factors = false;
+    const float* pb = nullptr;  // [chunk-head][dv/16][dk/16][64 lanes][4] fp32, or null
 };
+
+// Backward of kda_chunk_fwd (see kda_bwd.hip).
+struct BwdArgs {
+    ChunkArgs fwd;    // forward recompute: fp32 factors, h_n and V_new kept
+    ChunkArgs rec;    // state-gradient recursion over reversed chunk slots
+    const float* d_o;  // [T, H, dv]
+    float *dq, *dk, *dv, *dla, *dbeta;
+    float* scr;        // per chunk-head scratch, bwd_scr_floats(D) floats each
+};
+__host__ __device__ inline int64_t bwd_scr_floats(int D) { return 4LL * 64 * D + 3LL * 64 * 64; }
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_local(const BwdArgs& a, hipStream_t st);
 
 // Workspace carve-up shared by the size query and the launcher.
 struct WsPlan {

@@ -609,14 +609,18 @@ static hipError_t launch_prep_t(const ChunkArgs& a, hipStream_t st) {
 
 template <int D, bool F32>
 static hipError_t launch_prep_d(const ChunkArgs& a, hipStream_t st) {
-    using TIn = typename std::conditional<F32, float, uint16_t>::type;
-    if (a.gate_f32) return launch_prep_t<D, TIn, float, F32>(a, st);
-    return launch_prep_t<D, TIn, uint16_t, F32>(a, st);
+    if constexpr (F32) {
+        if (a.in_f32)
+            return a.gate_f32 ? launch_prep_t<D, float, float, true>(a, st) : launch_prep_t<D, float, uint16_t, true>(a, st);
+    }
+    // bf16 inputs: fp16 factors, or fp32 factors for the backward's recompute
+    return a.gate_f32 ? launch_prep_t<D, uint16_t, float, F32>(a, st) : launch_prep_t<D, uint16_t, uint16_t, F32>(a, st);
 }
 
 hipError_t launch_prep(const ChunkArgs& a, hipStream_t st) {
-    if (a.D == 128) return a.in_f32 ? launch_prep_d<128, true>(a, st) : launch_prep_d<128, false>(a, st);
-    return a.in_f32 ? launch_prep_d<64, true>(a, st) : launch_prep_d<64, false>(a, st);
+    const bool f32 = a.in_f32 || a.f32_factors;
+    if (a.D == 128) return f32 ? launch_prep_d<128, true>(a, st) : launch_prep_d<128, false>(a, st);
+    return f32 ? launch_prep_d<64, true>(a, st) : launch_prep_d<64, false>(a, st);
 }
 
 }  // namespace kda

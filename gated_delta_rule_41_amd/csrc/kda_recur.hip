@@ -209,7 +209,7 @@ __device__ __forceinline__ void warm_chunk(const Ws<typename Pol<F32>::E>& ws, i
 // output adds A_qk V (from the workspace, as the output accumulators' start).
 // The prep kernel computes K-^T V; a seventh wave copies this slab's share of
 // it into an LDS buffer (by chunk parity) one chunk ahead of the compute wave.
-template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false>
+template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false, bool ADDP = false>
 __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 192) void recur_kernel(const float* __restrict__ s0,
                                                                   float* __restrict__ s_final,
                                                                   const int32_t* __restrict__ cu, int N, int T,
@@ -220,6 +220,7 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 192) void recur_kernel
     using Frag = typename P::Frag;
     using PL = RecurPlan<D, F32, FUSED, DPLR>;
     static_assert(!DPLR || (FUSED && !F32), "the DPLR chain runs on 16-bit factors with the fused output");
+    static_assert(!ADDP || (F32 && !FUSED), "the added state term is for the fp32 unfused chain");
     constexpr int NS = D / 32;
     constexpr int NT = D / 16;  // row tiles over dk == column slabs over dv
     constexpr int RING = PL::RING;
@@ -423,6 +424,17 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 192) void recur_kernel
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[t][i] = s0 ? s0[sbase + (int64_t)(16 * t + 4 * g + i) * D] : 0.f;
 
+    // ADDP (the backward's state-gradient recursion): a state-independent term
+    // per chunk, loaded one chunk ahead into registers
+    f32x4_t pn[ADDP ? NT : 1];
+    auto load_p = [&](int c) {
+        if constexpr (ADDP) {
+            const float* pp = ws.pb + ((int64_t)(co + c) * H + h) * D * D + (int64_t)ct * NT * 64 * 4;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) pn[t] = *reinterpret_cast<const f32x4_t*>(pp + (t * 64 + l) * 4);
+        }
+    };
+    if (nch > 0) load_p(0);
     Frag wf[4][NS];  // -W fragments (with LOOK, of the chunk after the current one once read)
     auto load_w = [&](int c) {
         const char* wsl = ring + (c % RING) * PL::SLOT;
@@ -505,9 +517,12 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 192) void recur_kernel
             if constexpr (DPLR)
                 S[t] = gm[t] * S[t] + f32x4_t{h2f(kv[t][0] & 0xffffu), h2f(kv[t][0] >> 16), h2f(kv[t][1] & 0xffffu),
                                               h2f(kv[t][1] >> 16)};
+            else if constexpr (ADDP)
+                S[t] = gm[t] * S[t] + pn[t];
             else
                 S[t] = gm[t] * S[t];
         }
+        if (ADDP && c + 1 < nch) load_p(c + 1);
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -523,14 +538,14 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 192) void recur_kernel
     }
 }
 
-template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false>
+template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false, bool ADDP = false>
 static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     using E = typename Pol<F32>::E;
     using PL = RecurPlan<D, F32, FUSED, DPLR>;
-    Ws<E> ws{(E*)a.qp, (E*)a.km, (E*)a.wn, (E*)a.u, (E*)a.aqk, a.gam, (E*)a.h, (E*)a.vn, (E*)a.am, (E*)a.oh};
+    Ws<E> ws{(E*)a.qp, (E*)a.km, (E*)a.wn, (E*)a.u, (E*)a.aqk, a.gam, (E*)a.h, (E*)a.vn, (E*)a.am, (E*)a.oh, a.pb};
     constexpr int NT = D / 16;
     const int NU = a.N * a.H;
-    auto kern = recur_kernel<D, F32, FUSED, OUT_F32, DPLR>;
+    auto kern = recur_kernel<D, F32, FUSED, OUT_F32, DPLR, ADDP>;
     const hipError_t e = allow_dynamic_lds((const void*)kern, PL::LDS);
     if (e != hipSuccess) return e;
     dim3 grid(NU * NT), block(FUSED ? (DPLR ? 448 : 384) : 192);
@@ -540,7 +555,8 @@ static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
 
 template <int D>
 static hipError_t launch_recur_d(const ChunkArgs& a, hipStream_t st) {
-    if (a.in_f32) return launch_recur_t<D, true, false, true>(a, st);
+    if (a.in_f32 || a.f32_factors)
+        return a.pb ? launch_recur_t<D, true, false, true, false, true>(a, st) : launch_recur_t<D, true, false, true>(a, st);
     return a.out_f32 ? launch_recur_t<D, false, true, true>(a, st) : launch_recur_t<D, false, true, false>(a, st);
 }
 

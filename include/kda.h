@@ -148,6 +148,46 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
                                size_t workspace_bytes, void* stream, void* const* events);
 
 /*
+ * Bytes of device workspace kda_chunk_bwd needs (host call, no device access):
+ * the forward recomputed with fp32 factors, the state-gradient recursion's
+ * operands and outputs, and per-chunk scratch, for at most
+ * floor((T_total + 63*N) / 64) chunks per head.
+ *   bytes: host out-pointer, written on KDA_OK.
+ */
+kda_status kda_chunk_bwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
+                                        size_t* bytes);
+
+/*
+ * Backward of kda_chunk_fwd: given the gradients of o and of the final states,
+ * the gradients of q, k, v, log_alpha, beta and of the initial states. The
+ * chunkwise form is differentiated chunk by chunk (GeekNews "Kimi Linear"
+ * summary, section "Algoritmo paralelo por chunks", presents it as a training
+ * algorithm): the forward is recomputed with fp32 factors, the state gradient
+ * runs backwards over the chunks, and the chunk-local adjoints (output, state
+ * update, UT transform, gated products and scalings, cumulative gate) follow.
+ *
+ *   q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, T_total, H, dk,
+ *   dv, in_dtype, gate_dtype: as for kda_chunk_fwd
+ *   d_o             [T_total, H, dv] fp32, gradient of o
+ *   d_final_state   [N, H, dk, dv] fp32, gradient of the final states, or NULL (zero)
+ *   dq, dk, dlog_alpha [T_total, H, dk] fp32; dv [T_total, H, dv] fp32;
+ *   dbeta [T_total, H] fp32  (outputs, written for every token)
+ *   d_initial_state [N, H, dk, dv] fp32 or NULL; it may be the same pointer as
+ *                   d_final_state (in place), any other overlap is KDA_ERR_ALIAS
+ *   workspace       at least kda_chunk_bwd_workspace_size() bytes, 256-byte
+ *                   aligned; contents on entry do not matter
+ * All arithmetic is fp32 (bf16 inputs are widened exactly). Five kernels are
+ * enqueued. Deterministic: no atomics on global memory.
+ */
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                         int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
+                         kda_dtype in_dtype, kda_dtype gate_dtype, const float* d_o,
+                         const float* d_final_state, float* dq, float* dk_out, float* dv_out,
+                         float* dlog_alpha, float* dbeta, float* d_initial_state, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace kda_dplr_chunk_fwd needs (host call, no device
  * access): seven 16-bit per-chunk factors and the chunk decay, for at most
  * floor((T_total + 63*N) / 64) chunks per head. in_dtype must be KDA_BF16.

@@ -28,7 +28,8 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = kda._load()
     names = declared_functions()
-    assert names == ["kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_timed",
+    assert names == ["kda_abi_version", "kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd",
+                     "kda_chunk_fwd_timed",
                      "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_dplr_chunk_fwd",
                      "kda_dplr_chunk_fwd_workspace_size", "kda_status_str"]
     for nm in names:
@@ -184,6 +185,59 @@ def test_dplr_validation():
     assert dplr_call(ws=w, b=w + need // 2) == ALIAS
 
 
+def test_bwd_workspace_size_formula():
+    # per chunk-head, d = 128: the fp32 forward recompute (Q+, K-, -W, U, V_new
+    # 32 KiB each, A_qk 16 KiB, gamma 512 B, h_n 64 KiB) twice (forward and the
+    # state-gradient recursion), the added term Q+^T dO 64 KiB and the local
+    # kernel's scratch (4 [64][128] + 3 [64][64] fp32) 176 KiB -> 738304 B
+    fwd = 5 * 32768 + 16384 + 512 + 65536
+    assert kda.bwd_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * (2 * fwd + 65536 + 180224)
+    assert kda.bwd_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 738304
+    fwd64 = 5 * 16384 + 16384 + 256 + 16384
+    assert kda.bwd_workspace_size(2, 100, 1, 64, 64) == ((100 + 63 * 2) // 64) * (
+        2 * fwd64 + 16384 + 4 * (4 * 64 * 64 + 3 * 4096))
+    with pytest.raises(kda.KDAError):
+        kda.bwd_workspace_size(1, 10, 1, 64, 128)
+
+
+def bwd_call(**over):
+    f = Fake()
+    a = dict(q=f(), k=f(), v=f(), la=f(), beta=f(), s0=None, cu=None, N=1, T=256, H=2, dk=64, dv=64,
+             in_dt=BF16, gate_dt=BF16, do=f(), dfin=None, dq=f(), dk_=f(), dv_=f(), dla=f(), db=f(), ds0=f(),
+             ws=f(), ws_bytes=1 << 40, stream=None)
+    a.update(over)
+    P = ctypes.c_void_p
+    return kda._load().kda_chunk_bwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["la"]), P(a["beta"]), P(a["s0"]),
+                                     P(a["cu"]), a["N"], a["T"], a["H"], a["dk"], a["dv"], a["in_dt"],
+                                     a["gate_dt"], P(a["do"]), P(a["dfin"]), P(a["dq"]), P(a["dk_"]),
+                                     P(a["dv_"]), P(a["dla"]), P(a["db"]), P(a["ds0"]), P(a["ws"]),
+                                     a["ws_bytes"], P(a["stream"]))
+
+
+def test_bwd_validation():
+    assert bwd_call(do=None) == NULL
+    assert bwd_call(db=None) == NULL
+    assert bwd_call(N=2) == SHAPE
+    assert bwd_call(T=-1) == SHAPE
+    assert bwd_call(dk=64, dv=128) == UNSUP
+    assert bwd_call(gate_dt=7) == UNSUP
+    f = Fake()
+    assert bwd_call(dla=f(4)) == ALIGN
+    assert bwd_call(db=f(2)) == ALIGN
+    q = f()
+    assert bwd_call(q=q, dq=q + 64) == ALIAS
+    dq = f()
+    assert bwd_call(dq=dq, dk_=dq + 1024) == ALIAS
+    d = 0x100000000000  # below every address bwd_call makes up
+    assert bwd_call(dfin=d, ds0=d) != ALIAS  # in place: the initial states' gradient replaces d_final
+    assert bwd_call(dfin=d, ds0=d + 256) == ALIAS
+    assert bwd_call(ws=f(64)) == WORKSPACE
+    need = kda.bwd_workspace_size(1, 256, 2, 64, 64)
+    assert bwd_call(ws_bytes=need - 1) == WORKSPACE
+    w = f()
+    assert bwd_call(ws=w, do=w + need // 2) == ALIAS
+
+
 @pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="would launch on fake pointers")
 def test_valid_arguments_reach_the_launch_without_gpu():
     """With no GPU present, valid arguments pass validation and the launch
@@ -191,3 +245,4 @@ def test_valid_arguments_reach_the_launch_without_gpu():
     assert decode_call() == HIP
     assert chunk_call() == HIP
     assert dplr_call() == HIP
+    assert bwd_call() == HIP
