@@ -9,9 +9,11 @@ of the hot path) is timed in the same run on ``decode-256`` (256 sequences x 32
 heads, fp32 states of 512 MiB, updated in place) and reported in the same JSON
 line. Prints ONE JSON line. The general-DPLR comparison operator (the transition KDA specialises,
 with free low-rank vectors a, b) is timed on the same workload and reported
-beside it under "dplr_comparison".
+beside it under "dplr_comparison", and the chunkwise backward (gradients of
+q, k, v, log_alpha, beta and the initial state) under "backward".
 
     python bench.py [--steps K] [--warmup W] [--decode-steps S] [--no-cpu-baseline] [--no-dplr]
+                    [--no-bwd]
 
 Profiling helpers (used to write the summaries under profiles/):
     python bench.py --copy-calibration MIB        # counter calibration kernel only
@@ -47,18 +49,36 @@ KERNEL_BYTES_PER_TOKEN_HEAD = {            # compulsory traffic of each prefill 
 # fp32 inputs (not benchmarked) run the unfused pair: recursion 776 + 768 (h_n,
 # V_new written), output 1152 + 512
 KERNEL_SYMBOL = {"prep": "prep_kernel", "recur": "recur_kernel", "decode": "decode_kernel",
-                 "dplr_prep": "dplr_prep_kernel", "dplr_recur": "recur_kernel"}
+                 "dplr_prep": "dplr_prep_kernel", "dplr_recur": "recur_kernel",
+                 "bwd_fwd_prep": "prep_kernel", "bwd_fwd_recur": "recur_kernel",
+                 "bwd_prep": "bwd_prep_kernel", "bwd_recur": "recur_kernel", "bwd_local": "bwd_local_kernel"}
 KERNEL_SOURCE = {"prep": "kda_prep.hip", "recur": "kda_recur.hip", "decode": "kda_decode.hip",
-                 "dplr_prep": "kda_dplr_prep.hip", "dplr_recur": "kda_recur.hip"}
+                 "dplr_prep": "kda_dplr_prep.hip", "dplr_recur": "kda_recur.hip",
+                 "bwd_fwd_prep": "kda_prep.hip", "bwd_fwd_recur": "kda_recur.hip",
+                 "bwd_prep": "kda_bwd.hip", "bwd_recur": "kda_recur.hip", "bwd_local": "kda_bwd.hip"}
 
 
 def kernel_key(short_name: str):
     """Which of this library's kernels a demangled name (arguments stripped) is.
-    The state recursion's last template argument selects the DPLR chain."""
-    if short_name.startswith("recur_kernel<"):
-        return "dplr_recur" if short_name.endswith(", true>") else "recur"
-    for key in ("dplr_prep", "prep", "decode"):
-        if short_name.startswith(KERNEL_SYMBOL[key] + "<"):
+    The template arguments tell the instantiations apart: the preparation's
+    last one is fp32 factors (the backward's forward recompute); the state
+    recursion's are <D, fp32 factors, fused output, fp32 output, DPLR chain,
+    added per-chunk term (the backward's state-gradient recursion)>."""
+    if "<" not in short_name:
+        return None
+    sym, args = short_name.split("<", 1)
+    args = [x.strip() for x in args.rstrip(">").split(",")]
+    flag = lambda i: len(args) > i and args[i] == "true"
+    if sym == "recur_kernel":
+        if flag(5):
+            return "bwd_recur"
+        if flag(4):
+            return "dplr_recur"
+        return "bwd_fwd_recur" if flag(1) else "recur"
+    if sym == "prep_kernel":
+        return "bwd_fwd_prep" if flag(3) else "prep"
+    for key in ("dplr_prep", "decode", "bwd_prep", "bwd_local"):
+        if sym == KERNEL_SYMBOL[key]:
             return key
     return None
 
@@ -191,6 +211,36 @@ def time_dplr(kda, case, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps, o, fs
+
+
+def time_bwd(kda, case, steps, warmup):
+    """Whole-call time of the chunkwise backward (its five kernels: the fp32
+    forward recompute, the operand preparation, the reverse state-gradient
+    recursion and the local adjoints), torch events on torch's current stream,
+    which the binding launches on."""
+    import torch
+    dev = case.q.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    d_o = torch.randn(case.T_total, case.H, case.dv, generator=g, device=dev)
+    d_fin = torch.randn(case.N, case.H, case.dk, case.dv, generator=g, device=dev) * 0.1
+    ws = torch.empty(kda.bwd_workspace_size(case.N, case.T_total, case.H, case.dk, case.dv),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        return kda.chunk_bwd(case.q, case.k, case.v, case.log_alpha, case.beta, d_o, case.initial_state,
+                             case.cu_seqlens, d_fin, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g_ = call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, g_, ws.numel()
 
 
 def time_decode(kda, dec, steps, warmup, hip, stream):
@@ -355,6 +405,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dplr", action="store_true", help="skip the general-DPLR comparison")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run the counter calibration copy kernel over MIB MiB")
     args = ap.parse_args(argv)
@@ -427,6 +478,13 @@ def main(argv=None):
             "hbm_bytes_per_launch": {"prep": traffic_from_profiles("dplr_prep", TH),
                                      "recur": traffic_from_profiles("dplr_recur", TH)}}
         del dcase
+
+    if not args.no_bwd:
+        bwd_ms, _, ws_bytes = time_bwd(kda, case, max(5, args.steps // 5), max(3, min(50, args.warmup)))
+        out["backward"] = {
+            "workload": "prefill-4k, d_o ~ N(0,1), d_final_state ~ N(0, 0.01)",
+            "ms_per_step": round(bwd_ms, 5), "tokens_per_s": round(case.T_total / (bwd_ms * 1e-3), 1),
+            "time_ratio_bwd_over_fwd": round(bwd_ms / wall_ms, 3), "workspace_bytes": ws_bytes}
 
     if not args.no_decode:
         dec_inputs = min(args.decode_steps, 100)  # distinct per-step inputs, cycled
