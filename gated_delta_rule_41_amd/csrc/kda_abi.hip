@@ -330,16 +330,19 @@ kda_status kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const
 }
 
 // backward workspace: forward recompute (fp32 factors, h_n, V_new), the state-gradient
-// recursion's operands and outputs, its added term, and the local kernel's scratch
-static size_t bwd_workspace(int64_t NC, int H, int D, size_t off[4]) {
+// recursion's operands and outputs, its added term, the gated key products and the
+// local kernel's scratch
+static size_t bwd_workspace(int64_t NC, int H, int D, size_t off[5]) {
     const size_t f = plan_workspace(NC, H, D, true).total;
     const size_t pb = align_up((size_t)NC * H * D * D * 4, 256);
+    const size_t pk = align_up((size_t)NC * H * 64 * 64 * 4, 256);
     const size_t sc = align_up((size_t)NC * H * (size_t)bwd_scr_floats(D) * 4, 256);
     off[0] = 0;
     off[1] = f;
     off[2] = 2 * f;
     off[3] = 2 * f + pb;
-    return 2 * f + pb + sc;
+    off[4] = 2 * f + pb + pk;
+    return 2 * f + pb + pk + sc;
 }
 
 static void carve(ChunkArgs& a, char* base, int64_t NC, int H, int D) {
@@ -359,7 +362,7 @@ kda_status kda_chunk_bwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
     if (!bytes) return KDA_ERR_NULL;
     if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
     if (!head_ok(dk, dv)) return KDA_ERR_UNSUPPORTED;
-    size_t off[4];
+    size_t off[5];
     *bytes = bwd_workspace(chunk_capacity(N, T_total, true), H, dk, off);
     return KDA_OK;
 }
@@ -401,7 +404,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
         if (!(i == 5 && outs[i] == dfin) && overlaps(outs[i], nout[i], dfin, ns)) return KDA_ERR_ALIAS;
     }
     const int64_t NC = chunk_capacity(N, T_total, cu_seqlens != nullptr);
-    size_t off[4];
+    size_t off[5];
     const size_t need = bwd_workspace(NC, H, dk, off);
     if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return KDA_ERR_WORKSPACE;
     for (int j = 0; j < 8; ++j)
@@ -433,8 +436,10 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     F.out_f32 = true;
     F.f32_factors = true;
     carve(F, w + off[0], NC, H, dk);
+    F.am = w + off[3];  // the prep keeps the gated key products there
     ChunkArgs& R = b.rec;
     R = F;
+    R.am = nullptr;
     R.s0 = d_final_state;
     R.s_final = d_initial_state;
     carve(R, w + off[1], NC, H, dk);
@@ -445,7 +450,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     b.dv = dv_out;
     b.dla = dlog_alpha;
     b.dbeta = dbeta;
-    b.scr = reinterpret_cast<float*>(w + off[3]);
+    b.scr = reinterpret_cast<float*>(w + off[4]);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (NC > 0 && launch_prep(F, st) != hipSuccess) return KDA_ERR_HIP;
     if (NC > 0 && launch_recur(F, st) != hipSuccess) return KDA_ERR_HIP;

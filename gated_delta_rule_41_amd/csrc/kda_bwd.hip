@@ -12,45 +12,53 @@
 // shape (two dependent products per chunk), so it reuses the state-recursion
 // kernel on reversed chunk slots, with K- in place of -W, (-W)^T in place of
 // K-^T, A_qk^T dO in place of U and the state-independent term Q+^T dO added
-// each chunk (bwd_prep_kernel lays these out). What stays is chunk-local and
-// parallel over chunks (bwd_local_kernel): the adjoints of the output and the
-// state update (dQ+ = dO h^T, dA_qk = tril(dO V^T), dK- = V dh'^T,
-// dgamma = rowsum(h * dh'), dW = -dV h^T), of the UT transform X = T B with
-// T = (I + A_kk)^-1 (dB = T^T dX, dA_kk = -T^T (dX B^T) T^T on the strictly
-// lower part), of the gated products (pairwise exponentials of gate
-// differences <= 0, as in the forward's exact path) and of the gated scalings,
-// then a reverse cumulative sum turns the gate gradient into dlog_alpha.
+// each chunk (bwd_prep_kernel computes and lays these out). What stays is
+// chunk-local and parallel over chunks (bwd_local_kernel):
+//   * the adjoints of the output and the state update: dQ+ = dO h^T,
+//     dA_qk = tril(dO V^T), dK- = V dh'^T, dgamma = rowsum(h * dh'),
+//     dW = -dV h^T;
+//   * the UT transform X = [W | U] = T B with T = (I + A_kk)^-1 and
+//     B = [beta K+ | beta V]: dB = T^T dX and, since dT = dX B^T,
+//     dA_kk = -T^T dX B^T T^T = -dB X^T on the strictly lower part;
+//   * the gated products P[r,i] = sum_c x_rc y_ic e^(g_rc - g_ic): for 16-row
+//     blocks below the diagonal the exponential splits at a row between the
+//     two blocks (every factor e^(.) <= 1 for decaying gates, so nothing
+//     overflows, and an underflowing factor only drops a term smaller than
+//     itself) and the adjoints are matrix-core products; the four diagonal
+//     blocks are summed pair by pair with the exact exponential;
+//   * the gated scalings, then a reverse cumulative sum over the chunk turns the
+//     gate gradient into dlog_alpha.
 //
-// Everything runs in fp32: the forward is recomputed with fp32 factors (the
-// prep and recursion kernels' fp32 path, which keeps h_n and V_new).
+// Everything runs in fp32, the products on the matrix cores (16 x 16 x 4 fp32):
+// the forward is recomputed with fp32 factors (the prep and recursion kernels'
+// fp32 path, which keeps h_n, V_new and the gated key products).
+//
+// Product convention (v_mfma_f32_16x16x4f32): lane l = 16 G + n supplies A[n][k]
+// and B[k][n] for the k of its lane group G; the accumulator holds C[4 G + i][n],
+// i < 4. Over four consecutive products lane group G takes k = 4 G + t at step t
+// (A and B agree on it), so one 16-byte read per lane feeds four products, and
+// an accumulator tile feeds a later product as its B operand unchanged.
+//
+// Every cross-lane or cross-wave sum runs in a fixed order: the results are
+// bitwise repeatable.
 #include "kda_common.h"
 #include "kda_launch.h"
 #include "kda_prep_util.h"
 
 namespace kda {
 
-// element (kk, j) of a chunk-entry state stored as B-operand fragments
-// [D/16 col tile][D/32 slice][64 lanes][8] (the fp32 recursion's h array)
-template <int D>
-__device__ __forceinline__ int hfrag_index(int kk, int j) {
-    const int ct = j >> 4, n = j & 15, s = kk >> 5, k = kk & 31;
-    const int g = (k & 15) >> 2, jj = 4 * (k >> 4) + (k & 3);
-    return ((ct * (D / 32) + s) * 64 + 16 * g + n) * 8 + jj;
-}
-// element (r, j) of a chunk's corrected values stored as B-operand fragments
-// [D/16 col tile][2 slices][64 lanes][8]
-__device__ __forceinline__ int vfrag_index(int r, int j) {
-    const int ct = j >> 4, n = j & 15, s = r >> 5, k = r & 31;
-    const int g = (k & 15) >> 2, jj = 4 * (k >> 4) + (k & 3);
-    return ((ct * 2 + s) * 64 + 16 * g + n) * 8 + jj;
-}
+// row (of a 32-row slice) of element jj held by B-operand fragment lane group g,
+// in the fp32 recursion's fragment arrays: h [D/16][D/32][64 lanes][8] and
+// V_new [D/16][2][64 lanes][8]
+__device__ __forceinline__ int frag_row(int g, int jj) { return 16 * (jj >> 2) + 4 * g + (jj & 3); }
 // row-major [rows][ncol] array with columns in the split order per 32
 __device__ __forceinline__ int split_index(int row, int col, int ncol) {
     return row * ncol + 32 * (col >> 5) + split_pos(col);
 }
-// element (r, j) of [D/16][4][64 lanes][4] accumulator tiles (64 rows)
-__device__ __forceinline__ int tile_index(int r, int j) {
-    return (((j >> 4) * 4 + (r >> 4)) * 64 + 16 * ((r & 15) >> 2) + (j & 15)) * 4 + (r & 3);
+// channel stored at position p of a split-ordered row (inverse of split_pos)
+__device__ __forceinline__ int split_chan(int p) {
+    const int q = p & 31;
+    return (p & ~31) + 16 * ((q >> 2) & 1) + 4 * (q >> 3) + (q & 3);
 }
 
 // Chunk slot gc of a sequence -> the slot the reversed recursion uses for it.
@@ -60,98 +68,164 @@ __device__ __forceinline__ int reversed_slot(const int32_t* cu, int T, int seq, 
     return co + nch - 1 - (gc - co);
 }
 
+__device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// acc += sum over 16 k of A[.][k] B[.][k], both read as 4 consecutive k per lane
+__device__ __forceinline__ void mma16(f32x4_t& acc, const float* a, const float* b) {
+    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(a);
+    const f32x4_t y = *reinterpret_cast<const f32x4_t*>(b);
+    acc = mfma4(x[0], y[0], acc);
+    acc = mfma4(x[1], y[1], acc);
+    acc = mfma4(x[2], y[2], acc);
+    acc = mfma4(x[3], y[3], acc);
+}
+// e^x for x formed as a difference of cumulative gates (natural log units): the
+// sums of 16-bit gates are exact in fp32, so is their difference, and the one
+// rounding left is that of x * log2 e
+__device__ __forceinline__ float ee(float x) { return ex2(x * LOG2E); }
+__device__ __forceinline__ float sum16(float x) {  // over the 16 lanes n of a lane group
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+
+// Stage a [64][D] fragment array (V_new, dV) into LDS rows [64][RS].
+template <int D, int RS>
+__device__ __forceinline__ void stage_vfrag(float* dst, const float* src, int tid, int nth) {
+    for (int q = tid; q < 64 * D / 8; q += nth) {
+        const int blk = q >> 6, fl = q & 63, ct = blk >> 1, s = blk & 1, g = fl >> 4, j = 16 * ct + (fl & 15);
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src + q * 8);
+        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(src + q * 8 + 4);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) dst[(32 * s + frag_row(g, jj)) * RS + j] = jj < 4 ? a[jj] : b[jj - 4];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Operands of the state-gradient recursion for chunk slot gc, written to its
-// reversed slot: -W := K-, K-^T := (-W)^T, U := A_qk^T dO, gamma, and the added
-// term Q+^T dO in [dv/16][dk/16][64 lanes][4].
+// reversed slot: -W := K-, K-^T := (-W)^T, gamma, U := A_qk^T dO (accumulator
+// tiles [dv/16][4][64 lanes][4]) and the added term P = Q+^T dO
+// ([dv/16][dk/16][64 lanes][4]). Wave w owns value columns 16 w .. 16 w + 15.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const int32_t* __restrict__ cu, int N, int T, int H,
-                                                       Ws<float> f, Ws<float> b, const float* __restrict__ d_o) {
-    constexpr int NS = D / 32, NT = D / 16, RS = D + 4;
+struct BwdPrepSmem {
+    static constexpr int RS = D + 4, SQS = 68;
+    static constexpr int BYTES = (2 * 64 * RS + 64 * SQS) * 4;
+};
+
+template <int D>
+__global__ __launch_bounds__(4 * D) void bwd_prep_kernel(const int32_t* __restrict__ cu, int N, int T, int H,
+                                                         Ws<float> f, Ws<float> b,
+                                                         const float* __restrict__ d_o) {
+    constexpr int NT = D / 16, NTH = 4 * D, RS = BwdPrepSmem<D>::RS, SQS = BwdPrepSmem<D>::SQS;
     extern __shared__ __align__(16) float sm[];
     float* dO = sm;                // [64][RS]
-    float* Qp = dO + 64 * RS;      // [64][RS]
-    float* Aq = Qp + 64 * RS;      // [64][65]
+    float* Qp = dO + 64 * RS;      // [64][RS], channels in natural order
+    float* Aq = Qp + 64 * RS;      // [64][SQS] A_qk
     const int gc = blockIdx.x / H, h = blockIdx.x - gc * H;
     ChunkLoc loc;
     if (!locate_chunk(cu, N, T, gc, loc)) return;
     const int rev = reversed_slot(cu, T, loc.seq, gc);
     const int64_t src = (int64_t)gc * H + h, dst = (int64_t)rev * H + h;
-    const int tid = threadIdx.x;
-    for (int e = tid; e < 64 * D; e += 256) {
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, n = l & 15;
+    for (int e = tid; e < 64 * D / 4; e += NTH) {
+        const int r = e / (D / 4), c4 = 4 * (e - r * (D / 4));
+        const f32x4_t x = r < loc.L ? *reinterpret_cast<const f32x4_t*>(d_o + ((int64_t)(loc.t0 + r) * H + h) * D + c4)
+                                    : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4_t*>(dO + r * RS + c4) = x;
+        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(f.qp + src * 64 * D + 4 * e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Qp[r * RS + split_chan(c4 + j)] = y[j];
+    }
+    for (int e = tid; e < 64 * 64 / 4; e += NTH) {
+        const int r = e >> 4, p = 4 * (e & 15);
+        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(f.aqk + src * 64 * 64 + 4 * e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Aq[r * SQS + split_chan(p + j)] = y[j];
+    }
+    // K- to the -W layout; (-W)^T to the K-^T layout; gamma
+    for (int e = tid; e < 64 * D; e += NTH) {
         const int r = e / D, c = e - r * D;
-        dO[r * RS + c] = r < loc.L ? d_o[((int64_t)(loc.t0 + r) * H + h) * D + c] : 0.f;
-        Qp[r * RS + c] = f.qp[src * 64 * D + split_index(r, c, D)];
-        // K- to the -W layout; (-W)^T to the K-^T layout
         b.wn[dst * 64 * D + split_index(r, c, D)] = f.km[src * D * 64 + split_index(c, r, 64)];
         b.km[dst * D * 64 + split_index(c, r, 64)] = f.wn[src * 64 * D + split_index(r, c, D)];
     }
-    for (int e = tid; e < 64 * 64; e += 256) {
-        const int r = e >> 6, i = e & 63;
-        Aq[r * 65 + i] = f.aqk[src * 64 * 64 + split_index(r, i, 64)];
-    }
-    for (int c = tid; c < D; c += 256) b.gam[dst * D + c] = f.gam[src * D + c];
+    for (int c = tid; c < D; c += NTH) b.gam[dst * D + c] = f.gam[src * D + c];
     __syncthreads();
-    // U := A_qk^T dO (A_qk is lower triangular: rows i >= r)
-    for (int e = tid; e < 64 * D; e += 256) {
-        const int r = e / D, j = e - r * D;
-        float acc = 0.f;
-        for (int i = r; i < 64; ++i) acc += Aq[i * 65 + r] * dO[i * RS + j];
-        b.u[dst * 64 * D + tile_index(r, j)] = acc;
+    const int j0 = 16 * w;
+    // P[c][j] = sum_r Q+[r][c] dO[r][j]; U[r][j] = sum_{i >= r} A_qk[i][r] dO[i][j]
+    f32x4_t accP[NT], accU[4];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) accP[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int R = 0; R < 4; ++R) accU[R] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int kk = 0; kk < 16; ++kk) {
+        const int r = 4 * kk + G;  // k index of this lane group
+        const float bo = dO[r * RS + j0 + n];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) accP[ct] = mfma4(Qp[r * RS + 16 * ct + n], bo, accP[ct]);
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+            if (R <= (kk >> 2)) accU[R] = mfma4(Aq[r * SQS + 16 * R + n], bo, accU[R]);
     }
-    // P := Q+^T dO
     float* pb = const_cast<float*>(b.pb) + dst * D * D;
-    for (int e = tid; e < D * D; e += 256) {
-        const int c = e / D, j = e - c * D;
-        float acc = 0.f;
-        for (int r = 0; r < 64; ++r) acc += Qp[r * RS + c] * dO[r * RS + j];
-        const int lane = 16 * ((c & 15) >> 2) + (j & 15);
-        pb[(((j >> 4) * NT + (c >> 4)) * 64 + lane) * 4 + (c & 3)] = acc;
-    }
-    (void)NS;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) *reinterpret_cast<f32x4_t*>(pb + ((w * NT + ct) * 64 + l) * 4) = accP[ct];
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+        *reinterpret_cast<f32x4_t*>(b.u + dst * 64 * D + ((w * 4 + R) * 64 + l) * 4) = accU[R];
 }
 
 // ---------------------------------------------------------------------------
-// Chunk-local adjoints, one 256-thread workgroup per (chunk, head). Thread t
-// owns channel c = t % D of rows r0 .. r0 + RPT - 1 for every elementwise
-// quantity, so per-(row, channel) partial gradients stay in its registers.
+// Chunk-local adjoints, one workgroup of D/16 waves per (chunk, head). Wave w
+// owns key/value channels c = 16 w + n (lane n of each lane group); lane group
+// G owns rows 16 R + 4 G + i (R, i < 4) of them: the "own" elements, which is
+// the accumulator layout of a 64-row product tile, so every per-channel sum
+// over rows stays inside a wave.
 template <int D>
 struct BwdSmem {
-    static constexpr int RS = D + 4;                 // row stride of [rows][D] matrices
-    static constexpr int BIGR = D > 128 ? D : 128;   // rows of BIG: h or dh' (D), or q and G (2 x 64)
-    static constexpr int BIG = BIGR * RS;
-    static constexpr int MAT = 64 * RS;              // [64][RS]
-    static constexpr int SQ = 64 * 65;               // [64][65]
-    static constexpr int SQX = 2 * SQ <= MAT ? 0 : 2 * SQ;  // two 64 x 64 matrices: in M2 if they fit
-    static constexpr int NG = 64 / (64 * D / 256);   // row groups of the thread layout
-    static constexpr int FLOATS = BIG + 2 * MAT + SQX + 2 * 64 + 3 * D + NG * D;
+    static constexpr int NW = D / 16;
+    static constexpr int RS = D + 4;          // [rows][D] matrices
+    static constexpr int RX = 2 * D + 4;      // dB = [dB_k | dB_v]
+    static constexpr int SQS = 68;            // [64][64] matrices
+    // phase 0: h then dh' [D][RS] at 0, dV then V [64][RS], dO [64][RS];
+    // later: T^T (stride SQS), -W, -U [64][RS] at 0, dB [64][RX], P_kk then dP_kk [64][SQS]
+    static constexpr int R_VV = D * RS, R_DO = R_VV + 64 * RS;
+    static constexpr int R_DB = 64 * RS, R_PK = R_DB + 64 * RX;
+    static constexpr int PH0_END = R_DO + 64 * RS, LATER_END = R_PK + 64 * SQS;
+    static constexpr int R_DPQ = PH0_END > LATER_END ? PH0_END : LATER_END;  // dA_qk, kept to the end
+    static constexpr int R_SMALL = R_DPQ + 64 * SQS;
+    // small: beta [64], dbeta partials [NW][64] and [4][64], dgamma halves [2][D]
+    static constexpr int FLOATS = R_SMALL + 64 + NW * 64 + 4 * 64 + 2 * D;
     static constexpr int BYTES = FLOATS * 4;
-    static_assert(2 * SQ <= BIG, "A and T fit in BIG");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
+    static_assert(64 * SQS <= R_DB, "T^T below dB");
 };
 
 template <int D, typename TIn, typename TG>
-__global__ __launch_bounds__(256) void bwd_local_kernel(const TIn* q, const TIn* k, const TIn* v, const TG* la,
-                                                        const TG* beta, const int32_t* __restrict__ cu, int N,
-                                                        int T, int H, Ws<float> f, Ws<float> b,
-                                                        const float* __restrict__ d_o, float* __restrict__ scr,
-                                                        float* __restrict__ dq, float* __restrict__ dk,
-                                                        float* __restrict__ dv, float* __restrict__ dla,
-                                                        float* __restrict__ dbeta) {
+__global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TIn* k, const TIn* v, const TG* la,
+                                                          const TG* beta, const int32_t* __restrict__ cu, int N,
+                                                          int T, int H, Ws<float> f, Ws<float> b,
+                                                          const float* __restrict__ d_o, float* __restrict__ scr,
+                                                          float* __restrict__ dq, float* __restrict__ dk,
+                                                          float* __restrict__ dv, float* __restrict__ dla,
+                                                          float* __restrict__ dbeta) {
     using SM = BwdSmem<D>;
-    constexpr int RS = SM::RS, RPT = 64 * D / 256, NG = 64 / RPT;  // rows per thread, row groups
+    constexpr int NW = SM::NW, NTH = 64 * NW, NS = D / 32, RS = SM::RS, RX = SM::RX, SQS = SM::SQS;
     extern __shared__ __align__(16) float sm[];
-    float* BIGm = sm;                  // [D][RS]
-    float* M1 = BIGm + SM::BIG;        // [64][RS]
-    float* M2 = M1 + SM::MAT;          // [64][RS]
-    float* S1 = SM::SQX ? M2 + SM::MAT : M2;  // [64][65], in M2 (once M2 is free) when it fits
-    float* S2 = S1 + SM::SQ;                  // [64][65]
-    float* bet = M2 + SM::MAT + SM::SQX;      // [64] beta
-    float* dbs = bet + 64;             // [64] dbeta: the dA_kk term (one thread per row)
-    float* dgam = dbs + 64;            // [D]
-    float* gl = dgam + D;              // [D] cumulative gate at the chunk's last row
-    float* gtot = gl + D;              // [NG][D] row-group totals of dg, then of the last-row terms
-    // (every cross-thread sum below runs in a fixed order: the results are deterministic)
+    float* HB = sm;                    // h, then dh' ([key channel][value column])
+    float* VV = sm + SM::R_VV;         // dV, then V
+    float* DO = sm + SM::R_DO;         // dO
+    float* TT = sm;                    // T^T (stride SQS), then -W, then -U (stride RS)
+    float* DB = sm + SM::R_DB;         // [64][RX]
+    float* PK = sm + SM::R_PK;         // P_kk, then dP_kk
+    float* DPQ = sm + SM::R_DPQ;       // dA_qk
+    float* bet = sm + SM::R_SMALL;     // [64]
+    float* dbp = bet + 64;             // [NW][64] dbeta: K+ dB_k + v dB_v, per wave
+    float* dap = dbp + NW * 64;        // [4][64] dbeta: dA_kk P_kk, per column block
+    float* dgp = dap + 4 * 64;         // [2][D] dgamma halves
 
     const int gc = blockIdx.x / H, h = blockIdx.x - gc * H;
     ChunkLoc loc;
@@ -159,334 +233,435 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(const TIn* q, const TIn*
     const int t0 = loc.t0, L = loc.L;
     const int rev = reversed_slot(cu, T, loc.seq, gc);
     const int64_t fs = (int64_t)gc * H + h, bs = (int64_t)rev * H + h;
-    const int tid = threadIdx.x;
-    const int c = tid % D, r0 = (tid / D) * RPT, grp = tid / D;
-    float* G = scr + fs * bwd_scr_floats(D);   // [64][D] cumulative gate (natural log)
-    float* SQp = G + 64 * D;                   // [64][D] dQ+
-    float* SW = SQp + 64 * D;                  // [64][D] dW
-    float* SKm = SW + 64 * D;                  // [64][D] dK-
-    float* SPq = SKm + 64 * D;                 // [64][64] dA_qk
-    float* SPk = SPq + 64 * 64;                // [64][64] P_kk (ungated by beta)
-    float* SdPk = SPk + 64 * 64;               // [64][64] dP_kk
-    const float* hF = f.h + fs * D * D;        // forward chunk-entry state
-    const float* vF = f.vn + fs * 64 * D;      // forward corrected values
-    const float* dhB = b.h + bs * D * D;       // gradient of the chunk's exit state
-    const float* dVB = b.vn + bs * 64 * D;     // dV
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, n = l & 15;
+    const int c = 16 * w + n;  // own channel
+    const float* Pkk = f.am + fs * 64 * 64;     // [64][64] from the forward recompute
+    float* SQ = scr + fs * bwd_scr_floats(D);   // dQ+, own-element tiles [NW][4][64][4]
+    float* SK = SQ + 64 * D;                    // dK-, same layout
+    const float* hF = f.h + fs * D * D;
+    const float* vF = f.vn + fs * 64 * D;
+    const float* dhB = b.h + bs * D * D;
+    const float* dVB = b.vn + bs * 64 * D;
     auto rowoff = [&](int r) { return ((int64_t)(t0 + r) * H + h) * D; };
-    auto in_q = [&](int r, int cc) { return r < L ? ld_in(q, rowoff(r) + cc) : 0.f; };
-    auto in_k = [&](int r, int cc) { return r < L ? ld_in(k, rowoff(r) + cc) : 0.f; };
-    auto in_v = [&](int r, int cc) { return r < L ? ld_in(v, rowoff(r) + cc) : 0.f; };
+    auto own_row = [&](int R, int i) { return 16 * R + 4 * G + i; };
 
-    // ---- 0. beta, cumulative gate, dgamma = rowsum(h * dh')
-    if (tid < 64) {
-        bet[tid] = tid < L ? ld_in(beta, (int64_t)(t0 + tid) * H + h) : 0.f;
-        dbs[tid] = 0.f;
+    if (tid < 64) bet[tid] = tid < L ? ld_in(beta, (int64_t)(t0 + tid) * H + h) : 0.f;
+
+    // ---- 0a. h, dV, dO to LDS; dQ+ = dO h^T and dW = -dV h^T (own tiles)
+    for (int qq = tid; qq < D * D / 8; qq += NTH) {
+        const int blk = qq >> 6, fl = qq & 63, ct = blk / NS, s = blk - ct * NS, g = fl >> 4;
+        const int j = 16 * ct + (fl & 15);
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(hF + qq * 8);
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(hF + qq * 8 + 4);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) HB[(32 * s + frag_row(g, jj)) * RS + j] = jj < 4 ? x0[jj] : x1[jj - 4];
     }
-    for (int cc = tid; cc < D; cc += 256) {
-        float x = 0.f;
-        for (int r = 0; r < 64; ++r) {
-            if (r < L) x += ld_in(la, rowoff(r) + cc);
-            G[r * D + cc] = x;
-        }
-        gl[cc] = x;
-        float s = 0.f;
-        for (int j = 0; j < D; ++j) s += hF[hfrag_index<D>(cc, j)] * dhB[hfrag_index<D>(cc, j)];
-        dgam[cc] = s;
-    }
-    // ---- 1. dQ+ = dO h^T and dW = -dV h^T (h in BIG, dO in M1, dV in M2)
-    for (int e = tid; e < D * D; e += 256) {
-        const int kk = e / D, j = e - kk * D;
-        BIGm[kk * RS + j] = hF[hfrag_index<D>(kk, j)];
-    }
-    for (int e = tid; e < 64 * D; e += 256) {
-        const int r = e / D, j = e - r * D;
-        M1[r * RS + j] = r < L ? d_o[rowoff(r) + j] : 0.f;
-        M2[r * RS + j] = dVB[vfrag_index(r, j)];
+    stage_vfrag<D, RS>(VV, dVB, tid, NTH);
+    for (int e = tid; e < 64 * D / 4; e += NTH) {
+        const int r = e / (D / 4), c4 = 4 * (e - r * (D / 4));
+        *reinterpret_cast<f32x4_t*>(DO + r * RS + c4) =
+            r < L ? *reinterpret_cast<const f32x4_t*>(d_o + rowoff(r) + c4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     __syncthreads();
+    float dWo[4][4], dVo[4][4];  // own dW and dV
     {
-        float aq[RPT], aw[RPT];
+        f32x4_t aq[4], aw[4];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) aq[i] = aw[i] = 0.f;
-        for (int j = 0; j < D; j += 4) {
-            const f32x4_t hv = *reinterpret_cast<const f32x4_t*>(BIGm + c * RS + j);
+        for (int R = 0; R < 4; ++R) aq[R] = aw[R] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+        for (int s16 = 0; s16 < D / 16; ++s16) {
+            const float* hb = HB + c * RS + 16 * s16 + 4 * G;
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const f32x4_t o4 = *reinterpret_cast<const f32x4_t*>(M1 + (r0 + i) * RS + j);
-                const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(M2 + (r0 + i) * RS + j);
-                aq[i] += o4[0] * hv[0] + o4[1] * hv[1] + o4[2] * hv[2] + o4[3] * hv[3];
-                aw[i] -= v4[0] * hv[0] + v4[1] * hv[1] + v4[2] * hv[2] + v4[3] * hv[3];
+            for (int R = 0; R < 4; ++R) {
+                mma16(aq[R], DO + (16 * R + n) * RS + 16 * s16 + 4 * G, hb);
+                mma16(aw[R], VV + (16 * R + n) * RS + 16 * s16 + 4 * G, hb);
             }
         }
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            SQp[(r0 + i) * D + c] = aq[i];
-            SW[(r0 + i) * D + c] = aw[i];
+        for (int R = 0; R < 4; ++R) {
+            *reinterpret_cast<f32x4_t*>(SQ + ((w * 4 + R) * 64 + l) * 4) = aq[R];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dWo[R][i] = -aw[R][i];
+                dVo[R][i] = VV[own_row(R, i) * RS + c];
+            }
         }
     }
     __syncthreads();
-    // ---- 2. dA_qk = tril(dO V^T) (V in BIG's first 64 rows, dO still in M1)
-    for (int e = tid; e < 64 * D; e += 256) {
-        const int r = e / D, j = e - r * D;
-        BIGm[r * RS + j] = vF[vfrag_index(r, j)];
-    }
-    __syncthreads();
-    for (int e = tid; e < 64 * 64; e += 256) {
-        const int r = e >> 6, i = e & 63;
-        float acc = 0.f;
-        if (i <= r)
-            for (int j = 0; j < D; j += 4) {
-                const f32x4_t a4 = *reinterpret_cast<const f32x4_t*>(M1 + r * RS + j);
-                const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(BIGm + i * RS + j);
-                acc += a4[0] * b4[0] + a4[1] * b4[1] + a4[2] * b4[2] + a4[3] * b4[3];
-            }
-        SPq[r * 64 + i] = acc;
-    }
-    __syncthreads();
-    // ---- 3. dK- = V dh'^T (V to M1, dh' in BIG)
-    for (int e = tid; e < 64 * D; e += 256) {
-        const int r = e / D, j = e - r * D;
-        M1[r * RS + j] = BIGm[r * RS + j];
-    }
-    __syncthreads();
-    for (int e = tid; e < D * D; e += 256) {
-        const int kk = e / D, j = e - kk * D;
-        BIGm[kk * RS + j] = dhB[hfrag_index<D>(kk, j)];
-    }
-    __syncthreads();
+    // ---- 0b. dh' over h (dgamma = rowsum(h * dh') on the way), V over dV
     {
-        float ak[RPT];
+        float pg[8];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) ak[i] = 0.f;
-        for (int j = 0; j < D; j += 4) {
-            const f32x4_t hv = *reinterpret_cast<const f32x4_t*>(BIGm + c * RS + j);
+        for (int jj = 0; jj < 8; ++jj) pg[jj] = 0.f;
+        const int g = l >> 4, s = w % NS;  // fixed per thread (the block count per pass is 2 NS)
+        for (int qq = tid; qq < D * D / 8; qq += NTH) {
+            const int ct = (qq >> 6) / NS, j = 16 * ct + (l & 15);
+            const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(dhB + qq * 8);
+            const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(dhB + qq * 8 + 4);
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(M1 + (r0 + i) * RS + j);
-                ak[i] += v4[0] * hv[0] + v4[1] * hv[1] + v4[2] * hv[2] + v4[3] * hv[3];
+            for (int jj = 0; jj < 8; ++jj) {
+                const float x = jj < 4 ? x0[jj] : x1[jj - 4];
+                float* p = HB + (32 * s + frag_row(g, jj)) * RS + j;
+                pg[jj] += *p * x;
+                *p = x;
             }
         }
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) SKm[(r0 + i) * D + c] = ak[i];
+        for (int jj = 0; jj < 8; ++jj) {
+            const float t = sum16(pg[jj]);
+            if (n == 0) dgp[(w / NS) * D + 32 * s + frag_row(g, jj)] = t;
+        }
+    }
+    stage_vfrag<D, RS>(VV, vF, tid, NTH);
+    __syncthreads();
+    // dK- = V dh'^T (own tiles); dA_qk = tril(dO V^T) (tiles spread over the waves)
+    {
+        f32x4_t ak[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) ak[R] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+        for (int s16 = 0; s16 < D / 16; ++s16) {
+            const float* hb = HB + c * RS + 16 * s16 + 4 * G;
+#pragma unroll
+            for (int R = 0; R < 4; ++R) mma16(ak[R], VV + (16 * R + n) * RS + 16 * s16 + 4 * G, hb);
+        }
+#pragma unroll
+        for (int R = 0; R < 4; ++R) *reinterpret_cast<f32x4_t*>(SK + ((w * 4 + R) * 64 + l) * 4) = ak[R];
+    }
+    for (int tile = w; tile < 16; tile += NW) {
+        const int R = tile >> 2, I = tile & 3;
+        if (I > R) {  // above the diagonal: zero
+#pragma unroll
+            for (int i = 0; i < 4; ++i) DPQ[own_row(R, i) * SQS + 16 * I + n] = 0.f;
+            continue;
+        }
+        f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+        for (int s16 = 0; s16 < D / 16; ++s16)
+            mma16(a, DO + (16 * R + n) * RS + 16 * s16 + 4 * G, VV + (16 * I + n) * RS + 16 * s16 + 4 * G);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            DPQ[own_row(R, i) * SQS + 16 * I + n] = (I < R || n <= 4 * G + i) ? a[i] : 0.f;
+    }
+    // own inputs and the cumulative gate (natural log units)
+    float qo[4][4], ko[4][4], g2[4][4];
+    {
+        float part[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            float x = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = own_row(R, i);
+                const bool ok = r < L;
+                qo[R][i] = ok ? ld_in(q, rowoff(r) + c) : 0.f;
+                ko[R][i] = ok ? ld_in(k, rowoff(r) + c) : 0.f;
+                x += ok ? ld_in(la, rowoff(r) + c) : 0.f;
+                g2[R][i] = x;  // prefix over the lane's 4 rows
+            }
+            part[R] = x;
+        }
+        // plus the lane groups before this one in the block and the blocks before
+        float off = 0.f;
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            float before = 0.f, total = 0.f;
+#pragma unroll
+            for (int G2 = 0; G2 < 4; ++G2) {
+                const float t = __shfl(part[R], 16 * G2 + n);
+                if (G2 < G) before += t;
+                total += t;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) g2[R][i] += off + before;
+            off += total;
+        }
+    }
+    __syncthreads();  // phase-0 arrays dead
+
+    // ---- 1. T = (I + diag(beta) P_kk)^-1, stored transposed: TT[r][m] = T[m][r]
+    for (int e = tid; e < 64 * 16; e += NTH) {
+        const int r = e >> 4, i4 = 4 * (e & 15);
+        *reinterpret_cast<f32x4_t*>(PK + r * SQS + i4) = *reinterpret_cast<const f32x4_t*>(Pkk + r * 64 + i4);
     }
     __syncthreads();
-    // ---- 4. UT transform. k -> M1, G -> M2; P_kk[r][i] = sum_c k_rc k_ic exp(G_rc - G_ic), i < r
-    for (int e = tid; e < 64 * D; e += 256) {
-        const int r = e / D, cc = e - r * D;
-        M1[r * RS + cc] = in_k(r, cc);
-        M2[r * RS + cc] = G[r * D + cc];
+    if (w == 0) {  // diagonal blocks by forward substitution: lane = (block, column)
+        const int bb = l >> 4, j = l & 15;
+        float acc[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) acc[rr] = (rr == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float ti = acc[i];
+#pragma unroll
+            for (int rr = i + 1; rr < 16; ++rr)
+                acc[rr] -= bet[16 * bb + rr] * PK[(16 * bb + rr) * SQS + 16 * bb + i] * ti;
+        }
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<f32x4_t*>(TT + (16 * bb + j) * SQS + 16 * bb + 4 * r4) =
+                f32x4_t{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
     }
     __syncthreads();
-    float* A = BIGm;            // [64][65]: beta_r P_kk, then dT, then Y
-    float* Tm = BIGm + 64 * 65; // [64][65]: T = (I + A_kk)^-1
-    for (int e = tid; e < 64 * 64; e += 256) {
-        const int r = e >> 6, i = e & 63;
-        float acc = 0.f;
-        if (i < r)
-            for (int cc = 0; cc < D; ++cc)
-                acc += M1[r * RS + cc] * M1[i * RS + cc] * __expf(M2[r * RS + cc] - M2[i * RS + cc]);
-        SPk[r * 64 + i] = acc;
-        A[r * 65 + i] = bet[r] * acc;
-    }
-    __syncthreads();
-    // forward substitution, row by row: T[r][i] = [r == i] - sum_{m=i}^{r-1} A[r][m] T[m][i]
-    for (int r = 0; r < 64; ++r) {
-        if (tid < 64) {
-            const int i = tid;
-            float x = (i == r) ? 1.f : 0.f;
-            if (i < r)
-                for (int m = i; m < r; ++m) x -= A[r * 65 + m] * Tm[m * 65 + i];
-            Tm[r * 65 + i] = x;
+    // blocks below the diagonal: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, block row by block row
+    for (int I = 1; I < 4; ++I) {
+        if (w < I) {
+            const int J = w;
+            f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+            const float bi = bet[16 * I + n];
+            for (int K = J; K < I; ++K) {
+                const f32x4_t a = *reinterpret_cast<const f32x4_t*>(PK + (16 * I + n) * SQS + 16 * K + 4 * G);
+                const f32x4_t t = *reinterpret_cast<const f32x4_t*>(TT + (16 * J + n) * SQS + 16 * K + 4 * G);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) y = mfma4(bi * a[s], t[s], y);
+            }
+            f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) x = mfma4(TT[(16 * I + 4 * G + s) * SQS + 16 * I + n], y[s], x);
+            *reinterpret_cast<f32x4_t*>(TT + (16 * J + n) * SQS + 16 * I + 4 * G) = -x;
         }
         __syncthreads();
     }
-    // K+ = exp(G) k into M1 (G still in M2), dW into M2's place after: stage dW to S? -> use BIG's tail
-    float* dT = A;  // reuse: A is dead after T
-    for (int e = tid; e < 64 * D; e += 256) {
-        const int r = e / D, cc = e - r * D;
-        M1[r * RS + cc] = __expf(M2[r * RS + cc]) * M1[r * RS + cc];  // K+
-    }
-    __syncthreads();
-    for (int e = tid; e < 64 * D; e += 256) {
-        const int r = e / D, cc = e - r * D;
-        M2[r * RS + cc] = SW[r * D + cc];  // dW
-    }
-    for (int e = tid; e < 64 * 64; e += 256) dT[(e >> 6) * 65 + (e & 63)] = 0.f;
-    __syncthreads();
-    // part K: dT[r][i] += sum_c dW[r][c] beta_i K+[i][c];  dB_k = T^T dW
-    for (int e = tid; e < 64 * 64; e += 256) {
-        const int r = e >> 6, i = e & 63;
-        float acc = 0.f;
-        for (int cc = 0; cc < D; cc += 4) {
-            const f32x4_t a4 = *reinterpret_cast<const f32x4_t*>(M2 + r * RS + cc);
-            const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(M1 + i * RS + cc);
-            acc += a4[0] * b4[0] + a4[1] * b4[1] + a4[2] * b4[2] + a4[3] * b4[3];
-        }
-        dT[r * 65 + i] += bet[i] * acc;
-    }
-    float dKp[RPT], dbr[RPT];  // dbr: this thread's (row, channel) terms of dbeta
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = r0 + i;
-        float acc = 0.f;
-        for (int m = r; m < 64; ++m) acc += Tm[m * 65 + r] * M2[m * RS + c];
-        dKp[i] = bet[r] * acc;
-        dbr[i] = M1[r * RS + c] * acc;  // K+[r][c] dB_k[r][c]
-    }
-    __syncthreads();
-    // part V: v -> M1, dV -> M2; dT[r][i] += sum_j dV[r][j] beta_i v[i][j]; dv = beta T^T dV
-    for (int e = tid; e < 64 * D; e += 256) {
-        const int r = e / D, j = e - r * D;
-        M1[r * RS + j] = in_v(r, j);
-        M2[r * RS + j] = dVB[vfrag_index(r, j)];
-    }
-    __syncthreads();
-    for (int e = tid; e < 64 * 64; e += 256) {
-        const int r = e >> 6, i = e & 63;
-        float acc = 0.f;
-        for (int j = 0; j < D; j += 4) {
-            const f32x4_t a4 = *reinterpret_cast<const f32x4_t*>(M2 + r * RS + j);
-            const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(M1 + i * RS + j);
-            acc += a4[0] * b4[0] + a4[1] * b4[1] + a4[2] * b4[2] + a4[3] * b4[3];
-        }
-        dT[r * 65 + i] += bet[i] * acc;
-    }
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = r0 + i;
-        float acc = 0.f;
-        for (int m = r; m < 64; ++m) acc += Tm[m * 65 + r] * M2[m * RS + c];
-        if (r < L) dv[rowoff(r) + c] = bet[r] * acc;
-        dbr[i] += M1[r * RS + c] * acc;  // v[r][c] dB_v[r][c]
-    }
-    __syncthreads();
-    // dA_kk = -T^T (dT T^T), strictly lower: Y = dT T^T into S1, then dA into S2
-    for (int e = tid; e < 64 * 64; e += 256) {
-        const int r = e >> 6, i = e & 63;
-        float acc = 0.f;
-        for (int m = 0; m <= i; ++m) acc += dT[r * 65 + m] * Tm[i * 65 + m];  // T[i][m] = 0 for m > i
-        S1[r * 65 + i] = acc;
-    }
-    __syncthreads();
-    for (int e = tid; e < 64 * 64; e += 256) {
-        const int r = e >> 6, i = e & 63;
-        float acc = 0.f;
-        if (i < r)
-            for (int m = r; m < 64; ++m) acc += Tm[m * 65 + r] * S1[m * 65 + i];  // T[m][r] = 0 for m < r
-        const float dA = -acc;
-        SdPk[r * 64 + i] = bet[r] * dA;
-        S2[r * 65 + i] = dA * SPk[r * 64 + i];
-    }
-    __syncthreads();
-    if (tid < 64) {
-        float s = 0.f;
-        for (int i = 0; i < tid; ++i) s += S2[tid * 65 + i];
-        dbs[tid] = s;
-    }
-    __syncthreads();
-    // ---- 5. gated products' adjoints. q -> BIG[0:64], G -> BIG[64:128] (D = 128) or
-    // M-matrices; k -> M1; dA_qk -> S1, dP_kk -> S2
-    float* Qm = BIGm;
-    float* Gm = BIGm + 64 * RS;  // BIG has at least 128 rows
-    for (int e = tid; e < 64 * D; e += 256) {
-        const int r = e / D, cc = e - r * D;
-        Qm[r * RS + cc] = in_q(r, cc);
-        Gm[r * RS + cc] = G[r * D + cc];
-        M1[r * RS + cc] = in_k(r, cc);
-    }
-    for (int e = tid; e < 64 * 64; e += 256) {
-        const int r = e >> 6, i = e & 63;
-        S1[r * 65 + i] = SPq[r * 64 + i];
-        S2[r * 65 + i] = SdPk[r * 64 + i];
-    }
-    __syncthreads();
-    float dqv[RPT], dkv[RPT], dgv[RPT];
-#pragma unroll
-    for (int ii = 0; ii < RPT; ++ii) {
-        const int r = r0 + ii;
-        const float gr = Gm[r * RS + c], qr = Qm[r * RS + c], kr = M1[r * RS + c];
-        float sq = 0.f, skb = 0.f, ska = 0.f, skc = 0.f;
-        for (int i = 0; i <= r; ++i) {  // row r as the left factor: i <= r
-            const float e = __expf(gr - Gm[i * RS + c]);  // G_r - G_i <= 0
-            const float ki = M1[i * RS + c];
-            sq += S1[r * 65 + i] * ki * e;
-            if (i < r) skb += S2[r * 65 + i] * ki * e;
-        }
-        for (int rr = r; rr < 64; ++rr) {  // row r as the right factor: rr >= r
-            const float e = __expf(Gm[rr * RS + c] - gr);
-            ska += S1[rr * 65 + r] * Qm[rr * RS + c] * e;
-            if (rr > r) skc += S2[rr * 65 + r] * M1[rr * RS + c] * e;
-        }
-        dqv[ii] = sq;
-        dkv[ii] = ska + skb + skc;
-        dgv[ii] = qr * sq - kr * ska + kr * skb - kr * skc;
-    }
-    // ---- 6. gated scalings, the last row's terms, and the reverse cumulative sum
+
+    // ---- 2. dB = T^T [dW | dV] (own tiles); dv = beta dB_v; dbeta's first terms
+    float dBk[4][4];
     {
-        float ls = 0.f;
+        float rowp[4][4];
 #pragma unroll
-        for (int ii = 0; ii < RPT; ++ii) {
-            const int r = r0 + ii;
-            const float gr = Gm[r * RS + c], qr = Qm[r * RS + c], kr = M1[r * RS + c];
-            const float E = __expf(gr), Em = __expf(gl[c] - gr);
-            const float dQp = SQp[r * D + c], dKm = SKm[r * D + c];
-            dqv[ii] += E * dQp;
-            dkv[ii] += E * dKp[ii] + Em * dKm;
-            const float km = Em * kr;
-            dgv[ii] += dQp * E * qr + dKp[ii] * E * kr - dKm * km;
-            ls += dKm * km;
+        for (int R = 0; R < 4; ++R) {
+            f32x4_t ak = {0.f, 0.f, 0.f, 0.f}, av = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int R2 = R; R2 < 4; ++R2) {
+                const f32x4_t t = *reinterpret_cast<const f32x4_t*>(TT + (16 * R + n) * SQS + 16 * R2 + 4 * G);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    ak = mfma4(t[s], dWo[R2][s], ak);
+                    av = mfma4(t[s], dVo[R2][s], av);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = own_row(R, i);
+                dBk[R][i] = ak[i];
+                const float vv = r < L ? ld_in(v, rowoff(r) + c) : 0.f;
+                if (r < L) dv[rowoff(r) + c] = bet[r] * av[i];
+                rowp[R][i] = ee(g2[R][i]) * ko[R][i] * ak[i] + vv * av[i];
+                DB[r * RX + c] = ak[i];
+                DB[r * RX + D + c] = av[i];
+            }
         }
-        gtot[grp * D + c] = ls;
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float t = sum16(rowp[R][i]);
+                if (n == 0) dbp[w * 64 + own_row(R, i)] = t;
+            }
+    }
+    __syncthreads();  // T dead, dB complete
+    // ---- 3. dA_kk = -dB X^T = dB_k (-W)^T + dB_v (-U)^T on the lower tiles
+    for (int e = tid; e < 64 * D / 4; e += NTH) {  // -W, stored in the split order
+        const int r = e / (D / 4), p = 4 * (e - r * (D / 4));
+        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(f.wn + fs * 64 * D + 4 * e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) TT[r * RS + split_chan(p + j)] = y[j];
     }
     __syncthreads();
-    // the chunk's last cumulative gate is G at row 63 (padding rows add 0): its
-    // terms go to row 63, which the reverse sum spreads over every row
-    if (r0 + RPT == 64) {
-        float ls = 0.f;
-        for (int gg = 0; gg < NG; ++gg) ls += gtot[gg * D + c];
-        dgv[RPT - 1] += ls + dgam[c] * __expf(gl[c]);
-    }
-    __syncthreads();  // gtot is reused below
-    {
-        float s = 0.f;
+    constexpr int MT = (10 + NW - 1) / NW;  // lower tiles per wave
+    f32x4_t da[MT];
+    auto tile_of = [](int t, int& R, int& I) {  // t < 10 -> (R, I), I <= R
+        R = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        I = t - R * (R + 1) / 2;
+    };
 #pragma unroll
-        for (int ii = RPT - 1; ii >= 0; --ii) {
-            s += dgv[ii];
-            dgv[ii] = s;
+    for (int m = 0; m < MT; ++m) {
+        da[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int t = w + NW * m;
+        if (t < 10) {
+            int R, I;
+            tile_of(t, R, I);
+            for (int s16 = 0; s16 < D / 16; ++s16)
+                mma16(da[m], DB + (16 * R + n) * RX + 16 * s16 + 4 * G, TT + (16 * I + n) * RS + 16 * s16 + 4 * G);
         }
-        gtot[grp * D + c] = s;
     }
     __syncthreads();
-    {
-        float later = 0.f;
-        for (int gg = grp + 1; gg < NG; ++gg) later += gtot[gg * D + c];
+    for (int e = tid; e < 64 * D / 4; e += NTH) {  // -U, stored as accumulator tiles
+        const int qd = e >> 6, ll = e & 63, ct = qd >> 2, R = qd & 3;
+        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(f.u + fs * 64 * D + 4 * e);
 #pragma unroll
-        for (int ii = 0; ii < RPT; ++ii) {
-            const int r = r0 + ii;
-            if (r < L) {
-                dq[rowoff(r) + c] = dqv[ii];
-                dk[rowoff(r) + c] = dkv[ii];
-                dla[rowoff(r) + c] = dgv[ii] + later;
+        for (int i = 0; i < 4; ++i) TT[(16 * R + 4 * (ll >> 4) + i) * RS + 16 * ct + (ll & 15)] = -y[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int t = w + NW * m;
+        if (t < 10) {
+            int R, I;
+            tile_of(t, R, I);
+            for (int s16 = 0; s16 < D / 16; ++s16)
+                mma16(da[m], DB + (16 * R + n) * RX + D + 16 * s16 + 4 * G,
+                      TT + (16 * I + n) * RS + 16 * s16 + 4 * G);
+            // dbeta's last term (sum_i dA_kk P_kk per row), then dP_kk = beta dA_kk over P_kk
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = own_row(R, i);
+                float* pk = PK + r * SQS + 16 * I + n;
+                const float x = (I < R || n < 4 * G + i) ? da[m][i] : 0.f;
+                const float t2 = sum16(x * *pk);
+                if (n == 0) dap[I * 64 + r] = t2;
+                *pk = bet[r] * x;
             }
         }
     }
-    // dbeta: this thread's terms to M2 (free by now), then one thread per row
-    // sums them over the channels in order
+    __syncthreads();
+
+    // ---- 4. adjoints of the gated products. Lq, Lk: row r as the left factor of
+    // A_qk / A_kk; Rr: row i as their right factor (both take the key there)
+    float Lq[4][4], Lk[4][4], Rr[4][4];
 #pragma unroll
-    for (int ii = 0; ii < RPT; ++ii) M2[(r0 + ii) * RS + c] = dbr[ii];
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Lq[R][i] = Lk[R][i] = Rr[R][i] = 0.f;
+    // blocks below the diagonal, split at the first row of the left factor's block ...
+#pragma unroll
+    for (int R = 1; R < 4; ++R) {
+        const float bR = __shfl(g2[R][0], n);
+        f32x4_t aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int R2 = 0; R2 < R; ++R2) {
+            const f32x4_t pq = *reinterpret_cast<const f32x4_t*>(DPQ + (16 * R + n) * SQS + 16 * R2 + 4 * G);
+            const f32x4_t pk = *reinterpret_cast<const f32x4_t*>(PK + (16 * R + n) * SQS + 16 * R2 + 4 * G);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float y = ko[R2][s] * ee(bR - g2[R2][s]);
+                aq = mfma4(pq[s], y, aq);
+                ak = mfma4(pk[s], y, ak);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float e = ee(g2[R][i] - bR);
+            Lq[R][i] = aq[i] * e;
+            Lk[R][i] = ak[i] * e;
+        }
+    }
+    // ... and at the last row of the right factor's block
+#pragma unroll
+    for (int I = 0; I < 3; ++I) {
+        const float aI = __shfl(g2[I][3], 48 + n);
+        f32x4_t ar = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int R2 = I + 1; R2 < 4; ++R2)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int r = 16 * R2 + 4 * G + s;
+                const float e = ee(g2[R2][s] - aI);
+                ar = mfma4(DPQ[r * SQS + 16 * I + n], qo[R2][s] * e, ar);
+                ar = mfma4(PK[r * SQS + 16 * I + n], ko[R2][s] * e, ar);
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Rr[I][i] = ar[i] * ee(aI - g2[I][i]);
+    }
+    // diagonal blocks, pair by pair with the exact exponential
+#pragma unroll
+    for (int B = 0; B < 4; ++B) {
+#pragma unroll 1
+        for (int G2 = 0; G2 < 4; ++G2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int p = 16 * B + 4 * G2 + j;
+                const float kp = __shfl(ko[B][j], 16 * G2 + n);
+                const float qp = __shfl(qo[B][j], 16 * G2 + n);
+                const float gp = __shfl(g2[B][j], 16 * G2 + n);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int x = 16 * B + 4 * G + i;
+                    const bool left = p <= x, right = p >= x;
+                    const int at = left ? x * SQS + p : p * SQS + x;
+                    const float e = ee(left ? g2[B][i] - gp : gp - g2[B][i]);
+                    const float pq = DPQ[at], pk = PK[at];
+                    if (left) {
+                        Lq[B][i] += pq * kp * e;
+                        Lk[B][i] += pk * kp * e;
+                    }
+                    if (right) Rr[B][i] += (pq * qp + pk * kp) * e;
+                }
+            }
+    }
+
+    // ---- 5. gated scalings, the last row's terms, the reverse cumulative sum
+    const float gl = __shfl(g2[3][3], 48 + n);  // cumulative gate of the chunk's last row
+    const float dgam = dgp[c] + dgp[D + c];
+    float dg[4][4], lsum = 0.f;
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+        const f32x4_t dqp = *reinterpret_cast<const f32x4_t*>(SQ + ((w * 4 + R) * 64 + l) * 4);
+        const f32x4_t dkm = *reinterpret_cast<const f32x4_t*>(SK + ((w * 4 + R) * 64 + l) * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = own_row(R, i);
+            const float E = ee(g2[R][i]), Em = ee(gl - g2[R][i]);
+            const float dkp = bet[r] * dBk[R][i];
+            const float qv = qo[R][i], kv = ko[R][i];
+            const float dqv = Lq[R][i] + E * dqp[i];
+            const float dkv = Lk[R][i] + Rr[R][i] + E * dkp + Em * dkm[i];
+            dg[R][i] = qv * Lq[R][i] + kv * Lk[R][i] - kv * Rr[R][i] + dqp[i] * E * qv + dkp * E * kv -
+                       dkm[i] * Em * kv;
+            lsum += dkm[i] * Em * kv;
+            if (r < L) {
+                dq[rowoff(r) + c] = dqv;
+                dk[rowoff(r) + c] = dkv;
+            }
+        }
+    }
+    {
+        float tot = 0.f;
+#pragma unroll
+        for (int G2 = 0; G2 < 4; ++G2) tot += __shfl(lsum, 16 * G2 + n);
+        if (G == 3) dg[3][3] += tot + dgam * ee(gl);  // row 63 (padding rows add nothing)
+    }
+    {
+        float S[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 3; i >= 0; --i) {
+                s += dg[R][i];
+                dg[R][i] = s;
+            }
+            S[R] = s;
+        }
+        float later = 0.f;  // whole blocks after R
+#pragma unroll
+        for (int R = 3; R >= 0; --R) {
+            float after = 0.f, total = 0.f;
+#pragma unroll
+            for (int G2 = 3; G2 >= 0; --G2) {
+                const float t = __shfl(S[R], 16 * G2 + n);
+                if (G2 > G) after += t;
+                total += t;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = own_row(R, i);
+                if (r < L) dla[rowoff(r) + c] = dg[R][i] + after + later;
+            }
+            later += total;
+        }
+    }
     __syncthreads();
     if (tid < L) {
-        float s = dbs[tid];
-        for (int cc = 0; cc < D; ++cc) s += M2[tid * RS + cc];
+        float s = 0.f;
+        for (int ww = 0; ww < NW; ++ww) s += dbp[ww * 64 + tid];
+        for (int I = 0; I <= (tid >> 4); ++I) s += dap[I * 64 + tid];
         dbeta[(int64_t)(t0 + tid) * H + h] = s;
     }
 }
 
 template <int D>
 static hipError_t launch_bwd_prep_d(const BwdArgs& a, hipStream_t st) {
-    constexpr int RS = D + 4;
-    const int bytes = (2 * 64 * RS + 64 * 65) * 4;
     auto kern = bwd_prep_kernel<D>;
+    const int bytes = BwdPrepSmem<D>::BYTES;
     const hipError_t e = allow_dynamic_lds((const void*)kern, bytes);
     if (e != hipSuccess) return e;
     const ChunkArgs& F = a.fwd;
@@ -495,7 +670,7 @@ static hipError_t launch_bwd_prep_d(const BwdArgs& a, hipStream_t st) {
                 (float*)F.vn};
     Ws<float> b{(float*)B.qp, (float*)B.km, (float*)B.wn, (float*)B.u, (float*)B.aqk, B.gam, (float*)B.h,
                 (float*)B.vn, nullptr, nullptr, B.pb};
-    hipLaunchKernelGGL(kern, dim3(F.NC * F.H), dim3(256), bytes, st, F.cu, F.N, F.T, F.H, f, b, a.d_o);
+    hipLaunchKernelGGL(kern, dim3(F.NC * F.H), dim3(4 * D), bytes, st, F.cu, F.N, F.T, F.H, f, b, a.d_o);
     return hipGetLastError();
 }
 
@@ -512,10 +687,10 @@ static hipError_t launch_bwd_local_t(const BwdArgs& a, hipStream_t st) {
     const ChunkArgs& F = a.fwd;
     const ChunkArgs& B = a.rec;
     Ws<float> f{(float*)F.qp, (float*)F.km, (float*)F.wn, (float*)F.u, (float*)F.aqk, F.gam, (float*)F.h,
-                (float*)F.vn};
+                (float*)F.vn, (float*)F.am};
     Ws<float> b{(float*)B.qp, (float*)B.km, (float*)B.wn, (float*)B.u, (float*)B.aqk, B.gam, (float*)B.h,
                 (float*)B.vn, nullptr, nullptr, B.pb};
-    hipLaunchKernelGGL(kern, dim3(F.NC * F.H), dim3(256), SM::BYTES, st, (const TIn*)F.q, (const TIn*)F.k,
+    hipLaunchKernelGGL(kern, dim3(F.NC * F.H), dim3(4 * D), SM::BYTES, st, (const TIn*)F.q, (const TIn*)F.k,
                        (const TIn*)F.v, (const TG*)F.la, (const TG*)F.beta, F.cu, F.N, F.T, F.H, f, b, a.d_o,
                        a.scr, a.dq, a.dk, a.dv, a.dla, a.dbeta);
     return hipGetLastError();

@@ -45,9 +45,10 @@ struct BwdArgs {
     ChunkArgs rec;    // state-gradient recursion over reversed chunk slots
     const float* d_o;  // [T, H, dv]
     float *dq, *dk, *dv, *dla, *dbeta;
-    float* scr;        // per chunk-head scratch, bwd_scr_floats(D) floats each
+    float* scr;        // per chunk-head scratch, bwd_scr_floats(D) floats each (dQ+, dK-)
 };
-__host__ __device__ inline int64_t bwd_scr_floats(int D) { return 4LL * 64 * D + 3LL * 64 * 64; }
+// (the gated key products the forward recompute keeps go to fwd.am, [64][64] fp32 per chunk-head)
+__host__ __device__ inline int64_t bwd_scr_floats(int D) { return 2LL * 64 * D; }
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_local(const BwdArgs& a, hipStream_t st);
 

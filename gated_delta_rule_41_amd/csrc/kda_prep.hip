@@ -31,9 +31,10 @@
 //     serves both factors (nothing downstream inverts again).
 //
 // Outputs (workspace, layouts in kda_common.h): Q+, K-^T, -W, U, A_qk and
-// gamma = 2^G_last for the chunk. Rows past the end of a sequence are
-// zero-padded (k = q = v = 0, beta = 0, log alpha = 0), which is exactly
-// neutral for every factor.
+// gamma = 2^G_last for the chunk; with fp32 factors and a destination given,
+// also the gated key products A_kk / beta, which the backward differentiates.
+// Rows past the end of a sequence are zero-padded (k = q = v = 0, beta = 0,
+// log alpha = 0), which is exactly neutral for every factor.
 #include "kda_common.h"
 #include "kda_launch.h"
 #include "kda_prep_util.h"
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
                 }
             }
             aqk_sl[m] = sq;
-            akk_sl[m] = ii < rr ? sk * beta_s[rr] : 0.f;
+            akk_sl[m] = ii < rr ? sk : 0.f;  // beta is applied where A_kk is stored
         }
     }
     if (slow || !SM::MT) __syncthreads();  // (block-uniform condition)
@@ -386,6 +387,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
         const int s2 = cc >> 5, c2 = cc & 31;
         aqk_out[(rr * 2 + s2) * 32 + 8 * ((c2 & 15) >> 2) + 4 * (c2 >> 4) + (c2 & 3)] = P::from_f(x);
     };
+    // the backward's forward recompute (fp32 factors) also keeps the gated key
+    // products P_kk = A_kk / beta, row-major [64][64], zero on and above the diagonal
+    float* pkk_out = nullptr;
+    if constexpr (F32) pkk_out = ws.am ? ws.am + chh * 64 * 64 : nullptr;
     // Wave I computes the blocks (I, J <= I) of both matrices, slice by slice
     // over the channels so that the operands of every block of a slice are
     // read together (I is made a compile-time constant per wave).
@@ -428,7 +433,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
         for (int J = 0; J < 4; ++J) {
             if (J > I) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) aqk_put(16 * I + 4 * g + i, 16 * J + n, 0.f);
+                for (int i = 0; i < 4; ++i) {
+                    aqk_put(16 * I + 4 * g + i, 16 * J + n, 0.f);
+                    if (pkk_out) pkk_out[(16 * I + 4 * g + i) * 64 + 16 * J + n] = 0.f;
+                }
                 continue;
             }
             const int blk = (J == I) ? I : 4 + pair_index(I, J);
@@ -439,6 +447,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
                 const bool lo_strict = (J < I) || (n < rl);
                 aqk_put(16 * I + rl, 16 * J + n, lo_incl ? aq[J][i] : 0.f);
                 Akk_s[blk * AKB + rl * AKS + n] = lo_strict ? ak[J][i] * beta_s[16 * I + rl] : 0.f;
+                if (pkk_out) pkk_out[(16 * I + rl) * 64 + 16 * J + n] = lo_strict ? ak[J][i] : 0.f;
             }
         }
     };
@@ -455,9 +464,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
             const int p = tid + 256 * m;
             const int rr = p >> 6, ii = p & 63, I = rr >> 4, J = ii >> 4;
             aqk_put(rr, ii, aqk_sl[m]);
+            if (pkk_out) pkk_out[rr * 64 + ii] = akk_sl[m];
             if (J <= I) {
                 const int blk = (J == I) ? I : 4 + pair_index(I, J);
-                Akk_s[blk * AKB + (rr & 15) * AKS + (ii & 15)] = akk_sl[m];
+                Akk_s[blk * AKB + (rr & 15) * AKS + (ii & 15)] = akk_sl[m] * beta_s[rr];
             }
         }
     }
@@ -597,7 +607,7 @@ template <int D, typename TIn, typename TG, bool F32>
 static hipError_t launch_prep_t(const ChunkArgs& a, hipStream_t st) {
     using E = typename Pol<F32>::E;
     using SM = PrepSmem<D, F32>;
-    Ws<E> ws{(E*)a.qp, (E*)a.km, (E*)a.wn, (E*)a.u, (E*)a.aqk, a.gam, (E*)a.h, (E*)a.vn};
+    Ws<E> ws{(E*)a.qp, (E*)a.km, (E*)a.wn, (E*)a.u, (E*)a.aqk, a.gam, (E*)a.h, (E*)a.vn, (E*)a.am};
     auto kern = prep_kernel<D, TIn, TG, F32>;
     const hipError_t e = allow_dynamic_lds((const void*)kern, SM::BYTES);
     if (e != hipSuccess) return e;

@@ -188,14 +188,14 @@ def test_dplr_validation():
 def test_bwd_workspace_size_formula():
     # per chunk-head, d = 128: the fp32 forward recompute (Q+, K-, -W, U, V_new
     # 32 KiB each, A_qk 16 KiB, gamma 512 B, h_n 64 KiB) twice (forward and the
-    # state-gradient recursion), the added term Q+^T dO 64 KiB and the local
-    # kernel's scratch (4 [64][128] + 3 [64][64] fp32) 176 KiB -> 738304 B
+    # state-gradient recursion), the added term Q+^T dO 64 KiB, the gated key
+    # products 16 KiB and the local kernel's scratch (dQ+, dK-) 64 KiB -> 640000 B
     fwd = 5 * 32768 + 16384 + 512 + 65536
-    assert kda.bwd_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * (2 * fwd + 65536 + 180224)
-    assert kda.bwd_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 738304
+    assert kda.bwd_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * (2 * fwd + 65536 + 16384 + 65536)
+    assert kda.bwd_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 640000
     fwd64 = 5 * 16384 + 16384 + 256 + 16384
     assert kda.bwd_workspace_size(2, 100, 1, 64, 64) == ((100 + 63 * 2) // 64) * (
-        2 * fwd64 + 16384 + 4 * (4 * 64 * 64 + 3 * 4096))
+        2 * fwd64 + 16384 + 16384 + 32768)
     with pytest.raises(kda.KDAError):
         kda.bwd_workspace_size(1, 10, 1, 64, 128)
 
