@@ -92,18 +92,6 @@ __device__ __forceinline__ float sum16(float x) {  // over the 16 lanes n of a l
     return x;
 }
 
-// Stage a [64][D] fragment array (V_new, dV) into LDS rows [64][RS].
-template <int D, int RS>
-__device__ __forceinline__ void stage_vfrag(float* dst, const float* src, int tid, int nth) {
-    for (int q = tid; q < 64 * D / 8; q += nth) {
-        const int blk = q >> 6, fl = q & 63, ct = blk >> 1, s = blk & 1, g = fl >> 4, j = 16 * ct + (fl & 15);
-        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src + q * 8);
-        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(src + q * 8 + 4);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) dst[(32 * s + frag_row(g, jj)) * RS + j] = jj < 4 ? a[jj] : b[jj - 4];
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Operands of the state-gradient recursion for chunk slot gc, written to its
 // reversed slot: -W := K-, K-^T := (-W)^T, gamma, U := A_qk^T dO (accumulator
@@ -112,7 +100,8 @@ __device__ __forceinline__ void stage_vfrag(float* dst, const float* src, int ti
 template <int D>
 struct BwdPrepSmem {
     static constexpr int RS = D + 4, SQS = 68;
-    static constexpr int BYTES = (2 * 64 * RS + 64 * SQS) * 4;
+    static constexpr int PRODUCTS = 2 * 64 * RS + 64 * SQS, COPIES = D * SQS + 64 * RS;
+    static constexpr int BYTES = (PRODUCTS > COPIES ? PRODUCTS : COPIES) * 4;
 };
 
 template <int D>
@@ -120,39 +109,53 @@ __global__ __launch_bounds__(4 * D) void bwd_prep_kernel(const int32_t* __restri
                                                          Ws<float> f, Ws<float> b,
                                                          const float* __restrict__ d_o) {
     constexpr int NT = D / 16, NTH = 4 * D, RS = BwdPrepSmem<D>::RS, SQS = BwdPrepSmem<D>::SQS;
+    constexpr int NQ = 64 * D / 4 / NTH;      // float4 per thread of a [64][D] array (= 4)
+    constexpr int NA = 64 * 64 / 4 / NTH;     // ... of a [64][64] array (1 or 2)
     extern __shared__ __align__(16) float sm[];
     float* dO = sm;                // [64][RS]
     float* Qp = dO + 64 * RS;      // [64][RS], channels in natural order
     float* Aq = Qp + 64 * RS;      // [64][SQS] A_qk
+    float* KmL = sm;               // after the products: K-^T as stored, [D][SQS]
+    float* WnL = sm + D * SQS;     // -W as stored, [64][RS]
     const int gc = blockIdx.x / H, h = blockIdx.x - gc * H;
     ChunkLoc loc;
     if (!locate_chunk(cu, N, T, gc, loc)) return;
     const int rev = reversed_slot(cu, T, loc.seq, gc);
     const int64_t src = (int64_t)gc * H + h, dst = (int64_t)rev * H + h;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, n = l & 15;
-    for (int e = tid; e < 64 * D / 4; e += NTH) {
-        const int r = e / (D / 4), c4 = 4 * (e - r * (D / 4));
-        const f32x4_t x = r < loc.L ? *reinterpret_cast<const f32x4_t*>(d_o + ((int64_t)(loc.t0 + r) * H + h) * D + c4)
-                                    : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4_t*>(dO + r * RS + c4) = x;
-        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(f.qp + src * 64 * D + 4 * e);
+    // every load of the stage first, then the LDS stores
+    f32x4_t xo[NQ], xq[NQ], xa[NA];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Qp[r * RS + split_chan(c4 + j)] = y[j];
+    for (int m = 0; m < NQ; ++m) {
+        const int e = tid + NTH * m, r = e / (D / 4), c4 = 4 * (e - r * (D / 4));
+        xo[m] = r < loc.L ? *reinterpret_cast<const f32x4_t*>(d_o + ((int64_t)(loc.t0 + r) * H + h) * D + c4)
+                          : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        xq[m] = *reinterpret_cast<const f32x4_t*>(f.qp + src * 64 * D + 4 * e);
     }
-    for (int e = tid; e < 64 * 64 / 4; e += NTH) {
-        const int r = e >> 4, p = 4 * (e & 15);
-        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(f.aqk + src * 64 * 64 + 4 * e);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Aq[r * SQS + split_chan(p + j)] = y[j];
+    for (int m = 0; m < NA; ++m) xa[m] = *reinterpret_cast<const f32x4_t*>(f.aqk + src * 64 * 64 + 4 * (tid + NTH * m));
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+        const int e = tid + NTH * m, r = e / (D / 4), c4 = 4 * (e - r * (D / 4));
+        *reinterpret_cast<f32x4_t*>(dO + r * RS + c4) = xo[m];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Qp[r * RS + split_chan(c4 + j)] = xq[m][j];
     }
-    // K- to the -W layout; (-W)^T to the K-^T layout; gamma
-    for (int e = tid; e < 64 * D; e += NTH) {
-        const int r = e / D, c = e - r * D;
-        b.wn[dst * 64 * D + split_index(r, c, D)] = f.km[src * D * 64 + split_index(c, r, 64)];
-        b.km[dst * D * 64 + split_index(c, r, 64)] = f.wn[src * 64 * D + split_index(r, c, D)];
+#pragma unroll
+    for (int m = 0; m < NA; ++m) {
+        const int e = tid + NTH * m, r = e >> 4, p = 4 * (e & 15);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Aq[r * SQS + split_chan(p + j)] = xa[m][j];
     }
     for (int c = tid; c < D; c += NTH) b.gam[dst * D + c] = f.gam[src * D + c];
     __syncthreads();
+    // the copies' sources, in flight during the products
+    f32x4_t ykm[NQ], ywn[NQ];
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+        ykm[m] = *reinterpret_cast<const f32x4_t*>(f.km + src * D * 64 + 4 * (tid + NTH * m));
+        ywn[m] = *reinterpret_cast<const f32x4_t*>(f.wn + src * 64 * D + 4 * (tid + NTH * m));
+    }
     const int j0 = 16 * w;
     // P[c][j] = sum_r Q+[r][c] dO[r][j]; U[r][j] = sum_{i >= r} A_qk[i][r] dO[i][j]
     f32x4_t accP[NT], accU[4];
@@ -176,6 +179,36 @@ __global__ __launch_bounds__(4 * D) void bwd_prep_kernel(const int32_t* __restri
 #pragma unroll
     for (int R = 0; R < 4; ++R)
         *reinterpret_cast<f32x4_t*>(b.u + dst * 64 * D + ((w * 4 + R) * 64 + l) * 4) = accU[R];
+    __syncthreads();  // the products' operands are dead
+    // K- to the -W layout and (-W)^T to the K-^T layout, both through LDS so that
+    // global reads and writes are whole 16-byte vectors
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+        const int e = tid + NTH * m;
+        const int c = e >> 4, p = 4 * (e & 15);           // K-^T: row c, positions p.. of its 64
+        *reinterpret_cast<f32x4_t*>(KmL + c * SQS + p) = ykm[m];
+        const int r = e / (D / 4), p2 = 4 * (e - r * (D / 4));  // -W: row r, positions p2..
+        *reinterpret_cast<f32x4_t*>(WnL + r * RS + p2) = ywn[m];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+        const int e = tid + NTH * m;
+        {   // -W layout: row r, positions p..p+3 hold channels split_chan(p..p+3) of K-
+            const int r = e / (D / 4), p = 4 * (e - r * (D / 4)), pr = split_pos(r) + 32 * (r >> 5);
+            f32x4_t o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = KmL[split_chan(p + j) * SQS + pr];
+            *reinterpret_cast<f32x4_t*>(b.wn + dst * 64 * D + 4 * e) = o;
+        }
+        {   // K-^T layout: row c, positions p..p+3 hold rows split_chan(p..p+3) of -W
+            const int c = e >> 4, p = 4 * (e & 15), pc = split_pos(c) + 32 * (c >> 5);
+            f32x4_t o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = WnL[split_chan(p + j) * RS + pc];
+            *reinterpret_cast<f32x4_t*>(b.km + dst * D * 64 + 4 * e) = o;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -247,22 +280,61 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
 
     if (tid < 64) bet[tid] = tid < L ? ld_in(beta, (int64_t)(t0 + tid) * H + h) : 0.f;
 
-    // ---- 0a. h, dV, dO to LDS; dQ+ = dO h^T and dW = -dV h^T (own tiles)
-    for (int qq = tid; qq < D * D / 8; qq += NTH) {
-        const int blk = qq >> 6, fl = qq & 63, ct = blk / NS, s = blk - ct * NS, g = fl >> 4;
-        const int j = 16 * ct + (fl & 15);
-        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(hF + qq * 8);
-        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(hF + qq * 8 + 4);
+    // ---- 0a. h, dV, dO to LDS; dQ+ = dO h^T and dW = -dV h^T (own tiles).
+    // Every stage issues all of its global loads before it stores any of them, and
+    // the next stage's loads are issued before this stage's products.
+    constexpr int NHQ = D * D / 8 / NTH, NVQ = 64 * D / 8 / NTH, NOQ = 64 * D / 4 / NTH;
+    const int g = l >> 4, s0 = w % NS;  // a thread's fragment lane group and 32-row slice of h
+    auto h_row = [&](int jj) { return 32 * s0 + frag_row(g, jj); };
+    auto h_col = [&](int m) { return 16 * (((tid + NTH * m) >> 6) / NS) + (l & 15); };
+    f32x4_t xh[NHQ][2], xv[NVQ][2], xo[NOQ];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) HB[(32 * s + frag_row(g, jj)) * RS + j] = jj < 4 ? x0[jj] : x1[jj - 4];
+    for (int m = 0; m < NHQ; ++m) {
+        xh[m][0] = *reinterpret_cast<const f32x4_t*>(hF + (tid + NTH * m) * 8);
+        xh[m][1] = *reinterpret_cast<const f32x4_t*>(hF + (tid + NTH * m) * 8 + 4);
     }
-    stage_vfrag<D, RS>(VV, dVB, tid, NTH);
-    for (int e = tid; e < 64 * D / 4; e += NTH) {
-        const int r = e / (D / 4), c4 = 4 * (e - r * (D / 4));
-        *reinterpret_cast<f32x4_t*>(DO + r * RS + c4) =
-            r < L ? *reinterpret_cast<const f32x4_t*>(d_o + rowoff(r) + c4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NVQ; ++m) {
+        xv[m][0] = *reinterpret_cast<const f32x4_t*>(dVB + (tid + NTH * m) * 8);
+        xv[m][1] = *reinterpret_cast<const f32x4_t*>(dVB + (tid + NTH * m) * 8 + 4);
+    }
+#pragma unroll
+    for (int m = 0; m < NOQ; ++m) {
+        const int e = tid + NTH * m, r = e / (D / 4), c4 = 4 * (e - r * (D / 4));
+        xo[m] = r < L ? *reinterpret_cast<const f32x4_t*>(d_o + rowoff(r) + c4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    // (the fragment blocks of thread tid + NTH m all share the slice s0: NTH / 64 = 2 NS)
+#pragma unroll
+    for (int m = 0; m < NHQ; ++m)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) HB[h_row(jj) * RS + h_col(m)] = jj < 4 ? xh[m][0][jj] : xh[m][1][jj - 4];
+    auto v_put = [&](float* dst, const f32x4_t (&x)[NVQ][2]) {
+#pragma unroll
+        for (int m = 0; m < NVQ; ++m) {
+            const int q2 = tid + NTH * m, blk = q2 >> 6, ct = blk >> 1, sv = blk & 1, j = 16 * ct + (l & 15);
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                dst[(32 * sv + frag_row(g, jj)) * RS + j] = jj < 4 ? x[m][0][jj] : x[m][1][jj - 4];
+        }
+    };
+    v_put(VV, xv);
+#pragma unroll
+    for (int m = 0; m < NOQ; ++m) {
+        const int e = tid + NTH * m, r = e / (D / 4), c4 = 4 * (e - r * (D / 4));
+        *reinterpret_cast<f32x4_t*>(DO + r * RS + c4) = xo[m];
     }
     __syncthreads();
+    // dh' and V in flight during the products
+#pragma unroll
+    for (int m = 0; m < NHQ; ++m) {
+        xh[m][0] = *reinterpret_cast<const f32x4_t*>(dhB + (tid + NTH * m) * 8);
+        xh[m][1] = *reinterpret_cast<const f32x4_t*>(dhB + (tid + NTH * m) * 8 + 4);
+    }
+#pragma unroll
+    for (int m = 0; m < NVQ; ++m) {
+        xv[m][0] = *reinterpret_cast<const f32x4_t*>(vF + (tid + NTH * m) * 8);
+        xv[m][1] = *reinterpret_cast<const f32x4_t*>(vF + (tid + NTH * m) * 8 + 4);
+    }
     float dWo[4][4], dVo[4][4];  // own dW and dV
     {
         f32x4_t aq[4], aw[4];
@@ -293,27 +365,28 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
         float pg[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) pg[jj] = 0.f;
-        const int g = l >> 4, s = w % NS;  // fixed per thread (the block count per pass is 2 NS)
-        for (int qq = tid; qq < D * D / 8; qq += NTH) {
-            const int ct = (qq >> 6) / NS, j = 16 * ct + (l & 15);
-            const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(dhB + qq * 8);
-            const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(dhB + qq * 8 + 4);
+#pragma unroll
+        for (int m = 0; m < NHQ; ++m)
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
-                const float x = jj < 4 ? x0[jj] : x1[jj - 4];
-                float* p = HB + (32 * s + frag_row(g, jj)) * RS + j;
+                const float x = jj < 4 ? xh[m][0][jj] : xh[m][1][jj - 4];
+                float* p = HB + h_row(jj) * RS + h_col(m);
                 pg[jj] += *p * x;
                 *p = x;
             }
-        }
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
             const float t = sum16(pg[jj]);
-            if (n == 0) dgp[(w / NS) * D + 32 * s + frag_row(g, jj)] = t;
+            if (n == 0) dgp[(w / NS) * D + h_row(jj)] = t;
         }
     }
-    stage_vfrag<D, RS>(VV, vF, tid, NTH);
+    v_put(VV, xv);
     __syncthreads();
+    // P_kk in flight during the products
+    constexpr int NPK = 64 * 64 / 4 / NTH;
+    f32x4_t xp[NPK];
+#pragma unroll
+    for (int m = 0; m < NPK; ++m) xp[m] = *reinterpret_cast<const f32x4_t*>(Pkk + 4 * (tid + NTH * m));
     // dK- = V dh'^T (own tiles); dA_qk = tril(dO V^T) (tiles spread over the waves)
     {
         f32x4_t ak[4];
@@ -379,9 +452,10 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
     __syncthreads();  // phase-0 arrays dead
 
     // ---- 1. T = (I + diag(beta) P_kk)^-1, stored transposed: TT[r][m] = T[m][r]
-    for (int e = tid; e < 64 * 16; e += NTH) {
-        const int r = e >> 4, i4 = 4 * (e & 15);
-        *reinterpret_cast<f32x4_t*>(PK + r * SQS + i4) = *reinterpret_cast<const f32x4_t*>(Pkk + r * 64 + i4);
+#pragma unroll
+    for (int m = 0; m < NPK; ++m) {
+        const int e = tid + NTH * m;
+        *reinterpret_cast<f32x4_t*>(PK + (e >> 4) * SQS + 4 * (e & 15)) = xp[m];
     }
     __syncthreads();
     if (w == 0) {  // diagonal blocks by forward substitution: lane = (block, column)
@@ -423,6 +497,12 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
     }
 
     // ---- 2. dB = T^T [dW | dV] (own tiles); dv = beta dB_v; dbeta's first terms
+    f32x4_t xw[NOQ], xu[NOQ];  // -W and U in flight
+#pragma unroll
+    for (int m = 0; m < NOQ; ++m) {
+        xw[m] = *reinterpret_cast<const f32x4_t*>(f.wn + fs * 64 * D + 4 * (tid + NTH * m));
+        xu[m] = *reinterpret_cast<const f32x4_t*>(f.u + fs * 64 * D + 4 * (tid + NTH * m));
+    }
     float dBk[4][4];
     {
         float rowp[4][4];
@@ -459,11 +539,11 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
     }
     __syncthreads();  // T dead, dB complete
     // ---- 3. dA_kk = -dB X^T = dB_k (-W)^T + dB_v (-U)^T on the lower tiles
-    for (int e = tid; e < 64 * D / 4; e += NTH) {  // -W, stored in the split order
-        const int r = e / (D / 4), p = 4 * (e - r * (D / 4));
-        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(f.wn + fs * 64 * D + 4 * e);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) TT[r * RS + split_chan(p + j)] = y[j];
+    for (int m = 0; m < NOQ; ++m) {  // -W, stored in the split order
+        const int e = tid + NTH * m, r = e / (D / 4), p = 4 * (e - r * (D / 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) TT[r * RS + split_chan(p + j)] = xw[m][j];
     }
     __syncthreads();
     constexpr int MT = (10 + NW - 1) / NW;  // lower tiles per wave
@@ -484,11 +564,11 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
         }
     }
     __syncthreads();
-    for (int e = tid; e < 64 * D / 4; e += NTH) {  // -U, stored as accumulator tiles
-        const int qd = e >> 6, ll = e & 63, ct = qd >> 2, R = qd & 3;
-        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(f.u + fs * 64 * D + 4 * e);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) TT[(16 * R + 4 * (ll >> 4) + i) * RS + 16 * ct + (ll & 15)] = -y[i];
+    for (int m = 0; m < NOQ; ++m) {  // -U, stored as accumulator tiles
+        const int e = tid + NTH * m, qd = e >> 6, ll = e & 63, ct = qd >> 2, R = qd & 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) TT[(16 * R + 4 * (ll >> 4) + i) * RS + 16 * ct + (ll & 15)] = -xu[m][i];
     }
     __syncthreads();
 #pragma unroll
@@ -561,7 +641,44 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
 #pragma unroll
         for (int i = 0; i < 4; ++i) Rr[I][i] = ar[i] * ee(aI - g2[I][i]);
     }
-    // diagonal blocks, pair by pair with the exact exponential
+    // diagonal blocks. When no gate falls by more than DIAG_RANGE across a block,
+    // the exponential splits at the block's row 8 with every factor at most
+    // e^DIAG_RANGE (only the products' true size survives the rescale), and the
+    // blocks go to the matrix cores like the others; otherwise pair by pair with
+    // the exact exponential.
+    constexpr float DIAG_RANGE = 60.f;
+    int wide = 0;
+#pragma unroll
+    for (int B = 0; B < 4; ++B) wide |= __shfl(g2[B][0], n) - __shfl(g2[B][3], 48 + n) > DIAG_RANGE;
+    if (!__syncthreads_or(wide)) {
+#pragma unroll
+        for (int B = 0; B < 4; ++B) {
+            const float a = __shfl(g2[B][0], 32 + n);  // the gate at row 16 B + 8
+            float up[4], dn[4];                        // e^(g - a), e^(a - g) of the own rows
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                up[i] = ee(g2[B][i] - a);
+                dn[i] = ee(a - g2[B][i]);
+            }
+            f32x4_t aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f}, ar = {0.f, 0.f, 0.f, 0.f};
+            const f32x4_t pq = *reinterpret_cast<const f32x4_t*>(DPQ + (16 * B + n) * SQS + 16 * B + 4 * G);
+            const f32x4_t pk = *reinterpret_cast<const f32x4_t*>(PK + (16 * B + n) * SQS + 16 * B + 4 * G);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = 16 * B + 4 * G + t;
+                aq = mfma4(pq[t], ko[B][t] * dn[t], aq);
+                ak = mfma4(pk[t], ko[B][t] * dn[t], ak);
+                ar = mfma4(DPQ[r * SQS + 16 * B + n], qo[B][t] * up[t], ar);
+                ar = mfma4(PK[r * SQS + 16 * B + n], ko[B][t] * up[t], ar);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Lq[B][i] += aq[i] * up[i];
+                Lk[B][i] += ak[i] * up[i];
+                Rr[B][i] += ar[i] * dn[i];
+            }
+        }
+    } else {
 #pragma unroll
     for (int B = 0; B < 4; ++B) {
 #pragma unroll 1
@@ -586,6 +703,7 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
                     if (right) Rr[B][i] += (pq * qp + pk * kp) * e;
                 }
             }
+    }
     }
 
     // ---- 5. gated scalings, the last row's terms, the reverse cumulative sum

@@ -63,6 +63,15 @@ def test_slow_gates_no_final_gradient():
     check(case, "slow gates, no d_final", with_final=False)
 
 
+@pytest.mark.parametrize("shift", [3.5, 6.0])
+def test_strong_decay(shift):
+    """Gates falling by more than 60 nats across a 16-row block take the exact
+    pairwise path for the diagonal blocks (every block at shift 6, a mix of both
+    paths over the chunks at shift 3.5)."""
+    case = ki.make_prefill("prefill-4k", DEV, lengths=[200, 77], H=2, gate_shift=shift, s0_std=0.02)
+    check(case, f"strong decay, gate shift {shift}")
+
+
 def test_prefill_4k_shape_four_heads():
     """T = 4096, d = 128 (64 chained chunks backwards), bf16 inputs, 4 heads."""
     case = ki.make_prefill("prefill-4k", DEV, H=4)
