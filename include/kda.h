@@ -149,9 +149,10 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
 
 /*
  * Bytes of device workspace kda_chunk_bwd needs (host call, no device access):
- * the forward recomputed with fp32 factors, the state-gradient recursion's
- * operands and outputs, and per-chunk scratch, for at most
- * floor((T_total + 63*N) / 64) chunks per head.
+ * the forward recomputed with fp32 factors (with the gated key products), the
+ * state-gradient recursion's operands and outputs, and per-chunk scratch, for
+ * at most floor((T_total + 63*N) / 64) chunks per head (640,000 bytes per
+ * chunk-head at dk = dv = 128).
  *   bytes: host out-pointer, written on KDA_OK.
  */
 kda_status kda_chunk_bwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
@@ -176,8 +177,12 @@ kda_status kda_chunk_bwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
  *                   d_final_state (in place), any other overlap is KDA_ERR_ALIAS
  *   workspace       at least kda_chunk_bwd_workspace_size() bytes, 256-byte
  *                   aligned; contents on entry do not matter
- * All arithmetic is fp32 (bf16 inputs are widened exactly). Five kernels are
- * enqueued. Deterministic: no atomics on global memory.
+ * Arithmetic is fp32 (bf16 inputs are widened exactly): fp32 matrix-core
+ * products, except the recomputed forward chain, whose products use split
+ * bf16 operands (about 16 significant bits) with fp32 accumulation. The same
+ * log_alpha condition as kda_chunk_fwd holds (<= 0 for the overflow
+ * guarantees). Five kernels are enqueued. Deterministic: every sum has a
+ * fixed order, so equal inputs give bitwise equal gradients.
  */
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* beta, const float* initial_state, const int32_t* cu_seqlens,
