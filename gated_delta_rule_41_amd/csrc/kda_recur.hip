@@ -56,8 +56,12 @@ struct RecurPlan {
     // target of the L2 warm-up loads (never read); DPLR has no room for it and
     // aims them at the unread tail of ring slot 0's gamma region instead
     static constexpr int WARM = (FUSED && !DPLR) ? 256 : 0;
-    static constexpr int RING = (4 * SLOT + HV + PB + WARM <= 160 * 1024) ? 4 : 2;
-    static constexpr int LDS = RING * SLOT + HV + PB + WARM;
+    // unfused (fp32 factors): NCW compute waves exchange their row tiles of the
+    // state ([D/16][64 lanes][4]) and of V_new ([4][64][4]) through LDS
+    static constexpr int NCW = FUSED ? 1 : 4;
+    static constexpr int XCH = FUSED ? 0 : (D / 16 + 4) * 64 * 4 * (int)sizeof(E);
+    static constexpr int RING = (4 * SLOT + HV + PB + WARM + XCH <= 160 * 1024) ? 4 : 2;
+    static constexpr int LDS = RING * SLOT + HV + PB + WARM + XCH;
     static_assert(!DPLR || (FUSED && GPAD - GB >= 256), "warm-up target in the gamma pad");
     static_assert(LDS <= 160 * 1024, "LDS budget");
     // global->LDS loads per chunk and producer wave (16 bytes per lane, 1 KiB per load)
@@ -203,6 +207,12 @@ __device__ __forceinline__ void warm_chunk(const Ws<typename Pol<F32>::E>& ws, i
 // output, 3-4 producers, 5 L2 warm-up (6: DPLR state-independent update).
 // Every wave executes the same 1 + nch barriers.
 //
+// Unfused (fp32 factors, 16x16x4 fp32 products): one chain step is 256
+// products at d = 128, too many for one wave's matrix core, so four compute
+// waves share it (each the state's row tiles of one quarter and one 16-row
+// tile of V_new), and the tiles meet in LDS twice per chunk. Waves: 0-3
+// compute, 4-5 producers; every wave executes 1 + 2 nch barriers.
+//
 // DPLR (the general transition, factors from kda_dplr_prep.hip): the chain is
 // the same with -u = -U' + (-W') h in place of V_new and A-^T in place of
 // K-^T, plus two state-independent terms: the state update adds K-^T V and the
@@ -210,7 +220,7 @@ __device__ __forceinline__ void warm_chunk(const Ws<typename Pol<F32>::E>& ws, i
 // The prep kernel computes K-^T V; a seventh wave copies this slab's share of
 // it into an LDS buffer (by chunk parity) one chunk ahead of the compute wave.
 template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false, bool ADDP = false>
-__global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 192) void recur_kernel(const float* __restrict__ s0,
+__global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel(const float* __restrict__ s0,
                                                                   float* __restrict__ s_final,
                                                                   const int32_t* __restrict__ cu, int N, int T,
                                                                   int H, Ws<typename Pol<F32>::E> ws,
@@ -389,9 +399,9 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 192) void recur_kernel
         return;
     }
 
-    if (wv > 0) {
-        // ---------------- producers (waves 1 and 2; 3 and 4 when fused)
-        const int pw = FUSED ? wv - 3 : wv - 1;
+    if (wv >= (FUSED ? 1 : PL::NCW)) {
+        // ---------------- producers (waves 3 and 4 when fused, else the two after the compute waves)
+        const int pw = FUSED ? wv - 3 : wv - PL::NCW;
         const int pre = nch < RING - 1 ? nch : RING - 1;
         for (int c = 0; c < pre; ++c)
             produce<D, F32, FUSED, DPLR>(ws, (int64_t)(co + c) * H + h, ct, pw, l, ring + c * PL::SLOT);
@@ -407,11 +417,117 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 192) void recur_kernel
             const int nx = c + RING - 1;
             if (nx < nch)
                 produce<D, F32, FUSED, DPLR>(ws, (int64_t)(co + nx) * H + h, ct, pw, l, ring + (nx % RING) * PL::SLOT);
+            if constexpr (!FUSED) __builtin_amdgcn_s_barrier();  // the compute waves' V_new exchange
             // chunk c + 1 + LOOK has landed once only the chunks issued after it are outstanding
             const int last = nch - 1 < nx ? nch - 1 : nx;
             const int need = nch - 1 < c + 1 + LOOK ? nch - 1 : c + 1 + LOOK;
             wait_chunks<OPS, RING>(last - need);
             __builtin_amdgcn_s_barrier();
+        }
+        return;
+    }
+
+    if constexpr (!FUSED) {
+        // ---------------- NCW compute waves (fp32 factors). Wave q owns the
+        // state's row tiles TH q .. TH q + TH - 1 and V_new's row tile q; both
+        // are exchanged as accumulator tiles through LDS and every wave builds
+        // the B fragments of the whole state and V_new from them.
+        constexpr int NCW = PL::NCW, TH = NT / NCW;
+        const int q = wv;
+        f32x4_t* XS = reinterpret_cast<f32x4_t*>(ring + RING * PL::SLOT);  // [NT][64 lanes] state tiles
+        f32x4_t* XV = XS + NT * 64;                                        // [4][64] V_new tiles
+        f32x4_t S[TH];  // rows 16 (TH q + tt) + 4g + i, column 16 ct + n
+        const int64_t sbase = (int64_t)unit * D * D + 16 * ct + n;
+#pragma unroll
+        for (int tt = 0; tt < TH; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[tt][i] = s0 ? s0[sbase + (int64_t)(16 * (TH * q + tt) + 4 * g + i) * D] : 0.f;
+        // ADDP: the added term of chunk c + 1 is loaded at the start of chunk c
+        f32x4_t pc[ADDP ? TH : 1], pnx[ADDP ? TH : 1];
+        auto load_p = [&](int c, f32x4_t (&dst)[ADDP ? TH : 1]) {
+            if constexpr (ADDP) {
+                const float* pp = ws.pb + ((int64_t)(co + c) * H + h) * D * D + (int64_t)ct * NT * 64 * 4;
+#pragma unroll
+                for (int tt = 0; tt < TH; ++tt)
+                    dst[tt] = *reinterpret_cast<const f32x4_t*>(pp + ((TH * q + tt) * 64 + l) * 4);
+            }
+        };
+        auto put_s = [&]() {
+#pragma unroll
+            for (int tt = 0; tt < TH; ++tt) XS[(TH * q + tt) * 64 + l] = S[tt];
+        };
+        put_s();
+        if (nch > 0) load_p(0, pc);
+        __builtin_amdgcn_s_barrier();
+        for (int c = 0; c < nch; ++c) {
+            const char* slot = ring + (c % RING) * PL::SLOT;
+            const char* wsl = slot;
+            const char* ksl = slot + PL::FB;
+            const E* usl = reinterpret_cast<const E*>(slot + 2 * PL::FB);
+            const float* gsl = reinterpret_cast<const float*>(slot + 2 * PL::FB + PL::UB);
+            const int64_t chh = (int64_t)(co + c) * H + h;
+            if (ADDP && c + 1 < nch) load_p(c + 1, pnx);
+            // the whole state as B fragments; this wave's share of h_n out
+            Frag sb[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) sb[s] = frag_from_acc<F32>(XS[(2 * s) * 64 + l], XS[(2 * s + 1) * 64 + l]);
+            E* hp = ws.h + chh * D * D + (int64_t)ct * NS * 64 * 8;
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                if (s % NCW == q) P::store(hp + (s * 64 + l) * 8, sb[s]);
+            // V_new = U + (-W) S on row tile q
+            f32x4_t V = *reinterpret_cast<const f32x4_t*>(usl + (q * 64 + l) * 4);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int gr = ((16 * q + n) * NS + s) * 4 + g;
+                P::mma(V, P::load(reinterpret_cast<const E*>(wsl + gr * 8 * sizeof(E))), sb[s]);
+            }
+            XV[q * 64 + l] = V;
+            // this wave's K-^T fragments and gamma while the other tiles land
+            Frag kf[TH][2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int tt = 0; tt < TH; ++tt) {
+                    const int gr = ((16 * (TH * q + tt) + n) * 2 + s) * 4 + g;
+                    kf[tt][s] = P::load(reinterpret_cast<const E*>(ksl + gr * 8 * sizeof(E)));
+                }
+            f32x4_t gm[TH];
+#pragma unroll
+            for (int tt = 0; tt < TH; ++tt) gm[tt] = *reinterpret_cast<const f32x4_t*>(gsl + 16 * (TH * q + tt) + 4 * g);
+            __builtin_amdgcn_s_barrier();  // every V_new tile in LDS
+            Frag vb[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) vb[s] = frag_from_acc<F32>(XV[(2 * s) * 64 + l], XV[(2 * s + 1) * 64 + l]);
+            E* vp = ws.vn + chh * 64 * D + (int64_t)ct * 2 * 64 * 8;
+            if (q == 0) P::store(vp + l * 8, vb[0]);  // (no index by q: it would put vb in scratch)
+            if (q == 1) P::store(vp + (64 + l) * 8, vb[1]);
+            // S <- Diag(gamma) S (+ the added term) + K-^T V_new on this wave's row tiles
+#pragma unroll
+            for (int tt = 0; tt < TH; ++tt) {
+                if constexpr (ADDP)
+                    S[tt] = gm[tt] * S[tt] + pc[tt];
+                else
+                    S[tt] = gm[tt] * S[tt];
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int tt = 0; tt < TH; ++tt) P::mma(S[tt], kf[tt][s], vb[s]);
+            put_s();
+            if constexpr (ADDP) {
+#pragma unroll
+                for (int tt = 0; tt < TH; ++tt) pc[tt] = pnx[tt];
+            }
+            __builtin_amdgcn_s_barrier();  // end of chunk: slot free, state tiles in LDS
+        }
+        if (s_final) {
+#pragma unroll
+            for (int tt = 0; tt < TH; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    s_final[sbase + (int64_t)(16 * (TH * q + tt) + 4 * g + i) * D] = S[tt][i];
         }
         return;
     }
@@ -548,7 +664,7 @@ static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     auto kern = recur_kernel<D, F32, FUSED, OUT_F32, DPLR, ADDP>;
     const hipError_t e = allow_dynamic_lds((const void*)kern, PL::LDS);
     if (e != hipSuccess) return e;
-    dim3 grid(NU * NT), block(FUSED ? (DPLR ? 448 : 384) : 192);
+    dim3 grid(NU * NT), block(FUSED ? (DPLR ? 448 : 384) : 64 * (PL::NCW + 2));
     hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.cu, a.N, a.T, a.H, ws, a.o);
     return hipGetLastError();
 }

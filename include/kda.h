@@ -177,11 +177,9 @@ kda_status kda_chunk_bwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
  *                   d_final_state (in place), any other overlap is KDA_ERR_ALIAS
  *   workspace       at least kda_chunk_bwd_workspace_size() bytes, 256-byte
  *                   aligned; contents on entry do not matter
- * Arithmetic is fp32 (bf16 inputs are widened exactly): fp32 matrix-core
- * products, except the recomputed forward chain, whose products use split
- * bf16 operands (about 16 significant bits) with fp32 accumulation. The same
- * log_alpha condition as kda_chunk_fwd holds (<= 0 for the overflow
- * guarantees). Five kernels are enqueued. Deterministic: every sum has a
+ * Arithmetic is fp32 throughout (bf16 inputs are widened exactly; every
+ * product runs on fp32 matrix cores). The same log_alpha condition as
+ * kda_chunk_fwd holds (<= 0 for the overflow guarantees). Five kernels are enqueued. Deterministic: every sum has a
  * fixed order, so equal inputs give bitwise equal gradients.
  */
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
