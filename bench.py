@@ -484,7 +484,9 @@ def main(argv=None):
         out["backward"] = {
             "workload": "prefill-4k, d_o ~ N(0,1), d_final_state ~ N(0, 0.01)",
             "ms_per_step": round(bwd_ms, 5), "tokens_per_s": round(case.T_total / (bwd_ms * 1e-3), 1),
-            "time_ratio_bwd_over_fwd": round(bwd_ms / wall_ms, 3), "workspace_bytes": ws_bytes}
+            "time_ratio_bwd_over_fwd": round(bwd_ms / wall_ms, 3), "workspace_bytes": ws_bytes,
+            "hbm_bytes_per_launch": {k_: traffic_from_profiles(k_, TH) for k_ in
+                                     ("bwd_fwd_prep", "bwd_fwd_recur", "bwd_prep", "bwd_recur", "bwd_local")}}
 
     if not args.no_decode:
         dec_inputs = min(args.decode_steps, 100)  # distinct per-step inputs, cycled
