@@ -443,6 +443,11 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     R.s0 = d_final_state;
     R.s_final = d_initial_state;
     carve(R, w + off[1], NC, H, dk);
+    // the state-gradient chain reads the forward's factors in swapped roles (K- as
+    // its "-W", (-W)^T as its "K-^T", the same gamma) and walks the chunks in reverse
+    R.wn = F.km;
+    R.km = F.wn;
+    R.gam = F.gam;
     R.pb = reinterpret_cast<const float*>(w + off[2]);
     b.d_o = d_o;
     b.dq = dq;

@@ -10,9 +10,10 @@
 //
 // The state gradient runs backwards over the chunks with the forward chain's
 // shape (two dependent products per chunk), so it reuses the state-recursion
-// kernel on reversed chunk slots, with K- in place of -W, (-W)^T in place of
-// K-^T, A_qk^T dO in place of U and the state-independent term Q+^T dO added
-// each chunk (bwd_prep_kernel computes and lays these out). What stays is
+// kernel, walking each sequence's chunks in reverse, with K- in place of -W
+// and (-W)^T in place of K-^T (read transposed from the forward's own arrays),
+// A_qk^T dO in place of U and the state-independent term Q+^T dO added each
+// chunk (bwd_prep_kernel computes these two). What stays is
 // chunk-local and parallel over chunks (bwd_local_kernel):
 //   * the adjoints of the output and the state update: dQ+ = dO h^T,
 //     dA_qk = tril(dO V^T), dK- = V dh'^T, dgamma = rowsum(h * dh'),
@@ -61,13 +62,6 @@ __device__ __forceinline__ int split_chan(int p) {
     return (p & ~31) + 16 * ((q >> 2) & 1) + 4 * (q >> 3) + (q & 3);
 }
 
-// Chunk slot gc of a sequence -> the slot the reversed recursion uses for it.
-__device__ __forceinline__ int reversed_slot(const int32_t* cu, int T, int seq, int gc) {
-    int co, nch;
-    seq_chunks(cu, T, seq, co, nch);
-    return co + nch - 1 - (gc - co);
-}
-
 __device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -93,15 +87,14 @@ __device__ __forceinline__ float sum16(float x) {  // over the 16 lanes n of a l
 }
 
 // ---------------------------------------------------------------------------
-// Operands of the state-gradient recursion for chunk slot gc, written to its
-// reversed slot: -W := K-, K-^T := (-W)^T, gamma, U := A_qk^T dO (accumulator
-// tiles [dv/16][4][64 lanes][4]) and the added term P = Q+^T dO
-// ([dv/16][dk/16][64 lanes][4]). Wave w owns value columns 16 w .. 16 w + 15.
+// The state-gradient recursion's per-chunk operands for chunk slot gc:
+// U := A_qk^T dO (accumulator tiles [dv/16][4][64 lanes][4]) and the added term
+// P = Q+^T dO ([dv/16][dk/16][64 lanes][4]). Wave w owns value columns
+// 16 w .. 16 w + 15.
 template <int D>
 struct BwdPrepSmem {
     static constexpr int RS = D + 4, SQS = 68;
-    static constexpr int PRODUCTS = 2 * 64 * RS + 64 * SQS, COPIES = D * SQS + 64 * RS;
-    static constexpr int BYTES = (PRODUCTS > COPIES ? PRODUCTS : COPIES) * 4;
+    static constexpr int BYTES = (2 * 64 * RS + 64 * SQS) * 4;
 };
 
 template <int D>
@@ -115,13 +108,10 @@ __global__ __launch_bounds__(4 * D) void bwd_prep_kernel(const int32_t* __restri
     float* dO = sm;                // [64][RS]
     float* Qp = dO + 64 * RS;      // [64][RS], channels in natural order
     float* Aq = Qp + 64 * RS;      // [64][SQS] A_qk
-    float* KmL = sm;               // after the products: K-^T as stored, [D][SQS]
-    float* WnL = sm + D * SQS;     // -W as stored, [64][RS]
     const int gc = blockIdx.x / H, h = blockIdx.x - gc * H;
     ChunkLoc loc;
     if (!locate_chunk(cu, N, T, gc, loc)) return;
-    const int rev = reversed_slot(cu, T, loc.seq, gc);
-    const int64_t src = (int64_t)gc * H + h, dst = (int64_t)rev * H + h;
+    const int64_t src = (int64_t)gc * H + h;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, n = l & 15;
     // every load of the stage first, then the LDS stores
     f32x4_t xo[NQ], xq[NQ], xa[NA];
@@ -147,15 +137,7 @@ __global__ __launch_bounds__(4 * D) void bwd_prep_kernel(const int32_t* __restri
 #pragma unroll
         for (int j = 0; j < 4; ++j) Aq[r * SQS + split_chan(p + j)] = xa[m][j];
     }
-    for (int c = tid; c < D; c += NTH) b.gam[dst * D + c] = f.gam[src * D + c];
     __syncthreads();
-    // the copies' sources, in flight during the products
-    f32x4_t ykm[NQ], ywn[NQ];
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-        ykm[m] = *reinterpret_cast<const f32x4_t*>(f.km + src * D * 64 + 4 * (tid + NTH * m));
-        ywn[m] = *reinterpret_cast<const f32x4_t*>(f.wn + src * 64 * D + 4 * (tid + NTH * m));
-    }
     const int j0 = 16 * w;
     // P[c][j] = sum_r Q+[r][c] dO[r][j]; U[r][j] = sum_{i >= r} A_qk[i][r] dO[i][j]
     f32x4_t accP[NT], accU[4];
@@ -173,42 +155,12 @@ __global__ __launch_bounds__(4 * D) void bwd_prep_kernel(const int32_t* __restri
         for (int R = 0; R < 4; ++R)
             if (R <= (kk >> 2)) accU[R] = mfma4(Aq[r * SQS + 16 * R + n], bo, accU[R]);
     }
-    float* pb = const_cast<float*>(b.pb) + dst * D * D;
+    float* pb = const_cast<float*>(b.pb) + src * D * D;
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) *reinterpret_cast<f32x4_t*>(pb + ((w * NT + ct) * 64 + l) * 4) = accP[ct];
 #pragma unroll
     for (int R = 0; R < 4; ++R)
-        *reinterpret_cast<f32x4_t*>(b.u + dst * 64 * D + ((w * 4 + R) * 64 + l) * 4) = accU[R];
-    __syncthreads();  // the products' operands are dead
-    // K- to the -W layout and (-W)^T to the K-^T layout, both through LDS so that
-    // global reads and writes are whole 16-byte vectors
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-        const int e = tid + NTH * m;
-        const int c = e >> 4, p = 4 * (e & 15);           // K-^T: row c, positions p.. of its 64
-        *reinterpret_cast<f32x4_t*>(KmL + c * SQS + p) = ykm[m];
-        const int r = e / (D / 4), p2 = 4 * (e - r * (D / 4));  // -W: row r, positions p2..
-        *reinterpret_cast<f32x4_t*>(WnL + r * RS + p2) = ywn[m];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-        const int e = tid + NTH * m;
-        {   // -W layout: row r, positions p..p+3 hold channels split_chan(p..p+3) of K-
-            const int r = e / (D / 4), p = 4 * (e - r * (D / 4)), pr = split_pos(r) + 32 * (r >> 5);
-            f32x4_t o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = KmL[split_chan(p + j) * SQS + pr];
-            *reinterpret_cast<f32x4_t*>(b.wn + dst * 64 * D + 4 * e) = o;
-        }
-        {   // K-^T layout: row c, positions p..p+3 hold rows split_chan(p..p+3) of -W
-            const int c = e >> 4, p = 4 * (e & 15), pc = split_pos(c) + 32 * (c >> 5);
-            f32x4_t o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = WnL[split_chan(p + j) * RS + pc];
-            *reinterpret_cast<f32x4_t*>(b.km + dst * D * 64 + 4 * e) = o;
-        }
-    }
+        *reinterpret_cast<f32x4_t*>(b.u + src * 64 * D + ((w * 4 + R) * 64 + l) * 4) = accU[R];
 }
 
 // ---------------------------------------------------------------------------
@@ -264,8 +216,7 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
     ChunkLoc loc;
     if (!locate_chunk(cu, N, T, gc, loc)) return;
     const int t0 = loc.t0, L = loc.L;
-    const int rev = reversed_slot(cu, T, loc.seq, gc);
-    const int64_t fs = (int64_t)gc * H + h, bs = (int64_t)rev * H + h;
+    const int64_t fs = (int64_t)gc * H + h;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, n = l & 15;
     const int c = 16 * w + n;  // own channel
     const float* Pkk = f.am + fs * 64 * 64;     // [64][64] from the forward recompute
@@ -273,8 +224,8 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
     float* SK = SQ + 64 * D;                    // dK-, same layout
     const float* hF = f.h + fs * D * D;
     const float* vF = f.vn + fs * 64 * D;
-    const float* dhB = b.h + bs * D * D;
-    const float* dVB = b.vn + bs * 64 * D;
+    const float* dhB = b.h + fs * D * D;        // gradient of the chunk's exit state
+    const float* dVB = b.vn + fs * 64 * D;      // dV
     auto rowoff = [&](int r) { return ((int64_t)(t0 + r) * H + h) * D; };
     auto own_row = [&](int R, int i) { return 16 * R + 4 * G + i; };
 

@@ -42,7 +42,7 @@ struct ChunkArgs {
 // Backward of kda_chunk_fwd (see kda_bwd.hip).
 struct BwdArgs {
     ChunkArgs fwd;    // forward recompute: fp32 factors, h_n and V_new kept
-    ChunkArgs rec;    // state-gradient recursion over reversed chunk slots
+    ChunkArgs rec;    // state-gradient recursion: chunks in reverse, the forward factors in swapped roles
     const float* d_o;  // [T, H, dv]
     float *dq, *dk, *dv, *dla, *dbeta;
     float* scr;        // per chunk-head scratch, bwd_scr_floats(D) floats each (dQ+, dK-)

@@ -32,6 +32,7 @@
 // that head's W and K- factors.
 #include "kda_common.h"
 #include "kda_launch.h"
+#include "kda_prep_util.h"  // split_pos
 
 #include <type_traits>
 
@@ -107,6 +108,16 @@ __device__ __forceinline__ void wait_vm() {
 
 // wait until this wave's LDS operations have completed
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// Workgroup barrier for an LDS exchange between waves: this wave's LDS writes
+// complete first (s_barrier alone does not wait for them), and the compiler may
+// move no memory access across it (the builtin is not a fence)
+__device__ __forceinline__ void lds_exchange_barrier() {
+    wait_lgkm0();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // wait until only the loads of the `after` chunks issued last are outstanding
 template <int OPS, int RING>
@@ -404,7 +415,8 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
         const int pw = FUSED ? wv - 3 : wv - PL::NCW;
         const int pre = nch < RING - 1 ? nch : RING - 1;
         for (int c = 0; c < pre; ++c)
-            produce<D, F32, FUSED, DPLR>(ws, (int64_t)(co + c) * H + h, ct, pw, l, ring + c * PL::SLOT);
+            produce<D, F32, FUSED, DPLR>(ws, (int64_t)(co + (ADDP ? nch - 1 - c : c)) * H + h, ct, pw, l,
+                                         ring + c * PL::SLOT);
         // chunks 0 .. LOOK have landed once only the chunks issued after them are outstanding
         {
             const int need = nch - 1 < LOOK ? nch - 1 : LOOK;
@@ -416,7 +428,8 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
             // c - 1, which it finished before the barrier that ended that chunk
             const int nx = c + RING - 1;
             if (nx < nch)
-                produce<D, F32, FUSED, DPLR>(ws, (int64_t)(co + nx) * H + h, ct, pw, l, ring + (nx % RING) * PL::SLOT);
+                produce<D, F32, FUSED, DPLR>(ws, (int64_t)(co + (ADDP ? nch - 1 - nx : nx)) * H + h, ct, pw, l,
+                                             ring + (nx % RING) * PL::SLOT);
             if constexpr (!FUSED) __builtin_amdgcn_s_barrier();  // the compute waves' V_new exchange
             // chunk c + 1 + LOOK has landed once only the chunks issued after it are outstanding
             const int last = nch - 1 < nx ? nch - 1 : nx;
@@ -447,7 +460,7 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
         f32x4_t pc[ADDP ? TH : 1], pnx[ADDP ? TH : 1];
         auto load_p = [&](int c, f32x4_t (&dst)[ADDP ? TH : 1]) {
             if constexpr (ADDP) {
-                const float* pp = ws.pb + ((int64_t)(co + c) * H + h) * D * D + (int64_t)ct * NT * 64 * 4;
+                const float* pp = ws.pb + ((int64_t)(co + nch - 1 - c) * H + h) * D * D + (int64_t)ct * NT * 64 * 4;
 #pragma unroll
                 for (int tt = 0; tt < TH; ++tt)
                     dst[tt] = *reinterpret_cast<const f32x4_t*>(pp + ((TH * q + tt) * 64 + l) * 4);
@@ -457,16 +470,37 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
 #pragma unroll
             for (int tt = 0; tt < TH; ++tt) XS[(TH * q + tt) * 64 + l] = S[tt];
         };
+        // ADDP (the backward's chain) runs on the forward's own factor arrays with
+        // their roles swapped: the slot's "-W" part holds K-^T as the forward stored
+        // it ([dk][64], rows split-ordered) and its "K-^T" part holds -W ([64][dk],
+        // channels split-ordered), so the operand fragments are read transposed,
+        // one element at a time
+        auto w_transposed = [&](const char* sl, int s) {  // K- rows 16q + n, channels of slice s
+            const float* kt = reinterpret_cast<const float*>(sl);
+            const int r = 16 * q + n, pr = 32 * (r >> 5) + split_pos(r);
+            Frag f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) f.v[j] = kt[(32 * s + kslot(g, j)) * 64 + pr];
+            return f;
+        };
+        auto k_transposed = [&](const char* sl, int t, int s) {  // (-W)^T rows 16t + n, chunk rows of slice s
+            const float* wn = reinterpret_cast<const float*>(sl);
+            const int c = 16 * t + n, pc = 32 * (c >> 5) + split_pos(c);
+            Frag f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) f.v[j] = wn[(32 * s + kslot(g, j)) * D + pc];
+            return f;
+        };
         put_s();
         if (nch > 0) load_p(0, pc);
-        __builtin_amdgcn_s_barrier();
+        lds_exchange_barrier();
         for (int c = 0; c < nch; ++c) {
             const char* slot = ring + (c % RING) * PL::SLOT;
             const char* wsl = slot;
             const char* ksl = slot + PL::FB;
             const E* usl = reinterpret_cast<const E*>(slot + 2 * PL::FB);
             const float* gsl = reinterpret_cast<const float*>(slot + 2 * PL::FB + PL::UB);
-            const int64_t chh = (int64_t)(co + c) * H + h;
+            const int64_t chh = (int64_t)(co + (ADDP ? nch - 1 - c : c)) * H + h;
             if (ADDP && c + 1 < nch) load_p(c + 1, pnx);
             // the whole state as B fragments; this wave's share of h_n out
             Frag sb[NS];
@@ -481,7 +515,8 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const int gr = ((16 * q + n) * NS + s) * 4 + g;
-                P::mma(V, P::load(reinterpret_cast<const E*>(wsl + gr * 8 * sizeof(E))), sb[s]);
+                P::mma(V, ADDP ? w_transposed(wsl, s) : P::load(reinterpret_cast<const E*>(wsl + gr * 8 * sizeof(E))),
+                       sb[s]);
             }
             XV[q * 64 + l] = V;
             // this wave's K-^T fragments and gamma while the other tiles land
@@ -491,12 +526,13 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
 #pragma unroll
                 for (int tt = 0; tt < TH; ++tt) {
                     const int gr = ((16 * (TH * q + tt) + n) * 2 + s) * 4 + g;
-                    kf[tt][s] = P::load(reinterpret_cast<const E*>(ksl + gr * 8 * sizeof(E)));
+                    kf[tt][s] = ADDP ? k_transposed(ksl, TH * q + tt, s)
+                                     : P::load(reinterpret_cast<const E*>(ksl + gr * 8 * sizeof(E)));
                 }
             f32x4_t gm[TH];
 #pragma unroll
             for (int tt = 0; tt < TH; ++tt) gm[tt] = *reinterpret_cast<const f32x4_t*>(gsl + 16 * (TH * q + tt) + 4 * g);
-            __builtin_amdgcn_s_barrier();  // every V_new tile in LDS
+            lds_exchange_barrier();  // every V_new tile in LDS
             Frag vb[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) vb[s] = frag_from_acc<F32>(XV[(2 * s) * 64 + l], XV[(2 * s + 1) * 64 + l]);
@@ -520,7 +556,7 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
 #pragma unroll
                 for (int tt = 0; tt < TH; ++tt) pc[tt] = pnx[tt];
             }
-            __builtin_amdgcn_s_barrier();  // end of chunk: slot free, state tiles in LDS
+            lds_exchange_barrier();  // end of chunk: slot free, state tiles in LDS
         }
         if (s_final) {
 #pragma unroll
