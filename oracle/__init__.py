@@ -18,6 +18,10 @@ Contents
   diagonal-plus-low-rank transition S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1}
   + k_t v_t^T that KDA specialises (the comparison operator).
 * ``build``       -- compiles ``kda_oracle.c`` with the host C compiler.
+* ``backward``    -- (module) the gradients: fp64 autograd through the recurrence.
+* ``layer``       -- (module) the layer's prologue (short convolution, Swish,
+  L2 norm, decay and beta gates) and epilogue (RMSNorm, output gate) around
+  the operator, pinned by ``tests/test_layer_cpu.py``.
 
 Pinned by ``tests/test_oracle_pins.py`` (exact retrieval, beta = 0 closed form,
 DeltaNet and Gated DeltaNet reductions, dense-transition brute force,
