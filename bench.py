@@ -9,11 +9,12 @@ of the hot path) is timed in the same run on ``decode-256`` (256 sequences x 32
 heads, fp32 states of 512 MiB, updated in place) and reported in the same JSON
 line. Prints ONE JSON line. The general-DPLR comparison operator (the transition KDA specialises,
 with free low-rank vectors a, b) is timed on the same workload and reported
-beside it under "dplr_comparison", and the chunkwise backward (gradients of
-q, k, v, log_alpha, beta and the initial state) under "backward".
+beside it under "dplr_comparison", the chunkwise backward (gradients of
+q, k, v, log_alpha, beta and the initial state) under "backward", and the layer
+around the operator (prologue, operator, epilogue) under "layer".
 
     python bench.py [--steps K] [--warmup W] [--decode-steps S] [--no-cpu-baseline] [--no-dplr]
-                    [--no-bwd]
+                    [--no-bwd] [--no-layer]
 
 Profiling helpers (used to write the summaries under profiles/):
     python bench.py --copy-calibration MIB        # counter calibration kernel only
@@ -243,6 +244,76 @@ def time_bwd(kda, case, steps, warmup):
     return e0.elapsed_time(e1) / steps, g_, ws.numel()
 
 
+def time_layer(kda, lc, steps, warmup, hip, stream):
+    """The layer path around the operator on one workload: prologue, the
+    operator, epilogue. Outputs and the operator's workspace are allocated once;
+    the three calls go straight through the C ABI (so no host work sits between
+    the launches) and HIP events on the launch stream bracket each part. Returns ms per prologue, operator call, epilogue and whole layer."""
+    import torch
+    lib = kda._load()
+    T, H, d = lc.xq.shape
+    dev = lc.xq.device
+    q, k, v, la = (torch.empty(T, H, d, dtype=lc.xq.dtype, device=dev) for _ in range(4))
+    beta = torch.empty(T, H, dtype=lc.xq.dtype, device=dev)
+    o = torch.empty(T, H, d, dtype=torch.float32, device=dev)
+    N = 1 if lc.cu_seqlens is None else lc.cu_seqlens.numel() - 1
+    fs = torch.empty(N, H, d, d, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_size(N, T, H, d, d, q.dtype), dtype=torch.uint8, device=dev)
+    y = torch.empty(T, H, d, dtype=lc.xg.dtype, device=dev)
+    P = ctypes.c_void_p
+
+    def ptr(t):
+        return None if t is None else P(t.data_ptr())
+    dtc = kda.KDA_BF16 if lc.xq.dtype == torch.bfloat16 else kda.KDA_F32
+    pro_args = (*(ptr(t) for t in (lc.xq, lc.xk, lc.xv, lc.xa, lc.xb, lc.wq, lc.wk, lc.wv, lc.A_log,
+                                   lc.dt_bias, lc.cu_seqlens)),
+                N, T, H, d, dtc, *(ptr(t) for t in (q, k, v, la, beta)), P(stream))
+    epi_args = (ptr(o), ptr(lc.xg), ptr(lc.rms_w), T, H, d, dtc, ptr(y), P(stream))
+    op_args = (*(ptr(t) for t in (q, k, v, la, beta, lc.initial_state, lc.cu_seqlens)), N, T, H, d, d, dtc, dtc,
+               kda.KDA_F32, ptr(o), ptr(fs), ptr(ws), ws.numel(), P(stream))
+
+    def step(ev=None, b=0):
+        if ev is not None:
+            ev.record(b, stream)
+        if lib.kda_layer_prologue(*pro_args) != 0:
+            raise RuntimeError("kda_layer_prologue failed")
+        if ev is not None:
+            ev.record(b + 1, stream)
+        if lib.kda_chunk_fwd(*op_args) != 0:
+            raise RuntimeError("kda_chunk_fwd failed")
+        if ev is not None:
+            ev.record(b + 2, stream)
+        if lib.kda_layer_epilogue(*epi_args) != 0:
+            raise RuntimeError("kda_layer_epilogue failed")
+        if ev is not None:
+            ev.record(b + 3, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # the whole layer back to back, events only around the loop
+    ev = Events(hip, 2)
+    ev.record(0, stream)
+    for _ in range(steps):
+        step()
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    out = {"layer": ev.ms(0, 1) / steps, "prologue": 0.0, "operator": 0.0, "epilogue": 0.0}
+    ev.close()
+    # the parts, each bracketed by its own events (which add a little idle time)
+    ev = Events(hip, 4 * steps)
+    for s_ in range(steps):
+        step(ev, 4 * s_)
+    torch.cuda.synchronize()
+    for s_ in range(steps):
+        b = 4 * s_
+        out["prologue"] += ev.ms(b, b + 1) / steps
+        out["operator"] += ev.ms(b + 1, b + 2) / steps
+        out["epilogue"] += ev.ms(b + 2, b + 3) / steps
+    ev.close()
+    return out
+
+
 def time_decode(kda, dec, steps, warmup, hip, stream):
     import torch
     state = dec["state"]
@@ -406,6 +477,7 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dplr", action="store_true", help="skip the general-DPLR comparison")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward")
+    ap.add_argument("--no-layer", action="store_true", help="skip the layer prologue/epilogue")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run the counter calibration copy kernel over MIB MiB")
     args = ap.parse_args(argv)
@@ -487,6 +559,25 @@ def main(argv=None):
             "time_ratio_bwd_over_fwd": round(bwd_ms / wall_ms, 3), "workspace_bytes": ws_bytes,
             "hbm_bytes_per_launch": {k_: traffic_from_profiles(k_, TH) for k_ in
                                      ("bwd_fwd_prep", "bwd_fwd_recur", "bwd_prep", "bwd_recur", "bwd_local")}}
+
+    if not args.no_layer:
+        lc = ki.make_layer("prefill-4k", dev)
+        lt = time_layer(kda, lc, max(10, args.steps // 5), max(3, min(50, args.warmup)), hip, stream)
+        # compulsory bytes per token-head: prologue reads xq, xk, xv, xa (bf16, 4 x 256) and
+        # xb (2), writes q, k, v, log_alpha (4 x 256) and beta (2); epilogue reads o (fp32 512)
+        # and xg (256), writes y (256)
+        pro_b, epi_b = 2052 * TH, 1024 * TH
+        out["layer"] = {
+            "workload": "prefill-4k pre-activations (bf16)",
+            "ms": {k_: round(v_, 5) for k_, v_ in lt.items()},
+            "tokens_per_s": round(case.T_total / (lt["layer"] * 1e-3), 1),
+            "prologue_roofline": {"bound": "hbm", "achieved": round(pro_b / (lt["prologue"] * 1e-3) / 1e9, 1),
+                                  "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                                  "frac": round(pro_b / (lt["prologue"] * 1e-3) / PEAK_HBM, 4)},
+            "epilogue_roofline": {"bound": "hbm", "achieved": round(epi_b / (lt["epilogue"] * 1e-3) / 1e9, 1),
+                                  "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                                  "frac": round(epi_b / (lt["epilogue"] * 1e-3) / PEAK_HBM, 4)}}
+        del lc
 
     if not args.no_decode:
         dec_inputs = min(args.decode_steps, 100)  # distinct per-step inputs, cycled

@@ -76,6 +76,11 @@ def _load():
     lib.kda_chunk_bwd.restype = ctypes.c_int
     lib.kda_chunk_bwd.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int, ctypes.c_int,
                                   P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.kda_layer_prologue.restype = ctypes.c_int
+    lib.kda_layer_prologue.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I32, I64, I32, I32, ctypes.c_int,
+                                       P, P, P, P, P, P]
+    lib.kda_layer_epilogue.restype = ctypes.c_int
+    lib.kda_layer_epilogue.argtypes = [P, P, P, I64, I32, I32, ctypes.c_int, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
@@ -227,6 +232,63 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: to
     if st != 0:
         raise KDAError(st, "kda_decode_step")
     return o
+
+
+def layer_prologue(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, xa: torch.Tensor, xb: torch.Tensor,
+                   wq: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor, A_log: torch.Tensor,
+                   dt_bias: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None):
+    """The layer's prologue (see ``kda_layer_prologue``): pre-activations xq, xk,
+    xv, xa [T, H, d] and xb [T, H] (all bf16 or all fp32), filters wq, wk, wv
+    [H, d, 4], A_log [H], dt_bias [H, d] (fp32). Returns (q, k, v, log_alpha,
+    beta) in the pre-activations' dtype, ready for ``chunk_fwd``."""
+    lib = _load()
+    dev = xq.device
+    if xq.dim() != 3:
+        raise ValueError("xq must be [T, H, d]")
+    T, H, d = xq.shape
+    N = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    items = [("xq", xq, (T, H, d)), ("xk", xk, (T, H, d)), ("xv", xv, (T, H, d)), ("xa", xa, (T, H, d)),
+             ("xb", xb, (T, H)), ("wq", wq, (H, d, 4)), ("wk", wk, (H, d, 4)), ("wv", wv, (H, d, 4)),
+             ("A_log", A_log, (H,)), ("dt_bias", dt_bias, (H, d))]
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 >= 2 offsets")
+        items.append(("cu_seqlens", cu_seqlens, None))
+    _check(items, dev)
+    for name, t in (("xk", xk), ("xv", xv), ("xa", xa), ("xb", xb)):
+        if t.dtype != xq.dtype:
+            raise TypeError(f"{name} must have xq's dtype")
+    for name, t in (("wq", wq), ("wk", wk), ("wv", wv), ("A_log", A_log), ("dt_bias", dt_bias)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    outs = [torch.empty(T, H, d, dtype=xq.dtype, device=dev) for _ in range(4)]
+    beta = torch.empty(T, H, dtype=xq.dtype, device=dev)
+    st = lib.kda_layer_prologue(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(xa), _ptr(xb), _ptr(wq), _ptr(wk), _ptr(wv),
+                                _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), N, T, H, d, _dtype_code(xq, "xq"),
+                                *(_ptr(t) for t in outs), _ptr(beta), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_layer_prologue")
+    return outs[0], outs[1], outs[2], outs[3], beta
+
+
+def layer_epilogue(o: torch.Tensor, xg: torch.Tensor, rms_w: torch.Tensor) -> torch.Tensor:
+    """The layer's epilogue (see ``kda_layer_epilogue``): o [T, H, dv] fp32, the
+    output gate's pre-activation xg [T, H, dv] (bf16 or fp32), rms_w [dv] fp32.
+    Returns y [T, H, dv] in xg's dtype."""
+    lib = _load()
+    dev = o.device
+    if o.dim() != 3:
+        raise ValueError("o must be [T, H, dv]")
+    T, H, dv = o.shape
+    _check([("o", o, (T, H, dv)), ("xg", xg, (T, H, dv)), ("rms_w", rms_w, (dv,))], dev)
+    if o.dtype != torch.float32 or rms_w.dtype != torch.float32:
+        raise TypeError("o and rms_w must be float32")
+    y = torch.empty(T, H, dv, dtype=xg.dtype, device=dev)
+    st = lib.kda_layer_epilogue(_ptr(o), _ptr(xg), _ptr(rms_w), T, H, dv, _dtype_code(xg, "xg"), _ptr(y),
+                                _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_layer_epilogue")
+    return y
 
 
 def dplr_workspace_size(N: int, T_total: int, H: int, dk: int, dv: int) -> int:

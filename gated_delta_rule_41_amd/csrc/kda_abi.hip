@@ -465,6 +465,70 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     return KDA_OK;
 }
 
+kda_status kda_layer_prologue(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
+                              const float* wq, const float* wk, const float* wv, const float* A_log,
+                              const float* dt_bias, const int32_t* cu_seqlens, int32_t N, int64_t T_total,
+                              int32_t H, int32_t d, kda_dtype dtype, void* q, void* k, void* v, void* log_alpha,
+                              void* beta, void* stream) {
+    if (!chunk_sizes_ok(N, T_total, H) || T_total * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    if (!cu_seqlens && N != 1) return KDA_ERR_SHAPE;
+    if (!head_ok(d, d) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+    if (T_total > 0 && (!xq || !xk || !xv || !xa || !xb || !wq || !wk || !wv || !A_log || !dt_bias || !q || !k ||
+                        !v || !log_alpha || !beta))
+        return KDA_ERR_NULL;
+    const size_t es = esize(dtype), T = (size_t)T_total;
+    const size_t nx = T * H * d * es, nb = T * H * es, nw = (size_t)H * d * 4 * 4, nh = (size_t)H * 4,
+                 nd = (size_t)H * d * 4, ncu = cu_seqlens ? (size_t)(N + 1) * 4 : 0;
+    const void* ins[11] = {xq, xk, xv, xa, xb, wq, wk, wv, A_log, dt_bias, cu_seqlens};
+    const size_t nin[11] = {nx, nx, nx, nx, nb, nw, nw, nw, nh, nd, ncu};
+    void* outs[5] = {q, k, v, log_alpha, beta};
+    const size_t nout[5] = {nx, nx, nx, nx, nb};
+    // [T, H, d] tensors move in channel pairs: 2 * es bytes
+    for (int i = 0; i < 11; ++i)
+        if (!aligned_to(ins[i], i < 4 ? 2 * es : i == 4 ? es : 4)) return KDA_ERR_ALIGN;
+    for (int i = 0; i < 5; ++i) {
+        if (!aligned_to(outs[i], i < 4 ? 2 * es : es)) return KDA_ERR_ALIGN;
+        for (int j = 0; j < 11; ++j)
+            if (overlaps(outs[i], nout[i], ins[j], nin[j])) return KDA_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], nout[i], outs[j], nout[j])) return KDA_ERR_ALIAS;
+    }
+    if (T_total == 0) return KDA_OK;
+    LayerArgs a{};
+    a.N = N;
+    a.T = (int)T_total;
+    a.H = H;
+    a.D = d;
+    a.f32 = dtype == KDA_F32;
+    a.cu = cu_seqlens;
+    a.xq = xq, a.xk = xk, a.xv = xv, a.xa = xa, a.xb = xb;
+    a.wq = wq, a.wk = wk, a.wv = wv, a.A_log = A_log, a.dt_bias = dt_bias;
+    a.q = q, a.k = k, a.v = v, a.la = log_alpha, a.beta = beta;
+    return launch_layer_prologue(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_layer_epilogue(const float* o, const void* g, const float* rms_w, int64_t T_total, int32_t H,
+                              int32_t dv, kda_dtype dtype, void* y, void* stream) {
+    if (T_total < 0 || T_total >= (int64_t(1) << 31) || H <= 0 || H > 65536 || T_total * H >= (int64_t(1) << 31))
+        return KDA_ERR_SHAPE;
+    if (!(dv == 64 || dv == 128) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+    if (T_total > 0 && (!o || !g || !rms_w || !y)) return KDA_ERR_NULL;
+    const size_t es = esize(dtype), n = (size_t)T_total * H * dv;
+    // rows move in channel pairs
+    if (!aligned_to(o, 8) || !aligned_to(g, 2 * es) || !aligned_to(rms_w, 4) || !aligned_to(y, 2 * es))
+        return KDA_ERR_ALIGN;
+    if (overlaps(y, n * es, o, n * 4) || overlaps(y, n * es, g, n * es) || overlaps(y, n * es, rms_w, (size_t)dv * 4))
+        return KDA_ERR_ALIAS;
+    if (T_total == 0) return KDA_OK;
+    LayerArgs a{};
+    a.T = (int)T_total;
+    a.H = H;
+    a.D = dv;
+    a.f32 = dtype == KDA_F32;
+    a.o = o, a.g = g, a.rms_w = rms_w, a.y = y;
+    return launch_layer_epilogue(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
                            float* state, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype,
                            kda_dtype gate_dtype, kda_dtype out_dtype, void* o, void* stream) {

@@ -52,6 +52,24 @@ __host__ __device__ inline int64_t bwd_scr_floats(int D) { return 2LL * 64 * D; 
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_local(const BwdArgs& a, hipStream_t st);
 
+// The layer's prologue and epilogue around the operator (see kda_layer.hip).
+struct LayerArgs {
+    int N, T, H, D;
+    bool f32;  // element type of every pre-activation and output: fp32, else bf16
+    const int32_t* cu;
+    // prologue
+    const void *xq, *xk, *xv, *xa, *xb;
+    const float *wq, *wk, *wv, *A_log, *dt_bias;
+    void *q, *k, *v, *la, *beta;
+    // epilogue
+    const float* o;
+    const void* g;
+    const float* rms_w;
+    void* y;
+};
+hipError_t launch_layer_prologue(const LayerArgs& a, hipStream_t st);
+hipError_t launch_layer_epilogue(const LayerArgs& a, hipStream_t st);
+
 // Workspace carve-up shared by the size query and the launcher.
 struct WsPlan {
     size_t off[8];   // qp, km, wn, u, aqk, gam, h, vn

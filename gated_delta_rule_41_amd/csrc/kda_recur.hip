@@ -568,7 +568,7 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
         return;
     }
 
-    // ---------------- compute wave
+    // ---------------- compute wave (the fused chain; the unfused one returned above)
     f32x4_t S[NT];  // state slab: rows 16t + 4g + i, column 16 ct + n
     const int64_t sbase = (int64_t)unit * D * D + 16 * ct + n;
 #pragma unroll
@@ -576,17 +576,6 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[t][i] = s0 ? s0[sbase + (int64_t)(16 * t + 4 * g + i) * D] : 0.f;
 
-    // ADDP (the backward's state-gradient recursion): a state-independent term
-    // per chunk, loaded one chunk ahead into registers
-    f32x4_t pn[ADDP ? NT : 1];
-    auto load_p = [&](int c) {
-        if constexpr (ADDP) {
-            const float* pp = ws.pb + ((int64_t)(co + c) * H + h) * D * D + (int64_t)ct * NT * 64 * 4;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) pn[t] = *reinterpret_cast<const f32x4_t*>(pp + (t * 64 + l) * 4);
-        }
-    };
-    if (nch > 0) load_p(0);
     Frag wf[4][NS];  // -W fragments (with LOOK, of the chunk after the current one once read)
     auto load_w = [&](int c) {
         const char* wsl = ring + (c % RING) * PL::SLOT;
@@ -669,12 +658,9 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
             if constexpr (DPLR)
                 S[t] = gm[t] * S[t] + f32x4_t{h2f(kv[t][0] & 0xffffu), h2f(kv[t][0] >> 16), h2f(kv[t][1] & 0xffffu),
                                               h2f(kv[t][1] >> 16)};
-            else if constexpr (ADDP)
-                S[t] = gm[t] * S[t] + pn[t];
             else
                 S[t] = gm[t] * S[t];
         }
-        if (ADDP && c + 1 < nch) load_p(c + 1);
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll

@@ -191,6 +191,53 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
                          size_t workspace_bytes, void* stream);
 
 /*
+ * The layer's prologue: from the pre-activations (the outputs of a KDA layer's
+ * q, k, v, gate and beta projections) to kda_chunk_fwd's inputs (GeekNews
+ * "Kimi Linear" summary, section "Configuração do modelo Kimi Linear": short
+ * convolution and Swish on q, k, v; L2 normalisation of q and k; a per-channel
+ * decay gate through a GDN/Mamba-like decay function):
+ *
+ *   q = L2(swish(conv(xq))), k = L2(swish(conv(xk))), v = swish(conv(xv)),
+ *   log_alpha = -exp(A_log[h]) * softplus(xa + dt_bias[h, c]),  beta = sigmoid(xb)
+ *
+ * conv: causal depthwise filter of width 4, y[t] = sum_i w[h, c, i] x[t - 3 + i],
+ * with x = 0 before the first token of t's sequence (per cu_seqlens);
+ * swish(x) = x sigmoid(x); L2(x) = x / sqrt(sum_c x^2 + 1e-6).
+ *
+ *   xq, xk, xv, xa  [T_total, H, d] dtype;  xb [T_total, H] dtype
+ *   wq, wk, wv      [H, d, 4] fp32;  A_log [H] fp32;  dt_bias [H, d] fp32
+ *   cu_seqlens      as kda_chunk_fwd (NULL = one sequence, N = 1)
+ *   q, k, v, log_alpha [T_total, H, d] dtype;  beta [T_total, H] dtype (outputs,
+ *                   ready to pass to kda_chunk_fwd with in_dtype = gate_dtype = dtype)
+ * d must be 64 or 128; dtype KDA_BF16 or KDA_F32 (fp32 arithmetic, outputs
+ * rounded to nearest even for bf16). The [T_total, H, d] tensors must be aligned
+ * to two elements, the others to one (KDA_ERR_ALIGN). No output may overlap an
+ * input or another output (KDA_ERR_ALIAS). T_total * H < 2^31. One kernel is
+ * enqueued: one wave per head and tile of 16 tokens, the filters in registers.
+ */
+kda_status kda_layer_prologue(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
+                              const float* wq, const float* wk, const float* wv, const float* A_log,
+                              const float* dt_bias, const int32_t* cu_seqlens, int32_t N, int64_t T_total,
+                              int32_t H, int32_t d, kda_dtype dtype, void* q, void* k, void* v,
+                              void* log_alpha, void* beta, void* stream);
+
+/*
+ * The layer's epilogue (same section: a per-head RMSNorm and a data-dependent
+ * output gate before the output projection):
+ *
+ *   y = o / sqrt(mean_c o^2 + 1e-6) * rms_w[c] * sigmoid(xg)
+ *
+ *   o      [T_total, H, dv] fp32 (kda_chunk_fwd's output)
+ *   xg     [T_total, H, dv] dtype (the output gate's pre-activation)
+ *   rms_w  [dv] fp32 (one weight per value channel, shared by the heads)
+ *   y      [T_total, H, dv] dtype (output; must not overlap an input)
+ * dv must be 64 or 128. o, xg and y must be aligned to two elements, rms_w to
+ * one (KDA_ERR_ALIGN). One kernel is enqueued: one wave per four rows.
+ */
+kda_status kda_layer_epilogue(const float* o, const void* xg, const float* rms_w, int64_t T_total, int32_t H,
+                              int32_t dv, kda_dtype dtype, void* y, void* stream);
+
+/*
  * Bytes of device workspace kda_dplr_chunk_fwd needs (host call, no device
  * access): seven 16-bit per-chunk factors and the chunk decay, for at most
  * floor((T_total + 63*N) / 64) chunks per head. in_dtype must be KDA_BF16.

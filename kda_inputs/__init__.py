@@ -31,6 +31,14 @@ the workload's sigmoid draw). Then Diag(alpha) - a b^T is symmetric with
 eigenvalues in [-beta, 1], so the state stays bounded over any length while
 a and b share nothing with the written key k.
 
+Layer inputs (``make_layer``): the pre-activations of a KDA layer's
+projections for the prologue/epilogue path, drawn N(0,1) in fp32 and rounded
+to the workload's dtype: xq, xk, xv, xa [T, H, d], xb [T, H], xg [T, H, dv];
+short-convolution filters N(0, 0.5) [H, d, 4] (fp32); A_log = 0 and dt_bias =
+the workload's gate shift, so that the decay gate the prologue forms,
+-softplus(xa + shift), has the workload's distribution; RMSNorm weights
+1 + N(0, 0.1) [dv]. (N(0, s): standard deviation s.)
+
 Random numbers come from torch generators seeded from (workload, tensor,
 window); on a GPU device the draws happen on that device (Philox), so the same
 seed gives the same tensors on every run of the same software stack.
@@ -245,3 +253,71 @@ def make_dplr(workload: str = "prefill-4k", device="cpu", **kw) -> DplrCase:
         a[sl] = (base.beta[sl].float()[..., None] * ah).to(a.dtype)
         b[sl] = ah.to(b.dtype)
     return DplrCase(**{f.name: getattr(base, f.name) for f in dataclasses.fields(PrefillCase)}, a=a, b=b)
+
+
+@dataclasses.dataclass
+class LayerCase:
+    name: str
+    xq: torch.Tensor
+    xk: torch.Tensor
+    xv: torch.Tensor
+    xa: torch.Tensor
+    xb: torch.Tensor
+    xg: torch.Tensor
+    wq: torch.Tensor
+    wk: torch.Tensor
+    wv: torch.Tensor
+    A_log: torch.Tensor
+    dt_bias: torch.Tensor
+    rms_w: torch.Tensor
+    initial_state: Optional[torch.Tensor]
+    cu_seqlens: Optional[torch.Tensor]
+    lengths: List[int]
+
+    @property
+    def T_total(self) -> int:
+        return self.xq.shape[0]
+
+    @property
+    def H(self) -> int:
+        return self.xq.shape[1]
+
+    @property
+    def N(self) -> int:
+        return len(self.lengths)
+
+
+def make_layer(workload: str = "prefill-4k", device="cpu", *, lengths: Optional[Sequence[int]] = None,
+               H: Optional[int] = None, d: Optional[int] = None, dtype: Optional[torch.dtype] = None,
+               s0_std: Optional[float] = None, seed: int = 0, packed: Optional[bool] = None) -> LayerCase:
+    """Pre-activations of the named workload's shape for the layer path (see the
+    module docstring); overrides as in ``make_prefill``."""
+    wl = WORKLOADS[workload]
+    H = wl.H if H is None else H
+    d = wl.dk if d is None else d
+    dtype = wl.dtype if dtype is None else dtype
+    s0_std = wl.s0_std if s0_std is None else s0_std
+    if lengths is None:
+        lengths = list(wl.lengths) if wl.lengths is not None else varlen_lengths(wl.n_seqs, seed=seed)
+    lengths = [int(x) for x in lengths]
+    T = sum(lengths)
+    parts = ("layer", workload, seed, H, d, str(dtype), tuple(lengths) if len(lengths) <= 64 else len(lengths))
+    x = {nm: _normal((T, H, d), device, *parts, nm).to(dtype) for nm in ("xq", "xk", "xv", "xa", "xg")}
+    xb = _normal((T, H), device, *parts, "xb").to(dtype)
+    w = {nm: _normal((H, d, 4), device, *parts, nm) * 0.5 for nm in ("wq", "wk", "wv")}
+    A_log = torch.zeros(H, dtype=torch.float32, device=device)
+    dt_bias = torch.full((H, d), float(wl.gate_shift), dtype=torch.float32, device=device)
+    rms_w = 1.0 + 0.1 * _normal((d,), device, *parts, "rms_w")
+    s0 = _normal((len(lengths), H, d, d), device, *parts, "s0") * s0_std if s0_std > 0 else None
+    if packed is None:
+        packed = len(lengths) > 1
+    cu = None
+    if packed:
+        cu_list = [0]
+        for L in lengths:
+            cu_list.append(cu_list[-1] + L)
+        cu = torch.tensor(cu_list, dtype=torch.int32, device=device)
+    elif len(lengths) != 1:
+        raise ValueError("more than one sequence needs cu_seqlens")
+    return LayerCase(workload, x["xq"], x["xk"], x["xv"], x["xa"], xb, x["xg"], w["wq"], w["wk"], w["wv"],
+                     A_log, dt_bias, rms_w, s0, cu, lengths)

@@ -31,7 +31,8 @@ def test_library_exports_every_declared_function():
     assert names == ["kda_abi_version", "kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd",
                      "kda_chunk_fwd_timed",
                      "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_dplr_chunk_fwd",
-                     "kda_dplr_chunk_fwd_workspace_size", "kda_status_str"]
+                     "kda_dplr_chunk_fwd_workspace_size", "kda_layer_epilogue", "kda_layer_prologue",
+                     "kda_status_str"]
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -238,6 +239,54 @@ def test_bwd_validation():
     assert bwd_call(ws=w, do=w + need // 2) == ALIAS
 
 
+def prologue_call(**over):
+    f = Fake()
+    a = dict(xq=f(), xk=f(), xv=f(), xa=f(), xb=f(), wq=f(), wk=f(), wv=f(), A_log=f(), dtb=f(), cu=None, N=1,
+             T=100, H=2, d=64, dt=BF16, q=f(), k=f(), v=f(), la=f(), beta=f(), stream=None)
+    a.update(over)
+    P = ctypes.c_void_p
+    return kda._load().kda_layer_prologue(*(P(a[x]) for x in ("xq", "xk", "xv", "xa", "xb", "wq", "wk", "wv",
+                                                              "A_log", "dtb", "cu")),
+                                          a["N"], a["T"], a["H"], a["d"], a["dt"],
+                                          *(P(a[x]) for x in ("q", "k", "v", "la", "beta", "stream")))
+
+
+def epilogue_call(**over):
+    f = Fake()
+    a = dict(o=f(), g=f(), w=f(), T=100, H=2, dv=128, dt=BF16, y=f(), stream=None)
+    a.update(over)
+    P = ctypes.c_void_p
+    return kda._load().kda_layer_epilogue(P(a["o"]), P(a["g"]), P(a["w"]), a["T"], a["H"], a["dv"], a["dt"],
+                                          P(a["y"]), P(a["stream"]))
+
+
+def test_layer_validation():
+    assert prologue_call(xq=None) == NULL
+    assert prologue_call(beta=None) == NULL
+    assert prologue_call(N=2) == SHAPE
+    assert prologue_call(T=1 << 31) == SHAPE
+    assert prologue_call(T=1 << 30, H=4) == SHAPE  # T * H >= 2^31
+    assert prologue_call(d=96) == UNSUP
+    assert prologue_call(dt=3) == UNSUP
+    f = Fake()
+    assert prologue_call(wq=f(2)) == ALIGN
+    assert prologue_call(q=f(1)) == ALIGN
+    assert prologue_call(xk=f(2)) == ALIGN  # bf16 channel pairs move as 4 bytes
+    assert prologue_call(T=0, xb=f(2), beta=f(2)) == OK  # [T, H] tensors: one element (no launch at T = 0)
+    x = f()
+    assert prologue_call(xq=x, q=x + 64) == ALIAS
+    y = f()
+    assert prologue_call(q=y, k=y + 128) == ALIAS
+    assert prologue_call(T=0, xq=None, q=None) == OK  # nothing to do
+    assert epilogue_call(o=None) == NULL
+    assert epilogue_call(dv=96) == UNSUP
+    assert epilogue_call(T=-1) == SHAPE
+    assert epilogue_call(y=f(1)) == ALIGN
+    assert epilogue_call(o=f(4)) == ALIGN  # fp32 channel pairs move as 8 bytes
+    o = f()
+    assert epilogue_call(o=o, y=o + 4) == ALIAS
+
+
 @pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="would launch on fake pointers")
 def test_valid_arguments_reach_the_launch_without_gpu():
     """With no GPU present, valid arguments pass validation and the launch
@@ -246,3 +295,5 @@ def test_valid_arguments_reach_the_launch_without_gpu():
     assert chunk_call() == HIP
     assert dplr_call() == HIP
     assert bwd_call() == HIP
+    assert prologue_call() == HIP
+    assert epilogue_call() == HIP

@@ -1,0 +1,138 @@
+"""GPU parity of the layer prologue and epilogue (kda_layer_prologue,
+kda_layer_epilogue, through the C ABI) against the fp64 layer oracle
+(oracle/layer.py, pinned in tests/test_layer_cpu.py), and of the whole layer
+between the projections: prologue -> kda_chunk_fwd -> epilogue.
+
+Bars:
+* fp32 outputs: max-abs error relative to the RMS within 1e-5 (fp32 arithmetic
+  against fp64);
+* bf16 outputs: every element within one bf16 step (the spacing at the fp64
+  value, plus 1e-5 rms(ref)) of the fp64 value (the GPU rounds its fp32 result,
+  which can fall on the other side of a rounding boundary than the fp64 value);
+* the operator inside the layer: its own bf16 bar, 2e-2, scaled by how much
+  heavier the tail of its value input is than in the prefill-4k workload the
+  bar was set on (max|v| / rms(v) = 5.4 there): the fp16 value-path
+  intermediates round each element relative to its own size, so the max-abs
+  error grows with that ratio;
+* the whole fp32 layer against the fp64 composition: the operator's 1e-4."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_41_amd as kda
+import kda_inputs as ki
+import oracle
+from oracle import layer as ly
+from parity import err, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+WORKLOAD_V_TAIL = 5.4  # max|v| / rms(v) of prefill-4k's value input
+
+
+def host(t):
+    return None if t is None else t.cpu()
+
+
+def steps(x, ref) -> float:
+    """Largest |x - ref| in units of the bf16 spacing at ref (2^(e - 7) for
+    |ref| in [2^e, 2^(e+1))), plus an fp32 floor of 1e-5 rms(ref)."""
+    x = x.detach().double().cpu().numpy()
+    ref = np.asarray(ref, dtype=np.float64)
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 1e-300)))
+    allow = 2.0 ** (e - 7) + 1e-5 * np.sqrt(np.mean(ref * ref))
+    return float(np.max(np.abs(x - ref) / allow))
+
+
+def check_outputs(label, got, ref, bf16):
+    if bf16:
+        worst = [steps(g, r) for g, r in zip(got, ref)]
+        say(f"    {label} (bf16 steps): " + " ".join(f"{w:.2f}" for w in worst))
+        assert max(worst) <= 1.0, worst
+    else:
+        errs = [err(g, r) for g, r in zip(got, ref)]
+        say(f"    {label}: " + " ".join(f"{e:.2e}" for e in errs))
+        assert max(errs) <= 1e-5, errs
+
+
+def prologue(c):
+    return kda.layer_prologue(c.xq, c.xk, c.xv, c.xa, c.xb, c.wq, c.wk, c.wv, c.A_log, c.dt_bias, c.cu_seqlens)
+
+
+def prologue_ref(c):
+    return ly.layer_prologue(c.xq, c.xk, c.xv, c.xa, c.xb, c.wq, c.wk, c.wv, c.A_log, c.dt_bias,
+                             host(c.cu_seqlens))
+
+
+@pytest.mark.parametrize("d,dt", [(128, torch.bfloat16), (64, torch.bfloat16), (128, torch.float32),
+                                  (64, torch.float32)])
+def test_prologue(d, dt):
+    """Packed sequences of lengths 1-3 (shorter than the filter), an empty one and
+    ragged ones: the convolution starts from zero at every sequence."""
+    c = ki.make_layer("varlen-16", DEV, lengths=[1, 2, 0, 3, 70, 150], H=3, d=d, dtype=dt)
+    say(f"[layer] prologue d={d} {dt}")
+    got = prologue(c)
+    torch.cuda.synchronize()
+    check_outputs("q, k, v, log_alpha, beta", got, prologue_ref(c), dt == torch.bfloat16)
+
+
+@pytest.mark.parametrize("lengths", [[16, 0, 0, 17, 3, 44, 0], [0, 5, 11, 16, 1, 31]])
+def test_prologue_boundaries_at_tiles(lengths):
+    """The kernel walks 16-token tiles: sequences (and empty ones) that start
+    exactly on a tile boundary, just after one, or span several tiles."""
+    c = ki.make_layer("varlen-16", DEV, lengths=lengths, H=2, d=128, dtype=torch.float32)
+    say(f"[layer] prologue boundaries {lengths}")
+    got = prologue(c)
+    torch.cuda.synchronize()
+    check_outputs("q, k, v, log_alpha, beta", got, prologue_ref(c), False)
+
+
+@pytest.mark.parametrize("d,dt", [(128, torch.bfloat16), (128, torch.float32), (64, torch.float32)])
+def test_epilogue(d, dt):
+    c = ki.make_layer("varlen-16", DEV, lengths=[100, 37], H=3, d=d, dtype=dt)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    o = torch.randn(c.T_total, c.H, d, generator=g, device=DEV) * 3.0
+    say(f"[layer] epilogue d={d} {dt}")
+    y = kda.layer_epilogue(o, c.xg, c.rms_w)
+    torch.cuda.synchronize()
+    check_outputs("y", [y], [ly.layer_epilogue(o.cpu(), c.xg.cpu(), c.rms_w.cpu())], dt == torch.bfloat16)
+
+
+def test_whole_layer_fp32():
+    """fp32 pre-activations: prologue -> operator -> epilogue against the fp64
+    composition."""
+    c = ki.make_layer("prefill-4k", DEV, lengths=[300, 5, 190], H=4, dtype=torch.float32, s0_std=0.02)
+    q, k, v, la, b = prologue(c)
+    o, S = kda.chunk_fwd(q, k, v, la, b, c.initial_state, c.cu_seqlens)
+    y = kda.layer_epilogue(o, c.xg, c.rms_w)
+    torch.cuda.synchronize()
+    y_ref, S_ref, _ = ly.layer(c.xq, c.xk, c.xv, c.xa, c.xb, c.xg, c.wq, c.wk, c.wv, c.A_log, c.dt_bias,
+                               c.rms_w, host(c.initial_state), host(c.cu_seqlens))
+    ey, es = err(y, y_ref), err(S, S_ref)
+    say(f"[layer] whole fp32 layer: y {ey:.2e}  final state {es:.2e}")
+    assert ey <= 1e-4 and es <= 1e-4
+
+
+@pytest.mark.parametrize("shape", ["ragged", "prefill-4k"])
+def test_whole_bf16_layer(shape):
+    """bf16 pre-activations, each stage against fp64 on the inputs it actually
+    received: the prologue element-wise, the operator on the prologue's bf16
+    outputs (tail-scaled bar), the epilogue element-wise on the operator's o.
+    Together they pin the composed layer."""
+    kw = dict(lengths=[300, 5, 190], H=4, s0_std=0.02) if shape == "ragged" else {}
+    c = ki.make_layer("prefill-4k", DEV, **kw)
+    say(f"[layer] whole bf16 layer, {shape}")
+    q, k, v, la, b = prologue(c)
+    o, S = kda.chunk_fwd(q, k, v, la, b, c.initial_state, c.cu_seqlens)
+    y = kda.layer_epilogue(o, c.xg, c.rms_w)
+    torch.cuda.synchronize()
+    check_outputs("prologue", (q, k, v, la, b), prologue_ref(c), True)
+    o_ref, S_ref, _ = oracle.recurrence(q, k, v, la, b, c.initial_state, host(c.cu_seqlens))
+    vf = v.float()
+    tail = float(vf.abs().max() / vf.pow(2).mean().sqrt())
+    bar = 2e-2 * max(1.0, tail / WORKLOAD_V_TAIL)
+    eo, es = err(o, o_ref), err(S, S_ref)
+    say(f"    operator: o {eo:.2e}  final state {es:.2e}  (v tail {tail:.1f}, bar {bar:.2e})")
+    assert eo <= bar and es <= bar
+    check_outputs("epilogue", [y], [ly.layer_epilogue(o.cpu(), c.xg.cpu(), c.rms_w.cpu())], True)
