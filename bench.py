@@ -52,11 +52,13 @@ KERNEL_BYTES_PER_TOKEN_HEAD = {            # compulsory traffic of each prefill 
 KERNEL_SYMBOL = {"prep": "prep_kernel", "recur": "recur_kernel", "decode": "decode_kernel",
                  "dplr_prep": "dplr_prep_kernel", "dplr_recur": "recur_kernel",
                  "bwd_fwd_prep": "prep_kernel", "bwd_fwd_recur": "recur_kernel",
-                 "bwd_prep": "bwd_prep_kernel", "bwd_recur": "recur_kernel", "bwd_local": "bwd_local_kernel"}
+                 "bwd_prep": "bwd_prep_kernel", "bwd_recur": "recur_kernel", "bwd_local": "bwd_local_kernel",
+                 "layer_prologue": "layer_prologue_kernel", "layer_epilogue": "layer_epilogue_kernel"}
 KERNEL_SOURCE = {"prep": "kda_prep.hip", "recur": "kda_recur.hip", "decode": "kda_decode.hip",
                  "dplr_prep": "kda_dplr_prep.hip", "dplr_recur": "kda_recur.hip",
                  "bwd_fwd_prep": "kda_prep.hip", "bwd_fwd_recur": "kda_recur.hip",
-                 "bwd_prep": "kda_bwd.hip", "bwd_recur": "kda_recur.hip", "bwd_local": "kda_bwd.hip"}
+                 "bwd_prep": "kda_bwd.hip", "bwd_recur": "kda_recur.hip", "bwd_local": "kda_bwd.hip",
+                 "layer_prologue": "kda_layer.hip", "layer_epilogue": "kda_layer.hip"}
 
 
 def kernel_key(short_name: str):
@@ -78,7 +80,7 @@ def kernel_key(short_name: str):
         return "bwd_fwd_recur" if flag(1) else "recur"
     if sym == "prep_kernel":
         return "bwd_fwd_prep" if flag(3) else "prep"
-    for key in ("dplr_prep", "decode", "bwd_prep", "bwd_local"):
+    for key in ("dplr_prep", "decode", "bwd_prep", "bwd_local", "layer_prologue", "layer_epilogue"):
         if sym == KERNEL_SYMBOL[key]:
             return key
     return None
@@ -573,10 +575,12 @@ def main(argv=None):
             "tokens_per_s": round(case.T_total / (lt["layer"] * 1e-3), 1),
             "prologue_roofline": {"bound": "hbm", "achieved": round(pro_b / (lt["prologue"] * 1e-3) / 1e9, 1),
                                   "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                                  "frac": round(pro_b / (lt["prologue"] * 1e-3) / PEAK_HBM, 4)},
+                                  "frac": round(pro_b / (lt["prologue"] * 1e-3) / PEAK_HBM, 4),
+                                  "traffic": traffic_from_profiles("layer_prologue", TH)},
             "epilogue_roofline": {"bound": "hbm", "achieved": round(epi_b / (lt["epilogue"] * 1e-3) / 1e9, 1),
                                   "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                                  "frac": round(epi_b / (lt["epilogue"] * 1e-3) / PEAK_HBM, 4)}}
+                                  "frac": round(epi_b / (lt["epilogue"] * 1e-3) / PEAK_HBM, 4),
+                                  "traffic": traffic_from_profiles("layer_epilogue", TH)}}
         del lc
 
     if not args.no_decode:
