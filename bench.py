@@ -273,6 +273,10 @@ def time_layer(kda, lc, steps, warmup, hip, stream):
     epi_args = (ptr(o), ptr(lc.xg), ptr(lc.rms_w), T, H, d, dtc, ptr(y), P(stream))
     op_args = (*(ptr(t) for t in (q, k, v, la, beta, lc.initial_state, lc.cu_seqlens)), N, T, H, d, d, dtc, dtc,
                kda.KDA_F32, ptr(o), ptr(fs), ptr(ws), ws.numel(), P(stream))
+    fws = torch.empty(kda.layer_chunk_fwd_workspace_size(N, T, H, d), dtype=torch.uint8, device=dev)
+    fused_args = (*(ptr(t) for t in (lc.xq, lc.xk, lc.xv, lc.xa, lc.xb, lc.wq, lc.wk, lc.wv, lc.A_log, lc.dt_bias,
+                                     lc.initial_state, lc.cu_seqlens)),
+                  N, T, H, d, ptr(o), ptr(fs), ptr(fws), fws.numel(), P(stream))
 
     def step(ev=None, b=0):
         if ev is not None:
@@ -313,6 +317,24 @@ def time_layer(kda, lc, steps, warmup, hip, stream):
         out["operator"] += ev.ms(b + 1, b + 2) / steps
         out["epilogue"] += ev.ms(b + 2, b + 3) / steps
     ev.close()
+    # the fused path (bf16): prologue inside the chunk preparation, then the epilogue
+    if lc.xq.dtype == torch.bfloat16:
+        def fused_step():
+            if lib.kda_layer_chunk_fwd(*fused_args) != 0:
+                raise RuntimeError("kda_layer_chunk_fwd failed")
+            if lib.kda_layer_epilogue(*epi_args) != 0:
+                raise RuntimeError("kda_layer_epilogue failed")
+        for _ in range(warmup):
+            fused_step()
+        torch.cuda.synchronize()
+        ev = Events(hip, 2)
+        ev.record(0, stream)
+        for _ in range(steps):
+            fused_step()
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        out["fused_layer"] = ev.ms(0, 1) / steps
+        ev.close()
     return out
 
 
@@ -573,6 +595,7 @@ def main(argv=None):
             "workload": "prefill-4k pre-activations (bf16)",
             "ms": {k_: round(v_, 5) for k_, v_ in lt.items()},
             "tokens_per_s": round(case.T_total / (lt["layer"] * 1e-3), 1),
+            "fused_tokens_per_s": round(case.T_total / (lt["fused_layer"] * 1e-3), 1),
             "prologue_roofline": {"bound": "hbm", "achieved": round(pro_b / (lt["prologue"] * 1e-3) / 1e9, 1),
                                   "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                                   "frac": round(pro_b / (lt["prologue"] * 1e-3) / PEAK_HBM, 4),

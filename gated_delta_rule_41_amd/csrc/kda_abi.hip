@@ -507,6 +507,90 @@ kda_status kda_layer_prologue(const void* xq, const void* xk, const void* xv, co
     return launch_layer_prologue(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+// bytes of the fused layer forward's workspace: the forward's (16-bit factors)
+// and the exact path's q, k rows ([chunk-head][2][64][d] bf16)
+static size_t layer_fwd_workspace(int64_t NC, int H, int d, size_t* scr_off) {
+    const size_t base = plan_workspace(NC, H, d, false).total;
+    if (scr_off) *scr_off = base;
+    return base + align_up((size_t)NC * H * 2 * KDA_CHUNK * d * 2, 256);
+}
+
+kda_status kda_layer_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t d, size_t* bytes) {
+    if (!bytes) return KDA_ERR_NULL;
+    if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
+    if (!head_ok(d, d)) return KDA_ERR_UNSUPPORTED;
+    *bytes = layer_fwd_workspace(chunk_capacity(N, T_total, true), H, d, nullptr);
+    return KDA_OK;
+}
+
+kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
+                               const float* wq, const float* wk, const float* wv, const float* A_log,
+                               const float* dt_bias, const float* initial_state, const int32_t* cu_seqlens,
+                               int32_t N, int64_t T_total, int32_t H, int32_t d, float* o, float* final_state,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    if (!chunk_sizes_ok(N, T_total, H) || T_total * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    if (!cu_seqlens && N != 1) return KDA_ERR_SHAPE;
+    if (!head_ok(d, d)) return KDA_ERR_UNSUPPORTED;
+    if (T_total > 0 && (!xq || !xk || !xv || !xa || !xb || !wq || !wk || !wv || !A_log || !dt_bias || !o))
+        return KDA_ERR_NULL;
+    const size_t T = (size_t)T_total;
+    const size_t nx = T * H * d * 2, nb = T * H * 2, nw = (size_t)H * d * 4 * 4, nh = (size_t)H * 4,
+                 nd = (size_t)H * d * 4, ncu = cu_seqlens ? (size_t)(N + 1) * 4 : 0;
+    const size_t no = T * H * d * 4, ns = (size_t)N * H * d * d * 4;
+    const void* ins[12] = {xq, xk, xv, xa, xb, wq, wk, wv, A_log, dt_bias, cu_seqlens, initial_state};
+    const size_t nin[12] = {nx, nx, nx, nx, nb, nw, nw, nw, nh, nd, ncu, ns};
+    for (int i = 0; i < 12; ++i)  // [T, H, d] inputs move in bf16 channel pairs
+        if (!aligned_to(ins[i], i < 4 ? 4 : i == 4 ? 2 : i == 11 ? 16 : 4)) return KDA_ERR_ALIGN;
+    if (!aligned16(o) || !aligned16(final_state)) return KDA_ERR_ALIGN;
+    const int64_t NC = chunk_capacity(N, T_total, cu_seqlens != nullptr);
+    if (NC >= (int64_t(1) << 31) / H) return KDA_ERR_SHAPE;
+    size_t scr_off = 0;
+    const size_t wbytes = layer_fwd_workspace(NC, H, d, &scr_off);
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < wbytes) return KDA_ERR_WORKSPACE;
+    for (int i = 0; i < 12; ++i) {
+        if (overlaps(o, no, ins[i], nin[i]) || overlaps(workspace, wbytes, ins[i], nin[i])) return KDA_ERR_ALIAS;
+        if (i != 11 && overlaps(final_state, ns, ins[i], nin[i])) return KDA_ERR_ALIAS;
+    }
+    if (overlaps(o, no, final_state, ns) || overlaps(workspace, wbytes, o, no) ||
+        overlaps(workspace, wbytes, final_state, ns))
+        return KDA_ERR_ALIAS;
+    if (final_state && initial_state && final_state != initial_state &&
+        overlaps(final_state, ns, initial_state, ns))
+        return KDA_ERR_ALIAS;
+    const WsPlan plan = plan_workspace(NC, H, d, false);
+    char* w = static_cast<char*>(workspace);
+    ChunkArgs a;
+    a.q = a.k = a.v = a.la = a.beta = nullptr;  // computed inside the preparation
+    a.s0 = initial_state;
+    a.cu = cu_seqlens;
+    a.s_final = final_state;
+    a.o = o;
+    a.N = N;
+    a.T = (int)T_total;
+    a.H = H;
+    a.D = d;
+    a.NC = (int)NC;
+    a.in_f32 = false;
+    a.gate_f32 = false;
+    a.out_f32 = true;
+    a.qp = w + plan.off[0];
+    a.km = w + plan.off[1];
+    a.wn = w + plan.off[2];
+    a.u = w + plan.off[3];
+    a.aqk = w + plan.off[4];
+    a.gam = reinterpret_cast<float*>(w + plan.off[5]);
+    a.h = w + plan.off[6];
+    a.vn = w + plan.off[7];
+    a.pro = true;
+    a.xq = xq, a.xk = xk, a.xv = xv, a.xa = xa, a.xb = xb;
+    a.wq = wq, a.wk = wk, a.wv = wv, a.A_log = A_log, a.dt_bias = dt_bias;
+    a.qk_scr = w + scr_off;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (NC > 0 && launch_prep(a, st) != hipSuccess) return KDA_ERR_HIP;
+    if (launch_recur(a, st) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
 kda_status kda_layer_epilogue(const float* o, const void* g, const float* rms_w, int64_t T_total, int32_t H,
                               int32_t dv, kda_dtype dtype, void* y, void* stream) {
     if (T_total < 0 || T_total >= (int64_t(1) << 31) || H <= 0 || H > 65536 || T_total * H >= (int64_t(1) << 31))

@@ -37,6 +37,13 @@ struct ChunkArgs {
     // and the state-gradient recursion's extra state-independent term
     bool f32_factors = false;
     const float* pb = nullptr;  // [chunk-head][dv/16][dk/16][64 lanes][4] fp32, or null
+    // the layer prologue fused into the preparation (bf16 only): pre-activations
+    // and the prologue's parameters replace q, k, v, la, beta; qk_scr holds the
+    // q, k rows of chunks that take the exact path ([chunk-head][2][64][D] bf16)
+    bool pro = false;
+    const void *xq = nullptr, *xk = nullptr, *xv = nullptr, *xa = nullptr, *xb = nullptr;
+    const float *wq = nullptr, *wk = nullptr, *wv = nullptr, *A_log = nullptr, *dt_bias = nullptr;
+    void* qk_scr = nullptr;
 };
 
 // Backward of kda_chunk_fwd (see kda_bwd.hip).

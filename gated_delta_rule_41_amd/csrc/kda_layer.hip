@@ -19,96 +19,17 @@
 // once and are bound by HBM.
 #include "kda_common.h"
 #include "kda_launch.h"
+#include "kda_layer_util.h"
 
 namespace kda {
 
-constexpr int CONV_W = 4;
-constexpr float LAYER_EPS = 1e-6f;
-
-// Sum over the 64 lanes, the same in every lane: DPP swaps within each row of
-// 16 lanes (xor 1, xor 2, then the half-row and row mirrors, which pair every
-// lane with one holding the other partial sum), then the four row sums read out
-// in a fixed order. No LDS traffic; deterministic.
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float x) {
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float wave_sum(float x) {
-    x = dpp_add<0xB1>(x);   // quad_perm [1, 0, 3, 2]
-    x = dpp_add<0x4E>(x);   // quad_perm [2, 3, 0, 1]
-    x = dpp_add<0x141>(x);  // row_half_mirror
-    x = dpp_add<0x140>(x);  // row_mirror
-    const int u = __float_as_int(x);
-    return (__int_as_float(__builtin_amdgcn_readlane(u, 0)) + __int_as_float(__builtin_amdgcn_readlane(u, 16))) +
-           (__int_as_float(__builtin_amdgcn_readlane(u, 32)) + __int_as_float(__builtin_amdgcn_readlane(u, 48)));
-}
-// Transcendentals on the hardware units (v_exp_f32, v_log_f32, v_rcp_f32, each
-// within about an ulp): the library's range-reduced exp, IEEE division and
-// log1p would cost several times the instructions of the whole kernel's loads.
-constexpr float L_LOG2E = 1.4426950408889634f, L_LN2 = 0.6931471805599453f;
-__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-// 1 / (1 + e^-x); saturates to 0 and 1 (e^-x overflows to inf or underflows to 0)
-__device__ __forceinline__ float sigm(float x) { return rcp(1.f + __builtin_amdgcn_exp2f(-x * L_LOG2E)); }
-// log(1 + e^x) = max(x, 0) + log1p(e^-|x|). log1p(e) for e in (0, 1] by the
-// identity log1p(e) = log(u) e / (u - 1), u = 1 + e rounded (exact when u = 1),
-// which cancels the rounding of u to a few ulps (Goldberg, "What every computer
-// scientist should know about floating-point arithmetic", theorem 4).
-__device__ __forceinline__ float softplus_f(float x) {
-    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * L_LOG2E), u = 1.f + e;
-    const float lp = u == 1.f ? e : __builtin_amdgcn_logf(u) * L_LN2 * e * rcp(u - 1.f);
-    return fmaxf(x, 0.f) + lp;
-}
-
-template <typename T>
-__device__ __forceinline__ void st_out(T* p, int64_t i, float x);
-template <> __device__ __forceinline__ void st_out<float>(float* p, int64_t i, float x) { p[i] = x; }
-template <> __device__ __forceinline__ void st_out<uint16_t>(uint16_t* p, int64_t i, float x) { p[i] = f2bf(x); }
-
 // Prologue: a block of four waves covers 16 consecutive tokens of one head,
-// each wave four of them (G). A wave issues every load it needs at once: the
-// three rows before its first token and its own four rows of xq, xk, xv (the
-// convolution window), its four rows of xa and its four beta inputs, with row
-// indices clamped into [0, T) so that no load sits behind a branch; taps that
-// reach before a token's sequence are masked, never loaded from a neighbour
-// that matters. Lane j holds the channel pair 2j, 2j + 1 (d = 128; channel j
-// for d = 64).
-constexpr int G = 4;   // tokens per wave
+// each wave four of them (G), with every load issued before the first wait.
+constexpr int G = 4;       // tokens per wave
 constexpr int PT = 4 * G;  // tokens per block
 
-template <typename TE, int PER>
-struct Pair;  // PER consecutive channels of one row, loaded and stored together
-template <>
-struct Pair<uint16_t, 2> {
-    static __device__ __forceinline__ void ld(const uint16_t* p, float (&x)[2]) {
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-        x[0] = __uint_as_float(u << 16);
-        x[1] = __uint_as_float(u & 0xffff0000u);
-    }
-    static __device__ __forceinline__ void st(uint16_t* p, const float (&x)[2]) {
-        *reinterpret_cast<uint32_t*>(p) = pack2bf(x[0], x[1]);
-    }
-};
-template <>
-struct Pair<float, 2> {
-    static __device__ __forceinline__ void ld(const float* p, float (&x)[2]) {
-        const float2 u = *reinterpret_cast<const float2*>(p);
-        x[0] = u.x;
-        x[1] = u.y;
-    }
-    static __device__ __forceinline__ void st(float* p, const float (&x)[2]) {
-        *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
-    }
-};
-template <typename TE>
-struct Pair<TE, 1> {
-    static __device__ __forceinline__ void ld(const TE* p, float (&x)[1]) { x[0] = ld_in(p, 0); }
-    static __device__ __forceinline__ void st(TE* p, const float (&x)[1]) { st_out(p, 0, x[0]); }
-};
-
 template <int D, typename TE>
-__global__ __launch_bounds__(256) void layer_prologue_kernel(const TE* __restrict__ xq, const TE* __restrict__ xk,
-                                                             const TE* __restrict__ xv, const TE* __restrict__ xa,
-                                                             const TE* __restrict__ xb, const float* __restrict__ wq,
+__global__ __launch_bounds__(256) void layer_prologue_kernel(PrologueIn<TE> in, const float* __restrict__ wq,
                                                              const float* __restrict__ wk, const float* __restrict__ wv,
                                                              const float* __restrict__ A_log,
                                                              const float* __restrict__ dt_bias,
@@ -116,39 +37,16 @@ __global__ __launch_bounds__(256) void layer_prologue_kernel(const TE* __restric
                                                              TE* __restrict__ q, TE* __restrict__ k,
                                                              TE* __restrict__ v, TE* __restrict__ la,
                                                              TE* __restrict__ beta) {
-    constexpr int PER = D / 64;  // channels per lane
-    constexpr int W = CONV_W - 1 + G;  // window rows t0 - 3 .. t0 + G - 1
+    constexpr int PER = D / 64;
     using PR = Pair<TE, PER>;
     const int h = blockIdx.x % H;
     const int t0 = (blockIdx.x / H) * PT + (threadIdx.x >> 6) * G;  // this wave's first token
     if (t0 >= T) return;  // uniform over the wave
     const int l = threadIdx.x & 63, c0 = PER * l;
-    float win[3][W][PER], xg[G][PER];
-#pragma unroll
-    for (int i = 0; i < W; ++i) {
-        const int s = min(max(t0 - (CONV_W - 1) + i, 0), T - 1);
-        const int64_t ro = ((int64_t)s * H + h) * D + c0;
-        PR::ld(xq + ro, win[0][i]);
-        PR::ld(xk + ro, win[1][i]);
-        PR::ld(xv + ro, win[2][i]);
-    }
-#pragma unroll
-    for (int j = 0; j < G; ++j) PR::ld(xa + ((int64_t)min(t0 + j, T - 1) * H + h) * D + c0, xg[j]);
-    const int tb = min(t0 + (l & (G - 1)), T - 1);
-    const float xbl = ld_in(xb, (int64_t)tb * H + h);  // lane j < G: token t0 + j
-    float fw[3][PER][CONV_W], db[PER];
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-#pragma unroll
-        for (int i = 0; i < CONV_W; ++i) {
-            const int64_t wi = ((int64_t)h * D + c0 + p) * CONV_W + i;
-            fw[0][p][i] = wq[wi];
-            fw[1][p][i] = wk[wi];
-            fw[2][p][i] = wv[wi];
-        }
-        db[p] = dt_bias[h * D + c0 + p];
-    }
-    const float scale = __expf(A_log[h]);
+    PrologueWindow<D, G, TE> win;
+    win.load(in, h, t0, T, H, c0, l);
+    ConvFilters<D> f;
+    f.load(wq, wk, wv, A_log, dt_bias, h, c0);
     // the sequence holding t0 (cu_seqlens sorted; NULL = one sequence), then
     // walk forward across boundaries
     int n = 0, first = 0, next = INT_MAX;
@@ -161,47 +59,23 @@ __global__ __launch_bounds__(256) void layer_prologue_kernel(const TE* __restric
         first = cu[n];
         next = cu[n + 1];
     }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const int t = t0 + j;
-        if (t >= T) break;
+    auto seq_first = [&](int t) {
         while (n + 1 < N && t >= next) {  // empty sequences end where they start
             first = next;
             ++n;
             next = cu[n + 1];
         }
-        float y[3][PER];
-#pragma unroll
-        for (int m = 0; m < 3; ++m)
-#pragma unroll
-            for (int p = 0; p < PER; ++p) {
-                float acc = 0.f;
-#pragma unroll
-                for (int i = 0; i < CONV_W; ++i)
-                    if (t - (CONV_W - 1) + i >= first) acc += fw[m][p][i] * win[m][j + i][p];
-                y[m][p] = acc * sigm(acc);  // swish
-            }
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            sq += y[0][p] * y[0][p];
-            sk += y[1][p] * y[1][p];
-        }
-        const float nq = rsqrtf(wave_sum(sq) + LAYER_EPS), nk = rsqrtf(wave_sum(sk) + LAYER_EPS);
-        const int64_t ro = ((int64_t)t * H + h) * D + c0;
-        float oq[PER], ok[PER], og[PER];
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            oq[p] = y[0][p] * nq;
-            ok[p] = y[1][p] * nk;
-            og[p] = -scale * softplus_f(xg[j][p] + db[p]);
-        }
+        return first;
+    };
+    const float bl = win.compute(f, t0, T, seq_first, [&](int j, const float (&oq)[PER], const float (&ok)[PER],
+                                                          const float (&ov)[PER], const float (&og)[PER]) {
+        const int64_t ro = ((int64_t)(t0 + j) * H + h) * D + c0;
         PR::st(q + ro, oq);
         PR::st(k + ro, ok);
-        PR::st(v + ro, y[2]);
+        PR::st(v + ro, ov);
         PR::st(la + ro, og);
-    }
-    if (l < G && t0 + l < T) st_out(beta, (int64_t)(t0 + l) * H + h, sigm(xbl));
+    });
+    if (l < G && t0 + l < T) st_out(beta, (int64_t)(t0 + l) * H + h, bl);
 }
 
 // Epilogue: each wave takes G consecutive (token, head) rows and issues all of
@@ -241,10 +115,10 @@ __global__ __launch_bounds__(256) void layer_epilogue_kernel(const float* __rest
 template <int D, typename TE>
 static hipError_t launch_prologue_t(const LayerArgs& a, hipStream_t st) {
     const int64_t blocks = (int64_t)((a.T + PT - 1) / PT) * a.H;  // (tile, head), head fastest
-    hipLaunchKernelGGL((layer_prologue_kernel<D, TE>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const TE*)a.xq, (const TE*)a.xk, (const TE*)a.xv, (const TE*)a.xa, (const TE*)a.xb, a.wq,
-                       a.wk, a.wv, a.A_log, a.dt_bias, a.cu, a.N, a.T, a.H, (TE*)a.q, (TE*)a.k, (TE*)a.v,
-                       (TE*)a.la, (TE*)a.beta);
+    const PrologueIn<TE> in{(const TE*)a.xq, (const TE*)a.xk, (const TE*)a.xv, (const TE*)a.xa, (const TE*)a.xb};
+    hipLaunchKernelGGL((layer_prologue_kernel<D, TE>), dim3((unsigned)blocks), dim3(256), 0, st, in, a.wq, a.wk,
+                       a.wv, a.A_log, a.dt_bias, a.cu, a.N, a.T, a.H, (TE*)a.q, (TE*)a.k, (TE*)a.v, (TE*)a.la,
+                       (TE*)a.beta);
     return hipGetLastError();
 }
 

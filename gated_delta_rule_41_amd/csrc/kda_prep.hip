@@ -35,8 +35,16 @@
 // also the gated key products A_kk / beta, which the backward differentiates.
 // Rows past the end of a sequence are zero-padded (k = q = v = 0, beta = 0,
 // log alpha = 0), which is exactly neutral for every factor.
+//
+// The fused-prologue variant (PRO, bf16 only) starts from the layer's
+// pre-activations instead of q, k, v, log alpha, beta: each wave first runs the
+// layer prologue (kda_layer_util.h) for its 16 rows into LDS, rounded to bf16
+// exactly as the prologue kernel stores them, and phase 0 reads that stage.
+// A chunk that takes the exact slow path copies its q, k rows to a workspace
+// scratch, which that path reads instead of the inputs.
 #include "kda_common.h"
 #include "kda_launch.h"
+#include "kda_layer_util.h"
 #include "kda_prep_util.h"
 
 #include <type_traits>
@@ -83,13 +91,27 @@ struct PrepSmem {
     static_assert(64 * D * (int)sizeof(E) <= R1, "-W staging must fit in R1");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     static_assert(4 * AK_BLOCK * 4 <= CONST, "T_II must fit in the constants area");
+    // fused prologue: q, k, v, log alpha [64][SS] bf16 and beta [64] fp32, over
+    // everything else (all of it is written only after phase 0)
+    static constexpr int SS = D + 16;
+    static constexpr int STAGE = 4 * 64 * SS * 2 + 64 * 4;
+    static_assert(F32 || STAGE <= BYTES, "the prologue stage must fit in the 16-bit plan");
 };
 
-template <int D, typename TIn, typename TG, bool F32>
+// The fused prologue's inputs (unused by the other instantiations).
+struct ProArgs {
+    PrologueIn<uint16_t> in;
+    const float *wq, *wk, *wv, *A_log, *dt_bias;
+    uint16_t* qk_scr;  // [chunk-head][q, k][64][D] bf16, written by slow chunks only
+};
+
+template <int D, typename TIn, typename TG, bool F32, bool PRO = false>
 __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k, const TIn* v,
                                                       const TG* la, const TG* beta,
                                                       const int32_t* __restrict__ cu, int N, int T, int H,
-                                                      Ws<typename Pol<F32>::E> ws) {
+                                                      Ws<typename Pol<F32>::E> ws, ProArgs pa) {
+    static_assert(!PRO || (!F32 && std::is_same<TIn, uint16_t>::value && std::is_same<TG, uint16_t>::value),
+                  "the fused prologue is bf16 only");
     using P = Pol<F32>;
     using E = typename P::E;
     using Frag = typename P::Frag;
@@ -149,17 +171,95 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     // behind the gate scans. The empty asm statement below pins them.)
     RowRaw<TG, NS> rla;
     RowRaw<TIn, NS> rq, rk, rv;
-    rla.load(la, ldoff, g);  // first: the scans wait only for it
-    rq.load(q, ldoff, g);
-    rk.load(k, ldoff, g);
-    rv.load(v, ldoff, g);
-    const float bval = ld_in(beta, (int64_t)(valid ? t0 + r : t0) * H + h);
-    asm volatile("" ::: "memory");
+    float bval;
+    bool maybe_slow = false;  // fused prologue: this chunk may take the exact path
+    if constexpr (PRO) {
+        // the layer prologue for rows 16 w .. 16 w + 15 into the stage
+        constexpr int SS = SM::SS, PER = D / 64;
+        uint16_t* st_q = reinterpret_cast<uint16_t*>(smem);
+        uint16_t* st_k = st_q + 64 * SS;
+        uint16_t* st_v = st_k + 64 * SS;
+        uint16_t* st_la = st_v + 64 * SS;
+        float* st_b = reinterpret_cast<float*>(st_la + 64 * SS);
+        {
+            constexpr int PG = 8;  // tokens per load group
+            const int c0 = PER * l;
+            const int sstart = cu != nullptr ? cu[loc.seq] : 0;  // the chunk lies in one sequence
+            ConvFilters<D> f;
+            using PR = Pair<uint16_t, PER>;
+            float gs[PER] = {};  // log2 gate summed over rows 1..15 of this wave's block
+#pragma unroll 1
+            for (int gi = 0; gi < 16 / PG; ++gi) {
+                const int rw = 16 * w + PG * gi, tw = t0 + rw;
+                PrologueWindow<D, PG, uint16_t> pw;
+                pw.load(pa.in, h, tw, T, H, c0, l);
+                if (gi == 0) f.load(pa.wq, pa.wk, pa.wv, pa.A_log, pa.dt_bias, h, c0);
+                const float bl = pw.compute(f, tw, t0 + L, [&](int) { return sstart; },
+                                            [&](int j, const float (&oq)[PER], const float (&ok)[PER],
+                                                const float (&ov)[PER], const float (&og)[PER]) {
+                                                const int so = (rw + j) * SS + c0;
+                                                PR::st(st_q + so, oq);
+                                                PR::st(st_k + so, ok);
+                                                PR::st(st_v + so, ov);
+                                                PR::st(st_la + so, og);
+                                                if (rw + j > 16 * w) {
+#pragma unroll
+                                                    for (int p = 0; p < PER; ++p)
+                                                        gs[p] += bf2f(f2bf(og[p])) * LOG2E;
+                                                }
+                                            });
+                if (l < PG) st_b[rw + l] = bf2f(f2bf(bl));  // as a bf16 beta input reads
+            }
+            // Phase 2 sends the chunk to the exact path when some block's gate
+            // range, minus the sum of its rows 1..15, exceeds GUARD. These sums
+            // of the same fp32 terms in another order differ by ~1e-4 near the
+            // guard, so a margin of 1 flags every chunk that phase 2 will send
+            // (and NaN or infinite gates too).
+            bool flag = false;
+#pragma unroll
+            for (int p = 0; p < PER; ++p) flag |= !(-gs[p] <= GUARD - 1.f);
+            maybe_slow = __syncthreads_or(flag);  // also publishes the stage
+        }
+        const int so = (valid ? r : 0) * SS;
+        rla.load(reinterpret_cast<const TG*>(st_la), so, g);
+        rq.load(reinterpret_cast<const TIn*>(st_q), so, g);
+        rk.load(reinterpret_cast<const TIn*>(st_k), so, g);
+        rv.load(reinterpret_cast<const TIn*>(st_v), so, g);
+        bval = st_b[valid ? r : 0];
+    } else {
+        rla.load(la, ldoff, g);  // first: the scans wait only for it
+        rq.load(q, ldoff, g);
+        rk.load(k, ldoff, g);
+        rv.load(v, ldoff, g);
+        bval = ld_in(beta, (int64_t)(valid ? t0 + r : t0) * H + h);
+        asm volatile("" ::: "memory");
+    }
     float xl[NS][8], q8[NS][8], k8[NS][8], v8[NS][8];
     rla.get(xl, valid, LOG2E);
     rq.get(q8, valid, 1.f);
     rk.get(k8, valid, 1.f);
     rv.get(v8, valid, 1.f);
+    if constexpr (PRO) {
+        __syncthreads();  // the stage is read; later phases reuse its LDS
+        // the exact path re-reads q and k rows: a chunk that may take it keeps
+        // its rows in the scratch (published by the barriers of phases 1-3)
+        if (maybe_slow && valid) {
+            uint16_t* sq = pa.qk_scr + chh * 2 * 64 * D + r * D;
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int c = 32 * s + 16 * hf + 4 * g;
+                    u32x2_t pq, pk;
+                    pq[0] = pack2bf(q8[s][4 * hf], q8[s][4 * hf + 1]);
+                    pq[1] = pack2bf(q8[s][4 * hf + 2], q8[s][4 * hf + 3]);
+                    pk[0] = pack2bf(k8[s][4 * hf], k8[s][4 * hf + 1]);
+                    pk[1] = pack2bf(k8[s][4 * hf + 2], k8[s][4 * hf + 3]);
+                    *reinterpret_cast<u32x2_t*>(sq + c) = pq;
+                    *reinterpret_cast<u32x2_t*>(sq + 64 * D + c) = pk;
+                }
+        }
+    }
 
     // ---- 1. log2 gate scanned inside each 16-row block (lanes n of one DPP row)
 #pragma unroll
@@ -228,7 +328,6 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     if (l == 0) slow_s[w] = wave_bad;
     __syncthreads();
     const bool slow = (slow_s[0] | slow_s[1] | slow_s[2] | slow_s[3]) != 0;
-
     // 0/1 selectors for the matrix-core transposes (16-bit operands): with A a
     // lane-per-row operand over a 32-channel slice, A sel[hf] is the 16 x 16
     // block of channels 16 hf .. 16 hf + 15 in accumulator layout (lane n holds
@@ -365,14 +464,22 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
             float sq = 0.f, sk = 0.f;
             if (ii <= rr && rr < L) {
                 const int I = rr >> 4, J = ii >> 4;
-                const int64_t ro = ((int64_t)(t0 + rr) * H + h) * D;
-                const int64_t io = ((int64_t)(t0 + ii) * H + h) * D;
+                const TIn* qsrc = q;
+                const TIn* ksrc = k;
+                int64_t ro = ((int64_t)(t0 + rr) * H + h) * D;
+                int64_t io = ((int64_t)(t0 + ii) * H + h) * D;
+                if constexpr (PRO) {
+                    qsrc = reinterpret_cast<const TIn*>(pa.qk_scr + chh * 2 * 64 * D);
+                    ksrc = qsrc + 64 * D;
+                    ro = (int64_t)rr * D;
+                    io = (int64_t)ii * D;
+                }
                 for (int c = 0; c < D; ++c) {
                     float ex = xl_slow[rr * D + c] - xl_slow[ii * D + c];
                     for (int K = J; K < I; ++K) ex += tot[K * D + c];
-                    const float kv = ld_in(k, io + c) * exp2f(ex);
-                    sq += ld_in(q, ro + c) * kv;
-                    sk += ld_in(k, ro + c) * kv;
+                    const float kv = ld_in(ksrc, io + c) * exp2f(ex);
+                    sq += ld_in(qsrc, ro + c) * kv;
+                    sk += ld_in(ksrc, ro + c) * kv;
                 }
             }
             aqk_sl[m] = sq;
@@ -603,17 +710,22 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     }
 }
 
-template <int D, typename TIn, typename TG, bool F32>
+template <int D, typename TIn, typename TG, bool F32, bool PRO = false>
 static hipError_t launch_prep_t(const ChunkArgs& a, hipStream_t st) {
     using E = typename Pol<F32>::E;
     using SM = PrepSmem<D, F32>;
     Ws<E> ws{(E*)a.qp, (E*)a.km, (E*)a.wn, (E*)a.u, (E*)a.aqk, a.gam, (E*)a.h, (E*)a.vn, (E*)a.am};
-    auto kern = prep_kernel<D, TIn, TG, F32>;
+    ProArgs pa{};
+    if constexpr (PRO)
+        pa = ProArgs{{(const uint16_t*)a.xq, (const uint16_t*)a.xk, (const uint16_t*)a.xv, (const uint16_t*)a.xa,
+                      (const uint16_t*)a.xb},
+                     a.wq, a.wk, a.wv, a.A_log, a.dt_bias, (uint16_t*)a.qk_scr};
+    auto kern = prep_kernel<D, TIn, TG, F32, PRO>;
     const hipError_t e = allow_dynamic_lds((const void*)kern, SM::BYTES);
     if (e != hipSuccess) return e;
     dim3 grid(a.NC * a.H), block(256);  // NC * H < 2^31 (checked by the caller)
     hipLaunchKernelGGL(kern, grid, block, SM::BYTES, st, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                       (const TG*)a.la, (const TG*)a.beta, a.cu, a.N, a.T, a.H, ws);
+                       (const TG*)a.la, (const TG*)a.beta, a.cu, a.N, a.T, a.H, ws, pa);
     return hipGetLastError();
 }
 
@@ -628,6 +740,9 @@ static hipError_t launch_prep_d(const ChunkArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_prep(const ChunkArgs& a, hipStream_t st) {
+    if (a.pro)  // bf16 pre-activations, fp16 factors (checked by the caller)
+        return a.D == 128 ? launch_prep_t<128, uint16_t, uint16_t, false, true>(a, st)
+                          : launch_prep_t<64, uint16_t, uint16_t, false, true>(a, st);
     const bool f32 = a.in_f32 || a.f32_factors;
     if (a.D == 128) return f32 ? launch_prep_d<128, true>(a, st) : launch_prep_d<128, false>(a, st);
     return f32 ? launch_prep_d<64, true>(a, st) : launch_prep_d<64, false>(a, st);

@@ -222,6 +222,30 @@ kda_status kda_layer_prologue(const void* xq, const void* xk, const void* xv, co
                               void* log_alpha, void* beta, void* stream);
 
 /*
+ * Bytes of device workspace kda_layer_chunk_fwd needs (host call, no device
+ * access): kda_chunk_fwd's for bf16 inputs, plus 32 KiB per chunk-head at
+ * d = 128 (16 KiB at d = 64) for the q, k rows of chunks that take the exact
+ * path.
+ */
+kda_status kda_layer_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t d, size_t* bytes);
+
+/*
+ * kda_layer_prologue and kda_chunk_fwd in one pass (bf16 only): the chunk
+ * preparation computes the prologue for its own rows (and the three rows before
+ * them) in LDS, rounded to bf16 exactly as kda_layer_prologue stores them, so
+ * the results equal those of kda_layer_prologue followed by kda_chunk_fwd with
+ * bf16 inputs and fp32 o, without q, k, v, log_alpha, beta ever reaching
+ * memory. Arguments as kda_layer_prologue (dtype bf16) and kda_chunk_fwd
+ * (initial_state, final_state, workspace, o fp32 [T_total, H, d]); the same
+ * alignment, aliasing and size rules. Two kernels are enqueued.
+ */
+kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
+                               const float* wq, const float* wk, const float* wv, const float* A_log,
+                               const float* dt_bias, const float* initial_state, const int32_t* cu_seqlens,
+                               int32_t N, int64_t T_total, int32_t H, int32_t d, float* o, float* final_state,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The layer's epilogue (same section: a per-head RMSNorm and a data-dependent
  * output gate before the output projection):
  *

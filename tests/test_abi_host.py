@@ -31,7 +31,8 @@ def test_library_exports_every_declared_function():
     assert names == ["kda_abi_version", "kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd",
                      "kda_chunk_fwd_timed",
                      "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_dplr_chunk_fwd",
-                     "kda_dplr_chunk_fwd_workspace_size", "kda_layer_epilogue", "kda_layer_prologue",
+                     "kda_dplr_chunk_fwd_workspace_size", "kda_layer_chunk_fwd", "kda_layer_chunk_fwd_workspace_size",
+                     "kda_layer_epilogue", "kda_layer_prologue",
                      "kda_status_str"]
     for nm in names:
         assert hasattr(lib, nm), nm
@@ -297,3 +298,40 @@ def test_valid_arguments_reach_the_launch_without_gpu():
     assert bwd_call() == HIP
     assert prologue_call() == HIP
     assert epilogue_call() == HIP
+
+
+def layer_fwd_call(**over):
+    f = Fake()
+    a = dict(xq=f(), xk=f(), xv=f(), xa=f(), xb=f(), wq=f(), wk=f(), wv=f(), A_log=f(), dtb=f(), s0=None, cu=None,
+             N=1, T=100, H=2, d=64, o=f(), fs=f(), ws=f(), wsb=1 << 40, stream=None)
+    a.update(over)
+    P = ctypes.c_void_p
+    return kda._load().kda_layer_chunk_fwd(*(P(a[x]) for x in ("xq", "xk", "xv", "xa", "xb", "wq", "wk", "wv",
+                                                               "A_log", "dtb", "s0", "cu")),
+                                           a["N"], a["T"], a["H"], a["d"], P(a["o"]), P(a["fs"]), P(a["ws"]),
+                                           a["wsb"], P(a["stream"]))
+
+
+def test_layer_fwd_workspace_and_validation():
+    """The fused prologue + prefill: workspace = the bf16 forward's plus 2 x 64 x d
+    bf16 per chunk-head (the exact path's q, k rows); host validation refuses
+    every malformed call before any launch."""
+    assert kda.layer_chunk_fwd_workspace_size(1, 4096, 32, 128) == 64 * 32 * (74240 + 2 * 64 * 128 * 2)
+    assert kda.layer_chunk_fwd_workspace_size(16, 135000, 32, 64) == (
+        kda.workspace_size(16, 135000, 32, 64, 64) + ((135000 + 63 * 16) // 64) * 32 * 2 * 64 * 64 * 2)
+    with pytest.raises(kda.KDAError):
+        kda.layer_chunk_fwd_workspace_size(1, 10, 1, 96)
+    assert layer_fwd_call(xq=None) == NULL
+    assert layer_fwd_call(o=None) == NULL
+    assert layer_fwd_call(N=2) == SHAPE  # no cu_seqlens
+    assert layer_fwd_call(T=1 << 30, H=4) == SHAPE
+    assert layer_fwd_call(d=96) == UNSUP
+    f = Fake()
+    assert layer_fwd_call(xq=f(2)) == ALIGN  # bf16 channel pairs
+    assert layer_fwd_call(o=f(8)) == ALIGN
+    assert layer_fwd_call(wsb=1024) == WORKSPACE
+    assert layer_fwd_call(ws=f(128)) == WORKSPACE  # 256-byte aligned
+    x = f()
+    assert layer_fwd_call(xq=x, o=x + 64) == ALIAS
+    y = f()
+    assert layer_fwd_call(o=y, fs=y + 256) == ALIAS

@@ -136,3 +136,45 @@ def test_whole_bf16_layer(shape):
     say(f"    operator: o {eo:.2e}  final state {es:.2e}  (v tail {tail:.1f}, bar {bar:.2e})")
     assert eo <= bar and es <= bar
     check_outputs("epilogue", [y], [ly.layer_epilogue(o.cpu(), c.xg.cpu(), c.rms_w.cpu())], True)
+
+
+FUSED_CASES = {
+    "ragged": dict(lengths=[300, 5, 0, 190], H=4, s0_std=0.02),
+    "ragged-d64": dict(lengths=[70, 1, 129], H=3, d=64),
+    "strong-decay": dict(lengths=[200, 77], H=2),  # dt_bias raised below: the exact path
+    "prefill-4k": {},
+}
+
+
+@pytest.mark.parametrize("shape", list(FUSED_CASES))
+def test_fused_layer_forward(shape):
+    """kda_layer_chunk_fwd (the prologue computed inside the chunk preparation)
+    against kda_layer_prologue followed by kda_chunk_fwd: the fused stage rounds
+    the prologue's outputs to bf16 as the prologue kernel stores them, so the two
+    agree to fp32 rounding (bar 1e-6 of the RMS; bitwise equality is reported).
+    The operator's output is also checked against the oracle on those inputs
+    (the tail-scaled bar of the whole-layer test)."""
+    c = ki.make_layer("prefill-4k", DEV, **FUSED_CASES[shape])
+    if shape == "strong-decay":
+        # log alpha about -6 per token: a 16-row block spans ~130 in log2 units,
+        # beyond the fast path's guard, so every chunk takes the exact path,
+        # which reads its q, k rows from the fused path's scratch
+        c.dt_bias.fill_(6.0)
+    say(f"[layer] fused prologue + prefill, {shape}")
+    q, k, v, la, b = prologue(c)
+    o_ref, S_ref = kda.chunk_fwd(q, k, v, la, b, c.initial_state, c.cu_seqlens)
+    o, S = kda.layer_chunk_fwd(c.xq, c.xk, c.xv, c.xa, c.xb, c.wq, c.wk, c.wv, c.A_log, c.dt_bias,
+                               c.initial_state, c.cu_seqlens)
+    torch.cuda.synchronize()
+    same = torch.equal(o, o_ref) and torch.equal(S, S_ref)
+    eo, es = err(o, o_ref.cpu()), err(S, S_ref.cpu())
+    say(f"    fused vs unfused: o {eo:.2e}  final state {es:.2e}  bitwise {same}")
+    assert eo <= 1e-6 and es <= 1e-6
+    if shape != "prefill-4k":  # the whole-layer test covers the oracle at that size
+        oo, So, _ = oracle.recurrence(q, k, v, la, b, c.initial_state, host(c.cu_seqlens))
+        vf = v.float()
+        tail = float(vf.abs().max() / vf.pow(2).mean().sqrt())
+        bar = 2e-2 * max(1.0, tail / WORKLOAD_V_TAIL)
+        e1, e2 = err(o, oo), err(S, So)
+        say(f"    fused vs oracle: o {e1:.2e}  final state {e2:.2e}  (bar {bar:.2e})")
+        assert e1 <= bar and e2 <= bar
