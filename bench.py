@@ -53,18 +53,21 @@ KERNEL_SYMBOL = {"prep": "prep_kernel", "recur": "recur_kernel", "decode": "deco
                  "dplr_prep": "dplr_prep_kernel", "dplr_recur": "recur_kernel",
                  "bwd_fwd_prep": "prep_kernel", "bwd_fwd_recur": "recur_kernel",
                  "bwd_prep": "bwd_prep_kernel", "bwd_recur": "recur_kernel", "bwd_local": "bwd_local_kernel",
-                 "layer_prologue": "layer_prologue_kernel", "layer_epilogue": "layer_epilogue_kernel"}
+                 "layer_prologue": "layer_prologue_kernel", "layer_epilogue": "layer_epilogue_kernel",
+                 "layer_prep": "prep_kernel"}
 KERNEL_SOURCE = {"prep": "kda_prep.hip", "recur": "kda_recur.hip", "decode": "kda_decode.hip",
                  "dplr_prep": "kda_dplr_prep.hip", "dplr_recur": "kda_recur.hip",
                  "bwd_fwd_prep": "kda_prep.hip", "bwd_fwd_recur": "kda_recur.hip",
                  "bwd_prep": "kda_bwd.hip", "bwd_recur": "kda_recur.hip", "bwd_local": "kda_bwd.hip",
-                 "layer_prologue": "kda_layer.hip", "layer_epilogue": "kda_layer.hip"}
+                 "layer_prologue": ("kda_layer.hip", "kda_layer_util.h"), "layer_epilogue": "kda_layer.hip",
+                 "layer_prep": ("kda_prep.hip", "kda_layer_util.h")}
 
 
 def kernel_key(short_name: str):
     """Which of this library's kernels a demangled name (arguments stripped) is.
     The template arguments tell the instantiations apart: the preparation's
-    last one is fp32 factors (the backward's forward recompute); the state
+    last two are fp32 factors (the backward's forward recompute) and the fused
+    layer prologue; the state
     recursion's are <D, fp32 factors, fused output, fp32 output, DPLR chain,
     added per-chunk term (the backward's state-gradient recursion)>."""
     if "<" not in short_name:
@@ -78,7 +81,9 @@ def kernel_key(short_name: str):
         if flag(4):
             return "dplr_recur"
         return "bwd_fwd_recur" if flag(1) else "recur"
-    if sym == "prep_kernel":
+    if sym == "prep_kernel":  # <D, TIn, TG, fp32 factors, fused layer prologue>
+        if flag(4):
+            return "layer_prep"
         return "bwd_fwd_prep" if flag(3) else "prep"
     for key in ("dplr_prep", "decode", "bwd_prep", "bwd_local", "layer_prologue", "layer_epilogue"):
         if sym == KERNEL_SYMBOL[key]:
@@ -131,7 +136,8 @@ class Events:
 
 def source_sha(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCE[kernel], "kda_common.h"):
+    src = KERNEL_SOURCE[kernel]
+    for f in (*(src if isinstance(src, tuple) else (src,)), "kda_common.h"):
         with open(os.path.join(ROOT, "gated_delta_rule_41_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -596,6 +602,7 @@ def main(argv=None):
             "ms": {k_: round(v_, 5) for k_, v_ in lt.items()},
             "tokens_per_s": round(case.T_total / (lt["layer"] * 1e-3), 1),
             "fused_tokens_per_s": round(case.T_total / (lt["fused_layer"] * 1e-3), 1),
+            "fused_prep_hbm_bytes_per_launch": traffic_from_profiles("layer_prep", TH),
             "prologue_roofline": {"bound": "hbm", "achieved": round(pro_b / (lt["prologue"] * 1e-3) / 1e9, 1),
                                   "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                                   "frac": round(pro_b / (lt["prologue"] * 1e-3) / PEAK_HBM, 4),
