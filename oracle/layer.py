@@ -107,6 +107,45 @@ def layer_prologue(xq, xk, xv, xa, xb, wq, wk, wv, A_log, dt_bias, cu_seqlens=No
     return q, k, v, decay_gate(xa, A_log, dt_bias), sigmoid(_f64(xb))
 
 
+def conv_state(xq, xk, xv, cu_seqlens=None):
+    """The convolution's history after each sequence, for one-token decoding: the
+    last CONV_WIDTH - 1 rows of xq, xk, xv, oldest first, with zero rows where
+    the sequence is shorter. Returns [N, H, 3 (q, k, v), CONV_WIDTH - 1, d]."""
+    xs = [_f64(x) for x in (xq, xk, xv)]
+    T, H, d = xs[0].shape
+    b = _bounds(T, cu_seqlens)
+    out = np.zeros((len(b) - 1, H, 3, CONV_WIDTH - 1, d))
+    for n in range(len(b) - 1):
+        for i in range(CONV_WIDTH - 1):
+            t = b[n + 1] - (CONV_WIDTH - 1) + i
+            if t >= b[n]:
+                for m in range(3):
+                    out[n, :, m, i] = xs[m][t]
+    return out
+
+
+def layer_decode_prologue(xq, xk, xv, xa, xb, state, wq, wk, wv, A_log, dt_bias):
+    """One token per sequence (xq, xk, xv, xa [N, H, d], xb [N, H]) after the
+    history ``state`` [N, H, 3, CONV_WIDTH - 1, d]: the convolution reads the
+    history's rows and then the new one. Returns (q, k, v, log_alpha, beta,
+    the history shifted by the new row)."""
+    state = _f64(state)
+    new = [_f64(x) for x in (xq, xk, xv)]
+    ws = [_f64(w) for w in (wq, wk, wv)]
+    y = []
+    for m in range(3):
+        win = np.concatenate([state[:, :, m], new[m][:, :, None]], axis=2)  # [N, H, 4, d]
+        acc = np.zeros_like(new[m])
+        for i in range(CONV_WIDTH):
+            acc += ws[m][None, :, :, i] * win[:, :, i]
+        y.append(acc)
+    q = l2norm(swish(y[0]))
+    k = l2norm(swish(y[1]))
+    v = swish(y[2])
+    nxt = np.concatenate([state[:, :, :, 1:], np.stack(new, axis=2)[:, :, :, None]], axis=3)
+    return q, k, v, decay_gate(xa, A_log, dt_bias), sigmoid(_f64(xb)), nxt
+
+
 def layer_epilogue(o, g, rms_w):
     """The operator's output o [T, H, dv] -> RMSNorm(o) * rms_w * sigmoid(g), fp64."""
     o, g, rms_w = _f64(o), _f64(g), _f64(rms_w)

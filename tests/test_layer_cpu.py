@@ -104,3 +104,37 @@ def test_prologue_outputs_are_valid_operator_inputs():
     # the second sequence's first value row sees only its own first pre-activation row
     ref = ly.swish(ws[2][:, :, 3] * xs[2][5])
     np.testing.assert_allclose(v[5], ref, rtol=1e-13)
+
+
+@pytest.mark.parametrize("L", [0, 1, 2, 3, 9])
+def test_decode_prologue_continues_the_prefill(L):
+    """The history after L tokens plus the prologue of token L in decode form
+    equals the prefill prologue's row L over L + 1 tokens, and the shifted
+    history equals the history after L + 1 tokens (lengths below the filter's
+    width included: the history starts as zeros)."""
+    H, d = 2, 6
+    x = [rng.standard_normal((L + 1, H, d)) for _ in range(4)]
+    xb = rng.standard_normal((L + 1, H))
+    w = [rng.standard_normal((H, d, 4)) for _ in range(3)]
+    A_log, dtb = rng.standard_normal(H), rng.standard_normal((H, d))
+    full = ly.layer_prologue(*x, xb, *w, A_log, dtb)
+    st = ly.conv_state(x[0][:L], x[1][:L], x[2][:L])
+    got = ly.layer_decode_prologue(x[0][L:], x[1][L:], x[2][L:], x[3][L:], xb[L:], st, *w, A_log, dtb)
+    for a, b in zip(got[:5], full):
+        np.testing.assert_allclose(a, b[L:], rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(got[5], ly.conv_state(x[0], x[1], x[2]))
+
+
+def test_conv_state_packed_and_short():
+    """Per sequence, oldest row first; an empty sequence's history is zero, a
+    one-token sequence's is (0, 0, x_0)."""
+    lens = [5, 0, 1]
+    cu = np.array([0, 5, 5, 6])
+    x = [rng.standard_normal((6, 1, 3)) for _ in range(3)]
+    st = ly.conv_state(*x, cu)
+    assert st.shape == (3, 1, 3, 3, 3)
+    for m in range(3):
+        np.testing.assert_array_equal(st[0, :, m], np.moveaxis(x[m][2:5], 0, 1))
+        np.testing.assert_array_equal(st[2, :, m, 2], x[m][5])
+    np.testing.assert_array_equal(st[1], 0.0)
+    np.testing.assert_array_equal(st[2, :, :, :2], 0.0)
