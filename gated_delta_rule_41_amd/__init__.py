@@ -81,6 +81,11 @@ def _load():
                                        P, P, P, P, P, P]
     lib.kda_layer_epilogue.restype = ctypes.c_int
     lib.kda_layer_epilogue.argtypes = [P, P, P, I64, I32, I32, ctypes.c_int, P, P]
+    lib.kda_layer_conv_state.restype = ctypes.c_int
+    lib.kda_layer_conv_state.argtypes = [P, P, P, P, I32, I64, I32, I32, ctypes.c_int, P, P]
+    lib.kda_layer_decode_prologue.restype = ctypes.c_int
+    lib.kda_layer_decode_prologue.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, ctypes.c_int,
+                                              P, P, P, P, P, P]
     lib.kda_layer_chunk_fwd_workspace_size.restype = ctypes.c_int
     lib.kda_layer_chunk_fwd_workspace_size.argtypes = [I32, I64, I32, I32, ctypes.POINTER(SZ)]
     lib.kda_layer_chunk_fwd.restype = ctypes.c_int
@@ -272,6 +277,63 @@ def layer_prologue(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, xa: tor
                                 *(_ptr(t) for t in outs), _ptr(beta), _stream(dev))
     if st != 0:
         raise KDAError(st, "kda_layer_prologue")
+    return outs[0], outs[1], outs[2], outs[3], beta
+
+
+def layer_conv_state(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor,
+                     cu_seqlens: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The convolution history after a prefill (see ``kda_layer_conv_state``):
+    [N, H, 3 (q, k, v), 3 (oldest first), d] in the pre-activations' dtype."""
+    lib = _load()
+    dev = xq.device
+    if xq.dim() != 3:
+        raise ValueError("xq must be [T, H, d]")
+    T, H, d = xq.shape
+    N = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    items = [("xq", xq, (T, H, d)), ("xk", xk, (T, H, d)), ("xv", xv, (T, H, d))]
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 >= 2 offsets")
+        items.append(("cu_seqlens", cu_seqlens, None))
+    _check(items, dev)
+    if xk.dtype != xq.dtype or xv.dtype != xq.dtype:
+        raise TypeError("xq, xk, xv must share a dtype")
+    cs = torch.empty(N, H, 3, 3, d, dtype=xq.dtype, device=dev)
+    st = lib.kda_layer_conv_state(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(cu_seqlens), N, T, H, d,
+                                  _dtype_code(xq, "xq"), _ptr(cs), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_layer_conv_state")
+    return cs
+
+
+def layer_decode_prologue(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, xa: torch.Tensor,
+                          xb: torch.Tensor, conv_state: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor,
+                          wv: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor):
+    """One token per sequence (see ``kda_layer_decode_prologue``): xq, xk, xv, xa
+    [N, H, d], xb [N, H]; ``conv_state`` [N, H, 3, 3, d] is read and shifted in
+    place. Returns (q, k, v, log_alpha, beta) for ``decode_step``."""
+    lib = _load()
+    dev = xq.device
+    if xq.dim() != 3:
+        raise ValueError("xq must be [N, H, d]")
+    N, H, d = xq.shape
+    items = [("xq", xq, (N, H, d)), ("xk", xk, (N, H, d)), ("xv", xv, (N, H, d)), ("xa", xa, (N, H, d)),
+             ("xb", xb, (N, H)), ("conv_state", conv_state, (N, H, 3, 3, d)), ("wq", wq, (H, d, 4)),
+             ("wk", wk, (H, d, 4)), ("wv", wv, (H, d, 4)), ("A_log", A_log, (H,)), ("dt_bias", dt_bias, (H, d))]
+    _check(items, dev)
+    for name, t in (("xk", xk), ("xv", xv), ("xa", xa), ("xb", xb), ("conv_state", conv_state)):
+        if t.dtype != xq.dtype:
+            raise TypeError(f"{name} must have xq's dtype")
+    for name, t in (("wq", wq), ("wk", wk), ("wv", wv), ("A_log", A_log), ("dt_bias", dt_bias)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    outs = [torch.empty(N, H, d, dtype=xq.dtype, device=dev) for _ in range(4)]
+    beta = torch.empty(N, H, dtype=xq.dtype, device=dev)
+    st = lib.kda_layer_decode_prologue(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(xa), _ptr(xb), _ptr(conv_state),
+                                       _ptr(wq), _ptr(wk), _ptr(wv), _ptr(A_log), _ptr(dt_bias), N, H, d,
+                                       _dtype_code(xq, "xq"), *(_ptr(t) for t in outs), _ptr(beta), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_layer_decode_prologue")
     return outs[0], outs[1], outs[2], outs[3], beta
 
 

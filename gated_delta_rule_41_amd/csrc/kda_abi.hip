@@ -591,6 +591,74 @@ kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, c
     return KDA_OK;
 }
 
+kda_status kda_layer_conv_state(const void* xq, const void* xk, const void* xv, const int32_t* cu_seqlens,
+                                int32_t N, int64_t T_total, int32_t H, int32_t d, kda_dtype dtype, void* conv_state,
+                                void* stream) {
+    if (!chunk_sizes_ok(N, T_total, H) || T_total * H >= (int64_t(1) << 31) || (int64_t)N * H >= (int64_t(1) << 31))
+        return KDA_ERR_SHAPE;
+    if (!cu_seqlens && N != 1) return KDA_ERR_SHAPE;
+    if (!head_ok(d, d) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!conv_state || (T_total > 0 && (!xq || !xk || !xv))) return KDA_ERR_NULL;
+    const size_t es = esize(dtype), nx = (size_t)T_total * H * d * es, ncs = (size_t)N * H * 9 * d * es;
+    const size_t ncu = cu_seqlens ? (size_t)(N + 1) * 4 : 0;
+    if (!aligned_to(xq, 2 * es) || !aligned_to(xk, 2 * es) || !aligned_to(xv, 2 * es) ||
+        !aligned_to(conv_state, 2 * es) || !aligned_to(cu_seqlens, 4))
+        return KDA_ERR_ALIGN;
+    if (overlaps(conv_state, ncs, xq, nx) || overlaps(conv_state, ncs, xk, nx) || overlaps(conv_state, ncs, xv, nx) ||
+        overlaps(conv_state, ncs, cu_seqlens, ncu))
+        return KDA_ERR_ALIAS;
+    LayerArgs a{};
+    a.N = N;
+    a.T = (int)T_total;
+    a.H = H;
+    a.D = d;
+    a.f32 = dtype == KDA_F32;
+    a.cu = cu_seqlens;
+    a.xq = xq, a.xk = xk, a.xv = xv;
+    a.cs = conv_state;
+    return launch_layer_conv_state(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_layer_decode_prologue(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
+                                     void* conv_state, const float* wq, const float* wk, const float* wv,
+                                     const float* A_log, const float* dt_bias, int32_t N, int32_t H, int32_t d,
+                                     kda_dtype dtype, void* q, void* k, void* v, void* log_alpha, void* beta,
+                                     void* stream) {
+    if (N <= 0 || H <= 0 || H > 65536 || (int64_t)N * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    if (!head_ok(d, d) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!xq || !xk || !xv || !xa || !xb || !conv_state || !wq || !wk || !wv || !A_log || !dt_bias || !q || !k ||
+        !v || !log_alpha || !beta)
+        return KDA_ERR_NULL;
+    const size_t es = esize(dtype), NH = (size_t)N * H;
+    const size_t nx = NH * d * es, nb = NH * es, ncs = NH * 9 * d * es, nw = (size_t)H * d * 16, nh = (size_t)H * 4,
+                 nd = (size_t)H * d * 4;
+    const void* ins[11] = {xq, xk, xv, xa, xb, wq, wk, wv, A_log, dt_bias, conv_state};
+    const size_t nin[11] = {nx, nx, nx, nx, nb, nw, nw, nw, nh, nd, ncs};
+    void* outs[5] = {q, k, v, log_alpha, beta};
+    const size_t nout[5] = {nx, nx, nx, nx, nb};
+    for (int i = 0; i < 11; ++i)  // [N, H, d] tensors and the history move in channel pairs
+        if (!aligned_to(ins[i], i < 4 || i == 10 ? 2 * es : i == 4 ? es : 4)) return KDA_ERR_ALIGN;
+    for (int i = 0; i < 10; ++i)  // the history is updated in place
+        if (overlaps(conv_state, ncs, ins[i], nin[i])) return KDA_ERR_ALIAS;
+    for (int i = 0; i < 5; ++i) {
+        if (!aligned_to(outs[i], i < 4 ? 2 * es : es)) return KDA_ERR_ALIGN;
+        for (int j = 0; j < 11; ++j)
+            if (overlaps(outs[i], nout[i], ins[j], nin[j])) return KDA_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], nout[i], outs[j], nout[j])) return KDA_ERR_ALIAS;
+    }
+    LayerArgs a{};
+    a.N = N;
+    a.H = H;
+    a.D = d;
+    a.f32 = dtype == KDA_F32;
+    a.xq = xq, a.xk = xk, a.xv = xv, a.xa = xa, a.xb = xb;
+    a.wq = wq, a.wk = wk, a.wv = wv, a.A_log = A_log, a.dt_bias = dt_bias;
+    a.q = q, a.k = k, a.v = v, a.la = log_alpha, a.beta = beta;
+    a.cs = conv_state;
+    return launch_layer_decode_prologue(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_layer_epilogue(const float* o, const void* g, const float* rms_w, int64_t T_total, int32_t H,
                               int32_t dv, kda_dtype dtype, void* y, void* stream) {
     if (T_total < 0 || T_total >= (int64_t(1) << 31) || H <= 0 || H > 65536 || T_total * H >= (int64_t(1) << 31))

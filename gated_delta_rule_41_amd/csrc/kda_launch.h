@@ -73,7 +73,11 @@ struct LayerArgs {
     const void* g;
     const float* rms_w;
     void* y;
+    // decoding: the convolution's history [N][H][q, k, v][3][D]
+    void* cs = nullptr;
 };
+hipError_t launch_layer_conv_state(const LayerArgs& a, hipStream_t st);
+hipError_t launch_layer_decode_prologue(const LayerArgs& a, hipStream_t st);
 hipError_t launch_layer_prologue(const LayerArgs& a, hipStream_t st);
 hipError_t launch_layer_epilogue(const LayerArgs& a, hipStream_t st);
 

@@ -112,6 +112,103 @@ __global__ __launch_bounds__(256) void layer_epilogue_kernel(const float* __rest
     }
 }
 
+// The convolution's history after each sequence, for one-token decoding: the
+// last three rows of xq, xk, xv (oldest first, zero where the sequence is
+// shorter), [N][H][q, k, v][3][D]. One wave per (sequence, head).
+template <int D, typename TE>
+__global__ __launch_bounds__(256) void layer_conv_state_kernel(PrologueIn<TE> in, const int32_t* __restrict__ cu,
+                                                               int N, int T, int H, TE* __restrict__ cs) {
+    constexpr int PER = D / 64;
+    using PR = Pair<TE, PER>;
+    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= N * H) return;  // uniform over the wave
+    const int n = item / H, h = item - n * H, c0 = PER * (threadIdx.x & 63);
+    const int start = cu != nullptr ? cu[n] : 0, end = cu != nullptr ? cu[n + 1] : T;
+    const TE* xs[3] = {in.xq, in.xk, in.xv};
+    TE* dst = cs + (int64_t)item * 3 * (CONV_W - 1) * D + c0;
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int i = 0; i < CONV_W - 1; ++i) {
+            const int t = end - (CONV_W - 1) + i;
+            float x[PER] = {};
+            if (t >= start) PR::ld(xs[m] + ((int64_t)t * H + h) * D + c0, x);
+            PR::st(dst + (m * (CONV_W - 1) + i) * D, x);
+        }
+}
+
+// One token per sequence after the history cs: the same prologue arithmetic,
+// the window being the history's three rows and the new one; the history is
+// then shifted by the new row in place. One wave per (sequence, head).
+template <int D, typename TE>
+__global__ __launch_bounds__(256) void layer_decode_prologue_kernel(
+    PrologueIn<TE> in, TE* __restrict__ cs, const float* __restrict__ wq, const float* __restrict__ wk,
+    const float* __restrict__ wv, const float* __restrict__ A_log, const float* __restrict__ dt_bias, int NH, int H,
+    TE* __restrict__ q, TE* __restrict__ k, TE* __restrict__ v, TE* __restrict__ la, TE* __restrict__ beta) {
+    constexpr int PER = D / 64;
+    using PR = Pair<TE, PER>;
+    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= NH) return;  // uniform over the wave
+    const int h = item % H, l = threadIdx.x & 63, c0 = PER * l;
+    TE* hist = cs + (int64_t)item * 3 * (CONV_W - 1) * D + c0;
+    const int64_t ro = (int64_t)item * D + c0;
+    PrologueWindow<D, 1, TE> pw;
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int i = 0; i < CONV_W - 1; ++i) PR::ld(hist + (m * (CONV_W - 1) + i) * D, pw.win[m][i]);
+    PR::ld(in.xq + ro, pw.win[0][CONV_W - 1]);
+    PR::ld(in.xk + ro, pw.win[1][CONV_W - 1]);
+    PR::ld(in.xv + ro, pw.win[2][CONV_W - 1]);
+    PR::ld(in.xa + ro, pw.xg[0]);
+    pw.xbl = ld_in(in.xb, item);
+    ConvFilters<D> f;
+    f.load(wq, wk, wv, A_log, dt_bias, h, c0);
+    const float bl = pw.compute(f, 0, 1, [](int) { return INT_MIN; },  // every tap reads the window
+                                [&](int, const float (&oq)[PER], const float (&ok)[PER], const float (&ov)[PER],
+                                    const float (&og)[PER]) {
+                                    PR::st(q + ro, oq);
+                                    PR::st(k + ro, ok);
+                                    PR::st(v + ro, ov);
+                                    PR::st(la + ro, og);
+                                });
+    if (l == 0) st_out(beta, item, bl);
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int i = 0; i < CONV_W - 1; ++i) PR::st(hist + (m * (CONV_W - 1) + i) * D, pw.win[m][i + 1]);
+}
+
+template <int D, typename TE>
+static hipError_t launch_conv_state_t(const LayerArgs& a, hipStream_t st) {
+    const int64_t items = (int64_t)a.N * a.H;
+    const PrologueIn<TE> in{(const TE*)a.xq, (const TE*)a.xk, (const TE*)a.xv, nullptr, nullptr};
+    hipLaunchKernelGGL((layer_conv_state_kernel<D, TE>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, in,
+                       a.cu, a.N, a.T, a.H, (TE*)a.cs);
+    return hipGetLastError();
+}
+
+hipError_t launch_layer_conv_state(const LayerArgs& a, hipStream_t st) {
+    if (a.D == 128) return a.f32 ? launch_conv_state_t<128, float>(a, st) : launch_conv_state_t<128, uint16_t>(a, st);
+    return a.f32 ? launch_conv_state_t<64, float>(a, st) : launch_conv_state_t<64, uint16_t>(a, st);
+}
+
+template <int D, typename TE>
+static hipError_t launch_decode_prologue_t(const LayerArgs& a, hipStream_t st) {
+    const int64_t items = (int64_t)a.N * a.H;
+    const PrologueIn<TE> in{(const TE*)a.xq, (const TE*)a.xk, (const TE*)a.xv, (const TE*)a.xa, (const TE*)a.xb};
+    hipLaunchKernelGGL((layer_decode_prologue_kernel<D, TE>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st,
+                       in, (TE*)a.cs, a.wq, a.wk, a.wv, a.A_log, a.dt_bias, (int)items, a.H, (TE*)a.q, (TE*)a.k,
+                       (TE*)a.v, (TE*)a.la, (TE*)a.beta);
+    return hipGetLastError();
+}
+
+hipError_t launch_layer_decode_prologue(const LayerArgs& a, hipStream_t st) {
+    if (a.D == 128)
+        return a.f32 ? launch_decode_prologue_t<128, float>(a, st) : launch_decode_prologue_t<128, uint16_t>(a, st);
+    return a.f32 ? launch_decode_prologue_t<64, float>(a, st) : launch_decode_prologue_t<64, uint16_t>(a, st);
+}
+
 template <int D, typename TE>
 static hipError_t launch_prologue_t(const LayerArgs& a, hipStream_t st) {
     const int64_t blocks = (int64_t)((a.T + PT - 1) / PT) * a.H;  // (tile, head), head fastest

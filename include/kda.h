@@ -222,6 +222,46 @@ kda_status kda_layer_prologue(const void* xq, const void* xk, const void* xv, co
                               void* log_alpha, void* beta, void* stream);
 
 /*
+ * The layer's convolution history after a prefill, for one-token decoding
+ * (the short convolution of kda_layer_prologue is causal, so the next token
+ * needs the last three pre-activation rows of q, k, v of its sequence):
+ *
+ *   conv_state[n, h, m, i, :] = x_m[end_n - 3 + i, h, :]   (0 where before start_n)
+ *
+ *   xq, xk, xv  [T_total, H, d] dtype (the prefill's pre-activations)
+ *   cu_seqlens  as kda_chunk_fwd (NULL = one sequence, N = 1)
+ *   conv_state  [N, H, 3 (q, k, v), 3 (oldest first), d] dtype (output)
+ * The [.., d] tensors must be aligned to two elements (KDA_ERR_ALIGN); the
+ * output may not overlap an input (KDA_ERR_ALIAS). One kernel is enqueued.
+ */
+kda_status kda_layer_conv_state(const void* xq, const void* xk, const void* xv, const int32_t* cu_seqlens,
+                                int32_t N, int64_t T_total, int32_t H, int32_t d, kda_dtype dtype, void* conv_state,
+                                void* stream);
+
+/*
+ * kda_layer_prologue for one new token per sequence after the history
+ * conv_state (kda_layer_conv_state's layout): the convolution reads the
+ * history's three rows, then the new row; the history is then shifted by the
+ * new row, in place. With kda_decode_step and kda_layer_epilogue this is the
+ * layer's decode step; the results equal those of kda_layer_prologue over the
+ * whole sequence at its last row.
+ *
+ *   xq, xk, xv, xa  [N, H, d] dtype;  xb [N, H] dtype (one token per sequence)
+ *   conv_state      [N, H, 3, 3, d] dtype (in and out)
+ *   wq ... dt_bias  as kda_layer_prologue
+ *   q, k, v, log_alpha [N, H, d] dtype; beta [N, H] dtype (outputs, ready for
+ *                   kda_decode_step)
+ * Alignment and aliasing as kda_layer_prologue (conv_state as the [.., d]
+ * tensors; it may not overlap any other argument). N * H < 2^31. One kernel is
+ * enqueued.
+ */
+kda_status kda_layer_decode_prologue(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
+                                     void* conv_state, const float* wq, const float* wk, const float* wv,
+                                     const float* A_log, const float* dt_bias, int32_t N, int32_t H, int32_t d,
+                                     kda_dtype dtype, void* q, void* k, void* v, void* log_alpha, void* beta,
+                                     void* stream);
+
+/*
  * Bytes of device workspace kda_layer_chunk_fwd needs (host call, no device
  * access): kda_chunk_fwd's for bf16 inputs, plus 32 KiB per chunk-head at
  * d = 128 (16 KiB at d = 64) for the q, k rows of chunks that take the exact

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
                      "kda_chunk_fwd_timed",
                      "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_dplr_chunk_fwd",
                      "kda_dplr_chunk_fwd_workspace_size", "kda_layer_chunk_fwd", "kda_layer_chunk_fwd_workspace_size",
-                     "kda_layer_epilogue", "kda_layer_prologue",
+                     "kda_layer_conv_state", "kda_layer_decode_prologue", "kda_layer_epilogue", "kda_layer_prologue",
                      "kda_status_str"]
     for nm in names:
         assert hasattr(lib, nm), nm
@@ -335,3 +335,43 @@ def test_layer_fwd_workspace_and_validation():
     assert layer_fwd_call(xq=x, o=x + 64) == ALIAS
     y = f()
     assert layer_fwd_call(o=y, fs=y + 256) == ALIAS
+
+
+def test_layer_decode_validation():
+    """The convolution history and the one-token prologue refuse malformed calls
+    before any launch."""
+    f = Fake()
+    P = ctypes.c_void_p
+    lib = kda._load()
+
+    def cs_call(**over):
+        a = dict(xq=f(), xk=f(), xv=f(), cu=None, N=1, T=10, H=2, d=64, dt=BF16, cs=f())
+        a.update(over)
+        return lib.kda_layer_conv_state(P(a["xq"]), P(a["xk"]), P(a["xv"]), P(a["cu"]), a["N"], a["T"], a["H"],
+                                        a["d"], a["dt"], P(a["cs"]), None)
+
+    def dp_call(**over):
+        a = dict(xq=f(), xk=f(), xv=f(), xa=f(), xb=f(), cs=f(), wq=f(), wk=f(), wv=f(), A_log=f(), dtb=f(), N=3,
+                 H=2, d=64, dt=BF16, q=f(), k=f(), v=f(), la=f(), beta=f())
+        a.update(over)
+        return lib.kda_layer_decode_prologue(*(P(a[x]) for x in ("xq", "xk", "xv", "xa", "xb", "cs", "wq", "wk",
+                                                                 "wv", "A_log", "dtb")),
+                                             a["N"], a["H"], a["d"], a["dt"],
+                                             *(P(a[x]) for x in ("q", "k", "v", "la", "beta")), None)
+
+    assert cs_call(cs=None) == NULL
+    assert cs_call(xq=None) == NULL
+    assert cs_call(N=2) == SHAPE
+    assert cs_call(d=96) == UNSUP
+    assert cs_call(cs=f(2)) == ALIGN
+    x = f()
+    assert cs_call(xq=x, cs=x + 64) == ALIAS
+    assert dp_call(N=0) == SHAPE
+    assert dp_call(cs=None) == NULL
+    assert dp_call(d=32) == UNSUP
+    assert dp_call(cs=f(2)) == ALIGN
+    assert dp_call(q=f(2)) == ALIGN
+    y = f()
+    assert dp_call(xq=y, cs=y + 64) == ALIAS  # the history is written in place
+    z = f()
+    assert dp_call(cs=z, q=z + 128) == ALIAS

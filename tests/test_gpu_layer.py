@@ -178,3 +178,77 @@ def test_fused_layer_forward(shape):
         e1, e2 = err(o, oo), err(S, So)
         say(f"    fused vs oracle: o {e1:.2e}  final state {e2:.2e}  (bar {bar:.2e})")
         assert e1 <= bar and e2 <= bar
+
+
+def split_last(c, S):
+    """Packed rows of c without each sequence's last S tokens (the prefill), and
+    the S decode steps' rows [N, H, ...] each."""
+    cu = [0]
+    for L in c.lengths:
+        cu.append(cu[-1] + L)
+    pre = [i for n in range(c.N) for i in range(cu[n], cu[n + 1] - S)]
+    dec = [[cu[n + 1] - S + s for n in range(c.N)] for s in range(S)]
+    idx = torch.tensor(pre, dtype=torch.long, device=DEV)
+    lens = [L - S for L in c.lengths]
+    cu_pre = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=DEV)
+    return idx, [torch.tensor(d, dtype=torch.long, device=DEV) for d in dec], cu_pre
+
+
+@pytest.mark.parametrize("d,dt", [(128, torch.bfloat16), (64, torch.float32)])
+def test_conv_state(d, dt):
+    """The history after each sequence: its last three rows, oldest first, zero
+    where the sequence is shorter (lengths 0, 1, 2 included); an exact copy."""
+    c = ki.make_layer("varlen-16", DEV, lengths=[0, 1, 2, 70, 5], H=3, d=d, dtype=dt)
+    say(f"[layer] convolution history d={d} {dt}")
+    cs = kda.layer_conv_state(c.xq, c.xk, c.xv, c.cu_seqlens)
+    torch.cuda.synchronize()
+    ref = torch.from_numpy(ly.conv_state(c.xq, c.xk, c.xv, host(c.cu_seqlens))).to(dt)
+    assert torch.equal(cs.cpu(), ref)
+
+
+@pytest.mark.parametrize("d,dt", [(128, torch.bfloat16), (64, torch.bfloat16), (128, torch.float32)])
+def test_decode_prologue(d, dt):
+    """One new token per sequence after the history: element-wise against the
+    oracle (bf16: within one step; fp32: 1e-5 of the RMS), and the shifted
+    history exactly."""
+    c = ki.make_layer("varlen-16", DEV, lengths=[5, 1, 0, 40], H=3, d=d, dtype=dt)
+    cs = kda.layer_conv_state(c.xq, c.xk, c.xv, c.cu_seqlens)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    new = [torch.randn(c.N, c.H, d, generator=g, device=DEV).to(dt) for _ in range(4)]
+    xb = torch.randn(c.N, c.H, generator=g, device=DEV).to(dt)
+    cs_before = cs.cpu()
+    say(f"[layer] decode prologue d={d} {dt}")
+    got = kda.layer_decode_prologue(*new, xb, cs, c.wq, c.wk, c.wv, c.A_log, c.dt_bias)
+    torch.cuda.synchronize()
+    ref = ly.layer_decode_prologue(*new, xb, cs_before, c.wq, c.wk, c.wv, c.A_log, c.dt_bias)
+    check_outputs("q, k, v, log_alpha, beta", got, ref[:5], dt == torch.bfloat16)
+    assert torch.equal(cs.cpu(), torch.from_numpy(ref[5]).to(dt))
+
+
+def test_layer_decode_continues_prefill():
+    """A served layer (fp32): prefill of each sequence but its last four tokens
+    (prologue, kda_chunk_fwd, history), then four one-token steps (decode
+    prologue, kda_decode_step in place, epilogue). Every step's output and the
+    final states against the fp64 layer over the whole sequences (bar 1e-4);
+    lengths 0 and 1 before decoding included."""
+    S = 4
+    c = ki.make_layer("prefill-4k", DEV, lengths=[41, 68, 5, 4], H=2, d=64, dtype=torch.float32, s0_std=0.02)
+    idx, dec, cu_pre = split_last(c, S)
+    pre = [x.index_select(0, idx) for x in (c.xq, c.xk, c.xv, c.xa, c.xb)]
+    q, k, v, la, b = kda.layer_prologue(*pre, c.wq, c.wk, c.wv, c.A_log, c.dt_bias, cu_pre)
+    _, state = kda.chunk_fwd(q, k, v, la, b, c.initial_state, cu_pre)
+    cs = kda.layer_conv_state(pre[0], pre[1], pre[2], cu_pre)
+    ys = []
+    for s in range(S):
+        step = [x.index_select(0, dec[s]) for x in (c.xq, c.xk, c.xv, c.xa, c.xb, c.xg)]
+        qd, kd, vd, lad, bd = kda.layer_decode_prologue(*step[:5], cs, c.wq, c.wk, c.wv, c.A_log, c.dt_bias)
+        od = kda.decode_step(qd, kd, vd, lad, bd, state)
+        ys.append(kda.layer_epilogue(od, step[5], c.rms_w))
+    torch.cuda.synchronize()
+    y_ref, S_ref, _ = ly.layer(c.xq, c.xk, c.xv, c.xa, c.xb, c.xg, c.wq, c.wk, c.wv, c.A_log, c.dt_bias, c.rms_w,
+                               host(c.initial_state), host(c.cu_seqlens))
+    rows = np.stack([y_ref[dec[s].cpu().numpy()] for s in range(S)])
+    ey, es = err(torch.stack(ys), rows), err(state, S_ref)
+    say(f"[layer] decode after prefill, {S} steps: y {ey:.2e}  final state {es:.2e}")
+    assert ey <= 1e-4 and es <= 1e-4
