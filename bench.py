@@ -344,6 +344,49 @@ def time_layer(kda, lc, steps, warmup, hip, stream):
     return out
 
 
+def time_layer_decode(kda, ki, steps, warmup, hip, stream, N=256, H=32, d=128):
+    """The layer's decode step at decode-256 size (one bf16 token per sequence):
+    decode prologue (history in place), kda_decode_step (fp32 state in place),
+    epilogue, all through the C ABI between two events around the loop.
+    Returns ms per step."""
+    import torch
+    lib = kda._load()
+    lc = ki.make_layer("decode-256", "cuda:0", lengths=[1] * N, H=H, d=d, s0_std=0.0)  # one token's pre-activations each
+    dev = lc.xq.device
+    cs = torch.zeros(N, H, 3, 3, d, dtype=torch.bfloat16, device=dev)
+    state = 0.02 * torch.randn(N, H, d, d, device=dev)
+    q, k, v, la = (torch.empty(N, H, d, dtype=torch.bfloat16, device=dev) for _ in range(4))
+    beta = torch.empty(N, H, dtype=torch.bfloat16, device=dev)
+    o = torch.empty(N, H, d, dtype=torch.float32, device=dev)
+    y = torch.empty(N, H, d, dtype=torch.bfloat16, device=dev)
+    P = ctypes.c_void_p
+    bf = kda.KDA_BF16
+
+    def ptr(t):
+        return P(t.data_ptr())
+    pro = (*(ptr(t) for t in (lc.xq, lc.xk, lc.xv, lc.xa, lc.xb, cs, lc.wq, lc.wk, lc.wv, lc.A_log, lc.dt_bias)),
+           N, H, d, bf, *(ptr(t) for t in (q, k, v, la, beta)), P(stream))
+    dec = (*(ptr(t) for t in (q, k, v, la, beta, state)), N, H, d, d, bf, bf, kda.KDA_F32, ptr(o), P(stream))
+    epi = (ptr(o), ptr(lc.xg), ptr(lc.rms_w), N, H, d, bf, ptr(y), P(stream))
+
+    def step():
+        if lib.kda_layer_decode_prologue(*pro) != 0 or lib.kda_decode_step(*dec) != 0 or \
+                lib.kda_layer_epilogue(*epi) != 0:
+            raise RuntimeError("layer decode step failed")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = Events(hip, 2)
+    ev.record(0, stream)
+    for _ in range(steps):
+        step()
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(0, 1) / steps
+    ev.close()
+    return ms
+
+
 def time_decode(kda, dec, steps, warmup, hip, stream):
     import torch
     state = dec["state"]
@@ -612,6 +655,10 @@ def main(argv=None):
                                   "frac": round(epi_b / (lt["epilogue"] * 1e-3) / PEAK_HBM, 4),
                                   "traffic": traffic_from_profiles("layer_epilogue", TH)}}
         del lc
+        ld_ms = time_layer_decode(kda, ki, 200, 50, hip, stream)
+        out["layer"]["decode_step"] = {
+            "workload": "decode-256 pre-activations (bf16), 256 sequences x 32 heads, fp32 states",
+            "ms_per_step": round(ld_ms, 5), "tokens_per_s": round(256 / (ld_ms * 1e-3), 1)}
 
     if not args.no_decode:
         dec_inputs = min(args.decode_steps, 100)  # distinct per-step inputs, cycled
