@@ -551,6 +551,9 @@ def main(argv=None):
     ap.add_argument("--no-dplr", action="store_true", help="skip the general-DPLR comparison")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward")
     ap.add_argument("--no-layer", action="store_true", help="skip the layer prologue/epilogue")
+    ap.add_argument("--no-layer-decode", action="store_true",
+                    help="skip the layer's decode step (its epilogue launches are far smaller than the prefill's, "
+                         "and a profile averages them together)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run the counter calibration copy kernel over MIB MiB")
     args = ap.parse_args(argv)
@@ -655,10 +658,11 @@ def main(argv=None):
                                   "frac": round(epi_b / (lt["epilogue"] * 1e-3) / PEAK_HBM, 4),
                                   "traffic": traffic_from_profiles("layer_epilogue", TH)}}
         del lc
-        ld_ms = time_layer_decode(kda, ki, 200, 50, hip, stream)
-        out["layer"]["decode_step"] = {
-            "workload": "decode-256 pre-activations (bf16), 256 sequences x 32 heads, fp32 states",
-            "ms_per_step": round(ld_ms, 5), "tokens_per_s": round(256 / (ld_ms * 1e-3), 1)}
+        if not args.no_layer_decode:
+            ld_ms = time_layer_decode(kda, ki, 200, 50, hip, stream)
+            out["layer"]["decode_step"] = {
+                "workload": "decode-256 pre-activations (bf16), 256 sequences x 32 heads, fp32 states",
+                "ms_per_step": round(ld_ms, 5), "tokens_per_s": round(256 / (ld_ms * 1e-3), 1)}
 
     if not args.no_decode:
         dec_inputs = min(args.decode_steps, 100)  # distinct per-step inputs, cycled
