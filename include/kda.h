@@ -24,7 +24,18 @@
  *  - All tensor pointers are DEVICE pointers (HIP, gfx950) unless marked host.
  *    Every tensor is dense and contiguous in the layout given; base addresses
  *    must be 16-byte aligned, except beta and cu_seqlens, which need only the
- *    alignment of their element type (KDA_ERR_ALIGN otherwise).
+ *    alignment of their element type (KDA_ERR_ALIGN otherwise). The layer
+ *    entry points (kda_layer_*) state their own, weaker alignment rules.
+ *
+ * Entry points
+ * ------------
+ *  - the operator: kda_chunk_fwd (prefill), kda_decode_step, kda_chunk_bwd,
+ *    with their workspace sizes, and kda_dplr_chunk_fwd (the general DPLR
+ *    transition, for comparison);
+ *  - the layer around it: kda_layer_prologue, kda_layer_epilogue,
+ *    kda_layer_chunk_fwd (the prologue fused into the prefill), and for
+ *    decoding kda_layer_conv_state and kda_layer_decode_prologue;
+ *  - kda_status_str, kda_abi_version.
  *  - Layouts are token-major: q, k, log_alpha [T, H, dk]; v [T, H, dv];
  *    beta [T, H]; o [T, H, dv]; states [N, H, dk, dv] fp32 (dv fastest).
  *  - No query scaling is applied (callers pre-scale q if they want 1/sqrt(dk)).
