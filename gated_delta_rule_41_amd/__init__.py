@@ -20,7 +20,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "workspace_size", "bwd_workspace_size", "dplr_chunk_fwd",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "decode_step", "workspace_size", "bwd_workspace_size", "dplr_chunk_fwd",
            "dplr_workspace_size", "abi_version", "status_str", "library_path", "KDAError", "CHUNK"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +64,9 @@ def _load():
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, SZ, P]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P]
     lib.kda_chunk_fwd_timed.restype = ctypes.c_int
     lib.kda_chunk_fwd_timed.argtypes = lib.kda_chunk_fwd.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
     lib.kda_dplr_chunk_fwd_workspace_size.restype = ctypes.c_int
@@ -212,6 +215,51 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     if st != 0:
         raise KDAError(st, "kda_chunk_fwd")
     return o, final_state
+
+
+NOALLOC_WORKSPACE_BYTES = 64 * 1024 * 1024  # KDA_NOALLOC_WORKSPACE_BYTES in include/kda.h
+
+
+def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+                      beta: torch.Tensor, o: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                      cu_seqlens: Optional[torch.Tensor] = None,
+                      final_state: Optional[torch.Tensor] = None) -> None:
+    """``chunk_fwd`` through ``kda_chunk_fwd_noalloc``: the library's static
+    per-device workspace instead of an allocated one, and caller-supplied
+    outputs (o [T, H, dv] fp32 or bf16; final_state [N, H, dk, dv] fp32 or
+    None), so that the call allocates nothing. Shapes are checked as in
+    ``chunk_fwd``."""
+    lib = _load()
+    dev = q.device
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, log_alpha must be [T, H, dk] and v [T, H, dv]")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    items = [("q", q, (T, H, dk)), ("k", k, (T, H, dk)), ("v", v, (T, H, dv)),
+             ("log_alpha", log_alpha, (T, H, dk)), ("beta", beta, (T, H)), ("o", o, (T, H, dv))]
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 >= 2 offsets")
+        items.append(("cu_seqlens", cu_seqlens, None))
+        N = cu_seqlens.numel() - 1
+    else:
+        N = 1
+    if initial_state is not None:
+        items.append(("initial_state", initial_state, (N, H, dk, dv)))
+    if final_state is not None:
+        items.append(("final_state", final_state, (N, H, dk, dv)))
+    _check(items, dev)
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != log_alpha.dtype:
+        raise TypeError("q, k, v must share a dtype; log_alpha and beta must share a dtype")
+    st = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+                                   _ptr(cu_seqlens), N, T, H, dk, dv, _dtype_code(q, "q"),
+                                   _dtype_code(log_alpha, "log_alpha"), _dtype_code(o, "o"), _ptr(o),
+                                   _ptr(final_state), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_fwd_noalloc")
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,

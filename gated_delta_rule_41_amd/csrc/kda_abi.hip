@@ -97,7 +97,33 @@ WsPlan plan_workspace_dplr(int64_t NC, int H, int D) {
 
 using namespace kda;
 
+// Workspace of kda_chunk_fwd_noalloc: one copy per device, allocated by the HIP
+// runtime when this code object is loaded and held until the process ends.
+// Host code never uses this name as an address (on the host it names a
+// stand-in); it uses the device address cached by noalloc_scratch().
+static __device__ __align__(256) char scratch[KDA_NOALLOC_WORKSPACE_BYTES];
+
 namespace {
+
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current (each device holds its own copy at its own address).
+hipError_t noalloc_scratch(void** out) {
+    constexpr int MAXDEV = 64;
+    static std::atomic<void*> addr[MAXDEV];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAXDEV) return hipErrorInvalidDevice;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev].store(p, std::memory_order_release);  // a race stores the same address twice
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned_to(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -715,6 +741,24 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
     a.out_f32 = out_dtype == KDA_F32;
     if (launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
+}
+
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* log_alpha,
+                                 const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                                 int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
+                                 kda_dtype in_dtype, kda_dtype gate_dtype, kda_dtype out_dtype, void* o,
+                                 float* final_state, void* stream) {
+    // A call whose workspace would not fit the scratch is refused before any
+    // device call. Sizes the workspace query rejects go to kda_chunk_fwd's own
+    // validation with no workspace, which reports them exactly as it would.
+    size_t need = 0;
+    const bool sized = kda_chunk_fwd_workspace_size(N, T_total, H, dk, dv, in_dtype, &need) == KDA_OK;
+    if (sized && need > (size_t)KDA_NOALLOC_WORKSPACE_BYTES) return KDA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (sized && noalloc_scratch(&ws) != hipSuccess) return KDA_ERR_HIP;
+    return kda_chunk_fwd_timed(q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, T_total, H, dk, dv,
+                               in_dtype, gate_dtype, out_dtype, o, final_state, ws,
+                               sized ? (size_t)KDA_NOALLOC_WORKSPACE_BYTES : 0, stream, nullptr);
 }
 
 }  // extern "C"

@@ -31,7 +31,8 @@
  * ------------
  *  - the operator: kda_chunk_fwd (prefill), kda_decode_step, kda_chunk_bwd,
  *    with their workspace sizes, and kda_dplr_chunk_fwd (the general DPLR
- *    transition, for comparison);
+ *    transition, for comparison); kda_chunk_fwd_noalloc (the prefill with a
+ *    static workspace, for callers that cannot allocate);
  *  - the layer around it: kda_layer_prologue, kda_layer_epilogue,
  *    kda_layer_chunk_fwd (the prologue fused into the prefill), and for
  *    decoding kda_layer_conv_state and kda_layer_decode_prologue;
@@ -51,7 +52,9 @@
  *  - log_alpha must be finite (<= 0 for the overflow guarantees; 0 is allowed).
  *    Non-finite inputs give undefined (typically NaN) outputs; inputs are not scanned.
  *  - Ownership: the caller owns every buffer. The library never allocates or
- *    frees device memory and keeps no pointer after a call returns.
+ *    frees device memory and keeps no pointer after a call returns (the one
+ *    exception is the static workspace of kda_chunk_fwd_noalloc, which the
+ *    HIP runtime allocates with the library's code on each device).
  *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream) and the call returns without synchronising. Buffers must stay
  *    valid until the stream has passed the enqueued work. No host<->device
@@ -61,7 +64,9 @@
  *    a launch failure. No C++ exception crosses this boundary.
  *  - Thread safety: every entry point may be called from several host threads
  *    at once; calls on one stream run in order. The library holds no mutable
- *    global state besides a lazily filled, read-only device-properties cache.
+ *    global state besides lazily filled, read-only caches (kernel attributes
+ *    set per device; the static scratch's address per device), except the
+ *    static scratch of kda_chunk_fwd_noalloc (see there).
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -157,6 +162,39 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
                                int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype gate_dtype,
                                kda_dtype out_dtype, void* o, float* final_state, void* workspace,
                                size_t workspace_bytes, void* stream, void* const* events);
+
+/* Largest workspace kda_chunk_fwd_noalloc serves from its static scratch: 64 MiB. */
+#define KDA_NOALLOC_WORKSPACE_BYTES (64 * 1024 * 1024)
+
+/*
+ * kda_chunk_fwd without a caller-supplied workspace and without any device
+ * allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). The
+ * caller still passes every input and output.
+ *
+ * The workspace is a static device array of KDA_NOALLOC_WORKSPACE_BYTES that
+ * the library holds on each device it runs on until the process ends; the
+ * current device's copy is used (stream must belong to the current device).
+ * Its address is looked up once per device, on the first call there. The
+ * call neither allocates nor frees device memory.
+ *
+ * Arguments, results, validation and determinism are those of kda_chunk_fwd.
+ * In addition, KDA_ERR_WORKSPACE is returned, before any device call, when
+ * kda_chunk_fwd_workspace_size(N, T_total, H, dk, dv, in_dtype) exceeds
+ * KDA_NOALLOC_WORKSPACE_BYTES (with bf16 inputs at dk = dv = 128: 74,240 bytes
+ * per chunk-head, so at most 903 chunk-heads, e.g. H = 32 and 28 chunks of
+ * 64 tokens; fp32 inputs need about 3.3 times as much per chunk-head).
+ * Every call on one device shares that device's scratch, and each call leaves
+ * its contents behind; nothing in it needs to start at zero. Calls that
+ * overlap in time on one device (on different streams, or from different host
+ * threads without ordering) race on the scratch and give undefined results;
+ * calls in order on one stream are safe.
+ */
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* log_alpha,
+                                 const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                                 int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
+                                 kda_dtype in_dtype, kda_dtype gate_dtype, kda_dtype out_dtype, void* o,
+                                 float* final_state, void* stream);
 
 /*
  * Bytes of device workspace kda_chunk_bwd needs (host call, no device access):

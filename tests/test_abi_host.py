@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     lib = kda._load()
     names = declared_functions()
     assert names == ["kda_abi_version", "kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd",
-                     "kda_chunk_fwd_timed",
+                     "kda_chunk_fwd_noalloc", "kda_chunk_fwd_timed",
                      "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_dplr_chunk_fwd",
                      "kda_dplr_chunk_fwd_workspace_size", "kda_layer_chunk_fwd", "kda_layer_chunk_fwd_workspace_size",
                      "kda_layer_conv_state", "kda_layer_decode_prologue", "kda_layer_epilogue", "kda_layer_prologue",
@@ -375,3 +375,21 @@ def test_layer_decode_validation():
     assert dp_call(xq=y, cs=y + 64) == ALIAS  # the history is written in place
     z = f()
     assert dp_call(cs=z, q=z + 128) == ALIAS
+
+
+def test_noalloc_refuses_oversized_and_bad_shapes_on_host():
+    """kda_chunk_fwd_noalloc refuses a call whose workspace exceeds its static
+    scratch (KDA_ERR_WORKSPACE) and bad sizes (as kda_chunk_fwd does) before
+    any device call, so these run without a GPU."""
+    import ctypes as C
+    lib = kda._load()
+    f = Fake()
+    def call(N, T, H, d, cu=None):
+        return lib.kda_chunk_fwd_noalloc(f(), f(), f(), f(), f(), None, cu, N, T, H, d, d, BF16, BF16, F32,
+                                         f(), f(), None)
+    assert kda.workspace_size(1, 29 * 64, 32, 128, 128) > kda.NOALLOC_WORKSPACE_BYTES
+    assert kda.workspace_size(1, 28 * 64, 32, 128, 128) <= kda.NOALLOC_WORKSPACE_BYTES
+    assert call(1, 29 * 64, 32, 128) == WORKSPACE
+    assert call(1, 1 << 20, 32, 128) == WORKSPACE
+    assert call(0, 100, 32, 128) == SHAPE
+    assert call(1, 100, 2, 96) == UNSUP
