@@ -62,8 +62,8 @@ WsPlan plan_workspace(int64_t NC, int H, int D, bool f32) {
         ch * KDA_CHUNK * D * es,       // qp
         ch * D * KDA_CHUNK * es,       // km
         ch * KDA_CHUNK * D * es,       // wn
-        ch * KDA_CHUNK * D * es,       // u
-        ch * KDA_CHUNK * KDA_CHUNK * es,  // aqk
+        ch * KDA_CHUNK * D * 4,        // u (fp32 on both paths)
+        ch * KDA_CHUNK * KDA_CHUNK * 4,   // aqk (fp32, or two fp16 planes)
         ch * D * 4,                    // gam
         output_fused(f32) ? 0 : ch * (size_t)D * D * es,   // h (only without the fused output)
         output_fused(f32) ? 0 : ch * KDA_CHUNK * D * es,   // vn

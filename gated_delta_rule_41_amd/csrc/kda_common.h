@@ -55,12 +55,14 @@ __host__ __device__ constexpr int kslot(int g, int j) { return 16 * (j >> 2) + 4
 // ---------------------------------------------------------------- operands
 // Value-path products (WY solve, W S, K-^T V_new, Q+ h, A_qk V_new) take fp16
 // operands with fp32 accumulation when the inputs are bf16: fp16 has 3 more
-// mantissa bits than bf16 at the same matrix-core rate, which the accuracy
-// target needs (a single bf16 rounding of the dominant k u^T term already costs
-// a few percent of the state's RMS). Every value-path operand is bounded by the
-// input magnitudes (|q|, |k| for the gated factors; |v| for U, V_new and the
-// state), so the fp16 range holds while |v| and the state stay below ~3e4.
-// With fp32 inputs every product runs in fp32.
+// mantissa bits than bf16 at the same matrix-core rate. Operands that carry
+// the values themselves (beta V in the solve, V_new) are two-term fp16 (Frag2
+// below), and U is stored in fp32: the error is judged max-abs relative to the
+// RMS, and on heavy-tailed values one fp16 rounding of the largest value is
+// already a sizeable part of that budget. Every value-path operand is bounded
+// by the input magnitudes (|q|, |k| for the gated factors; |v| for U, V_new
+// and the state), so the fp16 range holds while |v| and the state stay below
+// ~3e4. With fp32 inputs every product runs in fp32.
 template <bool F32> struct Pol;
 template <> struct Pol<false> {
     using E = uint16_t;  // fp16 bits
@@ -327,8 +329,10 @@ __device__ __forceinline__ void seq_chunks(const int32_t* __restrict__ cu, int T
 //   qp   [64][D]   gated queries  Q+ = exp(g) * q, rows in order, k = key channel (split order per 32)
 //   km   [D][64]   decayed keys K- = exp(g_last - g) * k, transposed: row = key channel, k = chunk row
 //   wn   [64][D]   -W (negated key WY factor), k = key channel (split order)
-//   u    [D/16][4][64 lanes][4]   U in accumulator-tile order (value col tile, row tile, lane, i)
-//   aqk  [64][64]  gated query-key matrix (lower incl. diagonal), k = chunk col (split order)
+//   u    [D/16][4][64 lanes][4]   U in accumulator-tile order (value col tile, row tile, lane, i);
+//                  fp32 with 16-bit KDA factors (uf), so the values are never rounded to fp16
+//   aqk  [64][64]  gated query-key matrix (lower incl. diagonal), k = chunk col (split order);
+//                  with 16-bit KDA factors two fp16 planes [hi][64][64], [lo][64][64] (x = hi + lo)
 //   gam  [D] fp32  exp(g_last) per key channel
 //   h    [D/16][D/32][64 lanes][8]   chunk-entry state as B-operand fragments (value col tile, k slice)
 //   vn   [D/16][2][64 lanes][8]      corrected values V_new as B-operand fragments
@@ -353,6 +357,36 @@ struct Ws {
     // backward state-gradient recursion: a state-independent term added to the
     // state each chunk, [dv/16][dk/16][64 lanes][4] fp32 per chunk-head
     const float* pb = nullptr;
+    // KDA with 16-bit factors: U in fp32 (the same array as u)
+    float* uf = nullptr;
 };
+
+// Two-term fp16 operand: x = hi + lo with hi = fp16(x) and lo = fp16(x - hi),
+// about 22 significant bits. A product a x runs as two matrix-core products,
+// a lo + a hi, accumulated in fp32. The bf16 path carries its large-magnitude
+// values (beta V inside the WY solve, the corrected values V_new) this way,
+// because one fp16 rounding of a heavy-tailed value already costs a sizeable
+// fraction of the max-abs error budget.
+struct Frag2 {
+    Pol<false>::Frag hi, lo;
+};
+__device__ __forceinline__ Frag2 split_frag(const float (&x)[8]) {
+    float h[8], r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        h[j] = h2f(f2h(x[j]));
+        r[j] = x[j] - h[j];
+    }
+    return Frag2{Pol<false>::make(h), Pol<false>::make(r)};
+}
+__device__ __forceinline__ Frag2 split_from_acc(const f32x4_t& t0, const f32x4_t& t1) {
+    const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+    return split_frag(x);
+}
+// acc += a x for a two-term B operand (the small term first)
+__device__ __forceinline__ void mma2(f32x4_t& acc, const Pol<false>::Frag& a, const Frag2& x) {
+    Pol<false>::mma(acc, a, x.lo);
+    Pol<false>::mma(acc, a, x.hi);
+}
 
 }  // namespace kda

@@ -77,18 +77,25 @@ struct PrepSmem {
     static constexpr int R4b = 10 * AK_BLOCK * 4;                             // A_kk lower blocks
     static constexpr int R4 = MT ? R4b : (R4a > R4b ? R4a : R4b);
     static constexpr int R3 = MT ? 64 * D * (int)sizeof(E) : D * BK_STRIDE * (int)sizeof(E);  // beta K+, transposed
-    static constexpr int CONST = 22 * D * 4;                                  // tot xf eA eL cIJ; later T_II
+    // tot xf eA eL cIJ (fp32 operands: + the low parts of tot and xf); later T_II
+    static constexpr int NCONST = F32 ? 30 : 22;
+    static constexpr int CONST = NCONST * D * 4;
     static constexpr int BETA = 64 * 4 + 16;  // beta per row, then one overflow flag per wave
-    // beta V (transposed) and the -W staging share R1 once Kt is dead when both
-    // fit (16-bit operands); otherwise beta V gets a region of its own
-    static constexpr int RBV = MT ? 64 * D * (int)sizeof(E) : D * BK_STRIDE * (int)sizeof(E);
-    static constexpr bool BV_IN_R1 = RBV + 64 * D * (int)sizeof(E) <= R1;
+    // beta V: with 16-bit operands fp32 accumulator tiles (exact, the WY solve
+    // carries it as two fp16 terms) in R1 once Kt is dead, and the -W staging
+    // goes to the beta K+ tile region R3 after the barrier that ends the solve;
+    // with fp32 operands beta V (transposed rows) gets a region of its own and
+    // the -W staging takes R1
+    static constexpr int RBV = MT ? 64 * D * 4 : D * BK_STRIDE * (int)sizeof(E);
+    static constexpr bool BV_IN_R1 = MT;
     static constexpr int R5 = BV_IN_R1 ? 0 : RBV;
     static constexpr int BYTES = R1 + R4 + R3 + CONST + BETA + R5;
     static constexpr int BV_AT = BV_IN_R1 ? 0 : R1 + R4 + R3 + CONST + BETA;
-    static constexpr int WS_AT = BV_IN_R1 ? RBV : 0;
+    static constexpr int WS_AT = MT ? R1 + R4 : 0;
     static_assert(64 * D * 4 <= R1, "slow-path scans must fit in R1");
-    static_assert(64 * D * (int)sizeof(E) <= R1, "-W staging must fit in R1");
+    static_assert(!F32 || 64 * D * 4 <= R4, "slow-path low parts must fit in R4");
+    static_assert(!MT || RBV <= R1, "beta V tiles must fit in R1");
+    static_assert(64 * D * (int)sizeof(E) <= (MT ? R3 : R1), "-W staging must fit its region");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     static_assert(4 * AK_BLOCK * 4 <= CONST, "T_II must fit in the constants area");
     // fused prologue: q, k, v, log alpha [64][SS] bf16 and beta [64] fp32, over
@@ -106,7 +113,9 @@ struct ProArgs {
 };
 
 template <int D, typename TIn, typename TG, bool F32, bool PRO = false>
-__global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k, const TIn* v,
+// (fp32 operands at d = 128 need more than 80 KiB of LDS, so one workgroup per
+// CU; the register budget follows)
+__global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(const TIn* q, const TIn* k, const TIn* v,
                                                       const TG* la, const TG* beta,
                                                       const int32_t* __restrict__ cu, int N, int T, int H,
                                                       Ws<typename Pol<F32>::E> ws, ProArgs pa) {
@@ -127,9 +136,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
 
     extern __shared__ __align__(16) char smem[];
     AE* Kt_s = reinterpret_cast<AE*>(smem);                     // [planes][64][KTS] keys 2^(G_aJ - G)
-    E* Bv_t = reinterpret_cast<E*>(smem + SM::BV_AT);           // beta V transposed ([D][BKS] or tiles)
-    E* Ws_s = reinterpret_cast<E*>(smem + SM::WS_AT);           // [64][NS][4][8] -W (after Kt is dead)
+    E* Bv_t = reinterpret_cast<E*>(smem + SM::BV_AT);           // beta V transposed ([D][BKS]; fp32 operands)
+    float* Bv_f = reinterpret_cast<float*>(smem + SM::BV_AT);   // beta V fp32 tiles (16-bit operands)
+    E* Ws_s = reinterpret_cast<E*>(smem + SM::WS_AT);           // [64][NS][4][8] -W staging (after the solve)
     float* xl_slow = reinterpret_cast<float*>(smem);            // [64][D] slow path: local scans
+    float* xl_slow_lo = reinterpret_cast<float*>(smem + SM::R1); // [64][D] their low parts (fp32 operands)
     char* r4 = smem + SM::R1;
     E* Km_s = reinterpret_cast<E*>(r4);                         // [D][KMS] K-^T in split row order
     float* Akk_s = reinterpret_cast<float*>(r4);                // 10 blocks [16][AKS]: diag I at I, (I,J) at 4+pair
@@ -141,7 +152,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     float* eL = eA + 4 * D;           // [4][D]  2^(G_last - G(first row of I))
     float* cIJ = eL + 4 * D;          // [6][D]  2^(G(first row of I) - G(first row of J)), I > J
     float* Td_s = cst;                // [4][16][AKS] T_II, after the constants are dead
-    float* beta_s = cst + 22 * D;     // [64]
+    float* tot_lo = cst + 22 * D;     // [4][D]  (fp32 operands) low parts of tot and xf, whose
+    float* xf_lo = tot_lo + 4 * D;    // [4][D]  scans are carried as hi + lo pairs
+    float* beta_s = cst + SM::NCONST * D;  // [64]
     int* slow_s = reinterpret_cast<int*>(beta_s + 64);  // [4] per-wave overflow flags
 
     // head fastest: the workgroups dispatched together read whole token rows of
@@ -235,7 +248,22 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
         asm volatile("" ::: "memory");
     }
     float xl[NS][8], q8[NS][8], k8[NS][8], v8[NS][8];
-    rla.get(xl, valid, LOG2E);
+    // With fp32 operands the gate is carried as a pair, x = xl + xlo: the exact
+    // log2-unit value of each gate, then block scans in double-float. The
+    // exponents that matter are differences of two partial sums of the same
+    // block (magnitudes up to ~280 under extreme decay); plain fp32 scans leave
+    // independent roundings of ~1e-5 in neighbouring rows, which decide the
+    // fp32 path's accuracy. With 16-bit operands the plain scan suffices.
+    float xlo[F32 ? NS : 1][8];
+    if constexpr (F32) {
+        rla.get(xl, valid, 1.f);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) log2_units(xl[s][j], xl[s][j], xlo[s][j]);
+    } else {
+        rla.get(xl, valid, LOG2E);
+    }
     rq.get(q8, valid, 1.f);
     rk.get(k8, valid, 1.f);
     rv.get(v8, valid, 1.f);
@@ -267,7 +295,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) xl[s][j] += dpp_shr(xl[s][j], d);
+            for (int j = 0; j < 8; ++j) {
+                if constexpr (F32) {
+                    const float yh = dpp_shr(xl[s][j], d), yl = dpp_shr(xlo[s][j], d);
+                    float sh, er;
+                    two_sum(xl[s][j], yh, sh, er);
+                    xl[s][j] = sh;
+                    xlo[s][j] = __fadd_rn(__fadd_rn(xlo[s][j], yl), er);
+                } else {
+                    xl[s][j] += dpp_shr(xl[s][j], d);
+                }
+            }
     }
     if (n == 0 || n == 15) {
         float* dst = (n == 0 ? xf : tot) + w * D;
@@ -276,6 +314,13 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
             *reinterpret_cast<f32x4_t*>(dst + 32 * s + 4 * g) = f32x4_t{xl[s][0], xl[s][1], xl[s][2], xl[s][3]};
             *reinterpret_cast<f32x4_t*>(dst + 32 * s + 16 + 4 * g) =
                 f32x4_t{xl[s][4], xl[s][5], xl[s][6], xl[s][7]};
+            if constexpr (F32) {
+                float* dl = (n == 0 ? xf_lo : tot_lo) + w * D;
+                *reinterpret_cast<f32x4_t*>(dl + 32 * s + 4 * g) =
+                    f32x4_t{xlo[s][0], xlo[s][1], xlo[s][2], xlo[s][3]};
+                *reinterpret_cast<f32x4_t*>(dl + 32 * s + 16 + 4 * g) =
+                    f32x4_t{xlo[s][4], xlo[s][5], xlo[s][6], xlo[s][7]};
+            }
         }
     }
     if (g == 0) beta_s[r] = valid ? bval : 0.f;
@@ -288,11 +333,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     {
         constexpr int P = 256 / D;
         const int c = tid % D, part = tid / D;
+        // (every constant below is a sum of same-sign gate terms, or a block
+        // total minus its own first row, so the pairs can be folded here)
         float tt[4], ff[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             tt[I] = tot[I * D + c];
             ff[I] = xf[I * D + c];
+            if constexpr (F32) {
+                tt[I] += tot_lo[I * D + c];
+                ff[I] += xf_lo[I * D + c];
+            }
         }
 #pragma unroll
         for (int ty = 0; ty < 15; ++ty) {
@@ -374,6 +425,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             float xf8[8], ea8[8], el8[8], ktv[8], kmv[8], bkv[8], qpv[8];
+            float xfl8[F32 ? 8 : 1];
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const int c0 = 32 * s + 16 * hf + 4 * g;
@@ -386,11 +438,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
                     ea8[4 * hf + j] = b[j];
                     el8[4 * hf + j] = c[j];
                 }
+                if constexpr (F32) {
+                    const f32x4_t al = *reinterpret_cast<const f32x4_t*>(xf_lo + w * D + c0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) xfl8[4 * hf + j] = al[j];
+                }
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int c = 32 * s + kslot(g, j);
-                const float dA = xl[s][j] - xf8[j];  // G_r - G_aw, local sums only
+                float dA = xl[s][j] - xf8[j];  // G_r - G_aw, local sums only
+                if constexpr (F32) dA += xlo[s][j] - xfl8[j];
                 const float e = ex2(dA);
                 const float ei = ex2(-dA);
                 qs[s][j] = q8[s][j] * e;
@@ -418,10 +476,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int c = 32 * s + kslot(g, j);
-                float pre = 0.f, post = tot[w * D + c] - xl[s][j];
-                for (int J = 0; J < w; ++J) pre += tot[J * D + c];
-                for (int J = w + 1; J < 4; ++J) post += tot[J * D + c];
-                const float eg = exp2f(pre + xl[s][j]);  // 2^G_r
+                // pre: totals of the blocks before this one; post: G_last - G_r
+                // (the difference of two partial sums of this block comes first,
+                // with the low parts on the fp32 path)
+                float pre = 0.f, post = tot[w * D + c] - xl[s][j], xr = xl[s][j];
+                if constexpr (F32) {
+                    post += tot_lo[w * D + c] - xlo[s][j];
+                    xr += xlo[s][j];
+                }
+                for (int J = 0; J < w; ++J) pre += tot[J * D + c] + (F32 ? tot_lo[J * D + c] : 0.f);
+                for (int J = w + 1; J < 4; ++J) post += tot[J * D + c] + (F32 ? tot_lo[J * D + c] : 0.f);
+                const float eg = exp2f(pre + xr);  // 2^G_r
                 qpv[j] = q8[s][j] * eg;
                 kmv[j] = k8[s][j] * exp2f(post);
                 bkv[j] = k8[s][j] * eg * br;
@@ -430,6 +495,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
                     Bk_t[c * BKS + r] = P::from_f(bkv[j]);
                 }
                 xl_slow[r * D + c] = xl[s][j];
+                if constexpr (F32) xl_slow_lo[r * D + c] = xlo[s][j];
                 qs[s][j] = 0.f;
                 ks[s][j] = 0.f;
             }
@@ -475,8 +541,22 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
                     io = (int64_t)ii * D;
                 }
                 for (int c = 0; c < D; ++c) {
-                    float ex = xl_slow[rr * D + c] - xl_slow[ii * D + c];
-                    for (int K = J; K < I; ++K) ex += tot[K * D + c];
+                    // G_rr - G_ii: with the low parts (fp32 operands), each
+                    // difference of two partial sums of one block is formed first
+                    float ex;
+                    if constexpr (F32) {
+                        if (J == I) {
+                            ex = (xl_slow[rr * D + c] - xl_slow[ii * D + c]) +
+                                 (xl_slow_lo[rr * D + c] - xl_slow_lo[ii * D + c]);
+                        } else {
+                            ex = (tot[J * D + c] - xl_slow[ii * D + c]) + (tot_lo[J * D + c] - xl_slow_lo[ii * D + c]);
+                            for (int K = J + 1; K < I; ++K) ex += tot[K * D + c] + tot_lo[K * D + c];
+                            ex += xl_slow[rr * D + c] + xl_slow_lo[rr * D + c];
+                        }
+                    } else {
+                        ex = xl_slow[rr * D + c] - xl_slow[ii * D + c];
+                        for (int K = J; K < I; ++K) ex += tot[K * D + c];
+                    }
                     const float kv = ld_in(ksrc, io + c) * exp2f(ex);
                     sq += ld_in(qsrc, ro + c) * kv;
                     sk += ld_in(ksrc, ro + c) * kv;
@@ -489,10 +569,15 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     if (slow || !SM::MT) __syncthreads();  // (block-uniform condition)
 
     // ---- 3c. A_qk (straight to the workspace) and A_kk (LDS, lower blocks only)
-    E* aqk_out = ws.aqk + chh * 64 * 64;
+    // (16-bit operands: two fp16 planes, hi then lo, so the output's A_qk V_new
+    // product sees about 22 significant bits of A_qk)
+    E* aqk_out = ws.aqk + chh * 64 * 64 * (SM::MT ? 2 : 1);
     auto aqk_put = [&](int rr, int cc, float x) {
         const int s2 = cc >> 5, c2 = cc & 31;
-        aqk_out[(rr * 2 + s2) * 32 + 8 * ((c2 & 15) >> 2) + 4 * (c2 >> 4) + (c2 & 3)] = P::from_f(x);
+        const int at = (rr * 2 + s2) * 32 + 8 * ((c2 & 15) >> 2) + 4 * (c2 >> 4) + (c2 & 3);
+        const E hi = P::from_f(x);
+        aqk_out[at] = hi;
+        if constexpr (SM::MT) aqk_out[64 * 64 + at] = P::from_f(x - P::to_f(hi));
     };
     // the backward's forward recompute (fp32 factors) also keeps the gated key
     // products P_kk = A_kk / beta, row-major [64][64], zero on and above the diagonal
@@ -580,14 +665,25 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     }
     __syncthreads();
 
-    // beta V, transposed like beta K+, into the now free Kt region
+    // beta V, transposed like beta K+, into the now free Kt region. With 16-bit
+    // operands each 32-channel slice is split into fp16 hi and lo parts, both
+    // transposed on the matrix cores (exact: a selector product), and summed
+    // into fp32 accumulator tiles [column tile][row block][lane][4], so beta V
+    // reaches the solve unrounded (beta v of bf16 inputs has 16 significant bits)
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         if constexpr (SM::MT) {
             float bvv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) bvv[j] = v8[s][j] * br;
-            tr_slice(bvv, s, std::false_type{}, Bv_t);
+            const Frag2 bx = split_frag(bvv);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+                P::mma(t, bx.lo, sel[hf]);
+                P::mma(t, bx.hi, sel[hf]);
+                *reinterpret_cast<f32x4_t*>(Bv_f + (((2 * s + hf) * 4 + w) * 64 + l) * 4) = t;
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) Bv_t[(32 * s + kslot(g, j)) * BKS + r] = P::from_f(v8[s][j] * br);
@@ -611,10 +707,15 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
     }
     __syncthreads();
 
-    // ---- 4b. WY factors by blocked forward substitution: X = (I + A_kk)^-1 [beta K+ | beta V]
+    // ---- 4b. WY factors by blocked forward substitution: X = (I + A_kk)^-1 [beta K+ | beta V].
+    // With 16-bit operands the B operands of every product here (the blocks X_K
+    // and the right-hand side Y) are two-term fp16 (hi + lo): U carries the
+    // values themselves, whose single fp16 rounding would already cost a
+    // sizeable part of the error budget on heavy-tailed values. The W waves run
+    // the same code (their time is hidden behind the U waves' anyway).
     {
         const bool isW = w < 2;
-        E* u_out = ws.u + chh * 64 * D;
+        float* u_out = (F32 ? reinterpret_cast<float*>(ws.u) : ws.uf) + chh * 64 * D;
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
         f32x4_t X[TPW][4];
 #pragma unroll
@@ -651,9 +752,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
                 const int ct = (w & 1) * TPW + tt;  // column tile inside W (waves 0-1) or U (waves 2-3)
                 f32x4_t Y;
                 if constexpr (SM::MT) {
-                    const u32x2_t bb =
-                        *reinterpret_cast<const u32x2_t*>((isW ? Bk_t : Bv_t) + ((ct * 4 + I) * 64 + l) * 4);
-                    Y = f32x4_t{h2f(bb[0] & 0xffffu), h2f(bb[0] >> 16), h2f(bb[1] & 0xffffu), h2f(bb[1] >> 16)};
+                    if (isW) {
+                        const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(Bk_t + ((ct * 4 + I) * 64 + l) * 4);
+                        Y = f32x4_t{h2f(bb[0] & 0xffffu), h2f(bb[0] >> 16), h2f(bb[1] & 0xffffu), h2f(bb[1] >> 16)};
+                    } else {
+                        Y = *reinterpret_cast<const f32x4_t*>(Bv_f + ((ct * 4 + I) * 64 + l) * 4);
+                    }
                 } else {
                     const E* bsrc = (isW ? Bk_t : Bv_t) + (16 * ct + n) * BKS + 16 * I + 4 * g;
                     if constexpr (F32) {
@@ -666,12 +770,21 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     if (2 * s >= I) break;
-                    P::mma(Y, aoff[s], frag_from_acc<F32>(X[tt][2 * s], (2 * s + 1 < I) ? X[tt][2 * s + 1] : zero));
+                    const f32x4_t& x1 = (2 * s + 1 < I) ? X[tt][2 * s + 1] : zero;
+                    if constexpr (SM::MT)
+                        mma2(Y, aoff[s], split_from_acc(X[tt][2 * s], x1));
+                    else
+                        P::mma(Y, aoff[s], frag_from_acc<F32>(X[tt][2 * s], x1));
                 }
                 X[tt][I] = zero;
-                P::mma(X[tt][I], at, frag_from_acc<F32>(Y, zero));
+                if constexpr (SM::MT)
+                    mma2(X[tt][I], at, split_from_acc(Y, zero));
+                else
+                    P::mma(X[tt][I], at, frag_from_acc<F32>(Y, zero));
             }
         }
+        // with 16-bit operands the -W staging reuses the beta K+ tiles' region
+        if constexpr (SM::MT) __syncthreads();
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             const int ct = (w & 1) * TPW + tt;
@@ -686,18 +799,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const TIn* q, const TIn* k
                         Ws_s[(rr * NS + s) * 32 + gg * 8 + jj] = P::from_f(-X[tt][I][i]);
                     }
             } else {
+                // U in fp32 accumulator-tile order
 #pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    E* dst = u_out + ((ct * 4 + I) * 64 + l) * 4;
-                    if constexpr (F32) {
-                        *reinterpret_cast<f32x4_t*>(dst) = X[tt][I];
-                    } else {
-                        u32x2_t pk;
-                        pk[0] = (uint32_t)f2h(X[tt][I][0]) | ((uint32_t)f2h(X[tt][I][1]) << 16);
-                        pk[1] = (uint32_t)f2h(X[tt][I][2]) | ((uint32_t)f2h(X[tt][I][3]) << 16);
-                        *reinterpret_cast<u32x2_t*>(dst) = pk;
-                    }
-                }
+                for (int I = 0; I < 4; ++I)
+                    *reinterpret_cast<f32x4_t*>(u_out + ((ct * 4 + I) * 64 + l) * 4) = X[tt][I];
             }
         }
     }
@@ -715,6 +820,7 @@ static hipError_t launch_prep_t(const ChunkArgs& a, hipStream_t st) {
     using E = typename Pol<F32>::E;
     using SM = PrepSmem<D, F32>;
     Ws<E> ws{(E*)a.qp, (E*)a.km, (E*)a.wn, (E*)a.u, (E*)a.aqk, a.gam, (E*)a.h, (E*)a.vn, (E*)a.am};
+    ws.uf = static_cast<float*>(a.u);  // U is fp32 on every path
     ProArgs pa{};
     if constexpr (PRO)
         pa = ProArgs{{(const uint16_t*)a.xq, (const uint16_t*)a.xk, (const uint16_t*)a.xv, (const uint16_t*)a.xa,

@@ -7,6 +7,20 @@
 namespace kda {
 
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LOG2E_LO = 1.925963033500011e-08f;  // log2(e) - LOG2E
+
+// Error-free transformations (Knuth's TwoSum; the product residual by FMA),
+// written with explicitly rounded operations so that no step is contracted.
+__device__ __forceinline__ void two_sum(float a, float b, float& s, float& e) {
+    s = __fadd_rn(a, b);
+    const float bb = __fsub_rn(s, a);
+    e = __fadd_rn(__fsub_rn(a, __fsub_rn(s, bb)), __fsub_rn(b, bb));
+}
+// x log2(e) as hi + lo with hi = fl(x LOG2E), to about 2^-48 relative
+__device__ __forceinline__ void log2_units(float x, float& hi, float& lo) {
+    hi = __fmul_rn(x, LOG2E);
+    lo = __fadd_rn(__builtin_fmaf(x, LOG2E, -hi), __fmul_rn(x, LOG2E_LO));
+}
 constexpr float GUARD = 100.0f;  // max gate range inside a 16-row sub-chunk, log2 units
 
 __device__ __forceinline__ float dpp_shr(float x, int d) {

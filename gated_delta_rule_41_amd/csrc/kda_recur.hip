@@ -41,13 +41,18 @@ namespace kda {
 template <int D, bool F32, bool FUSED, bool DPLR = false>
 struct RecurPlan {
     using E = typename Pol<F32>::E;
+    // KDA with 16-bit factors: U is fp32 and the compute wave loads its slab
+    // itself, one chunk ahead (it is not in the ring); V_new is two-term fp16
+    static constexpr bool HP = FUSED && !DPLR && !F32;
     static constexpr int FB = 64 * D * (int)sizeof(E);   // bytes of -W (and of K-^T) per chunk-head
-    static constexpr int UB = 64 * 16 * (int)sizeof(E);  // bytes of one slab's U
+    static constexpr int UB = HP ? 0 : 64 * 16 * (int)sizeof(E);  // bytes of one slab's U in the ring
+    static constexpr int UBG = HP ? 64 * 16 * 4 : UB;    // bytes of one slab's U in the workspace
     static constexpr int GB = D * 4;                     // bytes of gamma
     static constexpr int GPAD = 1024;                    // gamma region rounded up to one whole load
     static constexpr int SLOT = 2 * FB + UB + GPAD;      // one ring slot
-    // with the fused output: two buffers of (h_n slab [D x 16], V_new slab [64 x 16])
-    static constexpr int HVS = (D * 16 + 64 * 16) * (int)sizeof(E);
+    // with the fused output: two buffers of (h_n slab [D x 16], V_new slab [64 x 16],
+    // with HP its hi then lo part)
+    static constexpr int HVS = (D * 16 + (HP ? 2 : 1) * 64 * 16) * (int)sizeof(E);
     static constexpr int HV = FUSED ? 2 * HVS : 0;
     // DPLR: two buffers of the state-independent update K-^T V of this slab
     // (fp16, accumulator-tile order), by chunk parity
@@ -75,14 +80,15 @@ struct RecurPlan {
     // L2 warm-up (fused kernel): the 128-byte lines of one chunk-head's -W, K-^T,
     // Q+ and A_qk are shared out over the head's D/16 slab workgroups; a second
     // load covers this slab's U and the head's gamma
-    static constexpr int LINES_W = FB / 128, LINES_A = 64 * 64 * (int)sizeof(E) / 128;
+    static constexpr int LINES_W = FB / 128, LINES_A = 64 * 64 * (int)sizeof(E) * (HP ? 2 : 1) / 128;
     static constexpr int LINES = 3 * LINES_W + LINES_A;
     static constexpr int LINES_PER = (LINES + D / 16 - 1) / (D / 16);
-    static constexpr int LINES_U = UB / 128, LINES_G = GB / 128;
+    static constexpr int WARM_LOADS = (LINES_PER + 63) / 64;  // first-part loads per lane and chunk
+    static constexpr int LINES_U = UBG / 128, LINES_G = GB / 128;
     // DPLR: the second load also covers this slab's A_qk V tiles, a third its K-^T V share
     static constexpr int LINES_O = DPLR ? UB / 128 : 0, LINES_KV = DPLR ? PBS / 128 : 0;
     static constexpr int LINES_2 = LINES_U + LINES_G + LINES_O;
-    static_assert(!FUSED || (LINES_PER <= 64 && LINES_2 <= 64 && LINES_KV <= 64), "warm-up loads per chunk");
+    static_assert(!FUSED || (LINES_PER <= 128 && LINES_2 <= 64 && LINES_KV <= 64), "warm-up loads per chunk");
     static constexpr int AHEAD = 3;  // chunks warmed ahead of the compute wave (2..6 measured; 3 best)
 };
 
@@ -148,13 +154,20 @@ __device__ __forceinline__ void produce(const Ws<typename Pol<F32>::E>& ws, int6
         const char* wp = reinterpret_cast<const char*>(ws.wn + chh * 64 * D);
 #pragma unroll
         for (int j = 0; j < PL::OPS_W; ++j) dma16(wp + swz<F32>(64 * j + l) * 16, slot + j * 1024);
-        const char* up = reinterpret_cast<const char*>(ws.u + chh * 64 * D + (int64_t)ct * 4 * 64 * 4);
+        if constexpr (PL::OPS_U > 0) {
+            const char* up = reinterpret_cast<const char*>(ws.u + chh * 64 * D + (int64_t)ct * 4 * 64 * 4);
 #pragma unroll
-        for (int j = 0; j < PL::OPS_U; ++j) dma16(up + (64 * j + l) * 16, slot + 2 * PL::FB + j * 1024);
-        // pad to OPS loads: repeat the last U load (same source, same destination)
+            for (int j = 0; j < PL::OPS_U; ++j) dma16(up + (64 * j + l) * 16, slot + 2 * PL::FB + j * 1024);
+            // pad to OPS loads: repeat the last U load (same source, same destination)
 #pragma unroll
-        for (int j = PL::OPS0; j < PL::OPS; ++j)
-            dma16(up + (64 * (PL::OPS_U - 1) + l) * 16, slot + 2 * PL::FB + (PL::OPS_U - 1) * 1024);
+            for (int j = PL::OPS0; j < PL::OPS; ++j)
+                dma16(up + (64 * (PL::OPS_U - 1) + l) * 16, slot + 2 * PL::FB + (PL::OPS_U - 1) * 1024);
+        } else {
+            // pad to OPS loads: repeat the last -W load (same source, same destination)
+#pragma unroll
+            for (int j = PL::OPS0; j < PL::OPS; ++j)
+                dma16(wp + swz<F32>(64 * (PL::OPS_W - 1) + l) * 16, slot + (PL::OPS_W - 1) * 1024);
+        }
     } else {
         // the state update's key factor: K-^T (KDA) or A-^T (DPLR)
         const char* kp = reinterpret_cast<const char*>((DPLR ? ws.am : ws.km) + chh * D * 64);
@@ -178,23 +191,29 @@ template <int D, bool F32, bool FUSED, bool DPLR>
 __device__ __forceinline__ void warm_chunk(const Ws<typename Pol<F32>::E>& ws, int64_t chh, int ct, int l,
                                            char* dst) {
     using PL = RecurPlan<D, F32, FUSED, DPLR>;
-    int L = ct * PL::LINES_PER + (l < PL::LINES_PER ? l : PL::LINES_PER - 1);
-    L = L < PL::LINES ? L : PL::LINES - 1;
-    const char* p;
-    if (L < PL::LINES_W)
-        p = reinterpret_cast<const char*>(ws.wn + chh * 64 * D) + L * 128;
-    else if (L < 2 * PL::LINES_W)
-        p = reinterpret_cast<const char*>((DPLR ? ws.am : ws.km) + chh * 64 * D) + (L - PL::LINES_W) * 128;
-    else if (L < 3 * PL::LINES_W)
-        p = reinterpret_cast<const char*>(ws.qp + chh * 64 * D) + (L - 2 * PL::LINES_W) * 128;
-    else
-        p = reinterpret_cast<const char*>(ws.aqk + chh * 64 * 64) + (L - 3 * PL::LINES_W) * 128;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)p,
-                                     (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+#pragma unroll
+    for (int k = 0; k < PL::WARM_LOADS; ++k) {
+        const int li = 64 * k + l;
+        int L = ct * PL::LINES_PER + (li < PL::LINES_PER ? li : PL::LINES_PER - 1);
+        L = L < PL::LINES ? L : PL::LINES - 1;
+        const char* p;
+        if (L < PL::LINES_W)
+            p = reinterpret_cast<const char*>(ws.wn + chh * 64 * D) + L * 128;
+        else if (L < 2 * PL::LINES_W)
+            p = reinterpret_cast<const char*>((DPLR ? ws.am : ws.km) + chh * 64 * D) + (L - PL::LINES_W) * 128;
+        else if (L < 3 * PL::LINES_W)
+            p = reinterpret_cast<const char*>(ws.qp + chh * 64 * D) + (L - 2 * PL::LINES_W) * 128;
+        else
+            p = reinterpret_cast<const char*>(ws.aqk + chh * 64 * 64 * (PL::HP ? 2 : 1)) + (L - 3 * PL::LINES_W) * 128;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)p,
+                                         (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+    }
     const int m = l < PL::LINES_2 ? l : 0;
     const char* pu;
     if (m < PL::LINES_U)
-        pu = reinterpret_cast<const char*>(ws.u + chh * 64 * D + (int64_t)ct * 4 * 64 * 4) + m * 128;
+        pu = (PL::HP ? reinterpret_cast<const char*>(ws.uf + chh * 64 * D + (int64_t)ct * 4 * 64 * 4)
+                     : reinterpret_cast<const char*>(ws.u + chh * 64 * D + (int64_t)ct * 4 * 64 * 4)) +
+             m * 128;
     else if (m < PL::LINES_U + PL::LINES_G)
         pu = reinterpret_cast<const char*>(ws.gam + chh * D) + (m - PL::LINES_U) * 128;
     else
@@ -281,11 +300,12 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
         const int tstart = cu ? cu[seq] : 0;
         const int len = cu ? cu[seq + 1] - tstart : T;
         Frag qa[4][NS], aa[4][2];
+        Frag al[PL::HP ? 4 : 1][2];  // HP: the low plane of A_qk
         u32x2_t ohr[4];  // DPLR: this slab's A_qk V tiles (fp16)
         auto issue = [&](int c) {
             const int64_t chh = (int64_t)(co + c) * H + h;
             const E* qp = ws.qp + chh * 64 * D;
-            const E* ap = ws.aqk + chh * 64 * 64;
+            const E* ap = ws.aqk + chh * 64 * 64 * (PL::HP ? 2 : 1);
             if constexpr (DPLR) {
 #pragma unroll
                 for (int I = 0; I < 4; ++I)
@@ -299,7 +319,10 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    if (16 * I + 15 >= 32 * s) aa[I][s] = P::load(ap + ((16 * I + n) * 2 + s) * 32 + g * 8);
+                    if (16 * I + 15 >= 32 * s) {
+                        aa[I][s] = P::load(ap + ((16 * I + n) * 2 + s) * 32 + g * 8);
+                        if constexpr (PL::HP) al[I][s] = P::load(ap + 64 * 64 + ((16 * I + n) * 2 + s) * 32 + g * 8);
+                    }
         };
         // only a sequence's last chunk can be partial; every other chunk stores
         // all 64 rows without a per-row branch
@@ -331,9 +354,21 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const Frag bv = P::load(vb + (s * 64 + l) * 8);
+                if constexpr (PL::HP) {
+                    // A_qk V_new with both operands two-term: lo hi + hi lo + hi hi
+                    const Frag bvl = P::load(vb + (2 * 64 + s * 64 + l) * 8);
 #pragma unroll
-                for (int I = 0; I < 4; ++I)
-                    if (16 * I + 15 >= 32 * s) P::mma(acc[I], aa[I][s], bv);
+                    for (int I = 0; I < 4; ++I)
+                        if (16 * I + 15 >= 32 * s) {
+                            P::mma(acc[I], al[I][s], bv);
+                            P::mma(acc[I], aa[I][s], bvl);
+                            P::mma(acc[I], aa[I][s], bv);
+                        }
+                } else {
+#pragma unroll
+                    for (int I = 0; I < 4; ++I)
+                        if (16 * I + 15 >= 32 * s) P::mma(acc[I], aa[I][s], bv);
+                }
             }
             const int t0 = tstart + 64 * c;
             const int L = min(64, len - 64 * c);
@@ -576,6 +611,18 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[t][i] = s0 ? s0[sbase + (int64_t)(16 * t + 4 * g + i) * D] : 0.f;
 
+    // HP: this slab's fp32 U of the next chunk, loaded from the workspace one
+    // chunk ahead (the compute wave's only global loads in the loop, so the
+    // wait before their use finds them landed a whole chain step later)
+    f32x4_t un[PL::HP ? 4 : 1];
+    auto load_u = [&](int c) {
+        if constexpr (PL::HP) {
+            const float* up = ws.uf + ((int64_t)(co + c) * H + h) * 64 * D + (int64_t)ct * 4 * 64 * 4;
+#pragma unroll
+            for (int I = 0; I < 4; ++I) un[I] = *reinterpret_cast<const f32x4_t*>(up + (I * 64 + l) * 4);
+        }
+    };
+    if (PL::HP && nch > 0) load_u(0);
     Frag wf[4][NS];  // -W fragments (with LOOK, of the chunk after the current one once read)
     auto load_w = [&](int c) {
         const char* wsl = ring + (c % RING) * PL::SLOT;
@@ -600,9 +647,16 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
         Frag kf[NT][2];
         if (!LOOK) load_w(c);
         f32x4_t V[4];
+        if constexpr (PL::HP) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) V[I] = un[I];
+            if (c + 1 < nch) load_u(c + 1);
+            asm volatile("" ::: "memory");  // issue the next chunk's U loads here
+        }
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            if constexpr (F32) {
+            if constexpr (PL::HP) {
+            } else if constexpr (F32) {
                 V[I] = *reinterpret_cast<const f32x4_t*>(usl + (I * 64 + l) * 4);
             } else {
                 const u32x2_t u = *reinterpret_cast<const u32x2_t*>(usl + (I * 64 + l) * 4);
@@ -645,11 +699,19 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
         // last chunk re-reads its own)
         if (LOOK) load_w(c + 1 < nch ? c + 1 : c);
         Frag vb[2];
+        Frag vl[PL::HP ? 2 : 1];  // HP: the low terms of V_new
         E* vp = FUSED ? reinterpret_cast<E*>(hvbase + (c & 1) * PL::HVS) + D * 16
                       : ws.vn + chh * 64 * D + (int64_t)ct * 2 * 64 * 8;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            vb[s] = frag_from_acc<F32>(V[2 * s], V[2 * s + 1]);
+            if constexpr (PL::HP) {
+                const Frag2 x = split_from_acc(V[2 * s], V[2 * s + 1]);
+                vb[s] = x.hi;
+                vl[s] = x.lo;
+                P::store(vp + (2 * 64 + s * 64 + l) * 8, vl[s]);
+            } else {
+                vb[s] = frag_from_acc<F32>(V[2 * s], V[2 * s + 1]);
+            }
             P::store(vp + (s * 64 + l) * 8, vb[s]);
         }
         // S <- Diag(gamma) S + K-^T V_new  (DPLR: + K-^T V + A-^T (-u))
@@ -660,6 +722,12 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
                                               h2f(kv[t][1] >> 16)};
             else
                 S[t] = gm[t] * S[t];
+        }
+        if constexpr (PL::HP) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) P::mma(S[t], kf[t][s], vl[s]);
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -681,6 +749,7 @@ static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     using E = typename Pol<F32>::E;
     using PL = RecurPlan<D, F32, FUSED, DPLR>;
     Ws<E> ws{(E*)a.qp, (E*)a.km, (E*)a.wn, (E*)a.u, (E*)a.aqk, a.gam, (E*)a.h, (E*)a.vn, (E*)a.am, (E*)a.oh, a.pb};
+    ws.uf = static_cast<float*>(a.u);  // KDA with 16-bit factors: U is fp32
     constexpr int NT = D / 16;
     const int NU = a.N * a.H;
     auto kern = recur_kernel<D, F32, FUSED, OUT_F32, DPLR, ADDP>;

@@ -46,9 +46,22 @@
  *  - Supported dtypes: in_dtype (q, k, v) and gate_dtype (log_alpha, beta) are
  *    each KDA_BF16 or KDA_F32; out_dtype (o) KDA_F32 or KDA_BF16. With
  *    in_dtype == KDA_BF16 the chunk products run on 16-bit matrix cores with
- *    fp32 accumulation and an fp32 state (fp16 operands for the value path;
- *    the gated query-key products use bf16 operands split into a high and a
- *    low part); with KDA_F32 they run on fp32 matrix cores.
+ *    fp32 accumulation and an fp32 state: fp16 operands for the value path,
+ *    where the values themselves (beta v in the WY solve, the corrected values
+ *    V_new) and the intra-chunk query-key matrix are carried as two fp16 terms
+ *    (hi + lo, about 22 bits) and U is kept in fp32; the gated query-key
+ *    products use bf16 operands split into a high and a low part. With KDA_F32
+ *    they run on fp32 matrix cores.
+ *  - Value range with in_dtype == KDA_BF16 (fp16 operands): the accuracy
+ *    holds while |v|, the state entries and the corrected values stay below
+ *    about 3e4 (fp16 overflows at 65504) and the values are not much smaller
+ *    than 1e-4 in magnitude (fp16 loses precision below 6.1e-5). Tested at the
+ *    edges: v and the initial state scaled together by 1e-4 and by 1e4 from
+ *    N(0,1) values and an N(0, 0.02) state. Outputs dominated by a carried
+ *    state up to 100 times larger than the new values' share (v x 1e-2, or the
+ *    initial state x 1e2) are tested too; beyond that the fp16 gated queries
+ *    round those rows at 2^-12 of their own size. With fp32 inputs the range
+ *    is fp32's.
  *  - log_alpha must be finite (<= 0 for the overflow guarantees; 0 is allowed).
  *    Non-finite inputs give undefined (typically NaN) outputs; inputs are not scanned.
  *  - Ownership: the caller owns every buffer. The library never allocates or
@@ -181,9 +194,9 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
  * Arguments, results, validation and determinism are those of kda_chunk_fwd.
  * In addition, KDA_ERR_WORKSPACE is returned, before any device call, when
  * kda_chunk_fwd_workspace_size(N, T_total, H, dk, dv, in_dtype) exceeds
- * KDA_NOALLOC_WORKSPACE_BYTES (with bf16 inputs at dk = dv = 128: 74,240 bytes
- * per chunk-head, so at most 903 chunk-heads, e.g. H = 32 and 28 chunks of
- * 64 tokens; fp32 inputs need about 3.3 times as much per chunk-head).
+ * KDA_NOALLOC_WORKSPACE_BYTES (with bf16 inputs at dk = dv = 128: 98,816 bytes
+ * per chunk-head, so at most 679 chunk-heads, e.g. H = 32 and 21 chunks of
+ * 64 tokens; fp32 inputs need about 2.5 times as much per chunk-head).
  * Every call on one device shares that device's scratch, and each call leaves
  * its contents behind; nothing in it needs to start at zero. Calls that
  * overlap in time on one device (on different streams, or from different host

@@ -46,11 +46,11 @@ def test_version_and_status_strings():
 
 
 def test_workspace_size_formula():
-    # per chunk-head, d = 128, 16-bit factors: Q+, K-, -W, U 16 KiB each, A_qk 8 KiB,
-    # gamma 512 B -> 74240 B (the fused output keeps h_n and V_new on chip);
-    # chunks = floor((T + 63 N) / 64)
-    assert kda.workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 74240
-    assert kda.workspace_size(16, 135000, 32, 128, 128) == ((135000 + 63 * 16) // 64) * 32 * 74240
+    # per chunk-head, d = 128, 16-bit factors: Q+, K-, -W 16 KiB each, U 32 KiB (fp32),
+    # A_qk 16 KiB (two fp16 planes), gamma 512 B -> 98816 B (the fused output keeps
+    # h_n and V_new on chip); chunks = floor((T + 63 N) / 64)
+    assert kda.workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 98816
+    assert kda.workspace_size(16, 135000, 32, 128, 128) == ((135000 + 63 * 16) // 64) * 32 * 98816
     # fp32 factors double every array but gamma, and add h_n and V_new
     assert kda.workspace_size(1, 256, 1, 64, 64, __import__("torch").float32) == 4 * (
         4 * (64 * 64 * 4) + 64 * 64 * 4 + 64 * 4 + 64 * 64 * 4 + 64 * 64 * 4)
@@ -316,7 +316,7 @@ def test_layer_fwd_workspace_and_validation():
     """The fused prologue + prefill: workspace = the bf16 forward's plus 2 x 64 x d
     bf16 per chunk-head (the exact path's q, k rows); host validation refuses
     every malformed call before any launch."""
-    assert kda.layer_chunk_fwd_workspace_size(1, 4096, 32, 128) == 64 * 32 * (74240 + 2 * 64 * 128 * 2)
+    assert kda.layer_chunk_fwd_workspace_size(1, 4096, 32, 128) == 64 * 32 * (98816 + 2 * 64 * 128 * 2)
     assert kda.layer_chunk_fwd_workspace_size(16, 135000, 32, 64) == (
         kda.workspace_size(16, 135000, 32, 64, 64) + ((135000 + 63 * 16) // 64) * 32 * 2 * 64 * 64 * 2)
     with pytest.raises(kda.KDAError):
@@ -387,9 +387,9 @@ def test_noalloc_refuses_oversized_and_bad_shapes_on_host():
     def call(N, T, H, d, cu=None):
         return lib.kda_chunk_fwd_noalloc(f(), f(), f(), f(), f(), None, cu, N, T, H, d, d, BF16, BF16, F32,
                                          f(), f(), None)
-    assert kda.workspace_size(1, 29 * 64, 32, 128, 128) > kda.NOALLOC_WORKSPACE_BYTES
-    assert kda.workspace_size(1, 28 * 64, 32, 128, 128) <= kda.NOALLOC_WORKSPACE_BYTES
-    assert call(1, 29 * 64, 32, 128) == WORKSPACE
+    assert kda.workspace_size(1, 22 * 64, 32, 128, 128) > kda.NOALLOC_WORKSPACE_BYTES
+    assert kda.workspace_size(1, 21 * 64, 32, 128, 128) <= kda.NOALLOC_WORKSPACE_BYTES
+    assert call(1, 22 * 64, 32, 128) == WORKSPACE
     assert call(1, 1 << 20, 32, 128) == WORKSPACE
     assert call(0, 100, 32, 128) == SHAPE
     assert call(1, 100, 2, 96) == UNSUP

@@ -176,21 +176,21 @@ def test_decode_bf16_output():
     assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(s_a, s_b)
 
 
-@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
-def test_extreme_decay_exact_path(dt):
-    """Gate ranges beyond the secondary-chunk guard (here up to -12 nats per
-    token on one channel) take the exact elementwise path for the gated
-    products. (With fp32 inputs this regime sits close to the 1e-4 bar: the
-    fp32 log-gate scans leave ~1e-5 relative error in the decay factors of the
-    other, strongly decaying channels; over 8 draws err(S) ranged 3e-5 to
-    1.1e-4. The draw is fixed here.)"""
-    case = ki.make_prefill("prefill-4k", DEV, lengths=[150, 64], H=2, dtype=dt, s0_std=0.02)
+@pytest.mark.parametrize("dt,seed", [(torch.bfloat16, 0), (torch.bfloat16, 1)] +
+                         [(torch.float32, sd) for sd in range(8)])
+def test_extreme_decay_exact_path(dt, seed):
+    """Gate ranges beyond the secondary-chunk guard (every channel of head 0
+    draws log alpha uniform on [-12, 0] nats per token) take the exact
+    elementwise path for the gated products. With fp32 inputs the chunk's
+    partial gate sums reach ~280 (log2 units) while the exponents that matter
+    are differences of nearby ones; eight draws check the fp32 bar there."""
+    case = ki.make_prefill("prefill-4k", DEV, lengths=[150, 64], H=2, dtype=dt, s0_std=0.02, seed=seed)
     gen = torch.Generator(device=DEV)
-    gen.manual_seed(0)
+    gen.manual_seed(seed)
     la = case.log_alpha.float()
     la[:, 0] = -12.0 * torch.rand(la[:, 0].shape, generator=gen, device=DEV)
     case.log_alpha.copy_(la.to(dt))
-    check_prefill(case, tol_for(dt), label=f"extreme decay {dt}")
+    check_prefill(case, tol_for(dt), label=f"extreme decay {dt} seed {seed}")
 
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
@@ -235,3 +235,33 @@ def test_all_empty_sequences():
     o, S = kda.chunk_fwd(e, e, e, e, torch.empty(0, H, dtype=torch.bfloat16, device=DEV), s0, cu)
     torch.cuda.synchronize()
     assert o.numel() == 0 and torch.equal(S, s0)
+
+
+# Value scales on the bf16 path (fp16 value operands, fp32 state): uniform
+# scaling of v and the initial state by 1e-4 (fp16's normal range starts at
+# 6.1e-5) and by 1e4 (entries up to ~6e3, against fp16's 65504); and mixed
+# scales, where the initial state's share of o and the new values' differ by
+# up to ~100x (v x 1e-2; the initial state x 1e2), and v x 1e3.
+@pytest.mark.parametrize("vs,ss", [(1e-4, 1e-4), (1e4, 1e4), (1e-2, 1.0), (1e3, 1.0), (1.0, 1e2)])
+def test_value_scale(vs, ss):
+    case = ki.make_prefill("prefill-4k", DEV, lengths=[1000, 333], H=4, s0_std=0.02)
+    case.v.copy_((case.v.float() * vs).to(case.v.dtype))
+    case.initial_state.mul_(ss)
+    check_prefill(case, TOL_BF16, label=f"v x {vs:g}, initial state x {ss:g}")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_scalar_gate_gated_deltanet(dt):
+    """A forget gate constant across key channels (one log alpha per token and
+    head) is Gated DeltaNet, the special case KDA generalises (GeekNews "Kimi
+    Linear" summary, section "Da atenção linear ao Gated DeltaNet"); the oracle's
+    reduction to it is pinned on the CPU. Fast (shift +2) and slow (shift -2)
+    gates on different heads."""
+    case = ki.make_prefill("varlen-16", DEV, lengths=[700, 1, 190], H=4, dtype=dt, s0_std=0.02)
+    T = case.T_total
+    z = torch.randn(T, case.H, 1, device=DEV, generator=torch.Generator(device=DEV).manual_seed(3))
+    shift = torch.tensor([2.0, 2.0, -2.0, -2.0], device=DEV).view(1, -1, 1)
+    la = -torch.nn.functional.softplus(z + shift)
+    case.log_alpha.copy_(la.expand(T, case.H, case.dk).to(dt))
+    assert bool((case.log_alpha == case.log_alpha[:, :, :1]).all())
+    check_prefill(case, tol_for(dt), label=f"scalar gate (Gated DeltaNet) {dt}")

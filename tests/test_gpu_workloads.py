@@ -14,10 +14,14 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def test_varlen_16_full():
-    case = ki.make_prefill("varlen-16", DEV)
-    heads = [0, 13, 31]
-    say(f"[varlen-16] T_total={case.T_total} lengths={case.lengths} heads={heads}")
+# The -slow variants draw log alpha = -softplus(N(0,1) - 2) (mean alpha about
+# 0.84, e^-12 per chunk): the carried state then survives many chunks, so the
+# state handoff between chunks is what the outputs and final states check.
+# Each variant checks other heads and positions.
+@pytest.mark.parametrize("wl,heads", [("varlen-16", [0, 13, 31]), ("varlen-16-slow", [2, 17, 30])])
+def test_varlen_16_full(wl, heads):
+    case = ki.make_prefill(wl, DEV)
+    say(f"[{wl}] T_total={case.T_total} lengths={case.lengths} heads={heads}")
     o, S = gpu_prefill(case)
     cu = case.cu_seqlens.cpu()
     q, k, v, la = (head_slice(t, heads) for t in (case.q, case.k, case.v, case.log_alpha))
@@ -53,15 +57,15 @@ def test_decode_256_full():
     assert es <= TOL_BF16
 
 
-def test_long_1m_sampled():
+@pytest.mark.parametrize("wl,heads,seed", [("long-1m", [5], 2024), ("long-1m-slow", [22], 7)])
+def test_long_1m_sampled(wl, heads, seed):
     T = 1 << 20
-    case = ki.make_prefill("long-1m", DEV)
-    heads = [5]
-    g = np.random.default_rng(2024)
+    case = ki.make_prefill(wl, DEV)
+    g = np.random.default_rng(seed)
     pos = np.unique(g.integers(0, T, 4096))
     bnd = np.array([0, 63, 64, 65535, 65536, T - 1])
     rec = np.unique(np.concatenate([pos, bnd]))
-    say(f"[long-1m] T={T} H={case.H} head={heads} positions={len(rec)}")
+    say(f"[{wl}] T={T} H={case.H} head={heads} positions={len(rec)}")
     o, S = gpu_prefill(case)
     q, k, v, la = (head_slice(t, heads) for t in (case.q, case.k, case.v, case.log_alpha))
     b = case.beta[:, heads].contiguous().cpu()

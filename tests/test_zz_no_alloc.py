@@ -44,9 +44,9 @@ def _check(case, label):
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 def test_noalloc_two_calls_second_smaller(dt):
-    # the first call fills most of the scratch (bf16: 28 chunks x 32 heads of
-    # 74,240 bytes = 63.4 MiB of the 64 MiB); the second is smaller and ragged
-    big = [1792] if dt == torch.bfloat16 else [300, 65, 1]
+    # the first call fills most of the scratch (bf16: 21 chunks x 32 heads of
+    # 98,816 bytes = 63.3 MiB of the 64 MiB); the second is smaller and ragged
+    big = [1344] if dt == torch.bfloat16 else [300, 65, 1]
     H1 = 32 if dt == torch.bfloat16 else 8
     _check(ki.make_prefill("prefill-4k", DEV, lengths=big, H=H1, dtype=dt), "first call")
     _check(ki.make_prefill("varlen-16", DEV, lengths=[100, 0, 37], H=2, dtype=dt, s0_std=0.02),
@@ -56,7 +56,7 @@ def test_noalloc_two_calls_second_smaller(dt):
 def test_noalloc_refuses_oversized_before_launch():
     # one chunk-head more than the scratch holds is refused with KDA_ERR_WORKSPACE
     # on the host; the outputs stay untouched
-    T = 29 * 64
+    T = 22 * 64
     case = ki.make_prefill("prefill-4k", DEV, lengths=[T], H=32)
     assert kda.workspace_size(1, T, 32, 128, 128) > kda.NOALLOC_WORKSPACE_BYTES
     say("[noalloc] oversized call")

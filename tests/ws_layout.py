@@ -23,13 +23,14 @@ def chunk_capacity(N, T, have_cu):
 
 
 def plan(NC, H, D, f32):
-    """Array offsets and total size. With 16-bit factors the output is fused
-    into the state recursion and the chunk-entry states / corrected values stay
-    on chip (their arrays are empty)."""
+    """Array offsets and total size. U is fp32 on both paths; with 16-bit
+    factors A_qk is two fp16 planes (hi, lo), the output is fused into the state
+    recursion and the chunk-entry states / corrected values stay on chip (their
+    arrays are empty)."""
     es = 4 if f32 else 2
     ch = NC * H
-    sizes = [ch * CH * D * es, ch * D * CH * es, ch * CH * D * es, ch * CH * D * es,
-             ch * CH * CH * es, ch * D * 4, ch * D * D * es if f32 else 0, ch * CH * D * es if f32 else 0]
+    sizes = [ch * CH * D * es, ch * D * CH * es, ch * CH * D * es, ch * CH * D * 4,
+             ch * CH * CH * 4, ch * D * 4, ch * D * D * es if f32 else 0, ch * CH * D * es if f32 else 0]
     off, o = [], 0
     for s in sizes:
         off.append(o)
@@ -69,7 +70,7 @@ def decode(ws: torch.Tensor, N, T, H, D, f32, have_cu, gc, h):
     W = np.zeros((CH, D))
     W[:, (np.arange(NS)[:, None] * 32 + SPLIT[None, :]).ravel()] = -wn.reshape(CH, -1)
     out["W"] = W
-    u = arr(3, CH * D).reshape(NCT, 4, 64, 4)
+    u = arr(3, CH * D, 4, True).reshape(NCT, 4, 64, 4)
     U = np.zeros((CH, D))
     for ct in range(NCT):
         for I in range(4):
@@ -78,7 +79,11 @@ def decode(ws: torch.Tensor, N, T, H, D, f32, have_cu, gc, h):
                 for i in range(4):
                     U[16 * I + 4 * g + i, 16 * ct + n] = u[ct, I, l, i]
     out["U"] = U
-    aq = arr(4, CH * CH).reshape(CH, 2, 32)
+    if f32:
+        aq = arr(4, CH * CH).reshape(CH, 2, 32)
+    else:  # hi plane + lo plane
+        planes = arr(4, 2 * CH * CH).reshape(2, CH, 2, 32)
+        aq = planes[0] + planes[1]
     A = np.zeros((CH, CH))
     A[:, (np.arange(2)[:, None] * 32 + SPLIT[None, :]).ravel()] = aq.reshape(CH, -1)
     out["Aqk"] = A
