@@ -173,7 +173,7 @@ kda_status kda_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
     if (!head_ok(dk, dv) || !dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
     // the workspace is sized for the packed case; it also covers one sequence
     const int64_t NC = chunk_capacity(N, T_total, true);
-    *bytes = plan_workspace(NC, H, dk, in_dtype == KDA_F32).total;
+    *bytes = plan_workspace(NC, H, dk, in_dtype == KDA_F32).total + seq_table_bytes(N);
     return KDA_OK;
 }
 
@@ -221,11 +221,12 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
     const bool f32 = in_dtype == KDA_F32;
     const int64_t NC = chunk_capacity(N, T_total, cu_seqlens != nullptr);
     const WsPlan plan = plan_workspace(NC, H, dk, f32);
-    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < plan.total)
+    const size_t need = plan.total + seq_table_bytes(N);  // the sequence table at the end
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need)
         return KDA_ERR_WORKSPACE;
     for (int i = 0; i < 7; ++i)
-        if (overlaps(workspace, plan.total, ins[i], nin[i])) return KDA_ERR_ALIAS;
-    if (overlaps(workspace, plan.total, o, no) || overlaps(workspace, plan.total, final_state, ns))
+        if (overlaps(workspace, need, ins[i], nin[i])) return KDA_ERR_ALIAS;
+    if (overlaps(workspace, need, o, no) || overlaps(workspace, need, final_state, ns))
         return KDA_ERR_ALIAS;
     if (NC >= (int64_t(1) << 31) / H) return KDA_ERR_SHAPE;
 
@@ -260,7 +261,9 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
     auto mark = [&](int i) {
         return !events || !events[i] || hipEventRecord(static_cast<hipEvent_t>(events[i]), st) == hipSuccess;
     };
+    a.tab = cu_seqlens ? reinterpret_cast<SeqMeta*>(w + plan.total) : nullptr;
     if (!mark(0)) return KDA_ERR_HIP;
+    if (cu_seqlens && launch_seq_table(cu_seqlens, N, a.T, a.NC, a.tab, st) != hipSuccess) return KDA_ERR_HIP;
     if (NC > 0 && launch_prep(a, st) != hipSuccess) return KDA_ERR_HIP;
     if (!mark(1)) return KDA_ERR_HIP;
     if (launch_recur(a, st) != hipSuccess) return KDA_ERR_HIP;
@@ -275,7 +278,7 @@ kda_status kda_dplr_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t
     if (!bytes) return KDA_ERR_NULL;
     if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
     if (!head_ok(dk, dv) || in_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-    *bytes = plan_workspace_dplr(chunk_capacity(N, T_total, true), H, dk).total;
+    *bytes = plan_workspace_dplr(chunk_capacity(N, T_total, true), H, dk).total + seq_table_bytes(N);
     return KDA_OK;
 }
 
@@ -309,11 +312,12 @@ kda_status kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const
         return KDA_ERR_ALIAS;
     const int64_t NC = chunk_capacity(N, T_total, cu_seqlens != nullptr);
     const WsPlan plan = plan_workspace_dplr(NC, H, dk);
-    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < plan.total)
+    const size_t need = plan.total + seq_table_bytes(N);  // the sequence table at the end
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need)
         return KDA_ERR_WORKSPACE;
     for (int i = 0; i < 8; ++i)
-        if (overlaps(workspace, plan.total, ins[i], nin[i])) return KDA_ERR_ALIAS;
-    if (overlaps(workspace, plan.total, o, no) || overlaps(workspace, plan.total, final_state, ns))
+        if (overlaps(workspace, need, ins[i], nin[i])) return KDA_ERR_ALIAS;
+    if (overlaps(workspace, need, o, no) || overlaps(workspace, need, final_state, ns))
         return KDA_ERR_ALIAS;
     if (NC >= (int64_t(1) << 31) / H) return KDA_ERR_SHAPE;
 
@@ -350,6 +354,8 @@ kda_status kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const
     c.h = nullptr;
     c.vn = nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    c.tab = cu_seqlens ? reinterpret_cast<SeqMeta*>(w + plan.total) : nullptr;
+    if (cu_seqlens && launch_seq_table(cu_seqlens, N, c.T, c.NC, c.tab, st) != hipSuccess) return KDA_ERR_HIP;
     if (NC > 0 && launch_dplr_prep(c, st) != hipSuccess) return KDA_ERR_HIP;
     if (launch_recur(c, st) != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
@@ -389,7 +395,7 @@ kda_status kda_chunk_bwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
     if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
     if (!head_ok(dk, dv)) return KDA_ERR_UNSUPPORTED;
     size_t off[5];
-    *bytes = bwd_workspace(chunk_capacity(N, T_total, true), H, dk, off);
+    *bytes = bwd_workspace(chunk_capacity(N, T_total, true), H, dk, off) + seq_table_bytes(N);
     return KDA_OK;
 }
 
@@ -431,7 +437,8 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     }
     const int64_t NC = chunk_capacity(N, T_total, cu_seqlens != nullptr);
     size_t off[5];
-    const size_t need = bwd_workspace(NC, H, dk, off);
+    const size_t bwd_base = bwd_workspace(NC, H, dk, off);
+    const size_t need = bwd_base + seq_table_bytes(N);  // the sequence table at the end
     if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return KDA_ERR_WORKSPACE;
     for (int j = 0; j < 8; ++j)
         if (overlaps(workspace, need, ins[j], nin[j])) return KDA_ERR_ALIAS;
@@ -483,6 +490,8 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     b.dbeta = dbeta;
     b.scr = reinterpret_cast<float*>(w + off[4]);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    F.tab = R.tab = cu_seqlens ? reinterpret_cast<SeqMeta*>(w + bwd_base) : nullptr;
+    if (cu_seqlens && launch_seq_table(cu_seqlens, N, F.T, F.NC, F.tab, st) != hipSuccess) return KDA_ERR_HIP;
     if (NC > 0 && launch_prep(F, st) != hipSuccess) return KDA_ERR_HIP;
     if (NC > 0 && launch_recur(F, st) != hipSuccess) return KDA_ERR_HIP;
     if (NC > 0 && launch_bwd_prep(b, st) != hipSuccess) return KDA_ERR_HIP;
@@ -545,7 +554,7 @@ kda_status kda_layer_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_
     if (!bytes) return KDA_ERR_NULL;
     if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
     if (!head_ok(d, d)) return KDA_ERR_UNSUPPORTED;
-    *bytes = layer_fwd_workspace(chunk_capacity(N, T_total, true), H, d, nullptr);
+    *bytes = layer_fwd_workspace(chunk_capacity(N, T_total, true), H, d, nullptr) + seq_table_bytes(N);
     return KDA_OK;
 }
 
@@ -571,7 +580,8 @@ kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, c
     const int64_t NC = chunk_capacity(N, T_total, cu_seqlens != nullptr);
     if (NC >= (int64_t(1) << 31) / H) return KDA_ERR_SHAPE;
     size_t scr_off = 0;
-    const size_t wbytes = layer_fwd_workspace(NC, H, d, &scr_off);
+    const size_t wbase = layer_fwd_workspace(NC, H, d, &scr_off);
+    const size_t wbytes = wbase + seq_table_bytes(N);  // the sequence table at the end
     if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < wbytes) return KDA_ERR_WORKSPACE;
     for (int i = 0; i < 12; ++i) {
         if (overlaps(o, no, ins[i], nin[i]) || overlaps(workspace, wbytes, ins[i], nin[i])) return KDA_ERR_ALIAS;
@@ -612,6 +622,8 @@ kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, c
     a.wq = wq, a.wk = wk, a.wv = wv, a.A_log = A_log, a.dt_bias = dt_bias;
     a.qk_scr = w + scr_off;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    a.tab = cu_seqlens ? reinterpret_cast<SeqMeta*>(w + wbase) : nullptr;
+    if (cu_seqlens && launch_seq_table(cu_seqlens, N, a.T, a.NC, a.tab, st) != hipSuccess) return KDA_ERR_HIP;
     if (NC > 0 && launch_prep(a, st) != hipSuccess) return KDA_ERR_HIP;
     if (launch_recur(a, st) != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;

@@ -98,7 +98,7 @@ struct BwdPrepSmem {
 };
 
 template <int D>
-__global__ __launch_bounds__(4 * D) void bwd_prep_kernel(const int32_t* __restrict__ cu, int N, int T, int H,
+__global__ __launch_bounds__(4 * D) void bwd_prep_kernel(const SeqMeta* __restrict__ tab, int N, int T, int H,
                                                          Ws<float> f, Ws<float> b,
                                                          const float* __restrict__ d_o) {
     constexpr int NT = D / 16, NTH = 4 * D, RS = BwdPrepSmem<D>::RS, SQS = BwdPrepSmem<D>::SQS;
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(4 * D) void bwd_prep_kernel(const int32_t* __restri
     float* Aq = Qp + 64 * RS;      // [64][SQS] A_qk
     const int gc = blockIdx.x / H, h = blockIdx.x - gc * H;
     ChunkLoc loc;
-    if (!locate_chunk(cu, N, T, gc, loc)) return;
+    if (!locate_chunk(tab, N, T, gc, loc)) return;
     const int64_t src = (int64_t)gc * H + h;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, n = l & 15;
     // every load of the stage first, then the LDS stores
@@ -191,7 +191,7 @@ struct BwdSmem {
 
 template <int D, typename TIn, typename TG>
 __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TIn* k, const TIn* v, const TG* la,
-                                                          const TG* beta, const int32_t* __restrict__ cu, int N,
+                                                          const TG* beta, const SeqMeta* __restrict__ tab, int N,
                                                           int T, int H, Ws<float> f, Ws<float> b,
                                                           const float* __restrict__ d_o, float* __restrict__ scr,
                                                           float* __restrict__ dq, float* __restrict__ dk,
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
 
     const int gc = blockIdx.x / H, h = blockIdx.x - gc * H;
     ChunkLoc loc;
-    if (!locate_chunk(cu, N, T, gc, loc)) return;
+    if (!locate_chunk(tab, N, T, gc, loc)) return;
     const int t0 = loc.t0, L = loc.L;
     const int64_t fs = (int64_t)gc * H + h;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, n = l & 15;
@@ -739,7 +739,7 @@ static hipError_t launch_bwd_prep_d(const BwdArgs& a, hipStream_t st) {
                 (float*)F.vn};
     Ws<float> b{(float*)B.qp, (float*)B.km, (float*)B.wn, (float*)B.u, (float*)B.aqk, B.gam, (float*)B.h,
                 (float*)B.vn, nullptr, nullptr, B.pb};
-    hipLaunchKernelGGL(kern, dim3(F.NC * F.H), dim3(4 * D), bytes, st, F.cu, F.N, F.T, F.H, f, b, a.d_o);
+    hipLaunchKernelGGL(kern, dim3(F.NC * F.H), dim3(4 * D), bytes, st, F.tab, F.N, F.T, F.H, f, b, a.d_o);
     return hipGetLastError();
 }
 
@@ -760,7 +760,7 @@ static hipError_t launch_bwd_local_t(const BwdArgs& a, hipStream_t st) {
     Ws<float> b{(float*)B.qp, (float*)B.km, (float*)B.wn, (float*)B.u, (float*)B.aqk, B.gam, (float*)B.h,
                 (float*)B.vn, nullptr, nullptr, B.pb};
     hipLaunchKernelGGL(kern, dim3(F.NC * F.H), dim3(4 * D), SM::BYTES, st, (const TIn*)F.q, (const TIn*)F.k,
-                       (const TIn*)F.v, (const TG*)F.la, (const TG*)F.beta, F.cu, F.N, F.T, F.H, f, b, a.d_o,
+                       (const TIn*)F.v, (const TG*)F.la, (const TG*)F.beta, F.tab, F.N, F.T, F.H, f, b, a.d_o,
                        a.scr, a.dq, a.dk, a.dv, a.dla, a.dbeta);
     return hipGetLastError();
 }

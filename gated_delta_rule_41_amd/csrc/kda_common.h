@@ -246,82 +246,59 @@ template <> __device__ __forceinline__ void ld_in4<float>(const float* p, int64_
     x[3] = u[3];
 }
 
-// ---------------------------------------------------------------- wave scans
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
-    }
-    return x;
-}
+// Sequence table of a packed batch, built on the device from cu_seqlens by
+// seq_table_kernel (kda_seq.hip) at the start of every call that has one:
+// entry i = {first token, length, first chunk slot, chunk count} of sequence
+// i, after sanitising the offsets (each clamped into [0, T], non-decreasing,
+// chunks capped at the workspace's capacity), so that a malformed cu_seqlens
+// can give wrong results but never an access outside the buffers. Entry N is
+// a sentinel {T, 0, total chunks, 0}. Chunk slots of sequence i are
+// [coff_i, coff_i + nch_i); they tile [0, total) in order.
+struct SeqMeta {
+    int32_t start, len, coff, nch;
+};
 
-// Chunk slot -> (sequence, first token, length). Chunk slots of sequence i are
-// [co_i, co_i + ceil(len_i / 64)) with co_i the running sum of chunk counts.
-// Every lane of the calling wave must call it with the same gc.
+// Chunk slot -> (sequence, first token, length, the sequence's first token).
+// tab == nullptr means one sequence of T tokens. Every lane of the calling
+// wave must call it with the same gc (the search is uniform).
 struct ChunkLoc {
     int seq;
     int t0;
     int L;
+    int start;
 };
-__device__ __forceinline__ bool locate_chunk(const int32_t* __restrict__ cu, int N, int T, int gc,
+__device__ __forceinline__ bool locate_chunk(const SeqMeta* __restrict__ tab, int N, int T, int gc,
                                              ChunkLoc& out) {
-    if (cu == nullptr) {
+    if (tab == nullptr) {
         const int t0 = gc * CH;
         if (t0 >= T) return false;
         out.seq = 0;
         out.t0 = t0;
         out.L = min(CH, T - t0);
+        out.start = 0;
         return true;
     }
-    const int lane = threadIdx.x & 63;
-    int base = 0;
-    for (int s0 = 0; s0 < N; s0 += 64) {
-        const int i = s0 + lane;
-        int start = 0, len = 0, nch = 0;
-        if (i < N) {
-            start = cu[i];
-            len = cu[i + 1] - start;
-            nch = (len + CH - 1) / CH;
-        }
-        const int incl = wave_incl_scan(nch);
-        const int total = __shfl(incl, 63, 64);
-        if (gc < base + total) {
-            const unsigned long long m = __ballot(i < N && base + incl > gc);
-            const int src = __ffsll((long long)m) - 1;
-            const int excl = __shfl(incl - nch, src, 64);
-            const int st = __shfl(start, src, 64);
-            const int ln = __shfl(len, src, 64);
-            const int lc = gc - base - excl;
-            out.seq = s0 + src;
-            out.t0 = st + lc * CH;
-            out.L = min(CH, ln - lc * CH);
-            return true;
-        }
-        base += total;
+    if (gc >= tab[N].coff) return false;
+    // the last sequence whose first chunk slot is <= gc (empty sequences share
+    // their successor's offset and are skipped by taking the last)
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tab[mid].coff <= gc) lo = mid; else hi = mid - 1;
     }
-    return false;
+    const SeqMeta m = tab[lo];
+    const int lc = gc - m.coff;
+    out.seq = lo;
+    out.t0 = m.start + lc * CH;
+    out.L = min(CH, m.len - lc * CH);
+    out.start = m.start;
+    return true;
 }
 
-// Chunk-slot offset and chunk count of sequence `seq` (uniform across the wave).
-__device__ __forceinline__ void seq_chunks(const int32_t* __restrict__ cu, int T, int seq, int& co, int& nch) {
-    if (cu == nullptr) {
-        co = 0;
-        nch = (T + CH - 1) / CH;
-        return;
-    }
-    const int lane = threadIdx.x & 63;
-    int base = 0;
-    for (int s0 = 0; s0 < seq; s0 += 64) {
-        const int i = s0 + lane;
-        int n = 0;
-        if (i < seq) n = (cu[i + 1] - cu[i] + CH - 1) / CH;
-        const int incl = wave_incl_scan(n);
-        base += __shfl(incl, 63, 64);
-    }
-    co = base;
-    nch = (cu[seq + 1] - cu[seq] + CH - 1) / CH;
+// First token, length, first chunk slot and chunk count of sequence `seq`.
+__device__ __forceinline__ SeqMeta seq_info(const SeqMeta* __restrict__ tab, int T, int seq) {
+    if (tab == nullptr) return SeqMeta{0, T, 0, (T + CH - 1) / CH};
+    return tab[seq];
 }
 
 // ---------------------------------------------------------------- workspace

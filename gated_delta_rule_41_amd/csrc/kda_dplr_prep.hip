@@ -136,7 +136,7 @@ __device__ __forceinline__ u32x2_t pack4h(const f32x4_t& x, float sign) {
 template <int D, typename TG>
 __global__ __launch_bounds__(256, 2) void dplr_prep_kernel(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                                            const uint16_t* av, const uint16_t* bv, const TG* la,
-                                                           const int32_t* __restrict__ cu, int N, int T, int H,
+                                                           const SeqMeta* __restrict__ tab, int N, int T, int H,
                                                            Ws<uint16_t> ws) {
     using P = Pol<false>;
     using E = uint16_t;
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void dplr_prep_kernel(const uint16_t* q, co
     const int gc = blockIdx.x / H;
     const int h = blockIdx.x - gc * H;
     ChunkLoc loc;
-    if (!locate_chunk(cu, N, T, gc, loc)) return;
+    if (!locate_chunk(tab, N, T, gc, loc)) return;
     const int t0 = loc.t0, L = loc.L;
     const int64_t chh = (int64_t)gc * H + h;
 
@@ -632,7 +632,7 @@ static hipError_t launch_dplr_prep_t(const ChunkArgs& a, hipStream_t st) {
     dim3 grid(a.NC * a.H), block(256);  // NC * H < 2^31 (checked by the caller)
     hipLaunchKernelGGL(kern, grid, block, SM::BYTES, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.lr_a, (const uint16_t*)a.lr_b, (const TG*)a.la,
-                       a.cu, a.N, a.T, a.H, ws);
+                       a.tab, a.N, a.T, a.H, ws);
     return hipGetLastError();
 }
 

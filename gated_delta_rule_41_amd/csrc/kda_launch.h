@@ -16,10 +16,13 @@ struct DecodeArgs {
     bool in_f32, gate_f32, out_f32;
 };
 
+struct SeqMeta;
+
 struct ChunkArgs {
     const void *q, *k, *v, *la, *beta;
     const float* s0;        // may be null
     const int32_t* cu;      // may be null (one sequence)
+    SeqMeta* tab = nullptr; // the sequence table built from cu (null when cu is)
     float* s_final;         // may be null
     void* o;
     int N, T, H, D;
@@ -95,6 +98,9 @@ int64_t chunk_capacity(int N, int64_t T, bool have_cu);
 hipError_t allow_dynamic_lds(const void* kernel, int bytes);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+// sequence table from cu_seqlens (kda_seq.hip); tab holds N + 1 entries
+hipError_t launch_seq_table(const int32_t* cu, int N, int T, int NC, SeqMeta* tab, hipStream_t st);
+inline size_t seq_table_bytes(int N) { return ((size_t)(N + 1) * 16 + 255) / 256 * 256; }
 hipError_t launch_prep(const ChunkArgs& a, hipStream_t st);
 hipError_t launch_recur(const ChunkArgs& a, hipStream_t st);
 hipError_t launch_output(const ChunkArgs& a, hipStream_t st);

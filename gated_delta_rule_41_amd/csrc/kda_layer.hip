@@ -123,7 +123,10 @@ __global__ __launch_bounds__(256) void layer_conv_state_kernel(PrologueIn<TE> in
     const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (item >= N * H) return;  // uniform over the wave
     const int n = item / H, h = item - n * H, c0 = PER * (threadIdx.x & 63);
-    const int start = cu != nullptr ? cu[n] : 0, end = cu != nullptr ? cu[n + 1] : T;
+    // (offsets clamped into [0, T]: a malformed cu_seqlens reads no row outside the inputs)
+    int start = cu != nullptr ? cu[n] : 0, end = cu != nullptr ? cu[n + 1] : T;
+    start = min(max(start, 0), T);
+    end = min(max(end, start), T);
     const TE* xs[3] = {in.xq, in.xk, in.xv};
     TE* dst = cs + (int64_t)item * 3 * (CONV_W - 1) * D + c0;
 #pragma unroll

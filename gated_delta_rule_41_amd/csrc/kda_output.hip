@@ -18,7 +18,7 @@
 namespace kda {
 
 template <int D, bool F32, bool OUT_F32>
-__global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__ cu, int N, int T, int H,
+__global__ __launch_bounds__(256) void output_kernel(const SeqMeta* __restrict__ tab, int N, int T, int H,
                                                      Ws<typename Pol<F32>::E> ws, void* __restrict__ o) {
     using P = Pol<F32>;
     using E = typename P::E;
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__
     const int gc = blockIdx.x;
     const int h = blockIdx.y;
     ChunkLoc loc;
-    if (!locate_chunk(cu, N, T, gc, loc)) return;
+    if (!locate_chunk(tab, N, T, gc, loc)) return;
     const int t0 = loc.t0, L = loc.L;
     const int64_t chh = (int64_t)gc * H + h;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 15, g = l >> 4;
@@ -104,9 +104,9 @@ static hipError_t launch_output_t(const ChunkArgs& a, hipStream_t st) {
     Ws<E> ws{(E*)a.qp, (E*)a.km, (E*)a.wn, (E*)a.u, (E*)a.aqk, a.gam, (E*)a.h, (E*)a.vn};
     dim3 grid(a.NC, a.H), block(256);
     if (a.out_f32)
-        hipLaunchKernelGGL((output_kernel<D, F32, true>), grid, block, 0, st, a.cu, a.N, a.T, a.H, ws, a.o);
+        hipLaunchKernelGGL((output_kernel<D, F32, true>), grid, block, 0, st, a.tab, a.N, a.T, a.H, ws, a.o);
     else
-        hipLaunchKernelGGL((output_kernel<D, F32, false>), grid, block, 0, st, a.cu, a.N, a.T, a.H, ws, a.o);
+        hipLaunchKernelGGL((output_kernel<D, F32, false>), grid, block, 0, st, a.tab, a.N, a.T, a.H, ws, a.o);
     return hipGetLastError();
 }
 

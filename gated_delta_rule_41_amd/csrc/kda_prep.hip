@@ -117,7 +117,7 @@ template <int D, typename TIn, typename TG, bool F32, bool PRO = false>
 // CU; the register budget follows)
 __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(const TIn* q, const TIn* k, const TIn* v,
                                                       const TG* la, const TG* beta,
-                                                      const int32_t* __restrict__ cu, int N, int T, int H,
+                                                      const SeqMeta* __restrict__ tab, int N, int T, int H,
                                                       Ws<typename Pol<F32>::E> ws, ProArgs pa) {
     static_assert(!PRO || (!F32 && std::is_same<TIn, uint16_t>::value && std::is_same<TG, uint16_t>::value),
                   "the fused prologue is bf16 only");
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
     const int gc = blockIdx.x / H;
     const int h = blockIdx.x - gc * H;
     ChunkLoc loc;
-    if (!locate_chunk(cu, N, T, gc, loc)) return;
+    if (!locate_chunk(tab, N, T, gc, loc)) return;
     const int t0 = loc.t0, L = loc.L;
     const int64_t chh = (int64_t)gc * H + h;
 
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
         {
             constexpr int PG = 8;  // tokens per load group
             const int c0 = PER * l;
-            const int sstart = cu != nullptr ? cu[loc.seq] : 0;  // the chunk lies in one sequence
+            const int sstart = loc.start;  // the chunk lies in one sequence
             ConvFilters<D> f;
             using PR = Pair<uint16_t, PER>;
             float gs[PER] = {};  // log2 gate summed over rows 1..15 of this wave's block
@@ -831,7 +831,7 @@ static hipError_t launch_prep_t(const ChunkArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     dim3 grid(a.NC * a.H), block(256);  // NC * H < 2^31 (checked by the caller)
     hipLaunchKernelGGL(kern, grid, block, SM::BYTES, st, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                       (const TG*)a.la, (const TG*)a.beta, a.cu, a.N, a.T, a.H, ws, pa);
+                       (const TG*)a.la, (const TG*)a.beta, a.tab, a.N, a.T, a.H, ws, pa);
     return hipGetLastError();
 }
 

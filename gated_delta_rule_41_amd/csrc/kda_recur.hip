@@ -252,7 +252,7 @@ __device__ __forceinline__ void warm_chunk(const Ws<typename Pol<F32>::E>& ws, i
 template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false, bool ADDP = false>
 __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel(const float* __restrict__ s0,
                                                                   float* __restrict__ s_final,
-                                                                  const int32_t* __restrict__ cu, int N, int T,
+                                                                  const SeqMeta* __restrict__ tab, int N, int T,
                                                                   int H, Ws<typename Pol<F32>::E> ws,
                                                                   void* __restrict__ o) {
     using P = Pol<F32>;
@@ -287,8 +287,8 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
     const int seq = unit / H, h = unit % H;
     const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 15, g = l >> 4;
 
-    int co, nch;
-    seq_chunks(cu, T, seq, co, nch);
+    const SeqMeta sq = seq_info(tab, T, seq);
+    const int co = sq.coff, nch = sq.nch;
     char* hvbase = ring + RING * PL::SLOT;  // h_n / V_new exchange buffers (FUSED)
     char* pbase = hvbase + PL::HV;          // K-^T V buffers (DPLR)
 
@@ -297,8 +297,8 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
         // chunks j = p (mod 2) in iteration j + 1, once the compute wave has left
         // h_j and V_j in the exchange buffer j & 1.
         const int p = wv - 1;
-        const int tstart = cu ? cu[seq] : 0;
-        const int len = cu ? cu[seq + 1] - tstart : T;
+        const int tstart = sq.start;
+        const int len = sq.len;
         Frag qa[4][NS], aa[4][2];
         Frag al[PL::HP ? 4 : 1][2];  // HP: the low plane of A_qk
         u32x2_t ohr[4];  // DPLR: this slab's A_qk V tiles (fp16)
@@ -756,7 +756,7 @@ static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     const hipError_t e = allow_dynamic_lds((const void*)kern, PL::LDS);
     if (e != hipSuccess) return e;
     dim3 grid(NU * NT), block(FUSED ? (DPLR ? 448 : 384) : 64 * (PL::NCW + 2));
-    hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.cu, a.N, a.T, a.H, ws, a.o);
+    hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.tab, a.N, a.T, a.H, ws, a.o);
     return hipGetLastError();
 }
 

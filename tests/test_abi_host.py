@@ -49,11 +49,14 @@ def test_workspace_size_formula():
     # per chunk-head, d = 128, 16-bit factors: Q+, K-, -W 16 KiB each, U 32 KiB (fp32),
     # A_qk 16 KiB (two fp16 planes), gamma 512 B -> 98816 B (the fused output keeps
     # h_n and V_new on chip); chunks = floor((T + 63 N) / 64)
-    assert kda.workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 98816
-    assert kda.workspace_size(16, 135000, 32, 128, 128) == ((135000 + 63 * 16) // 64) * 32 * 98816
+    # plus the sequence table at the end: (N + 1) x 16 B, rounded up to 256
+    assert kda.workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 98816 + 256
+    assert kda.workspace_size(16, 135000, 32, 128, 128) == ((135000 + 63 * 16) // 64) * 32 * 98816 + 512
+    assert kda.workspace_size(4096, 409600, 32, 128, 128) == (
+        ((409600 + 63 * 4096) // 64) * 32 * 98816 + (4097 * 16 + 255) // 256 * 256)
     # fp32 factors double every array but gamma, and add h_n and V_new
     assert kda.workspace_size(1, 256, 1, 64, 64, __import__("torch").float32) == 4 * (
-        4 * (64 * 64 * 4) + 64 * 64 * 4 + 64 * 4 + 64 * 64 * 4 + 64 * 64 * 4)
+        4 * (64 * 64 * 4) + 64 * 64 * 4 + 64 * 4 + 64 * 64 * 4 + 64 * 64 * 4) + 256
     with pytest.raises(kda.KDAError):
         kda.workspace_size(1, 10, 1, 96, 96)
     with pytest.raises(kda.KDAError):
@@ -148,8 +151,9 @@ def test_decode_validation():
 def test_dplr_workspace_size_formula():
     # per chunk-head, d = 128: Q+, A-^T, -W', -U', A_qk V 16 KiB each (fp16),
     # K-^T V 32 KiB, A_qa 8 KiB, gamma 512 B -> 123392 B
-    assert kda.dplr_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 123392
-    assert kda.dplr_workspace_size(3, 100, 2, 64, 64) == ((100 + 63 * 3) // 64) * 2 * (6 * 8192 + 8192 + 256)
+    # (+ the sequence table, (N + 1) x 16 B rounded up to 256)
+    assert kda.dplr_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 123392 + 256
+    assert kda.dplr_workspace_size(3, 100, 2, 64, 64) == ((100 + 63 * 3) // 64) * 2 * (6 * 8192 + 8192 + 256) + 256
     with pytest.raises(kda.KDAError):
         kda.dplr_workspace_size(1, 10, 1, 96, 96)
     out = ctypes.c_size_t(0)
@@ -193,11 +197,12 @@ def test_bwd_workspace_size_formula():
     # state-gradient recursion), the added term Q+^T dO 64 KiB, the gated key
     # products 16 KiB and the local kernel's scratch (dQ+, dK-) 64 KiB -> 640000 B
     fwd = 5 * 32768 + 16384 + 512 + 65536
-    assert kda.bwd_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * (2 * fwd + 65536 + 16384 + 65536)
-    assert kda.bwd_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 640000
+    # (+ the sequence table, (N + 1) x 16 B rounded up to 256)
+    assert kda.bwd_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * (2 * fwd + 65536 + 16384 + 65536) + 256
+    assert kda.bwd_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 640000 + 256
     fwd64 = 5 * 16384 + 16384 + 256 + 16384
     assert kda.bwd_workspace_size(2, 100, 1, 64, 64) == ((100 + 63 * 2) // 64) * (
-        2 * fwd64 + 16384 + 16384 + 32768)
+        2 * fwd64 + 16384 + 16384 + 32768) + 256
     with pytest.raises(kda.KDAError):
         kda.bwd_workspace_size(1, 10, 1, 64, 128)
 
@@ -316,7 +321,7 @@ def test_layer_fwd_workspace_and_validation():
     """The fused prologue + prefill: workspace = the bf16 forward's plus 2 x 64 x d
     bf16 per chunk-head (the exact path's q, k rows); host validation refuses
     every malformed call before any launch."""
-    assert kda.layer_chunk_fwd_workspace_size(1, 4096, 32, 128) == 64 * 32 * (98816 + 2 * 64 * 128 * 2)
+    assert kda.layer_chunk_fwd_workspace_size(1, 4096, 32, 128) == 64 * 32 * (98816 + 2 * 64 * 128 * 2) + 256
     assert kda.layer_chunk_fwd_workspace_size(16, 135000, 32, 64) == (
         kda.workspace_size(16, 135000, 32, 64, 64) + ((135000 + 63 * 16) // 64) * 32 * 2 * 64 * 64 * 2)
     with pytest.raises(kda.KDAError):

@@ -38,6 +38,14 @@ def plan(NC, H, D, f32):
     return off, o
 
 
+def seq_table(ws: torch.Tensor, N, T, H, D, f32, have_cu=True) -> np.ndarray:
+    """The sequence table at the end of the workspace: [N + 1][start, len,
+    first chunk slot, chunk count] int32."""
+    _, o = plan(chunk_capacity(N, T, have_cu), H, D, f32)
+    raw = ws[o:o + (N + 1) * 16].cpu().numpy()
+    return raw.view(np.int32).reshape(N + 1, 4).copy()
+
+
 def _as_f(raw: np.ndarray, f32: bool) -> np.ndarray:
     """fp32 factors with fp32 inputs; fp16 factors with bf16 inputs."""
     if f32:
