@@ -1,25 +1,29 @@
 """Benchmark of the KDA hot path on one MI355X.
 
 One step = one chunkwise prefill call (per-chunk preparation, then the
-inter-chunk state recursion with the chunk outputs fused in) on the
-``prefill-4k`` workload: B=1, H=32,
-T=4096, dk=dv=128, chunk 64, bf16 inputs, fp32 initial/final state and fp32
-output (synthetic, seeded; see kda_inputs). The decode step (the remaining row
-of the hot path) is timed in the same run on ``decode-256`` (256 sequences x 32
-heads, fp32 states of 512 MiB, updated in place) and reported in the same JSON
-line. Prints ONE JSON line. The general-DPLR comparison operator (the transition KDA specialises,
-with free low-rank vectors a, b) is timed on the same workload and reported
-beside it under "dplr_comparison", the chunkwise backward (gradients of
-q, k, v, log_alpha, beta and the initial state) under "backward", and the layer
-around the operator (prologue, operator, epilogue) under "layer".
+inter-chunk state recursion with the chunk outputs fused in) on ``long-1m``,
+the largest single-GPU workload: B=1, H=32, T=1,048,576 (16,384 chunks of 64
+chained per head), dk=dv=128, bf16 inputs, fp32 initial/final state and fp32
+output, inputs resident in HBM (synthetic, seeded; see kda_inputs). Timing
+protocol: W untimed warm-up calls; then K calls, each preceded by a 512 MiB
+write that flushes the 256 MB Infinity Cache (MALL), timed with HIP events on
+the launch stream ("cold", the primary figure; median and min), then K calls
+back to back ("warm"). The same protocol runs on ``prefill-4k`` and
+``varlen-16`` (reported under "workloads"). The decode step (the remaining row
+of the hot path) is timed on ``decode-256`` (256 sequences x 32 heads, fp32
+states of 512 MiB, updated in place, 1000 steps). The general-DPLR comparison
+operator, the chunkwise backward and the layer around the operator are timed on
+prefill-4k. Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--decode-steps S] [--no-cpu-baseline] [--no-dplr]
-                    [--no-bwd] [--no-layer]
+    python bench.py [--steps K] [--warmup W] [--decode-steps S] [--headline-only] [--no-cpu-baseline]
+                    [--no-dplr] [--no-bwd] [--no-layer] [--no-decode]
 
 Profiling helpers (used to write the summaries under profiles/):
     python bench.py --copy-calibration MIB        # counter calibration kernel only
     python bench.py --report-trace DB             # kernel-trace database -> markdown
-    python bench.py --report-pmc FETCH_DB WRITE_DB CAL_FETCH_DB CAL_WRITE_DB CAL_BYTES
+    python bench.py --report-pmc WORKLOAD FETCH_DB WRITE_DB CAL_FETCH_DB CAL_WRITE_DB CAL_BYTES
+    python bench.py --report-counters DB [DB ...]  # any --pmc counters -> markdown, per kernel
+    python bench.py --profile-set long-1m|prefill-4k   # one workload's dispatches per profile
 """
 from __future__ import annotations
 
@@ -42,10 +46,14 @@ PEAK_HBM = 8.0e12        # HBM3E, B/s
 # the operator's compulsory HBM bytes (its inputs and its output, once each)
 FLOP_PER_TOKEN_HEAD = 140629
 ALG_BYTES_PER_TOKEN_HEAD = 1538            # q,k,v,log_alpha bf16 + beta bf16 + o fp32
-KERNEL_BYTES_PER_TOKEN_HEAD = {            # compulsory traffic of each prefill kernel
-    "prep": 1026 + 1160,                   # reads q,k,v,log_alpha,beta; writes Q+,K-,W,U,A_qk,gamma
-    # with bf16 inputs the output is fused into the state recursion:
-    "recur": 776 + 384 + 512,              # reads W,K-,U,gamma,Q+,A_qk; writes o (fp32)
+# this design's own pipeline traffic (its intermediates included), per token-head:
+KERNEL_BYTES_PER_TOKEN_HEAD = {
+    # reads q,k,v,log_alpha,beta; writes Q+,K-,-W (fp16 256 each), U (fp32 512),
+    # A_qk (two fp16 planes 256), gamma 8
+    "prep": 1026 + 1544,
+    # with bf16 inputs the output is fused into the state recursion: reads -W, K-,
+    # Q+ (256 each), U 512, A_qk 256, gamma 8; writes o (fp32 512)
+    "recur": 1544 + 512,
 }
 # fp32 inputs (not benchmarked) run the unfused pair: recursion 776 + 768 (h_n,
 # V_new written), output 1152 + 512
@@ -143,11 +151,10 @@ def source_sha(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel: str, units: int):
+def traffic_from_profiles(kernel: str, workload: str = "prefill-4k"):
     """HBM bytes per launch from committed rocprofv3 --pmc counters, if they were
     taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_prefill-4k.json" if kernel != "decode"
-                        else "pmc_decode_decode-256.json")
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -159,7 +166,35 @@ def traffic_from_profiles(kernel: str, units: int):
     return rec.get("bytes_per_launch")
 
 
-def time_prefill(kda, case, steps, warmup, hip, stream):
+class Flusher:
+    """Writes a scratch buffer larger than the 256 MB Infinity Cache (MALL), on
+    torch's current stream, so the next call starts with cold caches."""
+
+    def __init__(self, mib: int, dev):
+        import torch
+        self.mib = mib
+        self.buf = torch.empty(mib * (1 << 20) // 4, dtype=torch.float32, device=dev) if mib > 0 else None
+
+    def __call__(self):
+        if self.buf is not None:
+            self.buf.fill_(1.0)
+
+
+def _stats(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return round(med, 5), round(xs[0], 5)
+
+
+def time_prefill(kda, case, steps, warmup, hip, stream, flush):
+    """The prefill timing protocol: ``warmup`` untimed calls; then ``steps``
+    calls each preceded by a cache flush ("cold"), with HIP events recorded by
+    the library on the launch stream before the preparation kernel, between it
+    and the recursion, and after the recursion (its output is fused with bf16
+    inputs); the wall clock brackets these steps (flushes included) between two
+    synchronizations; then ``steps`` calls back to back, each between two events
+    ("warm"). Returns a dict of per-call times (ms) and the outputs."""
     import torch
     dev = case.q.device
     ws = torch.empty(kda.workspace_size(case.N, case.T_total, case.H, case.dk, case.dv, case.q.dtype),
@@ -173,27 +208,63 @@ def time_prefill(kda, case, steps, warmup, hip, stream):
 
     for _ in range(warmup):
         call()
+    # the flush kernel and the event-recording path run once before the timed
+    # loop (the first launch of a kernel pays its module load on the host)
+    flush()
+    ev0 = Events(hip, 4)
+    call(events=ev0.ev)
     torch.cuda.synchronize()
+    ev0.close()
+    ev = Events(hip, 4 * steps)
     t0 = time.perf_counter()
-    for _ in range(steps):
-        call()
+    for s_ in range(steps):
+        flush()
+        call(events=ev.ev[4 * s_:4 * s_ + 4])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    # per-kernel durations: HIP events at the stage boundaries, on the launch stream
-    ev = Events(hip, 4 * steps)
-    for s in range(steps):
-        call(events=ev.ev[4 * s:4 * s + 4])
-    torch.cuda.synchronize()
-    per = {"prep": 0.0, "recur": 0.0}
-    span = 0.0
-    for s in range(steps):
-        b = 4 * s
-        per["prep"] += ev.ms(b, b + 1)
-        per["recur"] += ev.ms(b + 1, b + 3)  # state recursion with the fused output
-        span += ev.ms(b, b + 3)
+    res = {"wall_ms": wall_ms, "cold": [], "prep": [], "recur": []}
+    for s_ in range(steps):
+        b = 4 * s_
+        res["cold"].append(ev.ms(b, b + 3))
+        res["prep"].append(ev.ms(b, b + 1))
+        res["recur"].append(ev.ms(b + 1, b + 3))  # state recursion with the fused output
     ev.close()
-    per = {k_: v_ / steps for k_, v_ in per.items()}
-    return wall_ms, per, span / steps, o, fs
+    ev = Events(hip, 2 * steps)
+    for s_ in range(steps):
+        ev.record(2 * s_, stream)
+        call()
+        ev.record(2 * s_ + 1, stream)
+    torch.cuda.synchronize()
+    res["warm"] = [ev.ms(2 * s_, 2 * s_ + 1) for s_ in range(steps)]
+    ev.close()
+    del ws
+    return res, o, fs
+
+
+def prefill_report(case, res):
+    """Throughput and roofline figures of one prefill workload from its timings."""
+    TH = case.T_total * case.H
+    flops = FLOP_PER_TOKEN_HEAD * TH
+    states = (2 if case.initial_state is not None else 1) * case.N * case.H * case.dk * case.dv * 4
+    alg_bytes = ALG_BYTES_PER_TOKEN_HEAD * TH + states
+    ceiling = min(PEAK_BF16, flops / alg_bytes * PEAK_HBM)
+    cold_med, cold_min = _stats(res["cold"])
+    warm_med, warm_min = _stats(res["warm"])
+    kern = {"prep": _stats(res["prep"])[0], "recur": _stats(res["recur"])[0]}
+    dom = max(kern, key=kern.get)
+    achieved = alg_bytes / (kern[dom] * 1e-3)
+    rep = {"T_total": case.T_total, "N": case.N, "H": case.H,
+           "cold_ms_median": cold_med, "cold_ms_min": cold_min, "warm_ms_median": warm_med,
+           "warm_ms_min": warm_min, "tokens_per_s": round(case.T_total / (cold_med * 1e-3), 1),
+           "tflops": round(flops / (cold_med * 1e-3) / 1e12, 2),
+           "mfma_peak_frac": round(flops / (cold_med * 1e-3) / PEAK_BF16, 4),
+           "alg_roofline_frac": round(flops / (cold_med * 1e-3) / ceiling, 4),
+           "alg_ceiling_tflops": round(ceiling / 1e12, 1), "alg_bytes": alg_bytes,
+           "kernel_ms_cold_median": kern}
+    roof = {"kernel": KERNEL_SYMBOL[dom], "bound": "hbm", "achieved": round(achieved / 1e9, 1),
+            "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
+            "avg_launch_ms": kern[dom], "alg_bytes_per_launch": alg_bytes}
+    return rep, roof, dom
 
 
 def time_dplr(kda, case, steps, warmup):
@@ -432,23 +503,73 @@ def copy_bandwidth(hip, stream, mib: int = 1024, reps: int = 20):
     return 2 * 4 * n / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(case):
-    """The oracle (fp64 token recurrence, OpenMP over (sequence, head, column
-    block)) on the host cores, on the same prefill-4k inputs copied to host."""
+def cpu_baseline(host, T, H, dk, rec_pos, threads):
+    """The oracle (fp64 token recurrence, OpenMP over (head, column block)) on
+    the host cores, on the headline workload's own inputs copied to the host:
+    every head over the whole sequence, the output kept at ``rec_pos`` only."""
     import oracle
+    t0 = time.perf_counter()
+    _, S_ref, o_rec = oracle.recurrence(*host, None, want_o=False, rec_pos=rec_pos, col_blocks=1,
+                                        threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"long-1m in full (T={T}, all {H} heads, d={dk}, fp64 token recurrence; final states "
+                      f"and o at {len(rec_pos)} sampled positions kept), {dt:.1f} s wall"}, S_ref, o_rec
+
+
+def cpu_single_thread(case, heads=None):
+    """The oracle on one host thread, on a bounded sample of prefill-4k (the
+    first ``heads`` heads, default all, over the whole sequence), as tokens/s
+    of all heads."""
+    import oracle
+    heads = case.H if heads is None else heads
     host = [t.cpu() for t in (case.q, case.k, case.v, case.log_alpha, case.beta, case.initial_state)]
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
-    heads = list(range(case.H))
-    reps, t0 = 0, time.perf_counter()
-    while True:  # whole passes over the workload until about 10 s of host work
-        oracle.recurrence(*host, None, heads=heads, want_o=True, col_blocks=2, threads=threads)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or reps >= 1000:
+    t0 = time.perf_counter()
+    oracle.recurrence(*host, None, heads=list(range(heads)), want_o=True, col_blocks=1, threads=1)
+    dt = time.perf_counter() - t0
+    return {"value": case.T_total * heads / case.H / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"prefill-4k, {heads} of {case.H} heads over T={case.T_total}, one thread, {dt:.1f} s wall"}
+
+
+def environment():
+    """What ran: GPU, ROCm, torch, host CPU, and the library's source hash (and
+    the git commit when the tree has one)."""
+    import torch
+    env = {}
+    try:
+        p = torch.cuda.get_device_properties(0)
+        env["gpu"] = p.name
+        env["gpu_arch"] = getattr(p, "gcnArchName", None)
+        env["gpu_cus"] = p.multi_processor_count
+    except Exception:  # pragma: no cover
+        pass
+    for f in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(f):
+            env["rocm"] = open(f).read().strip()
             break
-    return {"value": reps * case.T_total / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"prefill-4k in full (T={case.T_total}, H={case.H}, d={case.dk}, fp64 token "
-                      f"recurrence), {reps} passes in {dt:.1f} s wall"}, host
+    env["torch"] = torch.__version__
+    env["torch_hip"] = getattr(torch.version, "hip", None)
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                env["host_cpu"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    env["host_threads_visible"] = os.cpu_count()
+    h = hashlib.sha256()
+    for d in ("gated_delta_rule_41_amd/csrc", "include"):
+        for f in sorted(os.listdir(os.path.join(ROOT, d))):
+            with open(os.path.join(ROOT, d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    env["library_source_sha16"] = h.hexdigest()[:16]
+    try:
+        import subprocess
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        env["git_commit"] = r.stdout.strip() if r.returncode == 0 else None
+    except Exception:  # pragma: no cover
+        env["git_commit"] = None
+    return env
 
 
 def copy_calibration(mib: int = 512, reps: int = 5):
@@ -497,12 +618,14 @@ def _counter_avg(db: str, counter: str, like: str):
                        (counter, like)).fetchall()
 
 
-def report_pmc(fetch_db: str, write_db: str, cal_fetch_db: str, cal_write_db: str, cal_bytes: int) -> int:
+def report_pmc(workload: str, fetch_db: str, write_db: str, cal_fetch_db: str, cal_write_db: str,
+               cal_bytes: int) -> int:
     """HBM traffic per launch of each library kernel from FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch, one rocprofv3 --pmc run each), each scaled by
     what the same counter reads for the calibration copy kernel of known size.
-    Writes profiles/pmc_<kernel>_<workload>.json (read back by the roofline
-    report while the kernel source is unchanged) and prints a markdown table."""
+    Writes profiles/pmc_<kernel>_<workload>.json (the decode kernel's as
+    decode-256; read back by the roofline report while the kernel source is
+    unchanged) and prints a markdown table."""
     cf = _counter_avg(cal_fetch_db, "FETCH_SIZE", "%MulFunctor%")
     cw = _counter_avg(cal_write_db, "WRITE_SIZE", "%MulFunctor%")
     if not cf or not cw:
@@ -524,7 +647,7 @@ def report_pmc(fetch_db: str, write_db: str, cal_fetch_db: str, cal_write_db: st
         print(f"| `{name}` | {fe[name][0]} | {fe[name][1]:.0f} | {wr[name][1]:.0f} | {b:.4g} |")
         if kern is None:
             continue
-        wl = "decode-256" if kern == "decode" else "prefill-4k"
+        wl = "decode-256" if kern == "decode" else workload
         rec = {"kernel": name, "workload": wl, "source_sha": source_sha(kern),
                "fetch_kib": fe[name][1], "write_kib": wr[name][1],
                "fetch_scale": f_fetch, "write_scale": f_write, "bytes_per_launch": round(b)}
@@ -533,19 +656,70 @@ def report_pmc(fetch_db: str, write_db: str, cal_fetch_db: str, cal_write_db: st
     return 0
 
 
+def report_counters(*dbs: str) -> int:
+    """Markdown table of every counter in one or more rocprofv3 --pmc databases,
+    averaged per dispatch of each of this library's kernels, with the derived
+    ratios used in the kernel analysis when their counters are present."""
+    rows = {}
+    for db in dbs:
+        cur = _rocpd(db)
+        for name, counter, n, val in cur.execute(
+                "select kernel_name, counter_name, count(*), avg(value) from counters_collection "
+                "where kernel_name like '%kda::%' group by kernel_name, counter_name").fetchall():
+            rows.setdefault(_short(name), {})[counter] = (n, val)
+    counters = sorted({c for r in rows.values() for c in r})
+    print("| kernel | " + " | ".join(counters) + " |")
+    print("|---|" + "---|" * len(counters))
+    for name in sorted(rows):
+        vals = [f"{rows[name][c][1]:.4g}" if c in rows[name] else "" for c in counters]
+        print(f"| `{name}` | " + " | ".join(vals) + " |")
+    print()
+    for name in sorted(rows):
+        r = {c: v for c, (_, v) in rows[name].items()}
+        parts = []
+        if "SQ_WAIT_INST_ANY" in r and "SQ_WAVE_CYCLES" in r and r["SQ_WAVE_CYCLES"]:
+            parts.append(f"wave cycles waiting on an instruction's inputs {r['SQ_WAIT_INST_ANY'] / r['SQ_WAVE_CYCLES']:.1%}")
+        if "SQ_WAIT_ANY" in r and "SQ_WAVE_CYCLES" in r and r["SQ_WAVE_CYCLES"]:
+            parts.append(f"waiting on anything {r['SQ_WAIT_ANY'] / r['SQ_WAVE_CYCLES']:.1%}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in r and "GRBM_GUI_ACTIVE" in r and r["GRBM_GUI_ACTIVE"]:
+            # MFMA busy cycles are summed over the 1,024 SIMDs; GRBM_GUI_ACTIVE
+            # over the 8 XCDs (8 x the kernel's elapsed cycles)
+            simd_cycles = r["GRBM_GUI_ACTIVE"] / 8 * 1024
+            parts.append(f"matrix cores busy {r['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.1%} of SIMD cycles")
+        if "SQ_LDS_BANK_CONFLICT" in r and "SQ_ACTIVE_INST_LDS" in r and r["SQ_ACTIVE_INST_LDS"]:
+            parts.append(f"LDS bank-conflict cycles per active LDS cycle "
+                         f"{r['SQ_LDS_BANK_CONFLICT'] / r['SQ_ACTIVE_INST_LDS']:.3f}")
+        if "TCC_HIT_sum" in r and "TCC_MISS_sum" in r and (r["TCC_HIT_sum"] + r["TCC_MISS_sum"]):
+            parts.append(f"L2 hit rate {r['TCC_HIT_sum'] / (r['TCC_HIT_sum'] + r['TCC_MISS_sum']):.1%}")
+        if "SQ_WAVES" in r:
+            parts.append(f"waves {r['SQ_WAVES']:.4g}")
+        if parts:
+            print(f"- `{name}`: " + "; ".join(parts))
+    return 0
+
+
 def main(argv=None):
     if argv is None:
         argv = sys.argv[1:]
     if argv[:1] == ["--report-trace"]:
         return report_trace(argv[1])
+    if argv[:1] == ["--report-counters"]:
+        return report_counters(*argv[1:])
     if argv[:1] == ["--report-pmc"]:
-        return report_pmc(argv[1], argv[2], argv[3], argv[4], int(argv[5]))
+        return report_pmc(argv[1], argv[2], argv[3], argv[4], argv[5], int(argv[6]))
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=500,
-                    help="untimed prefill steps first (500 take ~80 ms and bring the GPU to steady clocks)")
+    ap.add_argument("--steps", type=int, default=5, help="timed calls per protocol leg")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed calls first")
+    ap.add_argument("--flush-mib", type=int, default=512, help="cache flush written before each cold call")
     ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the long-1m prefill (for profiling runs)")
+    ap.add_argument("--profile-set", choices=["long-1m", "prefill-4k"], default=None,
+                    help="profiling runs: only the long-1m prefill, or only the prefill-4k-sized legs (prefill-4k, "
+                         "DPLR, backward, layer) and decode-256, so each profile holds one workload's dispatches")
+    ap.add_argument("--workloads", default="prefill-4k,varlen-16",
+                    help="prefill workloads timed beside the headline (same protocol)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dplr", action="store_true", help="skip the general-DPLR comparison")
@@ -563,7 +737,11 @@ def main(argv=None):
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "multi-GPU sharding is not implemented", file=sys.stderr)
         return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
 
+    import numpy as np
     import torch
     import gated_delta_rule_41_amd as kda
     import kda_inputs as ki
@@ -575,46 +753,101 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     hip = hip_runtime()
     stream = torch.cuda.current_stream(dev).cuda_stream
+    flush = Flusher(args.flush_mib, dev)
+    if args.profile_set == "long-1m":
+        args.headline_only = True
+    if args.headline_only:
+        args.no_cpu_baseline = args.no_decode = args.no_dplr = args.no_bwd = args.no_layer = True
+        args.workloads = ""
+    t_start = time.perf_counter()
+    if args.profile_set == "prefill-4k":
+        args.no_cpu_baseline = True
+        args.no_layer_decode = True
+        args.workloads = "prefill-4k"
+        return side_legs(args, kda, ki, hip, stream, flush, dev, {"profile_set": "prefill-4k"}, t_start)
 
-    case = ki.make_prefill("prefill-4k", dev)
-    TH = case.T_total * case.H
-    wall_ms, per, span_ms, o, fs = time_prefill(kda, case, args.steps, args.warmup, hip, stream)
-    tokens_per_s = case.T_total / (wall_ms * 1e-3)
-    flops = FLOP_PER_TOKEN_HEAD * TH
-    tflops = flops / (wall_ms * 1e-3) / 1e12
-    alg_bytes = ALG_BYTES_PER_TOKEN_HEAD * TH + 2 * case.N * case.H * case.dk * case.dv * 4
-    ai = flops / alg_bytes
-    ceiling = min(PEAK_BF16, ai * PEAK_HBM)
-
-    dom = max(per, key=per.get)
-    kb = KERNEL_BYTES_PER_TOKEN_HEAD[dom] * TH
-    if dom == "recur":  # plus the initial and final states
-        kb += 2 * case.N * case.H * case.dk * case.dv * 4
-    achieved = kb / (per[dom] * 1e-3) / 1e9
-    roof = {"kernel": KERNEL_SYMBOL[dom], "bound": "hbm", "achieved": round(achieved, 1),
-            "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4),
-            "traffic": traffic_from_profiles(dom, TH), "avg_launch_ms": round(per[dom], 5),
-            "alg_bytes_per_launch": kb}
-
+    # ---- headline: long-1m, the largest single-GPU workload
+    case = ki.make_prefill("long-1m", dev)
+    res, o, fs = time_prefill(kda, case, args.steps, args.warmup, hip, stream, flush)
+    rep, roof, dom = prefill_report(case, res)
+    roof["traffic"] = traffic_from_profiles(dom, "long-1m")
+    pipe = [traffic_from_profiles(k_, "long-1m") for k_ in ("prep", "recur")]
+    roof["pipeline_traffic_ratio"] = (round(sum(pipe) / rep["alg_bytes"], 3) if all(x is not None for x in pipe)
+                                      else None)
+    n_chunks = (case.T_total + 63) // 64
+    rep["recur_us_per_chunk_step"] = round(rep["kernel_ms_cold_median"]["recur"] * 1e3 / n_chunks, 4)
+    rep["wall_ms_per_step_incl_flush"] = round(res["wall_ms"], 5)
+    rep["flush_mib"] = args.flush_mib
     out = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
+        "metric": METRIC, "value": round(case.T_total / (res["wall_ms"] * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["wall_ms"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16/f32",
         "data": "synthetic",
-        "config": {"workload": "prefill-4k", "B": 1, "T": case.T_total, "H": case.H, "dk": case.dk,
+        "config": {"workload": "long-1m", "B": 1, "T": case.T_total, "H": case.H, "dk": case.dk,
                    "dv": case.dv, "chunk": 64, "inputs": "bf16", "state": "f32", "o": "f32",
-                   "log_alpha": "-softplus(N(0,1)+2)"},
-        "prefill": {"tflops": round(tflops, 2), "mfma_peak_frac": round(tflops * 1e12 / PEAK_BF16, 4),
-                    "alg_roofline_frac": round(flops / (wall_ms * 1e-3) / ceiling, 4),
-                    "alg_ceiling_tflops": round(ceiling / 1e12, 1),
-                    "kernel_ms": {k_: round(v_, 5) for k_, v_ in per.items()},
-                    "event_span_ms": round(span_ms, 5)},
+                   "log_alpha": "-softplus(N(0,1)+2)", "initial_state": "N(0, 0.02)"},
+        "prefill": rep,
         "roofline": roof,
     }
+    # what the oracle needs later, on the host; the GPU copies are freed
+    rec_pos = None
+    host = None
+    if not args.no_cpu_baseline:
+        g = np.random.default_rng(2024)
+        rec_pos = np.unique(np.concatenate([g.integers(0, case.T_total, 4096),
+                                            [0, 63, 64, 65535, 65536, case.T_total - 1]]))
+        o_samp = o[torch.tensor(rec_pos, device=dev)].double().cpu().numpy()
+        fs_host = fs.double().cpu().numpy()
+        host = [t.cpu() for t in (case.q, case.k, case.v, case.log_alpha, case.beta, case.initial_state)]
+    T_head, H_head, dk_head = case.T_total, case.H, case.dk
+    del case, o, fs
+    torch.cuda.empty_cache()
+    if args.headline_only:
+        out["env"] = environment()
+        out["bench_wall_s"] = round(time.perf_counter() - t_start, 1)
+        print(json.dumps(out))
+        return 0
+
+    return side_legs(args, kda, ki, hip, stream, flush, dev, out, t_start,
+                     (host, rec_pos, o_samp, fs_host, T_head, H_head, dk_head) if host is not None else None)
+
+
+def side_legs(args, kda, ki, hip, stream, flush, dev, out, t_start, headline_host=None):
+    """Everything after the headline: the other prefill workloads, the
+    comparison legs at prefill-4k size, decode-256, and the CPU baselines."""
+    import numpy as np
+    import torch
+    # ---- the other prefill workloads, same protocol
+    wls = [w for w in args.workloads.split(",") if w]
+    if wls:
+        out["workloads"] = {}
+    case4k = None
+    for wl in wls:
+        c = ki.make_prefill(wl, dev)
+        r_, o_, f_ = time_prefill(kda, c, max(args.steps, 20), max(args.warmup, 200 if c.T_total <= 8192 else 5),
+                                  hip, stream, flush)
+        wrep, wroof, wdom = prefill_report(c, r_)
+        wroof["traffic"] = traffic_from_profiles(wdom, wl)
+        wrep["roofline"] = wroof
+        out["workloads"][wl] = wrep
+        if wl == "prefill-4k":
+            case4k = c
+        del o_, f_
+    torch.cuda.empty_cache()
+    if case4k is None:
+        case4k = ki.make_prefill("prefill-4k", dev)
+    case = case4k
+    TH = case.T_total * case.H
+    if "prefill-4k" in wls:
+        wall_ms = out["workloads"]["prefill-4k"]["warm_ms_median"]
+    else:  # the comparisons below are against prefill-4k, warm, back to back
+        r_, _, _ = time_prefill(kda, case, 20, 200, hip, stream, Flusher(0, dev))
+        wall_ms = _stats(r_["warm"])[0]
+    side_steps, side_warm = 20, 50  # the comparison legs (prefill-4k size, warm clocks)
 
     if not args.no_dplr:
         dcase = ki.make_dplr("prefill-4k", dev)
-        dplr_ms, _, _ = time_dplr(kda, dcase, args.steps, max(3, min(200, args.warmup)))
+        dplr_ms, _, _ = time_dplr(kda, dcase, side_steps, side_warm)
         # per token-head, d = 128, chunk 64: four gated chunk matrices, three
         # WY/intra products, three d x d state products, output (see DESIGN)
         dplr_flops = 206165 * TH
@@ -623,22 +856,22 @@ def main(argv=None):
             "tokens_per_s": round(case.T_total / (dplr_ms * 1e-3), 1),
             "tflops": round(dplr_flops / (dplr_ms * 1e-3) / 1e12, 2),
             "time_ratio_dplr_over_kda": round(dplr_ms / wall_ms, 3),
-            "hbm_bytes_per_launch": {"prep": traffic_from_profiles("dplr_prep", TH),
-                                     "recur": traffic_from_profiles("dplr_recur", TH)}}
+            "hbm_bytes_per_launch": {"prep": traffic_from_profiles("dplr_prep"),
+                                     "recur": traffic_from_profiles("dplr_recur")}}
         del dcase
 
     if not args.no_bwd:
-        bwd_ms, _, ws_bytes = time_bwd(kda, case, max(5, args.steps // 5), max(3, min(50, args.warmup)))
+        bwd_ms, _, ws_bytes = time_bwd(kda, case, 5, 3)
         out["backward"] = {
             "workload": "prefill-4k, d_o ~ N(0,1), d_final_state ~ N(0, 0.01)",
             "ms_per_step": round(bwd_ms, 5), "tokens_per_s": round(case.T_total / (bwd_ms * 1e-3), 1),
             "time_ratio_bwd_over_fwd": round(bwd_ms / wall_ms, 3), "workspace_bytes": ws_bytes,
-            "hbm_bytes_per_launch": {k_: traffic_from_profiles(k_, TH) for k_ in
+            "hbm_bytes_per_launch": {k_: traffic_from_profiles(k_) for k_ in
                                      ("bwd_fwd_prep", "bwd_fwd_recur", "bwd_prep", "bwd_recur", "bwd_local")}}
 
     if not args.no_layer:
         lc = ki.make_layer("prefill-4k", dev)
-        lt = time_layer(kda, lc, max(10, args.steps // 5), max(3, min(50, args.warmup)), hip, stream)
+        lt = time_layer(kda, lc, side_steps, side_warm, hip, stream)
         # compulsory bytes per token-head: prologue reads xq, xk, xv, xa (bf16, 4 x 256) and
         # xb (2), writes q, k, v, log_alpha (4 x 256) and beta (2); epilogue reads o (fp32 512)
         # and xg (256), writes y (256)
@@ -648,15 +881,15 @@ def main(argv=None):
             "ms": {k_: round(v_, 5) for k_, v_ in lt.items()},
             "tokens_per_s": round(case.T_total / (lt["layer"] * 1e-3), 1),
             "fused_tokens_per_s": round(case.T_total / (lt["fused_layer"] * 1e-3), 1),
-            "fused_prep_hbm_bytes_per_launch": traffic_from_profiles("layer_prep", TH),
+            "fused_prep_hbm_bytes_per_launch": traffic_from_profiles("layer_prep"),
             "prologue_roofline": {"bound": "hbm", "achieved": round(pro_b / (lt["prologue"] * 1e-3) / 1e9, 1),
                                   "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                                   "frac": round(pro_b / (lt["prologue"] * 1e-3) / PEAK_HBM, 4),
-                                  "traffic": traffic_from_profiles("layer_prologue", TH)},
+                                  "traffic": traffic_from_profiles("layer_prologue")},
             "epilogue_roofline": {"bound": "hbm", "achieved": round(epi_b / (lt["epilogue"] * 1e-3) / 1e9, 1),
                                   "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                                   "frac": round(epi_b / (lt["epilogue"] * 1e-3) / PEAK_HBM, 4),
-                                  "traffic": traffic_from_profiles("layer_epilogue", TH)}}
+                                  "traffic": traffic_from_profiles("layer_epilogue")}}
         del lc
         if not args.no_layer_decode:
             ld_ms = time_layer_decode(kda, ki, 200, 50, hip, stream)
@@ -681,21 +914,25 @@ def main(argv=None):
                          "roofline": {"kernel": "decode_kernel", "bound": "hbm",
                                       "achieved": round(alg / dms / 1e6, 1), "peak": PEAK_HBM / 1e9,
                                       "unit": "GB/s", "frac": round(alg / dms / 1e6 / (PEAK_HBM / 1e9), 4),
-                                      "traffic": traffic_from_profiles("decode", NH)}}
+                                      "traffic": traffic_from_profiles("decode", "decode-256")}}
         del dec
 
-    if not args.no_cpu_baseline:
-        import numpy as np
-        cb, host = cpu_baseline(case)
+    if not args.no_cpu_baseline and headline_host is not None:
+        host, rec_pos, o_samp, fs_host, T_head, H_head, dk_head = headline_host
+        del case
+        torch.cuda.empty_cache()
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
+        cb, S_ref, o_rec = cpu_baseline(host, T_head, H_head, dk_head, rec_pos, threads)
         out["cpu_baseline"] = cb
-        # spot parity of this very run against the oracle (head 0, all tokens)
-        import oracle
-        o_ref, s_ref, _ = oracle.recurrence(*host, None, heads=[0], col_blocks=8)
-        oo = o[:, 0].double().cpu().numpy()
-        ss = fs[0, 0].double().cpu().numpy()
-        e_o = float(np.max(np.abs(oo - o_ref[:, 0])) / np.sqrt(np.mean(o_ref[:, 0] ** 2)))
-        e_s = float(np.max(np.abs(ss - s_ref[0, 0])) / np.sqrt(np.mean(s_ref[0, 0] ** 2)))
-        out["parity_head0"] = {"err_o": e_o, "err_state": e_s, "tol": 2e-2}
+        out["cpu_single_thread"] = cpu_single_thread(ki.make_prefill("prefill-4k", dev))
+        # parity of this very run's headline call against the oracle's results
+        rms = lambda x: float(np.sqrt(np.mean(x * x)))
+        out["parity_long_1m"] = {
+            "err_o_sampled": float(np.max(np.abs(o_samp - o_rec)) / rms(o_rec)),
+            "err_final_state": float(np.max(np.abs(fs_host - S_ref)) / rms(S_ref)),
+            "positions": int(len(rec_pos)), "heads": H_head, "tol": 2e-2}
+    out["env"] = environment()
+    out["bench_wall_s"] = round(time.perf_counter() - t_start, 1)
     print(json.dumps(out))
     return 0
 
