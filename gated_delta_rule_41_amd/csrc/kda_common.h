@@ -195,6 +195,29 @@ template <> struct APol<false> {
         cq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi, b.lo, cq, 0, 0, 0);
         cq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi, b.hi, cq, 0, 0, 0);
     }
+    // The same with the query-key product transposed: cq += (xq B)^T, i.e. B
+    // is the A operand and xq the B operand. Its accumulator tile then holds,
+    // in lane n + 16 g, row n of xq B at columns 4 g .. 4 g + 3, which is the
+    // matrix-core operand layout of xq B: the tile is stored as operand
+    // fragments without any exchange between lanes.
+    static __device__ __forceinline__ void mma_qk_t(f32x4_t& cq, const float (&xq)[8], f32x4_t& ck,
+                                                    const float (&xk)[8], const Frag& b) {
+        u32x4_t qh, ql, kh;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t b0 = __float_as_uint(xq[2 * j]) & 0xffff0000u;
+            const uint32_t b1 = __float_as_uint(xq[2 * j + 1]) & 0xffff0000u;
+            qh[j] = (b0 >> 16) | b1;
+            ql[j] = pack2bf(xq[2 * j] - __uint_as_float(b0), xq[2 * j + 1] - __uint_as_float(b1));
+            kh[j] = pack2bf(xk[2 * j], xk[2 * j + 1]);
+        }
+        const bf16x8_t qhi = __builtin_bit_cast(bf16x8_t, qh), qlo = __builtin_bit_cast(bf16x8_t, ql);
+        const bf16x8_t khi = __builtin_bit_cast(bf16x8_t, kh);
+        cq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.hi, qlo, cq, 0, 0, 0);
+        ck = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, b.hi, ck, 0, 0, 0);
+        cq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.lo, qhi, cq, 0, 0, 0);
+        cq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.hi, qhi, cq, 0, 0, 0);
+    }
 };
 template <> struct APol<true> {
     using E = float;
@@ -303,13 +326,16 @@ __device__ __forceinline__ SeqMeta seq_info(const SeqMeta* __restrict__ tab, int
 
 // ---------------------------------------------------------------- workspace
 // Per (chunk slot, head) intermediates, each array [NC][H][...]:
-//   qp   [64][D]   gated queries  Q+ = exp(g) * q, rows in order, k = key channel (split order per 32)
+//   qp   [64][D]   gated queries  Q+ = exp(g) * q, rows in order, k = key channel (split order per 32);
+//                  with 16-bit KDA factors in fragment order [4 row blocks][D/32 slices][64 lanes][8]
+//                  (lane n + 16 g holds row 16 I + n, channels 32 s + kslot(g, 0..7))
 //   km   [D][64]   decayed keys K- = exp(g_last - g) * k, transposed: row = key channel, k = chunk row
 //   wn   [64][D]   -W (negated key WY factor), k = key channel (split order)
 //   u    [D/16][4][64 lanes][4]   U in accumulator-tile order (value col tile, row tile, lane, i);
 //                  fp32 with 16-bit KDA factors (uf), so the values are never rounded to fp16
 //   aqk  [64][64]  gated query-key matrix (lower incl. diagonal), k = chunk col (split order);
-//                  with 16-bit KDA factors two fp16 planes [hi][64][64], [lo][64][64] (x = hi + lo)
+//                  with 16-bit KDA factors two fp16 planes (x = hi + lo), each in fragment order
+//                  [4 row blocks][2 slices][64 lanes][8] like qp
 //   gam  [D] fp32  exp(g_last) per key channel
 //   h    [D/16][D/32][64 lanes][8]   chunk-entry state as B-operand fragments (value col tile, k slice)
 //   vn   [D/16][2][64 lanes][8]      corrected values V_new as B-operand fragments

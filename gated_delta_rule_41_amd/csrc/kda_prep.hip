@@ -418,6 +418,13 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
     const float br = beta_s[r];
     float qs[NS][8], ks[NS][8];  // q 2^(G - G_aw), k 2^(G - G_aw)  (fast path)
     E* qp_out = ws.qp + chh * 64 * D;
+    // Q+: with 16-bit operands in fragment order, [row block][slice][64 lanes][8]
+    // (each matrix-core operand fragment of the output product one contiguous
+    // 1 KiB); with fp32 operands row-major, [64][slices][32] (split order)
+    auto qp_at = [&](int s) -> int64_t {
+        if constexpr (SM::MT) return ((int64_t)(w * NS + s) * 64 + l) * 8;
+        return (int64_t)(r * NS + s) * 32 + g * 8;
+    };
     E* km_out = ws.km + chh * D * 64;
     const int kmpos = 32 * (r >> 5) + split_pos(r);
     // fast and slow paths each cover every slice inside one branch
@@ -467,7 +474,7 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
                 tr_slice(bkv, s, std::false_type{}, Bk_t);
             }
             AP::store(Kt_s + r * KTS + s * 32 + g * 8, SM::KT_PLANE, AP::make(ktv));
-            P::store(qp_out + (r * NS + s) * 32 + g * 8, P::make(qpv));
+            P::store(qp_out + qp_at(s), P::make(qpv));
         }
     } else {
 #pragma unroll
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
                 tr_slice(kmv, s, std::true_type{}, km_out);
                 tr_slice(bkv, s, std::false_type{}, Bk_t);
             }
-            P::store(qp_out + (r * NS + s) * 32 + g * 8, P::make(qpv));
+            P::store(qp_out + qp_at(s), P::make(qpv));
         }
     }
     __syncthreads();
@@ -572,9 +579,13 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
     // (16-bit operands: two fp16 planes, hi then lo, so the output's A_qk V_new
     // product sees about 22 significant bits of A_qk)
     E* aqk_out = ws.aqk + chh * 64 * 64 * (SM::MT ? 2 : 1);
+    // (16-bit operands: fragment order, [row block][slice][64 lanes][8] per plane,
+    // as Q+; fp32 operands: row-major [64][2][32], split order)
     auto aqk_put = [&](int rr, int cc, float x) {
         const int s2 = cc >> 5, c2 = cc & 31;
-        const int at = (rr * 2 + s2) * 32 + 8 * ((c2 & 15) >> 2) + 4 * (c2 >> 4) + (c2 & 3);
+        const int g2 = (c2 & 15) >> 2, j2 = 4 * (c2 >> 4) + (c2 & 3);
+        const int at = SM::MT ? ((((rr >> 4) * 2 + s2) * 64 + (rr & 15) + 16 * g2) * 8 + j2)
+                              : (rr * 2 + s2) * 32 + 8 * g2 + j2;
         const E hi = P::from_f(x);
         aqk_out[at] = hi;
         if constexpr (SM::MT) aqk_out[64 * 64 + at] = P::from_f(x - P::to_f(hi));
@@ -618,7 +629,36 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
                     xq[4 + j] = qs[s][4 + j] * b;
                     xk[4 + j] = ks[s][4 + j] * b;
                 }
-                AP::mma_qk(aq[J], xq, ak[J], xk, bkt[J]);
+                if constexpr (SM::MT)
+                    AP::mma_qk_t(aq[J], xq, ak[J], xk, bkt[J]);  // aq transposed: operand fragments
+                else
+                    AP::mma_qk(aq[J], xq, ak[J], xk, bkt[J]);
+            }
+        }
+        if constexpr (SM::MT) {
+            // A_qk in fragment order: lane n + 16 g holds row 16 I + n at columns
+            // 16 J + 4 g + i of each block J (transposed tiles); fragment (I, s)
+            // joins blocks 2 s and 2 s + 1. Causal mask on the diagonal block:
+            // column 4 g + i <= row n. Two fp16 planes, hi then lo.
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                float x[8];
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    constexpr int NJ = I + 1;
+                    const int J = 2 * s2 + hb;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = 0.f;
+                        if (J < I) v = aq[J < NJ ? J : 0][i];
+                        else if (J == I) v = (4 * g + i <= n) ? aq[J < NJ ? J : 0][i] : 0.f;
+                        x[4 * hb + i] = v;
+                    }
+                }
+                const Frag2 fx = split_frag(x);
+                E* dst = aqk_out + ((I * 2 + s2) * 64 + l) * 8;
+                P::store(dst, fx.hi);
+                P::store(dst + 64 * 64, fx.lo);
             }
         }
 #pragma unroll
@@ -626,7 +666,7 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
             if (J > I) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    aqk_put(16 * I + 4 * g + i, 16 * J + n, 0.f);
+                    if constexpr (!SM::MT) aqk_put(16 * I + 4 * g + i, 16 * J + n, 0.f);
                     if (pkk_out) pkk_out[(16 * I + 4 * g + i) * 64 + 16 * J + n] = 0.f;
                 }
                 continue;
@@ -637,7 +677,7 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
                 const int rl = 4 * g + i;  // row inside the block
                 const bool lo_incl = (J < I) || (n <= rl);
                 const bool lo_strict = (J < I) || (n < rl);
-                aqk_put(16 * I + rl, 16 * J + n, lo_incl ? aq[J][i] : 0.f);
+                if constexpr (!SM::MT) aqk_put(16 * I + rl, 16 * J + n, lo_incl ? aq[J][i] : 0.f);
                 Akk_s[blk * AKB + rl * AKS + n] = lo_strict ? ak[J][i] * beta_s[16 * I + rl] : 0.f;
                 if (pkk_out) pkk_out[(16 * I + rl) * 64 + 16 * J + n] = lo_strict ? ak[J][i] : 0.f;
             }

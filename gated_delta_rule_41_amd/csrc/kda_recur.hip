@@ -311,25 +311,27 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
                 for (int I = 0; I < 4; ++I)
                     ohr[I] = *reinterpret_cast<const u32x2_t*>(ws.oh + chh * 64 * D + (((int64_t)ct * 4 + I) * 64 + l) * 4);
             }
+            // HP: Q+ and A_qk in fragment order (each fragment a contiguous 1 KiB);
+            // DPLR: row-major, split order
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
-                for (int s = 0; s < NS; ++s) qa[I][s] = P::load(qp + ((16 * I + n) * NS + s) * 32 + g * 8);
+                for (int s = 0; s < NS; ++s)
+                    qa[I][s] = P::load(qp + (PL::HP ? ((I * NS + s) * 64 + l) * 8 : ((16 * I + n) * NS + s) * 32 + g * 8));
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     if (16 * I + 15 >= 32 * s) {
-                        aa[I][s] = P::load(ap + ((16 * I + n) * 2 + s) * 32 + g * 8);
-                        if constexpr (PL::HP) al[I][s] = P::load(ap + 64 * 64 + ((16 * I + n) * 2 + s) * 32 + g * 8);
+                        const int at = PL::HP ? ((I * 2 + s) * 64 + l) * 8 : ((16 * I + n) * 2 + s) * 32 + g * 8;
+                        aa[I][s] = P::load(ap + at);
+                        if constexpr (PL::HP) al[I][s] = P::load(ap + 64 * 64 + at);
                     }
         };
-        // only a sequence's last chunk can be partial; every other chunk stores
-        // all 64 rows without a per-row branch
-        auto consume = [&](int c, auto masked) {
+        // chunk c's output tiles from the exchange buffer and the operands in registers
+        auto compute = [&](int c, f32x4_t (&acc)[4]) {
             const E* hb = reinterpret_cast<const E*>(hvbase + (c & 1) * PL::HVS);
             const E* vb = hb + D * 16;
-            f32x4_t acc[4];
             if constexpr (DPLR) {
                 // keep the conversion below the barrier that precedes this call:
                 // hoisted above it, it would make the wave wait there for every
@@ -370,6 +372,10 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
                         if (16 * I + 15 >= 32 * s) P::mma(acc[I], aa[I][s], bv);
                 }
             }
+        };
+        // only a sequence's last chunk can be partial; every other chunk stores
+        // all 64 rows without a per-row branch
+        auto store = [&](int c, auto masked, const f32x4_t (&acc)[4]) {
             const int t0 = tstart + 64 * c;
             const int L = min(64, len - 64 * c);
 #pragma unroll
@@ -387,18 +393,23 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
                 }
         };
         // chunk j's operands are fetched right after chunk j - 2's output is
-        // computed (in iteration j - 1), two chain steps before they are used
+        // computed (in iteration j - 1), two chain steps before they are used.
+        // The loads are issued before chunk j - 2's stores: loads and stores
+        // share the in-order vector-memory counter, so waiting for the loads
+        // does not wait for those stores to complete.
         if (p < nch) issue(p);
         __builtin_amdgcn_s_barrier();
         if (p == 1 && nch > 0) __builtin_amdgcn_s_barrier();  // iteration 0 (chunk 0 is wave 1's)
         for (int j = p; j < nch; j += 2) {
             __builtin_amdgcn_s_barrier();  // end of iteration j: h_j, V_j are in the buffer
+            f32x4_t acc[4];
+            compute(j, acc);
             if (j + 1 < nch) {
-                consume(j, std::false_type{});
                 if (j + 2 < nch) issue(j + 2);
+                store(j, std::false_type{}, acc);
                 __builtin_amdgcn_s_barrier();  // end of iteration j + 1
             } else {
-                consume(j, std::true_type{});
+                store(j, std::true_type{}, acc);
             }
         }
         return;

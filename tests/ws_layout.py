@@ -46,6 +46,13 @@ def seq_table(ws: torch.Tensor, N, T, H, D, f32, have_cu=True) -> np.ndarray:
     return raw.view(np.int32).reshape(N + 1, 4).copy()
 
 
+def frag_rows(x: np.ndarray, nsl: int) -> np.ndarray:
+    """Fragment order [4 row blocks][nsl slices][64 lanes][8] (lane n + 16 g: row
+    16 I + n, slots of group g) -> row-major [64][nsl][32] in the split order."""
+    t = x.reshape(4, nsl, 4, 16, 8)  # I, s, g, n, j
+    return t.transpose(0, 3, 1, 2, 4).reshape(CH, nsl, 32)
+
+
 def _as_f(raw: np.ndarray, f32: bool) -> np.ndarray:
     """fp32 factors with fp32 inputs; fp16 factors with bf16 inputs."""
     if f32:
@@ -67,7 +74,10 @@ def decode(ws: torch.Tensor, N, T, H, D, f32, have_cu, gc, h):
         return _as_f(raw[b:b + n_el * es_].copy(), f)
 
     out = {}
-    qp = arr(0, CH * D).reshape(CH, NS, 32)
+    if f32:
+        qp = arr(0, CH * D).reshape(CH, NS, 32)
+    else:
+        qp = frag_rows(arr(0, CH * D), NS)
     out["Qp"] = np.zeros((CH, D))
     out["Qp"][:, (np.arange(NS)[:, None] * 32 + SPLIT[None, :]).ravel()] = qp.reshape(CH, -1)
     km = arr(1, D * CH).reshape(D, 2, 32)
@@ -89,9 +99,9 @@ def decode(ws: torch.Tensor, N, T, H, D, f32, have_cu, gc, h):
     out["U"] = U
     if f32:
         aq = arr(4, CH * CH).reshape(CH, 2, 32)
-    else:  # hi plane + lo plane
-        planes = arr(4, 2 * CH * CH).reshape(2, CH, 2, 32)
-        aq = planes[0] + planes[1]
+    else:  # hi plane + lo plane, each in fragment order
+        planes = arr(4, 2 * CH * CH).reshape(2, CH * CH)
+        aq = frag_rows(planes[0], 2) + frag_rows(planes[1], 2)
     A = np.zeros((CH, CH))
     A[:, (np.arange(2)[:, None] * 32 + SPLIT[None, :]).ravel()] = aq.reshape(CH, -1)
     out["Aqk"] = A
