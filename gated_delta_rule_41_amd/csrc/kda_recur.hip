@@ -347,11 +347,19 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
                 else
                     acc[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
+            // HP: the output is formed transposed (each product's operands
+            // swapped), so lane n + 16 g holds row 16 I + n at columns 4 g .. 4 g + 3
+            // of the slab and stores them as one vector
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const Frag bh = P::load(hb + (s * 64 + l) * 8);
 #pragma unroll
-                for (int I = 0; I < 4; ++I) P::mma(acc[I], qa[I][s], bh);
+                for (int I = 0; I < 4; ++I) {
+                    if constexpr (PL::HP)
+                        P::mma(acc[I], bh, qa[I][s]);
+                    else
+                        P::mma(acc[I], qa[I][s], bh);
+                }
             }
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -362,9 +370,9 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
 #pragma unroll
                     for (int I = 0; I < 4; ++I)
                         if (16 * I + 15 >= 32 * s) {
-                            P::mma(acc[I], al[I][s], bv);
-                            P::mma(acc[I], aa[I][s], bvl);
-                            P::mma(acc[I], aa[I][s], bv);
+                            P::mma(acc[I], bv, al[I][s]);
+                            P::mma(acc[I], bvl, aa[I][s]);
+                            P::mma(acc[I], bv, aa[I][s]);
                         }
                 } else {
 #pragma unroll
@@ -378,6 +386,24 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
         auto store = [&](int c, auto masked, const f32x4_t (&acc)[4]) {
             const int t0 = tstart + 64 * c;
             const int L = min(64, len - 64 * c);
+            if constexpr (PL::HP) {
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const int rr = 16 * I + n;
+                    if (!decltype(masked)::value || rr < L) {
+                        const int64_t oi = ((int64_t)(t0 + rr) * H + h) * D + 16 * ct + 4 * g;
+                        if constexpr (OUT_F32) {
+                            *reinterpret_cast<f32x4_t*>(static_cast<float*>(o) + oi) = acc[I];
+                        } else {
+                            u32x2_t pk;
+                            pk[0] = pack2bf(acc[I][0], acc[I][1]);
+                            pk[1] = pack2bf(acc[I][2], acc[I][3]);
+                            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(o) + oi) = pk;
+                        }
+                    }
+                }
+                return;
+            }
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
@@ -393,10 +419,8 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
                 }
         };
         // chunk j's operands are fetched right after chunk j - 2's output is
-        // computed (in iteration j - 1), two chain steps before they are used.
-        // The loads are issued before chunk j - 2's stores: loads and stores
-        // share the in-order vector-memory counter, so waiting for the loads
-        // does not wait for those stores to complete.
+        // computed and stored (in iteration j - 1), two chain steps before they
+        // are used (issuing them before the stores measured slower).
         if (p < nch) issue(p);
         __builtin_amdgcn_s_barrier();
         if (p == 1 && nch > 0) __builtin_amdgcn_s_barrier();  // iteration 0 (chunk 0 is wave 1's)
@@ -405,8 +429,8 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
             f32x4_t acc[4];
             compute(j, acc);
             if (j + 1 < nch) {
-                if (j + 2 < nch) issue(j + 2);
                 store(j, std::false_type{}, acc);
+                if (j + 2 < nch) issue(j + 2);
                 __builtin_amdgcn_s_barrier();  // end of iteration j + 1
             } else {
                 store(j, std::true_type{}, acc);
