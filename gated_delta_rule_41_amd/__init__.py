@@ -24,7 +24,9 @@ __all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "decode_step", "worksp
            "dplr_workspace_size", "abi_version", "status_str", "library_path", "KDAError", "CHUNK"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkda.so")
+# the in-tree build; KDA_LIBRARY may name another build of the same sources
+# (e.g. one with host-side sanitizers)
+LIB_PATH = os.environ.get("KDA_LIBRARY") or os.path.join(_PKG, "libkda.so")
 CHUNK = 64
 
 KDA_F32, KDA_BF16 = 0, 1
@@ -549,11 +551,13 @@ def bwd_workspace_size(N: int, T_total: int, H: int, dk: int, dv: int) -> int:
 def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor, beta: torch.Tensor,
               d_o: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, d_final_state: Optional[torch.Tensor] = None, *,
-              want_initial_grad: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
+              want_initial_grad: bool = True, workspace: Optional[torch.Tensor] = None,
+              out: Optional[dict] = None) -> dict:
     """Backward of ``chunk_fwd`` (see ``kda_chunk_bwd`` in include/kda.h): the
     same inputs, d_o [T, H, dv] fp32 and optionally d_final_state [N, H, dk, dv]
     fp32. Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha, dbeta and
-    dinitial_state (None unless want_initial_grad)."""
+    dinitial_state (None unless want_initial_grad). ``out`` may supply any of
+    these tensors (fp32, contiguous, on q's device), which are then written."""
     lib = _load()
     dev = q.device
     if q.dim() != 3 or v.dim() != 3:
@@ -584,10 +588,18 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != log_alpha.dtype:
         raise TypeError("q, k, v must share a dtype; log_alpha and beta must share a dtype")
     f32 = dict(dtype=torch.float32, device=dev)
-    g = {"dq": torch.empty(T, H, dk, **f32), "dk": torch.empty(T, H, dk, **f32),
-         "dv": torch.empty(T, H, dv, **f32), "dlog_alpha": torch.empty(T, H, dk, **f32),
-         "dbeta": torch.empty(T, H, **f32),
-         "dinitial_state": torch.empty(N, H, dk, dv, **f32) if want_initial_grad else None}
+    shapes = {"dq": (T, H, dk), "dk": (T, H, dk), "dv": (T, H, dv), "dlog_alpha": (T, H, dk), "dbeta": (T, H),
+              "dinitial_state": (N, H, dk, dv)}
+    out = dict(out or {})
+    if set(out) - set(shapes):
+        raise ValueError(f"unknown gradient names {sorted(set(out) - set(shapes))}")
+    _check([(nm, t, shapes[nm]) for nm, t in out.items()], dev)
+    for nm, t in out.items():
+        if t.dtype != torch.float32:
+            raise TypeError(f"{nm} must be float32")
+    g = {nm: out[nm] if nm in out else torch.empty(*shp, **f32) for nm, shp in shapes.items()}
+    if not want_initial_grad and "dinitial_state" not in out:
+        g["dinitial_state"] = None
     sz = ctypes.c_size_t(0)
     lib.kda_chunk_bwd_workspace_size(max(N, 1), T, H, dk, dv, ctypes.byref(sz))
     if workspace is None:

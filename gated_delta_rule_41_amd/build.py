@@ -44,8 +44,8 @@ FILE_FLAGS = {
 }
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, extra, build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = [hipcc()] + HIPCC_FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + list(extra) + ["-c", src, "-o", obj]
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(line for line in res.stdout.splitlines() if "packed-fp32-ops" not in line)
@@ -56,21 +56,24 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra=(), jobs: int = 8, verbose: bool = False) -> str:
-    """Compile every csrc/*.hip and link libkda.so. Always recompiles."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(extra=(), jobs: int = 8, verbose: bool = False, out: str = LIB, build_dir: str = BUILD,
+          link_extra=()) -> str:
+    """Compile every csrc/*.hip and link libkda.so (or ``out``). Always
+    recompiles. ``extra`` / ``link_extra`` add compiler / linker options (the
+    host-sanitizer build of the tests uses them, with its own out and build_dir)."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), srcs))
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + list(link_extra) + ["-o", tmp] + objs
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -167,7 +167,7 @@ const char* kda_status_str(int s) {
 }
 
 kda_status kda_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
-                                        kda_dtype in_dtype, size_t* bytes) {
+                                        int32_t in_dtype, size_t* bytes) {
     if (!bytes) return KDA_ERR_NULL;
     if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
     if (!head_ok(dk, dv) || !dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
@@ -179,8 +179,8 @@ kda_status kda_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
 
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
                          const float* initial_state, const int32_t* cu_seqlens, int32_t N, int64_t T_total,
-                         int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype gate_dtype,
-                         kda_dtype out_dtype, void* o, float* final_state, void* workspace,
+                         int32_t H, int32_t dk, int32_t dv, int32_t in_dtype, int32_t gate_dtype,
+                         int32_t out_dtype, void* o, float* final_state, void* workspace,
                          size_t workspace_bytes, void* stream) {
     return kda_chunk_fwd_timed(q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, T_total, H, dk, dv,
                                in_dtype, gate_dtype, out_dtype, o, final_state, workspace, workspace_bytes,
@@ -190,7 +190,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
 kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* log_alpha,
                                const void* beta, const float* initial_state, const int32_t* cu_seqlens,
                                int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
-                               kda_dtype in_dtype, kda_dtype gate_dtype, kda_dtype out_dtype, void* o,
+                               int32_t in_dtype, int32_t gate_dtype, int32_t out_dtype, void* o,
                                float* final_state, void* workspace, size_t workspace_bytes, void* stream,
                                void* const* events) {
     if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
@@ -274,7 +274,7 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
 }
 
 kda_status kda_dplr_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
-                                             kda_dtype in_dtype, size_t* bytes) {
+                                             int32_t in_dtype, size_t* bytes) {
     if (!bytes) return KDA_ERR_NULL;
     if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
     if (!head_ok(dk, dv) || in_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -284,8 +284,8 @@ kda_status kda_dplr_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t
 
 kda_status kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const void* b,
                               const void* log_alpha, const float* initial_state, const int32_t* cu_seqlens,
-                              int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype,
-                              kda_dtype gate_dtype, kda_dtype out_dtype, void* o, float* final_state,
+                              int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv, int32_t in_dtype,
+                              int32_t gate_dtype, int32_t out_dtype, void* o, float* final_state,
                               void* workspace, size_t workspace_bytes, void* stream) {
     if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
     if (T_total > 0 && (!q || !k || !v || !a || !b || !log_alpha || !o)) return KDA_ERR_NULL;
@@ -401,7 +401,7 @@ kda_status kda_chunk_bwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
 
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
                          const float* initial_state, const int32_t* cu_seqlens, int32_t N, int64_t T_total,
-                         int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype gate_dtype,
+                         int32_t H, int32_t dk, int32_t dv, int32_t in_dtype, int32_t gate_dtype,
                          const float* d_o, const float* d_final_state, float* dq, float* dk_out, float* dv_out,
                          float* dlog_alpha, float* dbeta, float* d_initial_state, void* workspace,
                          size_t workspace_bytes, void* stream) {
@@ -503,7 +503,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
 kda_status kda_layer_prologue(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
                               const float* wq, const float* wk, const float* wv, const float* A_log,
                               const float* dt_bias, const int32_t* cu_seqlens, int32_t N, int64_t T_total,
-                              int32_t H, int32_t d, kda_dtype dtype, void* q, void* k, void* v, void* log_alpha,
+                              int32_t H, int32_t d, int32_t dtype, void* q, void* k, void* v, void* log_alpha,
                               void* beta, void* stream) {
     if (!chunk_sizes_ok(N, T_total, H) || T_total * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     if (!cu_seqlens && N != 1) return KDA_ERR_SHAPE;
@@ -630,7 +630,7 @@ kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, c
 }
 
 kda_status kda_layer_conv_state(const void* xq, const void* xk, const void* xv, const int32_t* cu_seqlens,
-                                int32_t N, int64_t T_total, int32_t H, int32_t d, kda_dtype dtype, void* conv_state,
+                                int32_t N, int64_t T_total, int32_t H, int32_t d, int32_t dtype, void* conv_state,
                                 void* stream) {
     if (!chunk_sizes_ok(N, T_total, H) || T_total * H >= (int64_t(1) << 31) || (int64_t)N * H >= (int64_t(1) << 31))
         return KDA_ERR_SHAPE;
@@ -660,7 +660,7 @@ kda_status kda_layer_conv_state(const void* xq, const void* xk, const void* xv, 
 kda_status kda_layer_decode_prologue(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
                                      void* conv_state, const float* wq, const float* wk, const float* wv,
                                      const float* A_log, const float* dt_bias, int32_t N, int32_t H, int32_t d,
-                                     kda_dtype dtype, void* q, void* k, void* v, void* log_alpha, void* beta,
+                                     int32_t dtype, void* q, void* k, void* v, void* log_alpha, void* beta,
                                      void* stream) {
     if (N <= 0 || H <= 0 || H > 65536 || (int64_t)N * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     if (!head_ok(d, d) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
@@ -698,7 +698,7 @@ kda_status kda_layer_decode_prologue(const void* xq, const void* xk, const void*
 }
 
 kda_status kda_layer_epilogue(const float* o, const void* g, const float* rms_w, int64_t T_total, int32_t H,
-                              int32_t dv, kda_dtype dtype, void* y, void* stream) {
+                              int32_t dv, int32_t dtype, void* y, void* stream) {
     if (T_total < 0 || T_total >= (int64_t(1) << 31) || H <= 0 || H > 65536 || T_total * H >= (int64_t(1) << 31))
         return KDA_ERR_SHAPE;
     if (!(dv == 64 || dv == 128) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
@@ -720,8 +720,8 @@ kda_status kda_layer_epilogue(const float* o, const void* g, const float* rms_w,
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
-                           float* state, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype,
-                           kda_dtype gate_dtype, kda_dtype out_dtype, void* o, void* stream) {
+                           float* state, int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t in_dtype,
+                           int32_t gate_dtype, int32_t out_dtype, void* o, void* stream) {
     if (!q || !k || !v || !log_alpha || !beta || !state || !o) return KDA_ERR_NULL;
     if (N <= 0 || H <= 0 || (int64_t)N * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     if (!head_ok(dk, dv) || !dtype_ok(in_dtype) || !dtype_ok(gate_dtype) || !dtype_ok(out_dtype))
@@ -758,7 +758,7 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
 kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* log_alpha,
                                  const void* beta, const float* initial_state, const int32_t* cu_seqlens,
                                  int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
-                                 kda_dtype in_dtype, kda_dtype gate_dtype, kda_dtype out_dtype, void* o,
+                                 int32_t in_dtype, int32_t gate_dtype, int32_t out_dtype, void* o,
                                  float* final_state, void* stream) {
     // A call whose workspace would not fit the scratch is refused before any
     // device call. Sizes the workspace query rejects go to kda_chunk_fwd's own

@@ -94,6 +94,8 @@ extern "C" {
 #define KDA_ABI_VERSION 1
 #define KDA_CHUNK 64 /* fixed chunk length of the prefill algorithm */
 
+/* Element type codes. The entry points take them as int32_t, so any value may
+ * be passed; values other than these return KDA_ERR_UNSUPPORTED. */
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
 typedef enum {
@@ -123,7 +125,7 @@ const char* kda_status_str(int status);
  *   bytes: host out-pointer, written on KDA_OK.
  */
 kda_status kda_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk,
-                                        int32_t dv, kda_dtype in_dtype, size_t* bytes);
+                                        int32_t dv, int32_t in_dtype, size_t* bytes);
 
 /*
  * Chunkwise prefill of a packed batch: kda_chunk_fwd(q, k, v, log_alpha, beta,
@@ -154,7 +156,7 @@ kda_status kda_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* beta, const float* initial_state, const int32_t* cu_seqlens,
                          int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
-                         kda_dtype in_dtype, kda_dtype gate_dtype, kda_dtype out_dtype, void* o,
+                         int32_t in_dtype, int32_t gate_dtype, int32_t out_dtype, void* o,
                          float* final_state, void* workspace, size_t workspace_bytes,
                          void* stream);
 
@@ -172,8 +174,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
 kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* log_alpha,
                                const void* beta, const float* initial_state,
                                const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
-                               int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype gate_dtype,
-                               kda_dtype out_dtype, void* o, float* final_state, void* workspace,
+                               int32_t dk, int32_t dv, int32_t in_dtype, int32_t gate_dtype,
+                               int32_t out_dtype, void* o, float* final_state, void* workspace,
                                size_t workspace_bytes, void* stream, void* const* events);
 
 /* Largest workspace kda_chunk_fwd_noalloc serves from its static scratch: 64 MiB. */
@@ -206,7 +208,7 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
 kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* log_alpha,
                                  const void* beta, const float* initial_state, const int32_t* cu_seqlens,
                                  int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
-                                 kda_dtype in_dtype, kda_dtype gate_dtype, kda_dtype out_dtype, void* o,
+                                 int32_t in_dtype, int32_t gate_dtype, int32_t out_dtype, void* o,
                                  float* final_state, void* stream);
 
 /*
@@ -247,7 +249,7 @@ kda_status kda_chunk_bwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* beta, const float* initial_state, const int32_t* cu_seqlens,
                          int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
-                         kda_dtype in_dtype, kda_dtype gate_dtype, const float* d_o,
+                         int32_t in_dtype, int32_t gate_dtype, const float* d_o,
                          const float* d_final_state, float* dq, float* dk_out, float* dv_out,
                          float* dlog_alpha, float* dbeta, float* d_initial_state, void* workspace,
                          size_t workspace_bytes, void* stream);
@@ -280,7 +282,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
 kda_status kda_layer_prologue(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
                               const float* wq, const float* wk, const float* wv, const float* A_log,
                               const float* dt_bias, const int32_t* cu_seqlens, int32_t N, int64_t T_total,
-                              int32_t H, int32_t d, kda_dtype dtype, void* q, void* k, void* v,
+                              int32_t H, int32_t d, int32_t dtype, void* q, void* k, void* v,
                               void* log_alpha, void* beta, void* stream);
 
 /*
@@ -297,7 +299,7 @@ kda_status kda_layer_prologue(const void* xq, const void* xk, const void* xv, co
  * output may not overlap an input (KDA_ERR_ALIAS). One kernel is enqueued.
  */
 kda_status kda_layer_conv_state(const void* xq, const void* xk, const void* xv, const int32_t* cu_seqlens,
-                                int32_t N, int64_t T_total, int32_t H, int32_t d, kda_dtype dtype, void* conv_state,
+                                int32_t N, int64_t T_total, int32_t H, int32_t d, int32_t dtype, void* conv_state,
                                 void* stream);
 
 /*
@@ -320,7 +322,7 @@ kda_status kda_layer_conv_state(const void* xq, const void* xk, const void* xv, 
 kda_status kda_layer_decode_prologue(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
                                      void* conv_state, const float* wq, const float* wk, const float* wv,
                                      const float* A_log, const float* dt_bias, int32_t N, int32_t H, int32_t d,
-                                     kda_dtype dtype, void* q, void* k, void* v, void* log_alpha, void* beta,
+                                     int32_t dtype, void* q, void* k, void* v, void* log_alpha, void* beta,
                                      void* stream);
 
 /*
@@ -361,7 +363,7 @@ kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, c
  * one (KDA_ERR_ALIGN). One kernel is enqueued: one wave per four rows.
  */
 kda_status kda_layer_epilogue(const float* o, const void* xg, const float* rms_w, int64_t T_total, int32_t H,
-                              int32_t dv, kda_dtype dtype, void* y, void* stream);
+                              int32_t dv, int32_t dtype, void* y, void* stream);
 
 /*
  * Bytes of device workspace kda_dplr_chunk_fwd needs (host call, no device
@@ -370,7 +372,7 @@ kda_status kda_layer_epilogue(const float* o, const void* xg, const float* rms_w
  *   bytes: host out-pointer, written on KDA_OK.
  */
 kda_status kda_dplr_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk,
-                                             int32_t dv, kda_dtype in_dtype, size_t* bytes);
+                                             int32_t dv, int32_t in_dtype, size_t* bytes);
 
 /*
  * Chunkwise prefill of the general diagonal-plus-low-rank (DPLR) transition,
@@ -396,8 +398,8 @@ kda_status kda_dplr_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t
 kda_status kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const void* b,
                               const void* log_alpha, const float* initial_state,
                               const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
-                              int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype gate_dtype,
-                              kda_dtype out_dtype, void* o, float* final_state, void* workspace,
+                              int32_t dk, int32_t dv, int32_t in_dtype, int32_t gate_dtype,
+                              int32_t out_dtype, void* o, float* final_state, void* workspace,
                               size_t workspace_bytes, void* stream);
 
 /*
@@ -412,8 +414,8 @@ kda_status kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const
  */
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
                            const void* beta, float* state, int32_t N, int32_t H, int32_t dk,
-                           int32_t dv, kda_dtype in_dtype, kda_dtype gate_dtype,
-                           kda_dtype out_dtype, void* o, void* stream);
+                           int32_t dv, int32_t in_dtype, int32_t gate_dtype,
+                           int32_t out_dtype, void* o, void* stream);
 
 #ifdef __cplusplus
 }

@@ -43,7 +43,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+# the in-tree build; KDA_ORACLE_LIBRARY may name another build of kda_oracle.c
+# (e.g. one with sanitizers)
+_LIB_PATH = os.environ.get("KDA_ORACLE_LIBRARY") or os.path.join(_HERE, "libkda_oracle.so")
 _lib = None
 
 ORC_F32, ORC_BF16, ORC_F64 = 0, 1, 2
