@@ -293,11 +293,21 @@ def time_dplr(kda, case, steps, warmup):
     return e0.elapsed_time(e1) / steps, o, fs
 
 
+def bwd_pieces(case):
+    """Pieces the backward runs in with the default workspace: one while the
+    chunk slots x heads fit 65536, else slots of floor(65536 / H) each."""
+    nc = (case.T_total + 63 * case.N) // 64 if case.cu_seqlens is not None else (case.T_total + 63) // 64
+    if nc * case.H <= 65536:
+        return 1
+    per = max(65536 // case.H, 1)
+    return -(-nc // per)
+
+
 def time_bwd(kda, case, steps, warmup):
-    """Whole-call time of the chunkwise backward (its five kernels: the fp32
-    forward recompute, the operand preparation, the reverse state-gradient
-    recursion and the local adjoints), torch events on torch's current stream,
-    which the binding launches on."""
+    """Whole-call time of the chunkwise backward (the fp32 forward recompute,
+    the operand preparation, the reverse state-gradient recursion and the local
+    adjoints; in pieces, the checkpoint forward first), torch events on torch's
+    current stream, which the binding launches on."""
     import torch
     dev = case.q.device
     g = torch.Generator(device=dev)
@@ -306,10 +316,14 @@ def time_bwd(kda, case, steps, warmup):
     d_fin = torch.randn(case.N, case.H, case.dk, case.dv, generator=g, device=dev) * 0.1
     ws = torch.empty(kda.bwd_workspace_size(case.N, case.T_total, case.H, case.dk, case.dv),
                      dtype=torch.uint8, device=dev)
+    shapes = {"dq": (case.T_total, case.H, case.dk), "dk": (case.T_total, case.H, case.dk),
+              "dv": (case.T_total, case.H, case.dv), "dlog_alpha": (case.T_total, case.H, case.dk),
+              "dbeta": (case.T_total, case.H), "dinitial_state": (case.N, case.H, case.dk, case.dv)}
+    outs = {k_: torch.empty(*s_, dtype=torch.float32, device=dev) for k_, s_ in shapes.items()}
 
     def call():
         return kda.chunk_bwd(case.q, case.k, case.v, case.log_alpha, case.beta, d_o, case.initial_state,
-                             case.cu_seqlens, d_fin, workspace=ws)
+                             case.cu_seqlens, d_fin, workspace=ws, out=outs)
 
     for _ in range(warmup):
         call()
@@ -317,10 +331,10 @@ def time_bwd(kda, case, steps, warmup):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        g_ = call()
+        call()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, g_, ws.numel()
+    return e0.elapsed_time(e1) / steps, ws.numel()
 
 
 def time_layer(kda, lc, steps, warmup, hip, stream):
@@ -861,13 +875,31 @@ def side_legs(args, kda, ki, hip, stream, flush, dev, out, t_start, headline_hos
         del dcase
 
     if not args.no_bwd:
-        bwd_ms, _, ws_bytes = time_bwd(kda, case, 5, 3)
-        out["backward"] = {
-            "workload": "prefill-4k, d_o ~ N(0,1), d_final_state ~ N(0, 0.01)",
-            "ms_per_step": round(bwd_ms, 5), "tokens_per_s": round(case.T_total / (bwd_ms * 1e-3), 1),
-            "time_ratio_bwd_over_fwd": round(bwd_ms / wall_ms, 3), "workspace_bytes": ws_bytes,
-            "hbm_bytes_per_launch": {k_: traffic_from_profiles(k_) for k_ in
-                                     ("bwd_fwd_prep", "bwd_fwd_recur", "bwd_prep", "bwd_recur", "bwd_local")}}
+        # the backward on prefill-4k (with the per-kernel traffic), varlen-16 and
+        # the 1M-token sequence (in pieces); each against its forward's time
+        out["backward"] = {}
+        legs = [("prefill-4k", case, 5, 3, wall_ms, "warm median")]
+        if args.profile_set is None:
+            wv = out.get("workloads", {}).get("varlen-16")
+            legs.append(("varlen-16", None, 5, 2, wv["warm_ms_median"] if wv else None, "warm median"))
+            legs.append(("long-1m", None, 2, 1, out.get("prefill", {}).get("cold_ms_median"), "cold median"))
+        for wl, c, steps, warm, fwd_ms, fwd_kind in legs:
+            c = c if c is not None else ki.make_prefill(wl, dev)
+            bwd_ms, ws_bytes = time_bwd(kda, c, steps, warm)
+            leg = {"workload": f"{wl}, d_o ~ N(0,1), d_final_state ~ N(0, 0.01)", "steps": steps,
+                   "warmup": warm, "ms_per_step": round(bwd_ms, 5),
+                   "tokens_per_s": round(c.T_total / (bwd_ms * 1e-3), 1),
+                   "workspace_bytes": ws_bytes, "pieces": bwd_pieces(c),
+                   "time_ratio_bwd_over_fwd": round(bwd_ms / fwd_ms, 3) if fwd_ms else None,
+                   "fwd_time": fwd_kind}
+            if wl == "prefill-4k":
+                leg["hbm_bytes_per_launch"] = {k_: traffic_from_profiles(k_) for k_ in
+                                               ("bwd_fwd_prep", "bwd_fwd_recur", "bwd_prep", "bwd_recur",
+                                                "bwd_local")}
+            out["backward"][wl] = leg
+            if c is not case:
+                del c
+            torch.cuda.empty_cache()
 
     if not args.no_layer:
         lc = ki.make_layer("prefill-4k", dev)

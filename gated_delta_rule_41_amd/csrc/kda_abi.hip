@@ -361,20 +361,67 @@ kda_status kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const
     return KDA_OK;
 }
 
-// backward workspace: forward recompute (fp32 factors, h_n, V_new), the state-gradient
-// recursion's operands and outputs, its added term, the gated key products and the
-// local kernel's scratch
-static size_t bwd_workspace(int64_t NC, int H, int D, size_t off[5]) {
-    const size_t f = plan_workspace(NC, H, D, true).total;
-    const size_t pb = align_up((size_t)NC * H * D * D * 4, 256);
-    const size_t pk = align_up((size_t)NC * H * 64 * 64 * 4, 256);
-    const size_t sc = align_up((size_t)NC * H * (size_t)bwd_scr_floats(D) * 4, 256);
-    off[0] = 0;
-    off[1] = f;
-    off[2] = 2 * f;
-    off[3] = 2 * f + pb;
-    off[4] = 2 * f + pb + pk;
-    return 2 * f + pb + pk + sc;
+// Backward workspace. Per chunk-head of a piece: the forward recomputed with
+// fp32 factors (with h_n and V_new), the state-gradient chain's operand U
+// (A_qk^T dO) and outputs (its states dh' and dV), the chain's added term
+// Q+^T dO (whose room the local kernel's scratch takes over once the chain has
+// read it) and the gated key products. With more than one piece, one [H][D][D]
+// fp32 state per piece: the forward state at the piece's first slot, later the
+// state gradient there. The sequence table last.
+struct BwdPlan {
+    int64_t pc = 0;  // chunk slots per piece
+    int64_t np = 1;  // pieces
+    size_t f = 0, ru = 0, rh = 0, rv = 0, pb = 0, pk = 0, ck = 0, tab = 0, total = 0;
+};
+
+static BwdPlan plan_bwd(int64_t NC, int H, int D, int N, int64_t pc) {
+    BwdPlan p;
+    p.pc = pc;
+    p.np = NC > 0 ? (NC + pc - 1) / pc : 1;
+    const size_t ch = (size_t)pc * H;
+    const size_t scr = (size_t)bwd_scr_floats(D) > (size_t)D * D ? (size_t)bwd_scr_floats(D) : (size_t)D * D;
+    size_t o = plan_workspace(pc, H, D, true).total;
+    p.ru = o;
+    o = align_up(o + ch * KDA_CHUNK * D * 4, 256);
+    p.rh = o;
+    o = align_up(o + ch * D * D * 4, 256);
+    p.rv = o;
+    o = align_up(o + ch * KDA_CHUNK * D * 4, 256);
+    p.pb = o;
+    o = align_up(o + ch * scr * 4, 256);
+    p.pk = o;
+    o = align_up(o + ch * KDA_CHUNK * KDA_CHUNK * 4, 256);
+    p.ck = o;
+    o = align_up(o + (p.np > 1 ? (size_t)p.np * H * D * D * 4 : 0), 256);
+    p.tab = o;
+    p.total = o + seq_table_bytes(N);
+    return p;
+}
+
+// the size query's piece: every slot when the chunk-heads fit the default
+// bound, else as many slots as fit it
+static int64_t bwd_default_piece(int64_t NC, int H) {
+    if (NC * H <= KDA_BWD_PIECE_CHUNK_HEADS) return NC;
+    const int64_t pc = KDA_BWD_PIECE_CHUNK_HEADS / H;
+    return pc > 0 ? pc : 1;
+}
+
+// the largest piece whose plan fits `bytes`; -1 when none does (0 when there
+// are no chunk slots)
+static int64_t bwd_fit_piece(int64_t NC, int H, int D, int N, size_t bytes) {
+    if (NC == 0) return plan_bwd(0, H, D, N, 0).total <= bytes ? 0 : -1;
+    const size_t per = plan_bwd(1, H, D, 0, 1).ck;  // bytes per chunk slot (every head)
+    int64_t pc = NC;
+    while (pc > 0) {
+        const BwdPlan p = plan_bwd(NC, H, D, N, pc);
+        if (p.total <= bytes) return pc;
+        // the bytes that do not scale with the piece at this piece count (a
+        // smaller piece only adds boundary states, so the guess never overshoots)
+        const size_t fixed = p.total - (size_t)pc * per;
+        const int64_t next = fixed < bytes ? (int64_t)((bytes - fixed) / per) : 0;
+        pc = next < pc ? next : pc - 1;
+    }
+    return -1;
 }
 
 static void carve(ChunkArgs& a, char* base, int64_t NC, int H, int D) {
@@ -394,8 +441,8 @@ kda_status kda_chunk_bwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
     if (!bytes) return KDA_ERR_NULL;
     if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
     if (!head_ok(dk, dv)) return KDA_ERR_UNSUPPORTED;
-    size_t off[5];
-    *bytes = bwd_workspace(chunk_capacity(N, T_total, true), H, dk, off) + seq_table_bytes(N);
+    const int64_t NC = chunk_capacity(N, T_total, true);
+    *bytes = plan_bwd(NC, H, dk, N, bwd_default_piece(NC, H)).total;
     return KDA_OK;
 }
 
@@ -436,16 +483,17 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
         if (!(i == 5 && outs[i] == dfin) && overlaps(outs[i], nout[i], dfin, ns)) return KDA_ERR_ALIAS;
     }
     const int64_t NC = chunk_capacity(N, T_total, cu_seqlens != nullptr);
-    size_t off[5];
-    const size_t bwd_base = bwd_workspace(NC, H, dk, off);
-    const size_t need = bwd_base + seq_table_bytes(N);  // the sequence table at the end
-    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    if (NC >= (int64_t(1) << 31) / H) return KDA_ERR_SHAPE;
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0) return KDA_ERR_WORKSPACE;
+    const int64_t pc = bwd_fit_piece(NC, H, dk, N, workspace_bytes);
+    if (pc < 0) return KDA_ERR_WORKSPACE;
+    const BwdPlan pl = plan_bwd(NC, H, dk, N, pc);
+    const size_t need = pl.total;
     for (int j = 0; j < 8; ++j)
         if (overlaps(workspace, need, ins[j], nin[j])) return KDA_ERR_ALIAS;
     for (int i = 0; i < 6; ++i)
         if (overlaps(workspace, need, outs[i], nout[i])) return KDA_ERR_ALIAS;
     if (overlaps(workspace, need, dfin, ns)) return KDA_ERR_ALIAS;
-    if (NC >= (int64_t(1) << 31) / H) return KDA_ERR_SHAPE;
 
     char* w = static_cast<char*>(workspace);
     BwdArgs b;
@@ -468,35 +516,69 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     F.gate_f32 = gate_dtype == KDA_F32;
     F.out_f32 = true;
     F.f32_factors = true;
-    carve(F, w + off[0], NC, H, dk);
-    F.am = w + off[3];  // the prep keeps the gated key products there
+    carve(F, w, pc, H, dk);
+    F.am = w + pl.pk;  // the prep keeps the gated key products there
     ChunkArgs& R = b.rec;
     R = F;
     R.am = nullptr;
     R.s0 = d_final_state;
     R.s_final = d_initial_state;
-    carve(R, w + off[1], NC, H, dk);
     // the state-gradient chain reads the forward's factors in swapped roles (K- as
-    // its "-W", (-W)^T as its "K-^T", the same gamma) and walks the chunks in reverse
+    // its "-W", (-W)^T as its "K-^T", the same gamma) and walks the chunks in reverse;
+    // of its own arrays it has U, h and V_new
+    R.qp = R.aqk = nullptr;
+    R.u = w + pl.ru;
+    R.h = w + pl.rh;
+    R.vn = w + pl.rv;
     R.wn = F.km;
     R.km = F.wn;
     R.gam = F.gam;
-    R.pb = reinterpret_cast<const float*>(w + off[2]);
+    R.pb = reinterpret_cast<const float*>(w + pl.pb);
     b.d_o = d_o;
     b.dq = dq;
     b.dk = dk_out;
     b.dv = dv_out;
     b.dla = dlog_alpha;
     b.dbeta = dbeta;
-    b.scr = reinterpret_cast<float*>(w + off[4]);
+    b.scr = reinterpret_cast<float*>(w + pl.pb);  // after the chain has read the added term
     hipStream_t st = static_cast<hipStream_t>(stream);
-    F.tab = R.tab = cu_seqlens ? reinterpret_cast<SeqMeta*>(w + bwd_base) : nullptr;
+    F.tab = R.tab = cu_seqlens ? reinterpret_cast<SeqMeta*>(w + pl.tab) : nullptr;
     if (cu_seqlens && launch_seq_table(cu_seqlens, N, F.T, F.NC, F.tab, st) != hipSuccess) return KDA_ERR_HIP;
-    if (NC > 0 && launch_prep(F, st) != hipSuccess) return KDA_ERR_HIP;
-    if (NC > 0 && launch_recur(F, st) != hipSuccess) return KDA_ERR_HIP;
-    if (NC > 0 && launch_bwd_prep(b, st) != hipSuccess) return KDA_ERR_HIP;
-    if (launch_recur(R, st) != hipSuccess) return KDA_ERR_HIP;
-    if (NC > 0 && launch_bwd_local(b, st) != hipSuccess) return KDA_ERR_HIP;
+    if (pl.np <= 1) {
+        if (NC > 0 && launch_prep(F, st) != hipSuccess) return KDA_ERR_HIP;
+        if (NC > 0 && launch_recur(F, st) != hipSuccess) return KDA_ERR_HIP;
+        if (NC > 0 && launch_bwd_prep(b, st) != hipSuccess) return KDA_ERR_HIP;
+        if (launch_recur(R, st) != hipSuccess) return KDA_ERR_HIP;
+        if (NC > 0 && launch_bwd_local(b, st) != hipSuccess) return KDA_ERR_HIP;
+        return KDA_OK;
+    }
+    // In pieces of pc chunk slots: the forward states at the pieces' first slots
+    // (checkpoint p, written by piece p - 1), then the pieces in reverse, each
+    // recomputing its forward from its checkpoint and handing the state gradient
+    // at its first slot to the piece before it (through the same checkpoint).
+    float* ck = reinterpret_cast<float*>(w + pl.ck);
+    const size_t cks = (size_t)H * dk * dk;
+    auto piece = [&](ChunkArgs& A, int64_t p, const float* cin, float* cout) {
+        A.piece.g0 = (int)(p * pc);
+        A.piece.g1 = (int)((p + 1) * pc < NC ? (p + 1) * pc : NC);
+        A.piece.last = A.piece.g1 == NC;
+        A.piece.cin = cin;
+        A.piece.cout = cout;
+    };
+    for (int64_t p = 0; p + 1 < pl.np; ++p) {
+        piece(F, p, ck + p * cks, ck + (p + 1) * cks);
+        if (launch_prep(F, st) != hipSuccess) return KDA_ERR_HIP;
+        if (launch_recur(F, st) != hipSuccess) return KDA_ERR_HIP;
+    }
+    for (int64_t p = pl.np - 1; p >= 0; --p) {
+        piece(F, p, ck + p * cks, nullptr);
+        piece(R, p, p + 1 < pl.np ? ck + (p + 1) * cks : nullptr, ck + p * cks);
+        if (launch_prep(F, st) != hipSuccess) return KDA_ERR_HIP;
+        if (launch_recur(F, st) != hipSuccess) return KDA_ERR_HIP;
+        if (launch_bwd_prep(b, st) != hipSuccess) return KDA_ERR_HIP;
+        if (launch_recur(R, st) != hipSuccess) return KDA_ERR_HIP;
+        if (launch_bwd_local(b, st) != hipSuccess) return KDA_ERR_HIP;
+    }
     return KDA_OK;
 }
 

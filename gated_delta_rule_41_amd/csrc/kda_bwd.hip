@@ -99,7 +99,7 @@ struct BwdPrepSmem {
 
 template <int D>
 __global__ __launch_bounds__(4 * D) void bwd_prep_kernel(const SeqMeta* __restrict__ tab, int N, int T, int H,
-                                                         Ws<float> f, Ws<float> b,
+                                                         int g0, Ws<float> f, Ws<float> b,
                                                          const float* __restrict__ d_o) {
     constexpr int NT = D / 16, NTH = 4 * D, RS = BwdPrepSmem<D>::RS, SQS = BwdPrepSmem<D>::SQS;
     constexpr int NQ = 64 * D / 4 / NTH;      // float4 per thread of a [64][D] array (= 4)
@@ -108,10 +108,10 @@ __global__ __launch_bounds__(4 * D) void bwd_prep_kernel(const SeqMeta* __restri
     float* dO = sm;                // [64][RS]
     float* Qp = dO + 64 * RS;      // [64][RS], channels in natural order
     float* Aq = Qp + 64 * RS;      // [64][SQS] A_qk
-    const int gc = blockIdx.x / H, h = blockIdx.x - gc * H;
+    const int lc = blockIdx.x / H, h = blockIdx.x - lc * H;  // slot g0 + lc, workspace slot lc
     ChunkLoc loc;
-    if (!locate_chunk(tab, N, T, gc, loc)) return;
-    const int64_t src = (int64_t)gc * H + h;
+    if (!locate_chunk(tab, N, T, g0 + lc, loc)) return;
+    const int64_t src = (int64_t)lc * H + h;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, n = l & 15;
     // every load of the stage first, then the LDS stores
     f32x4_t xo[NQ], xq[NQ], xa[NA];
@@ -192,7 +192,7 @@ struct BwdSmem {
 template <int D, typename TIn, typename TG>
 __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TIn* k, const TIn* v, const TG* la,
                                                           const TG* beta, const SeqMeta* __restrict__ tab, int N,
-                                                          int T, int H, Ws<float> f, Ws<float> b,
+                                                          int T, int H, int g0, Ws<float> f, Ws<float> b,
                                                           const float* __restrict__ d_o, float* __restrict__ scr,
                                                           float* __restrict__ dq, float* __restrict__ dk,
                                                           float* __restrict__ dv, float* __restrict__ dla,
@@ -212,11 +212,11 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
     float* dap = dbp + NW * 64;        // [4][64] dbeta: dA_kk P_kk, per column block
     float* dgp = dap + 4 * 64;         // [2][D] dgamma halves
 
-    const int gc = blockIdx.x / H, h = blockIdx.x - gc * H;
+    const int lc = blockIdx.x / H, h = blockIdx.x - lc * H;  // slot g0 + lc, workspace slot lc
     ChunkLoc loc;
-    if (!locate_chunk(tab, N, T, gc, loc)) return;
+    if (!locate_chunk(tab, N, T, g0 + lc, loc)) return;
     const int t0 = loc.t0, L = loc.L;
-    const int64_t fs = (int64_t)gc * H + h;
+    const int64_t fs = (int64_t)lc * H + h;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, n = l & 15;
     const int c = 16 * w + n;  // own channel
     const float* Pkk = f.am + fs * 64 * 64;     // [64][64] from the forward recompute
@@ -739,7 +739,8 @@ static hipError_t launch_bwd_prep_d(const BwdArgs& a, hipStream_t st) {
                 (float*)F.vn};
     Ws<float> b{(float*)B.qp, (float*)B.km, (float*)B.wn, (float*)B.u, (float*)B.aqk, B.gam, (float*)B.h,
                 (float*)B.vn, nullptr, nullptr, B.pb};
-    hipLaunchKernelGGL(kern, dim3(F.NC * F.H), dim3(4 * D), bytes, st, F.tab, F.N, F.T, F.H, f, b, a.d_o);
+    hipLaunchKernelGGL(kern, dim3(F.slots() * F.H), dim3(4 * D), bytes, st, F.tab, F.N, F.T, F.H, F.piece.g0, f, b,
+                       a.d_o);
     return hipGetLastError();
 }
 
@@ -759,8 +760,9 @@ static hipError_t launch_bwd_local_t(const BwdArgs& a, hipStream_t st) {
                 (float*)F.vn, (float*)F.am};
     Ws<float> b{(float*)B.qp, (float*)B.km, (float*)B.wn, (float*)B.u, (float*)B.aqk, B.gam, (float*)B.h,
                 (float*)B.vn, nullptr, nullptr, B.pb};
-    hipLaunchKernelGGL(kern, dim3(F.NC * F.H), dim3(4 * D), SM::BYTES, st, (const TIn*)F.q, (const TIn*)F.k,
-                       (const TIn*)F.v, (const TG*)F.la, (const TG*)F.beta, F.tab, F.N, F.T, F.H, f, b, a.d_o,
+    hipLaunchKernelGGL(kern, dim3(F.slots() * F.H), dim3(4 * D), SM::BYTES, st, (const TIn*)F.q, (const TIn*)F.k,
+                       (const TIn*)F.v, (const TG*)F.la, (const TG*)F.beta, F.tab, F.N, F.T, F.H, F.piece.g0, f, b,
+                       a.d_o,
                        a.scr, a.dq, a.dk, a.dv, a.dla, a.dbeta);
     return hipGetLastError();
 }

@@ -18,6 +18,21 @@ struct DecodeArgs {
 
 struct SeqMeta;
 
+// A piece of the chunk slots, [g0, g1): the chunk-parallel kernels cover only
+// these slots and index the workspace from g0; the recursion walks each
+// sequence's chunks inside the piece. A sequence that continues past the
+// piece's entry end (g0 for the forward walk, g1 for the reversed one) starts
+// from `cin`; one that continues past the exit end leaves its state in `cout`
+// (not written when null). Both are [H][D][D] fp32. An empty sequence belongs
+// to the piece holding its slot offset (the last piece also takes offset NC).
+// g1 == 0: no piece, every slot.
+struct Piece {
+    int g0 = 0, g1 = 0;
+    int last = 1;
+    const float* cin = nullptr;
+    float* cout = nullptr;
+};
+
 struct ChunkArgs {
     const void *q, *k, *v, *la, *beta;
     const float* s0;        // may be null
@@ -47,6 +62,8 @@ struct ChunkArgs {
     const void *xq = nullptr, *xk = nullptr, *xv = nullptr, *xa = nullptr, *xb = nullptr;
     const float *wq = nullptr, *wk = nullptr, *wv = nullptr, *A_log = nullptr, *dt_bias = nullptr;
     void* qk_scr = nullptr;
+    Piece piece;
+    int slots() const { return piece.g1 > 0 ? piece.g1 - piece.g0 : NC; }  // chunk slots launched
 };
 
 // Backward of kda_chunk_fwd (see kda_bwd.hip).
@@ -57,7 +74,8 @@ struct BwdArgs {
     float *dq, *dk, *dv, *dla, *dbeta;
     float* scr;        // per chunk-head scratch, bwd_scr_floats(D) floats each (dQ+, dK-)
 };
-// (the gated key products the forward recompute keeps go to fwd.am, [64][64] fp32 per chunk-head)
+// (the gated key products the forward recompute keeps go to fwd.am, [64][64] fp32 per chunk-head;
+// the chunk-parallel backward kernels cover fwd.piece's slots)
 __host__ __device__ inline int64_t bwd_scr_floats(int D) { return 2LL * 64 * D; }
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_local(const BwdArgs& a, hipStream_t st);

@@ -118,7 +118,7 @@ template <int D, typename TIn, typename TG, bool F32, bool PRO = false>
 __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(const TIn* q, const TIn* k, const TIn* v,
                                                       const TG* la, const TG* beta,
                                                       const SeqMeta* __restrict__ tab, int N, int T, int H,
-                                                      Ws<typename Pol<F32>::E> ws, ProArgs pa) {
+                                                      int g0, Ws<typename Pol<F32>::E> ws, ProArgs pa) {
     static_assert(!PRO || (!F32 && std::is_same<TIn, uint16_t>::value && std::is_same<TG, uint16_t>::value),
                   "the fused prologue is bf16 only");
     using P = Pol<F32>;
@@ -159,13 +159,13 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
 
     // head fastest: the workgroups dispatched together read whole token rows of
     // the inputs and write consecutive workspace blocks, in the chunk order the
-    // state recursion consumes them
-    const int gc = blockIdx.x / H;
-    const int h = blockIdx.x - gc * H;
+    // state recursion consumes them (slots from g0, the workspace from 0)
+    const int lc = blockIdx.x / H;
+    const int h = blockIdx.x - lc * H;
     ChunkLoc loc;
-    if (!locate_chunk(tab, N, T, gc, loc)) return;
+    if (!locate_chunk(tab, N, T, g0 + lc, loc)) return;
     const int t0 = loc.t0, L = loc.L;
-    const int64_t chh = (int64_t)gc * H + h;
+    const int64_t chh = (int64_t)lc * H + h;
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, n = l & 15, g = l >> 4;
@@ -869,9 +869,9 @@ static hipError_t launch_prep_t(const ChunkArgs& a, hipStream_t st) {
     auto kern = prep_kernel<D, TIn, TG, F32, PRO>;
     const hipError_t e = allow_dynamic_lds((const void*)kern, SM::BYTES);
     if (e != hipSuccess) return e;
-    dim3 grid(a.NC * a.H), block(256);  // NC * H < 2^31 (checked by the caller)
+    dim3 grid(a.slots() * a.H), block(256);  // NC * H < 2^31 (checked by the caller)
     hipLaunchKernelGGL(kern, grid, block, SM::BYTES, st, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                       (const TG*)a.la, (const TG*)a.beta, a.tab, a.N, a.T, a.H, ws, pa);
+                       (const TG*)a.la, (const TG*)a.beta, a.tab, a.N, a.T, a.H, a.piece.g0, ws, pa);
     return hipGetLastError();
 }
 

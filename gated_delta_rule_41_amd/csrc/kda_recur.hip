@@ -254,7 +254,7 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
                                                                   float* __restrict__ s_final,
                                                                   const SeqMeta* __restrict__ tab, int N, int T,
                                                                   int H, Ws<typename Pol<F32>::E> ws,
-                                                                  void* __restrict__ o) {
+                                                                  void* __restrict__ o, Piece pc) {
     using P = Pol<F32>;
     using E = typename P::E;
     using Frag = typename P::Frag;
@@ -288,7 +288,21 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
     const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 15, g = l >> 4;
 
     const SeqMeta sq = seq_info(tab, T, seq);
-    const int co = sq.coff, nch = sq.nch;
+    int co = sq.coff, nch = sq.nch;
+    // the state the walk starts from and the one it leaves (base of this unit's [D][D])
+    const float* s_in = s0 ? s0 + (int64_t)unit * D * D : nullptr;
+    float* s_out = s_final ? s_final + (int64_t)unit * D * D : nullptr;
+    if (pc.g1 > 0) {
+        // only this sequence's chunks inside the piece; a walk that enters or
+        // leaves through a cut takes its state from cin or leaves it in cout
+        const int lo = co > pc.g0 ? co : pc.g0, hi = co + nch < pc.g1 ? co + nch : pc.g1;
+        if (nch == 0 ? !(co >= pc.g0 && (co < pc.g1 || pc.last)) : lo >= hi) return;  // uniform
+        const bool cut_lo = nch > 0 && lo > co, cut_hi = nch > 0 && hi < co + nch;
+        if (ADDP ? cut_hi : cut_lo) s_in = pc.cin ? pc.cin + (int64_t)h * D * D : nullptr;
+        if (ADDP ? cut_lo : cut_hi) s_out = pc.cout ? pc.cout + (int64_t)h * D * D : nullptr;
+        co = lo - pc.g0;  // workspace slots count from the piece's start
+        nch = nch > 0 ? hi - lo : 0;
+    }
     char* hvbase = ring + RING * PL::SLOT;  // h_n / V_new exchange buffers (FUSED)
     char* pbase = hvbase + PL::HV;          // K-^T V buffers (DPLR)
 
@@ -520,12 +534,12 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
         f32x4_t* XS = reinterpret_cast<f32x4_t*>(ring + RING * PL::SLOT);  // [NT][64 lanes] state tiles
         f32x4_t* XV = XS + NT * 64;                                        // [4][64] V_new tiles
         f32x4_t S[TH];  // rows 16 (TH q + tt) + 4g + i, column 16 ct + n
-        const int64_t sbase = (int64_t)unit * D * D + 16 * ct + n;
+        const int sbase = 16 * ct + n;
 #pragma unroll
         for (int tt = 0; tt < TH; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                S[tt][i] = s0 ? s0[sbase + (int64_t)(16 * (TH * q + tt) + 4 * g + i) * D] : 0.f;
+                S[tt][i] = s_in ? s_in[sbase + (16 * (TH * q + tt) + 4 * g + i) * D] : 0.f;
         // ADDP: the added term of chunk c + 1 is loaded at the start of chunk c
         f32x4_t pc[ADDP ? TH : 1], pnx[ADDP ? TH : 1];
         auto load_p = [&](int c, f32x4_t (&dst)[ADDP ? TH : 1]) {
@@ -628,23 +642,22 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
             }
             lds_exchange_barrier();  // end of chunk: slot free, state tiles in LDS
         }
-        if (s_final) {
+        if (s_out) {
 #pragma unroll
             for (int tt = 0; tt < TH; ++tt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    s_final[sbase + (int64_t)(16 * (TH * q + tt) + 4 * g + i) * D] = S[tt][i];
+                for (int i = 0; i < 4; ++i) s_out[sbase + (16 * (TH * q + tt) + 4 * g + i) * D] = S[tt][i];
         }
         return;
     }
 
     // ---------------- compute wave (the fused chain; the unfused one returned above)
     f32x4_t S[NT];  // state slab: rows 16t + 4g + i, column 16 ct + n
-    const int64_t sbase = (int64_t)unit * D * D + 16 * ct + n;
+    const int sbase = 16 * ct + n;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[t][i] = s0 ? s0[sbase + (int64_t)(16 * t + 4 * g + i) * D] : 0.f;
+        for (int i = 0; i < 4; ++i) S[t][i] = s_in ? s_in[sbase + (16 * t + 4 * g + i) * D] : 0.f;
 
     // HP: this slab's fp32 U of the next chunk, loaded from the workspace one
     // chunk ahead (the compute wave's only global loads in the loop, so the
@@ -771,11 +784,11 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
         if constexpr (FUSED) wait_lgkm0();  // h_n / V_new in LDS before the hand-over
         __builtin_amdgcn_s_barrier();
     }
-    if (s_final) {
+    if (s_out) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s_final[sbase + (int64_t)(16 * t + 4 * g + i) * D] = S[t][i];
+            for (int i = 0; i < 4; ++i) s_out[sbase + (16 * t + 4 * g + i) * D] = S[t][i];
     }
 }
 
@@ -791,7 +804,7 @@ static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     const hipError_t e = allow_dynamic_lds((const void*)kern, PL::LDS);
     if (e != hipSuccess) return e;
     dim3 grid(NU * NT), block(FUSED ? (DPLR ? 448 : 384) : 64 * (PL::NCW + 2));
-    hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.tab, a.N, a.T, a.H, ws, a.o);
+    hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.tab, a.N, a.T, a.H, ws, a.o, a.piece);
     return hipGetLastError();
 }
 

@@ -212,11 +212,22 @@ kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, co
                                  float* final_state, void* stream);
 
 /*
- * Bytes of device workspace kda_chunk_bwd needs (host call, no device access):
- * the forward recomputed with fp32 factors (with the gated key products), the
- * state-gradient recursion's operands and outputs, and per-chunk scratch, for
- * at most floor((T_total + 63*N) / 64) chunks per head (640,000 bytes per
- * chunk-head at dk = dv = 128).
+ * The backward's default bound on the chunk-heads (chunk slots x heads) one
+ * piece of its work covers; see kda_chunk_bwd_workspace_size.
+ */
+#define KDA_BWD_PIECE_CHUNK_HEADS 65536
+
+/*
+ * Bytes of device workspace kda_chunk_bwd asks for by default (host call, no
+ * device access). Per chunk-head of a piece: the forward recomputed with fp32
+ * factors (with the gated key products, h_n and V_new), the state-gradient
+ * recursion's operand and outputs, its added term and the local kernel's
+ * scratch (one region, used in turn): 459,264 bytes at dk = dv = 128, 213,248
+ * at 64. The chunk slots are floor((T_total + 63*N) / 64); while slots x H is
+ * at most KDA_BWD_PIECE_CHUNK_HEADS one piece covers them all, else each piece
+ * covers floor(KDA_BWD_PIECE_CHUNK_HEADS / H) slots (at least one) and one
+ * [H, dk, dv] fp32 state per piece is added (the state at the piece's first
+ * slot). At N = 1, T_total = 2^20, H = 32, d = 128: 8 pieces, about 30.1 GB.
  *   bytes: host out-pointer, written on KDA_OK.
  */
 kda_status kda_chunk_bwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,
@@ -239,12 +250,22 @@ kda_status kda_chunk_bwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
  *   dbeta [T_total, H] fp32  (outputs, written for every token)
  *   d_initial_state [N, H, dk, dv] fp32 or NULL; it may be the same pointer as
  *                   d_final_state (in place), any other overlap is KDA_ERR_ALIAS
- *   workspace       at least kda_chunk_bwd_workspace_size() bytes, 256-byte
- *                   aligned; contents on entry do not matter
+ *   workspace       256-byte aligned; contents on entry do not matter. Its
+ *                   size sets the pieces: the call takes the largest piece
+ *                   (in chunk slots) whose workspace fits in workspace_bytes,
+ *                   all slots if they fit. Any size down to one slot per piece
+ *                   works; less is KDA_ERR_WORKSPACE.
+ * With more than one piece the forward runs twice: once over all pieces but
+ * the last for the states at the pieces' first slots, then piece by piece in
+ * reverse with the backward of each piece (the state gradient is handed from
+ * piece to piece at the same slots, in fp32 as the recursion carries it), so
+ * the gradients are bitwise the same for every piece size.
  * Arithmetic is fp32 throughout (bf16 inputs are widened exactly; every
  * product runs on fp32 matrix cores). The same log_alpha condition as
- * kda_chunk_fwd holds (<= 0 for the overflow guarantees). Five kernels are enqueued. Deterministic: every sum has a
- * fixed order, so equal inputs give bitwise equal gradients.
+ * kda_chunk_fwd holds (<= 0 for the overflow guarantees). One piece enqueues
+ * five kernels (six with cu_seqlens: the sequence table first); each further
+ * piece adds seven. Deterministic: every sum has a fixed order, so equal
+ * inputs give bitwise equal gradients.
  */
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* beta, const float* initial_state, const int32_t* cu_seqlens,

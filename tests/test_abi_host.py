@@ -11,6 +11,7 @@ import re
 import pytest
 
 import gated_delta_rule_41_amd as kda
+import ws_layout
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
@@ -193,18 +194,48 @@ def test_dplr_validation():
 
 def test_bwd_workspace_size_formula():
     # per chunk-head, d = 128: the fp32 forward recompute (Q+, K-, -W, U, V_new
-    # 32 KiB each, A_qk 16 KiB, gamma 512 B, h_n 64 KiB) twice (forward and the
-    # state-gradient recursion), the added term Q+^T dO 64 KiB, the gated key
-    # products 16 KiB and the local kernel's scratch (dQ+, dK-) 64 KiB -> 640000 B
+    # 32 KiB each, A_qk 16 KiB, gamma 512 B, h_n 64 KiB), the state-gradient
+    # chain's U, states and V_new (32 + 64 + 32 KiB), the added term Q+^T dO
+    # whose 64 KiB the local kernel's scratch (dQ+, dK-) reuses, the gated key
+    # products 16 KiB -> 459264 B
     fwd = 5 * 32768 + 16384 + 512 + 65536
-    # (+ the sequence table, (N + 1) x 16 B rounded up to 256)
-    assert kda.bwd_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * (2 * fwd + 65536 + 16384 + 65536) + 256
-    assert kda.bwd_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 640000 + 256
+    assert ws_layout.bwd_chunk_head_bytes(128) == fwd + 131072 + 65536 + 16384 == 459264
     fwd64 = 5 * 16384 + 16384 + 256 + 16384
-    assert kda.bwd_workspace_size(2, 100, 1, 64, 64) == ((100 + 63 * 2) // 64) * (
-        2 * fwd64 + 16384 + 16384 + 32768) + 256
+    assert ws_layout.bwd_chunk_head_bytes(64) == fwd64 + 3 * 16384 + 32768 + 16384 == 213248
+    # (+ the sequence table, (N + 1) x 16 B rounded up to 256)
+    assert kda.bwd_workspace_size(1, 4096, 32, 128, 128) == 64 * 32 * 459264 + 256
+    assert kda.bwd_workspace_size(2, 100, 1, 64, 64) == ((100 + 63 * 2) // 64) * 213248 + 256
     with pytest.raises(kda.KDAError):
         kda.bwd_workspace_size(1, 10, 1, 64, 128)
+
+
+def test_bwd_workspace_pieces():
+    """Beyond KDA_BWD_PIECE_CHUNK_HEADS chunk-heads the size query plans pieces
+    of floor(65536 / H) slots plus one [H, d, d] state per piece: the 1M-token
+    sequence at H = 32, d = 128 takes 8 pieces of 2048 slots, about 30.1 GB."""
+    T = 1 << 20
+    got = kda.bwd_workspace_size(1, T, 32, 128, 128)
+    assert got == ws_layout.bwd_bytes(1, T, 32, 128, 2048) == 2048 * 32 * 459264 + 8 * 32 * 65536 + 256
+    assert got < 100e9
+    # exactly at the bound: one piece; one slot more: pieces
+    assert kda.bwd_workspace_size(1, 2048 * 64, 32, 128, 128) == 2048 * 32 * 459264 + 256
+    assert kda.bwd_workspace_size(1, 2048 * 64 + 1, 32, 128, 128) == ws_layout.bwd_bytes(1, 2048 * 64 + 1, 32,
+                                                                                         128, 2048)
+    # as many heads as the bound: one slot per piece
+    assert kda.bwd_workspace_size(1, 128, 65536, 64, 64) == ws_layout.bwd_bytes(1, 128, 65536, 64, 1)
+
+
+def test_bwd_smallest_workspace():
+    """Any workspace down to one slot per piece passes validation (here the
+    call then fails at its first launch, with no GPU); one byte less is
+    KDA_ERR_WORKSPACE."""
+    for N, T, cu in ((1, 256, None), (3, 200, 0x100000000000 - 4096)):
+        least = ws_layout.bwd_bytes(N, T, 2, 64, 1, have_cu=cu is not None)
+        assert bwd_call(N=N, T=T, cu=cu, ws_bytes=least - 1) == WORKSPACE
+        assert bwd_call(N=N, T=T, cu=cu, ws_bytes=least) == HIP
+        for pc in (2, 3):
+            assert bwd_call(N=N, T=T, cu=cu, ws_bytes=ws_layout.bwd_bytes(N, T, 2, 64, pc,
+                                                                            have_cu=cu is not None)) == HIP
 
 
 def bwd_call(**over):
@@ -240,7 +271,8 @@ def test_bwd_validation():
     assert bwd_call(dfin=d, ds0=d + 256) == ALIAS
     assert bwd_call(ws=f(64)) == WORKSPACE
     need = kda.bwd_workspace_size(1, 256, 2, 64, 64)
-    assert bwd_call(ws_bytes=need - 1) == WORKSPACE
+    assert bwd_call(ws_bytes=need - 1) == HIP  # smaller pieces (then no GPU to launch on)
+    assert bwd_call(ws_bytes=ws_layout.bwd_bytes(1, 256, 2, 64, 1) - 1) == WORKSPACE
     w = f()
     assert bwd_call(ws=w, do=w + need // 2) == ALIAS
 

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import kda_inputs as ki
+import ws_layout
 from oracle import backward as bw
 from parity import err, kda, say
 
@@ -86,3 +87,60 @@ def test_deterministic():
     torch.cuda.synchronize()
     for nm in NAMES:
         assert torch.equal(a[nm], b[nm]), nm
+
+
+# The backward in pieces of a few chunk slots (the workspace given sets the
+# piece): the forward states at the pieces' first slots, then the pieces in
+# reverse. The state crosses each cut in fp32 exactly as the recursion carries
+# it, so every gradient must equal the one-piece call's bit for bit. The
+# lengths put cuts inside sequences, at sequence ends, next to empty sequences
+# and inside sequences spanning several pieces; [1, 1, 1, 0] fills the chunk
+# capacity, so its empty last sequence sits at slot offset NC (the last piece's).
+PIECE_CASES = [
+    ("ragged-d128-bf16", [70, 0, 150, 5, 0, 300, 1, 0], 128, torch.bfloat16, [1, 2, 3, 5]),
+    ("ragged-d64-fp32", [70, 0, 150, 5, 0, 300, 1, 0], 64, torch.float32, [1, 4, 7]),
+    ("full-capacity-d64-fp32", [1, 1, 1, 0], 64, torch.float32, [1, 2]),
+    ("one-sequence-d128-bf16", None, 128, torch.bfloat16, [1, 2]),
+]
+
+
+@pytest.mark.parametrize("label,lengths,d,dt,pieces", PIECE_CASES, ids=[c[0] for c in PIECE_CASES])
+def test_pieces_bitwise_equal(label, lengths, d, dt, pieces):
+    case = ki.make_prefill("varlen-16", DEV, lengths=lengths or [300], H=2, dk=d, dv=d, dtype=dt, s0_std=0.02)
+    cu = case.cu_seqlens if lengths is not None else None
+    T, H, N = case.T_total, case.H, case.N
+    d_o, d_fin = upstream(case)
+    args = (case.q, case.k, case.v, case.log_alpha, case.beta, d_o, case.initial_state, cu, d_fin)
+    whole = kda.chunk_bwd(*args)
+    assert kda.bwd_workspace_size(N, T, H, d, d) == ws_layout.bwd_bytes(N, T, H, d, ws_layout.chunk_capacity(
+        N, T, cu is not None), cu is not None)
+    for pc in pieces:
+        ws = torch.empty(ws_layout.bwd_bytes(N, T, H, d, pc, cu is not None), dtype=torch.uint8, device=DEV)
+        say(f"[bwd pieces] {label}: T={T} N={N} piece={pc} slots, workspace {ws.numel()} B")
+        got = kda.chunk_bwd(*args, workspace=ws)
+        torch.cuda.synchronize()
+        for nm in NAMES:
+            assert torch.equal(got[nm], whole[nm]), (pc, nm)
+    # in place (the initial states' gradient over d_final_state), one slot per piece
+    ws = torch.empty(ws_layout.bwd_bytes(N, T, H, d, 1, cu is not None), dtype=torch.uint8, device=DEV)
+    dfin = d_fin.clone()
+    kda.chunk_bwd(*args[:-1], dfin, workspace=ws, out={"dinitial_state": dfin})
+    torch.cuda.synchronize()
+    assert torch.equal(dfin, whole["dinitial_state"])
+
+
+def test_pieces_against_oracle():
+    """One piece per chunk slot, checked against the gradient oracle directly."""
+    case = ki.make_prefill("varlen-16", DEV, lengths=[70, 0, 150, 5], H=2, dk=64, dv=64, dtype=torch.float32,
+                           s0_std=0.02)
+    d_o, d_fin = upstream(case)
+    T, H, N = case.T_total, case.H, case.N
+    ws = torch.empty(ws_layout.bwd_bytes(N, T, H, 64, 1), dtype=torch.uint8, device=DEV)
+    got = kda.chunk_bwd(case.q, case.k, case.v, case.log_alpha, case.beta, d_o, case.initial_state,
+                        case.cu_seqlens, d_fin, workspace=ws)
+    torch.cuda.synchronize()
+    ref = bw.recurrence_grads(case.q, case.k, case.v, case.log_alpha, case.beta, case.initial_state,
+                              case.cu_seqlens.cpu(), d_o.cpu(), d_fin.cpu())
+    errs = {nm: err(got[nm], ref[nm]) for nm in NAMES}
+    say("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL_BWD for v in errs.values()), errs

@@ -1,5 +1,5 @@
 """Guard bands around every buffer a call writes: o, the final states, the
-workspace (prefill, backward), the decode state and its o. Each buffer is a
+workspace (prefill, backward, the backward in pieces), the decode state and its o. Each buffer is a
 view into a larger allocation whose 4 KiB before and after are filled with a
 byte pattern; after the call (and a synchronisation) the bands must be
 unchanged, and the call's results must still match the plain call's. Cases:
@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import kda_inputs as ki
+import ws_layout
 from parity import kda, say
 
 pytestmark = pytest.mark.gpu
@@ -70,6 +71,14 @@ def test_prefill_and_backward_write_only_their_buffers(name, lengths, d, dt):
                         case.cu_seqlens, d_fin, workspace=bws.t, out={k_: v_.t for k_, v_ in outs.items()})
     torch.cuda.synchronize()
     assert bws.intact() and all(v_.intact() for v_ in outs.values())
+    for k_ in outs:
+        assert torch.equal(got[k_], ref[k_]), k_
+    # in pieces of one chunk slot (a workspace with the boundary states at its end)
+    pws = Guarded((ws_layout.bwd_bytes(N, T, H, d, 1),), torch.uint8)
+    got = kda.chunk_bwd(case.q, case.k, case.v, case.log_alpha, case.beta, d_o, case.initial_state,
+                        case.cu_seqlens, d_fin, workspace=pws.t, out={k_: v_.t for k_, v_ in outs.items()})
+    torch.cuda.synchronize()
+    assert pws.intact() and all(v_.intact() for v_ in outs.values())
     for k_ in outs:
         assert torch.equal(got[k_], ref[k_]), k_
 

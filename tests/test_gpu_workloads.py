@@ -77,3 +77,39 @@ def test_long_1m_sampled(wl, heads, seed):
     es = err(S[:, heads], S_ref)
     say(f"    err(o@samples)={eo:.3e} err(o@boundaries)={eb:.3e} err(S)={es:.3e}")
     assert eo <= TOL_BF16 and eb <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_long_1m_backward_window():
+    """The backward at the 1M-token shape with the default workspace (8 pieces
+    of 2,048 chunk slots). d_o is nonzero only on a window of tokens across the
+    first piece boundary (token 131,072) and the final states get no gradient,
+    so the state gradient after the window is exactly zero: every gradient of
+    a later token must be exactly 0 (all heads), and the window's gradients
+    follow from the window alone given the state at its first token. The
+    oracle runs the forward recurrence up to the window for one head, then its
+    autograd backward over the window."""
+    from oracle import backward as bw
+    T = 1 << 20
+    case = ki.make_prefill("long-1m", DEV)
+    H, D = case.H, case.dk
+    t0, t1, head = 131072 - 150, 131072 + 106, [9]
+    assert kda.bwd_workspace_size(1, T, H, D, D) < 100e9
+    g = torch.Generator(device=DEV).manual_seed(13)
+    d_o = torch.zeros(T, H, D, device=DEV)
+    d_o[t0:t1] = torch.randn(t1 - t0, H, D, generator=g, device=DEV)
+    say(f"[long-1m backward] T={T} H={H} window [{t0}, {t1}) head={head}")
+    got = kda.chunk_bwd(case.q, case.k, case.v, case.log_alpha, case.beta, d_o, case.initial_state)
+    torch.cuda.synchronize()
+    for nm in ("dq", "dk", "dv", "dlog_alpha", "dbeta"):
+        assert not got[nm][t1:].any(), nm  # exactly zero after the window
+        assert torch.isfinite(got[nm]).all(), nm
+    assert torch.isfinite(got["dinitial_state"]).all()
+    q, k, v, la = (head_slice(t[:t1], head) for t in (case.q, case.k, case.v, case.log_alpha))
+    b = case.beta[:t1, head].contiguous().cpu()
+    s0 = case.initial_state[:, head].contiguous().cpu()
+    _, S_t0, _ = oracle.recurrence(q[:t0], k[:t0], v[:t0], la[:t0], b[:t0], s0, None, want_o=False, col_blocks=16)
+    ref = bw.recurrence_grads(q[t0:], k[t0:], v[t0:], la[t0:], b[t0:], S_t0, None,
+                              head_slice(d_o[t0:t1], head))
+    errs = {nm: err(got[nm][t0:t1, head], ref[nm]) for nm in ("dq", "dk", "dv", "dlog_alpha", "dbeta")}
+    say("    " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()))
+    assert all(v_ <= 1e-3 for v_ in errs.values()), errs

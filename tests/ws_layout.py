@@ -189,3 +189,23 @@ def decode_dplr(ws: torch.Tensor, N, T, H, D, have_cu, gc, h):
     b = off[7] + chh * D * 4
     out["gam"] = raw[b:b + D * 4].copy().view(np.float32).astype(np.float64)
     return out
+
+
+def bwd_chunk_head_bytes(D):
+    """Backward workspace per chunk-head of a piece: the fp32 forward plan, the
+    state-gradient chain's U, h and V_new, the region its added term and then
+    the local kernel's scratch share, and the gated key products."""
+    fwd = plan(1, 1, D, True)[1]
+    chain = CH * D * 4 + D * D * 4 + CH * D * 4
+    shared = max(2 * CH * D, D * D) * 4
+    return fwd + chain + shared + CH * CH * 4
+
+
+def bwd_bytes(N, T, H, D, piece, have_cu=True):
+    """Workspace of kda_chunk_bwd when it runs in pieces of `piece` chunk slots:
+    the per-piece arrays, one [H][D][D] fp32 state per piece when there is more
+    than one, the sequence table."""
+    NC = chunk_capacity(N, T, have_cu)
+    npieces = -(-NC // piece) if NC else 1
+    table = ((N + 1) * 16 + 255) // 256 * 256
+    return piece * H * bwd_chunk_head_bytes(D) + (npieces * H * D * D * 4 if npieces > 1 else 0) + table
