@@ -12,8 +12,9 @@ back to back ("warm"). The same protocol runs on ``prefill-4k`` and
 ``varlen-16`` (reported under "workloads"). The decode step (the remaining row
 of the hot path) is timed on ``decode-256`` (256 sequences x 32 heads, fp32
 states of 512 MiB, updated in place, 1000 steps). The general-DPLR comparison
-operator, the chunkwise backward and the layer around the operator are timed on
-prefill-4k. Prints ONE JSON line.
+operator and the layer around the operator are timed on prefill-4k, the
+chunkwise backward on prefill-4k, varlen-16 and long-1m (in pieces). Prints ONE
+JSON line.
 
     python bench.py [--steps K] [--warmup W] [--decode-steps S] [--headline-only] [--no-cpu-baseline]
                     [--no-dplr] [--no-bwd] [--no-layer] [--no-decode]
@@ -55,8 +56,9 @@ KERNEL_BYTES_PER_TOKEN_HEAD = {
     # Q+ (256 each), U 512, A_qk 256, gamma 8; writes o (fp32 512)
     "recur": 1544 + 512,
 }
-# fp32 inputs (not benchmarked) run the unfused pair: recursion 776 + 768 (h_n,
-# V_new written), output 1152 + 512
+# fp32 inputs (not benchmarked) run the unfused pair: the recursion reads -W, K-,
+# U (fp32 512 each) and gamma 8 and writes h_n 1024 + V_new 512; the output reads
+# Q+ 512, A_qk 256, h_n 1024, V_new 512 and writes o 512
 KERNEL_SYMBOL = {"prep": "prep_kernel", "recur": "recur_kernel", "decode": "decode_kernel",
                  "dplr_prep": "dplr_prep_kernel", "dplr_recur": "recur_kernel",
                  "bwd_fwd_prep": "prep_kernel", "bwd_fwd_recur": "recur_kernel",

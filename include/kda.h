@@ -139,8 +139,16 @@ kda_status kda_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
  *   cu_seqlens    [N+1] int32 device array of sequence starts (cu[0] = 0,
  *                 non-decreasing, cu[N] = T_total), or NULL for one sequence
  *                 (then N must be 1). Zero-length sequences are allowed (their
- *                 final state equals the initial state). A malformed array is
- *                 undefined behaviour (it is not read on the host).
+ *                 final state equals the initial state). It is read only on the
+ *                 device, where a first kernel turns it into a sequence table
+ *                 at the end of the workspace: sequence i covers tokens
+ *                 [s, e) with s = cu[i] clamped into [0, T_total] and e =
+ *                 cu[i+1] clamped into [s, T_total], and chunks beyond the
+ *                 workspace's floor((T_total + 63*N) / 64) slots are dropped
+ *                 (in order of the sequences). A malformed array thus gives
+ *                 defined, in-bounds work on those ranges; o rows no range
+ *                 covers are not written, and a row two ranges share holds
+ *                 either range's result.
  *   o             [T_total, H, dv] out_dtype, written for every token
  *                 (q, k, v, log_alpha, beta and o may be NULL when T_total == 0)
  *   final_state   [N, H, dk, dv] fp32, or NULL if not wanted. It may be the
