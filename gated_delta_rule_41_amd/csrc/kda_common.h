@@ -42,12 +42,22 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
     __bf16 h = (__bf16)f;
     return __builtin_bit_cast(uint16_t, h);
 }
+// Two values rounded to nearest even and packed (lo in bits 0-15) by one
+// conversion instruction (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32): written as a
+// vector conversion, because two scalar conversions joined by shifts compile to
+// two conversions plus the joining operations.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 // round-to-nearest-even fp32 <-> fp16
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
+}
 
 // k-slot -> logical k inside a 32-deep slice ("split" order, see above)
 __host__ __device__ constexpr int kslot(int g, int j) { return 16 * (j >> 2) + 4 * g + (j & 3); }
@@ -146,9 +156,9 @@ template <> struct APol<false> {
         u32x4_t h, l;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint16_t h0 = f2bf(x[2 * j]), h1 = f2bf(x[2 * j + 1]);
-            h[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            l[j] = pack2bf(x[2 * j] - bf2f(h0), x[2 * j + 1] - bf2f(h1));
+            const uint32_t hj = pack2bf(x[2 * j], x[2 * j + 1]);
+            h[j] = hj;
+            l[j] = pack2bf(x[2 * j] - __uint_as_float(hj << 16), x[2 * j + 1] - __uint_as_float(hj & 0xffff0000u));
         }
         f.hi = __builtin_bit_cast(bf16x8_t, h);
         f.lo = __builtin_bit_cast(bf16x8_t, l);
@@ -374,13 +384,19 @@ struct Frag2 {
     Pol<false>::Frag hi, lo;
 };
 __device__ __forceinline__ Frag2 split_frag(const float (&x)[8]) {
-    float h[8], r[8];
+    u32x4_t h, r;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        h[j] = h2f(f2h(x[j]));
-        r[j] = x[j] - h[j];
+    for (int j = 0; j < 4; ++j) {
+        // (through a scalar: a bit cast of the vector element itself reads element 0)
+        const uint32_t hj = pack2h(x[2 * j], x[2 * j + 1]);
+        h[j] = hj;
+        const f16x2_t hh = __builtin_bit_cast(f16x2_t, hj);
+        r[j] = pack2h(x[2 * j] - (float)hh[0], x[2 * j + 1] - (float)hh[1]);
     }
-    return Frag2{Pol<false>::make(h), Pol<false>::make(r)};
+    Frag2 f;
+    f.hi.v = __builtin_bit_cast(f16x8_t, h);
+    f.lo.v = __builtin_bit_cast(f16x8_t, r);
+    return f;
 }
 __device__ __forceinline__ Frag2 split_from_acc(const f32x4_t& t0, const f32x4_t& t1) {
     const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};

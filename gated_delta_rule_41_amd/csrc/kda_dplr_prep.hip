@@ -128,8 +128,8 @@ __device__ __forceinline__ Pol<false>::Frag tiles_frag(const uint16_t* tiles, in
 
 __device__ __forceinline__ u32x2_t pack4h(const f32x4_t& x, float sign) {
     u32x2_t pk;
-    pk[0] = (uint32_t)f2h(sign * x[0]) | ((uint32_t)f2h(sign * x[1]) << 16);
-    pk[1] = (uint32_t)f2h(sign * x[2]) | ((uint32_t)f2h(sign * x[3]) << 16);
+    pk[0] = pack2h(sign * x[0], sign * x[1]);
+    pk[1] = pack2h(sign * x[2], sign * x[3]);
     return pk;
 }
 

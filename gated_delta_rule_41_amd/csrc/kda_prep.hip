@@ -405,8 +405,8 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
             f32x4_t t = {0.f, 0.f, 0.f, 0.f};
             P::mma(t, a, sel[hf]);
             u32x2_t pk;
-            pk[0] = (uint32_t)f2h(t[0]) | ((uint32_t)f2h(t[1]) << 16);
-            pk[1] = (uint32_t)f2h(t[2]) | ((uint32_t)f2h(t[3]) << 16);
+            pk[0] = pack2h(t[0], t[1]);
+            pk[1] = pack2h(t[2], t[3]);
             if constexpr (decltype(to_km)::value)
                 *reinterpret_cast<u32x2_t*>(dst + (32 * s + 16 * hf + n) * 64 + 32 * (w >> 1) + 8 * g + 4 * (w & 1)) = pk;
             else
