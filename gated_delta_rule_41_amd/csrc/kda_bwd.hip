@@ -87,6 +87,76 @@ __device__ __forceinline__ float sum16(float x) {  // over the 16 lanes n of a l
 }
 
 // ---------------------------------------------------------------------------
+// Rows of a [T, H, D] array <-> the own-element layout (lane n + 16 G of wave w:
+// channel 16 w + n of rows 16 R + 4 G + i, as one f32x4 per row block R),
+// through the matrix cores: each lane moves 16 bytes of one row, and a product
+// with a 0/1 selector puts every element where the other layout wants it
+// (exact: one input times 1 plus zeros; a NaN or infinity among a tile's 16
+// channels spreads through the zero products to the rest of its row). Rows at
+// or past L read as zeros and are not stored.
+template <typename T> struct OwnRows;
+template <> struct OwnRows<uint16_t> {  // bf16: lane loads 8 channels of its 32-channel slice
+    using Raw = u32x4_t;
+    static __device__ __forceinline__ int64_t col(int w, int G) { return 32 * (w >> 1) + 8 * G; }
+    static __device__ __forceinline__ void to_own(const Raw (&raw)[4], int w, int l, f32x4_t (&out)[4]) {
+        const int G = l >> 4, n = l & 15, own = 16 * (w & 1) + n;
+        u32x4_t sv;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            sv[jj] = (8 * G + 2 * jj == own ? 0x3F80u : 0u) | (8 * G + 2 * jj + 1 == own ? 0x3F800000u : 0u);
+        const bf16x8_t sb = __builtin_bit_cast(bf16x8_t, sv);
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+            out[R] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, raw[R]), sb,
+                                                             f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    }
+};
+template <> struct OwnRows<float> {  // fp32: lane loads 4 channels of its wave's 16
+    using Raw = f32x4_t;
+    static __device__ __forceinline__ int64_t col(int w, int G) { return 16 * w + 4 * G; }
+    static __device__ __forceinline__ void to_own(const Raw (&raw)[4], int w, int l, f32x4_t (&out)[4]) {
+        const int G = l >> 4, n = l & 15;
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) a = mfma4(raw[R][t], 4 * G + t == n ? 1.f : 0.f, a);
+            out[R] = a;
+        }
+    }
+};
+// issue the loads of rows 16 R + n (the lane's row of each block) of head h
+template <typename T>
+__device__ __forceinline__ void own_load(const T* p, int t0, int L, int H, int h, int D, int w, int l,
+                                         typename OwnRows<T>::Raw (&raw)[4]) {
+    using Raw = typename OwnRows<T>::Raw;
+    const int n = l & 15;
+    const int64_t cc = OwnRows<T>::col(w, l >> 4);
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+        const int r = 16 * R + n;
+        raw[R] = *reinterpret_cast<const Raw*>(p + ((int64_t)(t0 + (r < L ? r : 0)) * H + h) * D + cc);
+    }
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+        if (16 * R + n >= L) raw[R] = Raw{};
+}
+// own tiles -> 16-byte row stores (fp32 outputs)
+__device__ __forceinline__ void own_store(float* p, int t0, int L, int H, int h, int D, int w, int l,
+                                          const f32x4_t (&x)[4]) {
+    const int G = l >> 4, n = l & 15;
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+        f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a = mfma4(x[R][t], 4 * G + t == n ? 1.f : 0.f, a);
+        // lane n + 16 G: row 16 R + n, channels 16 w + 4 G .. + 3
+        if (16 * R + n < L)
+            *reinterpret_cast<f32x4_t*>(p + ((int64_t)(t0 + 16 * R + n) * H + h) * D + 16 * w + 4 * G) = a;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // The state-gradient recursion's per-chunk operands for chunk slot gc:
 // U := A_qk^T dO (accumulator tiles [dv/16][4][64 lanes][4]) and the added term
 // P = Q+^T dO ([dv/16][dk/16][64 lanes][4]). Wave w owns value columns
@@ -369,17 +439,24 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
     // own inputs and the cumulative gate (natural log units)
     float qo[4][4], ko[4][4], g2[4][4];
     {
+        typename OwnRows<TIn>::Raw rq[4], rk[4];
+        typename OwnRows<TG>::Raw rg[4];
+        own_load(q, t0, L, H, h, D, w, l, rq);
+        own_load(k, t0, L, H, h, D, w, l, rk);
+        own_load(la, t0, L, H, h, D, w, l, rg);
+        f32x4_t tq[4], tk[4], tg[4];
+        OwnRows<TIn>::to_own(rq, w, l, tq);
+        OwnRows<TIn>::to_own(rk, w, l, tk);
+        OwnRows<TG>::to_own(rg, w, l, tg);
         float part[4];
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
             float x = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = own_row(R, i);
-                const bool ok = r < L;
-                qo[R][i] = ok ? ld_in(q, rowoff(r) + c) : 0.f;
-                ko[R][i] = ok ? ld_in(k, rowoff(r) + c) : 0.f;
-                x += ok ? ld_in(la, rowoff(r) + c) : 0.f;
+                qo[R][i] = tq[R][i];
+                ko[R][i] = tk[R][i];
+                x += tg[R][i];
                 g2[R][i] = x;  // prefix over the lane's 4 rows
             }
             part[R] = x;
@@ -454,8 +531,12 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
         xw[m] = *reinterpret_cast<const f32x4_t*>(f.wn + fs * 64 * D + 4 * (tid + NTH * m));
         xu[m] = *reinterpret_cast<const f32x4_t*>(f.u + fs * 64 * D + 4 * (tid + NTH * m));
     }
+    typename OwnRows<TIn>::Raw rv[4];
+    own_load(v, t0, L, H, h, D, w, l, rv);
     float dBk[4][4];
     {
+        f32x4_t vo[4], dvo[4];
+        OwnRows<TIn>::to_own(rv, w, l, vo);
         float rowp[4][4];
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
@@ -473,13 +554,13 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
             for (int i = 0; i < 4; ++i) {
                 const int r = own_row(R, i);
                 dBk[R][i] = ak[i];
-                const float vv = r < L ? ld_in(v, rowoff(r) + c) : 0.f;
-                if (r < L) dv[rowoff(r) + c] = bet[r] * av[i];
-                rowp[R][i] = ee(g2[R][i]) * ko[R][i] * ak[i] + vv * av[i];
+                dvo[R][i] = bet[r] * av[i];
+                rowp[R][i] = ee(g2[R][i]) * ko[R][i] * ak[i] + vo[R][i] * av[i];
                 DB[r * RX + c] = ak[i];
                 DB[r * RX + D + c] = av[i];
             }
         }
+        own_store(dv, t0, L, H, h, D, w, l, dvo);
 #pragma unroll
         for (int R = 0; R < 4; ++R)
 #pragma unroll
@@ -661,6 +742,7 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
     const float gl = __shfl(g2[3][3], 48 + n);  // cumulative gate of the chunk's last row
     const float dgam = dgp[c] + dgp[D + c];
     float dg[4][4], lsum = 0.f;
+    f32x4_t dqo[4], dko[4];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
         const f32x4_t dqp = *reinterpret_cast<const f32x4_t*>(SQ + ((w * 4 + R) * 64 + l) * 4);
@@ -676,12 +758,12 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
             dg[R][i] = qv * Lq[R][i] + kv * Lk[R][i] - kv * Rr[R][i] + dqp[i] * E * qv + dkp * E * kv -
                        dkm[i] * Em * kv;
             lsum += dkm[i] * Em * kv;
-            if (r < L) {
-                dq[rowoff(r) + c] = dqv;
-                dk[rowoff(r) + c] = dkv;
-            }
+            dqo[R][i] = dqv;
+            dko[R][i] = dkv;
         }
     }
+    own_store(dq, t0, L, H, h, D, w, l, dqo);
+    own_store(dk, t0, L, H, h, D, w, l, dko);
     {
         float tot = 0.f;
 #pragma unroll
@@ -701,6 +783,7 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
             S[R] = s;
         }
         float later = 0.f;  // whole blocks after R
+        f32x4_t dlo[4];
 #pragma unroll
         for (int R = 3; R >= 0; --R) {
             float after = 0.f, total = 0.f;
@@ -711,12 +794,10 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
                 total += t;
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = own_row(R, i);
-                if (r < L) dla[rowoff(r) + c] = dg[R][i] + after + later;
-            }
+            for (int i = 0; i < 4; ++i) dlo[R][i] = dg[R][i] + after + later;
             later += total;
         }
+        own_store(dla, t0, L, H, h, D, w, l, dlo);
     }
     __syncthreads();
     if (tid < L) {
