@@ -74,6 +74,25 @@ __device__ __forceinline__ void mma16(f32x4_t& acc, const float* a, const float*
     acc = mfma4(x[2], y[2], acc);
     acc = mfma4(x[3], y[3], acc);
 }
+// the same with the B operand's four k values in registers
+__device__ __forceinline__ void mma16b(f32x4_t& acc, const float* a, const f32x4_t& y) {
+    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(a);
+    acc = mfma4(x[0], y[0], acc);
+    acc = mfma4(x[1], y[1], acc);
+    acc = mfma4(x[2], y[2], acc);
+    acc = mfma4(x[3], y[3], acc);
+}
+// Transpose of a 16 x 16 fp32 tile held in accumulator layout (lane n + 16 G:
+// rows 4 G + i of column n) into the same layout of its transpose, on the
+// matrix cores (a product with the identity: exact up to NaN/infinity
+// spreading, as above)
+__device__ __forceinline__ f32x4_t tr16(const f32x4_t& x, int l) {
+    const int G = l >> 4, n = l & 15;
+    f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a = mfma4(x[t], 4 * G + t == n ? 1.f : 0.f, a);
+    return a;
+}
 // e^x for x formed as a difference of cumulative gates (natural log units): the
 // sums of 16-bit gates are exact in fp32, so is their difference, and the one
 // rounding left is that of x * log2 e
@@ -245,15 +264,15 @@ struct BwdSmem {
     static constexpr int RS = D + 4;          // [rows][D] matrices
     static constexpr int RX = 2 * D + 4;      // dB = [dB_k | dB_v]
     static constexpr int SQS = 68;            // [64][64] matrices
-    // phase 0: h then dh' [D][RS] at 0, dV then V [64][RS], dO [64][RS];
+    // phase 0: dV then V [64][RS] at 0, dO [64][RS] (h and dh' stay in registers);
     // later: T^T (stride SQS), -W, -U [64][RS] at 0, dB [64][RX], P_kk then dP_kk [64][SQS]
-    static constexpr int R_VV = D * RS, R_DO = R_VV + 64 * RS;
+    static constexpr int R_VV = 0, R_DO = R_VV + 64 * RS;
     static constexpr int R_DB = 64 * RS, R_PK = R_DB + 64 * RX;
     static constexpr int PH0_END = R_DO + 64 * RS, LATER_END = R_PK + 64 * SQS;
     static constexpr int R_DPQ = PH0_END > LATER_END ? PH0_END : LATER_END;  // dA_qk, kept to the end
     static constexpr int R_SMALL = R_DPQ + 64 * SQS;
-    // small: beta [64], dbeta partials [NW][64] and [4][64], dgamma halves [2][D]
-    static constexpr int FLOATS = R_SMALL + 64 + NW * 64 + 4 * 64 + 2 * D;
+    // small: beta [64], dbeta partials [NW][64] and [4][64]
+    static constexpr int FLOATS = R_SMALL + 64 + NW * 64 + 4 * 64;
     static constexpr int BYTES = FLOATS * 4;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     static_assert(64 * SQS <= R_DB, "T^T below dB");
@@ -270,7 +289,6 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
     using SM = BwdSmem<D>;
     constexpr int NW = SM::NW, NTH = 64 * NW, NS = D / 32, RS = SM::RS, RX = SM::RX, SQS = SM::SQS;
     extern __shared__ __align__(16) float sm[];
-    float* HB = sm;                    // h, then dh' ([key channel][value column])
     float* VV = sm + SM::R_VV;         // dV, then V
     float* DO = sm + SM::R_DO;         // dO
     float* TT = sm;                    // T^T (stride SQS), then -W, then -U (stride RS)
@@ -280,7 +298,6 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
     float* bet = sm + SM::R_SMALL;     // [64]
     float* dbp = bet + 64;             // [NW][64] dbeta: K+ dB_k + v dB_v, per wave
     float* dap = dbp + NW * 64;        // [4][64] dbeta: dA_kk P_kk, per column block
-    float* dgp = dap + 4 * 64;         // [2][D] dgamma halves
 
     const int lc = blockIdx.x / H, h = blockIdx.x - lc * H;  // slot g0 + lc, workspace slot lc
     ChunkLoc loc;
@@ -301,19 +318,23 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
 
     if (tid < 64) bet[tid] = tid < L ? ld_in(beta, (int64_t)(t0 + tid) * H + h) : 0.f;
 
-    // ---- 0a. h, dV, dO to LDS; dQ+ = dO h^T and dW = -dV h^T (own tiles).
+    // ---- 0a. dV, dO to LDS; dQ+ = dO h^T and dW = -dV h^T (own tiles), with
+    // h^T of this wave's key rows in registers: the recursion stores h (and dh')
+    // as [dv/16 value tiles][dk/32 key slices][64 lanes][8], lane n + 16 g
+    // holding key rows 32 s + 16 (jj >> 2) + 4 g + (jj & 3) of value column
+    // 16 ct + n; the half jj >> 2 = w & 1 of slice s = w >> 1 is the 16 x 16
+    // tile (key rows 16 w .., value columns 16 ct ..) in accumulator layout,
+    // whose transpose is the B operand of a product over value columns.
     // Every stage issues all of its global loads before it stores any of them, and
     // the next stage's loads are issued before this stage's products.
-    constexpr int NHQ = D * D / 8 / NTH, NVQ = 64 * D / 8 / NTH, NOQ = 64 * D / 4 / NTH;
-    const int g = l >> 4, s0 = w % NS;  // a thread's fragment lane group and 32-row slice of h
-    auto h_row = [&](int jj) { return 32 * s0 + frag_row(g, jj); };
-    auto h_col = [&](int m) { return 16 * (((tid + NTH * m) >> 6) / NS) + (l & 15); };
-    f32x4_t xh[NHQ][2], xv[NVQ][2], xo[NOQ];
+    constexpr int NVQ = 64 * D / 8 / NTH, NOQ = 64 * D / 4 / NTH, NT = D / 16;
+    const int g = l >> 4;
+    auto hfrag = [&](const float* base, int ct) {
+        return *reinterpret_cast<const f32x4_t*>(base + ((int64_t)(ct * NS + (w >> 1)) * 64 + l) * 8 + 4 * (w & 1));
+    };
+    f32x4_t hT[NT], xv[NVQ][2], xo[NOQ];
 #pragma unroll
-    for (int m = 0; m < NHQ; ++m) {
-        xh[m][0] = *reinterpret_cast<const f32x4_t*>(hF + (tid + NTH * m) * 8);
-        xh[m][1] = *reinterpret_cast<const f32x4_t*>(hF + (tid + NTH * m) * 8 + 4);
-    }
+    for (int ct = 0; ct < NT; ++ct) hT[ct] = hfrag(hF, ct);
 #pragma unroll
     for (int m = 0; m < NVQ; ++m) {
         xv[m][0] = *reinterpret_cast<const f32x4_t*>(dVB + (tid + NTH * m) * 8);
@@ -324,11 +345,6 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
         const int e = tid + NTH * m, r = e / (D / 4), c4 = 4 * (e - r * (D / 4));
         xo[m] = r < L ? *reinterpret_cast<const f32x4_t*>(d_o + rowoff(r) + c4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    // (the fragment blocks of thread tid + NTH m all share the slice s0: NTH / 64 = 2 NS)
-#pragma unroll
-    for (int m = 0; m < NHQ; ++m)
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) HB[h_row(jj) * RS + h_col(m)] = jj < 4 ? xh[m][0][jj] : xh[m][1][jj - 4];
     auto v_put = [&](float* dst, const f32x4_t (&x)[NVQ][2]) {
 #pragma unroll
         for (int m = 0; m < NVQ; ++m) {
@@ -344,13 +360,13 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
         const int e = tid + NTH * m, r = e / (D / 4), c4 = 4 * (e - r * (D / 4));
         *reinterpret_cast<f32x4_t*>(DO + r * RS + c4) = xo[m];
     }
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) hT[ct] = tr16(hT[ct], l);  // lane n + 16 G: key row c, values 16 ct + 4 G ..
     __syncthreads();
     // dh' and V in flight during the products
+    f32x4_t dhT[NT];
 #pragma unroll
-    for (int m = 0; m < NHQ; ++m) {
-        xh[m][0] = *reinterpret_cast<const f32x4_t*>(dhB + (tid + NTH * m) * 8);
-        xh[m][1] = *reinterpret_cast<const f32x4_t*>(dhB + (tid + NTH * m) * 8 + 4);
-    }
+    for (int ct = 0; ct < NT; ++ct) dhT[ct] = hfrag(dhB, ct);
 #pragma unroll
     for (int m = 0; m < NVQ; ++m) {
         xv[m][0] = *reinterpret_cast<const f32x4_t*>(vF + (tid + NTH * m) * 8);
@@ -361,13 +377,12 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
         f32x4_t aq[4], aw[4];
 #pragma unroll
         for (int R = 0; R < 4; ++R) aq[R] = aw[R] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-        for (int s16 = 0; s16 < D / 16; ++s16) {
-            const float* hb = HB + c * RS + 16 * s16 + 4 * G;
+#pragma unroll
+        for (int s16 = 0; s16 < NT; ++s16) {
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
-                mma16(aq[R], DO + (16 * R + n) * RS + 16 * s16 + 4 * G, hb);
-                mma16(aw[R], VV + (16 * R + n) * RS + 16 * s16 + 4 * G, hb);
+                mma16b(aq[R], DO + (16 * R + n) * RS + 16 * s16 + 4 * G, hT[s16]);
+                mma16b(aw[R], VV + (16 * R + n) * RS + 16 * s16 + 4 * G, hT[s16]);
             }
         }
 #pragma unroll
@@ -380,27 +395,21 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
             }
         }
     }
-    __syncthreads();
-    // ---- 0b. dh' over h (dgamma = rowsum(h * dh') on the way), V over dV
+    // ---- 0b. dgamma = rowsum(h * dh') over the value columns of this lane's
+    // key row (the four lane groups hold a quarter each), then V over dV
+    float dgam;
     {
-        float pg[8];
+        float pg = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) pg[jj] = 0.f;
+        for (int ct = 0; ct < NT; ++ct) {
+            dhT[ct] = tr16(dhT[ct], l);
 #pragma unroll
-        for (int m = 0; m < NHQ; ++m)
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const float x = jj < 4 ? xh[m][0][jj] : xh[m][1][jj - 4];
-                float* p = HB + h_row(jj) * RS + h_col(m);
-                pg[jj] += *p * x;
-                *p = x;
-            }
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const float t = sum16(pg[jj]);
-            if (n == 0) dgp[(w / NS) * D + h_row(jj)] = t;
+            for (int i = 0; i < 4; ++i) pg += hT[ct][i] * dhT[ct][i];
         }
+        pg += __shfl_xor(pg, 16);
+        dgam = pg + __shfl_xor(pg, 32);
     }
+    __syncthreads();
     v_put(VV, xv);
     __syncthreads();
     // P_kk in flight during the products
@@ -413,11 +422,10 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
         f32x4_t ak[4];
 #pragma unroll
         for (int R = 0; R < 4; ++R) ak[R] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-        for (int s16 = 0; s16 < D / 16; ++s16) {
-            const float* hb = HB + c * RS + 16 * s16 + 4 * G;
 #pragma unroll
-            for (int R = 0; R < 4; ++R) mma16(ak[R], VV + (16 * R + n) * RS + 16 * s16 + 4 * G, hb);
+        for (int s16 = 0; s16 < NT; ++s16) {
+#pragma unroll
+            for (int R = 0; R < 4; ++R) mma16b(ak[R], VV + (16 * R + n) * RS + 16 * s16 + 4 * G, dhT[s16]);
         }
 #pragma unroll
         for (int R = 0; R < 4; ++R) *reinterpret_cast<f32x4_t*>(SK + ((w * 4 + R) * 64 + l) * 4) = ak[R];
@@ -626,6 +634,13 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
     }
     __syncthreads();
 
+    // dQ+ and dK- (own tiles, from phase 0) come back from the scratch during phase 4
+    f32x4_t dqp4[4], dkm4[4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+        dqp4[R] = *reinterpret_cast<const f32x4_t*>(SQ + ((w * 4 + R) * 64 + l) * 4);
+        dkm4[R] = *reinterpret_cast<const f32x4_t*>(SK + ((w * 4 + R) * 64 + l) * 4);
+    }
     // ---- 4. adjoints of the gated products. Lq, Lk: row r as the left factor of
     // A_qk / A_kk; Rr: row i as their right factor (both take the key there)
     float Lq[4][4], Lk[4][4], Rr[4][4];
@@ -740,13 +755,12 @@ __global__ __launch_bounds__(4 * D) void bwd_local_kernel(const TIn* q, const TI
 
     // ---- 5. gated scalings, the last row's terms, the reverse cumulative sum
     const float gl = __shfl(g2[3][3], 48 + n);  // cumulative gate of the chunk's last row
-    const float dgam = dgp[c] + dgp[D + c];
     float dg[4][4], lsum = 0.f;
     f32x4_t dqo[4], dko[4];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
-        const f32x4_t dqp = *reinterpret_cast<const f32x4_t*>(SQ + ((w * 4 + R) * 64 + l) * 4);
-        const f32x4_t dkm = *reinterpret_cast<const f32x4_t*>(SK + ((w * 4 + R) * 64 + l) * 4);
+        const f32x4_t dqp = dqp4[R];
+        const f32x4_t dkm = dkm4[R];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = own_row(R, i);
