@@ -82,16 +82,15 @@ struct PrepSmem {
     static constexpr int CONST = NCONST * D * 4;
     static constexpr int BETA = 64 * 4 + 16;  // beta per row, then one overflow flag per wave
     // beta V: with 16-bit operands fp32 accumulator tiles (exact, the WY solve
-    // carries it as two fp16 terms) in R1 once Kt is dead, and the -W staging
-    // goes to the beta K+ tile region R3 after the barrier that ends the solve;
-    // with fp32 operands beta V (transposed rows) gets a region of its own and
-    // the -W staging takes R1
+    // carries it as two fp16 terms) in R1 once Kt is dead, and -W goes from the
+    // solve's registers straight to the workspace; with fp32 operands beta V
+    // (transposed rows) gets a region of its own and the -W staging takes R1
     static constexpr int RBV = MT ? 64 * D * 4 : D * BK_STRIDE * (int)sizeof(E);
     static constexpr bool BV_IN_R1 = MT;
     static constexpr int R5 = BV_IN_R1 ? 0 : RBV;
     static constexpr int BYTES = R1 + R4 + R3 + CONST + BETA + R5;
     static constexpr int BV_AT = BV_IN_R1 ? 0 : R1 + R4 + R3 + CONST + BETA;
-    static constexpr int WS_AT = MT ? R1 + R4 : 0;
+    static constexpr int WS_AT = 0;  // -W staging (fp32 operands only)
     static_assert(64 * D * 4 <= R1, "slow-path scans must fit in R1");
     static_assert(!F32 || 64 * D * 4 <= R4, "slow-path low parts must fit in R4");
     static_assert(!MT || RBV <= R1, "beta V tiles must fit in R1");
@@ -138,7 +137,7 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
     AE* Kt_s = reinterpret_cast<AE*>(smem);                     // [planes][64][KTS] keys 2^(G_aJ - G)
     E* Bv_t = reinterpret_cast<E*>(smem + SM::BV_AT);           // beta V transposed ([D][BKS]; fp32 operands)
     float* Bv_f = reinterpret_cast<float*>(smem + SM::BV_AT);   // beta V fp32 tiles (16-bit operands)
-    E* Ws_s = reinterpret_cast<E*>(smem + SM::WS_AT);           // [64][NS][4][8] -W staging (after the solve)
+    E* Ws_s = reinterpret_cast<E*>(smem + SM::WS_AT);           // [64][NS][4][8] -W staging (fp32 operands)
     float* xl_slow = reinterpret_cast<float*>(smem);            // [64][D] slow path: local scans
     float* xl_slow_lo = reinterpret_cast<float*>(smem + SM::R1); // [64][D] their low parts (fp32 operands)
     char* r4 = smem + SM::R1;
@@ -823,31 +822,81 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
                     P::mma(X[tt][I], at, frag_from_acc<F32>(Y, zero));
             }
         }
-        // with 16-bit operands the -W staging reuses the beta K+ tiles' region
-        if constexpr (SM::MT) __syncthreads();
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            const int ct = (w & 1) * TPW + tt;
+        if constexpr (SM::MT) {
             if (isW) {
-                // -W into LDS in the split k order over key channels
+                // -W straight to the workspace, 16 bytes per lane. A pair of row
+                // blocks (2q, 2q + 1) of column tile ct, rounded to fp16, is the A
+                // operand of its transpose (rows in the split k order); a product
+                // with a 0/-1 selector takes each 16-row half, leaving lane n + 16 G
+                // with row 16 I + n at channels 16 ct + 4 G .. + 3 (exact: fp16
+                // values times -1), and the wave's even and odd column tiles of one
+                // slice fill the split-order positions 8 G .. 8 G + 7 of that row.
+                E* wn_out = ws.wn + chh * 64 * D;
+                Frag wsel[2];
 #pragma unroll
-                for (int I = 0; I < 4; ++I)
+                for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int rr = 16 * I + 4 * g + i;
-                        const int s = ct >> 1, gg = n >> 2, jj = 4 * (ct & 1) + (n & 3);
-                        Ws_s[(rr * NS + s) * 32 + gg * 8 + jj] = P::from_f(-X[tt][I][i]);
+                    for (int j = 0; j < 8; ++j)
+                        wsel[hh].v[j] = ((j >> 2) == hh && 4 * g + (j & 3) == n) ? (_Float16)-1.f : (_Float16)0.f;
+#pragma unroll
+                for (int sp = 0; sp < TPW / 2; ++sp) {
+                    const int s = (w & 1) * (TPW / 2) + sp;
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const float xe[8] = {X[2 * sp][2 * q][0], X[2 * sp][2 * q][1], X[2 * sp][2 * q][2],
+                                             X[2 * sp][2 * q][3], X[2 * sp][2 * q + 1][0], X[2 * sp][2 * q + 1][1],
+                                             X[2 * sp][2 * q + 1][2], X[2 * sp][2 * q + 1][3]};
+                        const float xo[8] = {X[2 * sp + 1][2 * q][0], X[2 * sp + 1][2 * q][1],
+                                             X[2 * sp + 1][2 * q][2], X[2 * sp + 1][2 * q][3],
+                                             X[2 * sp + 1][2 * q + 1][0], X[2 * sp + 1][2 * q + 1][1],
+                                             X[2 * sp + 1][2 * q + 1][2], X[2 * sp + 1][2 * q + 1][3]};
+                        const Frag ae = P::make(xe), ao = P::make(xo);
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            f32x4_t ce = zero, co = zero;
+                            P::mma(ce, ae, wsel[hh]);
+                            P::mma(co, ao, wsel[hh]);
+                            const u32x4_t pk = {pack2h(ce[0], ce[1]), pack2h(ce[2], ce[3]), pack2h(co[0], co[1]),
+                                                pack2h(co[2], co[3])};
+                            *reinterpret_cast<u32x4_t*>(wn_out + (16 * (2 * q + hh) + n) * D + 32 * s + 8 * g) = pk;
+                        }
                     }
+                }
             } else {
                 // U in fp32 accumulator-tile order
 #pragma unroll
-                for (int I = 0; I < 4; ++I)
-                    *reinterpret_cast<f32x4_t*>(u_out + ((ct * 4 + I) * 64 + l) * 4) = X[tt][I];
+                for (int tt = 0; tt < TPW; ++tt) {
+                    const int ct = (w & 1) * TPW + tt;
+#pragma unroll
+                    for (int I = 0; I < 4; ++I)
+                        *reinterpret_cast<f32x4_t*>(u_out + ((ct * 4 + I) * 64 + l) * 4) = X[tt][I];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                const int ct = (w & 1) * TPW + tt;
+                if (isW) {
+                    // -W into LDS in the split k order over key channels
+#pragma unroll
+                    for (int I = 0; I < 4; ++I)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int rr = 16 * I + 4 * g + i;
+                            const int s = ct >> 1, gg = n >> 2, jj = 4 * (ct & 1) + (n & 3);
+                            Ws_s[(rr * NS + s) * 32 + gg * 8 + jj] = P::from_f(-X[tt][I][i]);
+                        }
+                } else {
+                    // U in fp32 accumulator-tile order
+#pragma unroll
+                    for (int I = 0; I < 4; ++I)
+                        *reinterpret_cast<f32x4_t*>(u_out + ((ct * 4 + I) * 64 + l) * 4) = X[tt][I];
+                }
             }
         }
     }
-    __syncthreads();
-    {
+    if constexpr (!SM::MT) {
+        __syncthreads();
         constexpr int VEC = 16 / sizeof(E);
         E* wn_out = ws.wn + chh * 64 * D;
         for (int idx = tid; idx < 64 * D / VEC; idx += 256)
