@@ -738,31 +738,8 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
             sb[s] = frag_from_acc<F32>(S[2 * s], S[2 * s + 1]);
             P::store(hp + (s * 64 + l) * 8, sb[s]);
         }
-        // V_new = U + (-W) S
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int I = 0; I < 4; ++I) P::mma(V[I], wf[I][s], sb[s]);
-        // the next chunk's -W while this chunk's key-value products run (the
-        // last chunk re-reads its own)
-        if (LOOK) load_w(c + 1 < nch ? c + 1 : c);
-        Frag vb[2];
-        Frag vl[PL::HP ? 2 : 1];  // HP: the low terms of V_new
-        E* vp = FUSED ? reinterpret_cast<E*>(hvbase + (c & 1) * PL::HVS) + D * 16
-                      : ws.vn + chh * 64 * D + (int64_t)ct * 2 * 64 * 8;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            if constexpr (PL::HP) {
-                const Frag2 x = split_from_acc(V[2 * s], V[2 * s + 1]);
-                vb[s] = x.hi;
-                vl[s] = x.lo;
-                P::store(vp + (2 * 64 + s * 64 + l) * 8, vl[s]);
-            } else {
-                vb[s] = frag_from_acc<F32>(V[2 * s], V[2 * s + 1]);
-            }
-            P::store(vp + (s * 64 + l) * 8, vb[s]);
-        }
-        // S <- Diag(gamma) S + K-^T V_new  (DPLR: + K-^T V + A-^T (-u))
+        // S <- Diag(gamma) S (+ K-^T V with DPLR) now that h_n is taken: off the
+        // V_new products' path
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             if constexpr (DPLR)
@@ -771,11 +748,36 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
             else
                 S[t] = gm[t] * S[t];
         }
-        if constexpr (PL::HP) {
+        // V_new = U + (-W) S, row tiles 0-1 first: their two-term split and the
+        // state products of their half run while tiles 2-3 are still in the matrix core
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+        for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int I = 2 * hv; I < 2 * hv + 2; ++I) P::mma(V[I], wf[I][s], sb[s]);
+        // the next chunk's -W while this chunk's key-value products run (the
+        // last chunk re-reads its own)
+        if (LOOK) load_w(c + 1 < nch ? c + 1 : c);
+        Frag vb[2];
+        Frag vl[PL::HP ? 2 : 1];  // HP: the low terms of V_new
+        E* vp = FUSED ? reinterpret_cast<E*>(hvbase + (c & 1) * PL::HVS) + D * 16
+                      : ws.vn + chh * 64 * D + (int64_t)ct * 2 * 64 * 8;
+        // S += K-^T V_new: with HP the low terms of both halves first, then the high
+        // terms (each tile accumulates lo 0, lo 1, hi 0, hi 1 in that order)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if constexpr (PL::HP) {
+                const Frag2 x = split_from_acc(V[2 * s], V[2 * s + 1]);
+                vb[s] = x.hi;
+                vl[s] = x.lo;
+                P::store(vp + (2 * 64 + s * 64 + l) * 8, vl[s]);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) P::mma(S[t], kf[t][s], vl[s]);
+            } else {
+                vb[s] = frag_from_acc<F32>(V[2 * s], V[2 * s + 1]);
+            }
+            P::store(vp + (s * 64 + l) * 8, vb[s]);
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s)
