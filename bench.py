@@ -519,6 +519,66 @@ def copy_bandwidth(hip, stream, mib: int = 1024, reps: int = 20):
     return 2 * 4 * n / (ms * 1e-3) / 1e9
 
 
+def machine_peaks(hip, stream):
+    """Achievable rates of this GPU, measured beside the datasheet peaks by the
+    probes in libkda_probe.so: a bf16 matrix-core loop (1,024 workgroups of four
+    waves, eight independent accumulators each, 16x16x32 products back to back)
+    and a streaming copy (16-byte nontemporal loads and stores over 2 GiB each
+    way). Both run on the launch stream between HIP events; the best of 5 calls
+    after 2 warm-ups is reported."""
+    import torch
+    path = os.path.join(ROOT, "gated_delta_rule_41_amd", "libkda_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.kda_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.kda_probe_mfma_bf16.restype = ctypes.c_int32
+    lib.kda_probe_mfma_bf16_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.kda_probe_mfma_bf16_flops.restype = ctypes.c_double
+    lib.kda_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    lib.kda_probe_copy.restype = ctypes.c_int32
+
+    def best(call, reps=5, warm=2):
+        for _ in range(warm):
+            call()
+        torch.cuda.synchronize()
+        ev = Events(hip, 2 * reps)
+        for r in range(reps):
+            ev.record(2 * r, stream)
+            call()
+            ev.record(2 * r + 1, stream)
+        torch.cuda.synchronize()
+        t = min(ev.ms(2 * r, 2 * r + 1) for r in range(reps))
+        ev.close()
+        return t
+
+    n_wg, iters = 1024, 20000
+    sink = torch.empty(n_wg * 4, dtype=torch.float32, device="cuda:0")
+
+    def mfma():
+        if lib.kda_probe_mfma_bf16(n_wg, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("kda_probe_mfma_bf16 failed")
+    ms = best(mfma)
+    tflops = lib.kda_probe_mfma_bf16_flops(n_wg, iters) / (ms * 1e-3) / 1e12
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+
+    def copy():
+        if lib.kda_probe_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes,
+                              ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("kda_probe_copy failed")
+    cms = best(copy)
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    probe_gbps = 2 * nbytes / (cms * 1e-3) / 1e9
+    torch_gbps = copy_bandwidth(hip, stream)
+    copy_gbps = max(probe_gbps, torch_gbps)
+    return {"bf16_mfma_tflops": round(tflops, 1), "bf16_mfma_frac_of_datasheet": round(tflops * 1e12 / PEAK_BF16, 4),
+            "copy_GBps": round(copy_gbps, 1), "copy_frac_of_datasheet": round(copy_gbps * 1e9 / PEAK_HBM, 4),
+            "copy_probe_GBps": round(probe_gbps, 1), "torch_copy_GBps": round(torch_gbps, 1),
+            "probes": "bf16 16x16x32 MFMA loop, 1024 workgroups x 4 waves x 8 accumulators; copy = the faster of "
+                      "a nontemporal 16-byte copy of 2 GiB and torch's y = x * 1 over 1 GiB (bytes read + written)"}
+
+
 def cpu_baseline(host, T, H, dk, rec_pos, threads):
     """The oracle (fp64 token recurrence, OpenMP over (head, column block)) on
     the host cores, on the headline workload's own inputs copied to the host:
@@ -737,6 +797,8 @@ def main(argv=None):
     ap.add_argument("--workloads", default="prefill-4k,varlen-16",
                     help="prefill workloads timed beside the headline (same protocol)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-machine-peaks", action="store_true",
+                    help="skip the measured MFMA and copy rates (libkda_probe.so)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dplr", action="store_true", help="skip the general-DPLR comparison")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward")
@@ -774,6 +836,7 @@ def main(argv=None):
         args.headline_only = True
     if args.headline_only:
         args.no_cpu_baseline = args.no_decode = args.no_dplr = args.no_bwd = args.no_layer = True
+        args.no_machine_peaks = True
         args.workloads = ""
     t_start = time.perf_counter()
     if args.profile_set == "prefill-4k":
@@ -805,6 +868,12 @@ def main(argv=None):
         "prefill": rep,
         "roofline": roof,
     }
+    # the achievable peaks of this GPU, beside the datasheet ones
+    if not args.no_machine_peaks:
+        mp = machine_peaks(hip, stream)
+        out["machine_peaks"] = mp
+        rep["mfma_frac_of_measured"] = round(rep["tflops"] / mp["bf16_mfma_tflops"], 4)
+        roof["frac_of_measured_copy"] = round(roof["achieved"] / mp["copy_GBps"], 4)
     # what the oracle needs later, on the host; the GPU copies are freed
     rec_pos = None
     host = None

@@ -19,6 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
+# the benchmark's machine probes (achievable MFMA and copy rates), a library of their own
+PROBE_SRC = os.path.join(PKG, "probe", "kda_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libkda_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -41,6 +44,9 @@ FILE_FLAGS = {
     # converted to fp16 operands every chunk, and AGPR<->VGPR moves would sit on
     # the sequential chain
     "kda_recur.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the MFMA probe's accumulators likewise (as AGPRs they are shuffled between
+    # loop iterations with moves that sit between the products)
+    "kda_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
@@ -76,5 +82,21 @@ def build(extra=(), jobs: int = 8, verbose: bool = False, out: str = LIB, build_
     return out
 
 
+def build_probe(verbose: bool = False) -> str:
+    """Compile and link the machine probes into libkda_probe.so. Always recompiles."""
+    os.makedirs(BUILD, exist_ok=True)
+    obj = _compile(PROBE_SRC, ())
+    tmp = PROBE_LIB + ".tmp"
+    res = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj],
+                         stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_probe(verbose=True)
