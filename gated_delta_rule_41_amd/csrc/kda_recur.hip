@@ -585,24 +585,40 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
             const E* usl = reinterpret_cast<const E*>(slot + 2 * PL::FB);
             const float* gsl = reinterpret_cast<const float*>(slot + 2 * PL::FB + PL::UB);
             const int64_t chh = (int64_t)(co + (ADDP ? nch - 1 - c : c)) * H + h;
-            if (ADDP && c + 1 < nch) load_p(c + 1, pnx);
-            // the whole state as B fragments; this wave's share of h_n out
-            Frag sb[NS];
-#pragma unroll
-            for (int s = 0; s < NS; ++s) sb[s] = frag_from_acc<F32>(XS[(2 * s) * 64 + l], XS[(2 * s + 1) * 64 + l]);
-            E* hp = ws.h + chh * D * D + (int64_t)ct * NS * 64 * 8;
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-                if (s % NCW == q) P::store(hp + (s * 64 + l) * 8, sb[s]);
-            // V_new = U + (-W) S on row tile q
-            f32x4_t V = *reinterpret_cast<const f32x4_t*>(usl + (q * 64 + l) * 4);
+            // (unconditional: the last chunk reloads its own term, unused)
+            if (ADDP) load_p(c + 1 < nch ? c + 1 : c, pnx);
+            // every LDS operand of the V_new products first (-W of row tile q, the
+            // whole state as B fragments), held here by the fence below so that
+            // their latencies overlap instead of each product waiting for its own
+            Frag wfr[NS];
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const int gr = ((16 * q + n) * NS + s) * 4 + g;
-                P::mma(V, ADDP ? w_transposed(wsl, s) : P::load(reinterpret_cast<const E*>(wsl + gr * 8 * sizeof(E))),
-                       sb[s]);
+                wfr[s] = ADDP ? w_transposed(wsl, s) : P::load(reinterpret_cast<const E*>(wsl + gr * 8 * sizeof(E)));
             }
+            Frag sb[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) sb[s] = frag_from_acc<F32>(XS[(2 * s) * 64 + l], XS[(2 * s + 1) * 64 + l]);
+            // V_new = U + (-W) S on row tile q, starting from U
+            f32x4_t V = *reinterpret_cast<const f32x4_t*>(usl + (q * 64 + l) * 4);
+            asm volatile("" ::: "memory");
+            // h_n out: each wave stores its own state tiles from its registers
+            // (tile t is half t & 1 of the B fragment of slice t >> 1). Every wave
+            // issues the same global operations in every chunk, with no branch, so
+            // the compiler's count of outstanding ones stays exact and the wait
+            // for the added term (ADDP) does not also wait for this chunk's stores
+            E* hp = ws.h + chh * D * D + (int64_t)ct * NS * 64 * 8;
+#pragma unroll
+            for (int tt = 0; tt < TH; ++tt) {
+                const int t = TH * q + tt;
+                *reinterpret_cast<f32x4_t*>(hp + ((t >> 1) * 64 + l) * 8 + (t & 1) * 4) = S[tt];
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) P::mma(V, wfr[s], sb[s]);
             XV[q * 64 + l] = V;
+            // V_new out: this wave's row tile q, stored as h_n's tiles above
+            E* vp = ws.vn + chh * 64 * D + (int64_t)ct * 2 * 64 * 8;
+            *reinterpret_cast<f32x4_t*>(vp + ((q >> 1) * 64 + l) * 8 + (q & 1) * 4) = V;
             // this wave's K-^T fragments and gamma while the other tiles land
             Frag kf[TH][2];
 #pragma unroll
@@ -620,9 +636,6 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
             Frag vb[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) vb[s] = frag_from_acc<F32>(XV[(2 * s) * 64 + l], XV[(2 * s + 1) * 64 + l]);
-            E* vp = ws.vn + chh * 64 * D + (int64_t)ct * 2 * 64 * 8;
-            if (q == 0) P::store(vp + l * 8, vb[0]);  // (no index by q: it would put vb in scratch)
-            if (q == 1) P::store(vp + (64 + l) * 8, vb[1]);
             // S <- Diag(gamma) S (+ the added term) + K-^T V_new on this wave's row tiles
 #pragma unroll
             for (int tt = 0; tt < TH; ++tt) {
