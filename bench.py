@@ -64,13 +64,18 @@ KERNEL_SYMBOL = {"prep": "prep_kernel", "recur": "recur_kernel", "decode": "deco
                  "bwd_fwd_prep": "prep_kernel", "bwd_fwd_recur": "recur_kernel",
                  "bwd_prep": "bwd_prep_kernel", "bwd_recur": "recur_kernel", "bwd_local": "bwd_local_kernel",
                  "layer_prologue": "layer_prologue_kernel", "layer_epilogue": "layer_epilogue_kernel",
-                 "layer_prep": "prep_kernel"}
-KERNEL_SOURCE = {"prep": "kda_prep.hip", "recur": "kda_recur.hip", "decode": "kda_decode.hip",
-                 "dplr_prep": "kda_dplr_prep.hip", "dplr_recur": "kda_recur.hip",
-                 "bwd_fwd_prep": "kda_prep.hip", "bwd_fwd_recur": "kda_recur.hip",
-                 "bwd_prep": "kda_bwd.hip", "bwd_recur": "kda_recur.hip", "bwd_local": "kda_bwd.hip",
-                 "layer_prologue": ("kda_layer.hip", "kda_layer_util.h"), "layer_epilogue": "kda_layer.hip",
-                 "layer_prep": ("kda_prep.hip", "kda_layer_util.h")}
+                 "layer_prep": "prep_kernel", "layer_recur": "recur_kernel"}
+# each kernel's source file and the library headers it includes (with kda_common.h, which all do)
+_PREP = ("kda_prep.hip", "kda_prep_util.h", "kda_layer_util.h")
+_RECUR = ("kda_recur.hip", "kda_prep_util.h", "kda_layer_util.h")
+KERNEL_SOURCE = {"prep": _PREP, "recur": _RECUR, "decode": "kda_decode.hip",
+                 "dplr_prep": ("kda_dplr_prep.hip", "kda_prep_util.h"), "dplr_recur": _RECUR,
+                 "bwd_fwd_prep": _PREP, "bwd_fwd_recur": _RECUR,
+                 "bwd_prep": ("kda_bwd.hip", "kda_prep_util.h"), "bwd_recur": _RECUR,
+                 "bwd_local": ("kda_bwd.hip", "kda_prep_util.h"),
+                 "layer_prologue": ("kda_layer.hip", "kda_layer_util.h"),
+                 "layer_epilogue": ("kda_layer.hip", "kda_layer_util.h"),
+                 "layer_prep": _PREP, "layer_recur": _RECUR}
 
 
 def kernel_key(short_name: str):
@@ -79,13 +84,16 @@ def kernel_key(short_name: str):
     last two are fp32 factors (the backward's forward recompute) and the fused
     layer prologue; the state
     recursion's are <D, fp32 factors, fused output, fp32 output, DPLR chain,
-    added per-chunk term (the backward's state-gradient recursion)>."""
+    added per-chunk term (the backward's state-gradient recursion), fused layer
+    epilogue>."""
     if "<" not in short_name:
         return None
     sym, args = short_name.split("<", 1)
     args = [x.strip() for x in args.rstrip(">").split(",")]
     flag = lambda i: len(args) > i and args[i] == "true"
     if sym == "recur_kernel":
+        if flag(6):
+            return "layer_recur"
         if flag(5):
             return "bwd_recur"
         if flag(4):
@@ -428,6 +436,27 @@ def time_layer(kda, lc, steps, warmup, hip, stream):
         torch.cuda.synchronize()
         out["fused_layer"] = ev.ms(0, 1) / steps
         ev.close()
+        # the whole layer in one call: the epilogue inside the recursion's output stage too
+        wws = torch.empty(kda.layer_fwd_workspace_size(N, T, H, d), dtype=torch.uint8, device=dev)
+        whole_args = (*(ptr(t) for t in (lc.xq, lc.xk, lc.xv, lc.xa, lc.xb, lc.xg, lc.wq, lc.wk, lc.wv, lc.A_log,
+                                         lc.dt_bias, lc.rms_w, lc.initial_state, lc.cu_seqlens)),
+                      N, T, H, d, ptr(y), ptr(fs), ptr(wws), wws.numel(), P(stream))
+
+        def whole_step():
+            if lib.kda_layer_fwd(*whole_args) != 0:
+                raise RuntimeError("kda_layer_fwd failed")
+        for _ in range(warmup):
+            whole_step()
+        torch.cuda.synchronize()
+        ev = Events(hip, 2)
+        ev.record(0, stream)
+        for _ in range(steps):
+            whole_step()
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        out["one_call_layer"] = ev.ms(0, 1) / steps
+        ev.close()
+        del wws
     return out
 
 
@@ -984,7 +1013,9 @@ def side_legs(args, kda, ki, hip, stream, flush, dev, out, t_start, headline_hos
             "ms": {k_: round(v_, 5) for k_, v_ in lt.items()},
             "tokens_per_s": round(case.T_total / (lt["layer"] * 1e-3), 1),
             "fused_tokens_per_s": round(case.T_total / (lt["fused_layer"] * 1e-3), 1),
+            "one_call_tokens_per_s": round(case.T_total / (lt["one_call_layer"] * 1e-3), 1),
             "fused_prep_hbm_bytes_per_launch": traffic_from_profiles("layer_prep"),
+            "one_call_recur_hbm_bytes_per_launch": traffic_from_profiles("layer_recur"),
             "prologue_roofline": {"bound": "hbm", "achieved": round(pro_b / (lt["prologue"] * 1e-3) / 1e9, 1),
                                   "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                                   "frac": round(pro_b / (lt["prologue"] * 1e-3) / PEAK_HBM, 4),

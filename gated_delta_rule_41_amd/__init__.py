@@ -95,6 +95,10 @@ def _load():
     lib.kda_layer_chunk_fwd_workspace_size.argtypes = [I32, I64, I32, I32, ctypes.POINTER(SZ)]
     lib.kda_layer_chunk_fwd.restype = ctypes.c_int
     lib.kda_layer_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I32, I64, I32, I32, P, P, P, SZ, P]
+    lib.kda_layer_fwd_workspace_size.restype = ctypes.c_int
+    lib.kda_layer_fwd_workspace_size.argtypes = [I32, I64, I32, I32, ctypes.POINTER(SZ)]
+    lib.kda_layer_fwd.restype = ctypes.c_int
+    lib.kda_layer_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, I32, I64, I32, I32, P, P, P, SZ, P]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
@@ -448,6 +452,70 @@ def layer_chunk_fwd(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, xa: to
     if st != 0:
         raise KDAError(st, "kda_layer_chunk_fwd")
     return o, final_state
+
+
+def layer_fwd_workspace_size(N: int, T: int, H: int, d: int) -> int:
+    """Bytes of workspace ``layer_fwd`` needs (see ``kda_layer_fwd_workspace_size``)."""
+    sz = ctypes.c_size_t(0)
+    st = _load().kda_layer_fwd_workspace_size(N, T, H, d, ctypes.byref(sz))
+    if st != 0:
+        raise KDAError(st, "kda_layer_fwd_workspace_size")
+    return int(sz.value)
+
+
+def layer_fwd(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, xa: torch.Tensor, xb: torch.Tensor,
+              xg: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor, A_log: torch.Tensor,
+              dt_bias: torch.Tensor, rms_w: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The whole layer between the projections (see ``kda_layer_fwd``): bf16
+    pre-activations as ``layer_chunk_fwd`` takes them, the output gate's
+    pre-activation xg [T, H, d] bf16 and rms_w [d] fp32. Returns
+    (y [T, H, d] bf16, final_state [N, H, d, d] fp32)."""
+    lib = _load()
+    dev = xq.device
+    if xq.dim() != 3:
+        raise ValueError("xq must be [T, H, d]")
+    T, H, d = xq.shape
+    N = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    items = [("xq", xq, (T, H, d)), ("xk", xk, (T, H, d)), ("xv", xv, (T, H, d)), ("xa", xa, (T, H, d)),
+             ("xb", xb, (T, H)), ("xg", xg, (T, H, d)), ("wq", wq, (H, d, 4)), ("wk", wk, (H, d, 4)),
+             ("wv", wv, (H, d, 4)), ("A_log", A_log, (H,)), ("dt_bias", dt_bias, (H, d)), ("rms_w", rms_w, (d,))]
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 >= 2 offsets")
+        items.append(("cu_seqlens", cu_seqlens, None))
+    if initial_state is not None:
+        items.append(("initial_state", initial_state, (N, H, d, d)))
+    if y is not None:
+        items.append(("y", y, (T, H, d)))
+    if final_state is not None:
+        items.append(("final_state", final_state, (N, H, d, d)))
+    if workspace is not None:
+        items.append(("workspace", workspace, None))
+    _check(items, dev)
+    for name, t in (("xq", xq), ("xk", xk), ("xv", xv), ("xa", xa), ("xb", xb), ("xg", xg), ("y", y)):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16 (the fused path is bf16 only)")
+    for name, t in (("wq", wq), ("wk", wk), ("wv", wv), ("A_log", A_log), ("dt_bias", dt_bias), ("rms_w", rms_w),
+                    ("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if y is None:
+        y = torch.empty(T, H, d, dtype=torch.bfloat16, device=dev)
+    if final_state is None:
+        final_state = torch.empty(N, H, d, d, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(layer_fwd_workspace_size(max(N, 1), T, H, d), 1), dtype=torch.uint8,
+                                device=dev)
+    st = lib.kda_layer_fwd(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(xa), _ptr(xb), _ptr(xg), _ptr(wq), _ptr(wk),
+                           _ptr(wv), _ptr(A_log), _ptr(dt_bias), _ptr(rms_w), _ptr(initial_state),
+                           _ptr(cu_seqlens), N, T, H, d, _ptr(y), _ptr(final_state), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_layer_fwd")
+    return y, final_state
 
 
 def layer_epilogue(o: torch.Tensor, xg: torch.Tensor, rms_w: torch.Tensor) -> torch.Tensor:

@@ -640,15 +640,43 @@ kda_status kda_layer_chunk_fwd_workspace_size(int32_t N, int64_t T_total, int32_
     return KDA_OK;
 }
 
-kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
-                               const float* wq, const float* wk, const float* wv, const float* A_log,
-                               const float* dt_bias, const float* initial_state, const int32_t* cu_seqlens,
-                               int32_t N, int64_t T_total, int32_t H, int32_t d, float* o, float* final_state,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+// The whole layer's epilogue (kda_layer_fwd): y = RMSNorm(o) rms_w sigmoid(xg).
+struct LayerEpi {
+    const void* xg;
+    const float* rms_w;
+    void* y;
+};
+
+// The epilogue joins the recursion's output stage when the slab workgroups of
+// every (sequence, head) share an XCD (N H a multiple of 8, so that their ids
+// are congruent mod 8) and every workgroup of the launch fits on the GPU at once
+// (one per CU); otherwise o goes to the workspace and the epilogue kernel follows.
+static bool layer_epi_fused(int N, int H, int d) {
+    if (((int64_t)N * H) % 8 != 0) return false;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return false;
+    return (int64_t)N * H * (d / 16) <= cus;
+}
+
+// bytes of kda_layer_fwd's own region after the fused layer forward's
+// workspace: the fused epilogue's per-row partial sums ([chunk-head][d/16][64]
+// fp32), or the operator's fp32 o for the separate epilogue kernel
+static size_t layer_epi_bytes(int64_t NC, int64_t T, int H, int d, bool fused) {
+    return fused ? align_up((size_t)NC * H * (d / 16) * 64 * 4, 256) : align_up((size_t)T * H * d * 4, 256);
+}
+
+static kda_status layer_fwd_impl(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
+                                 const float* wq, const float* wk, const float* wv, const float* A_log,
+                                 const float* dt_bias, const float* initial_state, const int32_t* cu_seqlens,
+                                 int32_t N, int64_t T_total, int32_t H, int32_t d, float* o, float* final_state,
+                                 void* workspace, size_t workspace_bytes, void* stream, const LayerEpi* ep) {
     if (!chunk_sizes_ok(N, T_total, H) || T_total * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     if (!cu_seqlens && N != 1) return KDA_ERR_SHAPE;
     if (!head_ok(d, d)) return KDA_ERR_UNSUPPORTED;
-    if (T_total > 0 && (!xq || !xk || !xv || !xa || !xb || !wq || !wk || !wv || !A_log || !dt_bias || !o))
+    if (T_total > 0 && (!xq || !xk || !xv || !xa || !xb || !wq || !wk || !wv || !A_log || !dt_bias ||
+                        (ep ? (!ep->xg || !ep->rms_w || !ep->y) : !o)))
         return KDA_ERR_NULL;
     const size_t T = (size_t)T_total;
     const size_t nx = T * H * d * 2, nb = T * H * 2, nw = (size_t)H * d * 4 * 4, nh = (size_t)H * 4,
@@ -662,7 +690,9 @@ kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, c
     const int64_t NC = chunk_capacity(N, T_total, cu_seqlens != nullptr);
     if (NC >= (int64_t(1) << 31) / H) return KDA_ERR_SHAPE;
     size_t scr_off = 0;
-    const size_t wbase = layer_fwd_workspace(NC, H, d, &scr_off);
+    const size_t wlayer = layer_fwd_workspace(NC, H, d, &scr_off);
+    const bool fused_epi = ep && layer_epi_fused(N, H, d);
+    const size_t wbase = wlayer + (ep ? layer_epi_bytes(NC, T_total, H, d, fused_epi) : 0);
     const size_t wbytes = wbase + seq_table_bytes(N);  // the sequence table at the end
     if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < wbytes) return KDA_ERR_WORKSPACE;
     for (int i = 0; i < 12; ++i) {
@@ -672,6 +702,20 @@ kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, c
     if (overlaps(o, no, final_state, ns) || overlaps(workspace, wbytes, o, no) ||
         overlaps(workspace, wbytes, final_state, ns))
         return KDA_ERR_ALIAS;
+    if (ep) {
+        // xg [T, H, d] and y [T, H, d] bf16 move 4 channels (8 bytes) per lane; rms_w [d]
+        const size_t ny = T * H * d * 2, nr = (size_t)d * 4;
+        if (!aligned_to(ep->xg, 8) || !aligned_to(ep->y, 8) || !aligned_to(ep->rms_w, 4)) return KDA_ERR_ALIGN;
+        const void* eins[2] = {ep->xg, ep->rms_w};
+        const size_t nein[2] = {ny, nr};
+        for (int i = 0; i < 12; ++i)
+            if (overlaps(ep->y, ny, ins[i], nin[i])) return KDA_ERR_ALIAS;
+        for (int i = 0; i < 2; ++i)
+            if (overlaps(ep->y, ny, eins[i], nein[i]) || overlaps(workspace, wbytes, eins[i], nein[i]) ||
+                overlaps(final_state, ns, eins[i], nein[i]))
+                return KDA_ERR_ALIAS;
+        if (overlaps(ep->y, ny, workspace, wbytes) || overlaps(ep->y, ny, final_state, ns)) return KDA_ERR_ALIAS;
+    }
     if (final_state && initial_state && final_state != initial_state &&
         overlaps(final_state, ns, initial_state, ns))
         return KDA_ERR_ALIAS;
@@ -703,12 +747,58 @@ kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, c
     a.xq = xq, a.xk = xk, a.xv = xv, a.xa = xa, a.xb = xb;
     a.wq = wq, a.wk = wk, a.wv = wv, a.A_log = A_log, a.dt_bias = dt_bias;
     a.qk_scr = w + scr_off;
+    if (fused_epi) {
+        a.epi = true;
+        a.out_f32 = false;
+        a.o = nullptr;
+        a.xg = ep->xg, a.rms_w = ep->rms_w, a.y = ep->y;
+        a.epi_part = reinterpret_cast<float*>(w + wlayer);
+    } else if (ep) {
+        a.o = w + wlayer;  // the operator's o, then the epilogue kernel
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     a.tab = cu_seqlens ? reinterpret_cast<SeqMeta*>(w + wbase) : nullptr;
     if (cu_seqlens && launch_seq_table(cu_seqlens, N, a.T, a.NC, a.tab, st) != hipSuccess) return KDA_ERR_HIP;
     if (NC > 0 && launch_prep(a, st) != hipSuccess) return KDA_ERR_HIP;
     if (launch_recur(a, st) != hipSuccess) return KDA_ERR_HIP;
+    if (ep && !fused_epi && T_total > 0) {
+        LayerArgs la{};
+        la.N = N, la.T = (int)T_total, la.H = H, la.D = d;
+        la.f32 = false;
+        la.o = static_cast<const float*>(a.o);
+        la.g = ep->xg, la.rms_w = ep->rms_w, la.y = ep->y;
+        if (launch_layer_epilogue(la, st) != hipSuccess) return KDA_ERR_HIP;
+    }
     return KDA_OK;
+}
+
+kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
+                               const float* wq, const float* wk, const float* wv, const float* A_log,
+                               const float* dt_bias, const float* initial_state, const int32_t* cu_seqlens,
+                               int32_t N, int64_t T_total, int32_t H, int32_t d, float* o, float* final_state,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    return layer_fwd_impl(xq, xk, xv, xa, xb, wq, wk, wv, A_log, dt_bias, initial_state, cu_seqlens, N, T_total, H,
+                          d, o, final_state, workspace, workspace_bytes, stream, nullptr);
+}
+
+kda_status kda_layer_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t d, size_t* bytes) {
+    if (!bytes) return KDA_ERR_NULL;
+    if (!chunk_sizes_ok(N, T_total, H)) return KDA_ERR_SHAPE;
+    if (!head_ok(d, d)) return KDA_ERR_UNSUPPORTED;
+    const int64_t NC = chunk_capacity(N, T_total, true);
+    *bytes = layer_fwd_workspace(NC, H, d, nullptr) + layer_epi_bytes(NC, T_total, H, d, layer_epi_fused(N, H, d)) +
+             seq_table_bytes(N);
+    return KDA_OK;
+}
+
+kda_status kda_layer_fwd(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
+                         const void* xg, const float* wq, const float* wk, const float* wv, const float* A_log,
+                         const float* dt_bias, const float* rms_w, const float* initial_state,
+                         const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H, int32_t d, void* y,
+                         float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    const LayerEpi ep{xg, rms_w, y};
+    return layer_fwd_impl(xq, xk, xv, xa, xb, wq, wk, wv, A_log, dt_bias, initial_state, cu_seqlens, N, T_total, H,
+                          d, nullptr, final_state, workspace, workspace_bytes, stream, &ep);
 }
 
 kda_status kda_layer_conv_state(const void* xq, const void* xk, const void* xv, const int32_t* cu_seqlens,

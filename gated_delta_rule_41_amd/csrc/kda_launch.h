@@ -62,6 +62,16 @@ struct ChunkArgs {
     const void *xq = nullptr, *xk = nullptr, *xv = nullptr, *xa = nullptr, *xb = nullptr;
     const float *wq = nullptr, *wk = nullptr, *wv = nullptr, *A_log = nullptr, *dt_bias = nullptr;
     void* qk_scr = nullptr;
+    // the layer epilogue fused into the recursion's output stage (with pro, bf16
+    // inputs, d x d heads, N H a multiple of 8): y = RMSNorm(o) * rms_w *
+    // sigmoid(xg) in bf16 instead of o. The workgroups of one (sequence, head)
+    // share each row's sum of squares through epi_part ([chunk-head][dv/16][64]
+    // fp32, set to -1 by the preparation kernel of that chunk-head)
+    bool epi = false;
+    const void* xg = nullptr;
+    const float* rms_w = nullptr;
+    void* y = nullptr;
+    float* epi_part = nullptr;
     Piece piece;
     int slots() const { return piece.g1 > 0 ? piece.g1 - piece.g0 : NC; }  // chunk slots launched
 };

@@ -109,6 +109,7 @@ struct ProArgs {
     PrologueIn<uint16_t> in;
     const float *wq, *wk, *wv, *A_log, *dt_bias;
     uint16_t* qk_scr;  // [chunk-head][q, k][64][D] bf16, written by slow chunks only
+    float* epi_part;   // the fused epilogue's per-row partial sums ([chunk-head][D/16][64]), set to -1 here (or null)
 };
 
 template <int D, typename TIn, typename TG, bool F32, bool PRO = false>
@@ -169,6 +170,12 @@ __global__ __launch_bounds__(256, (F32 && D == 128) ? 1 : 2) void prep_kernel(co
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, n = l & 15, g = l >> 4;
     const int r = 16 * w + n;  // this lane's chunk row
+    if constexpr (PRO) {
+        // the recursion's fused epilogue reads a slot's sign bit as "not written
+        // yet" (this kernel ends before that one starts)
+        if (pa.epi_part)
+            for (int i = tid; i < (D / 16) * 64; i += 256) pa.epi_part[chh * (D / 16) * 64 + i] = -1.f;
+    }
     const bool valid = r < L;
     const int64_t rowoff = ((int64_t)(t0 + r) * H + h) * D;
 
@@ -914,7 +921,7 @@ static hipError_t launch_prep_t(const ChunkArgs& a, hipStream_t st) {
     if constexpr (PRO)
         pa = ProArgs{{(const uint16_t*)a.xq, (const uint16_t*)a.xk, (const uint16_t*)a.xv, (const uint16_t*)a.xa,
                       (const uint16_t*)a.xb},
-                     a.wq, a.wk, a.wv, a.A_log, a.dt_bias, (uint16_t*)a.qk_scr};
+                     a.wq, a.wk, a.wv, a.A_log, a.dt_bias, (uint16_t*)a.qk_scr, a.epi ? a.epi_part : nullptr};
     auto kern = prep_kernel<D, TIn, TG, F32, PRO>;
     const hipError_t e = allow_dynamic_lds((const void*)kern, SM::BYTES);
     if (e != hipSuccess) return e;

@@ -33,6 +33,7 @@
 #include "kda_common.h"
 #include "kda_launch.h"
 #include "kda_prep_util.h"  // split_pos
+#include "kda_layer_util.h"  // sigm, LAYER_EPS (the fused layer epilogue)
 
 #include <type_traits>
 
@@ -249,18 +250,65 @@ __device__ __forceinline__ void warm_chunk(const Ws<typename Pol<F32>::E>& ws, i
 // output adds A_qk V (from the workspace, as the output accumulators' start).
 // The prep kernel computes K-^T V; a seventh wave copies this slab's share of
 // it into an LDS buffer (by chunk parity) one chunk ahead of the compute wave.
-template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false, bool ADDP = false>
+// The layer epilogue fused into the output stage (GeekNews "Kimi Linear"
+// summary, section "Configuração do modelo Kimi Linear": a per-head RMSNorm and
+// a data-dependent output gate before the output projection):
+//     y = o / sqrt(mean over the head's dv channels of o^2 + eps) * rms_w * sigmoid(xg)
+// The dv channels of a row are spread over the dv/16 slab workgroups of the
+// (sequence, head). Workgroup ids congruent mod 8 run on one XCD (the dispatch
+// is round-robin over the 8 XCDs, and the slab ids of a unit are congruent when
+// N H is a multiple of 8), so they share one L2: each output wave publishes the
+// per-row sums of squares of its slab there (part, which the preparation kernel
+// fills with -1, so a slot's sign bit says whether it has been written yet),
+// and finishes the chunk's y two turns later (four chain steps), from the sums
+// of every slab, added in one fixed order so that every workgroup normalises
+// with the same value. By then the other slabs have published, and the loads
+// overlap that turn's products: the chain does not wait for them. A wave keeps
+// its newer pending output tile in registers and the older one in LDS
+// (EPI_LDS bytes after the plan's own).
+struct EpiArgs {
+    const uint16_t* xg;  // [T, H, dv] bf16, the output gate's pre-activation
+    const float* rms_w;  // [dv]
+    uint16_t* y;         // [T, H, dv] bf16
+    float* part;         // [chunk-head][dv/16][64] fp32, -1 before the launch
+};
+// Re-reads of a chunk's partial sums before the wait gives up (each an L2 round
+// trip and a short sleep, some tens of ms in all); a wave that gave up once
+// waits no more, and the rows of every chunk it has not normalised are stored
+// as NaN, so a launch whose workgroups cannot meet still ends. The caller runs
+// this path only when every workgroup of the launch fits on the GPU at once,
+// where the slabs of a unit advance together.
+constexpr int EPI_SPIN_MAX = 1 << 16;
+constexpr int EPI_LDS = 2 * 64 * 16 * 4;  // one 64 x 16 fp32 tile per output wave
+
+// The value lane l ^ 16 (l ^ 32) of the wave holds, by gfx950's lane swaps: with
+// both operands x, permlane16_swap leaves each odd row of its first result
+// holding the even row before it and each even row of its second result the
+// odd row after it (permlane32_swap likewise for the two halves). No LDS traffic.
+__device__ __forceinline__ float lane_xor16(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lane_xor32(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
+}
+
+template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false, bool ADDP = false, bool EPI = false>
 __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel(const float* __restrict__ s0,
                                                                   float* __restrict__ s_final,
                                                                   const SeqMeta* __restrict__ tab, int N, int T,
                                                                   int H, Ws<typename Pol<F32>::E> ws,
-                                                                  void* __restrict__ o, Piece pc) {
+                                                                  void* __restrict__ o, Piece pc, EpiArgs ep) {
     using P = Pol<F32>;
     using E = typename P::E;
     using Frag = typename P::Frag;
     using PL = RecurPlan<D, F32, FUSED, DPLR>;
     static_assert(!DPLR || (FUSED && !F32), "the DPLR chain runs on 16-bit factors with the fused output");
     static_assert(!ADDP || (F32 && !FUSED), "the added state term is for the fp32 unfused chain");
+    static_assert(!EPI || (FUSED && !F32 && !DPLR && !OUT_F32), "the fused epilogue is for the 16-bit KDA chain");
     constexpr int NS = D / 32;
     constexpr int NT = D / 16;  // row tiles over dk == column slabs over dv
     constexpr int RING = PL::RING;
@@ -316,8 +364,23 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
         Frag qa[4][NS], aa[4][2];
         Frag al[PL::HP ? 4 : 1][2];  // HP: the low plane of A_qk
         u32x2_t ohr[4];  // DPLR: this slab's A_qk V tiles (fp16)
+        u32x2_t xgr[EPI ? 4 : 1];  // EPI: the gate's pre-activation at this lane's 4 columns of rows 16 I + n
+        float wc[4];     // EPI: rms_w at this lane's columns 16 ct + 4 g .. + 3
+        bool epi_gave_up = false;  // EPI: a wait of this wave gave up (it waits no more)
+        if constexpr (EPI) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wc[i] = ep.rms_w[16 * ct + 4 * g + i];
+        }
         auto issue = [&](int c) {
             const int64_t chh = (int64_t)(co + c) * H + h;
+            if constexpr (EPI) {
+                // rows past the sequence's end read its last row (not used)
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const int t = tstart + min(64 * c + 16 * I + n, len - 1);
+                    xgr[I] = *reinterpret_cast<const u32x2_t*>(ep.xg + ((int64_t)t * H + h) * D + 16 * ct + 4 * g);
+                }
+            }
             const E* qp = ws.qp + chh * 64 * D;
             const E* ap = ws.aqk + chh * 64 * 64 * (PL::HP ? 2 : 1);
             if constexpr (DPLR) {
@@ -432,12 +495,154 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
                     }
                 }
         };
+        // EPI: y instead of o. Lane n + 16 g holds row 16 I + n at columns
+        // 4 g .. 4 g + 3 of the slab (I = 0..3).
+        constexpr int NSL = D / 16;  // slab workgroups per (sequence, head)
+        auto prec = [&](int c) { return ep.part + ((int64_t)(co + c) * H + h) * NSL * 64; };  // [slab][64 rows]
+        // this slab's sum of squares per row (the lane's 4 columns, then the 4
+        // lanes of the row), published as one contiguous 256-byte record: lane
+        // n + 16 g writes row 16 g + n
+        auto publish = [&](int c, const f32x4_t (&acc)[4]) {
+            float ss[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                float x = acc[I][0] * acc[I][0] + acc[I][1] * acc[I][1];
+                x += acc[I][2] * acc[I][2] + acc[I][3] * acc[I][3];
+                x += lane_xor16(x);
+                x += lane_xor32(x);
+                ss[I] = x;
+            }
+            prec(c)[ct * 64 + 16 * g + n] = g == 0 ? ss[0] : g == 1 ? ss[1] : g == 2 ? ss[2] : ss[3];
+        };
+        // the partial sums this lane adds for its rows: slabs g and g + 4
+        auto load_parts = [&](int c, float (&pv)[4][2]) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const float* rp = prec(c) + 16 * I + n;
+                pv[I][0] = __hip_atomic_load(rp + g * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                pv[I][1] = NSL > 4 ? __hip_atomic_load(rp + (g + 4) * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                   : 0.f;
+            }
+        };
+        auto all_in = [&](const float (&pv)[4][2]) {
+            uint32_t sgn = 0;
+#pragma unroll
+            for (int I = 0; I < 4; ++I) sgn |= __float_as_uint(pv[I][0]) | __float_as_uint(pv[I][1]);
+            return __all((sgn >> 31) == 0);
+        };
+        // until every slab's sums of chunk c are in pv (re-read while not)
+        auto ensure_in = [&](int c, float (&pv)[4][2]) {
+            int it = epi_gave_up ? EPI_SPIN_MAX : 0;
+            while (it < EPI_SPIN_MAX && !all_in(pv)) {
+                __builtin_amdgcn_s_sleep(1);
+                load_parts(c, pv);
+                ++it;
+            }
+            if (it >= EPI_SPIN_MAX) epi_gave_up = true;
+        };
+        auto finish_y_m = [&](int c, auto masked, const f32x4_t (&acc)[4], const u32x2_t (&xg)[4],
+                              const float (&pv)[4][2]) {
+            // the sum over every slab of a row in one order for all of them: lane g
+            // adds slabs g and g + 4, then xor 16, then xor 32
+            float r[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                float a = pv[I][0] + pv[I][1];
+                a += lane_xor16(a);
+                a += lane_xor32(a);
+                r[I] = epi_gave_up ? __builtin_nanf("") : rsqrtf(a * (1.f / D) + LAYER_EPS);
+            }
+            const int t0 = tstart + 64 * c;
+            const int L = min(64, len - 64 * c);
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int rr = 16 * I + n;
+                if (!decltype(masked)::value || rr < L) {
+                    float yv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t gw = xg[I][i >> 1];
+                        const float x = __uint_as_float((i & 1) ? (gw & 0xffff0000u) : (gw << 16));
+                        yv[i] = acc[I][i] * r[I] * wc[i] * sigm(x);
+                    }
+                    u32x2_t pk;
+                    pk[0] = pack2bf(yv[0], yv[1]);
+                    pk[1] = pack2bf(yv[2], yv[3]);
+                    *reinterpret_cast<u32x2_t*>(ep.y + ((int64_t)(t0 + rr) * H + h) * D + 16 * ct + 4 * g) = pk;
+                }
+            }
+        };
+        // only a sequence's last chunk can be partial
+        auto finish_y = [&](int c, const f32x4_t (&acc)[4], const u32x2_t (&xg)[4], const float (&pv)[4][2]) {
+            if (64 * c + 64 <= len)
+                finish_y_m(c, std::false_type{}, acc, xg, pv);
+            else
+                finish_y_m(c, std::true_type{}, acc, xg, pv);
+        };
         // chunk j's operands are fetched right after chunk j - 2's output is
         // computed and stored (in iteration j - 1), two chain steps before they
         // are used (issuing them before the stores measured slower).
         if (p < nch) issue(p);
         __builtin_amdgcn_s_barrier();
         if (p == 1 && nch > 0) __builtin_amdgcn_s_barrier();  // iteration 0 (chunk 0 is wave 1's)
+        if constexpr (EPI) {
+            // chunk j's sums are published in this wave's turn j; its y is
+            // finished two turns later (or after the last), once every slab's are
+            // in. Pending: chunk pj (tile in pacc) and the older pj2 (tile in LDS).
+            f32x4_t* lds_tile = reinterpret_cast<f32x4_t*>(ring + PL::LDS) + p * 4 * 64;  // [I][lane]
+            f32x4_t pacc[4];
+            u32x2_t pxg[4], pxg2[4];
+            int pj = -1, pj2 = -1;
+            // the sums of the chunk to finish in a turn are read at the end of the
+            // turn before (they land during the barriers between), and checked at
+            // the start of the turn, where nothing else is in flight
+            float pv[4][2];
+            if (nch > 0) load_parts(p < nch ? p : 0, pv);  // (unused; keeps the loads in flight counted exactly)
+            for (int j = p; j < nch; j += 2) {
+                __builtin_amdgcn_s_barrier();  // end of iteration j: h_j, V_j are in the buffer
+                if (pj2 >= 0) ensure_in(pj2, pv);
+                f32x4_t acc[4];
+                compute(j, acc);
+                if (pj2 >= 0) {
+                    f32x4_t a2[4];
+#pragma unroll
+                    for (int I = 0; I < 4; ++I) a2[I] = lds_tile[I * 64 + l];
+                    finish_y(pj2, a2, pxg2, pv);
+                }
+                // (after the wait above, which then does not include this store)
+                publish(j, acc);
+                if (pj >= 0) {
+#pragma unroll
+                    for (int I = 0; I < 4; ++I) {
+                        lds_tile[I * 64 + l] = pacc[I];
+                        pxg2[I] = pxg[I];
+                    }
+                }
+                pj2 = pj;
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    pacc[I] = acc[I];
+                    pxg[I] = xgr[I];
+                }
+                pj = j;
+                if (j + 2 < nch) issue(j + 2);
+                load_parts(pj2 >= 0 ? pj2 : j, pv);  // the chunk finished in the next turn
+                if (j + 1 < nch) __builtin_amdgcn_s_barrier();  // end of iteration j + 1
+            }
+            if (pj2 >= 0) {
+                ensure_in(pj2, pv);
+                f32x4_t a2[4];
+#pragma unroll
+                for (int I = 0; I < 4; ++I) a2[I] = lds_tile[I * 64 + l];
+                finish_y(pj2, a2, pxg2, pv);
+            }
+            if (pj >= 0) {
+                load_parts(pj, pv);
+                ensure_in(pj, pv);
+                finish_y(pj, pacc, pxg, pv);
+            }
+            return;
+        }
         for (int j = p; j < nch; j += 2) {
             __builtin_amdgcn_s_barrier();  // end of iteration j: h_j, V_j are in the buffer
             f32x4_t acc[4];
@@ -807,7 +1012,7 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
     }
 }
 
-template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false, bool ADDP = false>
+template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false, bool ADDP = false, bool EPI = false>
 static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     using E = typename Pol<F32>::E;
     using PL = RecurPlan<D, F32, FUSED, DPLR>;
@@ -815,11 +1020,14 @@ static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     ws.uf = static_cast<float*>(a.u);  // KDA with 16-bit factors: U is fp32
     constexpr int NT = D / 16;
     const int NU = a.N * a.H;
-    auto kern = recur_kernel<D, F32, FUSED, OUT_F32, DPLR, ADDP>;
-    const hipError_t e = allow_dynamic_lds((const void*)kern, PL::LDS);
+    auto kern = recur_kernel<D, F32, FUSED, OUT_F32, DPLR, ADDP, EPI>;
+    constexpr int LDS = PL::LDS + (EPI ? EPI_LDS : 0);
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    const hipError_t e = allow_dynamic_lds((const void*)kern, LDS);
     if (e != hipSuccess) return e;
     dim3 grid(NU * NT), block(FUSED ? (DPLR ? 448 : 384) : 64 * (PL::NCW + 2));
-    hipLaunchKernelGGL(kern, grid, block, PL::LDS, st, a.s0, a.s_final, a.tab, a.N, a.T, a.H, ws, a.o, a.piece);
+    const EpiArgs ep{static_cast<const uint16_t*>(a.xg), a.rms_w, static_cast<uint16_t*>(a.y), a.epi_part};
+    hipLaunchKernelGGL(kern, grid, block, LDS, st, a.s0, a.s_final, a.tab, a.N, a.T, a.H, ws, a.o, a.piece, ep);
     return hipGetLastError();
 }
 
@@ -827,6 +1035,7 @@ template <int D>
 static hipError_t launch_recur_d(const ChunkArgs& a, hipStream_t st) {
     if (a.in_f32 || a.f32_factors)
         return a.pb ? launch_recur_t<D, true, false, true, false, true>(a, st) : launch_recur_t<D, true, false, true>(a, st);
+    if (a.epi) return launch_recur_t<D, false, true, false, false, false, true>(a, st);  // (checked by the caller)
     return a.out_f32 ? launch_recur_t<D, false, true, true>(a, st) : launch_recur_t<D, false, true, false>(a, st);
 }
 

@@ -34,8 +34,10 @@
  *    transition, for comparison); kda_chunk_fwd_noalloc (the prefill with a
  *    static workspace, for callers that cannot allocate);
  *  - the layer around it: kda_layer_prologue, kda_layer_epilogue,
- *    kda_layer_chunk_fwd (the prologue fused into the prefill), and for
- *    decoding kda_layer_conv_state and kda_layer_decode_prologue;
+ *    kda_layer_chunk_fwd (the prologue fused into the prefill),
+ *    kda_layer_fwd (the whole layer: prologue and epilogue fused into the
+ *    prefill), and for decoding kda_layer_conv_state and
+ *    kda_layer_decode_prologue;
  *  - kda_status_str, kda_abi_version.
  *  - Layouts are token-major: q, k, log_alpha [T, H, dk]; v [T, H, dv];
  *    beta [T, H]; o [T, H, dv]; states [N, H, dk, dv] fp32 (dv fastest).
@@ -393,6 +395,52 @@ kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, c
  */
 kda_status kda_layer_epilogue(const float* o, const void* xg, const float* rms_w, int64_t T_total, int32_t H,
                               int32_t dv, int32_t dtype, void* y, void* stream);
+
+/*
+ * Bytes of device workspace kda_layer_fwd needs on the current device (host
+ * call; it reads the device's CU count): kda_layer_chunk_fwd's, plus the
+ * epilogue's region: per-row partial sums of squares (32 bytes per token-head
+ * at d = 128) when the epilogue is fused for these shapes on this device, else
+ * room for the operator's fp32 o (4 d bytes per token-head), which is also the
+ * answer when no device can be queried. A call on a device with fewer CUs may
+ * need the larger size (KDA_ERR_WORKSPACE).
+ *   bytes: host out-pointer, written on KDA_OK.
+ */
+kda_status kda_layer_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, int32_t d, size_t* bytes);
+
+/*
+ * The whole layer between the projections, in bf16: kda_layer_prologue,
+ * kda_chunk_fwd and kda_layer_epilogue in one call, with the prologue fused
+ * into the chunk preparation (as kda_layer_chunk_fwd) and the epilogue fused
+ * into the recursion's output stage: o never reaches memory. Arguments as
+ * kda_layer_chunk_fwd, plus
+ *   xg     [T_total, H, d] bf16 (the output gate's pre-activation)
+ *   rms_w  [d] fp32
+ *   y      [T_total, H, d] bf16 (output, in place of o)
+ * xg and y must be 8-byte aligned and rms_w 4-byte aligned (KDA_ERR_ALIGN); y
+ * must not overlap an input, the workspace or final_state, and xg and rms_w must
+ * not overlap the workspace or final_state (KDA_ERR_ALIAS).
+ *
+ * A row's RMSNorm needs all d channels, which the recursion spreads over d/16
+ * workgroups of one (sequence, head). The epilogue is fused when those
+ * workgroups share an XCD's L2 and all fit on the GPU at once: N * H a
+ * multiple of 8 (workgroup ids are dispatched round-robin over the 8 XCDs) and
+ * N * H * d / 16 at most the device's CU count. Each workgroup then publishes
+ * its slab's per-row sums of squares in the workspace and finishes a chunk's y
+ * a turn later from every slab's sums, added in one fixed order. A wait for
+ * another slab's sums that has not ended after some tens of ms gives up, and
+ * the rows it had still to finish are NaN; this cannot happen unless other work
+ * keeps the launch's workgroups off the GPU for that long. Otherwise the operator writes o to
+ * the workspace and the epilogue kernel follows; both ways give the same y up
+ * to the order of the sum of squares (one rounding of the RMS). Calls that
+ * share a workspace must not run concurrently. Three kernels are enqueued
+ * (four with the separate epilogue).
+ */
+kda_status kda_layer_fwd(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
+                         const void* xg, const float* wq, const float* wk, const float* wv, const float* A_log,
+                         const float* dt_bias, const float* rms_w, const float* initial_state,
+                         const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H, int32_t d, void* y,
+                         float* final_state, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace kda_dplr_chunk_fwd needs (host call, no device

@@ -33,8 +33,8 @@ def test_library_exports_every_declared_function():
                      "kda_chunk_fwd_noalloc", "kda_chunk_fwd_timed",
                      "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_dplr_chunk_fwd",
                      "kda_dplr_chunk_fwd_workspace_size", "kda_layer_chunk_fwd", "kda_layer_chunk_fwd_workspace_size",
-                     "kda_layer_conv_state", "kda_layer_decode_prologue", "kda_layer_epilogue", "kda_layer_prologue",
-                     "kda_status_str"]
+                     "kda_layer_conv_state", "kda_layer_decode_prologue", "kda_layer_epilogue", "kda_layer_fwd",
+                     "kda_layer_fwd_workspace_size", "kda_layer_prologue", "kda_status_str"]
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -372,6 +372,53 @@ def test_layer_fwd_workspace_and_validation():
     assert layer_fwd_call(xq=x, o=x + 64) == ALIAS
     y = f()
     assert layer_fwd_call(o=y, fs=y + 256) == ALIAS
+
+
+def whole_layer_call(**over):
+    f = Fake()
+    a = dict(xq=f(), xk=f(), xv=f(), xa=f(), xb=f(), xg=f(), wq=f(), wk=f(), wv=f(), A_log=f(), dtb=f(), rw=f(),
+             s0=None, cu=None, N=1, T=100, H=2, d=64, y=f(), fs=f(), ws=f(), wsb=1 << 40, stream=None)
+    a.update(over)
+    P = ctypes.c_void_p
+    return kda._load().kda_layer_fwd(*(P(a[x]) for x in ("xq", "xk", "xv", "xa", "xb", "xg", "wq", "wk", "wv",
+                                                         "A_log", "dtb", "rw", "s0", "cu")),
+                                     a["N"], a["T"], a["H"], a["d"], P(a["y"]), P(a["fs"]), P(a["ws"]), a["wsb"],
+                                     P(a["stream"]))
+
+
+def test_whole_layer_workspace_and_validation():
+    """kda_layer_fwd: workspace = kda_layer_chunk_fwd's plus the epilogue's region,
+    rounded up to 256 bytes: with no device to query (as here) room for the
+    operator's fp32 o, which the epilogue kernel reads (the GPU tests cover the
+    fused epilogue's partial sums); host validation refuses every malformed
+    call before any launch."""
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    for N, T, H, d in ((1, 4096, 32, 128), (1000, 1000, 2, 128), (16, 135000, 32, 64), (3, 0, 4, 64)):
+        NC = (T + 63 * N) // 64
+        extra = up(T * H * d * 4)
+        assert kda.layer_fwd_workspace_size(N, T, H, d) == kda.layer_chunk_fwd_workspace_size(N, T, H, d) + extra
+    with pytest.raises(kda.KDAError):
+        kda.layer_fwd_workspace_size(1, 10, 1, 96)
+    assert whole_layer_call(xg=None) == NULL
+    assert whole_layer_call(rw=None) == NULL
+    assert whole_layer_call(y=None) == NULL
+    assert whole_layer_call(N=2) == SHAPE  # no cu_seqlens
+    assert whole_layer_call(d=96) == UNSUP
+    f = Fake()
+    assert whole_layer_call(xg=f(4)) == ALIGN  # 4 channels per lane
+    assert whole_layer_call(y=f(4)) == ALIGN
+    assert whole_layer_call(rw=f(2)) == ALIGN
+    assert whole_layer_call(wsb=kda.layer_chunk_fwd_workspace_size(1, 100, 2, 64)) == WORKSPACE
+    x = f()
+    assert whole_layer_call(xq=x, y=x + 64) == ALIAS
+    g = f()
+    assert whole_layer_call(xg=g, y=g + 8) == ALIAS
+    fs = f()
+    assert whole_layer_call(rw=fs + 64, fs=fs) == ALIAS
+    w = f()
+    assert whole_layer_call(ws=w, y=w + 1024) == ALIAS
 
 
 def test_layer_decode_validation():

@@ -1,7 +1,8 @@
 """GPU parity of the layer prologue and epilogue (kda_layer_prologue,
 kda_layer_epilogue, through the C ABI) against the fp64 layer oracle
 (oracle/layer.py, pinned in tests/test_layer_cpu.py), and of the whole layer
-between the projections: prologue -> kda_chunk_fwd -> epilogue.
+between the projections: prologue -> kda_chunk_fwd -> epilogue, the prologue
+fused into the prefill (kda_layer_chunk_fwd) and both fused (kda_layer_fwd).
 
 Bars:
 * fp32 outputs: max-abs error relative to the RMS within 1e-5 (fp32 arithmetic
@@ -245,3 +246,58 @@ def test_layer_decode_continues_prefill():
     ey, es = err(torch.stack(ys), rows), err(state, S_ref)
     say(f"[layer] decode after prefill, {S} steps: y {ey:.2e}  final state {es:.2e}")
     assert ey <= 1e-4 and es <= 1e-4
+
+
+WHOLE_CASES = {
+    # N H a multiple of 8 and N H d/16 workgroups within the CU count: the fused epilogue
+    "prefill-4k": {},
+    "ragged": dict(lengths=[300, 5, 0, 190, 64, 1, 129, 17], H=4, s0_std=0.02),
+    "d64": dict(lengths=[70, 1, 129, 200], H=2, d=64),
+    "strong-decay": dict(lengths=[200, 77], H=4),  # dt_bias raised below: the exact path
+    # N H = 9: the slab workgroups of a head are not all on one XCD -> the epilogue kernel
+    "not-mult-8": dict(lengths=[300, 5, 190], H=3),
+    # N H d/16 = 1,024 workgroups: more than fit at once -> the epilogue kernel
+    "many-heads": dict(lengths=[70, 130, 0, 64, 200, 9, 33, 100], H=16, s0_std=0.02),
+}
+
+
+@pytest.mark.parametrize("shape", list(WHOLE_CASES))
+def test_whole_layer_one_call(shape):
+    """kda_layer_fwd: prologue fused into the preparation and the epilogue into
+    the recursion's output stage (or the epilogue kernel after it, where the
+    slab workgroups of a head cannot share an XCD or all be resident). Against
+    kda_layer_chunk_fwd followed by kda_layer_epilogue: the final states are
+    bitwise equal (the chain is the same); y is within one bf16 step of the fp64
+    epilogue of the operator's own o (the epilogue kernel's bar), and bitwise
+    equal to the epilogue kernel's where the call falls back to it. Two calls
+    give the same y."""
+    c = ki.make_layer("prefill-4k", DEV, **WHOLE_CASES[shape])
+    if shape == "strong-decay":
+        c.dt_bias.fill_(6.0)
+    N, H, d = len(c.lengths), c.xq.shape[1], c.xq.shape[2]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    fused = (N * H) % 8 == 0 and N * H * (d // 16) <= cus
+    say(f"[layer] whole layer in one call, {shape}: N {N} H {H} d {d}, "
+        f"{'fused epilogue' if fused else 'epilogue kernel'}")
+    # the workspace holds the fused epilogue's per-row partial sums, or room for o
+    T = c.xq.shape[0]
+    NC = (T + 63 * N) // 64
+    region = NC * H * (d // 16) * 64 * 4 if fused else T * H * d * 4
+    assert kda.layer_fwd_workspace_size(N, T, H, d) == (kda.layer_chunk_fwd_workspace_size(N, T, H, d) +
+                                                        (region + 255) // 256 * 256)
+    o, S_ref = kda.layer_chunk_fwd(c.xq, c.xk, c.xv, c.xa, c.xb, c.wq, c.wk, c.wv, c.A_log, c.dt_bias,
+                                   c.initial_state, c.cu_seqlens)
+    y_ref = kda.layer_epilogue(o, c.xg, c.rms_w)
+    y, S = kda.layer_fwd(c.xq, c.xk, c.xv, c.xa, c.xb, c.xg, c.wq, c.wk, c.wv, c.A_log, c.dt_bias, c.rms_w,
+                         c.initial_state, c.cu_seqlens)
+    y2, _ = kda.layer_fwd(c.xq, c.xk, c.xv, c.xa, c.xb, c.xg, c.wq, c.wk, c.wv, c.A_log, c.dt_bias, c.rms_w,
+                          c.initial_state, c.cu_seqlens)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S_ref), "final states differ from kda_layer_chunk_fwd's"
+    assert torch.equal(y, y2), "two calls differ"
+    assert bool(torch.isfinite(y.float()).all()), "non-finite y"
+    n_diff = int((y != y_ref).sum())
+    say(f"    y elements differing from the epilogue kernel's: {n_diff} of {y.numel()}")
+    check_outputs("y", [y], [ly.layer_epilogue(o.cpu(), c.xg.cpu(), c.rms_w.cpu())], True)
+    if not fused:
+        assert n_diff == 0
