@@ -260,12 +260,10 @@ __device__ __forceinline__ void warm_chunk(const Ws<typename Pol<F32>::E>& ws, i
 // N H is a multiple of 8), so they share one L2: each output wave publishes the
 // per-row sums of squares of its slab there (part, which the preparation kernel
 // fills with -1, so a slot's sign bit says whether it has been written yet),
-// and finishes the chunk's y two turns later (four chain steps), from the sums
-// of every slab, added in one fixed order so that every workgroup normalises
-// with the same value. By then the other slabs have published, and the loads
-// overlap that turn's products: the chain does not wait for them. A wave keeps
-// its newer pending output tile in registers and the older one in LDS
-// (EPI_LDS bytes after the plan's own).
+// and finishes that chunk's y in its next free iteration (while the other
+// output wave computes), from the sums of every slab, added in one fixed order
+// so that every workgroup normalises with the same value. By then the other
+// slabs have published: the chain does not wait for them.
 struct EpiArgs {
     const uint16_t* xg;  // [T, H, dv] bf16, the output gate's pre-activation
     const float* rms_w;  // [dv]
@@ -279,7 +277,6 @@ struct EpiArgs {
 // this path only when every workgroup of the launch fits on the GPU at once,
 // where the slabs of a unit advance together.
 constexpr int EPI_SPIN_MAX = 1 << 16;
-constexpr int EPI_LDS = 2 * 64 * 16 * 4;  // one 64 x 16 fp32 tile per output wave
 
 // The value lane l ^ 16 (l ^ 32) of the wave holds, by gfx950's lane swaps: with
 // both operands x, permlane16_swap leaves each odd row of its first result
@@ -586,58 +583,40 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
         __builtin_amdgcn_s_barrier();
         if (p == 1 && nch > 0) __builtin_amdgcn_s_barrier();  // iteration 0 (chunk 0 is wave 1's)
         if constexpr (EPI) {
-            // chunk j's sums are published in this wave's turn j; its y is
-            // finished two turns later (or after the last), once every slab's are
-            // in. Pending: chunk pj (tile in pacc) and the older pj2 (tile in LDS).
-            f32x4_t* lds_tile = reinterpret_cast<f32x4_t*>(ring + PL::LDS) + p * 4 * 64;  // [I][lane]
+            // A wave computes chunk j in iteration j + 1 and publishes its sums;
+            // in iteration j + 2, where the other output wave computes chunk
+            // j + 1, it finishes y of its previous chunk j - 2, whose sums every
+            // slab published an iteration or more before and which it read at
+            // the end of its previous finish. The finish thus runs beside the
+            // other wave's products instead of after its own.
             f32x4_t pacc[4];
-            u32x2_t pxg[4], pxg2[4];
-            int pj = -1, pj2 = -1;
-            // the sums of the chunk to finish in a turn are read at the end of the
-            // turn before (they land during the barriers between), and checked at
-            // the start of the turn, where nothing else is in flight
+            u32x2_t pxg[4];
+            int pj = -1;
             float pv[4][2];
             if (nch > 0) load_parts(p < nch ? p : 0, pv);  // (unused; keeps the loads in flight counted exactly)
             for (int j = p; j < nch; j += 2) {
                 __builtin_amdgcn_s_barrier();  // end of iteration j: h_j, V_j are in the buffer
-                if (pj2 >= 0) ensure_in(pj2, pv);
                 f32x4_t acc[4];
                 compute(j, acc);
-                if (pj2 >= 0) {
-                    f32x4_t a2[4];
-#pragma unroll
-                    for (int I = 0; I < 4; ++I) a2[I] = lds_tile[I * 64 + l];
-                    finish_y(pj2, a2, pxg2, pv);
-                }
-                // (after the wait above, which then does not include this store)
                 publish(j, acc);
-                if (pj >= 0) {
+                u32x2_t xgj[4];
 #pragma unroll
-                    for (int I = 0; I < 4; ++I) {
-                        lds_tile[I * 64 + l] = pacc[I];
-                        pxg2[I] = pxg[I];
-                    }
+                for (int I = 0; I < 4; ++I) xgj[I] = xgr[I];  // (the next issue overwrites xgr)
+                if (j + 2 < nch) issue(j + 2);
+                if (j + 1 < nch) __builtin_amdgcn_s_barrier();  // end of iteration j + 1
+                if (pj >= 0) {
+                    ensure_in(pj, pv);
+                    finish_y(pj, pacc, pxg, pv);
                 }
-                pj2 = pj;
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     pacc[I] = acc[I];
-                    pxg[I] = xgr[I];
+                    pxg[I] = xgj[I];
                 }
                 pj = j;
-                if (j + 2 < nch) issue(j + 2);
-                load_parts(pj2 >= 0 ? pj2 : j, pv);  // the chunk finished in the next turn
-                if (j + 1 < nch) __builtin_amdgcn_s_barrier();  // end of iteration j + 1
-            }
-            if (pj2 >= 0) {
-                ensure_in(pj2, pv);
-                f32x4_t a2[4];
-#pragma unroll
-                for (int I = 0; I < 4; ++I) a2[I] = lds_tile[I * 64 + l];
-                finish_y(pj2, a2, pxg2, pv);
+                load_parts(pj, pv);  // for the finish in this wave's next free iteration
             }
             if (pj >= 0) {
-                load_parts(pj, pv);
                 ensure_in(pj, pv);
                 finish_y(pj, pacc, pxg, pv);
             }
@@ -1021,8 +1000,7 @@ static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     constexpr int NT = D / 16;
     const int NU = a.N * a.H;
     auto kern = recur_kernel<D, F32, FUSED, OUT_F32, DPLR, ADDP, EPI>;
-    constexpr int LDS = PL::LDS + (EPI ? EPI_LDS : 0);
-    static_assert(LDS <= 160 * 1024, "LDS budget");
+    constexpr int LDS = PL::LDS;
     const hipError_t e = allow_dynamic_lds((const void*)kern, LDS);
     if (e != hipSuccess) return e;
     dim3 grid(NU * NT), block(FUSED ? (DPLR ? 448 : 384) : 64 * (PL::NCW + 2));
