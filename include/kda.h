@@ -429,8 +429,12 @@ kda_status kda_layer_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
  * its slab's per-row sums of squares in the workspace and finishes a chunk's y
  * a turn later from every slab's sums, added in one fixed order. A wait for
  * another slab's sums that has not ended after some tens of ms gives up, and
- * the rows it had still to finish are NaN; this cannot happen unless other work
- * keeps the launch's workgroups off the GPU for that long. Otherwise the operator writes o to
+ * the rows it had still to finish are NaN. That needs other work to keep some
+ * of the launch's workgroups off the GPU for that long while others wait: in
+ * particular two kda_layer_fwd calls running at the same time on different
+ * streams can each hold CUs the other's workgroups need. Run such calls on one
+ * stream, or use kda_layer_chunk_fwd and kda_layer_epilogue, which never wait
+ * on one another's workgroups. Otherwise the operator writes o to
  * the workspace and the epilogue kernel follows; both ways give the same y up
  * to the order of the sum of squares (one rounding of the RMS). Calls that
  * share a workspace must not run concurrently. Three kernels are enqueued
