@@ -62,7 +62,7 @@ struct RecurPlan {
     static_assert(PBS % 1024 == 0, "K-^T V share in whole 1 KiB loads");
     // target of the L2 warm-up loads (never read); DPLR has no room for it and
     // aims them at the unread tail of ring slot 0's gamma region instead
-    static constexpr int WARM = (FUSED && !DPLR) ? 256 : 0;
+    static constexpr int WARM = !DPLR ? 256 : 0;
     // unfused (fp32 factors): NCW compute waves exchange their row tiles of the
     // state ([D/16][64 lanes][4]) and of V_new ([4][64][4]) through LDS
     static constexpr int NCW = FUSED ? 1 : 4;
@@ -294,7 +294,7 @@ __device__ __forceinline__ float lane_xor32(float x) {
 }
 
 template <int D, bool F32, bool FUSED, bool OUT_F32, bool DPLR = false, bool ADDP = false, bool EPI = false>
-__global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel(const float* __restrict__ s0,
+__global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 448) void recur_kernel(const float* __restrict__ s0,
                                                                   float* __restrict__ s_final,
                                                                   const SeqMeta* __restrict__ tab, int N, int T,
                                                                   int H, Ws<typename Pol<F32>::E> ws,
@@ -661,6 +661,39 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 384) void recur_kernel
         return;
     }
 
+    if (!FUSED && wv == PL::NCW + 2) {
+        // ---------------- L2 warm-up wave of the fp32 chain: during chunk c, this
+        // slab's share of chunk c + AHEAD's -W and K-^T lines (one load per lane)
+        // and its own U and gamma lines, so that the producers' DMA hits the L2
+        char* wdst = ring + RING * PL::SLOT + PL::XCH;
+        constexpr int LW = PL::FB / 128, LPER = 2 * LW / NT, LU = PL::UB / 128, LG = PL::GB / 128;
+        static_assert(LPER <= 64 && LU + LG <= 64, "one warm-up load per lane and part");
+        auto warm = [&](int c) {
+            const int64_t chh = (int64_t)(co + (ADDP ? nch - 1 - c : c)) * H + h;
+            const int L = ct * LPER + (l < LPER ? l : LPER - 1);
+            const char* p = L < LW ? reinterpret_cast<const char*>(ws.wn + chh * 64 * D) + L * 128
+                                   : reinterpret_cast<const char*>(ws.km + chh * D * 64) + (L - LW) * 128;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)p,
+                                             (__attribute__((address_space(3))) void*)wdst, 4, 0, 0);
+            const int m = l < LU + LG ? l : 0;
+            const char* pu = m < LU ? reinterpret_cast<const char*>(ws.u + chh * 64 * D + (int64_t)ct * 4 * 64 * 4) + m * 128
+                                    : reinterpret_cast<const char*>(ws.gam + chh * D) + (m - LU) * 128;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)pu,
+                                             (__attribute__((address_space(3))) void*)wdst, 4, 0, 0);
+        };
+        const int pre = nch < PL::AHEAD ? nch : PL::AHEAD;
+        for (int c = 0; c < pre; ++c) warm(c);
+        __builtin_amdgcn_s_barrier();
+        for (int c = 0; c < nch; ++c) {
+            if (c + PL::AHEAD < nch) warm(c + PL::AHEAD);
+            wait_vm<48>();
+            __builtin_amdgcn_s_barrier();  // the compute waves' V_new exchange
+            __builtin_amdgcn_s_barrier();  // end of chunk
+        }
+        wait_vm<0>();  // the LDS target stays allocated until the loads have landed
+        return;
+    }
+
     if (FUSED && wv == 5) {
         // ---------------- L2 warm-up wave: chunk c + AHEAD during chunk c; it
         // never waits for its loads except to bound the counter and at the end
@@ -1003,7 +1036,7 @@ static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     constexpr int LDS = PL::LDS;
     const hipError_t e = allow_dynamic_lds((const void*)kern, LDS);
     if (e != hipSuccess) return e;
-    dim3 grid(NU * NT), block(FUSED ? (DPLR ? 448 : 384) : 64 * (PL::NCW + 2));
+    dim3 grid(NU * NT), block(FUSED ? (DPLR ? 448 : 384) : 64 * (PL::NCW + 3));
     const EpiArgs ep{static_cast<const uint16_t*>(a.xg), a.rms_w, static_cast<uint16_t*>(a.y), a.epi_part};
     hipLaunchKernelGGL(kern, grid, block, LDS, st, a.s0, a.s_final, a.tab, a.N, a.T, a.H, ws, a.o, a.piece, ep);
     return hipGetLastError();
