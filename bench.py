@@ -64,18 +64,19 @@ KERNEL_SYMBOL = {"prep": "prep_kernel", "recur": "recur_kernel", "decode": "deco
                  "bwd_fwd_prep": "prep_kernel", "bwd_fwd_recur": "recur_kernel",
                  "bwd_prep": "bwd_prep_kernel", "bwd_recur": "recur_kernel", "bwd_local": "bwd_local_kernel",
                  "layer_prologue": "layer_prologue_kernel", "layer_epilogue": "layer_epilogue_kernel",
-                 "layer_prep": "prep_kernel", "layer_recur": "recur_kernel"}
+                 "layer_prep": "prep_kernel", "layer_recur": "recur_kernel", "layer_decode": "decode_kernel"}
 # each kernel's source file and the library headers it includes (with kda_common.h, which all do)
 _PREP = ("kda_prep.hip", "kda_prep_util.h", "kda_layer_util.h")
 _RECUR = ("kda_recur.hip", "kda_prep_util.h", "kda_layer_util.h")
-KERNEL_SOURCE = {"prep": _PREP, "recur": _RECUR, "decode": "kda_decode.hip",
+_DECODE = ("kda_decode.hip", "kda_layer_util.h")
+KERNEL_SOURCE = {"prep": _PREP, "recur": _RECUR, "decode": _DECODE,
                  "dplr_prep": ("kda_dplr_prep.hip", "kda_prep_util.h"), "dplr_recur": _RECUR,
                  "bwd_fwd_prep": _PREP, "bwd_fwd_recur": _RECUR,
                  "bwd_prep": ("kda_bwd.hip", "kda_prep_util.h"), "bwd_recur": _RECUR,
                  "bwd_local": ("kda_bwd.hip", "kda_prep_util.h"),
                  "layer_prologue": ("kda_layer.hip", "kda_layer_util.h"),
                  "layer_epilogue": ("kda_layer.hip", "kda_layer_util.h"),
-                 "layer_prep": _PREP, "layer_recur": _RECUR}
+                 "layer_prep": _PREP, "layer_recur": _RECUR, "layer_decode": _DECODE}
 
 
 def kernel_key(short_name: str):
@@ -103,7 +104,9 @@ def kernel_key(short_name: str):
         if flag(4):
             return "layer_prep"
         return "bwd_fwd_prep" if flag(3) else "prep"
-    for key in ("dplr_prep", "decode", "bwd_prep", "bwd_local", "layer_prologue", "layer_epilogue"):
+    if sym == "decode_kernel":  # <D, TIn, TG, fp32 o, fused layer epilogue>
+        return "layer_decode" if flag(4) else "decode"
+    for key in ("dplr_prep", "bwd_prep", "bwd_local", "layer_prologue", "layer_epilogue"):
         if sym == KERNEL_SYMBOL[key]:
             return key
     return None
@@ -463,8 +466,9 @@ def time_layer(kda, lc, steps, warmup, hip, stream):
 def time_layer_decode(kda, ki, steps, warmup, hip, stream, N=256, H=32, d=128):
     """The layer's decode step at decode-256 size (one bf16 token per sequence):
     decode prologue (history in place), kda_decode_step (fp32 state in place),
-    epilogue, all through the C ABI between two events around the loop.
-    Returns ms per step."""
+    epilogue, all through the C ABI between two events around the loop; then
+    the same with kda_layer_decode_step (the epilogue fused into the decode
+    kernel) in place of the last two. Returns ms per step of each."""
     import torch
     lib = kda._load()
     lc = ki.make_layer("decode-256", "cuda:0", lengths=[1] * N, H=H, d=d, s0_std=0.0)  # one token's pre-activations each
@@ -485,22 +489,30 @@ def time_layer_decode(kda, ki, steps, warmup, hip, stream, N=256, H=32, d=128):
     dec = (*(ptr(t) for t in (q, k, v, la, beta, state)), N, H, d, d, bf, bf, kda.KDA_F32, ptr(o), P(stream))
     epi = (ptr(o), ptr(lc.xg), ptr(lc.rms_w), N, H, d, bf, ptr(y), P(stream))
 
+    fused = (*(ptr(t) for t in (q, k, v, la, beta, state, lc.xg, lc.rms_w)), N, H, d, bf, ptr(y), P(stream))
+
     def step():
         if lib.kda_layer_decode_prologue(*pro) != 0 or lib.kda_decode_step(*dec) != 0 or \
                 lib.kda_layer_epilogue(*epi) != 0:
             raise RuntimeError("layer decode step failed")
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = Events(hip, 2)
-    ev.record(0, stream)
-    for _ in range(steps):
-        step()
-    ev.record(1, stream)
-    torch.cuda.synchronize()
-    ms = ev.ms(0, 1) / steps
-    ev.close()
-    return ms
+
+    def step_fused():
+        if lib.kda_layer_decode_prologue(*pro) != 0 or lib.kda_layer_decode_step(*fused) != 0:
+            raise RuntimeError("fused layer decode step failed")
+    res = []
+    for fn in (step, step_fused):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = Events(hip, 2)
+        ev.record(0, stream)
+        for _ in range(steps):
+            fn()
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        res.append(ev.ms(0, 1) / steps)
+        ev.close()
+    return res[0], res[1]
 
 
 def time_decode(kda, dec, steps, warmup, hip, stream):
@@ -752,7 +764,7 @@ def report_pmc(workload: str, fetch_db: str, write_db: str, cal_fetch_db: str, c
         print(f"| `{name}` | {fe[name][0]} | {fe[name][1]:.0f} | {wr[name][1]:.0f} | {b:.4g} |")
         if kern is None:
             continue
-        wl = "decode-256" if kern == "decode" else workload
+        wl = "decode-256" if kern in ("decode", "layer_decode") else workload
         rec = {"kernel": name, "workload": wl, "source_sha": source_sha(kern),
                "fetch_kib": fe[name][1], "write_kib": wr[name][1],
                "fetch_scale": f_fetch, "write_scale": f_write, "bytes_per_launch": round(b)}
@@ -1026,10 +1038,12 @@ def side_legs(args, kda, ki, hip, stream, flush, dev, out, t_start, headline_hos
                                   "traffic": traffic_from_profiles("layer_epilogue")}}
         del lc
         if not args.no_layer_decode:
-            ld_ms = time_layer_decode(kda, ki, 200, 50, hip, stream)
+            ld_ms, ldf_ms = time_layer_decode(kda, ki, 200, 50, hip, stream)
             out["layer"]["decode_step"] = {
                 "workload": "decode-256 pre-activations (bf16), 256 sequences x 32 heads, fp32 states",
-                "ms_per_step": round(ld_ms, 5), "tokens_per_s": round(256 / (ld_ms * 1e-3), 1)}
+                "ms_per_step": round(ld_ms, 5), "tokens_per_s": round(256 / (ld_ms * 1e-3), 1),
+                "fused_epilogue_ms_per_step": round(ldf_ms, 5),
+                "fused_epilogue_tokens_per_s": round(256 / (ldf_ms * 1e-3), 1)}
 
     if not args.no_decode:
         dec_inputs = min(args.decode_steps, 100)  # distinct per-step inputs, cycled

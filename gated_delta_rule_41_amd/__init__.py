@@ -20,8 +20,9 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "decode_step", "workspace_size", "bwd_workspace_size", "dplr_chunk_fwd",
-           "dplr_workspace_size", "abi_version", "status_str", "library_path", "KDAError", "CHUNK"]
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "decode_step", "layer_decode_step", "workspace_size",
+           "bwd_workspace_size", "dplr_chunk_fwd", "dplr_workspace_size", "abi_version", "status_str", "library_path",
+           "KDAError", "CHUNK"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # the in-tree build; KDA_LIBRARY may name another build of the same sources
@@ -102,6 +103,8 @@ def _load():
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+    lib.kda_layer_decode_step.restype = ctypes.c_int
+    lib.kda_layer_decode_step.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, ctypes.c_int, P, P]
     _lib = lib
     return lib
 
@@ -535,6 +538,41 @@ def layer_epilogue(o: torch.Tensor, xg: torch.Tensor, rms_w: torch.Tensor) -> to
                                 _stream(dev))
     if st != 0:
         raise KDAError(st, "kda_layer_epilogue")
+    return y
+
+
+def layer_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+                      beta: torch.Tensor, state: torch.Tensor, xg: torch.Tensor, rms_w: torch.Tensor,
+                      y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer's decode step after ``layer_decode_prologue`` (see
+    ``kda_layer_decode_step``): ``decode_step`` and ``layer_epilogue`` in one
+    kernel. q, k, v, log_alpha, xg [N, H, d]; beta [N, H] (all in one dtype,
+    bf16 or fp32); state [N, H, d, d] fp32, updated in place; rms_w [d] fp32.
+    Returns y [N, H, d] in the inputs' dtype."""
+    lib = _load()
+    dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q, k, v, log_alpha, xg must be [N, H, d]")
+    N, H, d = q.shape
+    items = [("q", q, (N, H, d)), ("k", k, (N, H, d)), ("v", v, (N, H, d)), ("log_alpha", log_alpha, (N, H, d)),
+             ("beta", beta, (N, H)), ("state", state, (N, H, d, d)), ("xg", xg, (N, H, d)), ("rms_w", rms_w, (d,))]
+    if y is not None:
+        items.append(("y", y, (N, H, d)))
+    _check(items, dev)
+    if state.dtype != torch.float32 or rms_w.dtype != torch.float32:
+        raise TypeError("state and rms_w must be float32")
+    dt = q.dtype
+    for name, t in (("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta), ("xg", xg)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must have q's dtype")
+    if y is None:
+        y = torch.empty(N, H, d, dtype=dt, device=dev)
+    elif y.dtype != dt:
+        raise TypeError("y must have q's dtype")
+    st = lib.kda_layer_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(xg),
+                                   _ptr(rms_w), N, H, d, _dtype_code(q, "q"), _ptr(y), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_layer_decode_step")
     return y
 
 

@@ -927,6 +927,44 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
     return KDA_OK;
 }
 
+kda_status kda_layer_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                                 const void* beta, float* state, const void* xg, const float* rms_w, int32_t N,
+                                 int32_t H, int32_t d, int32_t dtype, void* y, void* stream) {
+    if (!q || !k || !v || !log_alpha || !beta || !state || !xg || !rms_w || !y) return KDA_ERR_NULL;
+    if (N <= 0 || H <= 0 || (int64_t)N * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    if (!head_ok(d, d) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+    const size_t es = esize(dtype);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(state) ||
+        !aligned_to(beta, es) || !aligned_to(xg, 2 * es) || !aligned_to(y, 2 * es) || !aligned_to(rms_w, 4))
+        return KDA_ERR_ALIGN;
+    const size_t NH = (size_t)N * H;
+    const size_t ny = NH * d * es, ns = NH * d * d * 4;
+    const void* ins[7] = {q, k, v, log_alpha, beta, xg, rms_w};
+    const size_t nin[7] = {NH * d * es, NH * d * es, NH * d * es, NH * d * es, NH * es, NH * d * es, (size_t)d * 4};
+    for (int i = 0; i < 7; ++i)
+        if (overlaps(y, ny, ins[i], nin[i]) || overlaps(state, ns, ins[i], nin[i])) return KDA_ERR_ALIAS;
+    if (overlaps(y, ny, state, ns)) return KDA_ERR_ALIAS;
+    DecodeArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.la = log_alpha;
+    a.beta = beta;
+    a.state = state;
+    a.o = nullptr;
+    a.N = N;
+    a.H = H;
+    a.D = d;
+    a.in_f32 = a.gate_f32 = dtype == KDA_F32;
+    a.out_f32 = true;
+    a.epi = true;
+    a.xg = xg;
+    a.rms_w = rms_w;
+    a.y = y;
+    if (launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
 kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* log_alpha,
                                  const void* beta, const float* initial_state, const int32_t* cu_seqlens,
                                  int32_t N, int64_t T_total, int32_t H, int32_t dk, int32_t dv,

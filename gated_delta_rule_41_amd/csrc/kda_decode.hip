@@ -18,18 +18,30 @@
 // column sums (S^T (a*k) and S^T q) are reduced across row groups through LDS.
 // NT = 1024 for d = 128 (measured: 6.04 TB/s at 1024 threads, 5.87 at 256,
 // 5.56 at 512 on 256 x 32 heads); 256 for d = 64.
+//
+// EPI: the layer's epilogue (per-head RMSNorm, output gate; GeekNews "Kimi
+// Linear" summary, section "Configuração do modelo Kimi Linear") on the row o
+// before it leaves: the workgroup holds the whole row, so wave 0 takes its
+// channels as the epilogue kernel's lanes do (lane j: channels PER j ..) and
+// runs the same per-row code, and y is bitwise that of this kernel's fp32 o
+// followed by the epilogue kernel.
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_launch.h"
+#include "kda_layer_util.h"
 
 namespace kda {
 
 template <int D> constexpr int decode_threads() { return D == 128 ? 1024 : 256; }
 
-template <int D, typename TIn, typename TG, bool OUT_F32>
+template <int D, typename TIn, typename TG, bool OUT_F32, bool EPI = false>
 __global__ __launch_bounds__(decode_threads<D>()) void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                      const TIn* __restrict__ v, const TG* __restrict__ la,
                                                      const TG* __restrict__ beta, float* __restrict__ state,
-                                                     void* __restrict__ o, int NH) {
+                                                     void* __restrict__ o, int NH, const TIn* __restrict__ xg,
+                                                     const float* __restrict__ rms_w, TIn* __restrict__ y) {
+    static_assert(!EPI || OUT_F32, "the epilogue reads o in fp32");
     constexpr int CQ = D / 4;        // column quads
     constexpr int R = decode_threads<D>() / CQ;  // row groups
     constexpr int RPT = D / R;       // rows per thread
@@ -85,6 +97,31 @@ __global__ __launch_bounds__(decode_threads<D>()) void decode_kernel(const TIn* 
     __syncthreads();  // everyone has read red[] for the first sum
     red[rg][cq] = po;
     __syncthreads();
+    if constexpr (EPI) {
+        if (tid < 64) {  // wave 0; its lanes cq < CQ hold the row's column quads
+            f32x4_t ot = {0.f, 0.f, 0.f, 0.f};
+            if (tid < CQ) {
+#pragma unroll
+                for (int i = 0; i < R; ++i) ot += red[i][cq];
+            }
+            // lane j takes channels PER j .. PER j + PER - 1 from the quad holding them
+            constexpr int PER = D / 64;
+            const int c0 = PER * tid;
+            float e[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) e[m] = __shfl(ot[m], c0 >> 2);
+            float x[PER], xgv[PER], wc[PER];
+#pragma unroll
+            for (int p = 0; p < PER; ++p) {
+                const int m = (c0 + p) & 3;
+                x[p] = m == 0 ? e[0] : m == 1 ? e[1] : m == 2 ? e[2] : e[3];
+                wc[p] = rms_w[c0 + p];
+            }
+            Pair<TIn, PER>::ld(xg + vec + c0, xgv);
+            epilogue_row<D, TIn>(x, xgv, wc, y + vec + c0);
+        }
+        return;
+    }
     if (rg == 0) {
         f32x4_t ot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -104,14 +141,23 @@ template <int D, typename TIn, typename TG>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     const int NH = a.N * a.H;
     dim3 grid(NH), block(decode_threads<D>());
-    if (a.out_f32)
+    const TIn* xg = static_cast<const TIn*>(a.xg);
+    TIn* y = static_cast<TIn*>(a.y);
+    if (a.epi) {
+        if constexpr (std::is_same<TIn, TG>::value)  // the layer's one dtype (checked by the caller)
+            hipLaunchKernelGGL((decode_kernel<D, TIn, TG, true, true>), grid, block, 0, st, (const TIn*)a.q,
+                               (const TIn*)a.k, (const TIn*)a.v, (const TG*)a.la, (const TG*)a.beta, a.state,
+                               nullptr, NH, xg, a.rms_w, y);
+        else
+            return hipErrorInvalidValue;
+    } else if (a.out_f32)
         hipLaunchKernelGGL((decode_kernel<D, TIn, TG, true>), grid, block, 0, st, (const TIn*)a.q,
                            (const TIn*)a.k, (const TIn*)a.v, (const TG*)a.la, (const TG*)a.beta, a.state,
-                           a.o, NH);
+                           a.o, NH, nullptr, nullptr, nullptr);
     else
         hipLaunchKernelGGL((decode_kernel<D, TIn, TG, false>), grid, block, 0, st, (const TIn*)a.q,
                            (const TIn*)a.k, (const TIn*)a.v, (const TG*)a.la, (const TG*)a.beta, a.state,
-                           a.o, NH);
+                           a.o, NH, nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 

@@ -14,6 +14,11 @@ struct DecodeArgs {
     void* o;
     int N, H, D;
     bool in_f32, gate_f32, out_f32;
+    // the layer epilogue fused in (y in place of o; the inputs' dtype throughout)
+    bool epi = false;
+    const void* xg = nullptr;
+    const float* rms_w = nullptr;
+    void* y = nullptr;
 };
 
 struct SeqMeta;

@@ -101,14 +101,7 @@ __global__ __launch_bounds__(256) void layer_epilogue_kernel(const float* __rest
 #pragma unroll
     for (int j = 0; j < G; ++j) {
         if (r0 + j >= TH) break;
-        float s = 0.f;
-#pragma unroll
-        for (int p = 0; p < PER; ++p) s += x[j][p] * x[j][p];
-        const float r = rsqrtf(wave_sum(s) * (1.f / D) + LAYER_EPS);
-        float out[PER];
-#pragma unroll
-        for (int p = 0; p < PER; ++p) out[p] = x[j][p] * r * wc[p] * sigm(xg[j][p]);
-        Pair<TE, PER>::st(y + (int64_t)(r0 + j) * D + c0, out);
+        epilogue_row<D, TE>(x[j], xg[j], wc, y + (int64_t)(r0 + j) * D + c0);
     }
 }
 

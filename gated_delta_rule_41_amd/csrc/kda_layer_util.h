@@ -82,6 +82,23 @@ struct Pair<TE, 1> {
     static __device__ __forceinline__ void st(TE* p, const float (&x)[1]) { st_out(p, 0, x[0]); }
 };
 
+// The epilogue of one (token, head) row, held as lane j holding channels
+// PER j .. PER j + PER - 1 (PER = D / 64): y = x / sqrt(mean x^2 + eps) * w *
+// sigmoid(xg). Every lane of the wave takes part (the mean is a wave sum).
+template <int D, typename TE>
+__device__ __forceinline__ void epilogue_row(const float (&x)[D / 64], const float (&xg)[D / 64],
+                                             const float (&wc)[D / 64], TE* y) {
+    constexpr int PER = D / 64;
+    float s = 0.f;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) s += x[p] * x[p];
+    const float r = rsqrtf(wave_sum(s) * (1.f / D) + LAYER_EPS);
+    float out[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) out[p] = x[p] * r * wc[p] * sigm(xg[p]);
+    Pair<TE, PER>::st(y, out);
+}
+
 template <int D>
 struct ConvFilters {
     static constexpr int PER = D / 64;

@@ -36,8 +36,9 @@
  *  - the layer around it: kda_layer_prologue, kda_layer_epilogue,
  *    kda_layer_chunk_fwd (the prologue fused into the prefill),
  *    kda_layer_fwd (the whole layer: prologue and epilogue fused into the
- *    prefill), and for decoding kda_layer_conv_state and
- *    kda_layer_decode_prologue;
+ *    prefill), and for decoding kda_layer_conv_state,
+ *    kda_layer_decode_prologue and kda_layer_decode_step (the decode step
+ *    with the epilogue fused in);
  *  - kda_status_str, kda_abi_version.
  *  - Layouts are token-major: q, k, log_alpha [T, H, dk]; v [T, H, dv];
  *    beta [T, H]; o [T, H, dv]; states [N, H, dk, dv] fp32 (dv fastest).
@@ -337,8 +338,9 @@ kda_status kda_layer_conv_state(const void* xq, const void* xk, const void* xv, 
  * kda_layer_prologue for one new token per sequence after the history
  * conv_state (kda_layer_conv_state's layout): the convolution reads the
  * history's three rows, then the new row; the history is then shifted by the
- * new row, in place. With kda_decode_step and kda_layer_epilogue this is the
- * layer's decode step; the results equal those of kda_layer_prologue over the
+ * new row, in place. With kda_decode_step and kda_layer_epilogue (or with
+ * kda_layer_decode_step, which does both in one kernel) this is the layer's
+ * decode step; the results equal those of kda_layer_prologue over the
  * whole sequence at its last row.
  *
  *   xq, xk, xv, xa  [N, H, d] dtype;  xb [N, H] dtype (one token per sequence)
@@ -395,6 +397,28 @@ kda_status kda_layer_chunk_fwd(const void* xq, const void* xk, const void* xv, c
  */
 kda_status kda_layer_epilogue(const float* o, const void* xg, const float* rms_w, int64_t T_total, int32_t H,
                               int32_t dv, int32_t dtype, void* y, void* stream);
+
+/*
+ * The layer's decode step after kda_layer_decode_prologue: kda_decode_step
+ * (fp32 o) and kda_layer_epilogue in one kernel. The workgroup of a (sequence,
+ * head) holds the whole row o, so it normalises and gates it before it leaves:
+ * o never reaches memory, and y is bitwise that of the two calls.
+ *
+ *   q, k, v, log_alpha [N, H, d] dtype; beta [N, H] dtype (one token per
+ *                   sequence, as kda_layer_decode_prologue leaves them)
+ *   state           [N, H, d, d] fp32, updated in place
+ *   xg              [N, H, d] dtype (the output gate's pre-activation)
+ *   rms_w           [d] fp32
+ *   y               [N, H, d] dtype (output)
+ * d is 64 or 128; dtype KDA_BF16 or KDA_F32 for every tensor above but the
+ * state and rms_w. q, k, v, log_alpha and state must be 16-byte aligned, beta
+ * to its element, xg and y to two elements, rms_w to 4 bytes (KDA_ERR_ALIGN).
+ * y and state may not overlap an input or each other (KDA_ERR_ALIAS).
+ * N * H < 2^31. One kernel is enqueued.
+ */
+kda_status kda_layer_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                                 const void* beta, float* state, const void* xg, const float* rms_w, int32_t N,
+                                 int32_t H, int32_t d, int32_t dtype, void* y, void* stream);
 
 /*
  * Bytes of device workspace kda_layer_fwd needs on the current device (host

@@ -33,7 +33,8 @@ def test_library_exports_every_declared_function():
                      "kda_chunk_fwd_noalloc", "kda_chunk_fwd_timed",
                      "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_dplr_chunk_fwd",
                      "kda_dplr_chunk_fwd_workspace_size", "kda_layer_chunk_fwd", "kda_layer_chunk_fwd_workspace_size",
-                     "kda_layer_conv_state", "kda_layer_decode_prologue", "kda_layer_epilogue", "kda_layer_fwd",
+                     "kda_layer_conv_state", "kda_layer_decode_prologue", "kda_layer_decode_step",
+                     "kda_layer_epilogue", "kda_layer_fwd",
                      "kda_layer_fwd_workspace_size", "kda_layer_prologue", "kda_status_str"]
     for nm in names:
         assert hasattr(lib, nm), nm
@@ -459,6 +460,31 @@ def test_layer_decode_validation():
     assert dp_call(xq=y, cs=y + 64) == ALIAS  # the history is written in place
     z = f()
     assert dp_call(cs=z, q=z + 128) == ALIAS
+
+    def ds_call(**over):
+        a = dict(q=f(), k=f(), v=f(), la=f(), beta=f(), st=f(), xg=f(), w=f(), N=3, H=2, d=64, dt=BF16, y=f())
+        a.update(over)
+        return lib.kda_layer_decode_step(*(P(a[x]) for x in ("q", "k", "v", "la", "beta", "st", "xg", "w")),
+                                         a["N"], a["H"], a["d"], a["dt"], P(a["y"]), None)
+
+    assert ds_call(y=None) == NULL
+    assert ds_call(xg=None) == NULL
+    assert ds_call(w=None) == NULL
+    assert ds_call(N=0) == SHAPE
+    assert ds_call(H=-1) == SHAPE
+    assert ds_call(d=96) == UNSUP
+    assert ds_call(dt=7) == UNSUP
+    assert ds_call(q=f(8)) == ALIGN      # 16 bytes
+    assert ds_call(st=f(4)) == ALIGN
+    assert ds_call(xg=f(2)) == ALIGN     # two bf16 elements
+    assert ds_call(y=f(1)) == ALIGN
+    assert ds_call(w=f(2)) == ALIGN      # 4 bytes
+    u = f()
+    assert ds_call(q=u, y=u + 256) == ALIAS
+    w2 = f()
+    assert ds_call(xg=w2, st=w2 + 512) == ALIAS
+    v2 = f()
+    assert ds_call(st=v2, y=v2 + 1024) == ALIAS
 
 
 def test_noalloc_refuses_oversized_and_bad_shapes_on_host():

@@ -233,12 +233,16 @@ def test_layer_decode_continues_prefill():
     q, k, v, la, b = kda.layer_prologue(*pre, c.wq, c.wk, c.wv, c.A_log, c.dt_bias, cu_pre)
     _, state = kda.chunk_fwd(q, k, v, la, b, c.initial_state, cu_pre)
     cs = kda.layer_conv_state(pre[0], pre[1], pre[2], cu_pre)
+    state_f = state.clone()
     ys = []
     for s in range(S):
         step = [x.index_select(0, dec[s]) for x in (c.xq, c.xk, c.xv, c.xa, c.xb, c.xg)]
         qd, kd, vd, lad, bd = kda.layer_decode_prologue(*step[:5], cs, c.wq, c.wk, c.wv, c.A_log, c.dt_bias)
         od = kda.decode_step(qd, kd, vd, lad, bd, state)
         ys.append(kda.layer_epilogue(od, step[5], c.rms_w))
+        # the same step with the epilogue fused into the decode kernel: bitwise equal
+        yf = kda.layer_decode_step(qd, kd, vd, lad, bd, state_f, step[5], c.rms_w)
+        assert torch.equal(yf, ys[-1]) and torch.equal(state_f, state), f"fused decode step {s}"
     torch.cuda.synchronize()
     y_ref, S_ref, _ = ly.layer(c.xq, c.xk, c.xv, c.xa, c.xb, c.xg, c.wq, c.wk, c.wv, c.A_log, c.dt_bias, c.rms_w,
                                host(c.initial_state), host(c.cu_seqlens))
@@ -246,6 +250,38 @@ def test_layer_decode_continues_prefill():
     ey, es = err(torch.stack(ys), rows), err(state, S_ref)
     say(f"[layer] decode after prefill, {S} steps: y {ey:.2e}  final state {es:.2e}")
     assert ey <= 1e-4 and es <= 1e-4
+
+
+@pytest.mark.parametrize("d,dt", [(128, torch.bfloat16), (64, torch.bfloat16), (128, torch.float32),
+                                  (64, torch.float32)])
+def test_layer_decode_step_fused(d, dt):
+    """kda_layer_decode_step (the decode step with the epilogue fused in) on 96
+    sequences x 4 heads after kda_layer_decode_prologue: y and the state bitwise
+    equal to kda_decode_step (fp32 o) followed by kda_layer_epilogue, over three
+    steps in place; y of the first step against the fp64 decode step and layer
+    epilogue (within one bf16 step, or 1e-5 for fp32)."""
+    N, H = 96, 4
+    c = ki.make_layer("prefill-4k", DEV, lengths=[1] * N, H=H, d=d, dtype=dt, s0_std=0.02)
+    st0 = c.initial_state.clone()
+    cs = torch.randn(N, H, 3, 3, d, generator=torch.Generator(device=DEV).manual_seed(11), device=DEV).to(dt)
+    cs_f = cs.clone()
+    s_a, s_b = st0.clone(), st0.clone()
+    for step in range(3):
+        # each step draws new pre-activations from the first step's by a shift of rows
+        xs = [torch.roll(x, step, 0) for x in (c.xq, c.xk, c.xv, c.xa, c.xb, c.xg)]
+        qd, kd, vd, lad, bd = kda.layer_decode_prologue(*xs[:5], cs, c.wq, c.wk, c.wv, c.A_log, c.dt_bias)
+        q2 = kda.layer_decode_prologue(*xs[:5], cs_f, c.wq, c.wk, c.wv, c.A_log, c.dt_bias)
+        assert all(torch.equal(a, b) for a, b in zip((qd, kd, vd, lad, bd), q2))
+        if step == 0:
+            o_ref, _ = oracle.decode_step(qd.cpu(), kd.cpu(), vd.cpu(), lad.cpu(), bd.cpu(), st0.cpu())
+            y_ref = ly.layer_epilogue(np.asarray(o_ref), xs[5].cpu(), c.rms_w.cpu())
+        od = kda.decode_step(qd, kd, vd, lad, bd, s_a)
+        y_two = kda.layer_epilogue(od, xs[5], c.rms_w)
+        y_one = kda.layer_decode_step(qd, kd, vd, lad, bd, s_b, xs[5], c.rms_w)
+        assert y_one.dtype == dt and torch.equal(y_one, y_two) and torch.equal(s_a, s_b), f"step {step}"
+        if step == 0:
+            check_outputs("fused decode step y", [y_one], [y_ref], dt == torch.bfloat16)
+    say(f"[layer] fused decode step d={d} {dt}: bitwise equal to decode step + epilogue over 3 steps")
 
 
 WHOLE_CASES = {
