@@ -242,7 +242,8 @@ __device__ __forceinline__ void warm_chunk(const Ws<typename Pol<F32>::E>& ws, i
 // products at d = 128, too many for one wave's matrix core, so four compute
 // waves share it (each the state's row tiles of one quarter and one 16-row
 // tile of V_new), and the tiles meet in LDS twice per chunk. Waves: 0-3
-// compute, 4-5 producers; every wave executes 1 + 2 nch barriers.
+// compute, 4-5 producers, 6 L2 warm-up; every wave executes 1 + 2 nch
+// barriers.
 //
 // DPLR (the general transition, factors from kda_dplr_prep.hip): the chain is
 // the same with -u = -U' + (-W') h in place of V_new and A-^T in place of
