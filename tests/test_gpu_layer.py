@@ -284,6 +284,29 @@ def test_layer_decode_step_fused(d, dt):
     say(f"[layer] fused decode step d={d} {dt}: bitwise equal to decode step + epilogue over 3 steps")
 
 
+def test_layer_decode_step_fused_decode_256():
+    """The fused decode step at decode-256 size (256 sequences x 32 heads, d = 128,
+    bf16; 8,192 workgroups): y and the states bitwise equal to kda_decode_step
+    followed by kda_layer_epilogue, and y of sampled sequences against the fp64
+    decode step and epilogue."""
+    N, H, d = 256, 32, 128
+    c = ki.make_layer("decode-256", DEV, lengths=[1] * N, H=H, d=d, s0_std=0.02)
+    cs = torch.randn(N, H, 3, 3, d, generator=torch.Generator(device=DEV).manual_seed(4), device=DEV).to(torch.bfloat16)
+    qd, kd, vd, lad, bd = kda.layer_decode_prologue(c.xq, c.xk, c.xv, c.xa, c.xb, cs, c.wq, c.wk, c.wv, c.A_log,
+                                                    c.dt_bias)
+    s0 = c.initial_state
+    s_a, s_b = s0.clone(), s0.clone()
+    y_two = kda.layer_epilogue(kda.decode_step(qd, kd, vd, lad, bd, s_a), c.xg, c.rms_w)
+    y_one = kda.layer_decode_step(qd, kd, vd, lad, bd, s_b, c.xg, c.rms_w)
+    torch.cuda.synchronize()
+    assert torch.equal(y_one, y_two) and torch.equal(s_a, s_b)
+    seqs = [0, 97, 255]
+    sel = [x[seqs] for x in (qd, kd, vd, lad, bd)]
+    o_ref, _ = oracle.decode_step(*sel, s0[seqs])
+    y_ref = ly.layer_epilogue(np.asarray(o_ref), c.xg[seqs].cpu(), c.rms_w.cpu())
+    check_outputs("fused decode step y (decode-256, sequences 0, 97, 255)", [y_one[seqs]], [y_ref], True)
+
+
 WHOLE_CASES = {
     # N H a multiple of 8 and N H d/16 workgroups within the CU count: the fused epilogue
     "prefill-4k": {},
