@@ -1,0 +1,117 @@
+"""A seeded sweep of valid configurations against the oracles: the prefill
+(kda_chunk_fwd), the decode step (kda_decode_step) and the backward
+(kda_chunk_bwd), each on random draws of the sequence count and lengths (empty
+sequences, one token, the chunk edges 63/64/65 and 127/128/129, and lengths up
+to 300), the head count, the head size, the input and gate dtypes (each bf16 or
+fp32, mixed too), the gate regime (the workloads' fast decay, slow decay, or
+in between), the initial state (absent or N(0, 0.02)) and the output dtype.
+The draws come from fixed seeds, so every run checks the same cases; each case
+prints its draw before it runs.
+
+Bars: 1e-4 with fp32 inputs and 2e-2 with bf16 inputs (max-abs error over the
+oracle's RMS, for o and the final state); a bf16 o must equal the fp32 o
+rounded to bf16; the backward's six gradients 1e-3."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+import oracle
+from oracle import backward as bw
+from parity import err, kda, say, tol_for
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+EDGE = [0, 1, 2, 63, 64, 65, 127, 128, 129]
+
+
+def draw(seed):
+    rng = np.random.default_rng([41, seed])
+    N = int(rng.integers(1, 6))
+    lengths = [int(rng.choice(EDGE)) if rng.random() < 0.5 else int(rng.integers(3, 301)) for _ in range(N)]
+    if sum(lengths) == 0:
+        lengths[0] = 65
+    return dict(lengths=lengths, H=int(rng.integers(1, 5)), d=int(rng.choice([64, 128])),
+                in_dt=[torch.bfloat16, torch.float32][int(rng.integers(0, 2))],
+                gate_dt=[torch.bfloat16, torch.float32][int(rng.integers(0, 2))],
+                shift=float(rng.choice([2.0, 0.0, -2.0])), s0=float(rng.choice([0.0, 0.02])),
+                packed=bool(N > 1 or rng.random() < 0.5))
+
+
+def make_case(p, seed):
+    c = ki.make_prefill("prefill-4k", DEV, lengths=p["lengths"], H=p["H"], dk=p["d"], dv=p["d"], dtype=p["in_dt"],
+                        gate_shift=p["shift"], s0_std=p["s0"], seed=1000 + seed, packed=p["packed"])
+    # the gates in their own dtype: rounded once from the drawn values
+    c.log_alpha = c.log_alpha.float().to(p["gate_dt"]).contiguous()
+    c.beta = c.beta.float().to(p["gate_dt"]).contiguous()
+    return c
+
+
+def describe(p):
+    return (f"lengths={p['lengths']} H={p['H']} d={p['d']} in={str(p['in_dt'])[6:]} gate={str(p['gate_dt'])[6:]} "
+            f"shift={p['shift']} s0={p['s0']} packed={p['packed']}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_prefill_sweep(seed):
+    p = draw(seed)
+    say(f"[sweep prefill {seed}] {describe(p)}")
+    c = make_case(p, seed)
+    o, S = kda.chunk_fwd(c.q, c.k, c.v, c.log_alpha, c.beta, c.initial_state, c.cu_seqlens)
+    o16, S16 = kda.chunk_fwd(c.q, c.k, c.v, c.log_alpha, c.beta, c.initial_state, c.cu_seqlens,
+                             out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    cu = None if c.cu_seqlens is None else c.cu_seqlens.cpu()
+    o_ref, S_ref, _ = oracle.recurrence(c.q, c.k, c.v, c.log_alpha, c.beta, c.initial_state, cu)
+    tol = tol_for(p["in_dt"])
+    eo = err(o, o_ref) if o.numel() else 0.0
+    es = err(S, S_ref)
+    say(f"    err(o)={eo:.3e} err(S)={es:.3e} tol={tol:.0e}")
+    assert eo <= tol and es <= tol
+    assert torch.equal(o16, o.to(torch.bfloat16)) and torch.equal(S16, S)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_decode_sweep(seed):
+    """Two decode steps in place, each against the oracle's step from the
+    previous oracle state."""
+    rng = np.random.default_rng([42, seed])
+    N, H, d = int(rng.integers(1, 40)), int(rng.integers(1, 9)), int(rng.choice([64, 128]))
+    in_dt = [torch.bfloat16, torch.float32][int(rng.integers(0, 2))]
+    gate_dt = [torch.bfloat16, torch.float32][int(rng.integers(0, 2))]
+    say(f"[sweep decode {seed}] N={N} H={H} d={d} in={in_dt} gate={gate_dt}")
+    dec = ki.make_decode(N, H, d, 2, DEV, dtype=in_dt, seed=100 + seed)
+    state = dec["state"].clone()
+    S_ref = dec["state"].cpu().double()
+    tol = tol_for(in_dt)
+    for s in range(2):
+        la, b = (dec[n][s].float().to(gate_dt).contiguous() for n in ("log_alpha", "beta"))
+        o = kda.decode_step(dec["q"][s], dec["k"][s], dec["v"][s], la, b, state)
+        torch.cuda.synchronize()
+        o_ref, S_next = oracle.decode_step(dec["q"][s], dec["k"][s], dec["v"][s], la, b, S_ref)
+        eo, es = err(o, o_ref), err(state, S_next)
+        say(f"    step {s}: err(o)={eo:.3e} err(S)={es:.3e} tol={tol:.0e}")
+        assert eo <= tol and es <= tol
+        S_ref = torch.from_numpy(np.asarray(S_next))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_backward_sweep(seed):
+    p = draw(100 + seed)
+    p["lengths"] = [min(x, 200) for x in p["lengths"]][:3]  # the gradient oracle's size
+    if sum(p["lengths"]) == 0:
+        p["lengths"][0] = 65
+    p["packed"] = p["packed"] or len(p["lengths"]) > 1
+    say(f"[sweep backward {seed}] {describe(p)}")
+    c = make_case(p, 100 + seed)
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    d_o = torch.randn(c.T_total, c.H, c.dv, generator=g, device=DEV)
+    d_fin = torch.randn(c.N, c.H, c.dk, c.dv, generator=g, device=DEV) * 0.1
+    got = kda.chunk_bwd(c.q, c.k, c.v, c.log_alpha, c.beta, d_o, c.initial_state, c.cu_seqlens, d_fin)
+    torch.cuda.synchronize()
+    cu = None if c.cu_seqlens is None else c.cu_seqlens.cpu()
+    ref = bw.recurrence_grads(c.q, c.k, c.v, c.log_alpha, c.beta, c.initial_state, cu, d_o.cpu(), d_fin.cpu())
+    errs = {nm: err(got[nm], ref[nm]) for nm in ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dinitial_state")}
+    say("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= 1e-3}
+    assert not bad, bad
