@@ -1,16 +1,20 @@
 """A seeded sweep of valid configurations against the oracles: the prefill
-(kda_chunk_fwd), the decode step (kda_decode_step) and the backward
-(kda_chunk_bwd), each on random draws of the sequence count and lengths (empty
-sequences, one token, the chunk edges 63/64/65 and 127/128/129, and lengths up
-to 300), the head count, the head size, the input and gate dtypes (each bf16 or
-fp32, mixed too), the gate regime (the workloads' fast decay, slow decay, or
-in between), the initial state (absent or N(0, 0.02)) and the output dtype.
+(kda_chunk_fwd), the decode step (kda_decode_step), the backward
+(kda_chunk_bwd) and the one-call layer (kda_layer_fwd), each on random draws
+of the sequence count and lengths (empty sequences, one token, the chunk edges
+63/64/65 and 127/128/129, and lengths up to 300), the head count, the head
+size, the input and gate dtypes (each bf16 or fp32, mixed too), the gate
+regime (the workloads' fast decay, slow decay, or in between), the initial
+state (absent or N(0, 0.02)) and the output dtype.
 The draws come from fixed seeds, so every run checks the same cases; each case
 prints its draw before it runs.
 
 Bars: 1e-4 with fp32 inputs and 2e-2 with bf16 inputs (max-abs error over the
 oracle's RMS, for o and the final state); a bf16 o must equal the fp32 o
-rounded to bf16; the backward's six gradients 1e-3."""
+rounded to bf16; the backward's six gradients 1e-3; the one-call layer's
+final states bitwise those of kda_layer_chunk_fwd and its y within one bf16
+step of the fp64 epilogue of the operator's own o (bitwise the epilogue
+kernel's where the call falls back to it)."""
 import numpy as np
 import pytest
 import torch
@@ -18,6 +22,7 @@ import torch
 import kda_inputs as ki
 import oracle
 from oracle import backward as bw
+from oracle import layer as ly
 from parity import err, kda, say, tol_for
 
 pytestmark = pytest.mark.gpu
@@ -115,3 +120,44 @@ def test_backward_sweep(seed):
     say("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= 1e-3}
     assert not bad, bad
+
+
+def bf16_steps(x, ref) -> float:
+    """Largest |x - ref| in units of the bf16 spacing at ref, plus an fp32
+    floor of 1e-5 rms(ref)."""
+    x = x.detach().double().cpu().numpy()
+    ref = np.asarray(ref, dtype=np.float64)
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 1e-300)))
+    allow = 2.0 ** (e - 7) + 1e-5 * np.sqrt(np.mean(ref * ref))
+    return float(np.max(np.abs(x - ref) / allow))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_layer_sweep(seed):
+    """kda_layer_fwd over random shapes; N H a multiple of 8 (within the CU
+    count) takes the epilogue inside the recursion, any other the epilogue kernel."""
+    rng = np.random.default_rng([43, seed])
+    N = int(rng.integers(1, 5))
+    lengths = [int(rng.choice(EDGE)) if rng.random() < 0.4 else int(rng.integers(3, 301)) for _ in range(N)]
+    if sum(lengths) == 0:
+        lengths[0] = 64
+    H = int(rng.choice([1, 2, 3, 4, 8])) if rng.random() < 0.6 else int(8 // N if 8 % N == 0 else 8)
+    d = int(rng.choice([64, 128]))
+    s0 = float(rng.choice([0.0, 0.02]))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    fused = (N * H) % 8 == 0 and N * H * (d // 16) <= cus
+    say(f"[sweep layer {seed}] lengths={lengths} H={H} d={d} s0={s0} "
+        f"{'epilogue in the recursion' if fused else 'epilogue kernel'}")
+    c = ki.make_layer("prefill-4k", DEV, lengths=lengths, H=H, d=d, s0_std=s0, seed=200 + seed)
+    o, S_ref = kda.layer_chunk_fwd(c.xq, c.xk, c.xv, c.xa, c.xb, c.wq, c.wk, c.wv, c.A_log, c.dt_bias,
+                                   c.initial_state, c.cu_seqlens)
+    y_two = kda.layer_epilogue(o, c.xg, c.rms_w)
+    y, S = kda.layer_fwd(c.xq, c.xk, c.xv, c.xa, c.xb, c.xg, c.wq, c.wk, c.wv, c.A_log, c.dt_bias, c.rms_w,
+                         c.initial_state, c.cu_seqlens)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S_ref)
+    steps = bf16_steps(y, ly.layer_epilogue(o.cpu(), c.xg.cpu(), c.rms_w.cpu()))
+    say(f"    y within {steps:.2f} bf16 steps of the fp64 epilogue of o")
+    assert steps <= 1.0
+    if not fused:
+        assert torch.equal(y, y_two)
