@@ -1,6 +1,7 @@
 """A seeded sweep of valid configurations against the oracles: the prefill
 (kda_chunk_fwd), the decode step (kda_decode_step), the backward
-(kda_chunk_bwd) and the one-call layer (kda_layer_fwd), each on random draws
+(kda_chunk_bwd), the one-call layer (kda_layer_fwd) and the general-DPLR
+comparison operator (kda_dplr_chunk_fwd), each on random draws
 of the sequence count and lengths (empty sequences, one token, the chunk edges
 63/64/65 and 127/128/129, and lengths up to 300), the head count, the head
 size, the input and gate dtypes (each bf16 or fp32, mixed too), the gate
@@ -14,7 +15,8 @@ oracle's RMS, for o and the final state); a bf16 o must equal the fp32 o
 rounded to bf16; the backward's six gradients 1e-3; the one-call layer's
 final states bitwise those of kda_layer_chunk_fwd and its y within one bf16
 step of the fp64 epilogue of the operator's own o (bitwise the epilogue
-kernel's where the call falls back to it)."""
+kernel's where the call falls back to it); the DPLR operator (bf16 inputs)
+2e-2 against its own recurrence."""
 import numpy as np
 import pytest
 import torch
@@ -161,3 +163,31 @@ def test_layer_sweep(seed):
     assert steps <= 1.0
     if not fused:
         assert torch.equal(y, y_two)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_dplr_sweep(seed):
+    """kda_dplr_chunk_fwd (bf16 inputs; gates bf16 or fp32; fp32 or bf16 o)
+    against the oracle's DPLR recurrence."""
+    rng = np.random.default_rng([44, seed])
+    N = int(rng.integers(1, 5))
+    lengths = [int(rng.choice(EDGE)) if rng.random() < 0.5 else int(rng.integers(3, 301)) for _ in range(N)]
+    if sum(lengths) == 0:
+        lengths[0] = 65
+    H, d = int(rng.integers(1, 5)), int(rng.choice([64, 128]))
+    gate_dt = [torch.bfloat16, torch.float32][int(rng.integers(0, 2))]
+    out_dt = [torch.float32, torch.bfloat16][int(rng.integers(0, 2))]
+    say(f"[sweep dplr {seed}] lengths={lengths} H={H} d={d} gates={gate_dt} out={out_dt}")
+    c = ki.make_dplr("prefill-4k", DEV, lengths=lengths, H=H, dk=d, dv=d, seed=300 + seed, s0_std=0.02)
+    c.log_alpha = c.log_alpha.float().to(gate_dt).contiguous()
+    o, S = kda.dplr_chunk_fwd(c.q, c.k, c.v, c.a, c.b, c.log_alpha, c.initial_state, c.cu_seqlens)
+    torch.cuda.synchronize()
+    cu = None if c.cu_seqlens is None else c.cu_seqlens.cpu()
+    o_ref, S_ref = oracle.dplr_recurrence(c.q, c.k, c.v, c.a, c.b, c.log_alpha, c.initial_state, cu)
+    eo, es = err(o, o_ref), err(S, S_ref)
+    say(f"    err(o)={eo:.3e} err(S)={es:.3e} tol=2e-02")
+    assert eo <= 2e-2 and es <= 2e-2
+    if out_dt == torch.bfloat16:  # the fp32 o rounded once
+        o16, S16 = kda.dplr_chunk_fwd(c.q, c.k, c.v, c.a, c.b, c.log_alpha, c.initial_state, c.cu_seqlens,
+                                      out_dtype=out_dt)
+        assert torch.equal(o16, o.to(torch.bfloat16)) and torch.equal(S16, S)
