@@ -179,11 +179,14 @@ __device__ __forceinline__ void own_store(float* p, int t0, int L, int H, int h,
 // The state-gradient recursion's per-chunk operands for chunk slot gc:
 // U := A_qk^T dO (accumulator tiles [dv/16][4][64 lanes][4]) and the added term
 // P = Q+^T dO ([dv/16][dk/16][64 lanes][4]). Wave w owns value columns
-// 16 w .. 16 w + 15.
+// 16 w .. 16 w + 15. The chunk's rows pass through LDS in two halves of 32
+// (the second half's loads in flight during the first half's products), so a
+// workgroup holds 42.5 KiB and three fit on a CU; the products still run over
+// the rows in order, so the result is that of one 64-row pass.
 template <int D>
 struct BwdPrepSmem {
-    static constexpr int RS = D + 4, SQS = 68;
-    static constexpr int BYTES = (2 * 64 * RS + 64 * SQS) * 4;
+    static constexpr int RS = D + 4, SQS = 68, RH = 32;  // row strides; rows per half
+    static constexpr int BYTES = (2 * RH * RS + RH * SQS) * 4;
 };
 
 template <int D>
@@ -191,42 +194,46 @@ __global__ __launch_bounds__(4 * D) void bwd_prep_kernel(const SeqMeta* __restri
                                                          int g0, Ws<float> f, Ws<float> b,
                                                          const float* __restrict__ d_o) {
     constexpr int NT = D / 16, NTH = 4 * D, RS = BwdPrepSmem<D>::RS, SQS = BwdPrepSmem<D>::SQS;
-    constexpr int NQ = 64 * D / 4 / NTH;      // float4 per thread of a [64][D] array (= 4)
-    constexpr int NA = 64 * 64 / 4 / NTH;     // ... of a [64][64] array (1 or 2)
+    constexpr int RH = BwdPrepSmem<D>::RH;
+    constexpr int NQ = RH * D / 4 / NTH;      // float4 per thread of a [32][D] half (= 2)
+    constexpr int NA = RH * 64 / 4 / NTH;     // ... of a [32][64] half (1 or 2)
     extern __shared__ __align__(16) float sm[];
-    float* dO = sm;                // [64][RS]
-    float* Qp = dO + 64 * RS;      // [64][RS], channels in natural order
-    float* Aq = Qp + 64 * RS;      // [64][SQS] A_qk
+    float* dO = sm;                // [32][RS]
+    float* Qp = dO + RH * RS;      // [32][RS], channels in natural order
+    float* Aq = Qp + RH * RS;      // [32][SQS] rows of A_qk
     const int lc = blockIdx.x / H, h = blockIdx.x - lc * H;  // slot g0 + lc, workspace slot lc
     ChunkLoc loc;
     if (!locate_chunk(tab, N, T, g0 + lc, loc)) return;
     const int64_t src = (int64_t)lc * H + h;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, n = l & 15;
-    // every load of the stage first, then the LDS stores
     f32x4_t xo[NQ], xq[NQ], xa[NA];
+    auto load_half = [&](int hf) {  // every load of the half, into registers
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-        const int e = tid + NTH * m, r = e / (D / 4), c4 = 4 * (e - r * (D / 4));
-        xo[m] = r < loc.L ? *reinterpret_cast<const f32x4_t*>(d_o + ((int64_t)(loc.t0 + r) * H + h) * D + c4)
-                          : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        xq[m] = *reinterpret_cast<const f32x4_t*>(f.qp + src * 64 * D + 4 * e);
-    }
+        for (int m = 0; m < NQ; ++m) {
+            const int e = tid + NTH * m, r = RH * hf + e / (D / 4), c4 = 4 * (e - (e / (D / 4)) * (D / 4));
+            xo[m] = r < loc.L ? *reinterpret_cast<const f32x4_t*>(d_o + ((int64_t)(loc.t0 + r) * H + h) * D + c4)
+                              : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            xq[m] = *reinterpret_cast<const f32x4_t*>(f.qp + src * 64 * D + (int64_t)RH * D * hf + 4 * e);
+        }
 #pragma unroll
-    for (int m = 0; m < NA; ++m) xa[m] = *reinterpret_cast<const f32x4_t*>(f.aqk + src * 64 * 64 + 4 * (tid + NTH * m));
+        for (int m = 0; m < NA; ++m)
+            xa[m] = *reinterpret_cast<const f32x4_t*>(f.aqk + src * 64 * 64 + RH * 64 * hf + 4 * (tid + NTH * m));
+    };
+    auto store_half = [&]() {
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-        const int e = tid + NTH * m, r = e / (D / 4), c4 = 4 * (e - r * (D / 4));
-        *reinterpret_cast<f32x4_t*>(dO + r * RS + c4) = xo[m];
+        for (int m = 0; m < NQ; ++m) {
+            const int e = tid + NTH * m, r = e / (D / 4), c4 = 4 * (e - r * (D / 4));
+            *reinterpret_cast<f32x4_t*>(dO + r * RS + c4) = xo[m];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Qp[r * RS + split_chan(c4 + j)] = xq[m][j];
-    }
+            for (int j = 0; j < 4; ++j) Qp[r * RS + split_chan(c4 + j)] = xq[m][j];
+        }
 #pragma unroll
-    for (int m = 0; m < NA; ++m) {
-        const int e = tid + NTH * m, r = e >> 4, p = 4 * (e & 15);
+        for (int m = 0; m < NA; ++m) {
+            const int e = tid + NTH * m, r = e >> 4, p = 4 * (e & 15);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Aq[r * SQS + split_chan(p + j)] = xa[m][j];
-    }
-    __syncthreads();
+            for (int j = 0; j < 4; ++j) Aq[r * SQS + split_chan(p + j)] = xa[m][j];
+        }
+    };
     const int j0 = 16 * w;
     // P[c][j] = sum_r Q+[r][c] dO[r][j]; U[r][j] = sum_{i >= r} A_qk[i][r] dO[i][j]
     f32x4_t accP[NT], accU[4];
@@ -234,16 +241,28 @@ __global__ __launch_bounds__(4 * D) void bwd_prep_kernel(const SeqMeta* __restri
     for (int ct = 0; ct < NT; ++ct) accP[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int R = 0; R < 4; ++R) accU[R] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // rows 4 kk + G of the chunk, kk in [8 hf, 8 hf + 8), from the half in LDS
+    auto products = [&](int hf) {
 #pragma unroll 4
-    for (int kk = 0; kk < 16; ++kk) {
-        const int r = 4 * kk + G;  // k index of this lane group
-        const float bo = dO[r * RS + j0 + n];
+        for (int k8 = 0; k8 < 8; ++k8) {
+            const int kk = 8 * hf + k8, r = 4 * k8 + G;  // r: the row inside the half
+            const float bo = dO[r * RS + j0 + n];
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) accP[ct] = mfma4(Qp[r * RS + 16 * ct + n], bo, accP[ct]);
+            for (int ct = 0; ct < NT; ++ct) accP[ct] = mfma4(Qp[r * RS + 16 * ct + n], bo, accP[ct]);
 #pragma unroll
-        for (int R = 0; R < 4; ++R)
-            if (R <= (kk >> 2)) accU[R] = mfma4(Aq[r * SQS + 16 * R + n], bo, accU[R]);
-    }
+            for (int R = 0; R < 4; ++R)
+                if (R <= (kk >> 2)) accU[R] = mfma4(Aq[r * SQS + 16 * R + n], bo, accU[R]);
+        }
+    };
+    load_half(0);
+    store_half();
+    __syncthreads();
+    load_half(1);
+    products(0);
+    __syncthreads();  // the first half is read
+    store_half();
+    __syncthreads();
+    products(1);
     float* pb = const_cast<float*>(b.pb) + src * D * D;
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) *reinterpret_cast<f32x4_t*>(pb + ((w * NT + ct) * 64 + l) * 4) = accP[ct];
