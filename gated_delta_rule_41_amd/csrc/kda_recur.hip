@@ -666,6 +666,7 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 448) void recur_kernel
         // ---------------- L2 warm-up wave of the fp32 chain: during chunk c, this
         // slab's share of chunk c + AHEAD's -W and K-^T lines (one load per lane)
         // and its own U and gamma lines, so that the producers' DMA hits the L2
+        // (ADDP: also its added term's lines, which the compute waves load)
         char* wdst = ring + RING * PL::SLOT + PL::XCH;
         constexpr int LW = PL::FB / 128, LPER = 2 * LW / NT, LU = PL::UB / 128, LG = PL::GB / 128;
         static_assert(LPER <= 64 && LU + LG <= 64, "one warm-up load per lane and part");
@@ -681,6 +682,14 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 448) void recur_kernel
                                     : reinterpret_cast<const char*>(ws.gam + chh * D) + (m - LU) * 128;
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)pu,
                                              (__attribute__((address_space(3))) void*)wdst, 4, 0, 0);
+            if constexpr (ADDP) {
+                constexpr int LP = NT * 64 * 4 * 4 / 128;  // lines of this slab's added term
+                static_assert(LP <= 64, "one warm-up load per lane");
+                const char* pp = reinterpret_cast<const char*>(ws.pb + chh * D * D + (int64_t)ct * NT * 64 * 4) +
+                                 (l < LP ? l : 0) * 128;
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)pp,
+                                                 (__attribute__((address_space(3))) void*)wdst, 4, 0, 0);
+            }
         };
         const int pre = nch < PL::AHEAD ? nch : PL::AHEAD;
         for (int c = 0; c < pre; ++c) warm(c);
