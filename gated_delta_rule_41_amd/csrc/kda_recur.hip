@@ -838,14 +838,14 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 448) void recur_kernel
 #pragma unroll
             for (int tt = 0; tt < TH; ++tt) {
                 const int t = TH * q + tt;
-                __builtin_nontemporal_store(S[tt], reinterpret_cast<f32x4_t*>(hp + ((t >> 1) * 64 + l) * 8 + (t & 1) * 4));
+                *reinterpret_cast<f32x4_t*>(hp + ((t >> 1) * 64 + l) * 8 + (t & 1) * 4) = S[tt];
             }
 #pragma unroll
             for (int s = 0; s < NS; ++s) P::mma(V, wfr[s], sb[s]);
             XV[q * 64 + l] = V;
             // V_new out: this wave's row tile q, stored as h_n's tiles above
             E* vp = ws.vn + chh * 64 * D + (int64_t)ct * 2 * 64 * 8;
-            __builtin_nontemporal_store(V, reinterpret_cast<f32x4_t*>(vp + ((q >> 1) * 64 + l) * 8 + (q & 1) * 4));
+            *reinterpret_cast<f32x4_t*>(vp + ((q >> 1) * 64 + l) * 8 + (q & 1) * 4) = V;
             // this wave's K-^T fragments and gamma while the other tiles land
             Frag kf[TH][2];
 #pragma unroll
