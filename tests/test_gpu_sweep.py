@@ -1,7 +1,8 @@
 """A seeded sweep of valid configurations against the oracles: the prefill
 (kda_chunk_fwd), the decode step (kda_decode_step), the backward
-(kda_chunk_bwd), the one-call layer (kda_layer_fwd) and the general-DPLR
-comparison operator (kda_dplr_chunk_fwd), each on random draws
+(kda_chunk_bwd), the one-call layer (kda_layer_fwd), the layer's own kernels
+(prologue, epilogue, convolution history, one-token prologue) and the
+general-DPLR comparison operator (kda_dplr_chunk_fwd), each on random draws
 of the sequence count and lengths (empty sequences, one token, the chunk edges
 63/64/65 and 127/128/129, and lengths up to 300), the head count, the head
 size, the input and gate dtypes (each bf16 or fp32, mixed too), the gate
@@ -15,8 +16,10 @@ oracle's RMS, for o and the final state); a bf16 o must equal the fp32 o
 rounded to bf16; the backward's six gradients 1e-3; the one-call layer's
 final states bitwise those of kda_layer_chunk_fwd and its y within one bf16
 step of the fp64 epilogue of the operator's own o (bitwise the epilogue
-kernel's where the call falls back to it); the DPLR operator (bf16 inputs)
-2e-2 against its own recurrence."""
+kernel's where the call falls back to it); the layer's kernels within one
+bf16 step (bf16) or 1e-5 of the RMS (fp32) of the fp64 layer oracle, the
+histories exactly; the DPLR operator (bf16 inputs) 2e-2 against its own
+recurrence."""
 import numpy as np
 import pytest
 import torch
@@ -191,3 +194,53 @@ def test_dplr_sweep(seed):
         o16, S16 = kda.dplr_chunk_fwd(c.q, c.k, c.v, c.a, c.b, c.log_alpha, c.initial_state, c.cu_seqlens,
                                       out_dtype=out_dt)
         assert torch.equal(o16, o.to(torch.bfloat16)) and torch.equal(S16, S)
+
+
+def close_to(got, ref, bf16, label):
+    if bf16:
+        worst = max(bf16_steps(g, r) for g, r in zip(got, ref))
+        say(f"    {label}: within {worst:.2f} bf16 steps")
+        assert worst <= 1.0
+    else:
+        worst = max(err(g, r) for g, r in zip(got, ref))
+        say(f"    {label}: {worst:.2e} of the RMS")
+        assert worst <= 1e-5
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_layer_kernels_sweep(seed):
+    """The layer's prologue, epilogue, convolution history and one-token
+    prologue over random packed lengths (0-3 tokens, the 16-token tile edges, up
+    to 300), head counts, head sizes and dtypes."""
+    rng = np.random.default_rng([45, seed])
+    N = int(rng.integers(1, 7))
+    edges = [0, 1, 2, 3, 15, 16, 17, 63, 64, 65]
+    lengths = [int(rng.choice(edges)) if rng.random() < 0.5 else int(rng.integers(4, 301)) for _ in range(N)]
+    if sum(lengths) == 0:
+        lengths[0] = 17
+    H, d = int(rng.integers(1, 7)), int(rng.choice([64, 128]))
+    dt = [torch.bfloat16, torch.float32][int(rng.integers(0, 2))]
+    bf = dt == torch.bfloat16
+    say(f"[sweep layer kernels {seed}] lengths={lengths} H={H} d={d} {dt}")
+    c = ki.make_layer("varlen-16", DEV, lengths=lengths, H=H, d=d, dtype=dt, seed=400 + seed, packed=True)
+    cu = c.cu_seqlens.cpu()
+    got = kda.layer_prologue(c.xq, c.xk, c.xv, c.xa, c.xb, c.wq, c.wk, c.wv, c.A_log, c.dt_bias, c.cu_seqlens)
+    torch.cuda.synchronize()
+    ref = ly.layer_prologue(c.xq, c.xk, c.xv, c.xa, c.xb, c.wq, c.wk, c.wv, c.A_log, c.dt_bias, cu)
+    close_to(got, ref, bf, "prologue q, k, v, log_alpha, beta")
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    o = torch.randn(c.T_total, H, d, generator=g, device=DEV) * float(rng.choice([0.01, 1.0, 30.0]))
+    y = kda.layer_epilogue(o, c.xg, c.rms_w)
+    torch.cuda.synchronize()
+    close_to([y], [ly.layer_epilogue(o.cpu(), c.xg.cpu(), c.rms_w.cpu())], bf, "epilogue y")
+    cs = kda.layer_conv_state(c.xq, c.xk, c.xv, c.cu_seqlens)
+    torch.cuda.synchronize()
+    assert torch.equal(cs.cpu(), torch.from_numpy(ly.conv_state(c.xq, c.xk, c.xv, cu)).to(dt))
+    new = [torch.randn(N, H, d, generator=g, device=DEV).to(dt) for _ in range(4)]
+    xb = torch.randn(N, H, generator=g, device=DEV).to(dt)
+    cs_before = cs.cpu()
+    got = kda.layer_decode_prologue(*new, xb, cs, c.wq, c.wk, c.wv, c.A_log, c.dt_bias)
+    torch.cuda.synchronize()
+    ref = ly.layer_decode_prologue(*new, xb, cs_before, c.wq, c.wk, c.wv, c.A_log, c.dt_bias)
+    close_to(got, ref[:5], bf, "decode prologue")
+    assert torch.equal(cs.cpu(), torch.from_numpy(ref[5]).to(dt))
