@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdlib>
 #include <mutex>
 
 namespace kda {
@@ -667,6 +668,18 @@ static size_t layer_epi_bytes(int64_t NC, int64_t T, int H, int d, bool fused) {
     return fused ? align_up((size_t)NC * H * (d / 16) * 64 * 4, 256) : align_up((size_t)T * H * d * 4, 256);
 }
 
+// The fused epilogue's bound on re-reads before a wait gives up: the default,
+// or KDA_EPI_SPIN_MAX from the environment (a non-negative integer; read at
+// each call), which tests set to 0 to take the give-up path.
+static int epi_spin_max() {
+    const char* e = std::getenv("KDA_EPI_SPIN_MAX");
+    if (!e || !*e) return EPI_SPIN_DEFAULT;
+    char* end = nullptr;
+    const long v = std::strtol(e, &end, 10);
+    if (*end != '\0' || v < 0 || v > (1L << 30)) return EPI_SPIN_DEFAULT;
+    return (int)v;
+}
+
 static kda_status layer_fwd_impl(const void* xq, const void* xk, const void* xv, const void* xa, const void* xb,
                                  const float* wq, const float* wk, const float* wv, const float* A_log,
                                  const float* dt_bias, const float* initial_state, const int32_t* cu_seqlens,
@@ -753,6 +766,7 @@ static kda_status layer_fwd_impl(const void* xq, const void* xk, const void* xv,
         a.o = nullptr;
         a.xg = ep->xg, a.rms_w = ep->rms_w, a.y = ep->y;
         a.epi_part = reinterpret_cast<float*>(w + wlayer);
+        a.epi_spin_max = epi_spin_max();
     } else if (ep) {
         a.o = w + wlayer;  // the operator's o, then the epilogue kernel
     }

@@ -38,6 +38,10 @@ struct Piece {
     float* cout = nullptr;
 };
 
+// The fused epilogue's default bound on re-reads of another slab's partial
+// sums before a wait gives up (some tens of ms).
+constexpr int EPI_SPIN_DEFAULT = 1 << 16;
+
 struct ChunkArgs {
     const void *q, *k, *v, *la, *beta;
     const float* s0;        // may be null
@@ -77,6 +81,7 @@ struct ChunkArgs {
     const float* rms_w = nullptr;
     void* y = nullptr;
     float* epi_part = nullptr;
+    int epi_spin_max = EPI_SPIN_DEFAULT;  // the fused epilogue's bounded wait (re-reads)
     Piece piece;
     int slots() const { return piece.g1 > 0 ? piece.g1 - piece.g0 : NC; }  // chunk slots launched
 };

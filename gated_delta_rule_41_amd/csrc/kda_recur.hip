@@ -270,14 +270,15 @@ struct EpiArgs {
     const float* rms_w;  // [dv]
     uint16_t* y;         // [T, H, dv] bf16
     float* part;         // [chunk-head][dv/16][64] fp32, -1 before the launch
+    // Re-reads of a chunk's partial sums before the wait gives up (each an L2
+    // round trip and a short sleep; EPI_SPIN_DEFAULT, 65,536, is some tens of ms
+    // in all); a wave that gave up once waits no more, and the rows of every
+    // chunk it has not normalised are stored as NaN, so a launch whose
+    // workgroups cannot meet still ends. The caller runs this path only when
+    // every workgroup of the launch fits on the GPU at once, where the slabs of
+    // a unit advance together. 0 makes every wait give up at once.
+    int spin_max;
 };
-// Re-reads of a chunk's partial sums before the wait gives up (each an L2 round
-// trip and a short sleep, some tens of ms in all); a wave that gave up once
-// waits no more, and the rows of every chunk it has not normalised are stored
-// as NaN, so a launch whose workgroups cannot meet still ends. The caller runs
-// this path only when every workgroup of the launch fits on the GPU at once,
-// where the slabs of a unit advance together.
-constexpr int EPI_SPIN_MAX = 1 << 16;
 
 // The value lane l ^ 16 (l ^ 32) of the wave holds, by gfx950's lane swaps: with
 // both operands x, permlane16_swap leaves each odd row of its first result
@@ -530,13 +531,14 @@ __global__ __launch_bounds__(FUSED ? (DPLR ? 448 : 384) : 448) void recur_kernel
         };
         // until every slab's sums of chunk c are in pv (re-read while not)
         auto ensure_in = [&](int c, float (&pv)[4][2]) {
-            int it = epi_gave_up ? EPI_SPIN_MAX : 0;
-            while (it < EPI_SPIN_MAX && !all_in(pv)) {
+            const int smax = ep.spin_max;
+            int it = epi_gave_up ? smax : 0;
+            while (it < smax && !all_in(pv)) {
                 __builtin_amdgcn_s_sleep(1);
                 load_parts(c, pv);
                 ++it;
             }
-            if (it >= EPI_SPIN_MAX) epi_gave_up = true;
+            if (it >= smax) epi_gave_up = true;
         };
         auto finish_y_m = [&](int c, auto masked, const f32x4_t (&acc)[4], const u32x2_t (&xg)[4],
                               const float (&pv)[4][2]) {
@@ -1047,7 +1049,8 @@ static hipError_t launch_recur_t(const ChunkArgs& a, hipStream_t st) {
     const hipError_t e = allow_dynamic_lds((const void*)kern, LDS);
     if (e != hipSuccess) return e;
     dim3 grid(NU * NT), block(FUSED ? (DPLR ? 448 : 384) : 64 * (PL::NCW + 3));
-    const EpiArgs ep{static_cast<const uint16_t*>(a.xg), a.rms_w, static_cast<uint16_t*>(a.y), a.epi_part};
+    const EpiArgs ep{static_cast<const uint16_t*>(a.xg), a.rms_w, static_cast<uint16_t*>(a.y), a.epi_part,
+                     a.epi_spin_max};
     hipLaunchKernelGGL(kern, grid, block, LDS, st, a.s0, a.s_final, a.tab, a.N, a.T, a.H, ws, a.o, a.piece, ep);
     return hipGetLastError();
 }

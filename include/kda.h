@@ -458,7 +458,10 @@ kda_status kda_layer_fwd_workspace_size(int32_t N, int64_t T_total, int32_t H, i
  * particular two kda_layer_fwd calls running at the same time on different
  * streams can each hold CUs the other's workgroups need. Run such calls on one
  * stream, or use kda_layer_chunk_fwd and kda_layer_epilogue, which never wait
- * on one another's workgroups. Otherwise the operator writes o to
+ * on one another's workgroups. (The bound is 65,536 re-reads of the sums; the
+ * environment variable KDA_EPI_SPIN_MAX, a non-negative integer read at each
+ * call, replaces it: 0 makes every wait give up at once, every y row NaN, which
+ * tests use to exercise that path.) Otherwise the operator writes o to
  * the workspace and the epilogue kernel follows; both ways give the same y up
  * to the order of the sum of squares (one rounding of the RMS). Calls that
  * share a workspace must not run concurrently. Three kernels are enqueued

@@ -307,6 +307,29 @@ def test_layer_decode_step_fused_decode_256():
     check_outputs("fused decode step y (decode-256, sequences 0, 97, 255)", [y_one[seqs]], [y_ref], True)
 
 
+def test_whole_layer_epilogue_wait_gives_up(monkeypatch):
+    """The fused epilogue's bounded wait, forced from the host: with
+    KDA_EPI_SPIN_MAX=0 every wait gives up at once, so every y row is NaN, the
+    launch still ends, and the chain (the final states) is untouched; back at
+    the default bound the next call is normal again."""
+    c = ki.make_layer("prefill-4k", DEV, lengths=[300, 5, 190, 64], H=2, s0_std=0.02)  # N H = 8: fused
+    N, H, d = len(c.lengths), c.xq.shape[1], c.xq.shape[2]
+    assert (N * H) % 8 == 0 and N * H * (d // 16) <= torch.cuda.get_device_properties(0).multi_processor_count
+    args = (c.xq, c.xk, c.xv, c.xa, c.xb, c.xg, c.wq, c.wk, c.wv, c.A_log, c.dt_bias, c.rms_w, c.initial_state,
+            c.cu_seqlens)
+    y_ok, S_ok = kda.layer_fwd(*args)
+    monkeypatch.setenv("KDA_EPI_SPIN_MAX", "0")
+    y_nan, S_nan = kda.layer_fwd(*args)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("KDA_EPI_SPIN_MAX")
+    y_again, _ = kda.layer_fwd(*args)
+    torch.cuda.synchronize()
+    say(f"[layer] epilogue wait forced to give up: {int(torch.isnan(y_nan.float()).sum())} of {y_nan.numel()} NaN")
+    assert bool(torch.isnan(y_nan.float()).all())
+    assert torch.equal(S_nan, S_ok)
+    assert bool(torch.isfinite(y_ok.float()).all()) and torch.equal(y_again, y_ok)
+
+
 WHOLE_CASES = {
     # N H a multiple of 8 and N H d/16 workgroups within the CU count: the fused epilogue
     "prefill-4k": {},
