@@ -23,9 +23,11 @@
 
 namespace kda {
 
-// Prologue: a block of four waves covers 16 consecutive tokens of one head,
-// each wave four of them (G), with every load issued before the first wait.
-constexpr int G = 4;       // tokens per wave
+// Prologue: a block of four waves covers 32 consecutive tokens of one head,
+// each wave eight of them (G), with every load issued before the first wait.
+// Eight rather than four: more bytes in flight per wave (91 VGPRs at d = 128
+// with bf16, five waves per SIMD) and fewer halo rows per token.
+constexpr int G = 8;       // tokens per wave
 constexpr int PT = 4 * G;  // tokens per block
 
 template <int D, typename TE>
@@ -40,8 +42,10 @@ __global__ __launch_bounds__(256) void layer_prologue_kernel(PrologueIn<TE> in, 
     constexpr int PER = D / 64;
     using PR = Pair<TE, PER>;
     const int h = blockIdx.x % H;
-    const int t0 = (blockIdx.x / H) * PT + (threadIdx.x >> 6) * G;  // this wave's first token
-    if (t0 >= T) return;  // uniform over the wave
+    // this wave's first token, stated uniform so that the sequence search below
+    // runs on scalar loads (beside the window's vector loads, not behind them)
+    const int t0 = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / H) * PT + (int)(threadIdx.x >> 6) * G);
+    if (t0 >= T) return;
     const int l = threadIdx.x & 63, c0 = PER * l;
     PrologueWindow<D, G, TE> win;
     win.load(in, h, t0, T, H, c0, l);
@@ -67,8 +71,12 @@ __global__ __launch_bounds__(256) void layer_prologue_kernel(PrologueIn<TE> in, 
         }
         return first;
     };
-    const float bl = win.compute(f, t0, T, seq_first, [&](int j, const float (&oq)[PER], const float (&ok)[PER],
-                                                          const float (&ov)[PER], const float (&og)[PER]) {
+    int fst[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) fst[j] = seq_first(t0 + j);
+    const float bl = win.compute_all(f, t0, fst, [&](int j, const float (&oq)[PER], const float (&ok)[PER],
+                                                    const float (&ov)[PER], const float (&og)[PER]) {
+        if (t0 + j >= T) return;
         const int64_t ro = ((int64_t)(t0 + j) * H + h) * D + c0;
         PR::st(q + ro, oq);
         PR::st(k + ro, ok);

@@ -147,6 +147,36 @@ struct PrologueWindow {
         for (int j = 0; j < G; ++j) PR::ld(in.xa + ((int64_t)min(t0 + j, T - 1) * H + h) * D + c0, xg[j]);
         xbl = ld_in(in.xb, (int64_t)min(t0 + (l & (G - 1)), T - 1) * H + h);
     }
+    // Token t0 + j (its sequence starting at token fst): the four outputs'
+    // PER channels.
+    __device__ __forceinline__ void token(const ConvFilters<D>& f, int j, int t, int fst, float (&oq)[PER],
+                                          float (&ok)[PER], float (&ov)[PER], float (&og)[PER]) const {
+        float y[3][PER];
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+#pragma unroll
+            for (int p = 0; p < PER; ++p) {
+                float acc = 0.f;
+#pragma unroll
+                for (int i = 0; i < CONV_W; ++i)
+                    if (t - (CONV_W - 1) + i >= fst) acc += f.fw[m][p][i] * win[m][j + i][p];
+                y[m][p] = acc * sigm(acc);  // swish
+            }
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            sq += y[0][p] * y[0][p];
+            sk += y[1][p] * y[1][p];
+        }
+        const float nq = rsqrtf(wave_sum(sq) + LAYER_EPS), nk = rsqrtf(wave_sum(sk) + LAYER_EPS);
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            oq[p] = y[0][p] * nq;
+            ok[p] = y[1][p] * nk;
+            ov[p] = y[2][p];
+            og[p] = -f.scale * softplus_f(xg[j][p] + f.db[p]);
+        }
+    }
     // Tokens t0 + j < tend, in order: first(t) is the first token of t's
     // sequence (taps before it read zeros); sink(j, q, k, v, log_alpha) takes
     // each token's PER channels. Returns beta of token t0 + (lane & (G - 1)).
@@ -157,33 +187,24 @@ struct PrologueWindow {
         for (int j = 0; j < G; ++j) {
             const int t = t0 + j;
             if (t >= tend) break;
-            const int fst = first(t);
-            float y[3][PER];
+            float oq[PER], ok[PER], ov[PER], og[PER];
+            token(f, j, t, first(t), oq, ok, ov, og);
+            sink(j, oq, ok, ov, og);
+        }
+        return sigm(xbl);
+    }
+    // The same for all G tokens with no branch between them, so that their
+    // dependency chains interleave: fst[j] is token t0 + j's first token, every
+    // token is computed (rows past the end were clamped on load) and the sink
+    // decides what to store.
+    template <typename Sink>
+    __device__ __forceinline__ float compute_all(const ConvFilters<D>& f, int t0, const int (&fst)[G],
+                                                 Sink&& sink) const {
 #pragma unroll
-            for (int m = 0; m < 3; ++m)
-#pragma unroll
-                for (int p = 0; p < PER; ++p) {
-                    float acc = 0.f;
-#pragma unroll
-                    for (int i = 0; i < CONV_W; ++i)
-                        if (t - (CONV_W - 1) + i >= fst) acc += f.fw[m][p][i] * win[m][j + i][p];
-                    y[m][p] = acc * sigm(acc);  // swish
-                }
-            float sq = 0.f, sk = 0.f;
-#pragma unroll
-            for (int p = 0; p < PER; ++p) {
-                sq += y[0][p] * y[0][p];
-                sk += y[1][p] * y[1][p];
-            }
-            const float nq = rsqrtf(wave_sum(sq) + LAYER_EPS), nk = rsqrtf(wave_sum(sk) + LAYER_EPS);
-            float oq[PER], ok[PER], og[PER];
-#pragma unroll
-            for (int p = 0; p < PER; ++p) {
-                oq[p] = y[0][p] * nq;
-                ok[p] = y[1][p] * nk;
-                og[p] = -f.scale * softplus_f(xg[j][p] + f.db[p]);
-            }
-            sink(j, oq, ok, y[2], og);
+        for (int j = 0; j < G; ++j) {
+            float oq[PER], ok[PER], ov[PER], og[PER];
+            token(f, j, t0 + j, fst[j], oq, ok, ov, og);
+            sink(j, oq, ok, ov, og);
         }
         return sigm(xbl);
     }
