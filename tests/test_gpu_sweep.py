@@ -9,7 +9,8 @@ size, the input and gate dtypes (each bf16 or fp32, mixed too), the gate
 regime (the workloads' fast decay, slow decay, or in between), the initial
 state (absent or N(0, 0.02)) and the output dtype.
 The draws come from fixed seeds, so every run checks the same cases; each case
-prints its draw before it runs.
+prints its draw before it runs. KDA_SWEEP_SCALE=k in the environment runs k
+times as many draws of each sweep.
 
 Bars: 1e-4 with fp32 inputs and 2e-2 with bf16 inputs (max-abs error over the
 oracle's RMS, for o and the final state); a bf16 o must equal the fp32 o
@@ -20,6 +21,8 @@ kernel's where the call falls back to it); the layer's kernels within one
 bf16 step (bf16) or 1e-5 of the RMS (fp32) of the fp64 layer oracle, the
 histories exactly; the DPLR operator (bf16 inputs) 2e-2 against its own
 recurrence."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -33,6 +36,9 @@ from parity import err, kda, say, tol_for
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 EDGE = [0, 1, 2, 63, 64, 65, 127, 128, 129]
+# KDA_SWEEP_SCALE multiplies every sweep's number of draws (default 1); the
+# draws of a smaller scale are the first ones of a larger one.
+SCALE = max(1, int(os.environ.get("KDA_SWEEP_SCALE", "1")))
 
 
 def draw(seed):
@@ -62,7 +68,7 @@ def describe(p):
             f"shift={p['shift']} s0={p['s0']} packed={p['packed']}")
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(16 * SCALE))
 def test_prefill_sweep(seed):
     p = draw(seed)
     say(f"[sweep prefill {seed}] {describe(p)}")
@@ -81,7 +87,7 @@ def test_prefill_sweep(seed):
     assert torch.equal(o16, o.to(torch.bfloat16)) and torch.equal(S16, S)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(8 * SCALE))
 def test_decode_sweep(seed):
     """Two decode steps in place, each against the oracle's step from the
     previous oracle state."""
@@ -105,7 +111,7 @@ def test_decode_sweep(seed):
         S_ref = torch.from_numpy(np.asarray(S_next))
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(6 * SCALE))
 def test_backward_sweep(seed):
     p = draw(100 + seed)
     p["lengths"] = [min(x, 200) for x in p["lengths"]][:3]  # the gradient oracle's size
@@ -137,7 +143,7 @@ def bf16_steps(x, ref) -> float:
     return float(np.max(np.abs(x - ref) / allow))
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(8 * SCALE))
 def test_layer_sweep(seed):
     """kda_layer_fwd over random shapes; N H a multiple of 8 (within the CU
     count) takes the epilogue inside the recursion, any other the epilogue kernel."""
@@ -168,7 +174,7 @@ def test_layer_sweep(seed):
         assert torch.equal(y, y_two)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(6 * SCALE))
 def test_dplr_sweep(seed):
     """kda_dplr_chunk_fwd (bf16 inputs; gates bf16 or fp32; fp32 or bf16 o)
     against the oracle's DPLR recurrence."""
@@ -207,7 +213,7 @@ def close_to(got, ref, bf16, label):
         assert worst <= 1e-5
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(8 * SCALE))
 def test_layer_kernels_sweep(seed):
     """The layer's prologue, epilogue, convolution history and one-token
     prologue over random packed lengths (0-3 tokens, the 16-token tile edges, up
